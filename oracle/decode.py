@@ -1,0 +1,179 @@
+"""Oracle decode loops: full-KV greedy and the VeriCache draft / verify / accept loop.
+
+Greedy ([KV4] "Autoregressive Decoding and the KV Cache"): prefill the prompt
+at positions 0..T-1, emit g0 = argmax of row T-1, then g_i = argmax of the
+row for g_{i-1} at position T+i-1.  N emitted tokens include g0.
+
+VeriCache round ([VC1] "The Core Idea", pseudocode and worked example;
+[VC3] "实践案例" case 1):
+    rows    = [pending] + draft            pending = last emitted token, not yet in any cache
+    draft   : x greedy steps over the draft cache (compressed rows + committed
+              exact rows + this round's own draft rows)
+    verify  : the x + 1 rows at positions pos..pos+x, each seeing the full KV and
+              the verify rows before it; ver[i] = argmax of row i
+              (ver[0..x-1] check the drafts, ver[x] is the bonus prediction)
+    accept  : a = first i with draft[i] != ver[i], else x
+    emit    : draft[:a] + [ver[a]]          (a + 1 tokens; x + 1 when every draft matched)
+    commit  : the verifier's exact K/V rows 0..a (pending, draft[0..a-1]) are
+              appended to the full KV and to the draft cache's exact tail;
+              draft rows are discarded; pending = ver[a]; pos += a + 1
+Readings where the pages are silent (each listed in the design doc):
+    - the verifier's rows, not the draft's, are what the caches keep for accepted tokens;
+    - generated rows are never re-compressed: the tail stays in the model dtype;
+    - every round drafts a full x, and the output is cut to N at the end;
+    - the acceptance rule is greedy exact match (not rejection sampling).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .compress import Quantized, tokdrop
+from .kvcache import FixedRows, RowStore, chain
+from .model import Weights, argmax, row_forward
+
+
+def accept(draft, verified):
+    """Accept-until-first-mismatch ([VC1] "The Core Idea").
+
+    draft has x tokens, verified has x + 1 predictions.  Returns (a, emitted):
+    a = number of leading drafts equal to the verifier's predictions, emitted
+    = draft[:a] + [verified[a]] (the correction at a mismatch, the bonus token
+    when a == x).
+    """
+    x = len(draft)
+    assert len(verified) == x + 1
+    a = x
+    for i in range(x):
+        if draft[i] != verified[i]:
+            a = i
+            break
+    return a, list(draft[:a]) + [verified[a]]
+
+
+class Prefill:
+    __slots__ = ("full", "g0", "q_obs", "last_logits")
+
+    def __init__(self, full, g0, q_obs, last_logits):
+        self.full, self.g0, self.q_obs, self.last_logits = full, g0, q_obs, last_logits
+
+
+def prefill(W: Weights, prompt, obs_window: int = 32) -> Prefill:
+    """Rows 0..T-1 one at a time; keeps the post-RoPE queries of the last
+    obs_window positions ([L][Hq][W][D]) for the token-drop compressor."""
+    s = W.shape
+    T = len(prompt)
+    full = RowStore(s.n_layers, s.n_kv_heads, s.head_dim, max(T, 1))
+    wn = min(obs_window, T)
+    q_obs = np.zeros((s.n_layers, s.n_q_heads, wn, s.head_dim))
+    out = None
+    for p, tok in enumerate(prompt):
+        out = row_forward(W, int(tok), p, full.rows)
+        full.append(out.k, out.v)
+        if p >= T - wn:
+            q_obs[:, :, p - (T - wn)] = out.q
+    return Prefill(full, argmax(out.logits), q_obs, out.logits)
+
+
+def greedy(W: Weights, prompt, n_tokens: int, pre: Prefill | None = None, force=None):
+    """Full-KV greedy decode.  Returns (tokens, per-step logits).
+
+    force: optional token list; step i then consumes force[i-1] instead of the
+    model's own choice (teacher forcing after a flagged near-tie divergence)."""
+    pre = pre or prefill(W, prompt)
+    full = pre.full.copy()
+    T = len(prompt)
+    toks = [pre.g0]
+    logits = [pre.last_logits]
+    while len(toks) < n_tokens:
+        i = len(toks)
+        prev = toks[-1] if force is None else int(force[i - 1])
+        out = row_forward(W, prev, T + i - 1, full.rows)
+        full.append(out.k, out.v)
+        toks.append(argmax(out.logits))
+        logits.append(out.logits)
+    return toks, logits
+
+
+# --------------------------------------------------------------------------
+# draft caches built from the prefill
+# --------------------------------------------------------------------------
+def draft_cache_identity(pre: Prefill, **_):
+    """No compression: the draft cache equals the full prefill KV (every round then
+    accepts all x drafts; used to pin the bonus-token rule)."""
+    return pre.full.copy()
+
+
+def draft_cache_tokdrop(pre: Prefill, W: Weights, keep_total: int, keep_recent: int = 64, **_):
+    L, H = W.shape.n_layers, W.shape.n_kv_heads
+    n = pre.full.n
+    Kf = pre.full.K[:, :, :n]
+    Vf = pre.full.V[:, :, :n]
+    idx, Kk, Vk, _scores = tokdrop(Kf, Vf, pre.q_obs, keep_total, keep_recent, W.shape.group)
+    return FixedRows([[Kk[l, j] for j in range(H)] for l in range(L)],
+                     [[Vk[l, j] for j in range(H)] for l in range(L)])
+
+
+def draft_cache_quant(pre: Prefill, W: Weights, bits: int, group: int, **_):
+    n = pre.full.n
+    q = Quantized(pre.full.K[:, :, :n], pre.full.V[:, :, :n], bits, group)
+    Kd, Vd = q.rows_K(), q.rows_V()
+    L, H = Kd.shape[:2]
+    return FixedRows([[Kd[l, j] for j in range(H)] for l in range(L)],
+                     [[Vd[l, j] for j in range(H)] for l in range(L)])
+
+
+class RoundLog:
+    __slots__ = ("pos", "draft", "verified", "a", "emitted")
+
+    def __init__(self, pos, draft, verified, a, emitted):
+        self.pos, self.draft, self.verified, self.a, self.emitted = pos, draft, verified, a, emitted
+
+
+def vericache(W: Weights, prompt, n_tokens: int, x: int, make_draft_cache, pre: Prefill | None = None,
+              drafter=None):
+    """The VeriCache loop.  Returns (tokens, rounds).
+
+    make_draft_cache(pre) -> segment with rows(l, j) (the compressed cache).
+    drafter(round_index, pending, own_draft) -> replacement draft list (to test
+        that any drafter still yields the greedy output); None keeps the model's drafts.
+    """
+    s = W.shape
+    pre = pre or prefill(W, prompt)
+    full = pre.full.copy()
+    comp = make_draft_cache(pre)
+    tail = RowStore(s.n_layers, s.n_kv_heads, s.head_dim)
+    T = len(prompt)
+    out = [pre.g0]
+    pending, pos = pre.g0, T
+    rounds = []
+    while len(out) < n_tokens:
+        # ---- draft x tokens with the compressed cache
+        dtail = RowStore(s.n_layers, s.n_kv_heads, s.head_dim)
+        past = chain(comp, tail, dtail)
+        draft, t = [], pending
+        for i in range(x):
+            o = row_forward(W, t, pos + i, past)
+            dtail.append(o.k, o.v)
+            t = argmax(o.logits)
+            draft.append(t)
+        if drafter is not None:
+            draft = [int(v) for v in drafter(len(rounds), pending, draft)]
+        # ---- verify x + 1 rows against the full KV
+        rows = [pending] + draft
+        vrows = RowStore(s.n_layers, s.n_kv_heads, s.head_dim)
+        vpast = chain(full, vrows)
+        ver, kv = [], []
+        for i, tok in enumerate(rows):
+            o = row_forward(W, tok, pos + i, vpast)
+            vrows.append(o.k, o.v)
+            kv.append((o.k, o.v))
+            ver.append(argmax(o.logits))
+        # ---- accept and commit
+        a, emitted = accept(draft, ver)
+        rounds.append(RoundLog(pos, draft, ver, a, emitted))
+        out += emitted
+        for i in range(a + 1):
+            full.append(*kv[i])
+            tail.append(*kv[i])
+        pending, pos = out[-1], pos + a + 1
+    return out[:n_tokens], rounds

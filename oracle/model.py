@@ -1,0 +1,197 @@
+"""Oracle decoder: a pre-norm Llama-style model evaluated one row at a time.
+
+The pages never spell out the architecture; the workloads name RMSNorm, RoPE,
+SwiGLU and MHA/GQA with Xavier-initialised weights, which is read here as the
+usual pre-norm decoder:
+
+    h = E[tok]
+    per layer l:
+        a = rmsnorm(h) * g1[l]
+        q, k, v = Wq a, Wk a, Wv a ; q, k = rope(q, pos), rope(k, pos)   (K is cached after RoPE)
+        o_h = sum_t softmax_t(q_h . k_{j(h),t} / sqrt(D)) v_{j(h),t}      over cached rows + own row
+        h = h + Wo concat(o)
+        f = rmsnorm(h) * g2[l]
+        h = h + W2 (silu(W1 f) * (W3 f))
+    logits = Wlm (rmsnorm(h) * gF)
+
+Everything is float64.  Between steps the value is rounded to the storage type
+(bf16 or fp32) at the points where the GPU path stores a tensor in memory:
+norm outputs, q/k/v after RoPE, attention output, the residual after each add,
+the SwiGLU product, and the final norm.  Logits stay float64.
+
+Every row goes through ``row_forward`` with the keys visible to it given in
+absolute-position order, so a verification row and the greedy row at the same
+position are the same computation.  That is the property [KV4] "Autoregressive
+Decoding and the KV Cache" states: past rows' K/V do not depend on later
+tokens, so caching them is exact.
+
+Pins: tests/test_oracle_model.py checks RMSNorm against its closed form, RoPE
+at position 0 (identity), norm preservation and relative-position dependence,
+and the cached row-by-row greedy decode against a brute-force recomputation
+of the whole sequence in matrix form with no cache (``sequence_logits``).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import synth
+from synth.configs import ModelShape
+
+from .rounding import storage_round
+
+
+def _stored(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """Generated float64 draw -> the value the model stores (input recipe)."""
+    if dtype == "bf16":
+        return synth.bf16_bits_to_f32(synth.gen_bf16(x64)).astype(np.float64)
+    if dtype == "fp32":
+        return synth.f32(x64).astype(np.float64)
+    return np.asarray(x64, dtype=np.float64)
+
+
+class Weights:
+    """All weights of a model shape, as float64 arrays of the stored values.
+
+    Matrices are [out][in].  Norm gains are ones.  Xavier-uniform for every
+    matrix, with fan_in = in, fan_out = out (E is [V][d], Wlm is [V][d]).
+    """
+
+    def __init__(self, shape: ModelShape, seed: int = 0, dtype: str | None = None):
+        s = shape
+        dt = dtype or s.dtype
+        self.shape, self.dtype = s, dt
+        D = s.head_dim
+
+        def mat(stream, out_dim, in_dim):
+            return _stored(synth.xavier(stream, (out_dim, in_dim), in_dim, out_dim, seed), dt)
+
+        self.E = mat(synth.S_EMBED, s.vocab, s.d_model)
+        self.Wlm = mat(synth.S_LMHEAD, s.vocab, s.d_model)
+        self.Wq, self.Wk, self.Wv, self.Wo, self.W1, self.W3, self.W2 = ([] for _ in range(7))
+        for l in range(s.n_layers):
+            st = lambda t: synth.layer_stream(l, t)
+            self.Wq.append(mat(st(synth.T_WQ), s.n_q_heads * D, s.d_model))
+            self.Wk.append(mat(st(synth.T_WK), s.n_kv_heads * D, s.d_model))
+            self.Wv.append(mat(st(synth.T_WV), s.n_kv_heads * D, s.d_model))
+            self.Wo.append(mat(st(synth.T_WO), s.d_model, s.n_q_heads * D))
+            self.W1.append(mat(st(synth.T_W1), s.ffn, s.d_model))
+            self.W3.append(mat(st(synth.T_W3), s.ffn, s.d_model))
+            self.W2.append(mat(st(synth.T_W2), s.d_model, s.ffn))
+        self.g1 = [np.ones(s.d_model) for _ in range(s.n_layers)]
+        self.g2 = [np.ones(s.d_model) for _ in range(s.n_layers)]
+        self.gF = np.ones(s.d_model)
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g, over the last axis."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def rope_angles(pos: int, head_dim: int, theta: float) -> np.ndarray:
+    """theta_i = pos * theta**(-2i/D), i < D/2."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return pos * theta ** (-2.0 * i / head_dim)
+
+
+def rope(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """Rotate-half RoPE on [..., D]: pair (i, i + D/2) is rotated by angle theta_i."""
+    D = x.shape[-1]
+    ang = rope_angles(pos, D, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., : D // 2], x[..., D // 2:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """softmax(K q / sqrt(D)) V for one query row q [D] over keys K, V [n][D]."""
+    s = K @ q / math.sqrt(q.shape[-1])
+    p = np.exp(s - s.max())
+    return (p / p.sum()) @ V
+
+
+class RowOut:
+    __slots__ = ("logits", "k", "v", "q")
+
+    def __init__(self, logits, k, v, q):
+        self.logits, self.k, self.v, self.q = logits, k, v, q
+
+
+def row_forward(W: Weights, tok: int, pos: int, past, rdtype: str | None = None) -> RowOut:
+    """One token through the whole model.
+
+    past(l, j) -> (K [n][D], V [n][D]): the cached rows visible to this row for
+    layer l, KV head j, in absolute-position order (this row's own K/V is
+    appended after them).  Returns float64 logits [V], this row's K/V rows
+    [L][Hkv][D] (as stored) and its post-RoPE queries [L][Hq][D].
+    """
+    s = W.shape
+    R = storage_round(rdtype or W.dtype)
+    D, G = s.head_dim, s.group
+    L, Hq, Hkv = s.n_layers, s.n_q_heads, s.n_kv_heads
+    ks = np.empty((L, Hkv, D))
+    vs = np.empty((L, Hkv, D))
+    qs = np.empty((L, Hq, D))
+    h = R(W.E[tok])
+    for l in range(L):
+        a = R(rmsnorm(h, W.g1[l], s.eps))
+        q = R(rope((W.Wq[l] @ a).reshape(Hq, D), pos, s.rope_theta))
+        k = R(rope((W.Wk[l] @ a).reshape(Hkv, D), pos, s.rope_theta))
+        v = R((W.Wv[l] @ a).reshape(Hkv, D))
+        ks[l], vs[l], qs[l] = k, v, q
+        o = np.empty((Hq, D))
+        for hq in range(Hq):
+            j = hq // G
+            Kp, Vp = past(l, j)
+            o[hq] = attend(q[hq], np.concatenate([Kp, k[j][None]]), np.concatenate([Vp, v[j][None]]))
+        o = R(o)
+        h = R(h + W.Wo[l] @ o.reshape(-1))
+        f = R(rmsnorm(h, W.g2[l], s.eps))
+        m = R(silu(W.W1[l] @ f) * (W.W3[l] @ f))
+        h = R(h + W.W2[l] @ m)
+    z = R(rmsnorm(h, W.gF, s.eps))
+    return RowOut(W.Wlm @ z, ks, vs, qs)
+
+
+def argmax(logits: np.ndarray) -> int:
+    """Greedy choice; ties go to the lowest index (np.argmax returns the first maximum)."""
+    return int(np.argmax(logits))
+
+
+def sequence_logits(W: Weights, tokens, rdtype: str | None = None) -> np.ndarray:
+    """Brute-force reference with no cache: the whole sequence in matrix form,
+    causal mask, every position's logits [n][V].  Written independently of
+    row_forward (matrix attention, explicit mask) for the no-cache pin."""
+    s = W.shape
+    R = storage_round(rdtype or W.dtype)
+    D, G, n = s.head_dim, s.group, len(tokens)
+    Hq, Hkv = s.n_q_heads, s.n_kv_heads
+    H = R(W.E[np.asarray(tokens)])                                   # [n][d]
+    mask = np.tril(np.ones((n, n), dtype=bool))
+    for l in range(s.n_layers):
+        A = R(rmsnorm(H, W.g1[l], s.eps))
+        Q = (A @ W.Wq[l].T).reshape(n, Hq, D)
+        K = (A @ W.Wk[l].T).reshape(n, Hkv, D)
+        V = R((A @ W.Wv[l].T).reshape(n, Hkv, D))
+        Q = R(np.stack([rope(Q[p], p, s.rope_theta) for p in range(n)]))
+        K = R(np.stack([rope(K[p], p, s.rope_theta) for p in range(n)]))
+        O = np.empty((n, Hq, D))
+        for hq in range(Hq):
+            j = hq // G
+            S = (Q[:, hq, :] @ K[:, j, :].T) / math.sqrt(D)
+            S = np.where(mask, S, -np.inf)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            O[:, hq, :] = P @ V[:, j, :]
+        O = R(O)
+        H = R(H + O.reshape(n, -1) @ W.Wo[l].T)
+        F = R(rmsnorm(H, W.g2[l], s.eps))
+        M = R(silu(F @ W.W1[l].T) * (F @ W.W3[l].T))
+        H = R(H + M @ W.W2[l].T)
+    Z = R(rmsnorm(H, W.gF, s.eps))
+    return Z @ W.Wlm.T

@@ -1,0 +1,76 @@
+"""The pages' central invariant: VeriCache emits exactly the full-KV greedy
+tokens ([VC1] "The Core Idea" and "Final Takeaways"; [VC3] "是什么"), for any
+draft horizon, any compressor, and even an adversarial drafter."""
+import random
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import decode as D
+from oracle.model import Weights
+from synth.configs import ModelShape, c1
+
+TINY = ModelShape(n_layers=2, d_model=32, n_q_heads=4, n_kv_heads=2, head_dim=8, ffn=48, vocab=16,
+                  rope_theta=10000.0, dtype="fp32")
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    W = Weights(TINY)
+    p = synth.prompt(3, 48, TINY.vocab)
+    pre = D.prefill(W, p, obs_window=8)
+    ref, _ = D.greedy(W, p, 30, pre=pre)
+    return W, p, pre, ref
+
+
+@pytest.mark.parametrize("x", range(1, 9))
+@pytest.mark.parametrize("kind", ["tokdrop", "quant2", "quant4", "identity"])
+def test_vericache_equals_greedy(tiny, x, kind):
+    W, p, pre, ref = tiny
+    mk = {
+        "tokdrop": lambda pr: D.draft_cache_tokdrop(pr, W, keep_total=12, keep_recent=4),
+        "quant2": lambda pr: D.draft_cache_quant(pr, W, bits=2, group=8),
+        "quant4": lambda pr: D.draft_cache_quant(pr, W, bits=4, group=8),
+        "identity": D.draft_cache_identity,
+    }[kind]
+    out, rounds = D.vericache(W, p, 30, x, mk, pre=pre)
+    assert out == ref
+    for r in rounds:
+        assert len(r.emitted) == r.a + 1 and 0 <= r.a <= x
+        assert len(r.verified) == x + 1
+        if r.a == x:
+            assert r.emitted[-1] == r.verified[x]
+    if kind == "identity":
+        assert all(r.a == x for r in rounds)   # bonus token every round
+
+
+def test_adversarial_drafter_still_lossless(tiny):
+    W, p, pre, ref = tiny
+    rng = random.Random(0)
+    out, rounds = D.vericache(W, p, 30, 4, D.draft_cache_identity, pre=pre,
+                              drafter=lambda r, pend, own: [rng.randrange(TINY.vocab) for _ in own])
+    assert out == ref
+    assert sum(r.a == 0 for r in rounds) >= len(rounds) // 2
+
+
+def test_bf16_model_vericache_equals_greedy():
+    W = Weights(TINY, dtype="bf16")
+    p = synth.prompt(4, 40, TINY.vocab)
+    pre = D.prefill(W, p, obs_window=8)
+    ref, _ = D.greedy(W, p, 20, pre=pre)
+    out, _ = D.vericache(W, p, 20, 5, lambda pr: D.draft_cache_quant(pr, W, bits=3, group=8), pre=pre)
+    assert out == ref
+
+
+@pytest.mark.slow
+def test_c1_full_run():
+    w = c1()
+    W = Weights(w.model)
+    p = synth.prompt(0, w.ctx[0], w.model.vocab)
+    pre = D.prefill(W, p)
+    ref, _ = D.greedy(W, p, w.n_tokens, pre=pre)
+    out, rounds = D.vericache(W, p, w.n_tokens, w.x[0],
+                              lambda pr: D.draft_cache_tokdrop(pr, W, keep_total=256, keep_recent=64), pre=pre)
+    assert out == ref and len(out) == 64
+    assert sum(len(r.emitted) for r in rounds) >= 64

@@ -1,0 +1,288 @@
+/*
+ * vc.h -- C ABI of the VeriCache draft/verify hot path for AMD MI355X (gfx950).
+ *
+ * Method (cited by page title and section):
+ *   "VeriCache: Making Lossy KV Compression Exact" (devshah.ca), "The Core Idea":
+ *     the same weights draft x tokens greedily over a compressed KV cache; one
+ *     verification forward over the full KV cache returns x + 1 predictions
+ *     (one per drafted position plus a bonus); tokens are accepted left to right
+ *     until the first mismatch, where the full-cache token is emitted instead;
+ *     when every draft matches the bonus token is emitted too.
+ *   Same page, "Verifying Without Giving Back the Speedup": the full cache lives
+ *     off the GPU and is brought in only to verify; verification is staggered
+ *     across requests so transfers overlap other requests' drafting.
+ *   "VeriCache Guide: Lossless Inference with Lossy KV Caches" (aifetchly),
+ *     "The Uniform Compressor Interface": compress(full_k, full_v) -> (ck, cv)
+ *     for token-eviction and low-bit quantization families.
+ *
+ * Conventions
+ *   Pointers are device pointers unless the name ends in _host (pinned host
+ *   memory from hipHostMalloc).  Every buffer is allocated and owned by the
+ *   caller; the library allocates nothing on the hot path (vc_model_create
+ *   allocates its RoPE table once and vc_model_destroy frees it).
+ *   Element types: VC_F32 (IEEE float) or VC_BF16 (bfloat16 bit patterns).
+ *   KV rows are head-major: a cache buffer of one request is
+ *   [L][Hkv][cap][D], row t of (layer l, head j) at ((l*Hkv + j)*cap + t)*D.
+ *   All entry points only enqueue work on the given stream(s) and return;
+ *   kernel faults surface at the caller's next synchronisation.  Calls are
+ *   thread-compatible, not thread-safe: do not share one vc_model between
+ *   threads without external locking.
+ *   Outputs are bitwise reproducible, and the arithmetic of each verify row
+ *   does not depend on how many rows are verified together nor on whether a
+ *   key sits in the staged cache or in the verify tail (row invariance), so
+ *   vc_verify with n_rows = 1 is full-KV greedy decoding with exactly the
+ *   tokens VeriCache emits.
+ *
+ * Errors: every call returns vc_status; 0 is success.  Negative values:
+ *   VC_ERR_ARG (null pointer, bad shape or size), VC_ERR_UNSUPPORTED (e.g. a
+ *   head_dim or bit width the kernels do not implement), VC_ERR_CAPACITY (a
+ *   workspace, tail or slot too small), VC_ERR_HIP (a HIP launch or copy
+ *   failed).  vc_last_error() returns a message for the calling thread.
+ */
+#ifndef VC_H
+#define VC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vc_status;
+#define VC_OK 0
+#define VC_ERR_ARG (-1)
+#define VC_ERR_UNSUPPORTED (-2)
+#define VC_ERR_CAPACITY (-3)
+#define VC_ERR_HIP (-4)
+
+#define VC_F32 0
+#define VC_BF16 1
+
+#define VC_TOKDROP 1
+#define VC_QUANT 2
+
+#define VC_MAX_BATCH 16 /* requests per vc_draft_step / vc_attn_* call */
+
+const char* vc_last_error(void);
+int32_t vc_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Model: a pre-norm decoder (RMSNorm, rotate-half RoPE, GQA attention,
+ * SwiGLU FFN, untied LM head).  The pages do not describe the architecture;
+ * this is the Llama-style reading of the workloads' shapes.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t dtype;    /* VC_F32 (head_dim 64) or VC_BF16 (head_dim 128) */
+  float rope_theta; /* RoPE base */
+  float eps;        /* RMSNorm epsilon */
+  int32_t max_pos;  /* highest position + 1 the RoPE table must cover */
+} vc_model_desc;
+
+/* Weight pointers (caller-owned, model dtype, matrices row-major [out][in]). */
+typedef struct {
+  const void* embed;      /* [V][d]                                            */
+  const void* lm_head;    /* [V][d]                                            */
+  const void* norm_final; /* [d]                                               */
+  const void* norm_attn;  /* [L][d]                                            */
+  const void* norm_ffn;   /* [L][d]                                            */
+  const void* w_qkv;      /* [L][(Hq + 2 Hkv) D][d]: rows of Wq, then Wk, then Wv */
+  const void* w_o;        /* [L][d][Hq D]                                      */
+  const void* w_gu;       /* [L][2 ffn][d]: rows of W1 (gate), then W3 (up)    */
+  const void* w_down;     /* [L][d][ffn]                                       */
+} vc_weights;
+
+typedef struct vc_model vc_model;
+
+/* Validates shapes, copies the descriptor and pointers, and builds the RoPE
+ * cos/sin table (angles in float64, stored float32).  Synchronises `s`. */
+vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStream_t s, vc_model** out);
+vc_status vc_model_destroy(vc_model* m);
+
+/* Workspace bytes for vc_draft_step / vc_verify / vc_prefill with at most
+ * max_rows rows per call (draft batch, x + 1, or prefill chunk) and at most
+ * max_keys keys visible to any row. */
+vc_status vc_ws_size(const vc_model* m, int32_t max_rows, int32_t max_keys, size_t* bytes);
+
+/* ------------------------------------------------------------------------
+ * Compression ("The Uniform Compressor Interface").  Input: one request's
+ * full K (after RoPE) and V, [L][Hkv][src_cap][D] in `dtype`, rows [0, seq_len).
+ *
+ * VC_TOKDROP: per (layer, KV head), score each candidate row t < T - R by the
+ *   mean over the GQA group's observation queries of its causal softmax
+ *   probability (q_obs [L][W][Hq][D] in dtype: the post-RoPE queries of the
+ *   last W prompt positions); keep the top keep_total - R candidates (ties to
+ *   the smaller index) plus the last R rows, ascending.  Output blob:
+ *     K_keep [L][Hkv][Kk][D] dtype | V_keep same | idx [L][Hkv][Kk] int32
+ *   with Kk = min(T, max(keep_total, min(R, T))).
+ * VC_QUANT: b in {2,3,4} bits, group G in {64,128}, Tq = floor(T/G)*G.
+ *   K per channel (groups of G tokens), V per token (groups of G channels):
+ *   zero = fp16(min), scale = fp16((max - min) / (2^b - 1)),
+ *   code = scale == 0 ? 0 : clamp(rint((x - zero) / scale), 0, 2^b - 1),
+ *   IEEE float32 arithmetic.  Output blob:
+ *     Kc [L][Hkv][Tq][D*b/8]        u8  token rows; channel d at bits [d*b, d*b+b)
+ *     Vc [L][Hkv][Tq/64][D][64*b/8] u8  per channel, 64 tokens; token i at bits [i*b, i*b+b)
+ *     Ks, Kz [L][Hkv][Tq/G][D]      fp16
+ *     Vs, Vz [L][Hkv][Tq][D/G]      fp16
+ *     Kr, Vr [L][Hkv][T-Tq][D]      dtype (rows left unquantized)
+ *   Bitstreams are little-endian (stream bit n = bit n%8 of byte n/8).
+ * Every section starts at a multiple of 256 bytes.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t kind;                                /* VC_TOKDROP | VC_QUANT            */
+  int32_t bits, group;                         /* VC_QUANT                         */
+  int32_t keep_total, keep_recent, obs_window; /* VC_TOKDROP                       */
+  int32_t n_layers, n_q_heads, n_kv_heads, head_dim, seq_len, dtype;
+  int32_t src_cap; /* row pitch (rows) of the input K/V per (layer, head) */
+} vc_compress_desc;
+
+/* Byte offsets of the sections of a compressed blob. */
+typedef struct {
+  size_t total;
+  int32_t n_main;  /* Kk (token drop) or Tq (quant): rows in the main region     */
+  int32_t n_resid; /* rows left unquantized (quant); 0 for token drop            */
+  size_t k_main, v_main, idx;       /* token drop: K_keep, V_keep, idx           */
+  size_t kc, vc, ks, kz, vs, vz;    /* quant                                     */
+  size_t kr, vr;                    /* quant residual rows                       */
+} vc_compress_layout;
+
+vc_status vc_compress_layout_of(const vc_compress_desc* d, vc_compress_layout* out);
+vc_status vc_compress_size(const vc_compress_desc* d, size_t* out_bytes, size_t* ws_bytes);
+vc_status vc_compress(const vc_compress_desc* d, const void* k, const void* v, const void* q_obs, void* out,
+                      size_t out_bytes, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * Per-request state (host struct, caller-owned).
+ *   tail: exact rows after the compressed region (and after the quantizer's
+ *         residual rows, which stay in the blob), [L][Hkv][tail_cap][D] in
+ *         the model dtype: the verifier's rows of every committed token;
+ *         during a round the draft rows follow at n_tail + draft_idx.
+ *   ctx_len: rows in the full KV = absolute position of the pending token.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void* comp;          /* compressed blob (device)                                */
+  const vc_compress_desc* cd;
+  void* tail_k;
+  void* tail_v;
+  int32_t tail_cap, n_tail;
+  int32_t ctx_len;
+  int32_t draft_idx;         /* step within the current round (vc_draft_step)           */
+  void* full_k_host;         /* pinned [L][Hkv][full_cap][D]                            */
+  void* full_v_host;
+  int32_t full_cap;
+} vc_req;
+
+/* One batched greedy draft step over the compressed caches ("The Core Idea":
+ * the compressed-cache model autoregressively produces the draft).  Request r
+ * consumes in_tok[r] at position ctx_len + draft_idx, writes its K/V row to tail
+ * row n_tail + draft_idx, attends over the compressed region and tail rows
+ * [0, n_tail + draft_idx], and writes out_tok[r] = argmax (ties to the lowest
+ * id).  in_tok/out_tok: device int32 [n].  logits_opt: device float [n][V] or NULL. */
+vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, const int32_t* in_tok, int32_t* out_tok,
+                        float* logits_opt, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Verification forward of ONE request ("The Core Idea": predictions for every
+ * drafted position plus one bonus, in a single pass against the full cache).
+ * Rows tok[0..n_rows) (the pending token then the x drafts) sit at positions
+ * ctx_len .. ctx_len + n_rows - 1; row i attends to staged full-KV rows
+ * [0, ctx_len) and verify rows 0..i.  Writes out_argmax[n_rows] and the exact
+ * K/V of every row into vtail [L][Hkv][vtail_cap][D].  staged_k/v:
+ * [L][Hkv][staged_cap][D] in the model dtype.  n_rows = 1 is greedy decoding. */
+vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v, int32_t staged_cap,
+                    const int32_t* tok, int32_t n_rows, int32_t* out_argmax, float* logits_opt, void* vtail_k,
+                    void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Accept until the first mismatch ("The Core Idea", pseudocode and worked
+ * example).  On `s`: a = first i < x with draft[i] != verified[i] (else x);
+ * result[0] = a, result[1 .. a+1] = draft[0..a) followed by verified[a];
+ * then the verifier's rows 0..a are copied from vtail into the request's
+ * tail at n_tail (overwriting this round's draft rows).  draft: device int32
+ * [x]; verified: device int32 [x+1]; result: device int32 [x+2].
+ * Does not block and does not change *req: after result[0] is visible on the
+ * host, call vc_commit. */
+vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* draft, const int32_t* verified, int32_t x,
+                    const void* vtail_k, const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s);
+
+/* Host half of the commit: enqueue on `copy` the copy of vtail rows 0..a into
+ * the pinned full KV at row ctx_len, then advance req->n_tail and
+ * req->ctx_len by a + 1 and reset draft_idx.  `after` (may be NULL) is an
+ * event the copy stream waits for first (the verify/accept work). */
+vc_status vc_commit(vc_model* m, vc_req* req, int32_t a, const void* vtail_k, const void* vtail_v, int32_t vtail_cap,
+                    hipEvent_t after, hipStream_t copy);
+
+/* Stage the request's full KV rows [0, ctx_len) from pinned host memory into a
+ * device slot [L][Hkv][slot_cap][D] on `copy` (SDMA, hipMemcpy2DAsync), layers
+ * [l0, l1). */
+vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, int32_t slot_cap, int32_t l0, int32_t l1,
+                   hipStream_t copy);
+
+/* Prefill of one prompt (untimed setup): tokens[0..T) at positions 0..T-1 in
+ * chunks of `chunk` rows, each through the verification path with the rows
+ * before it as the staged cache.  Writes K/V into k_out/v_out
+ * [L][Hkv][cap][D], the post-RoPE queries of the last W rows into q_obs
+ * [L][W][Hq][D] (NULL to skip), and g0 = argmax of row T-1 into g0_out[0]. */
+vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out, void* v_out, int32_t cap,
+                     void* q_obs, int32_t W, int32_t* g0_out, int32_t chunk, void* ws, size_t ws_bytes,
+                     hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * Attention cores of one layer (the single-layer workload and tests).
+ * Query rows are [rows][Hq][D] bf16 (post-RoPE); outputs [rows][Hq][D] in out_dtype.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_q_heads, n_kv_heads, head_dim, dtype;
+  int32_t split_len; /* keys per split-K partial, multiple of 64 (0 = library default) */
+  int32_t out_dtype; /* VC_F32 or VC_BF16 element type of `out` (bf16 = round to nearest even of the fp32 result) */
+} vc_attn_desc;
+
+typedef struct {
+  const void* comp;            /* compressed blob of ONE layer (L = 1 in its descriptor) */
+  const vc_compress_desc* cd;
+  const void* tail_k;          /* [Hkv][tail_cap][D] */
+  const void* tail_v;
+  int32_t tail_cap;
+  int32_t n_tail;              /* tail rows visible to the draft row (own row included) */
+} vc_attn_draft_req;
+
+/* Decode attention of one query row per request over its compressed main
+ * region (dequantized in registers, or the kept rows) followed by its tail
+ * rows, split-K partials merged in ascending split order. q: [n][Hq][D]. */
+vc_status vc_attn_draft(const vc_attn_desc* d, const vc_attn_draft_req* reqs, int32_t n, const void* q, void* out,
+                        void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Verification attention of n_rows rows per request: row i of request r sees
+ * staged rows [0, ctx) and tail rows 0..i.  Arrays have n entries. q:
+ * [n][n_rows][Hq][D]; staged_k/v: per request [Hkv][staged_cap][D];
+ * tail_k/v: per request [Hkv][tail_cap][D]; out like q. */
+vc_status vc_attn_verify(const vc_attn_desc* d, int32_t n, const void* q, const void* const* staged_k,
+                         const void* const* staged_v, int32_t staged_cap, const int32_t* ctx_host,
+                         const void* const* tail_k, const void* const* tail_v, int32_t tail_cap, int32_t n_rows,
+                         void* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+vc_status vc_attn_ws_size(const vc_attn_desc* d, int32_t n, int32_t rows, int32_t max_keys, size_t* bytes);
+
+/* ------------------------------------------------------------------------
+ * Seeded synthetic inputs (not part of the method): the counter-based
+ * SplitMix64 generator of the input recipe, evaluated on the GPU so that
+ * large workloads need not be generated on the host.  Counter
+ * c = stream*2^40 + seed*2^32 + index, u = (splitmix64(c) >> 40) * 2^-24.
+ * ---------------------------------------------------------------------- */
+/* dst[i] = round((2u(start+i) - 1) * sqrt(6/(fan_in+fan_out))), i < n, dtype VC_F32 or VC_BF16
+ * (float64 -> float32 -> bf16, each round-to-nearest-even). */
+vc_status vc_synth_xavier(void* dst, int32_t dtype, int64_t n, uint32_t stream, uint32_t seed, int64_t start,
+                          int32_t fan_in, int32_t fan_out, hipStream_t s);
+/* Box-Muller normals into bf16 [B][H][rows][D] (element index = counter index),
+ * columns outl[(b*H+h)*n_outl + k] of head (b, h) multiplied by outl_scale
+ * before rounding; outl may be NULL. */
+vc_status vc_synth_normal_heads(void* dst_bf16, int32_t B, int32_t H, int32_t rows, int32_t D, uint32_t stream,
+                                uint32_t seed, const int32_t* outl, int32_t n_outl, float outl_scale, hipStream_t s);
+vc_status vc_synth_ids(int32_t* dst, int64_t n, uint32_t stream, uint32_t seed, int32_t vocab, hipStream_t s);
+vc_status vc_synth_fill(void* dst, int32_t dtype, int64_t n, float value, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VC_H */

@@ -1,0 +1,203 @@
+"""Thin torch-facing wrappers over the C ABI (same names as include/vc.h).
+
+Each wrapper converts torch tensors to device pointers and the current torch
+stream to a hipStream_t, allocates outputs/workspaces with torch, and calls
+the library.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _vc
+from ._vc import (VC_BF16, VC_F32, VC_QUANT, VC_TOKDROP, AttnDesc, AttnDraftReq, CompressDesc, CompressLayout,
+                  ModelDesc, Req, Weights, call)
+
+__all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "CompressDesc", "Req", "Model", "compress_desc",
+           "compress_layout", "vc_compress", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
+           "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes"]
+
+
+def stream_handle(s: torch.cuda.Stream | None = None) -> int:
+    s = s or torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    return t.data_ptr()
+
+
+def torch_dtype(vc_dtype: int):
+    return torch.bfloat16 if vc_dtype == VC_BF16 else torch.float32
+
+
+def elem_bytes(vc_dtype: int) -> int:
+    return 2 if vc_dtype == VC_BF16 else 4
+
+
+# ---------------------------------------------------------------- compression
+def compress_desc(kind: int, n_layers: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
+                  dtype: int, src_cap: int | None = None, bits: int = 0, group: int = 0, keep_total: int = 0,
+                  keep_recent: int = 64, obs_window: int = 32) -> CompressDesc:
+    return CompressDesc(kind=kind, bits=bits, group=group, keep_total=keep_total, keep_recent=keep_recent,
+                        obs_window=obs_window, n_layers=n_layers, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                        head_dim=head_dim, seq_len=seq_len, dtype=dtype, src_cap=src_cap or seq_len)
+
+
+def compress_layout(d: CompressDesc) -> CompressLayout:
+    lay = CompressLayout()
+    call("vc_compress_layout_of", C.byref(d), C.byref(lay))
+    return lay
+
+
+def vc_compress(d: CompressDesc, k: torch.Tensor, v: torch.Tensor, q_obs: torch.Tensor | None = None,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    ob, wb = C.c_size_t(), C.c_size_t()
+    call("vc_compress_size", C.byref(d), C.byref(ob), C.byref(wb))
+    if out is None:
+        out = torch.zeros(ob.value, dtype=torch.uint8, device=k.device)
+    ws = torch.empty(max(wb.value, 256), dtype=torch.uint8, device=k.device)
+    call("vc_compress", C.byref(d), ptr(k), ptr(v), ptr(q_obs), ptr(out), out.numel(), ptr(ws), ws.numel(),
+         stream_handle())
+    return out
+
+
+# ---------------------------------------------------------------- single-layer attention
+def vc_attn_draft(d: AttnDesc, comps, cds, tails_k, tails_v, n_tail, q: torch.Tensor) -> torch.Tensor:
+    n = len(comps)
+    reqs = (AttnDraftReq * n)()
+    keep = []
+    for r in range(n):
+        cd = cds[r]
+        keep.append(cd)
+        tk, tv = tails_k[r], tails_v[r]
+        reqs[r] = AttnDraftReq(comp=ptr(comps[r]), cd=C.pointer(cd), tail_k=ptr(tk), tail_v=ptr(tv),
+                               tail_cap=tk.shape[-2] if tk is not None else 0, n_tail=n_tail[r])
+    out = torch.empty(q.shape, dtype=torch_dtype(d.out_dtype), device=q.device)
+    wb = C.c_size_t()
+    max_keys = max(compress_layout(cd).n_main + compress_layout(cd).n_resid for cd in cds) + max(n_tail) + 1
+    call("vc_attn_ws_size", C.byref(d), n, 1, max_keys, C.byref(wb))
+    ws = torch.empty(wb.value, dtype=torch.uint8, device=q.device)
+    call("vc_attn_draft", C.byref(d), reqs, n, ptr(q), ptr(out), ptr(ws), ws.numel(), stream_handle())
+    return out
+
+
+def vc_attn_verify(d: AttnDesc, q: torch.Tensor, staged_k, staged_v, ctx, tails_k, tails_v, n_rows: int,
+                   split_len: int = 0) -> torch.Tensor:
+    """q [n][n_rows][Hq][D]; staged_* lists of [Hkv][cap][D]; tails_* lists of [Hkv][tcap][D]."""
+    n = q.shape[0]
+    P = C.c_void_p * n
+    sk = P(*[ptr(t) for t in staged_k])
+    sv = P(*[ptr(t) for t in staged_v])
+    tk = P(*[ptr(t) for t in tails_k])
+    tv = P(*[ptr(t) for t in tails_v])
+    cx = (C.c_int32 * n)(*ctx)
+    out = torch.empty(q.shape, dtype=torch_dtype(d.out_dtype), device=q.device)
+    d2 = AttnDesc(d.n_q_heads, d.n_kv_heads, d.head_dim, d.dtype, split_len or d.split_len, d.out_dtype)
+    split = d2.split_len or 1024
+    S = -(-(max(ctx) + n_rows) // split)
+    nbytes = n * n_rows * d.n_q_heads * S * (d.head_dim + 2) * 4 + 256
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    call("vc_attn_verify", C.byref(d2), n, ptr(q), sk, sv, staged_k[0].shape[-2], cx, tk, tv, tails_k[0].shape[-2],
+         n_rows, ptr(out), ptr(ws), ws.numel(), stream_handle())
+    return out
+
+
+# ---------------------------------------------------------------- synthetic inputs (GPU generator)
+def synth_xavier(t: torch.Tensor, stream_id: int, fan_in: int, fan_out: int, seed: int = 0, start: int = 0):
+    dt = VC_BF16 if t.dtype == torch.bfloat16 else VC_F32
+    call("vc_synth_xavier", ptr(t), dt, t.numel(), stream_id, seed, start, fan_in, fan_out, stream_handle())
+    return t
+
+
+def synth_normal_heads(t: torch.Tensor, stream_id: int, outl: torch.Tensor | None = None, outl_scale: float = 10.0,
+                       seed: int = 0):
+    B, H, rows, D = t.shape
+    n_outl = outl.shape[-1] if outl is not None else 0
+    call("vc_synth_normal_heads", ptr(t), B, H, rows, D, stream_id, seed, ptr(outl), n_outl, outl_scale,
+         stream_handle())
+    return t
+
+
+def synth_ids(t: torch.Tensor, stream_id: int, vocab: int, seed: int = 0):
+    call("vc_synth_ids", ptr(t), t.numel(), stream_id, seed, vocab, stream_handle())
+    return t
+
+
+def synth_fill(t: torch.Tensor, value: float):
+    dt = VC_BF16 if t.dtype == torch.bfloat16 else VC_F32
+    call("vc_synth_fill", ptr(t), dt, t.numel(), value, stream_handle())
+    return t
+
+
+# ---------------------------------------------------------------- model
+class Model:
+    """A vc_model over caller-owned torch weight tensors (kept alive here)."""
+
+    def __init__(self, shape, weights: dict, max_pos: int):
+        s = shape
+        self.shape = s
+        self.dtype = VC_BF16 if s.dtype == "bf16" else VC_F32
+        self.eb = elem_bytes(self.dtype)
+        self.w = weights
+        self.desc = ModelDesc(s.n_layers, s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab,
+                              self.dtype, s.rope_theta, s.eps, max_pos)
+        self.cw = Weights(*[ptr(weights[k]) for k in ("embed", "lm_head", "norm_final", "norm_attn", "norm_ffn",
+                                                      "w_qkv", "w_o", "w_gu", "w_down")])
+        h = C.c_void_p()
+        call("vc_model_create", C.byref(self.desc), C.byref(self.cw), stream_handle(), C.byref(h))
+        self.h = h
+
+    def close(self):
+        if self.h:
+            call("vc_model_destroy", self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def ws_size(self, max_rows: int, max_keys: int) -> int:
+        b = C.c_size_t()
+        call("vc_ws_size", self.h, max_rows, max_keys, C.byref(b))
+        return b.value
+
+    def workspace(self, max_rows: int, max_keys: int, device="cuda") -> torch.Tensor:
+        return torch.empty(self.ws_size(max_rows, max_keys), dtype=torch.uint8, device=device)
+
+    def prefill(self, tokens: torch.Tensor, k_out, v_out, q_obs, W: int, g0: torch.Tensor, ws: torch.Tensor,
+                chunk: int):
+        call("vc_prefill", self.h, ptr(tokens), tokens.numel(), ptr(k_out), ptr(v_out), k_out.shape[-2],
+             ptr(q_obs), W, ptr(g0), chunk, ptr(ws), ws.numel(), stream_handle())
+
+    def draft_step(self, reqs, in_tok: torch.Tensor, out_tok: torch.Tensor, ws: torch.Tensor, logits=None):
+        n = len(reqs)
+        arr = (Req * n)(*reqs)
+        call("vc_draft_step", self.h, arr, n, ptr(in_tok), ptr(out_tok), ptr(logits), ptr(ws), ws.numel(),
+             stream_handle())
+
+    def verify(self, req: Req, staged_k, staged_v, tok: torch.Tensor, n_rows: int, out: torch.Tensor, vtail_k,
+               vtail_v, ws: torch.Tensor, logits=None):
+        scap = staged_k.shape[-2] if staged_k is not None else 0
+        call("vc_verify", self.h, C.byref(req), ptr(staged_k), ptr(staged_v), scap, ptr(tok), n_rows, ptr(out),
+             ptr(logits), ptr(vtail_k), ptr(vtail_v), vtail_k.shape[-2], ptr(ws), ws.numel(), stream_handle())
+
+    def accept(self, req: Req, draft, verified, x: int, vtail_k, vtail_v, result: torch.Tensor):
+        call("vc_accept", self.h, C.byref(req), ptr(draft), ptr(verified), x, ptr(vtail_k), ptr(vtail_v),
+             vtail_k.shape[-2], ptr(result), stream_handle())
+
+    def commit(self, req: Req, a: int, vtail_k, vtail_v, after_event=None, copy_stream=None):
+        ev = after_event.cuda_event if after_event is not None else None
+        call("vc_commit", self.h, C.byref(req), a, ptr(vtail_k), ptr(vtail_v), vtail_k.shape[-2], ev,
+             stream_handle(copy_stream))
+
+    def stage(self, req: Req, slot_k, slot_v, l0: int, l1: int, copy_stream=None):
+        call("vc_stage", self.h, C.byref(req), ptr(slot_k), ptr(slot_v), slot_k.shape[-2], l0, l1,
+             stream_handle(copy_stream))

@@ -1,0 +1,770 @@
+// C ABI of the VeriCache hot path: model forward for drafting and
+// verification, accept / commit, full-KV staging, prefill, compression and
+// the single-layer attention entry points.  See include/vc.h for contracts.
+#include <algorithm>
+#include <cstdarg>
+#include <cstring>
+#include <functional>
+
+#include "attention.h"
+#include "compress.h"
+#include "elementwise.h"
+#include "gemm.h"
+
+namespace vc {
+
+static thread_local std::string g_err;
+
+void set_error(const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+struct vc_model {
+  vc_model_desc d;
+  vc_weights w;
+  float* rope;  // [max_pos][D/2][2]
+  int eb;       // bytes per activation / weight element
+};
+
+namespace {
+
+constexpr int SPLIT_VERIFY = 1024;
+constexpr int SPLIT_DRAFT = 512;
+constexpr int SPLIT_QUANT = 1024;
+
+inline const uint8_t* cptr(const void* p, int64_t off) { return static_cast<const uint8_t*>(p) + off; }
+inline uint8_t* mptr(void* p, int64_t off) { return static_cast<uint8_t*>(p) + off; }
+
+struct WsLayout {
+  size_t h, a, q, o, m, y, att, tok, total;
+};
+
+int64_t n_qkv(const vc_model_desc& d) { return int64_t(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim; }
+
+size_t gemm_part_bytes(const vc_model_desc& d, int R) {
+  const int dt = d.dtype;
+  const int64_t Ns[5] = {n_qkv(d), d.d_model, 2 * int64_t(d.ffn), d.d_model, d.vocab};
+  const int64_t Ks[5] = {d.d_model, int64_t(d.n_q_heads) * d.head_dim, d.d_model, d.ffn, d.d_model};
+  size_t best = 0;
+  for (int i = 0; i < 5; i++) {
+    const int rs = std::min(R, 64);
+    const int S = i == 4 ? 1 : gemm_splits(rs, int(Ns[i]), int(Ks[i]), dt);
+    best = std::max(best, size_t(S) * rs * Ns[i] * 4);
+    best = std::max(best, size_t(R) * Ns[i] * 4);
+  }
+  return best;
+}
+
+size_t att_part_bytes(const vc_model_desc& d, int R, int max_keys) {
+  const int64_t D2 = d.head_dim + 2;
+  const int64_t draft = int64_t(VC_MAX_BATCH) * d.n_q_heads * (cdiv(max_keys, SPLIT_DRAFT) + cdiv(max_keys, SPLIT_QUANT) + 2) * D2 * 4;
+  const int64_t verify = int64_t(R) * d.n_q_heads * (cdiv(max_keys, SPLIT_VERIFY) + 1) * D2 * 4;
+  return size_t(std::max(draft, verify));
+}
+
+WsLayout ws_layout(const vc_model* m, int R, int max_keys) {
+  const vc_model_desc& d = m->d;
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off = align256(off + b);
+    return o;
+  };
+  const int Rr = std::max(R, VC_MAX_BATCH);
+  L.h = take(size_t(Rr) * d.d_model * m->eb);
+  L.a = take(size_t(Rr) * d.d_model * m->eb);
+  L.q = take(size_t(Rr) * d.n_q_heads * d.head_dim * m->eb);
+  L.o = take(size_t(Rr) * d.n_q_heads * d.head_dim * m->eb);
+  L.m = take(size_t(Rr) * d.ffn * m->eb);
+  L.y = take(gemm_part_bytes(d, Rr));
+  L.att = take(att_part_bytes(d, Rr, max_keys));
+  L.tok = take(size_t(Rr) * 4 * 2);
+  L.total = off;
+  return L;
+}
+
+// One projection + epilogue.
+vc_status proj(const vc_model* m, const void* X, const void* W, int M, int N, int K, float* P, EpiArgs e,
+               hipStream_t s) {
+  const int S = gemm_splits(M, N, K, m->d.dtype);
+  vc_status st = gemm(X, W, P, M, N, K, S, m->d.dtype, s);
+  if (st) return st;
+  e.P = P;
+  e.M = M;
+  e.N = N;
+  e.S = S;
+  e.dtype = m->d.dtype;
+  return epilogue(e, s);
+}
+
+struct LayerPtrs {
+  const uint8_t *wqkv, *wo, *wgu, *wdown, *g1, *g2;
+};
+LayerPtrs layer_ptrs(const vc_model* m, int l) {
+  const vc_model_desc& d = m->d;
+  const int64_t eb = m->eb;
+  const int64_t dm = d.d_model, hd = int64_t(d.n_q_heads) * d.head_dim;
+  LayerPtrs p;
+  p.wqkv = cptr(m->w.w_qkv, l * n_qkv(d) * dm * eb);
+  p.wo = cptr(m->w.w_o, l * dm * hd * eb);
+  p.wgu = cptr(m->w.w_gu, l * 2 * int64_t(d.ffn) * dm * eb);
+  p.wdown = cptr(m->w.w_down, l * dm * d.ffn * eb);
+  p.g1 = cptr(m->w.norm_attn, l * dm * eb);
+  p.g2 = cptr(m->w.norm_ffn, l * dm * eb);
+  return p;
+}
+
+// Shared transformer forward over M rows already embedded in ws.h.
+vc_status forward_layers(const vc_model* m, int M, uint8_t* ws, const WsLayout& L, EpiArgs qkv_tmpl,
+                         const std::function<vc_status(int, EpiArgs&)>& set_kv,
+                         const std::function<vc_status(int, const void*, void*, float*)>& attend, hipStream_t s) {
+  const vc_model_desc& d = m->d;
+  float* P = reinterpret_cast<float*>(ws + L.y);
+  void* h = ws + L.h;
+  void* a = ws + L.a;
+  void* q = ws + L.q;
+  void* o = ws + L.o;
+  void* mb = ws + L.m;
+  const int hd = d.n_q_heads * d.head_dim;
+  vc_status st;
+  for (int l = 0; l < d.n_layers; l++) {
+    const LayerPtrs lp = layer_ptrs(m, l);
+    if ((st = k_rmsnorm(h, lp.g1, a, M, d.d_model, d.eps, d.dtype, s))) return st;
+    EpiArgs e = qkv_tmpl;
+    e.mode = EPI_QKV;
+    e.q_out = q;
+    e.rope = m->rope;
+    e.Hq = d.n_q_heads;
+    e.Hkv = d.n_kv_heads;
+    e.D = d.head_dim;
+    if ((st = set_kv(l, e))) return st;
+    if ((st = proj(m, a, lp.wqkv, M, int(n_qkv(d)), d.d_model, P, e, s))) return st;
+    if ((st = attend(l, q, o, reinterpret_cast<float*>(ws + L.att)))) return st;
+    EpiArgs r{};
+    r.mode = EPI_RESID;
+    r.out = h;
+    if ((st = proj(m, o, lp.wo, M, d.d_model, hd, P, r, s))) return st;
+    if ((st = k_rmsnorm(h, lp.g2, a, M, d.d_model, d.eps, d.dtype, s))) return st;
+    EpiArgs g{};
+    g.mode = EPI_SWIGLU;
+    g.out = mb;
+    if ((st = proj(m, a, lp.wgu, M, 2 * d.ffn, d.d_model, P, g, s))) return st;
+    EpiArgs r2{};
+    r2.mode = EPI_RESID;
+    r2.out = h;
+    if ((st = proj(m, mb, lp.wdown, M, d.d_model, d.ffn, P, r2, s))) return st;
+  }
+  return VC_OK;
+}
+
+// Final norm + LM head + argmax of rows [r0, r0 + M) of ws.h.
+vc_status head(const vc_model* m, int r0, int M, uint8_t* ws, const WsLayout& L, int32_t* out_tok, float* logits_opt,
+               hipStream_t s) {
+  const vc_model_desc& d = m->d;
+  vc_status st;
+  const void* hrow = ws + L.h + size_t(r0) * d.d_model * m->eb;
+  void* a = ws + L.a;
+  float* P = reinterpret_cast<float*>(ws + L.y);
+  if ((st = k_rmsnorm(hrow, m->w.norm_final, a, M, d.d_model, d.eps, d.dtype, s))) return st;
+  if ((st = gemm(a, m->w.lm_head, P, M, d.vocab, d.d_model, 1, d.dtype, s))) return st;
+  if ((st = k_argmax(P, M, d.vocab, out_tok, s))) return st;
+  if (logits_opt) VC_HIP(hipMemcpyAsync(logits_opt, P, size_t(M) * d.vocab * 4, hipMemcpyDeviceToDevice, s));
+  return VC_OK;
+}
+
+vc_status check_model(const vc_model* m) {
+  VC_REQUIRE(m != nullptr, VC_ERR_ARG, "null model");
+  return VC_OK;
+}
+
+// Per-layer views into a compressed blob of L layers.
+struct CompView {
+  vc_compress_layout lay;
+  int kind, bits, group, tq, kk, n_resid, Hkv, D, eb;
+  const uint8_t* base;
+  KVSeg main_bf16(int l) const {  // token drop: kept rows
+    const int64_t per = int64_t(Hkv) * kk * D * eb;
+    return KVSeg{base + lay.k_main + l * per, base + lay.v_main + l * per, int64_t(kk) * D, kk, 0};
+  }
+  KVSeg resid(int l) const {
+    const int64_t per = int64_t(Hkv) * n_resid * D * eb;
+    return KVSeg{base + lay.kr + l * per, base + lay.vr + l * per, int64_t(n_resid) * D, n_resid, 0};
+  }
+  QuantSeg quant(int l) const {
+    const int64_t ng = tq / group, nh = D / group;
+    QuantSeg q;
+    q.kc = base + lay.kc + l * int64_t(Hkv) * tq * D * bits / 8;
+    q.vc = base + lay.vc + l * int64_t(Hkv) * tq * D * bits / 8;
+    q.ks = reinterpret_cast<const uint16_t*>(base + lay.ks + l * int64_t(Hkv) * ng * D * 2);
+    q.kz = reinterpret_cast<const uint16_t*>(base + lay.kz + l * int64_t(Hkv) * ng * D * 2);
+    q.vs = reinterpret_cast<const uint16_t*>(base + lay.vs + l * int64_t(Hkv) * tq * nh * 2);
+    q.vz = reinterpret_cast<const uint16_t*>(base + lay.vz + l * int64_t(Hkv) * tq * nh * 2);
+    q.tq = tq;
+    q.pad_ = 0;
+    return q;
+  }
+};
+
+vc_status comp_view(const void* comp, const vc_compress_desc* cd, CompView& v) {
+  VC_REQUIRE(comp != nullptr && cd != nullptr, VC_ERR_ARG, "request without compressed cache");
+  vc_status st = compress_layout(cd, &v.lay);
+  if (st) return st;
+  v.kind = cd->kind;
+  v.bits = cd->bits;
+  v.group = cd->group;
+  v.tq = cd->kind == VC_QUANT ? v.lay.n_main : 0;
+  v.kk = cd->kind == VC_TOKDROP ? v.lay.n_main : 0;
+  v.n_resid = v.lay.n_resid;
+  v.Hkv = cd->n_kv_heads;
+  v.D = cd->head_dim;
+  v.eb = cd->dtype == VC_BF16 ? 2 : 4;
+  v.base = static_cast<const uint8_t*>(comp);
+  return VC_OK;
+}
+
+// Draft attention for a batch of requests over (compressed main region, exact tail), one layer.
+// tail_n[r]: visible tail rows (own row included).
+vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int n, const CompView* views, int l,
+                          const KVSeg* tails, const int* tail_n, const void* q, int64_t q_req_stride_bytes, void* o,
+                          int64_t o_req_stride_bytes, float* part, hipStream_t s) {
+  const int G = Hq / Hkv;
+  const float sl2 = LOG2E / sqrtf(float(D));
+  int s_tot = 0;
+  int qs_n[VC_MAX_BATCH], ts_n[VC_MAX_BATCH];
+  for (int r = 0; r < n; r++) {
+    const CompView& v = views[r];
+    if (v.kind == VC_QUANT) {
+      qs_n[r] = int(cdiv(v.tq, SPLIT_QUANT));
+      ts_n[r] = int(cdiv(v.n_resid + tail_n[r], SPLIT_DRAFT));
+    } else {
+      qs_n[r] = 0;
+      ts_n[r] = int(cdiv(v.kk + tail_n[r], SPLIT_DRAFT));
+    }
+    s_tot = std::max(s_tot, qs_n[r] + ts_n[r]);
+  }
+  const int64_t per_req = int64_t(Hq) * s_tot * (D + 2);
+  QuantArgs qa{};
+  qa.n_req = 0;
+  AttnArgs aa{};
+  aa.n_req = n;
+  aa.Hq = Hq;
+  aa.Hkv = Hkv;
+  aa.G = G;
+  aa.split_len = SPLIT_DRAFT;
+  aa.head_dim = D;
+  aa.scale_log2 = sl2;
+  aa.n_rowblocks = 1;
+  aa.max_splits = 0;
+  int q_bits = 0, q_group = 0;
+  for (int r = 0; r < n; r++) {
+    const CompView& v = views[r];
+    AttnReq& ar = aa.r[r];
+    ar.q = cptr(q, r * q_req_stride_bytes);
+    ar.part = part + r * per_req;
+    ar.n_rows = 1;
+    ar.s_total = s_tot;
+    if (v.kind == VC_QUANT) {
+      VC_REQUIRE(q_bits == 0 || (q_bits == v.bits && q_group == v.group), VC_ERR_UNSUPPORTED,
+                 "one draft batch must share the quantizer settings");
+      q_bits = v.bits;
+      q_group = v.group;
+      QuantReq& qr = qa.r[qa.n_req++];
+      qr.q = ar.q;
+      qr.m = v.quant(l);
+      qr.part = ar.part;
+      qr.s_total = s_tot;
+      qr.n_splits = qs_n[r];
+      qa.max_splits = std::max(qa.max_splits, qs_n[r]);
+      ar.a = v.resid(l);
+      ar.b = tails[r];
+      ar.b.n = tail_n[r];
+      ar.lim0 = v.n_resid + tail_n[r] - 1;
+      ar.s_off = qs_n[r];
+    } else {
+      ar.a = v.main_bf16(l);
+      ar.b = tails[r];
+      ar.b.n = tail_n[r];
+      ar.lim0 = v.kk + tail_n[r] - 1;
+      ar.s_off = 0;
+    }
+    ar.n_splits = ts_n[r];
+    aa.max_splits = std::max(aa.max_splits, ts_n[r]);
+  }
+  vc_status st;
+  if (qa.n_req > 0) {
+    qa.Hq = Hq;
+    qa.Hkv = Hkv;
+    qa.G = G;
+    qa.bits = q_bits;
+    qa.group = q_group;
+    qa.split_len = SPLIT_QUANT;
+    qa.scale_log2 = sl2;
+    VC_REQUIRE(D == 128 && dtype == VC_BF16, VC_ERR_UNSUPPORTED, "quantized draft needs bf16, head_dim 128");
+    if ((st = launch_attn_quant(qa, s))) return st;
+  }
+  if ((st = launch_attn(aa, dtype, s))) return st;
+  CombineArgs c{};
+  c.n_req = n;
+  c.n_rows = 1;
+  c.Hq = Hq;
+  c.s_total = s_tot;
+  c.head_dim = D;
+  c.out_dtype = out_dtype;
+  for (int r = 0; r < n; r++) {
+    c.part[r] = part + r * per_req;
+    c.out[r] = mptr(o, r * o_req_stride_bytes);
+    c.s_used[r] = qs_n[r] + ts_n[r];
+  }
+  return launch_combine(c, s);
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+extern "C" {
+
+const char* vc_last_error(void) { return g_err.c_str(); }
+int32_t vc_abi_version(void) { return 1; }
+
+vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStream_t s, vc_model** out) {
+  VC_REQUIRE(desc && w && out, VC_ERR_ARG, "vc_model_create: null argument");
+  const vc_model_desc& d = *desc;
+  VC_REQUIRE(d.n_layers > 0 && d.d_model > 0 && d.n_q_heads > 0 && d.n_kv_heads > 0 && d.ffn > 0 && d.vocab > 0 &&
+                 d.max_pos > 0 && d.n_q_heads % d.n_kv_heads == 0,
+             VC_ERR_ARG, "vc_model_create: bad shape");
+  VC_REQUIRE((d.dtype == VC_BF16 && d.head_dim == 128) || (d.dtype == VC_F32 && d.head_dim == 64),
+             VC_ERR_UNSUPPORTED, "vc_model_create: supported are bf16 with head_dim 128 and fp32 with head_dim 64");
+  VC_REQUIRE(d.n_q_heads * d.head_dim == d.d_model, VC_ERR_UNSUPPORTED, "vc_model_create: Hq * D must equal d_model");
+  VC_REQUIRE(d.n_q_heads / d.n_kv_heads <= 16, VC_ERR_UNSUPPORTED, "vc_model_create: GQA group > 16");
+  VC_REQUIRE(w->embed && w->lm_head && w->norm_final && w->norm_attn && w->norm_ffn && w->w_qkv && w->w_o && w->w_gu &&
+                 w->w_down,
+             VC_ERR_ARG, "vc_model_create: null weight pointer");
+  if (d.dtype == VC_BF16) {
+    VC_REQUIRE(d.d_model % 128 == 0 && d.ffn % 128 == 0 && d.vocab % 128 == 0, VC_ERR_UNSUPPORTED,
+               "vc_model_create: bf16 path needs d_model, ffn, vocab multiples of 128");
+  }
+  vc_model* m = new vc_model();
+  m->d = d;
+  m->w = *w;
+  m->eb = d.dtype == VC_BF16 ? 2 : 4;
+  hipError_t e = hipMalloc(&m->rope, size_t(d.max_pos) * d.head_dim * 4);
+  if (e != hipSuccess) {
+    delete m;
+    set_error("vc_model_create: hipMalloc of the RoPE table failed: %s", hipGetErrorString(e));
+    return VC_ERR_HIP;
+  }
+  vc_status st = k_rope_table(m->rope, d.max_pos, d.head_dim, double(d.rope_theta), s);
+  if (st == VC_OK && hipStreamSynchronize(s) != hipSuccess) st = VC_ERR_HIP;
+  if (st) {
+    hipFree(m->rope);
+    delete m;
+    return st;
+  }
+  *out = m;
+  return VC_OK;
+}
+
+vc_status vc_model_destroy(vc_model* m) {
+  if (!m) return VC_OK;
+  hipFree(m->rope);
+  delete m;
+  return VC_OK;
+}
+
+vc_status vc_ws_size(const vc_model* m, int32_t max_rows, int32_t max_keys, size_t* bytes) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(bytes && max_rows > 0 && max_keys > 0, VC_ERR_ARG, "vc_ws_size: bad arguments");
+  *bytes = ws_layout(m, max_rows, max_keys).total;
+  return VC_OK;
+}
+
+vc_status vc_compress_layout_of(const vc_compress_desc* d, vc_compress_layout* out) { return compress_layout(d, out); }
+
+vc_status vc_compress_size(const vc_compress_desc* d, size_t* out_bytes, size_t* ws_bytes) {
+  VC_REQUIRE(out_bytes && ws_bytes, VC_ERR_ARG, "vc_compress_size: null output");
+  vc_compress_layout L;
+  if (vc_status st = compress_layout(d, &L)) return st;
+  *out_bytes = L.total;
+  return compress_ws_bytes(d, ws_bytes);
+}
+
+vc_status vc_compress(const vc_compress_desc* d, const void* k, const void* v, const void* q_obs, void* out,
+                      size_t out_bytes, void* ws, size_t ws_bytes, hipStream_t s) {
+  return compress_run(d, k, v, q_obs, out, out_bytes, ws, ws_bytes, s);
+}
+
+vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, const int32_t* in_tok, int32_t* out_tok,
+                        float* logits_opt, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(reqs && in_tok && out_tok && ws, VC_ERR_ARG, "vc_draft_step: null argument");
+  VC_REQUIRE(n > 0 && n <= VC_MAX_BATCH, VC_ERR_ARG, "vc_draft_step: batch %d not in [1, %d]", n, VC_MAX_BATCH);
+  const vc_model_desc& d = m->d;
+  int max_keys = 1;
+  CompView views[VC_MAX_BATCH];
+  KVSeg tails_k[VC_MAX_BATCH];
+  int tail_n[VC_MAX_BATCH];
+  for (int r = 0; r < n; r++) {
+    const vc_req& q = reqs[r];
+    if (vc_status st = comp_view(q.comp, q.cd, views[r])) return st;
+    VC_REQUIRE(q.cd->n_layers == d.n_layers && q.cd->n_kv_heads == d.n_kv_heads && q.cd->head_dim == d.head_dim &&
+                   q.cd->dtype == d.dtype,
+               VC_ERR_ARG, "vc_draft_step: request %d compressed with another shape", r);
+    VC_REQUIRE(q.tail_k && q.tail_v && q.draft_idx >= 0 && q.n_tail >= 0, VC_ERR_ARG, "vc_draft_step: bad request %d",
+               r);
+    VC_REQUIRE(q.n_tail + q.draft_idx < q.tail_cap, VC_ERR_CAPACITY, "vc_draft_step: tail of request %d is full", r);
+    VC_REQUIRE(q.ctx_len + q.draft_idx < d.max_pos, VC_ERR_CAPACITY, "vc_draft_step: position beyond the RoPE table");
+    tail_n[r] = q.n_tail + q.draft_idx + 1;
+    max_keys = std::max(max_keys, views[r].lay.n_main + views[r].n_resid + tail_n[r]);
+  }
+  const WsLayout L = ws_layout(m, n, max_keys);
+  VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_draft_step: workspace %zu < %zu bytes", ws_bytes, L.total);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  vc_status st;
+  if ((st = k_embed(m->w.embed, in_tok, w8 + L.h, n, d.d_model, d.dtype, s))) return st;
+  EpiArgs tmpl{};
+  tmpl.batched = 1;
+  for (int r = 0; r < n; r++) tmpl.pos[r] = reqs[r].ctx_len + reqs[r].draft_idx;
+  auto set_kv = [&](int l, EpiArgs& e) -> vc_status {
+    for (int r = 0; r < n; r++) {
+      const vc_req& q = reqs[r];
+      const int64_t off = (int64_t(l) * d.n_kv_heads * q.tail_cap + q.n_tail + q.draft_idx) * d.head_dim * m->eb;
+      e.krow[r] = mptr(q.tail_k, off);
+      e.vrow[r] = mptr(q.tail_v, off);
+      e.rpitch[r] = q.tail_cap;
+    }
+    return VC_OK;
+  };
+  auto attend = [&](int l, const void* qb, void* ob, float* part) -> vc_status {
+    for (int r = 0; r < n; r++) {
+      const vc_req& q = reqs[r];
+      const int64_t lo = int64_t(l) * d.n_kv_heads * q.tail_cap * d.head_dim * m->eb;
+      tails_k[r] = KVSeg{cptr(q.tail_k, lo), cptr(q.tail_v, lo), int64_t(q.tail_cap) * d.head_dim, 0, 0};
+    }
+    const int64_t qstride = int64_t(d.n_q_heads) * d.head_dim * m->eb;
+    return draft_attention(d.n_q_heads, d.n_kv_heads, d.head_dim, d.dtype, d.dtype, n, views, l, tails_k, tail_n, qb,
+                           qstride, ob, qstride, part, s);
+  };
+  if ((st = forward_layers(m, n, w8, L, tmpl, set_kv, attend, s))) return st;
+  return head(m, 0, n, w8, L, out_tok, logits_opt, s);
+}
+
+vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v, int32_t staged_cap,
+                    const int32_t* tok, int32_t n_rows, int32_t* out_argmax, float* logits_opt, void* vtail_k,
+                    void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(req && tok && out_argmax && vtail_k && vtail_v && ws, VC_ERR_ARG, "vc_verify: null argument");
+  VC_REQUIRE(n_rows > 0 && n_rows <= 64, VC_ERR_ARG, "vc_verify: n_rows %d not in [1, 64]", n_rows);
+  VC_REQUIRE(vtail_cap >= n_rows, VC_ERR_CAPACITY, "vc_verify: vtail capacity %d < %d rows", vtail_cap, n_rows);
+  const vc_model_desc& d = m->d;
+  const int ctx = req->ctx_len;
+  VC_REQUIRE(ctx >= 0 && (ctx == 0 || (staged_k && staged_v && staged_cap >= ctx)), VC_ERR_ARG,
+             "vc_verify: staged cache smaller than ctx_len");
+  VC_REQUIRE(ctx + n_rows <= d.max_pos, VC_ERR_CAPACITY, "vc_verify: position beyond the RoPE table");
+  const WsLayout L = ws_layout(m, n_rows, ctx + n_rows);
+  VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_verify: workspace %zu < %zu bytes", ws_bytes, L.total);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  vc_status st;
+  if ((st = k_embed(m->w.embed, tok, w8 + L.h, n_rows, d.d_model, d.dtype, s))) return st;
+  EpiArgs tmpl{};
+  tmpl.batched = 0;
+  tmpl.pos0 = ctx;
+  tmpl.row0 = 0;
+  tmpl.pitch = vtail_cap;
+  const int64_t Hkv = d.n_kv_heads, D = d.head_dim, eb = m->eb;
+  auto set_kv = [&](int l, EpiArgs& e) -> vc_status {
+    e.kbase = mptr(vtail_k, l * Hkv * vtail_cap * D * eb);
+    e.vbase = mptr(vtail_v, l * Hkv * vtail_cap * D * eb);
+    return VC_OK;
+  };
+  auto attend = [&](int l, const void* qb, void* ob, float* part) -> vc_status {
+    AttnArgs a{};
+    a.n_req = 1;
+    a.Hq = d.n_q_heads;
+    a.Hkv = d.n_kv_heads;
+    a.G = d.n_q_heads / d.n_kv_heads;
+    a.split_len = SPLIT_VERIFY;
+    a.head_dim = d.head_dim;
+    a.scale_log2 = LOG2E / sqrtf(float(D));
+    a.n_rowblocks = int(cdiv(int64_t(n_rows) * a.G, ATT_RB));
+    const int S = int(cdiv(ctx + n_rows, SPLIT_VERIFY));
+    a.max_splits = S;
+    AttnReq& r = a.r[0];
+    r.q = qb;
+    r.a = KVSeg{ctx ? cptr(staged_k, l * Hkv * staged_cap * D * eb) : nullptr,
+                ctx ? cptr(staged_v, l * Hkv * staged_cap * D * eb) : nullptr, int64_t(staged_cap) * D, ctx, 0};
+    r.b = KVSeg{cptr(vtail_k, l * Hkv * vtail_cap * D * eb), cptr(vtail_v, l * Hkv * vtail_cap * D * eb),
+                int64_t(vtail_cap) * D, n_rows, 0};
+    r.part = part;
+    r.n_rows = n_rows;
+    r.lim0 = ctx;
+    r.s_off = 0;
+    r.s_total = S;
+    r.n_splits = S;
+    vc_status st2 = launch_attn(a, d.dtype, s);
+    if (st2) return st2;
+    CombineArgs c{};
+    c.n_req = 1;
+    c.n_rows = n_rows;
+    c.Hq = d.n_q_heads;
+    c.s_total = S;
+    c.head_dim = d.head_dim;
+    c.out_dtype = d.dtype;
+    c.part[0] = part;
+    c.out[0] = ob;
+    c.s_used[0] = S;
+    return launch_combine(c, s);
+  };
+  if ((st = forward_layers(m, n_rows, w8, L, tmpl, set_kv, attend, s))) return st;
+  return head(m, 0, n_rows, w8, L, out_argmax, logits_opt, s);
+}
+
+vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out, void* v_out, int32_t cap, void* q_obs,
+                     int32_t W, int32_t* g0_out, int32_t chunk, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(tokens && k_out && v_out && g0_out && ws, VC_ERR_ARG, "vc_prefill: null argument");
+  VC_REQUIRE(T > 0 && cap >= T && chunk > 0, VC_ERR_ARG, "vc_prefill: bad sizes");
+  VC_REQUIRE(T <= m->d.max_pos, VC_ERR_CAPACITY, "vc_prefill: prompt beyond the RoPE table");
+  VC_REQUIRE(q_obs == nullptr || (W > 0 && W <= T), VC_ERR_ARG, "vc_prefill: bad observation window");
+  const vc_model_desc& d = m->d;
+  const WsLayout L = ws_layout(m, chunk, T);
+  VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_prefill: workspace %zu < %zu bytes", ws_bytes, L.total);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  const int64_t Hkv = d.n_kv_heads, D = d.head_dim, eb = m->eb;
+  const int64_t qrow = int64_t(d.n_q_heads) * D * eb;
+  vc_status st;
+  for (int c0 = 0; c0 < T; c0 += chunk) {
+    const int C = std::min(chunk, T - c0);
+    if ((st = k_embed(m->w.embed, tokens + c0, w8 + L.h, C, d.d_model, d.dtype, s))) return st;
+    EpiArgs tmpl{};
+    tmpl.batched = 0;
+    tmpl.pos0 = c0;
+    tmpl.row0 = c0;
+    tmpl.pitch = cap;
+    auto set_kv = [&](int l, EpiArgs& e) -> vc_status {
+      e.kbase = mptr(k_out, l * Hkv * cap * D * eb);
+      e.vbase = mptr(v_out, l * Hkv * cap * D * eb);
+      return VC_OK;
+    };
+    auto attend = [&](int l, const void* qb, void* ob, float* part) -> vc_status {
+      if (q_obs && c0 + C > T - W) {  // keep the observation queries of the last W prompt rows
+        const int r_lo = std::max(c0, T - W);
+        const int64_t bytes = int64_t(c0 + C - r_lo) * qrow;
+        vc_status st3 = k_copy_words(cptr(qb, int64_t(r_lo - c0) * qrow),
+                                     mptr(q_obs, (int64_t(l) * W + (r_lo - (T - W))) * qrow), bytes, s);
+        if (st3) return st3;
+      }
+      AttnArgs a{};
+      a.n_req = 1;
+      a.Hq = d.n_q_heads;
+      a.Hkv = d.n_kv_heads;
+      a.G = d.n_q_heads / d.n_kv_heads;
+      a.split_len = int(cdiv(c0 + C, ATT_KT) * ATT_KT);
+      a.head_dim = d.head_dim;
+      a.scale_log2 = LOG2E / sqrtf(float(D));
+      a.n_rowblocks = int(cdiv(int64_t(C) * a.G, ATT_RB));
+      a.max_splits = 1;
+      AttnReq& r = a.r[0];
+      r.q = qb;
+      r.a = KVSeg{cptr(k_out, l * Hkv * cap * D * eb), cptr(v_out, l * Hkv * cap * D * eb), int64_t(cap) * D, c0 + C,
+                  0};
+      r.b = KVSeg{nullptr, nullptr, 0, 0, 0};
+      r.part = part;
+      r.n_rows = C;
+      r.lim0 = c0;
+      r.s_off = 0;
+      r.s_total = 1;
+      r.n_splits = 1;
+      vc_status st2 = launch_attn(a, d.dtype, s);
+      if (st2) return st2;
+      CombineArgs c{};
+      c.n_req = 1;
+      c.n_rows = C;
+      c.Hq = d.n_q_heads;
+      c.s_total = 1;
+      c.head_dim = d.head_dim;
+      c.out_dtype = d.dtype;
+      c.part[0] = part;
+      c.out[0] = ob;
+      c.s_used[0] = 1;
+      return launch_combine(c, s);
+    };
+    if ((st = forward_layers(m, C, w8, L, tmpl, set_kv, attend, s))) return st;
+    if (c0 + C == T) {
+      if ((st = head(m, C - 1, 1, w8, L, g0_out, nullptr, s))) return st;
+    }
+  }
+  return VC_OK;
+}
+
+vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* draft, const int32_t* verified, int32_t x,
+                    const void* vtail_k, const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(req && draft && verified && vtail_k && vtail_v && result, VC_ERR_ARG, "vc_accept: null argument");
+  VC_REQUIRE(x >= 1 && vtail_cap >= x + 1, VC_ERR_ARG, "vc_accept: bad draft length %d", x);
+  VC_REQUIRE(req->tail_k && req->tail_v, VC_ERR_ARG, "vc_accept: request without tail");
+  VC_REQUIRE(req->n_tail + x + 1 <= req->tail_cap, VC_ERR_CAPACITY, "vc_accept: tail capacity");
+  const vc_model_desc& d = m->d;
+  vc_status st;
+  if ((st = k_accept(draft, verified, x, result, s))) return st;
+  return k_commit_rows(vtail_k, vtail_v, vtail_cap, req->tail_k, req->tail_v, req->tail_cap, req->n_tail,
+                       d.head_dim * m->eb, d.n_layers * d.n_kv_heads, x + 1, result, s);
+}
+
+vc_status vc_commit(vc_model* m, vc_req* req, int32_t a, const void* vtail_k, const void* vtail_v, int32_t vtail_cap,
+                    hipEvent_t after, hipStream_t copy) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(req && vtail_k && vtail_v, VC_ERR_ARG, "vc_commit: null argument");
+  VC_REQUIRE(a >= 0 && a + 1 <= vtail_cap, VC_ERR_ARG, "vc_commit: bad accept count %d", a);
+  VC_REQUIRE(req->ctx_len + a + 1 <= req->full_cap, VC_ERR_CAPACITY, "vc_commit: full KV capacity");
+  VC_REQUIRE(req->n_tail + a + 1 <= req->tail_cap, VC_ERR_CAPACITY, "vc_commit: tail capacity");
+  const vc_model_desc& d = m->d;
+  const size_t row = size_t(d.head_dim) * m->eb;
+  if (after) VC_HIP(hipStreamWaitEvent(copy, after, 0));
+  if (req->full_k_host && req->full_v_host) {
+    VC_HIP(hipMemcpy2DAsync(mptr(req->full_k_host, int64_t(req->ctx_len) * row), size_t(req->full_cap) * row, vtail_k,
+                            size_t(vtail_cap) * row, size_t(a + 1) * row, size_t(d.n_layers) * d.n_kv_heads,
+                            hipMemcpyDeviceToHost, copy));
+    VC_HIP(hipMemcpy2DAsync(mptr(req->full_v_host, int64_t(req->ctx_len) * row), size_t(req->full_cap) * row, vtail_v,
+                            size_t(vtail_cap) * row, size_t(a + 1) * row, size_t(d.n_layers) * d.n_kv_heads,
+                            hipMemcpyDeviceToHost, copy));
+  }
+  req->ctx_len += a + 1;
+  req->n_tail += a + 1;
+  req->draft_idx = 0;
+  return VC_OK;
+}
+
+vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, int32_t slot_cap, int32_t l0, int32_t l1,
+                   hipStream_t copy) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(req && slot_k && slot_v && req->full_k_host && req->full_v_host, VC_ERR_ARG, "vc_stage: null argument");
+  const vc_model_desc& d = m->d;
+  VC_REQUIRE(0 <= l0 && l0 <= l1 && l1 <= d.n_layers, VC_ERR_ARG, "vc_stage: bad layer range");
+  VC_REQUIRE(slot_cap >= req->ctx_len, VC_ERR_CAPACITY, "vc_stage: slot %d < ctx %d rows", slot_cap, req->ctx_len);
+  if (l0 == l1 || req->ctx_len == 0) return VC_OK;
+  const size_t row = size_t(d.head_dim) * m->eb;
+  const int64_t lo_src = int64_t(l0) * d.n_kv_heads * req->full_cap * row;
+  const int64_t lo_dst = int64_t(l0) * d.n_kv_heads * slot_cap * row;
+  const size_t height = size_t(l1 - l0) * d.n_kv_heads;
+  VC_HIP(hipMemcpy2DAsync(mptr(slot_k, lo_dst), size_t(slot_cap) * row, cptr(req->full_k_host, lo_src),
+                          size_t(req->full_cap) * row, size_t(req->ctx_len) * row, height, hipMemcpyHostToDevice, copy));
+  VC_HIP(hipMemcpy2DAsync(mptr(slot_v, lo_dst), size_t(slot_cap) * row, cptr(req->full_v_host, lo_src),
+                          size_t(req->full_cap) * row, size_t(req->ctx_len) * row, height, hipMemcpyHostToDevice, copy));
+  return VC_OK;
+}
+
+// ---------------------------------------------------------------- single-layer attention
+vc_status vc_attn_ws_size(const vc_attn_desc* d, int32_t n, int32_t rows, int32_t max_keys, size_t* bytes) {
+  VC_REQUIRE(d && bytes && n > 0 && rows > 0 && max_keys > 0, VC_ERR_ARG, "vc_attn_ws_size: bad arguments");
+  const int64_t D2 = d->head_dim + 2;
+  const int64_t S = cdiv(max_keys, SPLIT_DRAFT) + cdiv(max_keys, SPLIT_QUANT) + 2;
+  *bytes = align256(size_t(n) * rows * d->n_q_heads * S * D2 * 4);
+  return VC_OK;
+}
+
+vc_status vc_attn_draft(const vc_attn_desc* d, const vc_attn_draft_req* reqs, int32_t n, const void* q, void* out,
+                        void* ws, size_t ws_bytes, hipStream_t s) {
+  VC_REQUIRE(d && reqs && q && out && ws, VC_ERR_ARG, "vc_attn_draft: null argument");
+  VC_REQUIRE(n > 0 && n <= VC_MAX_BATCH, VC_ERR_ARG, "vc_attn_draft: batch %d not in [1, %d]", n, VC_MAX_BATCH);
+  VC_REQUIRE(d->n_kv_heads > 0 && d->n_q_heads % d->n_kv_heads == 0, VC_ERR_ARG, "vc_attn_draft: bad heads");
+  CompView views[VC_MAX_BATCH];
+  KVSeg tails[VC_MAX_BATCH];
+  int tail_n[VC_MAX_BATCH];
+  int max_keys = 1;
+  for (int r = 0; r < n; r++) {
+    if (vc_status st = comp_view(reqs[r].comp, reqs[r].cd, views[r])) return st;
+    VC_REQUIRE(reqs[r].cd->n_layers == 1 && reqs[r].cd->n_kv_heads == d->n_kv_heads &&
+                   reqs[r].cd->head_dim == d->head_dim && reqs[r].cd->dtype == d->dtype,
+               VC_ERR_ARG, "vc_attn_draft: request %d has another shape", r);
+    VC_REQUIRE(reqs[r].n_tail >= 0 && reqs[r].n_tail <= reqs[r].tail_cap, VC_ERR_ARG, "vc_attn_draft: bad tail");
+    VC_REQUIRE(reqs[r].n_tail == 0 || (reqs[r].tail_k && reqs[r].tail_v), VC_ERR_ARG, "vc_attn_draft: null tail");
+    tails[r] = KVSeg{reqs[r].tail_k, reqs[r].tail_v, int64_t(reqs[r].tail_cap) * d->head_dim, 0, 0};
+    tail_n[r] = reqs[r].n_tail;
+    max_keys = std::max(max_keys, views[r].lay.n_main + views[r].n_resid + tail_n[r]);
+  }
+  size_t need = 0;
+  vc_attn_ws_size(d, n, 1, max_keys, &need);
+  VC_REQUIRE(ws_bytes >= need, VC_ERR_CAPACITY, "vc_attn_draft: workspace %zu < %zu bytes", ws_bytes, need);
+  VC_REQUIRE(d->out_dtype == VC_F32 || d->out_dtype == VC_BF16, VC_ERR_ARG, "vc_attn_draft: bad out_dtype");
+  const int eb = d->dtype == VC_BF16 ? 2 : 4;
+  const int ob = d->out_dtype == VC_BF16 ? 2 : 4;
+  const int64_t stride = int64_t(d->n_q_heads) * d->head_dim * eb;
+  const int64_t ostride = int64_t(d->n_q_heads) * d->head_dim * ob;
+  return draft_attention(d->n_q_heads, d->n_kv_heads, d->head_dim, d->dtype, d->out_dtype, n, views, 0, tails, tail_n,
+                         q, stride, out, ostride, static_cast<float*>(ws), s);
+}
+
+vc_status vc_attn_verify(const vc_attn_desc* d, int32_t n, const void* q, const void* const* staged_k,
+                         const void* const* staged_v, int32_t staged_cap, const int32_t* ctx_host,
+                         const void* const* tail_k, const void* const* tail_v, int32_t tail_cap, int32_t n_rows,
+                         void* out, void* ws, size_t ws_bytes, hipStream_t s) {
+  VC_REQUIRE(d && q && staged_k && staged_v && ctx_host && tail_k && tail_v && out && ws, VC_ERR_ARG,
+             "vc_attn_verify: null argument");
+  VC_REQUIRE(n > 0 && n <= VC_MAX_BATCH && n_rows > 0 && n_rows <= tail_cap, VC_ERR_ARG, "vc_attn_verify: bad sizes");
+  VC_REQUIRE(d->n_kv_heads > 0 && d->n_q_heads % d->n_kv_heads == 0, VC_ERR_ARG, "vc_attn_verify: bad heads");
+  VC_REQUIRE(d->out_dtype == VC_F32 || d->out_dtype == VC_BF16, VC_ERR_ARG, "vc_attn_verify: bad out_dtype");
+  const int eb = d->dtype == VC_BF16 ? 2 : 4;
+  const int ob = d->out_dtype == VC_BF16 ? 2 : 4;
+  const int D = d->head_dim;
+  const int split = d->split_len > 0 ? d->split_len : SPLIT_VERIFY;
+  VC_REQUIRE(split % ATT_KT == 0, VC_ERR_ARG, "vc_attn_verify: split_len must be a multiple of 64");
+  int max_keys = 1;
+  for (int r = 0; r < n; r++) {
+    VC_REQUIRE(ctx_host[r] >= 0 && ctx_host[r] <= staged_cap, VC_ERR_ARG, "vc_attn_verify: bad ctx");
+    max_keys = std::max(max_keys, ctx_host[r] + n_rows);
+  }
+  const int S = int(cdiv(max_keys, split));
+  const size_t need = align256(size_t(n) * n_rows * d->n_q_heads * S * (D + 2) * 4);
+  VC_REQUIRE(ws_bytes >= need, VC_ERR_CAPACITY, "vc_attn_verify: workspace %zu < %zu bytes", ws_bytes, need);
+  float* part = static_cast<float*>(ws);
+  const int64_t per_req = int64_t(n_rows) * d->n_q_heads * S * (D + 2);
+  const int64_t qstride = int64_t(n_rows) * d->n_q_heads * D * eb;
+  AttnArgs a{};
+  a.n_req = n;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.G = d->n_q_heads / d->n_kv_heads;
+  a.split_len = split;
+  a.head_dim = D;
+  a.scale_log2 = LOG2E / sqrtf(float(D));
+  a.n_rowblocks = int(cdiv(int64_t(n_rows) * a.G, ATT_RB));
+  a.max_splits = S;
+  CombineArgs c{};
+  c.n_req = n;
+  c.n_rows = n_rows;
+  c.Hq = d->n_q_heads;
+  c.s_total = S;
+  c.head_dim = D;
+  c.out_dtype = d->out_dtype;
+  const int64_t ostride = int64_t(n_rows) * d->n_q_heads * D * ob;
+  for (int r = 0; r < n; r++) {
+    AttnReq& ar = a.r[r];
+    ar.q = cptr(q, r * qstride);
+    ar.a = KVSeg{staged_k[r], staged_v[r], int64_t(staged_cap) * D, ctx_host[r], 0};
+    ar.b = KVSeg{tail_k[r], tail_v[r], int64_t(tail_cap) * D, n_rows, 0};
+    ar.part = part + r * per_req;
+    ar.n_rows = n_rows;
+    ar.lim0 = ctx_host[r];
+    ar.s_off = 0;
+    ar.s_total = S;
+    ar.n_splits = int(cdiv(ctx_host[r] + n_rows, split));
+    c.part[r] = ar.part;
+    c.out[r] = mptr(out, r * ostride);
+    c.s_used[r] = ar.n_splits;
+  }
+  vc_status st = launch_attn(a, d->dtype, s);
+  if (st) return st;
+  return launch_combine(c, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal launch interface of the attention kernels.
+//
+// Every attention call produces split-K partials (m, l, o[D]) per query row and
+// query head, then attn_combine merges them in ascending split order:
+//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s o_s 2^(m_s - M) / L
+// (m is kept in log2 units: scores are pre-multiplied by log2(e) / sqrt(D)).
+// Keys are addressed by a logical index t over up to two segments (a then b);
+// splits and 64-key tiles are aligned to t = 0, and query row i (position
+// index within the call) sees keys t <= lim0 + i.  For verification the
+// logical index is the absolute position (a = staged full cache, b = verify
+// tail), which makes each row's arithmetic independent of the row count.
+#pragma once
+#include "common.h"
+
+namespace vc {
+
+constexpr int ATT_KT = 64;   // keys per tile
+constexpr int ATT_RB = 64;   // query rows (row x GQA head) per workgroup
+
+struct KVSeg {
+  const void* k;
+  const void* v;
+  int64_t hstride;  // elements between consecutive KV heads
+  int32_t n;        // rows
+  int32_t pad_;
+};
+
+struct AttnReq {
+  const void* q;     // [rows][Hq][D]
+  KVSeg a, b;        // logical keys: t < a.n -> a[t], else b[t - a.n]
+  float* part;       // [rows][Hq][s_total][D + 2]
+  int32_t n_rows;
+  int32_t lim0;
+  int32_t s_off;     // partial slot of this launch's split 0
+  int32_t s_total;
+  int32_t n_splits;  // splits of this request in this launch
+  int32_t pad_;
+};
+
+struct AttnArgs {
+  AttnReq r[VC_MAX_BATCH];
+  int32_t n_req, Hq, Hkv, G, split_len, n_rowblocks, max_splits, head_dim;
+  float scale_log2;
+};
+
+// Quantized main region of one request (one layer), plus the per-request
+// view of the draft query.
+struct QuantSeg {
+  const uint8_t* kc;   // [Hkv][Tq][D*b/8]
+  const uint8_t* vc;   // [Hkv][Tq/64][D][64*b/8]
+  const uint16_t* ks;  // [Hkv][Tq/G][D] fp16
+  const uint16_t* kz;
+  const uint16_t* vs;  // [Hkv][Tq][D/G] fp16
+  const uint16_t* vz;
+  int32_t tq;          // quantized rows
+  int32_t pad_;
+};
+
+struct QuantReq {
+  const void* q;       // [1][Hq][D] bf16
+  QuantSeg m;
+  float* part;         // [1][Hq][s_total][D + 2]
+  int32_t s_total, n_splits;
+};
+
+struct QuantArgs {
+  QuantReq r[VC_MAX_BATCH];
+  int32_t n_req, Hq, Hkv, G, bits, group, split_len, max_splits;
+  float scale_log2;
+};
+
+// dtype: VC_BF16 (head_dim 128, MFMA) or VC_F32 (head_dim 64, VALU)
+vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s);
+vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* part[VC_MAX_BATCH];  // [rows][Hq][s_total][D+2]
+  void* out[VC_MAX_BATCH];          // [rows][Hq][D]
+  int32_t s_used[VC_MAX_BATCH];     // slots to merge (<= s_total)
+  int32_t n_req, n_rows, Hq, s_total, head_dim, out_dtype;
+};
+vc_status launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace vc

@@ -1,0 +1,358 @@
+// Attention kernels: split-K partials over bf16/fp32 key segments, the
+// fixed-order combine, and (in attention_quant.hip) the quantized-cache decode.
+//
+// bf16 kernel (head_dim 128), one workgroup = 4 waves = (request, KV head,
+// 64-row block, split).  Per 64-key tile the whole workgroup stages K (row
+// major) and V (transposed, keys contiguous per channel) in LDS; each wave
+// that owns 16 query rows then computes
+//     S^T = K Q^T      (16x16x32 bf16 MFMA, A = K rows, B = Q^T fragments)
+//     online softmax per query row (rows live in lanes l % 16)
+//     O^T += V^T P^T   (A = V^T from LDS, B = P^T straight from the S^T registers)
+// The S^T output layout puts row q = l%16 with keys 4*(l/16)+j of each 16-key
+// sub-tile in lane l, which is exactly the B-operand layout P^T needs once the
+// 32 keys of a chunk are enumerated as {4g..4g+3, 16+4g..16+4g+3}; V^T is read
+// in that same key order, so no cross-lane shuffle of P is needed.
+// The P.V product runs in fp16: V is converted from bf16 while it is staged
+// (exact for |v| in [2^-14, 65504]) and P is rounded to fp16 after scaling by
+// 2^10 (P <= 1), which keeps 11 significant bits of every weight instead of
+// bf16's 8; QK^T stays bf16 x bf16 with exact products.
+#include "attention.h"
+
+namespace vc {
+
+namespace {
+
+constexpr int D128 = 128;
+constexpr int KS_PITCH = D128 + 8;     // bf16 per K row in LDS (pad breaks bank aliasing)
+constexpr int VT_PITCH = ATT_KT + 8;   // fp16 per V^T row in LDS
+constexpr float P_SCALE = 1024.f;      // P is rounded to fp16 as P * 2^10
+constexpr float P_UNSCALE = 1.f / 1024.f;
+
+struct TileRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+__device__ __forceinline__ const uint16_t* seg_row(const KVSeg& a, const KVSeg& b, int j, int t, bool is_v) {
+  if (t < a.n) {
+    const uint16_t* base = static_cast<const uint16_t*>(is_v ? a.v : a.k);
+    return base + j * a.hstride + int64_t(t) * D128;
+  }
+  const uint16_t* base = static_cast<const uint16_t*>(is_v ? b.v : b.k);
+  return base + j * b.hstride + int64_t(t - a.n) * D128;
+}
+
+// K: thread (key = tid/4, q = tid%4) loads 16-byte chunks 4e+q (e = 0..3) of its row.
+// V: thread (dc = tid/16, kg = tid%16) loads channels 8dc..8dc+7 of keys 4kg..4kg+3.
+__device__ __forceinline__ void load_tile_bf16(TileRegs& r, const KVSeg& a, const KVSeg& b, int j, int t0,
+                                               int n_keys, int tid) {
+  {
+    const int key = tid >> 2, q = tid & 3, t = t0 + key;
+    if (t < n_keys) {
+      const uint16_t* row = seg_row(a, b, j, t, false);
+#pragma unroll
+      for (int e = 0; e < 4; e++) r.k[e] = *reinterpret_cast<const u32x4*>(row + 8 * (4 * e + q));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; e++) r.k[e] = u32x4{0, 0, 0, 0};
+    }
+  }
+  {
+    const int dc = tid >> 4, kg = tid & 15;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int t = t0 + 4 * kg + e;
+      if (t < n_keys) {
+        r.v[e] = *reinterpret_cast<const u32x4*>(seg_row(a, b, j, t, true) + 8 * dc);
+      } else {
+        r.v[e] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile_bf16(const TileRegs& r, uint16_t* Ks, uint16_t* Vt, int tid) {
+  {
+    const int key = tid >> 2, q = tid & 3;
+#pragma unroll
+    for (int e = 0; e < 4; e++) *reinterpret_cast<u32x4*>(Ks + key * KS_PITCH + 8 * (4 * e + q)) = r.k[e];
+  }
+  {
+    const int dc = tid >> 4, kg = tid & 15;
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const int w = c >> 1;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) x[e] = (c & 1) ? hi_bf(r.v[e][w]) : lo_bf(r.v[e][w]);
+      u32x2 out;
+      out.x = bitcast<uint32_t>(f16x2{(_Float16)x[0], (_Float16)x[1]});
+      out.y = bitcast<uint32_t>(f16x2{(_Float16)x[2], (_Float16)x[3]});
+      *reinterpret_cast<u32x2*>(Vt + (8 * dc + c) * VT_PITCH + 4 * kg) = out;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[ATT_KT * KS_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D128 * VT_PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int z = blockIdx.z;
+  if (z >= args.n_req) return;
+  const AttnReq& R = args.r[z];
+  const int Hkv = args.Hkv, G = args.G, Hq = args.Hq;
+  const int j = blockIdx.x % Hkv, rb = blockIdx.x / Hkv;
+  const int s = blockIdx.y;
+  const int n_qrows = R.n_rows * G;
+  const int qr0 = rb * ATT_RB;
+  if (qr0 >= n_qrows || s >= R.n_splits) return;  // uniform across the workgroup
+
+  const int n_keys = R.a.n + R.b.n;
+  const int key_lo = s * args.split_len;
+  const int i_max = (min(qr0 + ATT_RB, n_qrows) - 1) / G;
+  const int key_hi = min(min(key_lo + args.split_len, n_keys), R.lim0 + i_max + 1);
+
+  // this lane's query row
+  const int qr = qr0 + wave * 16 + (lane & 15);
+  const bool row_ok = qr < n_qrows;
+  const int qi = row_ok ? qr / G : 0;
+  const int hq = j * G + (row_ok ? qr % G : 0);
+  const bool wave_active = qr0 + wave * 16 < n_qrows;
+  const int lim = R.lim0 + qi;
+  const int grp = lane >> 4;
+
+  u32x4 qf[4];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(R.q) + (int64_t(qi) * Hq + hq) * D128;
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+      qf[c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * grp) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) oacc[dt] = f32x4{0, 0, 0, 0};
+  float m_run = NEG_INF, l_run = 0.f;
+  const float sl2 = args.scale_log2;
+
+  TileRegs regs;
+  if (key_lo < key_hi) load_tile_bf16(regs, R.a, R.b, j, key_lo, n_keys, tid);
+  for (int t0 = key_lo; t0 < key_hi; t0 += ATT_KT) {
+    __syncthreads();
+    store_tile_bf16(regs, Ks, Vt, tid);
+    __syncthreads();
+    if (t0 + ATT_KT < key_hi) load_tile_bf16(regs, R.a, R.b, j, t0 + ATT_KT, n_keys, tid);
+    if (!wave_active) continue;
+
+    // ---- S^T = K Q^T over 4 sub-tiles of 16 keys
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+      sacc[kt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (16 * kt + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
+        sacc[kt] = mfma_bf16(ka, qf[c], sacc[kt]);
+      }
+    }
+    // ---- scale, mask, online softmax (row q = lane % 16)
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int t = t0 + 16 * kt + 4 * grp + jj;
+        const bool vis = row_ok && t < n_keys && t <= lim;
+        const float v = vis ? sacc[kt][jj] * sl2 : NEG_INF;
+        sacc[kt][jj] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const bool none = (m_new == NEG_INF);
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sacc[kt][jj] - m_new);
+        sacc[kt][jj] = p;
+        rs += p;
+      }
+    }
+    rs += shfl_xor(rs, 16);
+    rs += shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) oacc[dt] *= alpha;
+
+    // ---- O^T += V^T P^T over 2 chunks of 32 keys
+#pragma unroll
+    for (int kc = 0; kc < 2; kc++) {
+      u32x4 pb;
+      pb.x = pack_h2(sacc[2 * kc][0] * P_SCALE, sacc[2 * kc][1] * P_SCALE);
+      pb.y = pack_h2(sacc[2 * kc][2] * P_SCALE, sacc[2 * kc][3] * P_SCALE);
+      pb.z = pack_h2(sacc[2 * kc + 1][0] * P_SCALE, sacc[2 * kc + 1][1] * P_SCALE);
+      pb.w = pack_h2(sacc[2 * kc + 1][2] * P_SCALE, sacc[2 * kc + 1][3] * P_SCALE);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        const uint16_t* vrow = Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 4 * grp;
+        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 16);
+        const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
+        oacc[dt] = mfma_f16(va, pb, oacc[dt]);
+      }
+    }
+  }
+
+  // ---- partial (m, l, o) of this lane's row; lane holds o[16dt + 4g + jj]
+  if (!wave_active || !row_ok) return;
+  float* dst = R.part + ((int64_t(qi) * Hq + hq) * R.s_total + (R.s_off + s)) * (D128 + 2);
+  if (grp == 0) {
+    dst[0] = m_run;
+    dst[1] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) {
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) dst[2 + 16 * dt + 4 * grp + jj] = oacc[dt][jj] * P_UNSCALE;
+  }
+}
+
+// ---------------------------------------------------------------- fp32 (head_dim 64), VALU
+// One workgroup (64 threads) per (request, KV head, query row, split).  Lane t
+// scores key t0 + t of each 64-key tile; lane d accumulates o[d].  The key
+// order and tile boundaries are fixed by absolute key index, so each row's
+// result does not depend on the other rows of the call.
+constexpr int D64 = 64;
+
+__global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs args) {
+  __shared__ float Kt[ATT_KT][D64 + 1];
+  __shared__ float Vs[ATT_KT][D64];
+  __shared__ float qs[D64];
+  __shared__ float ps[ATT_KT];
+  const int lane = threadIdx.x;
+  const int z = blockIdx.z;
+  if (z >= args.n_req) return;
+  const AttnReq& R = args.r[z];
+  const int Hkv = args.Hkv, G = args.G, Hq = args.Hq;
+  const int j = blockIdx.x % Hkv, qr = blockIdx.x / Hkv;
+  const int s = blockIdx.y;
+  const int n_qrows = R.n_rows * G;
+  if (qr >= n_qrows || s >= R.n_splits) return;
+  const int qi = qr / G, hq = j * G + qr % G;
+  const int n_keys = R.a.n + R.b.n;
+  const int key_lo = s * args.split_len;
+  const int lim = R.lim0 + qi;
+  const int key_hi = min(min(key_lo + args.split_len, n_keys), lim + 1);
+  const float* qp = static_cast<const float*>(R.q) + (int64_t(qi) * Hq + hq) * D64;
+  qs[lane] = qp[lane];
+  float m_run = NEG_INF, l_run = 0.f, o = 0.f;
+  const float sl2 = args.scale_log2;
+  for (int t0 = key_lo; t0 < key_hi; t0 += ATT_KT) {
+    __syncthreads();
+    for (int r = 0; r < ATT_KT; r++) {
+      const int t = t0 + r;
+      float kv = 0.f, vv = 0.f;
+      if (t < n_keys) {
+        const bool in_a = t < R.a.n;
+        const KVSeg& sg = in_a ? R.a : R.b;
+        const int tt = in_a ? t : t - R.a.n;
+        kv = static_cast<const float*>(sg.k)[j * sg.hstride + int64_t(tt) * D64 + lane];
+        vv = static_cast<const float*>(sg.v)[j * sg.hstride + int64_t(tt) * D64 + lane];
+      }
+      Kt[r][lane] = kv;
+      Vs[r][lane] = vv;
+    }
+    __syncthreads();
+    const int t = t0 + lane;
+    float sc = 0.f;
+    for (int d = 0; d < D64; d++) sc = fmaf(qs[d], Kt[lane][d], sc);
+    const bool vis = t < n_keys && t <= lim;
+    const float v = vis ? sc * sl2 : NEG_INF;
+    float mx = v;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+    const float m_new = fmaxf(m_run, mx);
+    const bool none = (m_new == NEG_INF);
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float p = none ? 0.f : __builtin_amdgcn_exp2f(v - m_new);
+    float rs = p;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) rs += shfl_xor(rs, off);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    ps[lane] = p;
+    __syncthreads();
+    float acc = 0.f;
+    for (int r = 0; r < ATT_KT; r++) acc = fmaf(ps[r], Vs[r][lane], acc);
+    o = o * alpha + acc;
+  }
+  float* dst = R.part + ((int64_t(qi) * Hq + hq) * R.s_total + (R.s_off + s)) * (D64 + 2);
+  if (lane == 0) {
+    dst[0] = m_run;
+    dst[1] = l_run;
+  }
+  dst[2 + lane] = o;
+}
+
+// ---------------------------------------------------------------- combine
+// One workgroup per (request, row, query head); thread d merges o[d].
+__global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
+  const int z = blockIdx.y;
+  if (z >= a.n_req) return;
+  const int rh = blockIdx.x;  // row * Hq + hq
+  const int D = a.head_dim;
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  const float* p = a.part[z] + int64_t(rh) * a.s_total * (D + 2);
+  const int S = a.s_used[z];
+  float M = NEG_INF;
+  for (int s = 0; s < S; s++) M = fmaxf(M, p[s * (D + 2)]);
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < S; s++) {
+    const float ms = p[s * (D + 2)];
+    const float w = (ms == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    L = fmaf(p[s * (D + 2) + 1], w, L);
+    O = fmaf(p[s * (D + 2) + 2 + d], w, O);
+  }
+  const float r = O / L;
+  if (a.out_dtype == VC_BF16) {
+    static_cast<uint16_t*>(a.out[z])[int64_t(rh) * D + d] = f2bf(r);
+  } else {
+    static_cast<float*>(a.out[z])[int64_t(rh) * D + d] = r;
+  }
+}
+
+}  // namespace
+
+vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s) {
+  if (a.n_req <= 0 || a.max_splits <= 0) return VC_OK;
+  if (dtype == VC_BF16) {
+    VC_REQUIRE(a.head_dim == 128, VC_ERR_UNSUPPORTED, "bf16 attention needs head_dim 128 (got %d)", a.head_dim);
+    dim3 grid(a.Hkv * a.n_rowblocks, a.max_splits, a.n_req);
+    hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(256), 0, s, a);
+  } else {
+    VC_REQUIRE(a.head_dim == 64, VC_ERR_UNSUPPORTED, "fp32 attention needs head_dim 64 (got %d)", a.head_dim);
+    int max_qrows = 0;
+    for (int i = 0; i < a.n_req; i++) max_qrows = max(max_qrows, a.r[i].n_rows * a.G);
+    dim3 grid(a.Hkv * max_qrows, a.max_splits, a.n_req);
+    hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), 0, s, a);
+  }
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+
+vc_status launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.n_req <= 0) return VC_OK;
+  dim3 grid(a.n_rows * a.Hq, a.n_req);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(128), 0, s, a);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+
+}  // namespace vc

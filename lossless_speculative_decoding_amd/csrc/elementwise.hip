@@ -1,0 +1,171 @@
+// Row-wise kernels of the forward pass and the accept / commit steps.
+#include "elementwise.h"
+
+namespace vc {
+
+namespace {
+
+__device__ __forceinline__ float ld(const void* p, int64_t i, int dt) {
+  return dt == VC_BF16 ? bf2f(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+__device__ __forceinline__ void st(void* p, int64_t i, float v, int dt) {
+  if (dt == VC_BF16) static_cast<uint16_t*>(p)[i] = f2bf(v);
+  else static_cast<float*>(p)[i] = v;
+}
+
+__global__ void embed_kernel(const void* E, const int32_t* tok, void* h, int d, int dt) {
+  const int r = blockIdx.y;
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= d) return;
+  const int64_t t = tok[r];
+  if (dt == VC_BF16) static_cast<uint16_t*>(h)[int64_t(r) * d + c] = static_cast<const uint16_t*>(E)[t * d + c];
+  else static_cast<float*>(h)[int64_t(r) * d + c] = static_cast<const float*>(E)[t * d + c];
+}
+
+// y = x / sqrt(mean(x^2) + eps) * g, one workgroup of 256 threads per row; the
+// sum of squares is reduced in a fixed tree so every row is computed identically.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void* g, void* y, int d, float eps, int dt) {
+  __shared__ float red[256];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t base = int64_t(r) * d;
+  float ss = 0.f;
+  for (int c = tid; c < d; c += 256) {
+    const float v = ld(x, base + c, dt);
+    ss = fmaf(v, v, ss);
+  }
+  red[tid] = ss;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const float inv = 1.f / sqrtf(red[0] / float(d) + eps);
+  for (int c = tid; c < d; c += 256) st(y, base + c, ld(x, base + c, dt) * inv * ld(g, c, dt), dt);
+}
+
+// Greedy choice per row: the largest logit, ties to the lowest index.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V, int32_t* out) {
+  __shared__ float bv[1024];
+  __shared__ int bi[1024];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* p = logits + int64_t(r) * V;
+  float best = -__builtin_huge_valf();
+  int bidx = 0x7fffffff;
+  for (int c = tid; c < V; c += 1024) {
+    const float v = p[c];
+    if (v > best) {  // ascending c per thread: strict > keeps the lowest index of ties
+      best = v;
+      bidx = c;
+    }
+  }
+  bv[tid] = best;
+  bi[tid] = bidx;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (tid < off) {
+      const float v2 = bv[tid + off];
+      const int i2 = bi[tid + off];
+      if (v2 > bv[tid] || (v2 == bv[tid] && i2 < bi[tid])) {
+        bv[tid] = v2;
+        bi[tid] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) out[r] = bi[0];
+}
+
+// a = first i < x with draft[i] != verified[i] (else x); result = [a, draft[0..a), verified[a]].
+__global__ void accept_kernel(const int32_t* draft, const int32_t* verified, int x, int32_t* result) {
+  if (threadIdx.x != 0) return;
+  int a = x;
+  for (int i = 0; i < x; i++) {
+    if (draft[i] != verified[i]) {
+      a = i;
+      break;
+    }
+  }
+  result[0] = a;
+  for (int i = 0; i < a; i++) result[1 + i] = draft[i];
+  result[1 + a] = verified[a];
+}
+
+// Copy rows 0..result[0] of vtail into tail at row n_tail, for every (layer, head).
+__global__ void commit_rows_kernel(const uint8_t* vk, const uint8_t* vv, int vcap, uint8_t* tk, uint8_t* tv, int tcap,
+                                   int n_tail, int row_bytes, int n_lh, const int32_t* result) {
+  const int a = result[0];
+  const int row = blockIdx.y;
+  if (row > a) return;
+  const int lh = blockIdx.z;
+  const int words = row_bytes / 4;
+  for (int w = threadIdx.x; w < words; w += blockDim.x) {
+    const int64_t so = (int64_t(lh) * vcap + row) * row_bytes;
+    const int64_t dof = (int64_t(lh) * tcap + n_tail + row) * row_bytes;
+    reinterpret_cast<uint32_t*>(tk + dof)[w] = reinterpret_cast<const uint32_t*>(vk + so)[w];
+    reinterpret_cast<uint32_t*>(tv + dof)[w] = reinterpret_cast<const uint32_t*>(vv + so)[w];
+  }
+}
+
+// cos/sin of pos * theta^(-2i/D) in float64, stored float32 [max_pos][D/2][2].
+__global__ void rope_table_kernel(float* tab, int max_pos, int D, double theta) {
+  const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int half = D / 2;
+  if (u >= int64_t(max_pos) * half) return;
+  const int i = int(u % half);
+  const int64_t pos = u / half;
+  const double ang = double(pos) * pow(theta, -2.0 * double(i) / double(D));
+  tab[2 * u] = float(cos(ang));
+  tab[2 * u + 1] = float(sin(ang));
+}
+
+__global__ void copy_words_kernel(const uint32_t* src, uint32_t* dst, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+}  // namespace
+
+vc_status k_embed(const void* E, const int32_t* tok, void* h, int M, int d, int dt, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(cdiv(d, 256), M), dim3(256), 0, s, E, tok, h, d, dt);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+vc_status k_rmsnorm(const void* x, const void* g, void* y, int M, int d, float eps, int dt, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, g, y, d, eps, dt);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+vc_status k_argmax(const float* logits, int M, int V, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(M), dim3(1024), 0, s, logits, V, out);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+vc_status k_accept(const int32_t* draft, const int32_t* verified, int x, int32_t* result, hipStream_t s) {
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, s, draft, verified, x, result);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+vc_status k_commit_rows(const void* vk, const void* vv, int vcap, void* tk, void* tv, int tcap, int n_tail,
+                        int row_bytes, int n_lh, int max_rows, const int32_t* result, hipStream_t s) {
+  hipLaunchKernelGGL(commit_rows_kernel, dim3(1, max_rows, n_lh), dim3(64), 0, s, static_cast<const uint8_t*>(vk),
+                     static_cast<const uint8_t*>(vv), vcap, static_cast<uint8_t*>(tk), static_cast<uint8_t*>(tv), tcap,
+                     n_tail, row_bytes, n_lh, result);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+vc_status k_rope_table(float* tab, int max_pos, int D, double theta, hipStream_t s) {
+  const int64_t n = int64_t(max_pos) * (D / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, tab, max_pos, D, theta);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+vc_status k_copy_words(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+  const int64_t n = bytes / 4;
+  if (n == 0) return VC_OK;
+  hipLaunchKernelGGL(copy_words_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, static_cast<const uint32_t*>(src),
+                     static_cast<uint32_t*>(dst), n);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+
+}  // namespace vc

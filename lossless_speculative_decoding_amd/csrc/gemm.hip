@@ -1,0 +1,318 @@
+// Projection GEMMs (Y = X W^T) and the fused per-layer epilogue.
+//
+// Decode / verify (M <= 64) are weight-streaming: every weight is read once
+// per forward.  gemm_skinny_bf16: a workgroup owns 64 output columns (16 per
+// wave) and one K range; the activations of that range are staged in LDS
+// 256 columns at a time and every wave runs 16x16x32 bf16 MFMAs over all
+// M rows (padded to 16) while its next weight fragments are in flight.
+// Prefill chunks (M > 64) use gemm_big_bf16, a 128x128x32 LDS double-buffered
+// MFMA tile.  The fp32 model uses a 16x16 tiled VALU kernel whose outputs are
+// single fma chains in ascending k.
+#include <algorithm>
+
+#include "gemm.h"
+
+namespace vc {
+
+namespace {
+
+constexpr int SK_NB = 64;
+constexpr int SK_KC = 256;
+constexpr int SK_XP = SK_KC + 8;
+
+__global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                        float* __restrict__ P, int M, int N, int K, int kps) {
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[64 * SK_XP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int n0 = blockIdx.x * SK_NB + wave * 16;
+  const int s = blockIdx.y;
+  const int k_lo = s * kps, k_hi = min(K, k_lo + kps);
+  const int n_mt = (M + 15) >> 4;
+  f32x4 acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4{0, 0, 0, 0};
+  const uint16_t* wrow = W + int64_t(n0 + r) * K;
+
+  u32x4 wf[2][4];
+  auto load_w = [&](int kc) {
+    const int klen = min(SK_KC, k_hi - kc);
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        wf[h][e] = (128 * h < klen) ? *reinterpret_cast<const u32x4*>(wrow + kc + 128 * h + 32 * e + 8 * g)
+                                    : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  if (k_lo < k_hi) load_w(k_lo);
+  for (int kc = k_lo; kc < k_hi; kc += SK_KC) {
+    const int klen = min(SK_KC, k_hi - kc);
+    __syncthreads();
+    const int rows = n_mt * 16;
+    for (int idx = tid; idx < rows * (SK_KC / 8); idx += 256) {
+      const int row = idx / (SK_KC / 8), c8 = idx % (SK_KC / 8);
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (row < M && 8 * c8 < klen) v = *reinterpret_cast<const u32x4*>(X + int64_t(row) * K + kc + 8 * c8);
+      *reinterpret_cast<u32x4*>(Xs + row * SK_XP + 8 * c8) = v;
+    }
+    __syncthreads();
+    u32x4 cur[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) cur[h][e] = wf[h][e];
+    if (kc + SK_KC < k_hi) load_w(kc + SK_KC);
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      if (128 * h >= klen) break;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          if (mt >= n_mt) break;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(Xs + (16 * mt + r) * SK_XP + 128 * h + 32 * e + 8 * g);
+          acc[mt] = mfma_bf16(a, cur[h][e], acc[mt]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+    if (mt >= n_mt) break;
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int m = 16 * mt + 4 * g + jj;
+      if (m < M) P[(int64_t(s) * M + m) * N + n0 + r] = acc[mt][jj];
+    }
+  }
+}
+
+constexpr int BG_P = 40;  // LDS pitch (bf16) of a 32-wide k slice
+
+__global__ __launch_bounds__(256) void gemm_big_bf16(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                     float* __restrict__ P, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][128 * BG_P];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * BG_P];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int jx = 0; jx < 4; jx++) acc[i][jx] = f32x4{0, 0, 0, 0};
+  u32x4 ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int c = tid + 256 * i;
+      const int row = c >> 2, c8 = c & 3;
+      const int m = m0 + row;
+      ra[i] = m < M ? *reinterpret_cast<const u32x4*>(X + int64_t(m) * K + k0 + 8 * c8) : u32x4{0, 0, 0, 0};
+      rb[i] = *reinterpret_cast<const u32x4*>(W + int64_t(n0 + row) * K + k0 + 8 * c8);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int c = tid + 256 * i;
+      const int row = c >> 2, c8 = c & 3;
+      *reinterpret_cast<u32x4*>(&As[buf][row * BG_P + 8 * c8]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[buf][row * BG_P + 8 * c8]) = rb[i];
+    }
+  };
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const bool more = k0 + 32 < K;
+    if (more) gload(k0 + 32);
+    u32x4 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      af[i] = *reinterpret_cast<const u32x4*>(&As[buf][(64 * wm + 16 * i + r) * BG_P + 8 * g]);
+      bfr[i] = *reinterpret_cast<const u32x4*>(&Bs[buf][(64 * wn + 16 * i + r) * BG_P + 8 * g]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int jx = 0; jx < 4; jx++) acc[i][jx] = mfma_bf16(af[i], bfr[jx], acc[i][jx]);
+    if (more) sstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * g + jj;
+      if (m >= M) continue;
+#pragma unroll
+      for (int jx = 0; jx < 4; jx++) P[int64_t(m) * N + n0 + 64 * wn + 16 * jx + r] = acc[i][jx][jj];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void gemm_f32_tiled(const float* __restrict__ X, const float* __restrict__ W,
+                                                      float* __restrict__ P, int M, int N, int K) {
+  __shared__ float Xs[16][17];
+  __shared__ float Ws[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m = blockIdx.y * 16 + ty, n = blockIdx.x * 16 + tx;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const int xm = blockIdx.y * 16 + ty, wn = blockIdx.x * 16 + ty;
+    Xs[ty][tx] = (xm < M && k0 + tx < K) ? X[int64_t(xm) * K + k0 + tx] : 0.f;
+    Ws[ty][tx] = (wn < N && k0 + tx < K) ? W[int64_t(wn) * K + k0 + tx] : 0.f;
+    __syncthreads();
+    const int kl = min(16, K - k0);
+    for (int kk = 0; kk < kl; kk++) acc = fmaf(Xs[ty][kk], Ws[tx][kk], acc);
+    __syncthreads();
+  }
+  if (m < M && n < N) P[int64_t(m) * N + n] = acc;
+}
+
+// ---------------------------------------------------------------- epilogue
+__device__ __forceinline__ float ld_act(const void* p, int64_t i, int dtype) {
+  return dtype == VC_BF16 ? bf2f(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+__device__ __forceinline__ void st_act(void* p, int64_t i, float v, int dtype) {
+  if (dtype == VC_BF16) static_cast<uint16_t*>(p)[i] = f2bf(v);
+  else static_cast<float*>(p)[i] = v;
+}
+__device__ __forceinline__ float psum(const float* P, int S, int M, int N, int r, int c) {
+  float v = P[int64_t(r) * N + c];
+  for (int s = 1; s < S; s++) v += P[(int64_t(s) * M + r) * N + c];
+  return v;
+}
+
+__global__ void epilogue_kernel(const EpiArgs a) {
+  const int r = blockIdx.y;
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  const int M = a.M, N = a.N, S = a.S;
+  if (a.mode == EPI_RESID) {
+    if (u >= N) return;
+    const float y = psum(a.P, S, M, N, r, u);
+    const int64_t i = int64_t(r) * N + u;
+    st_act(a.out, i, ld_act(a.out, i, a.dtype) + y, a.dtype);
+  } else if (a.mode == EPI_SWIGLU) {
+    const int F = N / 2;
+    if (u >= F) return;
+    const float gt = psum(a.P, S, M, N, r, u);
+    const float up = psum(a.P, S, M, N, r, F + u);
+    const float sg = gt / (1.f + expf(-gt));
+    st_act(a.out, int64_t(r) * F + u, sg * up, a.dtype);
+  } else if (a.mode == EPI_COPY) {
+    if (u >= N) return;
+    static_cast<float*>(a.out)[int64_t(r) * N + u] = psum(a.P, S, M, N, r, u);
+  } else {  // EPI_QKV: units = (Hq + 2 Hkv) * D / 2
+    const int D = a.D, half = D / 2;
+    const int nq = a.Hq * half, nk = a.Hkv * half;
+    if (u >= nq + 2 * nk) return;
+    const int pos = a.batched ? a.pos[r] : a.pos0 + r;
+    if (u < nq + nk) {
+      const bool isq = u < nq;
+      const int uu = isq ? u : u - nq;
+      const int h = uu / half, i = uu % half;
+      const int col = (isq ? 0 : a.Hq * D) + h * D + i;
+      const float ya = psum(a.P, S, M, N, r, col);
+      const float yb = psum(a.P, S, M, N, r, col + half);
+      const float c = a.rope[(int64_t(pos) * half + i) * 2];
+      const float sn = a.rope[(int64_t(pos) * half + i) * 2 + 1];
+      const float oa = ya * c - yb * sn;
+      const float ob = yb * c + ya * sn;
+      if (isq) {
+        const int64_t qi = (int64_t(r) * a.Hq + h) * D + i;
+        st_act(a.q_out, qi, oa, a.dtype);
+        st_act(a.q_out, qi + half, ob, a.dtype);
+      } else {
+        void* base;
+        int64_t off;
+        if (a.batched) {
+          base = a.krow[r];
+          off = int64_t(h) * a.rpitch[r] * D + i;
+        } else {
+          base = a.kbase;
+          off = (int64_t(h) * a.pitch + a.row0 + r) * D + i;
+        }
+        st_act(base, off, oa, a.dtype);
+        st_act(base, off + half, ob, a.dtype);
+      }
+    } else {
+      const int uu = u - nq - nk;  // v pair
+      const int h = uu / half, i = uu % half;
+      const int col = (a.Hq + a.Hkv) * D + h * D + 2 * i;
+      const float y0 = psum(a.P, S, M, N, r, col);
+      const float y1 = psum(a.P, S, M, N, r, col + 1);
+      void* base;
+      int64_t off;
+      if (a.batched) {
+        base = a.vrow[r];
+        off = int64_t(h) * a.rpitch[r] * D + 2 * i;
+      } else {
+        base = a.vbase;
+        off = (int64_t(h) * a.pitch + a.row0 + r) * D + 2 * i;
+      }
+      st_act(base, off, y0, a.dtype);
+      st_act(base, off + 1, y1, a.dtype);
+    }
+  }
+}
+
+}  // namespace
+
+int gemm_splits(int M, int N, int K, int dtype) {
+  if (dtype != VC_BF16 || M > 64) return 1;
+  const int col_blocks = N / SK_NB;
+  int want = std::max(1, 1024 / std::max(col_blocks, 1));
+  const int max_s = std::max(1, K / 128);
+  want = std::min(want, max_s);
+  // K range per split: multiple of 128
+  const int kps = int(cdiv(cdiv(K, want), 128) * 128);
+  return int(cdiv(K, kps));
+}
+
+vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int S, int dtype, hipStream_t s) {
+  VC_REQUIRE(M > 0 && N > 0 && K > 0, VC_ERR_ARG, "gemm: bad shape %d x %d x %d", M, N, K);
+  if (dtype == VC_BF16) {
+    VC_REQUIRE(K % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: K=%d not a multiple of 128", K);
+    if (M <= 64) {
+      VC_REQUIRE(N % SK_NB == 0, VC_ERR_UNSUPPORTED, "gemm: N=%d not a multiple of 64", N);
+      const int want = S;
+      const int kps = int(cdiv(cdiv(K, want), 128) * 128);
+      VC_REQUIRE(cdiv(K, kps) == S, VC_ERR_ARG, "gemm: split count %d inconsistent", S);
+      hipLaunchKernelGGL(gemm_skinny_bf16, dim3(N / SK_NB, S), dim3(256), 0, s, static_cast<const uint16_t*>(X),
+                         static_cast<const uint16_t*>(W), P, M, N, K, kps);
+    } else {
+      VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: prefill tiles use one split");
+      VC_REQUIRE(N % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: N=%d not a multiple of 128", N);
+      hipLaunchKernelGGL(gemm_big_bf16, dim3(N / 128, cdiv(M, 128)), dim3(256), 0, s, static_cast<const uint16_t*>(X),
+                         static_cast<const uint16_t*>(W), P, M, N, K);
+    }
+  } else {
+    VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: fp32 path uses one split");
+    hipLaunchKernelGGL(gemm_f32_tiled, dim3(cdiv(N, 16), cdiv(M, 16)), dim3(256), 0, s, static_cast<const float*>(X),
+                       static_cast<const float*>(W), P, M, N, K);
+  }
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+
+vc_status epilogue(const EpiArgs& a, hipStream_t s) {
+  int units;
+  switch (a.mode) {
+    case EPI_QKV: units = (a.Hq + 2 * a.Hkv) * a.D / 2; break;
+    case EPI_SWIGLU: units = a.N / 2; break;
+    default: units = a.N; break;
+  }
+  VC_REQUIRE(!a.batched || a.M <= EPI_MAX_ROWS, VC_ERR_ARG, "epilogue: too many batched rows");
+  hipLaunchKernelGGL(epilogue_kernel, dim3(cdiv(units, 256), a.M), dim3(256), 0, s, a);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+
+}  // namespace vc

@@ -73,4 +73,4 @@ def test_c1_full_run():
     out, rounds = D.vericache(W, p, w.n_tokens, w.x[0],
                               lambda pr: D.draft_cache_tokdrop(pr, W, keep_total=256, keep_recent=64), pre=pre)
     assert out == ref and len(out) == 64
-    assert sum(len(r.emitted) for r in rounds) >= 64
+    assert 1 + sum(len(r.emitted) for r in rounds) >= 64      # g0 comes from the prefill

@@ -173,16 +173,19 @@ typedef struct {
   void* full_k_host;         /* pinned [L][Hkv][full_cap][D]                            */
   void* full_v_host;
   int32_t full_cap;
+  int32_t* rows;             /* device int32 [>= x + 1]: rows[0] = pending token,        */
+                             /* rows[1 + i] = draft i of the current round              */
 } vc_req;
 
 /* One batched greedy draft step over the compressed caches ("The Core Idea":
  * the compressed-cache model autoregressively produces the draft).  Request r
- * consumes in_tok[r] at position ctx_len + draft_idx, writes its K/V row to tail
- * row n_tail + draft_idx, attends over the compressed region and tail rows
- * [0, n_tail + draft_idx], and writes out_tok[r] = argmax (ties to the lowest
- * id).  in_tok/out_tok: device int32 [n].  logits_opt: device float [n][V] or NULL. */
-vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, const int32_t* in_tok, int32_t* out_tok,
-                        float* logits_opt, void* ws, size_t ws_bytes, hipStream_t s);
+ * consumes rows[draft_idx] at position ctx_len + draft_idx, writes its K/V row to
+ * tail row n_tail + draft_idx, attends over the compressed region (including a
+ * quantizer's residual rows) and tail rows [0, n_tail + draft_idx], and writes
+ * rows[draft_idx + 1] = argmax (ties to the lowest id).  The caller advances
+ * draft_idx.  logits_opt: device float [n][V] or NULL. */
+vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, void* ws, size_t ws_bytes,
+                        hipStream_t s);
 
 /* Verification forward of ONE request ("The Core Idea": predictions for every
  * drafted position plus one bonus, in a single pass against the full cache).
@@ -196,15 +199,16 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
                     void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, hipStream_t s);
 
 /* Accept until the first mismatch ("The Core Idea", pseudocode and worked
- * example).  On `s`: a = first i < x with draft[i] != verified[i] (else x);
- * result[0] = a, result[1 .. a+1] = draft[0..a) followed by verified[a];
- * then the verifier's rows 0..a are copied from vtail into the request's
- * tail at n_tail (overwriting this round's draft rows).  draft: device int32
- * [x]; verified: device int32 [x+1]; result: device int32 [x+2].
- * Does not block and does not change *req: after result[0] is visible on the
- * host, call vc_commit. */
-vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* draft, const int32_t* verified, int32_t x,
-                    const void* vtail_k, const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s);
+ * example).  On `s`: with draft = req->rows + 1, a = first i < x with
+ * draft[i] != verified[i] (else x); result[0] = a, result[1 .. a+1] =
+ * draft[0..a) followed by verified[a] (the correction, or the bonus token when
+ * a == x); req->rows[0] = verified[a] (the next pending token); then the
+ * verifier's rows 0..a are copied from vtail into the request's tail at n_tail
+ * (overwriting this round's draft rows).  verified: device int32 [x+1];
+ * result: device int32 [x+2].  Does not block and does not change *req:
+ * after result[0] is visible on the host, call vc_commit. */
+vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* verified, int32_t x, const void* vtail_k,
+                    const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s);
 
 /* Host half of the commit: enqueue on `copy` the copy of vtail rows 0..a into
  * the pinned full KV at row ctx_len, then advance req->n_tail and

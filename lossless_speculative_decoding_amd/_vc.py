@@ -49,7 +49,8 @@ class CompressLayout(C.Structure):
 class Req(C.Structure):
     _fields_ = [("comp", C.c_void_p), ("cd", C.POINTER(CompressDesc)), ("tail_k", C.c_void_p), ("tail_v", C.c_void_p),
                 ("tail_cap", C.c_int32), ("n_tail", C.c_int32), ("ctx_len", C.c_int32), ("draft_idx", C.c_int32),
-                ("full_k_host", C.c_void_p), ("full_v_host", C.c_void_p), ("full_cap", C.c_int32)]
+                ("full_k_host", C.c_void_p), ("full_v_host", C.c_void_p), ("full_cap", C.c_int32),
+                ("rows", C.c_void_p)]
 
 
 class AttnDesc(C.Structure):
@@ -73,9 +74,9 @@ _SIGS = {
     "vc_compress_layout_of": (_I, [C.POINTER(CompressDesc), C.POINTER(CompressLayout)]),
     "vc_compress_size": (_I, [C.POINTER(CompressDesc), C.POINTER(_S), C.POINTER(_S)]),
     "vc_compress": (_I, [C.POINTER(CompressDesc), _P, _P, _P, _P, _S, _P, _S, _P]),
-    "vc_draft_step": (_I, [_P, C.POINTER(Req), _I, _P, _P, _P, _P, _S, _P]),
+    "vc_draft_step": (_I, [_P, C.POINTER(Req), _I, _P, _P, _S, _P]),
     "vc_verify": (_I, [_P, C.POINTER(Req), _P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
-    "vc_accept": (_I, [_P, C.POINTER(Req), _P, _P, _I, _P, _P, _I, _P, _P]),
+    "vc_accept": (_I, [_P, C.POINTER(Req), _P, _I, _P, _P, _I, _P, _P]),
     "vc_commit": (_I, [_P, C.POINTER(Req), _I, _P, _P, _I, _P, _P]),
     "vc_stage": (_I, [_P, C.POINTER(Req), _P, _P, _I, _I, _I, _P]),
     "vc_prefill": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _P, _I, _P, _S, _P]),

@@ -177,21 +177,26 @@ class Model:
         call("vc_prefill", self.h, ptr(tokens), tokens.numel(), ptr(k_out), ptr(v_out), k_out.shape[-2],
              ptr(q_obs), W, ptr(g0), chunk, ptr(ws), ws.numel(), stream_handle())
 
-    def draft_step(self, reqs, in_tok: torch.Tensor, out_tok: torch.Tensor, ws: torch.Tensor, logits=None):
+    def draft_step(self, reqs, ws: torch.Tensor, logits=None):
         n = len(reqs)
         arr = (Req * n)(*reqs)
-        call("vc_draft_step", self.h, arr, n, ptr(in_tok), ptr(out_tok), ptr(logits), ptr(ws), ws.numel(),
-             stream_handle())
+        call("vc_draft_step", self.h, arr, n, ptr(logits), ptr(ws), ws.numel(), stream_handle())
+        return arr
+
+    def verify_raw(self, req: Req, staged_k: int, staged_v: int, staged_cap: int, tok: int, n_rows: int, out: int,
+                   vtail_k: int, vtail_v: int, vtail_cap: int, ws: torch.Tensor, logits: int | None = None):
+        call("vc_verify", self.h, C.byref(req), staged_k, staged_v, staged_cap, tok, n_rows, out, logits, vtail_k,
+             vtail_v, vtail_cap, ptr(ws), ws.numel(), stream_handle())
 
     def verify(self, req: Req, staged_k, staged_v, tok: torch.Tensor, n_rows: int, out: torch.Tensor, vtail_k,
                vtail_v, ws: torch.Tensor, logits=None):
         scap = staged_k.shape[-2] if staged_k is not None else 0
-        call("vc_verify", self.h, C.byref(req), ptr(staged_k), ptr(staged_v), scap, ptr(tok), n_rows, ptr(out),
-             ptr(logits), ptr(vtail_k), ptr(vtail_v), vtail_k.shape[-2], ptr(ws), ws.numel(), stream_handle())
+        self.verify_raw(req, ptr(staged_k), ptr(staged_v), scap, ptr(tok), n_rows, ptr(out), ptr(vtail_k),
+                        ptr(vtail_v), vtail_k.shape[-2], ws, ptr(logits))
 
-    def accept(self, req: Req, draft, verified, x: int, vtail_k, vtail_v, result: torch.Tensor):
-        call("vc_accept", self.h, C.byref(req), ptr(draft), ptr(verified), x, ptr(vtail_k), ptr(vtail_v),
-             vtail_k.shape[-2], ptr(result), stream_handle())
+    def accept(self, req: Req, verified, x: int, vtail_k, vtail_v, result: torch.Tensor):
+        call("vc_accept", self.h, C.byref(req), ptr(verified), x, ptr(vtail_k), ptr(vtail_v), vtail_k.shape[-2],
+             ptr(result), stream_handle())
 
     def commit(self, req: Req, a: int, vtail_k, vtail_v, after_event=None, copy_stream=None):
         ev = after_event.cuda_event if after_event is not None else None

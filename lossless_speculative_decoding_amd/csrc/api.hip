@@ -403,10 +403,10 @@ vc_status vc_compress(const vc_compress_desc* d, const void* k, const void* v, c
   return compress_run(d, k, v, q_obs, out, out_bytes, ws, ws_bytes, s);
 }
 
-vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, const int32_t* in_tok, int32_t* out_tok,
-                        float* logits_opt, void* ws, size_t ws_bytes, hipStream_t s) {
+vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, void* ws, size_t ws_bytes,
+                        hipStream_t s) {
   if (vc_status st = check_model(m)) return st;
-  VC_REQUIRE(reqs && in_tok && out_tok && ws, VC_ERR_ARG, "vc_draft_step: null argument");
+  VC_REQUIRE(reqs && ws, VC_ERR_ARG, "vc_draft_step: null argument");
   VC_REQUIRE(n > 0 && n <= VC_MAX_BATCH, VC_ERR_ARG, "vc_draft_step: batch %d not in [1, %d]", n, VC_MAX_BATCH);
   const vc_model_desc& d = m->d;
   int max_keys = 1;
@@ -419,8 +419,8 @@ vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, const int32_
     VC_REQUIRE(q.cd->n_layers == d.n_layers && q.cd->n_kv_heads == d.n_kv_heads && q.cd->head_dim == d.head_dim &&
                    q.cd->dtype == d.dtype,
                VC_ERR_ARG, "vc_draft_step: request %d compressed with another shape", r);
-    VC_REQUIRE(q.tail_k && q.tail_v && q.draft_idx >= 0 && q.n_tail >= 0, VC_ERR_ARG, "vc_draft_step: bad request %d",
-               r);
+    VC_REQUIRE(q.tail_k && q.tail_v && q.rows && q.draft_idx >= 0 && q.n_tail >= 0, VC_ERR_ARG,
+               "vc_draft_step: bad request %d", r);
     VC_REQUIRE(q.n_tail + q.draft_idx < q.tail_cap, VC_ERR_CAPACITY, "vc_draft_step: tail of request %d is full", r);
     VC_REQUIRE(q.ctx_len + q.draft_idx < d.max_pos, VC_ERR_CAPACITY, "vc_draft_step: position beyond the RoPE table");
     tail_n[r] = q.n_tail + q.draft_idx + 1;
@@ -430,7 +430,16 @@ vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, const int32_
   VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_draft_step: workspace %zu < %zu bytes", ws_bytes, L.total);
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   vc_status st;
-  if ((st = k_embed(m->w.embed, in_tok, w8 + L.h, n, d.d_model, d.dtype, s))) return st;
+  int32_t* tok_in = reinterpret_cast<int32_t*>(w8 + L.tok);
+  int32_t* tok_out = tok_in + VC_MAX_BATCH;
+  const int32_t* src[VC_MAX_BATCH];
+  int32_t* dst[VC_MAX_BATCH];
+  for (int r = 0; r < n; r++) {
+    src[r] = reqs[r].rows + reqs[r].draft_idx;
+    dst[r] = reqs[r].rows + reqs[r].draft_idx + 1;
+  }
+  if ((st = k_gather_tok(src, n, tok_in, s))) return st;
+  if ((st = k_embed(m->w.embed, tok_in, w8 + L.h, n, d.d_model, d.dtype, s))) return st;
   EpiArgs tmpl{};
   tmpl.batched = 1;
   for (int r = 0; r < n; r++) tmpl.pos[r] = reqs[r].ctx_len + reqs[r].draft_idx;
@@ -455,7 +464,8 @@ vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, const int32_
                            qstride, ob, qstride, part, s);
   };
   if ((st = forward_layers(m, n, w8, L, tmpl, set_kv, attend, s))) return st;
-  return head(m, 0, n, w8, L, out_tok, logits_opt, s);
+  if ((st = head(m, 0, n, w8, L, tok_out, logits_opt, s))) return st;
+  return k_scatter_tok(dst, n, tok_out, s);
 }
 
 vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v, int32_t staged_cap,
@@ -606,16 +616,16 @@ vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out,
   return VC_OK;
 }
 
-vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* draft, const int32_t* verified, int32_t x,
-                    const void* vtail_k, const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s) {
+vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* verified, int32_t x, const void* vtail_k,
+                    const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s) {
   if (vc_status st = check_model(m)) return st;
-  VC_REQUIRE(req && draft && verified && vtail_k && vtail_v && result, VC_ERR_ARG, "vc_accept: null argument");
+  VC_REQUIRE(req && req->rows && verified && vtail_k && vtail_v && result, VC_ERR_ARG, "vc_accept: null argument");
   VC_REQUIRE(x >= 1 && vtail_cap >= x + 1, VC_ERR_ARG, "vc_accept: bad draft length %d", x);
   VC_REQUIRE(req->tail_k && req->tail_v, VC_ERR_ARG, "vc_accept: request without tail");
   VC_REQUIRE(req->n_tail + x + 1 <= req->tail_cap, VC_ERR_CAPACITY, "vc_accept: tail capacity");
   const vc_model_desc& d = m->d;
   vc_status st;
-  if ((st = k_accept(draft, verified, x, result, s))) return st;
+  if ((st = k_accept(req->rows, verified, x, result, s))) return st;
   return k_commit_rows(vtail_k, vtail_v, vtail_cap, req->tail_k, req->tail_v, req->tail_cap, req->n_tail,
                        d.head_dim * m->eb, d.n_layers * d.n_kv_heads, x + 1, result, s);
 }

@@ -7,7 +7,9 @@ namespace vc {
 vc_status k_embed(const void* E, const int32_t* tok, void* h, int M, int d, int dt, hipStream_t s);
 vc_status k_rmsnorm(const void* x, const void* g, void* y, int M, int d, float eps, int dt, hipStream_t s);
 vc_status k_argmax(const float* logits, int M, int V, int32_t* out, hipStream_t s);
-vc_status k_accept(const int32_t* draft, const int32_t* verified, int x, int32_t* result, hipStream_t s);
+vc_status k_accept(int32_t* rows, const int32_t* verified, int x, int32_t* result, hipStream_t s);
+vc_status k_gather_tok(const int32_t* const* src, int n, int32_t* tok, hipStream_t s);
+vc_status k_scatter_tok(int32_t* const* dst, int n, const int32_t* out, hipStream_t s);
 vc_status k_commit_rows(const void* vk, const void* vv, int vcap, void* tk, void* tv, int tcap, int n_tail,
                         int row_bytes, int n_lh, int max_rows, const int32_t* result, hipStream_t s);
 vc_status k_rope_table(float* tab, int max_pos, int D, double theta, hipStream_t s);

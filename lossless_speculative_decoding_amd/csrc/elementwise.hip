@@ -75,9 +75,11 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V
   if (tid == 0) out[r] = bi[0];
 }
 
-// a = first i < x with draft[i] != verified[i] (else x); result = [a, draft[0..a), verified[a]].
-__global__ void accept_kernel(const int32_t* draft, const int32_t* verified, int x, int32_t* result) {
+// a = first i < x with draft[i] != verified[i] (else x); result = [a, draft[0..a), verified[a]];
+// rows[0] = verified[a] (draft = rows + 1 is read completely before rows[0] is written).
+__global__ void accept_kernel(int32_t* rows, const int32_t* verified, int x, int32_t* result) {
   if (threadIdx.x != 0) return;
+  const int32_t* draft = rows + 1;
   int a = x;
   for (int i = 0; i < x; i++) {
     if (draft[i] != verified[i]) {
@@ -87,7 +89,24 @@ __global__ void accept_kernel(const int32_t* draft, const int32_t* verified, int
   }
   result[0] = a;
   for (int i = 0; i < a; i++) result[1 + i] = draft[i];
-  result[1 + a] = verified[a];
+  const int32_t next = verified[a];
+  result[1 + a] = next;
+  rows[0] = next;
+}
+
+// tok[r] = *src[r] and, after the step, *dst[r] = out[r] (per-request token slots).
+struct TokPtrs {
+  const int32_t* src[VC_MAX_BATCH];
+  int32_t* dst[VC_MAX_BATCH];
+  int32_t n;
+};
+__global__ void gather_tok_kernel(const TokPtrs p, int32_t* tok) {
+  const int r = threadIdx.x;
+  if (r < p.n) tok[r] = *p.src[r];
+}
+__global__ void scatter_tok_kernel(const TokPtrs p, const int32_t* out) {
+  const int r = threadIdx.x;
+  if (r < p.n) *p.dst[r] = out[r];
 }
 
 // Copy rows 0..result[0] of vtail into tail at row n_tail, for every (layer, head).
@@ -140,8 +159,24 @@ vc_status k_argmax(const float* logits, int M, int V, int32_t* out, hipStream_t 
   VC_LAUNCH_CHECK();
   return VC_OK;
 }
-vc_status k_accept(const int32_t* draft, const int32_t* verified, int x, int32_t* result, hipStream_t s) {
-  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, s, draft, verified, x, result);
+vc_status k_accept(int32_t* rows, const int32_t* verified, int x, int32_t* result, hipStream_t s) {
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, s, rows, verified, x, result);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+vc_status k_gather_tok(const int32_t* const* src, int n, int32_t* tok, hipStream_t s) {
+  TokPtrs p{};
+  p.n = n;
+  for (int r = 0; r < n; r++) p.src[r] = src[r];
+  hipLaunchKernelGGL(gather_tok_kernel, dim3(1), dim3(64), 0, s, p, tok);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+vc_status k_scatter_tok(int32_t* const* dst, int n, const int32_t* out, hipStream_t s) {
+  TokPtrs p{};
+  p.n = n;
+  for (int r = 0; r < n; r++) p.dst[r] = dst[r];
+  hipLaunchKernelGGL(scatter_tok_kernel, dim3(1), dim3(64), 0, s, p, out);
   VC_LAUNCH_CHECK();
   return VC_OK;
 }

@@ -1,0 +1,287 @@
+"""Host-side VeriCache scheduler over the C ABI.
+
+Per request ("Verifying Without Giving Back the Speedup", VeriCache: Making
+Lossy KV Compression Exact): the compressed cache and a tail of exact rows
+stay on the GPU; the full cache lives in pinned host memory and is staged into
+one of two device slots on a copy stream only for verification.  Requests
+start drafting at staggered ticks (request r joins after floor(r * x / B)
+ticks, the study note's "10 requests, x = 30: one verification every 3 draft
+rounds"), so one request's transfer and verification overlap the others'
+drafting.  A request's staging is issued `lead` ticks before its draft ends,
+lead = ceil(t_copy / t_tick) (the guide's drafting-horizon sizing rule);
+verification never blocks the compute stream on a copy: the host polls the
+copy event and keeps drafting other requests until the slot is ready.
+
+All arithmetic runs in libvc.so; this module only sequences calls, owns the
+buffers (torch allocations) and moves token ids it has already received.
+"""
+from __future__ import annotations
+
+import math
+import time
+from dataclasses import dataclass, field
+
+import torch
+
+import synth
+
+from . import binding as B
+from ._vc import Req
+
+DRAFT, WAIT_SLOT, ACCEPTING, DONE = range(4)
+
+
+def make_weights(shape, device="cuda", seed: int = 0) -> dict:
+    """Random-init weights in the library layout, generated on the GPU from the
+    seeded recipe (Xavier-uniform; norm gains 1)."""
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    L, d, Hq, Hkv, D, F, V = (shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                              shape.ffn, shape.vocab)
+    e = lambda *sh: torch.empty(*sh, dtype=dt, device=device)
+    W = {"embed": e(V, d), "lm_head": e(V, d), "norm_final": e(d), "norm_attn": e(L, d), "norm_ffn": e(L, d),
+         "w_qkv": e(L, (Hq + 2 * Hkv) * D, d), "w_o": e(L, d, Hq * D), "w_gu": e(L, 2 * F, d),
+         "w_down": e(L, d, F)}
+    B.synth_xavier(W["embed"], synth.S_EMBED, d, V, seed)
+    B.synth_xavier(W["lm_head"], synth.S_LMHEAD, d, V, seed)
+    for k in ("norm_final", "norm_attn", "norm_ffn"):
+        B.synth_fill(W[k], 1.0)
+    for l in range(L):
+        st = lambda t: synth.layer_stream(l, t)
+        q0, k0, v0 = 0, Hq * D, (Hq + Hkv) * D
+        B.synth_xavier(W["w_qkv"][l, q0:k0], st(synth.T_WQ), d, Hq * D, seed)
+        B.synth_xavier(W["w_qkv"][l, k0:v0], st(synth.T_WK), d, Hkv * D, seed)
+        B.synth_xavier(W["w_qkv"][l, v0:], st(synth.T_WV), d, Hkv * D, seed)
+        B.synth_xavier(W["w_o"][l], st(synth.T_WO), Hq * D, d, seed)
+        B.synth_xavier(W["w_gu"][l, :F], st(synth.T_W1), d, F, seed)
+        B.synth_xavier(W["w_gu"][l, F:], st(synth.T_W3), d, F, seed)
+        B.synth_xavier(W["w_down"][l], st(synth.T_W2), F, d, seed)
+    return W
+
+
+def compress_spec_desc(spec, shape, T: int, src_cap: int):
+    dt = B.VC_BF16 if shape.dtype == "bf16" else B.VC_F32
+    if spec.kind == "tokdrop":
+        return B.compress_desc(B.VC_TOKDROP, shape.n_layers, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, T, dt,
+                               src_cap=src_cap, keep_total=T // spec.ratio, keep_recent=spec.keep_recent,
+                               obs_window=spec.obs_window)
+    if spec.kind == "quant":
+        return B.compress_desc(B.VC_QUANT, shape.n_layers, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, T, dt,
+                               src_cap=src_cap, bits=spec.bits, group=spec.group)
+    raise ValueError(spec.kind)
+
+
+@dataclass
+class Request:
+    idx: int
+    T: int
+    x: int
+    n_tokens: int
+    cd: object = None
+    comp: torch.Tensor = None
+    tail_k: torch.Tensor = None
+    tail_v: torch.Tensor = None
+    full_k: torch.Tensor = None        # pinned host
+    full_v: torch.Tensor = None
+    rows: torch.Tensor = None          # device int32 [x + 1]
+    vtail_k: torch.Tensor = None
+    vtail_v: torch.Tensor = None
+    verified: torch.Tensor = None
+    result: torch.Tensor = None
+    result_host: torch.Tensor = None
+    req: Req = None
+    emitted: list = field(default_factory=list)
+    accepts: list = field(default_factory=list)
+    phase: int = DRAFT
+    start_tick: int = 0
+    slot: int = -1
+    stage_ev: object = None
+    acc_ev: object = None
+
+
+class Engine:
+    """Owns a vc_model, its workspaces and the per-request device/host buffers."""
+
+    def __init__(self, model: B.Model, spec, chunk: int = 1024, device="cuda"):
+        self.m = model
+        self.spec = spec
+        self.shape = model.shape
+        self.dt = torch.bfloat16 if self.shape.dtype == "bf16" else torch.float32
+        self.chunk = chunk
+        self.device = device
+        self.reqs: list[Request] = []
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.slots = []
+        self.slot_free_ev = []
+        self.ws_draft = None
+        self.ws_verify = None
+
+    # ------------------------------------------------------------ setup (untimed)
+    def add_request(self, prompt: torch.Tensor, x: int, n_tokens: int, keep_prefill_kv: bool = False):
+        s = self.shape
+        T = int(prompt.numel())
+        L, Hkv, D, Hq = s.n_layers, s.n_kv_heads, s.head_dim, s.n_q_heads
+        r = Request(idx=len(self.reqs), T=T, x=x, n_tokens=n_tokens)
+        full_cap = T + n_tokens + x + 2
+        kd = torch.empty(L, Hkv, T, D, dtype=self.dt, device=self.device)
+        vd = torch.empty_like(kd)
+        W = min(self.spec.obs_window, T)
+        q_obs = torch.empty(L, W, Hq, D, dtype=self.dt, device=self.device)
+        g0 = torch.empty(1, dtype=torch.int32, device=self.device)
+        ws = self.m.workspace(min(self.chunk, T), T)
+        self.m.prefill(prompt, kd, vd, q_obs, W, g0, ws, min(self.chunk, T))
+        del ws
+        r.cd = compress_spec_desc(self.spec, s, T, T)
+        r.comp = B.vc_compress(r.cd, kd, vd, q_obs)
+        r.full_k = torch.empty(L, Hkv, full_cap, D, dtype=self.dt, pin_memory=True)
+        r.full_v = torch.empty(L, Hkv, full_cap, D, dtype=self.dt, pin_memory=True)
+        r.full_k[:, :, :T].copy_(kd)
+        r.full_v[:, :, :T].copy_(vd)
+        tail_cap = n_tokens + x + 2
+        r.tail_k = torch.empty(L, Hkv, tail_cap, D, dtype=self.dt, device=self.device)
+        r.tail_v = torch.empty_like(r.tail_k)
+        r.rows = torch.zeros(x + 1, dtype=torch.int32, device=self.device)
+        r.rows[:1].copy_(g0)
+        r.vtail_k = torch.empty(L, Hkv, x + 1, D, dtype=self.dt, device=self.device)
+        r.vtail_v = torch.empty_like(r.vtail_k)
+        r.verified = torch.empty(x + 1, dtype=torch.int32, device=self.device)
+        r.result = torch.empty(x + 2, dtype=torch.int32, device=self.device)
+        r.result_host = torch.empty(x + 2, dtype=torch.int32, pin_memory=True)
+        r.req = Req(comp=r.comp.data_ptr(), cd=None, tail_k=r.tail_k.data_ptr(), tail_v=r.tail_v.data_ptr(),
+                    tail_cap=tail_cap, n_tail=0, ctx_len=T, draft_idx=0, full_k_host=r.full_k.data_ptr(),
+                    full_v_host=r.full_v.data_ptr(), full_cap=full_cap, rows=r.rows.data_ptr())
+        import ctypes as C
+        r.req.cd = C.pointer(r.cd)
+        torch.cuda.synchronize()
+        r.emitted = [int(g0.item())]
+        if keep_prefill_kv:
+            r.prefill_kv = (kd, vd)
+        self.reqs.append(r)
+        return r
+
+    def _alloc(self):
+        s = self.shape
+        n = len(self.reqs)
+        max_ctx = max(r.T + r.n_tokens + r.x + 2 for r in self.reqs)
+        max_x = max(r.x for r in self.reqs)
+        self.ws_draft = self.m.workspace(min(n, 16), max_ctx)
+        self.ws_verify = self.m.workspace(max_x + 1, max_ctx)
+        L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
+        n_slots = min(2, n)
+        if not self.slots:
+            self.slots = [(torch.empty(L, Hkv, max_ctx, D, dtype=self.dt, device=self.device),
+                           torch.empty(L, Hkv, max_ctx, D, dtype=self.dt, device=self.device)) for _ in range(n_slots)]
+            self.slot_free_ev = [None] * n_slots
+            self.slot_owner = [None] * n_slots
+
+    # ------------------------------------------------------------ the VeriCache loop
+    def run(self, lead: int | None = None, stagger: bool = True, trace: list | None = None):
+        """Decode every request to its n_tokens; returns wall seconds of the decode phase."""
+        self._alloc()
+        reqs = self.reqs
+        n = len(reqs)
+        xs = [r.x for r in reqs]
+        for r in reqs:
+            r.start_tick = (r.idx * r.x) // n if stagger else 0
+            r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
+        if lead is None:
+            lead = 2
+        cs = torch.cuda.current_stream()
+        tick = 0
+        t0 = time.perf_counter()
+        while any(r.phase != DONE for r in reqs):
+            # 1. finish accepts whose result reached the host
+            for r in reqs:
+                if r.phase == ACCEPTING and r.acc_ev.query():
+                    a = int(r.result_host[0])
+                    toks = r.result_host[1:a + 2].tolist()
+                    r.emitted += toks
+                    r.accepts.append(a)
+                    self.m.commit(r.req, a, r.vtail_k, r.vtail_v, after_event=r.acc_ev, copy_stream=self.copy_stream)
+                    r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
+            # 2. stage full KV for requests close to the end of their draft
+            for r in reqs:
+                if r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= r.x - lead and tick >= r.start_tick:
+                    self._try_stage(r)
+            # 3. one batched draft step for every drafting request
+            active = [r for r in reqs if r.phase == DRAFT and tick >= r.start_tick and r.req.draft_idx < r.x]
+            for k in range(0, len(active), 16):
+                grp = active[k:k + 16]
+                self.m.draft_step([r.req for r in grp], self.ws_draft)
+                for r in grp:
+                    r.req.draft_idx += 1
+                    if r.req.draft_idx == r.x:
+                        r.phase = WAIT_SLOT
+            # 4. verify requests whose drafts are complete and whose slot is staged
+            for r in reqs:
+                if r.phase == WAIT_SLOT:
+                    if r.slot < 0:
+                        self._try_stage(r)
+                    if r.slot >= 0 and r.stage_ev.query():
+                        self._verify(r, cs)
+            if trace is not None:
+                trace.append((tick, [r.phase for r in reqs], [r.req.draft_idx for r in reqs]))
+            tick += 1
+            if not active and all(r.phase in (ACCEPTING, WAIT_SLOT, DONE) for r in reqs):
+                time.sleep(0)  # nothing to draft: wait for copies / accepts
+        torch.cuda.synchronize()
+        self.copy_stream.synchronize()
+        for r in reqs:
+            r.emitted = r.emitted[: r.n_tokens]
+        return time.perf_counter() - t0
+
+    def _try_stage(self, r: Request):
+        for i in range(len(self.slots)):
+            if self.slot_owner[i] is None and (self.slot_free_ev[i] is None or self.slot_free_ev[i].query()):
+                self.slot_owner[i] = r.idx
+                r.slot = i
+                sk, sv = self.slots[i]
+                self.m.stage(r.req, sk, sv, 0, self.shape.n_layers, copy_stream=self.copy_stream)
+                ev = torch.cuda.Event()
+                ev.record(self.copy_stream)
+                r.stage_ev = ev
+                return True
+        return False
+
+    def _verify(self, r: Request, cs):
+        sk, sv = self.slots[r.slot]
+        self.m.verify(r.req, sk, sv, r.rows, r.x + 1, r.verified, r.vtail_k, r.vtail_v, self.ws_verify)
+        ev_free = torch.cuda.Event()
+        ev_free.record(cs)
+        self.slot_free_ev[r.slot] = ev_free
+        self.slot_owner[r.slot] = None
+        r.slot = -1
+        self.m.accept(r.req, r.verified, r.x, r.vtail_k, r.vtail_v, r.result)
+        r.result_host.copy_(r.result, non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(cs)
+        r.acc_ev = ev
+        r.phase = ACCEPTING
+
+
+# ---------------------------------------------------------------- greedy baselines
+def greedy_resident(model: B.Model, prompt: torch.Tensor, n_tokens: int, chunk: int = 1024, device="cuda"):
+    """Full-KV greedy decoding with the cache resident in HBM: each step is
+    vc_verify with one row, writing its K/V straight into the cache."""
+    s = model.shape
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    T = int(prompt.numel())
+    cap = T + n_tokens
+    L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
+    kd = torch.empty(L, Hkv, cap, D, dtype=dt, device=device)
+    vd = torch.empty_like(kd)
+    out = torch.empty(n_tokens, dtype=torch.int32, device=device)
+    ws = model.workspace(min(chunk, T), cap)
+    model.prefill(prompt, kd, vd, None, 0, out[:1], ws, min(chunk, T))
+    req = Req(ctx_len=T)
+    eb = 2 if s.dtype == "bf16" else 4
+    row = D * eb
+    t0 = None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(1, n_tokens):
+        req.ctx_len = T + i - 1
+        off = req.ctx_len * row
+        model.verify_raw(req, kd.data_ptr(), vd.data_ptr(), cap, out.data_ptr() + 4 * (i - 1), 1,
+                         out.data_ptr() + 4 * i, kd.data_ptr() + off, vd.data_ptr() + off, cap, ws)
+    torch.cuda.synchronize()
+    return out.tolist(), time.perf_counter() - t0, (kd, vd)

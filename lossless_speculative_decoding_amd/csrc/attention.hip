@@ -13,9 +13,12 @@
 // 32 keys of a chunk are enumerated as {4g..4g+3, 16+4g..16+4g+3}; V^T is read
 // in that same key order, so no cross-lane shuffle of P is needed.
 // The P.V product runs in fp16: V is converted from bf16 while it is staged
-// (exact for |v| in [2^-14, 65504]) and P is rounded to fp16 after scaling by
-// 2^10 (P <= 1), which keeps 11 significant bits of every weight instead of
-// bf16's 8; QK^T stays bf16 x bf16 with exact products.
+// (exact for |v| in [2^-14, 65504]) and P * 2^10 (P <= 1) is carried as an fp16
+// hi/lo pair (hi = fp16(P), lo = fp16(P - hi), two MFMAs), which keeps about
+// 22 significant bits of every weight; QK^T is bf16 x bf16 with exact products.
+// Attention outputs then agree with a float64 evaluation to ~1e-6, so the
+// bf16 rounding of the output (and of everything downstream) almost never
+// lands on the other side of a rounding boundary than the exact value does.
 #include "attention.h"
 
 namespace vc {
@@ -193,11 +196,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
     // ---- O^T += V^T P^T over 2 chunks of 32 keys
 #pragma unroll
     for (int kc = 0; kc < 2; kc++) {
-      u32x4 pb;
-      pb.x = pack_h2(sacc[2 * kc][0] * P_SCALE, sacc[2 * kc][1] * P_SCALE);
-      pb.y = pack_h2(sacc[2 * kc][2] * P_SCALE, sacc[2 * kc][3] * P_SCALE);
-      pb.z = pack_h2(sacc[2 * kc + 1][0] * P_SCALE, sacc[2 * kc + 1][1] * P_SCALE);
-      pb.w = pack_h2(sacc[2 * kc + 1][2] * P_SCALE, sacc[2 * kc + 1][3] * P_SCALE);
+      uint32_t h[4], lw[4];
+      split_h2(sacc[2 * kc][0] * P_SCALE, sacc[2 * kc][1] * P_SCALE, h[0], lw[0]);
+      split_h2(sacc[2 * kc][2] * P_SCALE, sacc[2 * kc][3] * P_SCALE, h[1], lw[1]);
+      split_h2(sacc[2 * kc + 1][0] * P_SCALE, sacc[2 * kc + 1][1] * P_SCALE, h[2], lw[2]);
+      split_h2(sacc[2 * kc + 1][2] * P_SCALE, sacc[2 * kc + 1][3] * P_SCALE, h[3], lw[3]);
+      const u32x4 pb = u32x4{h[0], h[1], h[2], h[3]};
+      const u32x4 pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
         const uint16_t* vrow = Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 4 * grp;
@@ -205,6 +210,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
         const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 16);
         const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
         oacc[dt] = mfma_f16(va, pb, oacc[dt]);
+        oacc[dt] = mfma_f16(va, pl, oacc[dt]);
       }
     }
   }

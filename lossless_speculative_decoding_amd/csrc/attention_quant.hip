@@ -9,12 +9,11 @@
 // computing wave instead:
 //     q . k_t       = sum_d (q_d s_gd) c_td + sum_d q_d z_gd        (K: scale/zero per channel and token group)
 //     sum_t p_t v_t = sum_t (p_t s_t) c_t  + sum_t p_t z_t          (V: scale/zero per token and channel group)
-// so the MFMA operands are Q' = q*s, the codes, and P' = p*s (fp16, scaled by
-// 2^10 to stay out of the fp16 subnormal range).  Two details keep the fold
-// accurate to a few 1e-4: codes are centred (c - 2^(b-1), zero moves to
-// z + 2^(b-1) s), so the folded sum no longer cancels against a large zero
-// term; and Q' is carried as an fp16 hi/lo pair (Q' = hi + lo, two MFMAs),
-// which leaves about 22 significant bits in every score.
+// so the MFMA operands are Q' = q*s, the codes, and P' = p*s (scaled by 2^10
+// to stay out of the fp16 subnormal range).  Codes are centred (c - 2^(b-1),
+// zero moves to z + 2^(b-1) s) so the folded sum does not cancel against a
+// large zero term, and Q' and P' are each carried as an fp16 hi/lo pair (two
+// MFMAs), which leaves about 22 significant bits in every score and weight.
 //
 // Within each group of 8 (4-bit) or 16 (2-bit) codes the conversion yields the
 // codes in the order [0,4,1,5,2,6,3,7] (resp. [0,8,1,9,...,7,15]); LDS
@@ -310,13 +309,13 @@ __global__ __launch_bounds__(256) void attn_quant_kernel(const QuantArgs args) {
         pv[e] = sacc[2 * kc2 + (e >> 2)][e & 3] * P_SCALE;
       }
       // P' for each channel group of V (group 1 only exists when the V group is 64 channels)
-      uint32_t w0[4], w1[4];
+      uint32_t w0[4], w1[4], l0[4], l1[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; e2++) {
         const int p0 = pos[2 * e2], p1 = pos[2 * e2 + 1];
         const float x0 = pv[2 * e2], x1 = pv[2 * e2 + 1];
-        w0[e2] = pack_h2(x0 * vsc[p0][0], x1 * vsc[p1][0]);
-        w1[e2] = pack_h2(x0 * vsc[p0][1], x1 * vsc[p1][1]);
+        split_h2(x0 * vsc[p0][0], x1 * vsc[p1][0], w0[e2], l0[e2]);
+        split_h2(x0 * vsc[p0][1], x1 * vsc[p1][1], w1[e2], l1[e2]);
         vb[0] = fmaf(x0, vzr[p0][0], vb[0]);
         vb[0] = fmaf(x1, vzr[p1][0], vb[0]);
         vb[1] = fmaf(x0, vzr[p0][1], vb[1]);
@@ -324,12 +323,16 @@ __global__ __launch_bounds__(256) void attn_quant_kernel(const QuantArgs args) {
       }
       const u32x4 pb0 = u32x4{w0[0], w0[1], w0[2], w0[3]};
       const u32x4 pb1 = two_groups ? u32x4{w1[0], w1[1], w1[2], w1[3]} : pb0;
+      const u32x4 pl0 = u32x4{l0[0], l0[1], l0[2], l0[3]};
+      const u32x4 pl1 = two_groups ? u32x4{l1[0], l1[1], l1[2], l1[3]} : pl0;
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
         const uint16_t* vrow = Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc2 + 4 * grp;
         const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 16);
-        oacc[dt] = mfma_f16(u32x4{v0.x, v0.y, v1.x, v1.y}, dt < 4 ? pb0 : pb1, oacc[dt]);
+        const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
+        oacc[dt] = mfma_f16(va, dt < 4 ? pb0 : pb1, oacc[dt]);
+        oacc[dt] = mfma_f16(va, dt < 4 ? pl0 : pl1, oacc[dt]);
       }
     }
   }

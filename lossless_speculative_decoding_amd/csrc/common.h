@@ -58,6 +58,13 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
 }
+// two floats -> fp16 hi pair and fp16 lo pair with a ~= hi + lo (about 22 significant bits)
+__device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  hi = __builtin_bit_cast(uint32_t, h2{ha, hb});
+  lo = __builtin_bit_cast(uint32_t, h2{(_Float16)(a - float(ha)), (_Float16)(b - float(hb))});
+}
 
 template <typename T>
 __device__ __forceinline__ T bitcast(const auto& x) {

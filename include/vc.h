@@ -217,6 +217,16 @@ vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* verified, int
 vc_status vc_commit(vc_model* m, vc_req* req, int32_t a, const void* vtail_k, const void* vtail_v, int32_t vtail_cap,
                     hipEvent_t after, hipStream_t copy);
 
+/* Pinned host memory of exactly `bytes` bytes (hipHostMalloc) for a full KV
+ * cache, and its release.  Setup-time helpers, not for the hot path. */
+vc_status vc_host_alloc(size_t bytes, void** out_host);
+vc_status vc_host_free(void* host);
+
+/* Offload (setup): copy rows [0, T) of a device cache [L][Hkv][src_cap][D] into
+ * the request's pinned full KV at rows [0, T), on `s` (D2H, hipMemcpy2DAsync). */
+vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const void* v_dev, int32_t src_cap, int32_t T,
+                     hipStream_t s);
+
 /* Stage the request's full KV rows [0, ctx_len) from pinned host memory into a
  * device slot [L][Hkv][slot_cap][D] on `copy` (SDMA, hipMemcpy2DAsync), layers
  * [l0, l1). */
@@ -267,6 +277,24 @@ vc_status vc_attn_verify(const vc_attn_desc* d, int32_t n, const void* q, const 
                          void* out, void* ws, size_t ws_bytes, hipStream_t s);
 
 vc_status vc_attn_ws_size(const vc_attn_desc* d, int32_t n, int32_t rows, int32_t max_keys, size_t* bytes);
+
+/* ------------------------------------------------------------------------
+ * Live measurement of the draft-attention kernels (the decode attention over
+ * compressed caches, the HBM-bound core of every draft step).  When enabled,
+ * each vc_draft_step / vc_attn_draft records a HIP event pair on its stream
+ * around the attention-partial launches of every layer, together with the
+ * algorithmic bytes those launches must move (codes, scales and zeros, or
+ * kept rows, plus exact tail rows, queries and split partials).
+ * vc_profile_read synchronises the recorded events and returns the totals;
+ * it clears the record.  Not thread-safe; intended for benchmarks.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t launches;   /* attention-partial launch groups timed              */
+  double total_ms;    /* summed event time of those launches               */
+  double bytes;       /* summed algorithmic bytes                          */
+} vc_profile_stats;
+vc_status vc_profile_enable(int32_t on);
+vc_status vc_profile_read(vc_profile_stats* out);
 
 /* ------------------------------------------------------------------------
  * Seeded synthetic inputs (not part of the method): the counter-based

@@ -57,6 +57,10 @@ class AttnDesc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_q_heads", "n_kv_heads", "head_dim", "dtype", "split_len", "out_dtype")]
 
 
+class ProfileStats(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("bytes", C.c_double)]
+
+
 class AttnDraftReq(C.Structure):
     _fields_ = [("comp", C.c_void_p), ("cd", C.POINTER(CompressDesc)), ("tail_k", C.c_void_p),
                 ("tail_v", C.c_void_p), ("tail_cap", C.c_int32), ("n_tail", C.c_int32)]
@@ -88,6 +92,11 @@ _SIGS = {
     "vc_synth_normal_heads": (_I, [_P, _I, _I, _I, _I, C.c_uint32, C.c_uint32, _P, _I, C.c_float, _P]),
     "vc_synth_ids": (_I, [_P, C.c_int64, C.c_uint32, C.c_uint32, _I, _P]),
     "vc_synth_fill": (_I, [_P, _I, C.c_int64, C.c_float, _P]),
+    "vc_profile_enable": (_I, [_I]),
+    "vc_host_alloc": (_I, [_S, C.POINTER(_P)]),
+    "vc_host_free": (_I, [_P]),
+    "vc_offload": (_I, [_P, C.POINTER(Req), _P, _P, _I, _I, _P]),
+    "vc_profile_read": (_I, [C.POINTER(ProfileStats)]),
 }
 
 if not os.path.exists(LIB_PATH):

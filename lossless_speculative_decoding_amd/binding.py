@@ -12,11 +12,12 @@ import torch
 
 from . import _vc
 from ._vc import (VC_BF16, VC_F32, VC_QUANT, VC_TOKDROP, AttnDesc, AttnDraftReq, CompressDesc, CompressLayout,
-                  ModelDesc, Req, Weights, call)
+                  ModelDesc, ProfileStats, Req, Weights, call)
 
 __all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "CompressDesc", "Req", "Model", "compress_desc",
            "compress_layout", "vc_compress", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
-           "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes"]
+           "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes",
+           "profile_enable", "profile_read", "HostBuffer"]
 
 
 def stream_handle(s: torch.cuda.Stream | None = None) -> int:
@@ -203,6 +204,44 @@ class Model:
         call("vc_commit", self.h, C.byref(req), a, ptr(vtail_k), ptr(vtail_v), vtail_k.shape[-2], ev,
              stream_handle(copy_stream))
 
+    def offload(self, req: Req, k_dev, v_dev, T: int):
+        call("vc_offload", self.h, C.byref(req), ptr(k_dev), ptr(v_dev), k_dev.shape[-2], T, stream_handle())
+
     def stage(self, req: Req, slot_k, slot_v, l0: int, l1: int, copy_stream=None):
         call("vc_stage", self.h, C.byref(req), ptr(slot_k), ptr(slot_v), slot_k.shape[-2], l0, l1,
              stream_handle(copy_stream))
+
+
+# ---------------------------------------------------------------- live kernel timing
+def profile_enable(on: bool = True):
+    call("vc_profile_enable", 1 if on else 0)
+
+
+def profile_read() -> dict:
+    st = ProfileStats()
+    call("vc_profile_read", C.byref(st))
+    return {"launches": st.launches, "ms": st.total_ms, "bytes": st.bytes}
+
+
+class HostBuffer:
+    """Pinned host memory of an exact size (vc_host_alloc), freed with the object."""
+
+    def __init__(self, nbytes: int):
+        p = C.c_void_p()
+        call("vc_host_alloc", nbytes, C.byref(p))
+        self.ptr = p.value
+        self.nbytes = nbytes
+
+    def data_ptr(self) -> int:
+        return self.ptr
+
+    def free(self):
+        if self.ptr:
+            call("vc_host_free", self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstring>
 #include <functional>
+#include <vector>
 
 #include "attention.h"
 #include "compress.h"
@@ -27,6 +28,28 @@ void set_error(const char* fmt, ...) {
 }  // namespace vc
 
 using namespace vc;
+
+namespace {
+// draft-attention timing record (vc_profile_*)
+struct ProfRec {
+  hipEvent_t a, b;
+  double bytes;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
 
 struct vc_model {
   vc_model_desc d;
@@ -300,6 +323,27 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     ar.n_splits = ts_n[r];
     aa.max_splits = std::max(aa.max_splits, ts_n[r]);
   }
+  // algorithmic bytes of the partial launches (for vc_profile_read)
+  double bytes = 0;
+  for (int r = 0; r < n; r++) {
+    const CompView& v = views[r];
+    const double row = double(D) * (dtype == VC_BF16 ? 2 : 4);
+    if (v.kind == VC_QUANT) {
+      const double ng = v.tq / v.group, nh = D / v.group;
+      bytes += double(Hkv) * (2.0 * v.tq * D * v.bits / 8 + 2.0 * ng * D * 2 + 2.0 * v.tq * nh * 2);
+      bytes += double(Hkv) * (v.n_resid + tail_n[r]) * row * 2;
+    } else {
+      bytes += double(Hkv) * (v.kk + tail_n[r]) * row * 2;
+    }
+    bytes += double(Hq) * row;                                       // query
+    bytes += double(Hq) * (qs_n[r] + ts_n[r]) * (D + 2) * 4.0;        // partials written
+  }
+  ProfRec rec{nullptr, nullptr, bytes};
+  if (g_prof_on) {
+    rec.a = prof_event();
+    rec.b = prof_event();
+    if (rec.a) VC_HIP(hipEventRecord(rec.a, s));
+  }
   vc_status st;
   if (qa.n_req > 0) {
     qa.Hq = Hq;
@@ -313,6 +357,10 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     if ((st = launch_attn_quant(qa, s))) return st;
   }
   if ((st = launch_attn(aa, dtype, s))) return st;
+  if (g_prof_on && rec.a && rec.b) {
+    VC_HIP(hipEventRecord(rec.b, s));
+    g_prof.push_back(rec);
+  }
   CombineArgs c{};
   c.n_req = n;
   c.n_rows = 1;
@@ -334,6 +382,28 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
 extern "C" {
 
 const char* vc_last_error(void) { return g_err.c_str(); }
+
+vc_status vc_profile_enable(int32_t on) {
+  g_prof_on = on != 0;
+  return VC_OK;
+}
+
+vc_status vc_profile_read(vc_profile_stats* out) {
+  VC_REQUIRE(out != nullptr, VC_ERR_ARG, "vc_profile_read: null output");
+  *out = vc_profile_stats{0, 0.0, 0.0};
+  for (ProfRec& r : g_prof) {
+    VC_HIP(hipEventSynchronize(r.b));
+    float ms = 0.f;
+    VC_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    out->launches += 1;
+    out->total_ms += ms;
+    out->bytes += r.bytes;
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  return VC_OK;
+}
 int32_t vc_abi_version(void) { return 1; }
 
 vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStream_t s, vc_model** out) {
@@ -670,6 +740,33 @@ vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, i
                           size_t(req->full_cap) * row, size_t(req->ctx_len) * row, height, hipMemcpyHostToDevice, copy));
   VC_HIP(hipMemcpy2DAsync(mptr(slot_v, lo_dst), size_t(slot_cap) * row, cptr(req->full_v_host, lo_src),
                           size_t(req->full_cap) * row, size_t(req->ctx_len) * row, height, hipMemcpyHostToDevice, copy));
+  return VC_OK;
+}
+
+vc_status vc_host_alloc(size_t bytes, void** out_host) {
+  VC_REQUIRE(out_host != nullptr && bytes > 0, VC_ERR_ARG, "vc_host_alloc: bad arguments");
+  *out_host = nullptr;
+  VC_HIP(hipHostMalloc(out_host, bytes, hipHostMallocDefault));
+  return VC_OK;
+}
+
+vc_status vc_host_free(void* host) {
+  if (host) VC_HIP(hipHostFree(host));
+  return VC_OK;
+}
+
+vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const void* v_dev, int32_t src_cap, int32_t T,
+                     hipStream_t s) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(req && k_dev && v_dev && req->full_k_host && req->full_v_host, VC_ERR_ARG, "vc_offload: null argument");
+  VC_REQUIRE(T > 0 && T <= src_cap && T <= req->full_cap, VC_ERR_CAPACITY, "vc_offload: bad row counts");
+  const vc_model_desc& d = m->d;
+  const size_t row = size_t(d.head_dim) * m->eb;
+  const size_t height = size_t(d.n_layers) * d.n_kv_heads;
+  VC_HIP(hipMemcpy2DAsync(req->full_k_host, size_t(req->full_cap) * row, k_dev, size_t(src_cap) * row, size_t(T) * row,
+                          height, hipMemcpyDeviceToHost, s));
+  VC_HIP(hipMemcpy2DAsync(req->full_v_host, size_t(req->full_cap) * row, v_dev, size_t(src_cap) * row, size_t(T) * row,
+                          height, hipMemcpyDeviceToHost, s));
   return VC_OK;
 }
 

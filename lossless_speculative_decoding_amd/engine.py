@@ -80,8 +80,8 @@ class Request:
     comp: torch.Tensor = None
     tail_k: torch.Tensor = None
     tail_v: torch.Tensor = None
-    full_k: torch.Tensor = None        # pinned host
-    full_v: torch.Tensor = None
+    full_k: object = None              # pinned host (HostBuffer)
+    full_v: object = None
     rows: torch.Tensor = None          # device int32 [x + 1]
     vtail_k: torch.Tensor = None
     vtail_v: torch.Tensor = None
@@ -132,10 +132,9 @@ class Engine:
         del ws
         r.cd = compress_spec_desc(self.spec, s, T, T)
         r.comp = B.vc_compress(r.cd, kd, vd, q_obs)
-        r.full_k = torch.empty(L, Hkv, full_cap, D, dtype=self.dt, pin_memory=True)
-        r.full_v = torch.empty(L, Hkv, full_cap, D, dtype=self.dt, pin_memory=True)
-        r.full_k[:, :, :T].copy_(kd)
-        r.full_v[:, :, :T].copy_(vd)
+        eb = 2 if self.dt == torch.bfloat16 else 4
+        r.full_k = B.HostBuffer(L * Hkv * full_cap * D * eb)
+        r.full_v = B.HostBuffer(L * Hkv * full_cap * D * eb)
         tail_cap = n_tokens + x + 2
         r.tail_k = torch.empty(L, Hkv, tail_cap, D, dtype=self.dt, device=self.device)
         r.tail_v = torch.empty_like(r.tail_k)
@@ -151,6 +150,7 @@ class Engine:
                     full_v_host=r.full_v.data_ptr(), full_cap=full_cap, rows=r.rows.data_ptr())
         import ctypes as C
         r.req.cd = C.pointer(r.cd)
+        self.m.offload(r.req, kd, vd, T)
         torch.cuda.synchronize()
         r.emitted = [int(g0.item())]
         if keep_prefill_kv:
@@ -174,60 +174,88 @@ class Engine:
             self.slot_owner = [None] * n_slots
 
     # ------------------------------------------------------------ the VeriCache loop
-    def run(self, lead: int | None = None, stagger: bool = True, trace: list | None = None):
-        """Decode every request to its n_tokens; returns wall seconds of the decode phase."""
+    def start(self, lead: int = 2, stagger: bool = True):
+        """Allocate slots/workspaces and set the staggered start ticks."""
         self._alloc()
-        reqs = self.reqs
-        n = len(reqs)
-        xs = [r.x for r in reqs]
-        for r in reqs:
+        n = len(self.reqs)
+        for r in self.reqs:
             r.start_tick = (r.idx * r.x) // n if stagger else 0
             r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
-        if lead is None:
-            lead = 2
+        self.lead = lead
+        self.tick = 0
+        self.draft_steps = 0
+
+    def step(self) -> bool:
+        """One scheduler iteration: finish accepts, issue staging, one batched
+        draft step, issue ready verifications.  Returns True if a draft step ran."""
+        reqs = self.reqs
         cs = torch.cuda.current_stream()
-        tick = 0
-        t0 = time.perf_counter()
-        while any(r.phase != DONE for r in reqs):
-            # 1. finish accepts whose result reached the host
-            for r in reqs:
-                if r.phase == ACCEPTING and r.acc_ev.query():
-                    a = int(r.result_host[0])
-                    toks = r.result_host[1:a + 2].tolist()
-                    r.emitted += toks
-                    r.accepts.append(a)
-                    self.m.commit(r.req, a, r.vtail_k, r.vtail_v, after_event=r.acc_ev, copy_stream=self.copy_stream)
-                    r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
-            # 2. stage full KV for requests close to the end of their draft
-            for r in reqs:
-                if r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= r.x - lead and tick >= r.start_tick:
-                    self._try_stage(r)
-            # 3. one batched draft step for every drafting request
-            active = [r for r in reqs if r.phase == DRAFT and tick >= r.start_tick and r.req.draft_idx < r.x]
-            for k in range(0, len(active), 16):
-                grp = active[k:k + 16]
-                self.m.draft_step([r.req for r in grp], self.ws_draft)
-                for r in grp:
-                    r.req.draft_idx += 1
-                    if r.req.draft_idx == r.x:
-                        r.phase = WAIT_SLOT
-            # 4. verify requests whose drafts are complete and whose slot is staged
-            for r in reqs:
-                if r.phase == WAIT_SLOT:
-                    if r.slot < 0:
-                        self._try_stage(r)
-                    if r.slot >= 0 and r.stage_ev.query():
-                        self._verify(r, cs)
-            if trace is not None:
-                trace.append((tick, [r.phase for r in reqs], [r.req.draft_idx for r in reqs]))
-            tick += 1
-            if not active and all(r.phase in (ACCEPTING, WAIT_SLOT, DONE) for r in reqs):
-                time.sleep(0)  # nothing to draft: wait for copies / accepts
-        torch.cuda.synchronize()
-        self.copy_stream.synchronize()
+        # 1. finish accepts whose result reached the host
         for r in reqs:
+            if r.phase == ACCEPTING and r.acc_ev.query():
+                self._finish_accept(r)
+        # 2. stage full KV for requests close to the end of their draft
+        for r in reqs:
+            if r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= r.x - self.lead and self.tick >= r.start_tick:
+                self._try_stage(r)
+        # 3. one batched draft step for every drafting request
+        active = [r for r in reqs if r.phase == DRAFT and self.tick >= r.start_tick and r.req.draft_idx < r.x]
+        for k in range(0, len(active), 16):
+            grp = active[k:k + 16]
+            self.m.draft_step([r.req for r in grp], self.ws_draft)
+            for r in grp:
+                r.req.draft_idx += 1
+                if r.req.draft_idx == r.x:
+                    r.phase = WAIT_SLOT
+        # 4. verify requests whose drafts are complete and whose slot is staged
+        for r in reqs:
+            if r.phase == WAIT_SLOT:
+                if r.slot < 0:
+                    self._try_stage(r)
+                if r.slot >= 0 and r.stage_ev.query():
+                    self._verify(r, cs)
+        if active:
+            self.draft_steps += 1
+        self.tick += 1
+        return bool(active)
+
+    def _finish_accept(self, r: Request):
+        a = int(r.result_host[0])
+        r.emitted += r.result_host[1:a + 2].tolist()
+        r.accepts.append(a)
+        self.m.commit(r.req, a, r.vtail_k, r.vtail_v, after_event=r.acc_ev, copy_stream=self.copy_stream)
+        r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
+
+    def drain(self):
+        """Wait for every in-flight verification and fold its accepted tokens in."""
+        torch.cuda.synchronize()
+        for r in self.reqs:
+            if r.phase == ACCEPTING:
+                r.acc_ev.synchronize()
+                self._finish_accept(r)
+        self.copy_stream.synchronize()
+
+    def emitted_total(self) -> int:
+        return sum(len(r.emitted) for r in self.reqs)
+
+    def run(self, lead: int = 2, stagger: bool = True, trace: list | None = None):
+        """Decode every request to its n_tokens; returns wall seconds of the decode phase."""
+        self.start(lead, stagger)
+        t0 = time.perf_counter()
+        while any(r.phase != DONE for r in self.reqs):
+            self.step()
+            if trace is not None:
+                trace.append((self.tick, [r.phase for r in self.reqs], [r.req.draft_idx for r in self.reqs]))
+        self.drain()
+        for r in self.reqs:
             r.emitted = r.emitted[: r.n_tokens]
         return time.perf_counter() - t0
+
+    def run_draft_steps(self, n: int):
+        """Run scheduler iterations until n more batched draft steps have executed."""
+        target = self.draft_steps + n
+        while self.draft_steps < target and any(r.phase != DONE for r in self.reqs):
+            self.step()
 
     def _try_stage(self, r: Request):
         for i in range(len(self.slots)):
@@ -285,3 +313,29 @@ def greedy_resident(model: B.Model, prompt: torch.Tensor, n_tokens: int, chunk: 
                          out.data_ptr() + 4 * i, kd.data_ptr() + off, vd.data_ptr() + off, cap, ws)
     torch.cuda.synchronize()
     return out.tolist(), time.perf_counter() - t0, (kd, vd)
+
+
+def greedy_from_host(model: B.Model, r: Request, n_steps: int, slot, ws: torch.Tensor, copy_stream):
+    """Full-KV greedy decoding with the cache in pinned host memory, the
+    comparator VeriCache is measured against: every token stages the request's
+    whole full KV over PCIe, runs one vc_verify row, and appends the new row to
+    the host copy.  Advances the request; returns (tokens, seconds)."""
+    sk, sv = slot
+    cs = torch.cuda.current_stream()
+    toks = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        model.stage(r.req, sk, sv, 0, model.shape.n_layers, copy_stream=copy_stream)
+        ev = torch.cuda.Event()
+        ev.record(copy_stream)
+        cs.wait_event(ev)
+        model.verify_raw(r.req, sk.data_ptr(), sv.data_ptr(), sk.shape[-2], r.rows.data_ptr(), 1, r.rows.data_ptr(),
+                         r.vtail_k.data_ptr(), r.vtail_v.data_ptr(), r.vtail_k.shape[-2], ws)
+        done = torch.cuda.Event()
+        done.record(cs)
+        model.commit(r.req, 0, r.vtail_k, r.vtail_v, after_event=done, copy_stream=copy_stream)
+        toks.append(r.rows[:1])
+    torch.cuda.synchronize()
+    copy_stream.synchronize()
+    return [int(t.item()) for t in toks], time.perf_counter() - t0

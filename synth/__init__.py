@@ -73,9 +73,27 @@ def splitmix64(c: np.ndarray) -> np.ndarray:
         return z ^ (z >> np.uint64(31))
 
 
-def uniform(stream: int, n: int, seed: int = 0, start: int = 0) -> np.ndarray:
+_CHUNK = 1 << 22
+
+
+def _uniform_chunk(stream: int, seed: int, start: int, n: int, out: np.ndarray) -> None:
     z = splitmix64(_counters(stream, seed, start, n))
-    return (z >> np.uint64(40)).astype(np.float64) * (2.0 ** -24)
+    out[:] = (z >> np.uint64(40)).astype(np.float64) * (2.0 ** -24)
+
+
+def uniform(stream: int, n: int, seed: int = 0, start: int = 0) -> np.ndarray:
+    """u(start + i), i < n; large draws are evaluated in chunks on a thread pool
+    (numpy releases the GIL), which changes nothing in the values."""
+    out = np.empty(n, dtype=np.float64)
+    if n <= _CHUNK:
+        _uniform_chunk(stream, seed, start, n, out)
+        return out
+    import concurrent.futures as cf
+    import os
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda o: _uniform_chunk(stream, seed, start + o, min(_CHUNK, n - o), out[o:o + _CHUNK]),
+                    range(0, n, _CHUNK)))
+    return out
 
 
 def xavier(stream: int, shape, fan_in: int, fan_out: int, seed: int = 0, start: int = 0) -> np.ndarray:

@@ -356,7 +356,7 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     VC_REQUIRE(D == 128 && dtype == VC_BF16, VC_ERR_UNSUPPORTED, "quantized draft needs bf16, head_dim 128");
     if ((st = launch_attn_quant(qa, s))) return st;
   }
-  if ((st = launch_attn(aa, dtype, s))) return st;
+  if ((st = launch_attn(aa, dtype, s, true))) return st;
   if (g_prof_on && rec.a && rec.b) {
     VC_HIP(hipEventRecord(rec.b, s));
     g_prof.push_back(rec);

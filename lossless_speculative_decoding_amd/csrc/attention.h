@@ -70,7 +70,7 @@ struct QuantArgs {
 };
 
 // dtype: VC_BF16 (head_dim 128, MFMA) or VC_F32 (head_dim 64, VALU)
-vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s);
+vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, bool draft = false);
 vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s);
 
 struct CombineArgs {

@@ -96,6 +96,10 @@ __device__ __forceinline__ void store_tile_bf16(const TileRegs& r, uint16_t* Ks,
   }
 }
 
+// DRAFT = 1 for decode over compressed caches (one query row per request), 0 for
+// verification / prefill rows; the code is identical, the symbol names differ so
+// profiles attribute the two uses separately.
+template <int DRAFT>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[ATT_KT * KS_PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D128 * VT_PITCH];
@@ -336,12 +340,13 @@ __global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
 
 }  // namespace
 
-vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s) {
+vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, bool draft) {
   if (a.n_req <= 0 || a.max_splits <= 0) return VC_OK;
   if (dtype == VC_BF16) {
     VC_REQUIRE(a.head_dim == 128, VC_ERR_UNSUPPORTED, "bf16 attention needs head_dim 128 (got %d)", a.head_dim);
     dim3 grid(a.Hkv * a.n_rowblocks, a.max_splits, a.n_req);
-    hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(256), 0, s, a);
+    if (draft) hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_bf16_kernel<0>, grid, dim3(256), 0, s, a);
   } else {
     VC_REQUIRE(a.head_dim == 64, VC_ERR_UNSUPPORTED, "fp32 attention needs head_dim 64 (got %d)", a.head_dim);
     int max_qrows = 0;

@@ -262,17 +262,16 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
                           int64_t o_req_stride_bytes, float* part, hipStream_t s) {
   const int G = Hq / Hkv;
   const float sl2 = LOG2E / sqrtf(float(D));
+  // bf16 head_dim 128: the one-row decode kernel, which numbers the exact-row segment's keys
+  // from a 64-aligned start (so its split count uses decode_keys)
+  const bool decode = dtype == VC_BF16 && D == 128 && G <= 16;
   int s_tot = 0;
   int qs_n[VC_MAX_BATCH], ts_n[VC_MAX_BATCH];
   for (int r = 0; r < n; r++) {
     const CompView& v = views[r];
-    if (v.kind == VC_QUANT) {
-      qs_n[r] = int(cdiv(v.tq, SPLIT_QUANT));
-      ts_n[r] = int(cdiv(v.n_resid + tail_n[r], SPLIT_DRAFT));
-    } else {
-      qs_n[r] = 0;
-      ts_n[r] = int(cdiv(v.kk + tail_n[r], SPLIT_DRAFT));
-    }
+    const int a_n = v.kind == VC_QUANT ? v.n_resid : v.kk;
+    qs_n[r] = v.kind == VC_QUANT ? int(cdiv(v.tq, SPLIT_QUANT)) : 0;
+    ts_n[r] = int(cdiv(decode ? decode_keys(a_n, tail_n[r]) : a_n + tail_n[r], SPLIT_DRAFT));
     s_tot = std::max(s_tot, qs_n[r] + ts_n[r]);
   }
   const int64_t per_req = int64_t(Hq) * s_tot * (D + 2);
@@ -356,7 +355,7 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     VC_REQUIRE(D == 128 && dtype == VC_BF16, VC_ERR_UNSUPPORTED, "quantized draft needs bf16, head_dim 128");
     if ((st = launch_attn_quant(qa, s))) return st;
   }
-  if ((st = launch_attn(aa, dtype, s, true))) return st;
+  if ((st = decode ? launch_attn_decode(aa, s) : launch_attn(aa, dtype, s, true))) return st;
   if (g_prof_on && rec.a && rec.b) {
     VC_HIP(hipEventRecord(rec.b, s));
     g_prof.push_back(rec);

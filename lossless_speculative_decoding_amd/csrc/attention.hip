@@ -233,6 +233,243 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
   }
 }
 
+// ---------------------------------------------------------------- bf16 decode, one query row
+// Draft steps attend with a single query row per request, so a 64-row block would leave
+// three of four waves idle.  Here one workgroup = 4 waves = (request, KV head, split) and
+// wave w streams the 64-key tiles w, w + 4, w + 8, ... of the split on its own, with its own
+// online softmax; the four states are merged in wave order at the end (fixed order, so the
+// result does not depend on timing).  The G query heads of the KV head are the 16 MFMA
+// columns.  K goes from HBM straight into A fragments (lane l: key l%16 of a 16-key group,
+// channels 8(l/16)..+8 of a 32-channel chunk); V is converted to fp16 and transposed
+// through a 16 KB LDS tile per wave.  A wave issues the next tile's loads as soon as the
+// current tile's registers are consumed, so its softmax and P.V overlap the next fetch;
+// KV loads are non-temporal (every byte is read once).
+// V^T tile layout: row d (channel) holds 64 fp16 slots; key 32kc + 16h + 4g + jj of the tile
+// sits in slot 32kc + 8g + 4h + jj, so the eight keys one lane's P^T fragment covers are
+// contiguous; 16-byte groups are XOR-swizzled by dec_sw(d) to spread the fragment reads of
+// 16 consecutive channels over all banks.
+constexpr int DEC_WAVES = 4;
+constexpr int DEC_TILE = D128 * ATT_KT;  // fp16 per wave LDS tile
+constexpr int DEC_RED = D128 + 4;        // floats per head in the merge buffer
+
+struct DecK {
+  u32x4 k[4][4];  // [16-key group kt][32-channel chunk c]
+};
+struct DecV {
+  u32x4 v[4][4];  // [16-key group a][key 4g + jj within it: jj]
+};
+
+__device__ __forceinline__ int dec_sw(int d) { return (d ^ (d >> 3)) & 7; }
+
+// The decode kernel numbers keys per tile-aligned segment: segment a occupies logical
+// keys [0, a_al) with a_al = a.n rounded up to 64 (keys a.n .. a_al - 1 are invisible),
+// segment b follows at a_al.  Every 64-key tile then lies in one segment and is fetched
+// through a buffer resource whose range ends at the segment's last row, so rows past it
+// read as zero without per-row branches.
+struct DecOff {
+  int k[4];  // byte offset of this lane's K fragment row in 16-key group kt
+  int v[4];  // byte offset of this lane's V row (jj = 0) in 16-key group q
+};
+
+__device__ __forceinline__ void dec_load(DecK& K, DecV& V, const KVSeg& a, const KVSeg& b, int a_al, int j, int t0,
+                                         const DecOff& off) {
+  const bool in_a = t0 < a_al;
+  const KVSeg& sg = in_a ? a : b;
+  const int row0 = in_a ? t0 : t0 - a_al;
+  const int64_t base = j * sg.hstride + int64_t(row0) * D128;
+  const int bytes = max(sg.n - row0, 0) * (D128 * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const uint16_t*>(sg.k) + base), 0, bytes, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const uint16_t*>(sg.v) + base), 0, bytes, BUF_DWORD3);
+#pragma unroll
+  for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+    for (int c = 0; c < 4; c++) K.k[kt][c] = ld_buf_nt(rk, off.k[kt] + 64 * c);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) V.v[q][jj] = ld_buf_nt(rv, off.v[q] + jj * D128 * 2);
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_decode_bf16_kernel(const AttnArgs args) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[DEC_WAVES * DEC_TILE];
+  // the wave index is uniform per wave; readfirstlane lets the compiler keep the tile
+  // addresses (and the buffer resources built from them) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int z = blockIdx.z;
+  if (z >= args.n_req) return;
+  const AttnReq& R = args.r[z];
+  const int G = args.G, Hq = args.Hq;
+  const int j = blockIdx.x, s = blockIdx.y;
+  if (s >= R.n_splits) return;  // uniform across the workgroup
+  const int a_n = R.a.n, a_al = (a_n + ATT_KT - 1) & ~(ATT_KT - 1);
+  const int key_lo = s * args.split_len;
+  const int key_hi = min(key_lo + args.split_len, a_al + R.b.n);
+  const int r16 = lane & 15, g = lane >> 4;
+  const bool head_ok = r16 < G;
+  uint16_t* Vt = lds + wave * DEC_TILE;
+  DecOff off;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    off.k[i] = ((16 * i + r16) * D128 + 8 * g) * 2;
+    off.v[i] = ((16 * i + 4 * g) * D128 + 8 * r16) * 2;
+  }
+
+  u32x4 qf[4];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(R.q) + int64_t(j * G + (head_ok ? r16 : 0)) * D128;
+#pragma unroll
+    for (int c = 0; c < 4; c++) qf[c] = head_ok ? *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
+  }
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) oacc[dt] = f32x4{0, 0, 0, 0};
+  float m_run = NEG_INF, l_run = 0.f;
+  const float sl2 = args.scale_log2;
+
+  DecK kr;
+  DecV vr;
+  int t0 = key_lo + ATT_KT * wave;
+  if (t0 < key_hi) dec_load(kr, vr, R.a, R.b, a_al, j, t0, off);
+  for (; t0 < key_hi; t0 += DEC_WAVES * ATT_KT) {
+    // The LDS addresses below are loop invariant; hoisted out of the loop they would not fit
+    // in registers next to two tiles, and their spill reloads would serialise every tile.
+    // Offsetting the tile base by an opaque zero makes the compiler recompute them (a few
+    // VALU operations per tile).
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    uint16_t* const Vw = Vt + zero;
+    // ---- S^T = K Q^T (16 keys x 16 heads per group)
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+      sacc[kt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < 4; c++) sacc[kt] = mfma_bf16(kr.k[kt][c], qf[c], sacc[kt]);
+    }
+    // ---- V -> fp16, transposed into this wave's LDS tile
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int grp = 4 * (q >> 1) + g, half = q & 1;
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        const int d = 8 * r16 + c;
+        float x[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) x[jj] = (c & 1) ? hi_bf(vr.v[q][jj][c >> 1]) : lo_bf(vr.v[q][jj][c >> 1]);
+        u32x2 w;
+        w.x = pack_h2(x[0], x[1]);
+        w.y = pack_h2(x[2], x[3]);
+        *reinterpret_cast<u32x2*>(Vw + d * ATT_KT + 8 * (grp ^ dec_sw(d)) + 4 * half) = w;
+      }
+    }
+    // ---- next tile in flight while this one finishes (the scheduling barrier keeps the
+    // loads from being hoisted above the last uses of the registers they overwrite)
+    __builtin_amdgcn_sched_barrier(0);
+    const int tn = t0 + DEC_WAVES * ATT_KT;
+    if (tn < key_hi) dec_load(kr, vr, R.a, R.b, a_al, j, tn, off);
+
+    // ---- scale, mask, online softmax per head (column l % 16)
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int t = t0 + 16 * kt + 4 * g + jj;
+        const bool vis = (t < key_hi) & ((t < a_n) | (t >= a_al));
+        const float v = vis ? sacc[kt][jj] * sl2 : NEG_INF;
+        sacc[kt][jj] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    // finite: key t0 of a processed tile is always visible (t0 < a_n or a_al <= t0 < key_hi)
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kt][jj] - m_new);
+        sacc[kt][jj] = p;
+        rs += p;
+      }
+    }
+    rs += shfl_xor(rs, 16);
+    rs += shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) oacc[dt] *= alpha;
+
+    // LDS operations of one wave complete in issue order; the fence keeps the compiler
+    // from moving the fragment reads above the tile stores (and later stores above them).
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // ---- O^T += V^T P^T over 2 chunks of 32 keys, P as an fp16 hi/lo pair
+#pragma unroll
+    for (int kc = 0; kc < 2; kc++) {
+      uint32_t h[4], lw[4];
+      split_h2(sacc[2 * kc][0] * P_SCALE, sacc[2 * kc][1] * P_SCALE, h[0], lw[0]);
+      split_h2(sacc[2 * kc][2] * P_SCALE, sacc[2 * kc][3] * P_SCALE, h[1], lw[1]);
+      split_h2(sacc[2 * kc + 1][0] * P_SCALE, sacc[2 * kc + 1][1] * P_SCALE, h[2], lw[2]);
+      split_h2(sacc[2 * kc + 1][2] * P_SCALE, sacc[2 * kc + 1][3] * P_SCALE, h[3], lw[3]);
+      const u32x4 pb = u32x4{h[0], h[1], h[2], h[3]};
+      const u32x4 pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        const int d = 16 * dt + r16;
+        const u32x4 va = *reinterpret_cast<const u32x4*>(Vw + d * ATT_KT + 8 * ((4 * kc + g) ^ dec_sw(d)));
+        oacc[dt] = mfma_f16(va, pb, oacc[dt]);
+        oacc[dt] = mfma_f16(va, pl, oacc[dt]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+
+  // ---- merge the four wave states in wave order; lane holds o[16dt + 4g + jj] of head l % 16
+  float* red = reinterpret_cast<float*>(Vt);  // [G][DEC_RED]: m, l, o[D]
+  if (head_ok) {
+    float* rh = red + r16 * DEC_RED;
+    if (g == 0) {
+      rh[0] = m_run;
+      rh[1] = l_run;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) rh[2 + 16 * dt + 4 * g + jj] = oacc[dt][jj] * P_UNSCALE;
+    }
+  }
+  __syncthreads();
+  const float* red0 = reinterpret_cast<const float*>(lds);
+  for (int idx = tid; idx < G * (D128 + 2); idx += 256) {
+    const int n = idx / (D128 + 2), e = idx - n * (D128 + 2);
+    float mw[DEC_WAVES];
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; w++) {
+      mw[w] = red0[w * (DEC_TILE / 2) + n * DEC_RED];
+      M = fmaxf(M, mw[w]);
+    }
+    float acc = 0.f;
+    if (e == 0) {
+      acc = M;
+    } else {
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; w++) {
+        const float wt = mw[w] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+        acc = fmaf(red0[w * (DEC_TILE / 2) + n * DEC_RED + e], wt, acc);
+      }
+    }
+    R.part[(int64_t(j * G + n) * R.s_total + (R.s_off + s)) * (D128 + 2) + e] = acc;
+  }
+}
+
 // ---------------------------------------------------------------- fp32 (head_dim 64), VALU
 // One workgroup (64 threads) per (request, KV head, query row, split).  Lane t
 // scores key t0 + t of each 64-key tile; lane d accumulates o[d].  The key
@@ -311,7 +548,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs args) {
 }
 
 // ---------------------------------------------------------------- combine
-// One workgroup per (request, row, query head); thread d merges o[d].
+// One workgroup per (request, row, query head); thread d merges o[d] over the splits in
+// ascending order.  The per-split loads are independent, so they are issued in unrolled
+// chunks of CMB_CHUNK and only the accumulation runs in sequence.
+constexpr int CMB_CHUNK = 16;
+
 __global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
   const int z = blockIdx.y;
   if (z >= a.n_req) return;
@@ -319,16 +560,35 @@ __global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
   const int D = a.head_dim;
   const int d = threadIdx.x;
   if (d >= D) return;
-  const float* p = a.part[z] + int64_t(rh) * a.s_total * (D + 2);
+  const int64_t ps = D + 2;
+  const float* p = a.part[z] + int64_t(rh) * a.s_total * ps;
   const int S = a.s_used[z];
   float M = NEG_INF;
-  for (int s = 0; s < S; s++) M = fmaxf(M, p[s * (D + 2)]);
+  for (int s0 = 0; s0 < S; s0 += CMB_CHUNK) {
+    float m[CMB_CHUNK];
+#pragma unroll
+    for (int i = 0; i < CMB_CHUNK; i++) m[i] = s0 + i < S ? p[(s0 + i) * ps] : NEG_INF;
+#pragma unroll
+    for (int i = 0; i < CMB_CHUNK; i++) M = fmaxf(M, m[i]);
+  }
   float L = 0.f, O = 0.f;
-  for (int s = 0; s < S; s++) {
-    const float ms = p[s * (D + 2)];
-    const float w = (ms == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    L = fmaf(p[s * (D + 2) + 1], w, L);
-    O = fmaf(p[s * (D + 2) + 2 + d], w, O);
+  for (int s0 = 0; s0 < S; s0 += CMB_CHUNK) {
+    float m[CMB_CHUNK], l[CMB_CHUNK], o[CMB_CHUNK];
+#pragma unroll
+    for (int i = 0; i < CMB_CHUNK; i++) {
+      const bool ok = s0 + i < S;
+      m[i] = ok ? p[(s0 + i) * ps] : NEG_INF;
+      l[i] = ok ? p[(s0 + i) * ps + 1] : 0.f;
+      o[i] = ok ? p[(s0 + i) * ps + 2 + d] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < CMB_CHUNK; i++) {
+      if (s0 + i < S) {
+        const float w = (m[i] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m[i] - M);
+        L = fmaf(l[i], w, L);
+        O = fmaf(o[i], w, O);
+      }
+    }
   }
   const float r = O / L;
   if (a.out_dtype == VC_BF16) {
@@ -340,13 +600,33 @@ __global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
 
 }  // namespace
 
+vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s) {
+  if (a.n_req <= 0 || a.max_splits <= 0) return VC_OK;
+  VC_REQUIRE(a.head_dim == 128 && a.G >= 1 && a.G <= 16 && a.split_len % (DEC_WAVES * ATT_KT) == 0, VC_ERR_UNSUPPORTED,
+             "decode attention needs head_dim 128, at most 16 query heads per KV head, split a multiple of 256");
+  for (int r = 0; r < a.n_req; r++) {
+    const AttnReq& q = a.r[r];
+    VC_REQUIRE(q.n_rows == 1, VC_ERR_UNSUPPORTED, "decode attention takes one query row per request");
+    VC_REQUIRE(int64_t(q.a.n) * D128 * 2 < (int64_t(1) << 31) && int64_t(q.b.n) * D128 * 2 < (int64_t(1) << 31),
+               VC_ERR_UNSUPPORTED, "decode attention: segment above 2 GiB per head");
+    VC_REQUIRE(int64_t(q.n_splits) * a.split_len >= decode_keys(q.a.n, q.b.n), VC_ERR_ARG,
+               "decode attention: %d splits do not cover the keys", q.n_splits);
+  }
+  hipLaunchKernelGGL(attn_decode_bf16_kernel, dim3(a.Hkv, a.max_splits, a.n_req), dim3(256), 0, s, a);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+
 vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, bool draft) {
   if (a.n_req <= 0 || a.max_splits <= 0) return VC_OK;
   if (dtype == VC_BF16) {
     VC_REQUIRE(a.head_dim == 128, VC_ERR_UNSUPPORTED, "bf16 attention needs head_dim 128 (got %d)", a.head_dim);
     dim3 grid(a.Hkv * a.n_rowblocks, a.max_splits, a.n_req);
-    if (draft) hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(attn_bf16_kernel<0>, grid, dim3(256), 0, s, a);
+    if (draft) {
+      hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(attn_bf16_kernel<0>, grid, dim3(256), 0, s, a);
+    }
   } else {
     VC_REQUIRE(a.head_dim == 64, VC_ERR_UNSUPPORTED, "fp32 attention needs head_dim 64 (got %d)", a.head_dim);
     int max_qrows = 0;

@@ -86,6 +86,19 @@ __device__ __forceinline__ f32x4 mfma_f16(const u32x4& a, const u32x4& b, f32x4 
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8>(a), bitcast<f16x8>(b), c, 0, 0, 0);
 }
 
+// 16-byte load marked non-temporal (streamed once, not kept in the caches)
+__device__ __forceinline__ u32x4 ld_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// dword 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle)
+constexpr int BUF_DWORD3 = 0x00020000;
+// 16-byte buffer load at byte offset off (range-checked against the resource: out of
+// range reads as zero), marked non-temporal
+__device__ __forceinline__ u32x4 ld_buf_nt(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_INF = -__builtin_huge_valf();
 

@@ -210,6 +210,56 @@ def test_tokdrop_blob_and_draft_attention():
     assert err <= TOL_BF16
 
 
+@pytest.mark.parametrize("reqs", [
+    [(700, 200, 64, 70)],                                  # kept count off the 64-key grid, tail > 1 tile
+    [(1536, 384, 64, 1), (900, 130, 32, 300), (2000, 777, 64, 65)],   # batch with mixed shapes
+    [(640, 64, 64, 0), (512, 100, 64, 256)],               # kept = recent only, empty tail; 4-tile tail
+])
+def test_draft_decode_ragged_batch(reqs):
+    """One-row decode over (kept rows, tail) for a batch of requests of different sizes:
+    kept counts off the tile grid, tails spanning tiles, an empty tail."""
+    need_gpu()
+    from lossless_speculative_decoding_amd import VC_BF16, VC_F32, VC_TOKDROP, compress_desc, compress_layout
+    from lossless_speculative_decoding_amd import vc_attn_draft, vc_compress
+    from lossless_speculative_decoding_amd._vc import AttnDesc
+    W = 32
+    blobs, cds, tks, tvs, ntl, host = [], [], [], [], [], []
+    for b, (T, keep, R, n_tail) in enumerate(reqs):
+        kb = _head_bits(synth.S_ATT_K, b, T, outl=False)[0]
+        vb = _head_bits(synth.S_ATT_V, b, T, outl=False)[0]
+        qo = synth.att_queries(synth.S_ATT_QV, b, W, HQ, D)
+        d = compress_desc(VC_TOKDROP, 1, HQ, HKV, D, T, VC_BF16, keep_total=keep, keep_recent=R, obs_window=W)
+        blob = vc_compress(d, dev_bf16(kb[None]), dev_bf16(vb[None]), dev_bf16(qo[None]))
+        cap = max(n_tail, 1) + 5
+        tk = np.zeros((HKV, cap, D), np.uint16)
+        tv = np.zeros((HKV, cap, D), np.uint16)
+        if n_tail:
+            tk[:, :n_tail] = _head_bits(synth.S_ATT_TK, b, n_tail, outl=False)[0]
+            tv[:, :n_tail] = _head_bits(synth.S_ATT_TV, b, n_tail, outl=False)[0]
+        blobs.append(blob)
+        cds.append(d)
+        tks.append(dev_bf16(tk))
+        tvs.append(dev_bf16(tv))
+        ntl.append(n_tail)
+        host.append((kb, vb, tk, tv, keep, n_tail))
+    qd = synth.att_queries(synth.S_ATT_QD, 0, len(reqs), HQ, D)          # [B][Hq][D]
+    out = vc_attn_draft(AttnDesc(HQ, HKV, D, VC_BF16, 0, VC_F32), blobs, cds, tks, tvs, ntl, dev_bf16(qd))
+    torch.cuda.synchronize()
+    for b, (kb, vb, tk, tv, keep, n_tail) in enumerate(host):
+        lay = compress_layout(cds[b])
+        raw = blobs[b].cpu().numpy()
+        idx = raw[lay.idx: lay.idx + HKV * keep * 4].view(np.int32).reshape(HKV, keep)
+        ref = np.zeros((HQ, D))
+        for j in range(HKV):
+            Kj = np.concatenate([_f(kb[j, idx[j]]), _f(tk[j, :n_tail])])
+            Vj = np.concatenate([_f(vb[j, idx[j]]), _f(tv[j, :n_tail])])
+            for g in range(HQ // HKV):
+                ref[j * (HQ // HKV) + g] = OA.attend(_f(qd[b, j * (HQ // HKV) + g]), Kj, Vj)
+        err = row_rel_err(host_f64(out[b]), ref)
+        log(f"  request {b} (T, keep, R, tail) = {reqs[b]}: rel err {err:.2e}")
+        assert err <= TOL_BF16
+
+
 def test_bf16_output_is_rounded_fp32_output():
     """The bf16 attention output is the fp32 result rounded to nearest even."""
     need_gpu()

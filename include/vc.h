@@ -116,8 +116,14 @@ vc_status vc_ws_size(const vc_model* m, int32_t max_rows, int32_t max_keys, size
  *   probability (q_obs [L][W][Hq][D] in dtype: the post-RoPE queries of the
  *   last W prompt positions); keep the top keep_total - R candidates (ties to
  *   the smaller index) plus the last R rows, ascending.  Output blob:
- *     K_keep [L][Hkv][Kk][D] dtype | V_keep same | idx [L][Hkv][Kk] int32
- *   with Kk = min(T, max(keep_total, min(R, T))).
+ *     K_keep [L][Hkv][Kk][D] dtype | V_keep same | idx [L][Hkv][Kk] int32 |
+ *     keep_mask [L][Hkv][nt] u64 | keep_cnt [L][Hkv][nt] int32
+ *   with Kk = min(T, max(keep_total, min(R, T))) and nt = ceil(T/64): bit o of
+ *   keep_mask[tile] says whether position 64*tile + o is kept, keep_cnt[tile]
+ *   counts the kept positions before the tile.  A position t is then K_keep row
+ *   cnt + (kept below it in the tile) when kept, else dropped row
+ *   t - cnt - (kept below it): the compacted order in which the host holds the
+ *   dropped rows (vc_offload) and verification stages them.
  * VC_QUANT: b in {2,3,4} bits, group G in {64,128}, Tq = floor(T/G)*G.
  *   K per channel (groups of G tokens), V per token (groups of G channels):
  *   zero = fp16(min), scale = fp16((max - min) / (2^b - 1)),
@@ -147,6 +153,10 @@ typedef struct {
   size_t k_main, v_main, idx;       /* token drop: K_keep, V_keep, idx           */
   size_t kc, vc, ks, kz, vs, vz;    /* quant                                     */
   size_t kr, vr;                    /* quant residual rows                       */
+  size_t keep_mask, keep_cnt;       /* token drop: per-tile kept map (below)      */
+  int32_t n_tiles;                  /* token drop: ceil(T / 64)                   */
+  int32_t n_host;  /* prompt rows per (layer, head) that only the host holds:
+                      T - Kk (token drop: the dropped rows), T (quant)              */
 } vc_compress_layout;
 
 vc_status vc_compress_layout_of(const vc_compress_desc* d, vc_compress_layout* out);
@@ -160,7 +170,15 @@ vc_status vc_compress(const vc_compress_desc* d, const void* k, const void* v, c
  *         residual rows, which stay in the blob), [L][Hkv][tail_cap][D] in
  *         the model dtype: the verifier's rows of every committed token;
  *         during a round the draft rows follow at n_tail + draft_idx.
- *   ctx_len: rows in the full KV = absolute position of the pending token.
+ *   ctx_len: rows in the full KV = absolute position of the pending token
+ *         (prompt length T + n_tail for a request with a compressed cache).
+ *   The full KV of a request with a compressed cache is split by where its
+ *   exact rows already are: the device holds the committed rows (tail) and,
+ *   for token drop, the kept prompt rows; the pinned host buffer holds the
+ *   other n_host prompt rows per (layer, head) (vc_compress_layout.n_host:
+ *   the dropped rows compacted in position order, or all T rows for quant),
+ *   and only those cross PCIe for a verification.  A request with comp ==
+ *   NULL is plain: the host holds its whole context (full-KV decoding).
  * ---------------------------------------------------------------------- */
 typedef struct {
   const void* comp;          /* compressed blob (device)                                */
@@ -170,7 +188,7 @@ typedef struct {
   int32_t tail_cap, n_tail;
   int32_t ctx_len;
   int32_t draft_idx;         /* step within the current round (vc_draft_step)           */
-  void* full_k_host;         /* pinned [L][Hkv][full_cap][D]                            */
+  void* full_k_host;         /* pinned [L][Hkv][full_cap][D]: host rows (see above)     */
   void* full_v_host;
   int32_t full_cap;
   int32_t* rows;             /* device int32 [>= x + 1]: rows[0] = pending token,        */
@@ -190,10 +208,15 @@ vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logit
 /* Verification forward of ONE request ("The Core Idea": predictions for every
  * drafted position plus one bonus, in a single pass against the full cache).
  * Rows tok[0..n_rows) (the pending token then the x drafts) sit at positions
- * ctx_len .. ctx_len + n_rows - 1; row i attends to staged full-KV rows
- * [0, ctx_len) and verify rows 0..i.  Writes out_argmax[n_rows] and the exact
- * K/V of every row into vtail [L][Hkv][vtail_cap][D].  staged_k/v:
- * [L][Hkv][staged_cap][D] in the model dtype.  n_rows = 1 is greedy decoding. */
+ * ctx_len .. ctx_len + n_rows - 1; row i attends to the full KV of positions
+ * [0, ctx_len) and verify rows 0..i, keys taken in position order from the
+ * staged host rows, the kept rows of a token-drop cache and the tail (see the
+ * per-request state).  Writes out_argmax[n_rows] and the exact K/V of every row
+ * into vtail [L][Hkv][vtail_cap][D].  staged_k/v: [L][Hkv][staged_cap][D] in
+ * the model dtype holding the request's host rows (vc_stage).  Each key
+ * contributes the same arithmetic whichever buffer holds it, so a request with
+ * a compressed cache verifies bit for bit like a plain request over the same
+ * full KV.  n_rows = 1 is greedy decoding. */
 vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v, int32_t staged_cap,
                     const int32_t* tok, int32_t n_rows, int32_t* out_argmax, float* logits_opt, void* vtail_k,
                     void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, hipStream_t s);
@@ -210,10 +233,12 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
 vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* verified, int32_t x, const void* vtail_k,
                     const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s);
 
-/* Host half of the commit: enqueue on `copy` the copy of vtail rows 0..a into
- * the pinned full KV at row ctx_len, then advance req->n_tail and
- * req->ctx_len by a + 1 and reset draft_idx.  `after` (may be NULL) is an
- * event the copy stream waits for first (the verify/accept work). */
+/* Host half of the commit, after result[0] = a is known: advance req->n_tail
+ * and req->ctx_len by a + 1 and reset draft_idx.  A request with a compressed
+ * cache keeps its committed rows in the device tail (vc_accept wrote them), so
+ * nothing is copied.  A plain request gets vtail rows 0..a appended to its
+ * pinned full KV at row ctx_len, enqueued on `copy` after `after` (may be
+ * NULL). */
 vc_status vc_commit(vc_model* m, vc_req* req, int32_t a, const void* vtail_k, const void* vtail_v, int32_t vtail_cap,
                     hipEvent_t after, hipStream_t copy);
 
@@ -222,13 +247,16 @@ vc_status vc_commit(vc_model* m, vc_req* req, int32_t a, const void* vtail_k, co
 vc_status vc_host_alloc(size_t bytes, void** out_host);
 vc_status vc_host_free(void* host);
 
-/* Offload (setup): copy rows [0, T) of a device cache [L][Hkv][src_cap][D] into
- * the request's pinned full KV at rows [0, T), on `s` (D2H, hipMemcpy2DAsync). */
+/* Offload (setup): from a device cache [L][Hkv][src_cap][D] holding prompt rows
+ * [0, T), copy the request's host rows into its pinned buffer on `s`: the
+ * dropped rows, compacted, for token drop (through a temporary device buffer;
+ * the call then synchronises `s`), all T rows otherwise. */
 vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const void* v_dev, int32_t src_cap, int32_t T,
                      hipStream_t s);
 
-/* Stage the request's full KV rows [0, ctx_len) from pinned host memory into a
- * device slot [L][Hkv][slot_cap][D] on `copy` (SDMA, hipMemcpy2DAsync), layers
+/* Stage the request's host rows (n_host per (layer, head) with a compressed
+ * cache, ctx_len for a plain request) from pinned host memory into a device
+ * slot [L][Hkv][slot_cap][D] on `copy` (SDMA, hipMemcpy2DAsync), layers
  * [l0, l1). */
 vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, int32_t slot_cap, int32_t l0, int32_t l1,
                    hipStream_t copy);

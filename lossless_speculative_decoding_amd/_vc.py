@@ -43,7 +43,9 @@ class CompressDesc(C.Structure):
 
 class CompressLayout(C.Structure):
     _fields_ = [("total", C.c_size_t), ("n_main", C.c_int32), ("n_resid", C.c_int32)] + \
-               [(n, C.c_size_t) for n in ("k_main", "v_main", "idx", "kc", "vc", "ks", "kz", "vs", "vz", "kr", "vr")]
+               [(n, C.c_size_t) for n in ("k_main", "v_main", "idx", "kc", "vc", "ks", "kz", "vs", "vz", "kr", "vr",
+                                          "keep_mask", "keep_cnt")] + \
+               [("n_tiles", C.c_int32), ("n_host", C.c_int32)]
 
 
 class Req(C.Structure):

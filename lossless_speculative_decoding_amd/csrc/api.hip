@@ -219,6 +219,18 @@ struct CompView {
     const int64_t per = int64_t(Hkv) * kk * D * eb;
     return KVSeg{base + lay.k_main + l * per, base + lay.v_main + l * per, int64_t(kk) * D, kk, 0};
   }
+  MixSeg mix(int l) const {  // token drop: the kept / dropped split of the prompt positions
+    const int64_t per = int64_t(Hkv) * kk * D * eb;
+    const int64_t nt = lay.n_tiles;
+    MixSeg m{};
+    m.k = base + lay.k_main + l * per;
+    m.v = base + lay.v_main + l * per;
+    m.hstride = int64_t(kk) * D;
+    m.mask = reinterpret_cast<const uint64_t*>(base + lay.keep_mask + l * int64_t(Hkv) * nt * 8);
+    m.cnt = reinterpret_cast<const int32_t*>(base + lay.keep_cnt + l * int64_t(Hkv) * nt * 4);
+    m.nt = int32_t(nt);
+    return m;
+  }
   KVSeg resid(int l) const {
     const int64_t per = int64_t(Hkv) * n_resid * D * eb;
     return KVSeg{base + lay.kr + l * per, base + lay.vr + l * per, int64_t(n_resid) * D, n_resid, 0};
@@ -537,6 +549,41 @@ vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logit
   return k_scatter_tok(dst, n, tok_out, s);
 }
 
+// Where a request's full cache lives.  A VeriCache request (comp != NULL) keeps exact rows on
+// the device: the kept prompt rows of a token-drop cache and the tail of committed rows;
+// the host holds the rest of the prompt (n_host rows per layer and head, compacted in
+// position order).  A plain request (comp == NULL) has its whole context on the host.
+struct HostPart {
+  bool vmode = false;  // VeriCache request
+  bool split = false;  // token drop: prompt positions split between kept rows and host rows
+  int prompt = 0;      // positions covered by segment a (T, or ctx_len for a plain request)
+  int rows = 0;        // rows per (layer, head) held on the host / staged
+  CompView view{};
+};
+
+vc_status host_part(const vc_model* m, const vc_req* req, HostPart& hp) {
+  hp = HostPart{};
+  if (req->comp == nullptr) {
+    hp.prompt = req->ctx_len;
+    hp.rows = req->ctx_len;
+    return VC_OK;
+  }
+  if (vc_status st = comp_view(req->comp, req->cd, hp.view)) return st;
+  const vc_compress_desc& cd = *req->cd;
+  const vc_model_desc& d = m->d;
+  VC_REQUIRE(cd.n_layers == d.n_layers && cd.n_kv_heads == d.n_kv_heads && cd.head_dim == d.head_dim &&
+                 cd.dtype == d.dtype,
+             VC_ERR_ARG, "request: compressed cache shape differs from the model");
+  VC_REQUIRE(req->ctx_len == cd.seq_len + req->n_tail, VC_ERR_ARG,
+             "request: ctx_len %d != prompt %d + committed tail %d", req->ctx_len, cd.seq_len, req->n_tail);
+  VC_REQUIRE(req->n_tail == 0 || (req->tail_k && req->tail_v), VC_ERR_ARG, "request: tail rows without a tail");
+  hp.vmode = true;
+  hp.split = cd.kind == VC_TOKDROP;
+  hp.prompt = cd.seq_len;
+  hp.rows = hp.view.lay.n_host;
+  return VC_OK;
+}
+
 vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v, int32_t staged_cap,
                     const int32_t* tok, int32_t n_rows, int32_t* out_argmax, float* logits_opt, void* vtail_k,
                     void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -546,8 +593,10 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
   VC_REQUIRE(vtail_cap >= n_rows, VC_ERR_CAPACITY, "vc_verify: vtail capacity %d < %d rows", vtail_cap, n_rows);
   const vc_model_desc& d = m->d;
   const int ctx = req->ctx_len;
-  VC_REQUIRE(ctx >= 0 && (ctx == 0 || (staged_k && staged_v && staged_cap >= ctx)), VC_ERR_ARG,
-             "vc_verify: staged cache smaller than ctx_len");
+  HostPart hp;
+  if (vc_status st0 = host_part(m, req, hp)) return st0;
+  VC_REQUIRE(ctx >= 0 && (hp.rows == 0 || (staged_k && staged_v && staged_cap >= hp.rows)), VC_ERR_ARG,
+             "vc_verify: staged cache smaller than the %d host rows", hp.rows);
   VC_REQUIRE(ctx + n_rows <= d.max_pos, VC_ERR_CAPACITY, "vc_verify: position beyond the RoPE table");
   const WsLayout L = ws_layout(m, n_rows, ctx + n_rows);
   VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_verify: workspace %zu < %zu bytes", ws_bytes, L.total);
@@ -579,10 +628,25 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
     a.max_splits = S;
     AttnReq& r = a.r[0];
     r.q = qb;
-    r.a = KVSeg{ctx ? cptr(staged_k, l * Hkv * staged_cap * D * eb) : nullptr,
-                ctx ? cptr(staged_v, l * Hkv * staged_cap * D * eb) : nullptr, int64_t(staged_cap) * D, ctx, 0};
-    r.b = KVSeg{cptr(vtail_k, l * Hkv * vtail_cap * D * eb), cptr(vtail_v, l * Hkv * vtail_cap * D * eb),
-                int64_t(vtail_cap) * D, n_rows, 0};
+    // keys in position order: prompt (or the whole context of a plain request), committed
+    // tail rows, this call's rows; each key is the same bytes whichever buffer holds it
+    const KVSeg vt{cptr(vtail_k, l * Hkv * vtail_cap * D * eb), cptr(vtail_v, l * Hkv * vtail_cap * D * eb),
+                   int64_t(vtail_cap) * D, n_rows, 0};
+    r.a = KVSeg{hp.rows ? cptr(staged_k, l * Hkv * staged_cap * D * eb) : nullptr,
+                hp.rows ? cptr(staged_v, l * Hkv * staged_cap * D * eb) : nullptr, int64_t(staged_cap) * D,
+                hp.prompt, 0};
+    if (hp.split) {
+      r.mix = hp.view.mix(l);
+      r.b = KVSeg{cptr(req->tail_k, l * Hkv * req->tail_cap * D * eb), cptr(req->tail_v, l * Hkv * req->tail_cap * D * eb),
+                  int64_t(req->tail_cap) * D, req->n_tail, 0};
+      r.c = vt;
+    } else if (hp.vmode) {
+      r.b = KVSeg{cptr(req->tail_k, l * Hkv * req->tail_cap * D * eb), cptr(req->tail_v, l * Hkv * req->tail_cap * D * eb),
+                  int64_t(req->tail_cap) * D, req->n_tail, 0};
+      r.c = vt;
+    } else {
+      r.b = vt;
+    }
     r.part = part;
     r.n_rows = n_rows;
     r.lim0 = ctx;
@@ -704,10 +768,18 @@ vc_status vc_commit(vc_model* m, vc_req* req, int32_t a, const void* vtail_k, co
   if (vc_status st = check_model(m)) return st;
   VC_REQUIRE(req && vtail_k && vtail_v, VC_ERR_ARG, "vc_commit: null argument");
   VC_REQUIRE(a >= 0 && a + 1 <= vtail_cap, VC_ERR_ARG, "vc_commit: bad accept count %d", a);
-  VC_REQUIRE(req->ctx_len + a + 1 <= req->full_cap, VC_ERR_CAPACITY, "vc_commit: full KV capacity");
-  VC_REQUIRE(req->n_tail + a + 1 <= req->tail_cap, VC_ERR_CAPACITY, "vc_commit: tail capacity");
   const vc_model_desc& d = m->d;
   const size_t row = size_t(d.head_dim) * m->eb;
+  if (req->comp != nullptr) {
+    // VeriCache request: vc_accept already placed the verifier's rows in the device tail,
+    // which is where the full cache keeps every committed row
+    VC_REQUIRE(req->n_tail + a + 1 <= req->tail_cap, VC_ERR_CAPACITY, "vc_commit: tail capacity");
+    req->ctx_len += a + 1;
+    req->n_tail += a + 1;
+    req->draft_idx = 0;
+    return VC_OK;
+  }
+  VC_REQUIRE(req->ctx_len + a + 1 <= req->full_cap, VC_ERR_CAPACITY, "vc_commit: full KV capacity");
   if (after) VC_HIP(hipStreamWaitEvent(copy, after, 0));
   if (req->full_k_host && req->full_v_host) {
     VC_HIP(hipMemcpy2DAsync(mptr(req->full_k_host, int64_t(req->ctx_len) * row), size_t(req->full_cap) * row, vtail_k,
@@ -729,16 +801,20 @@ vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, i
   VC_REQUIRE(req && slot_k && slot_v && req->full_k_host && req->full_v_host, VC_ERR_ARG, "vc_stage: null argument");
   const vc_model_desc& d = m->d;
   VC_REQUIRE(0 <= l0 && l0 <= l1 && l1 <= d.n_layers, VC_ERR_ARG, "vc_stage: bad layer range");
-  VC_REQUIRE(slot_cap >= req->ctx_len, VC_ERR_CAPACITY, "vc_stage: slot %d < ctx %d rows", slot_cap, req->ctx_len);
-  if (l0 == l1 || req->ctx_len == 0) return VC_OK;
+  HostPart hp;
+  if (vc_status st = host_part(m, req, hp)) return st;
+  const int rows = hp.rows;
+  VC_REQUIRE(slot_cap >= rows && req->full_cap >= rows, VC_ERR_CAPACITY, "vc_stage: slot %d / host %d < %d rows",
+             slot_cap, req->full_cap, rows);
+  if (l0 == l1 || rows == 0) return VC_OK;
   const size_t row = size_t(d.head_dim) * m->eb;
   const int64_t lo_src = int64_t(l0) * d.n_kv_heads * req->full_cap * row;
   const int64_t lo_dst = int64_t(l0) * d.n_kv_heads * slot_cap * row;
   const size_t height = size_t(l1 - l0) * d.n_kv_heads;
   VC_HIP(hipMemcpy2DAsync(mptr(slot_k, lo_dst), size_t(slot_cap) * row, cptr(req->full_k_host, lo_src),
-                          size_t(req->full_cap) * row, size_t(req->ctx_len) * row, height, hipMemcpyHostToDevice, copy));
+                          size_t(req->full_cap) * row, size_t(rows) * row, height, hipMemcpyHostToDevice, copy));
   VC_HIP(hipMemcpy2DAsync(mptr(slot_v, lo_dst), size_t(slot_cap) * row, cptr(req->full_v_host, lo_src),
-                          size_t(req->full_cap) * row, size_t(req->ctx_len) * row, height, hipMemcpyHostToDevice, copy));
+                          size_t(req->full_cap) * row, size_t(rows) * row, height, hipMemcpyHostToDevice, copy));
   return VC_OK;
 }
 
@@ -758,10 +834,50 @@ vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const vo
                      hipStream_t s) {
   if (vc_status st = check_model(m)) return st;
   VC_REQUIRE(req && k_dev && v_dev && req->full_k_host && req->full_v_host, VC_ERR_ARG, "vc_offload: null argument");
-  VC_REQUIRE(T > 0 && T <= src_cap && T <= req->full_cap, VC_ERR_CAPACITY, "vc_offload: bad row counts");
+  VC_REQUIRE(T > 0 && T <= src_cap, VC_ERR_CAPACITY, "vc_offload: bad row counts");
   const vc_model_desc& d = m->d;
   const size_t row = size_t(d.head_dim) * m->eb;
   const size_t height = size_t(d.n_layers) * d.n_kv_heads;
+  if (req->comp != nullptr) {
+    HostPart hp;
+    vc_req probe = *req;
+    probe.ctx_len = req->cd ? req->cd->seq_len + req->n_tail : 0;
+    if (vc_status st = host_part(m, &probe, hp)) return st;
+    VC_REQUIRE(T == hp.prompt, VC_ERR_ARG, "vc_offload: %d rows given for a %d-token prompt", T, hp.prompt);
+    VC_REQUIRE(hp.rows <= req->full_cap, VC_ERR_CAPACITY, "vc_offload: host capacity %d < %d rows", req->full_cap,
+               hp.rows);
+    if (hp.split) {
+      // the dropped rows, compacted, one layer at a time through a device staging buffer
+      if (hp.rows == 0) return VC_OK;
+      const size_t lbytes = size_t(d.n_kv_heads) * hp.rows * row;
+      void* tmp = nullptr;
+      VC_HIP(hipMalloc(&tmp, 2 * lbytes));
+      vc_status st = VC_OK;
+      for (int l = 0; l < d.n_layers && st == VC_OK; l++) {
+        for (int kv = 0; kv < 2 && st == VC_OK; kv++) {
+          void* dst = mptr(tmp, kv * lbytes);
+          st = gather_dropped(req->cd, req->comp, kv ? v_dev : k_dev, src_cap, l * d.n_kv_heads, d.n_kv_heads, dst,
+                              hp.rows, s);
+          if (st) break;
+          void* host = kv ? req->full_v_host : req->full_k_host;
+          const hipError_t e = hipMemcpy2DAsync(mptr(host, int64_t(l) * d.n_kv_heads * req->full_cap * row),
+                                                size_t(req->full_cap) * row, dst, size_t(hp.rows) * row,
+                                                size_t(hp.rows) * row, d.n_kv_heads, hipMemcpyDeviceToHost, s);
+          if (e != hipSuccess) {
+            set_error("vc_offload: copy failed: %s", hipGetErrorString(e));
+            st = VC_ERR_HIP;
+          }
+        }
+      }
+      const hipError_t e1 = hipStreamSynchronize(s);
+      const hipError_t e2 = hipFree(tmp);
+      if (st) return st;
+      VC_HIP(e1);
+      VC_HIP(e2);
+      return VC_OK;
+    }
+  }
+  VC_REQUIRE(T <= req->full_cap, VC_ERR_CAPACITY, "vc_offload: host capacity %d < %d rows", req->full_cap, T);
   VC_HIP(hipMemcpy2DAsync(req->full_k_host, size_t(req->full_cap) * row, k_dev, size_t(src_cap) * row, size_t(T) * row,
                           height, hipMemcpyDeviceToHost, s));
   VC_HIP(hipMemcpy2DAsync(req->full_v_host, size_t(req->full_cap) * row, v_dev, size_t(src_cap) * row, size_t(T) * row,

@@ -25,9 +25,24 @@ struct KVSeg {
   int32_t pad_;
 };
 
+// Segment a as the union of rows kept on the device and rows staged from the host:
+// position t of tile t / 64 is kept iff bit t % 64 of mask[j][tile]; then it is kept
+// row cnt[j][tile] + (kept positions below it in the tile), else staged row
+// t - cnt[j][tile] - (kept positions below it).
+struct MixSeg {
+  const void* k;          // kept rows of the layer, [Hkv][..][D]
+  const void* v;
+  int64_t hstride;        // elements between consecutive KV heads
+  const uint64_t* mask;   // [Hkv][nt]; null: segment a is plain
+  const int32_t* cnt;     // [Hkv][nt]
+  int32_t nt;
+  int32_t pad_;
+};
+
 struct AttnReq {
   const void* q;     // [rows][Hq][D]
-  KVSeg a, b;        // logical keys: t < a.n -> a[t], else b[t - a.n]
+  KVSeg a, b, c;     // logical keys: a[t], then b[t - a.n], then c[t - a.n - b.n]
+  MixSeg mix;        // optional split of segment a (decode attention ignores c and mix)
   float* part;       // [rows][Hq][s_total][D + 2]
   int32_t n_rows;
   int32_t lim0;
@@ -42,6 +57,37 @@ struct AttnArgs {
   int32_t n_req, Hq, Hkv, G, split_len, n_rowblocks, max_splits, head_dim;
   float scale_log2;
 };
+static_assert(sizeof(AttnArgs) <= 4096, "kernel argument block too large");
+
+// Element pointer of key t's K (is_v = false) or V row for KV head j.
+template <typename E, int D>
+__device__ __forceinline__ const E* key_row(const AttnReq& R, int j, int t, bool is_v) {
+  if (t < R.a.n) {
+    if (R.mix.mask != nullptr) {
+      const int64_t tl = int64_t(j) * R.mix.nt + (t >> 6);
+      const int o = t & 63;
+      const uint64_t m = R.mix.mask[tl];
+      const int c = R.mix.cnt[tl];
+      const int below = __popcll(m & ((uint64_t(1) << o) - 1));
+      if ((m >> o) & 1) {
+        const E* base = static_cast<const E*>(is_v ? R.mix.v : R.mix.k);
+        return base + j * R.mix.hstride + int64_t(c + below) * D;
+      }
+      const E* base = static_cast<const E*>(is_v ? R.a.v : R.a.k);
+      return base + j * R.a.hstride + int64_t(t - c - below) * D;
+    }
+    const E* base = static_cast<const E*>(is_v ? R.a.v : R.a.k);
+    return base + j * R.a.hstride + int64_t(t) * D;
+  }
+  t -= R.a.n;
+  if (t < R.b.n) {
+    const E* base = static_cast<const E*>(is_v ? R.b.v : R.b.k);
+    return base + j * R.b.hstride + int64_t(t) * D;
+  }
+  t -= R.b.n;
+  const E* base = static_cast<const E*>(is_v ? R.c.v : R.c.k);
+  return base + j * R.c.hstride + int64_t(t) * D;
+}
 
 // Quantized main region of one request (one layer), plus the per-request
 // view of the draft query.

@@ -36,23 +36,13 @@ struct TileRegs {
   u32x4 v[4];
 };
 
-__device__ __forceinline__ const uint16_t* seg_row(const KVSeg& a, const KVSeg& b, int j, int t, bool is_v) {
-  if (t < a.n) {
-    const uint16_t* base = static_cast<const uint16_t*>(is_v ? a.v : a.k);
-    return base + j * a.hstride + int64_t(t) * D128;
-  }
-  const uint16_t* base = static_cast<const uint16_t*>(is_v ? b.v : b.k);
-  return base + j * b.hstride + int64_t(t - a.n) * D128;
-}
-
 // K: thread (key = tid/4, q = tid%4) loads 16-byte chunks 4e+q (e = 0..3) of its row.
 // V: thread (dc = tid/16, kg = tid%16) loads channels 8dc..8dc+7 of keys 4kg..4kg+3.
-__device__ __forceinline__ void load_tile_bf16(TileRegs& r, const KVSeg& a, const KVSeg& b, int j, int t0,
-                                               int n_keys, int tid) {
+__device__ __forceinline__ void load_tile_bf16(TileRegs& r, const AttnReq& R, int j, int t0, int n_keys, int tid) {
   {
     const int key = tid >> 2, q = tid & 3, t = t0 + key;
     if (t < n_keys) {
-      const uint16_t* row = seg_row(a, b, j, t, false);
+      const uint16_t* row = key_row<uint16_t, D128>(R, j, t, false);
 #pragma unroll
       for (int e = 0; e < 4; e++) r.k[e] = *reinterpret_cast<const u32x4*>(row + 8 * (4 * e + q));
     } else {
@@ -66,7 +56,7 @@ __device__ __forceinline__ void load_tile_bf16(TileRegs& r, const KVSeg& a, cons
     for (int e = 0; e < 4; e++) {
       const int t = t0 + 4 * kg + e;
       if (t < n_keys) {
-        r.v[e] = *reinterpret_cast<const u32x4*>(seg_row(a, b, j, t, true) + 8 * dc);
+        r.v[e] = *reinterpret_cast<const u32x4*>(key_row<uint16_t, D128>(R, j, t, true) + 8 * dc);
       } else {
         r.v[e] = u32x4{0, 0, 0, 0};
       }
@@ -114,7 +104,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
   const int qr0 = rb * ATT_RB;
   if (qr0 >= n_qrows || s >= R.n_splits) return;  // uniform across the workgroup
 
-  const int n_keys = R.a.n + R.b.n;
+  const int n_keys = R.a.n + R.b.n + R.c.n;
   const int key_lo = s * args.split_len;
   const int i_max = (min(qr0 + ATT_RB, n_qrows) - 1) / G;
   const int key_hi = min(min(key_lo + args.split_len, n_keys), R.lim0 + i_max + 1);
@@ -143,12 +133,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
   const float sl2 = args.scale_log2;
 
   TileRegs regs;
-  if (key_lo < key_hi) load_tile_bf16(regs, R.a, R.b, j, key_lo, n_keys, tid);
+  if (key_lo < key_hi) load_tile_bf16(regs, R, j, key_lo, n_keys, tid);
   for (int t0 = key_lo; t0 < key_hi; t0 += ATT_KT) {
     __syncthreads();
     store_tile_bf16(regs, Ks, Vt, tid);
     __syncthreads();
-    if (t0 + ATT_KT < key_hi) load_tile_bf16(regs, R.a, R.b, j, t0 + ATT_KT, n_keys, tid);
+    if (t0 + ATT_KT < key_hi) load_tile_bf16(regs, R, j, t0 + ATT_KT, n_keys, tid);
     if (!wave_active) continue;
 
     // ---- S^T = K Q^T over 4 sub-tiles of 16 keys
@@ -492,7 +482,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs args) {
   const int n_qrows = R.n_rows * G;
   if (qr >= n_qrows || s >= R.n_splits) return;
   const int qi = qr / G, hq = j * G + qr % G;
-  const int n_keys = R.a.n + R.b.n;
+  const int n_keys = R.a.n + R.b.n + R.c.n;
   const int key_lo = s * args.split_len;
   const int lim = R.lim0 + qi;
   const int key_hi = min(min(key_lo + args.split_len, n_keys), lim + 1);
@@ -506,11 +496,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs args) {
       const int t = t0 + r;
       float kv = 0.f, vv = 0.f;
       if (t < n_keys) {
-        const bool in_a = t < R.a.n;
-        const KVSeg& sg = in_a ? R.a : R.b;
-        const int tt = in_a ? t : t - R.a.n;
-        kv = static_cast<const float*>(sg.k)[j * sg.hstride + int64_t(tt) * D64 + lane];
-        vv = static_cast<const float*>(sg.v)[j * sg.hstride + int64_t(tt) * D64 + lane];
+        kv = key_row<float, D64>(R, j, t, false)[lane];
+        vv = key_row<float, D64>(R, j, t, true)[lane];
       }
       Kt[r][lane] = kv;
       Vs[r][lane] = vv;

@@ -315,6 +315,44 @@ __global__ void gather_rows_kernel(const uint8_t* src, int src_cap, int row_byte
   reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src + (int64_t(lh) * src_cap + t) * row_bytes)[w];
 }
 
+// Per (layer*head, 64-position tile): bit o of mask = position 64*tile + o is kept;
+// cnt = kept positions before the tile (idx is ascending, so a binary search finds it).
+__global__ void keep_tiles_kernel(const int32_t* idx, int kk, int n_lh, int n_tiles, uint64_t* mask, int32_t* cnt) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(n_lh) * n_tiles) return;
+  const int lh = int(i / n_tiles), tile = int(i % n_tiles);
+  const int32_t* id = idx + int64_t(lh) * kk;
+  const int t0 = tile * 64;
+  int lo = 0, hi = kk;  // first r with id[r] >= t0
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (id[mid] < t0) lo = mid + 1;
+    else hi = mid;
+  }
+  uint64_t m = 0;
+  for (int r = lo; r < kk && id[r] < t0 + 64; r++) m |= uint64_t(1) << (id[r] - t0);
+  mask[i] = m;
+  cnt[i] = lo;
+}
+
+// Rows of [L*Hkv][src_cap] positions [0, T) that were not kept, compacted in position
+// order into dst [L*Hkv][dst_cap] (row_bytes each), for layers' heads [lh0, lh0 + n_lh).
+__global__ void gather_dropped_kernel(const uint8_t* src, int src_cap, int T, int row_bytes, const uint64_t* mask,
+                                      const int32_t* cnt, int n_tiles, int lh0, uint8_t* dst, int dst_cap) {
+  const int lh = lh0 + blockIdx.y;
+  const int t = blockIdx.x;  // position
+  if (t >= T) return;
+  const int tile = t >> 6, o = t & 63;
+  const uint64_t m = mask[int64_t(lh) * n_tiles + tile];
+  if ((m >> o) & 1) return;
+  const int below = __popcll(m & ((uint64_t(1) << o) - 1));
+  const int r = t - cnt[int64_t(lh) * n_tiles + tile] - below;
+  if (r < 0 || r >= dst_cap) return;  // never for a consistent (idx, mask, cnt)
+  const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + (int64_t(lh) * src_cap + t) * row_bytes);
+  uint32_t* dp = reinterpret_cast<uint32_t*>(dst + (int64_t(blockIdx.y) * dst_cap + r) * row_bytes);
+  for (int w = threadIdx.x; w < row_bytes / 4; w += blockDim.x) dp[w] = sp[w];
+}
+
 }  // namespace
 
 vc_status compress_layout(const vc_compress_desc* d, vc_compress_layout* L) {
@@ -339,9 +377,13 @@ vc_status compress_layout(const vc_compress_desc* d, vc_compress_layout* L) {
     const int64_t kk = std::min<int64_t>(T, std::max<int64_t>(d->keep_total, nrec));
     L->n_main = int32_t(kk);
     L->n_resid = 0;
+    L->n_tiles = int32_t(cdiv(T, 64));
+    L->n_host = int32_t(T - kk);
     L->k_main = sect(LH * kk * D * eb);
     L->v_main = sect(LH * kk * D * eb);
     L->idx = sect(LH * kk * 4);
+    L->keep_mask = sect(LH * L->n_tiles * 8);
+    L->keep_cnt = sect(LH * L->n_tiles * 4);
   } else if (d->kind == VC_QUANT) {
     VC_REQUIRE(d->bits >= 2 && d->bits <= 4, VC_ERR_UNSUPPORTED, "quant: bits must be 2, 3 or 4");
     VC_REQUIRE(d->group == 64 || d->group == 128, VC_ERR_UNSUPPORTED, "quant: group must be 64 or 128");
@@ -350,6 +392,7 @@ vc_status compress_layout(const vc_compress_desc* d, vc_compress_layout* L) {
     const int64_t ng = tq / d->group;
     L->n_main = int32_t(tq);
     L->n_resid = int32_t(T - tq);
+    L->n_host = int32_t(T);
     L->kc = sect(LH * tq * D * d->bits / 8);
     L->vc = sect(LH * tq * D * d->bits / 8);
     L->ks = sect(LH * ng * D * 2);
@@ -500,6 +543,32 @@ vc_status compress_run(const vc_compress_desc* d, const void* k, const void* v, 
                        d->src_cap, D * eb, idx, kk, n_lh, o + L.v_main);
     VC_LAUNCH_CHECK();
   }
+  {
+    const int64_t n = int64_t(n_lh) * L.n_tiles;
+    hipLaunchKernelGGL(keep_tiles_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, idx, kk, n_lh, L.n_tiles,
+                       reinterpret_cast<uint64_t*>(o + L.keep_mask), reinterpret_cast<int32_t*>(o + L.keep_cnt));
+    VC_LAUNCH_CHECK();
+  }
+  return VC_OK;
+}
+
+vc_status gather_dropped(const vc_compress_desc* d, const void* comp, const void* src, int src_cap, int lh0, int n_lh,
+                         void* dst, int dst_cap, hipStream_t s) {
+  vc_compress_layout L;
+  vc_status st = compress_layout(d, &L);
+  if (st) return st;
+  VC_REQUIRE(d->kind == VC_TOKDROP, VC_ERR_ARG, "gather_dropped: not a token-drop cache");
+  VC_REQUIRE(lh0 >= 0 && n_lh > 0 && lh0 + n_lh <= d->n_layers * d->n_kv_heads && dst_cap >= L.n_host &&
+                 src_cap >= d->seq_len,
+             VC_ERR_ARG, "gather_dropped: bad range");
+  if (L.n_host == 0) return VC_OK;
+  const int eb = d->dtype == VC_BF16 ? 2 : 4;
+  const uint8_t* o = static_cast<const uint8_t*>(comp);
+  hipLaunchKernelGGL(gather_dropped_kernel, dim3(d->seq_len, n_lh), dim3(64), 0, s, static_cast<const uint8_t*>(src),
+                     src_cap, d->seq_len, d->head_dim * eb, reinterpret_cast<const uint64_t*>(o + L.keep_mask),
+                     reinterpret_cast<const int32_t*>(o + L.keep_cnt), L.n_tiles, lh0, static_cast<uint8_t*>(dst),
+                     dst_cap);
+  VC_LAUNCH_CHECK();
   return VC_OK;
 }
 

@@ -2,8 +2,10 @@
 
 Per request ("Verifying Without Giving Back the Speedup", VeriCache: Making
 Lossy KV Compression Exact): the compressed cache and a tail of exact rows
-stay on the GPU; the full cache lives in pinned host memory and is staged into
-one of two device slots on a copy stream only for verification.  Requests
+stay on the GPU; the rest of the full cache lives in pinned host memory and is
+staged into one of two device slots on a copy stream only for verification.
+Rows the GPU already holds exactly (the committed tail, and the kept prompt
+rows of a token-drop cache) are not kept on the host and never cross PCIe.  Requests
 start drafting at staggered ticks (request r joins after floor(r * x / B)
 ticks, the study note's "10 requests, x = 30: one verification every 3 draft
 rounds"), so one request's transfer and verification overlap the others'
@@ -82,6 +84,7 @@ class Request:
     tail_v: torch.Tensor = None
     full_k: object = None              # pinned host (HostBuffer)
     full_v: object = None
+    n_host: int = 0                    # host rows per (layer, KV head)
     rows: torch.Tensor = None          # device int32 [x + 1]
     vtail_k: torch.Tensor = None
     vtail_v: torch.Tensor = None
@@ -121,7 +124,6 @@ class Engine:
         T = int(prompt.numel())
         L, Hkv, D, Hq = s.n_layers, s.n_kv_heads, s.head_dim, s.n_q_heads
         r = Request(idx=len(self.reqs), T=T, x=x, n_tokens=n_tokens)
-        full_cap = T + n_tokens + x + 2
         kd = torch.empty(L, Hkv, T, D, dtype=self.dt, device=self.device)
         vd = torch.empty_like(kd)
         W = min(self.spec.obs_window, T)
@@ -132,6 +134,8 @@ class Engine:
         del ws
         r.cd = compress_spec_desc(self.spec, s, T, T)
         r.comp = B.vc_compress(r.cd, kd, vd, q_obs)
+        r.n_host = B.compress_layout(r.cd).n_host
+        full_cap = max(r.n_host, 1)
         eb = 2 if self.dt == torch.bfloat16 else 4
         r.full_k = B.HostBuffer(L * Hkv * full_cap * D * eb)
         r.full_v = B.HostBuffer(L * Hkv * full_cap * D * eb)
@@ -167,9 +171,11 @@ class Engine:
         self.ws_verify = self.m.workspace(max_x + 1, max_ctx)
         L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
         n_slots = min(2, n)
+        slot_rows = max(max(r.n_host for r in self.reqs), 1)
         if not self.slots:
-            self.slots = [(torch.empty(L, Hkv, max_ctx, D, dtype=self.dt, device=self.device),
-                           torch.empty(L, Hkv, max_ctx, D, dtype=self.dt, device=self.device)) for _ in range(n_slots)]
+            self.slots = [(torch.empty(L, Hkv, slot_rows, D, dtype=self.dt, device=self.device),
+                           torch.empty(L, Hkv, slot_rows, D, dtype=self.dt, device=self.device))
+                          for _ in range(n_slots)]
             self.slot_free_ev = [None] * n_slots
             self.slot_owner = [None] * n_slots
 
@@ -315,27 +321,48 @@ def greedy_resident(model: B.Model, prompt: torch.Tensor, n_tokens: int, chunk: 
     return out.tolist(), time.perf_counter() - t0, (kd, vd)
 
 
-def greedy_from_host(model: B.Model, r: Request, n_steps: int, slot, ws: torch.Tensor, copy_stream):
+def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tensor, n_steps: int, ws: torch.Tensor,
+                     copy_stream):
     """Full-KV greedy decoding with the cache in pinned host memory, the
-    comparator VeriCache is measured against: every token stages the request's
-    whole full KV over PCIe, runs one vc_verify row, and appends the new row to
-    the host copy.  Advances the request; returns (tokens, seconds)."""
-    sk, sv = slot
+    comparator VeriCache is measured against: a plain request (no compressed
+    cache) whose whole context lives on the host; every token stages it over
+    PCIe, runs one vc_verify row, and appends the new row to the host copy.
+    prompt_kv: device (K, V) [L][Hkv][cap][D] holding prompt rows [0, T);
+    first_token: device int32 [1], the token at position T.
+    Returns (tokens after first_token, seconds)."""
+    s = model.shape
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
+    eb = 2 if dt == torch.bfloat16 else 4
+    cap = T + n_steps + 1
+    hk = B.HostBuffer(L * Hkv * cap * D * eb)
+    hv = B.HostBuffer(L * Hkv * cap * D * eb)
+    sk = torch.empty(L, Hkv, cap, D, dtype=dt, device=prompt_kv[0].device)
+    sv = torch.empty_like(sk)
+    vk = torch.empty(L, Hkv, 1, D, dtype=dt, device=sk.device)
+    vv = torch.empty_like(vk)
+    rows = first_token.clone()
+    req = Req(ctx_len=T, full_k_host=hk.data_ptr(), full_v_host=hv.data_ptr(), full_cap=cap, rows=rows.data_ptr())
+    model.offload(req, prompt_kv[0], prompt_kv[1], T)
     cs = torch.cuda.current_stream()
     toks = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(n_steps):
-        model.stage(r.req, sk, sv, 0, model.shape.n_layers, copy_stream=copy_stream)
+        model.stage(req, sk, sv, 0, L, copy_stream=copy_stream)
         ev = torch.cuda.Event()
         ev.record(copy_stream)
         cs.wait_event(ev)
-        model.verify_raw(r.req, sk.data_ptr(), sv.data_ptr(), sk.shape[-2], r.rows.data_ptr(), 1, r.rows.data_ptr(),
-                         r.vtail_k.data_ptr(), r.vtail_v.data_ptr(), r.vtail_k.shape[-2], ws)
+        model.verify_raw(req, sk.data_ptr(), sv.data_ptr(), cap, rows.data_ptr(), 1, rows.data_ptr(),
+                         vk.data_ptr(), vv.data_ptr(), 1, ws)
         done = torch.cuda.Event()
         done.record(cs)
-        model.commit(r.req, 0, r.vtail_k, r.vtail_v, after_event=done, copy_stream=copy_stream)
-        toks.append(r.rows[:1])
+        model.commit(req, 0, vk, vv, after_event=done, copy_stream=copy_stream)
+        toks.append(rows.clone())
     torch.cuda.synchronize()
     copy_stream.synchronize()
-    return [int(t.item()) for t in toks], time.perf_counter() - t0
+    secs = time.perf_counter() - t0
+    del sk, sv
+    hk.free()
+    hv.free()
+    return [int(t.item()) for t in toks], secs

@@ -160,6 +160,7 @@ def main():
     # whose whole cache is on the host (after the timed region); its tokens must be the ones
     # VeriCache emitted for request 0
     r0 = eng.reqs[0]
+    eng.release_host()  # the comparator needs host memory for a whole full KV
     first = torch.tensor([r0.emitted[0]], dtype=torch.int32, device="cuda")
     toks, bsecs = greedy_from_host(model, r0.prefill_kv, r0.T, first, args.baseline_steps, eng.ws_verify,
                                    eng.copy_stream)

@@ -17,7 +17,7 @@ from ._vc import (VC_BF16, VC_F32, VC_QUANT, VC_TOKDROP, AttnDesc, AttnDraftReq,
 __all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "CompressDesc", "Req", "Model", "compress_desc",
            "compress_layout", "vc_compress", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
            "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes",
-           "profile_enable", "profile_read", "HostBuffer"]
+           "profile_enable", "profile_read", "HostBuffer", "PageableBuffer"]
 
 
 def stream_handle(s: torch.cuda.Stream | None = None) -> int:
@@ -221,6 +221,22 @@ def profile_read() -> dict:
     st = ProfileStats()
     call("vc_profile_read", C.byref(st))
     return {"launches": st.launches, "ms": st.total_ms, "bytes": st.bytes}
+
+
+class PageableBuffer:
+    """Ordinary (pageable) host memory for host rows beyond the pinned budget.  Copies
+    from it block the calling thread (the runtime stages them through its own pinned
+    buffers), so the scheduler issues them from a worker thread."""
+
+    def __init__(self, nbytes: int):
+        self.t = torch.empty(nbytes, dtype=torch.uint8)
+        self.nbytes = nbytes
+
+    def data_ptr(self) -> int:
+        return self.t.data_ptr()
+
+    def free(self):
+        self.t = None
 
 
 class HostBuffer:

@@ -394,8 +394,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     rs += shfl_xor(rs, 32);
     l_run = l_run * alpha + rs;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {  // the running max rarely moves after the first tiles; x * 1 == x
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) oacc[dt] *= alpha;
+      for (int dt = 0; dt < 8; dt++) oacc[dt] *= alpha;
+    }
 
     // LDS operations of one wave complete in issue order; the fence keeps the compiler
     // from moving the fragment reads above the tile stores (and later stores above them).

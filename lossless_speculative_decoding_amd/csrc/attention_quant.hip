@@ -1,24 +1,30 @@
 // Draft-step decode attention over a per-group quantized KV cache (2/3/4-bit).
 //
-// One workgroup (256 threads) per (request, KV head, split of 64-key tiles).
-// Per tile, all threads turn packed codes into exact small integers in fp16
-// (magic-number trick: 0x6400 | c is 1024 + c, then subtract 1024) and stage
-// them in LDS: K codes row-major (one row per key), V codes transposed (the
-// packed layout is already per channel).  The quantization scale and zero are
-// never applied to the codes; they are folded into the operands of the one
-// computing wave instead:
+// One workgroup = 4 waves = (request, KV head, split); wave w streams the 64-key tiles
+// w, w + 4, ... of the split with its own online softmax, and the four states are merged
+// in wave order at the end.  Nothing goes through LDS on the way: every lane loads
+// exactly the packed codes its MFMA fragments need and turns them into exact small
+// integers in fp16 (magic-number trick: 0x6400 | c is 1024 + c, then subtract).  The
+// quantization scale and zero are never applied to the codes; they are folded into
+// the other operand instead:
 //     q . k_t       = sum_d (q_d s_gd) c_td + sum_d q_d z_gd        (K: scale/zero per channel and token group)
 //     sum_t p_t v_t = sum_t (p_t s_t) c_t  + sum_t p_t z_t          (V: scale/zero per token and channel group)
-// so the MFMA operands are Q' = q*s, the codes, and P' = p*s (scaled by 2^10
-// to stay out of the fp16 subnormal range).  Codes are centred (c - 2^(b-1),
-// zero moves to z + 2^(b-1) s) so the folded sum does not cancel against a
-// large zero term, and Q' and P' are each carried as an fp16 hi/lo pair (two
-// MFMAs), which leaves about 22 significant bits in every score and weight.
+// so the MFMA operands are Q' = q*s, the codes, and P' = p*s (scaled by 2^10 to stay
+// out of the fp16 subnormal range).  Codes are centred (c - 2^(b-1), the zero moves to
+// z + 2^(b-1) s) so the folded sums do not cancel against a large zero term (keeping the
+// 1024 of the conversion in the V codes instead costs ~5e-3 relative on outlier-heavy
+// heads), and Q' and P' are each carried as an fp16 hi/lo pair (two MFMAs), which leaves
+// about 22 significant bits in every score and weight.
 //
-// Within each group of 8 (4-bit) or 16 (2-bit) codes the conversion yields the
-// codes in the order [0,4,1,5,2,6,3,7] (resp. [0,8,1,9,...,7,15]); LDS
-// positions keep that order, for channels (K columns, mirrored in Q') and for
-// keys (K rows and V^T columns, mirrored in the key index of each score).
+// Operand assignment.  Lane l (g = l / 16, r = l % 16) holds for S^T = C_K Q'^T the
+// K codes of channels [32g, 32g + 32) of key 16 (r / 4) + 4 kt + r % 4 of the tile
+// (16-key block kt): one contiguous 4*BITS-byte piece of a code row, so a wave reads
+// whole rows.  The score accumulator of lane (g, head r) then holds keys
+// [16g, 16g + 16), which are exactly the keys whose V codes the lane loads for
+// O^T += C_V^T P'^T: the 16-code run of channel 16 dt + r starting at token 16g (one
+// contiguous 2*BITS-byte piece of a per-channel code row).  Within a conversion group
+// of 8 (4-bit) or 16 (2-bit) codes the conversion yields the order [0,4,1,5,2,6,3,7]
+// (resp. [0,8,1,9,...,7,15]); Q' and P' are built in that same order.
 #include "attention.h"
 
 namespace vc {
@@ -26,8 +32,6 @@ namespace vc {
 namespace {
 
 constexpr int D = 128;
-constexpr int KS_PITCH = D + 8;
-constexpr int VT_PITCH = ATT_KT + 8;
 constexpr float P_SCALE = 1024.f;
 constexpr float P_UNSCALE = 1.f / 1024.f;
 
@@ -36,6 +40,13 @@ template <int BITS>
 __device__ __forceinline__ uint32_t centre(uint32_t x) {
   constexpr float off = 1024.f + float(1 << (BITS - 1));
   return bitcast<uint32_t>(bitcast<f16x2>(x) - f16x2{(_Float16)off, (_Float16)off});
+}
+
+// (x & mask) | 0x64006400 (two codes -> two fp16 numbers 1024 + c) as one VALU operation
+__device__ __forceinline__ uint32_t and_or_mag(uint32_t x, uint32_t mask) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(0x64006400u));
+  return r;
 }
 
 // position -> code index within a conversion group
@@ -51,40 +62,10 @@ __device__ __forceinline__ int perm_pos(int p) {
     return p;
   }
 }
-// code index -> position (inverse of perm_pos)
-template <int BITS>
-__device__ __forceinline__ int inv_perm(int c) {
-  if constexpr (BITS == 4) {
-    const int k = c & 7;
-    return (c & ~7) | ((k < 4) ? 2 * k : 2 * (k - 4) + 1);
-  } else if constexpr (BITS == 2) {
-    const int k = c & 15;
-    return (c & ~15) | ((k < 8) ? 2 * k : 2 * (k - 8) + 1);
-  } else {
-    return c;
-  }
-}
-
 template <int BITS>
 struct Codes32 {
   uint32_t w[BITS];  // 32 * BITS bits
 };
-
-template <int BITS>
-__device__ __forceinline__ Codes32<BITS> ld_codes(const uint8_t* src) {
-  Codes32<BITS> c;
-  if constexpr (BITS == 4) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(src);
-    c.w[0] = x.x; c.w[1] = x.y; c.w[2] = x.z; c.w[3] = x.w;
-  } else if constexpr (BITS == 2) {
-    const u32x2 x = *reinterpret_cast<const u32x2*>(src);
-    c.w[0] = x.x; c.w[1] = x.y;
-  } else {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(src);
-    c.w[0] = p[0]; c.w[1] = p[1]; c.w[2] = p[2];
-  }
-  return c;
-}
 
 template <int BITS>
 __device__ __forceinline__ void cvt_codes(const Codes32<BITS>& c, u32x4 out[4]) {
@@ -93,23 +74,23 @@ __device__ __forceinline__ void cvt_codes(const Codes32<BITS>& c, u32x4 out[4]) 
 #pragma unroll
     for (int w = 0; w < 4; w++) {
       const uint32_t x = c.w[w];
-      out[w].x = centre<BITS>((x & 0x000F000Fu) | MAG);
-      out[w].y = centre<BITS>(((x >> 4) & 0x000F000Fu) | MAG);
-      out[w].z = centre<BITS>(((x >> 8) & 0x000F000Fu) | MAG);
-      out[w].w = centre<BITS>(((x >> 12) & 0x000F000Fu) | MAG);
+      out[w].x = centre<BITS>(and_or_mag(x, 0x000F000Fu));
+      out[w].y = centre<BITS>(and_or_mag(x >> 4, 0x000F000Fu));
+      out[w].z = centre<BITS>(and_or_mag(x >> 8, 0x000F000Fu));
+      out[w].w = centre<BITS>(and_or_mag(x >> 12, 0x000F000Fu));
     }
   } else if constexpr (BITS == 2) {
 #pragma unroll
     for (int w = 0; w < 2; w++) {
       const uint32_t x = c.w[w];
-      out[2 * w].x = centre<BITS>((x & 0x00030003u) | MAG);
-      out[2 * w].y = centre<BITS>(((x >> 2) & 0x00030003u) | MAG);
-      out[2 * w].z = centre<BITS>(((x >> 4) & 0x00030003u) | MAG);
-      out[2 * w].w = centre<BITS>(((x >> 6) & 0x00030003u) | MAG);
-      out[2 * w + 1].x = centre<BITS>(((x >> 8) & 0x00030003u) | MAG);
-      out[2 * w + 1].y = centre<BITS>(((x >> 10) & 0x00030003u) | MAG);
-      out[2 * w + 1].z = centre<BITS>(((x >> 12) & 0x00030003u) | MAG);
-      out[2 * w + 1].w = centre<BITS>(((x >> 14) & 0x00030003u) | MAG);
+      out[2 * w].x = centre<BITS>(and_or_mag(x, 0x00030003u));
+      out[2 * w].y = centre<BITS>(and_or_mag(x >> 2, 0x00030003u));
+      out[2 * w].z = centre<BITS>(and_or_mag(x >> 4, 0x00030003u));
+      out[2 * w].w = centre<BITS>(and_or_mag(x >> 6, 0x00030003u));
+      out[2 * w + 1].x = centre<BITS>(and_or_mag(x >> 8, 0x00030003u));
+      out[2 * w + 1].y = centre<BITS>(and_or_mag(x >> 10, 0x00030003u));
+      out[2 * w + 1].z = centre<BITS>(and_or_mag(x >> 12, 0x00030003u));
+      out[2 * w + 1].w = centre<BITS>(and_or_mag(x >> 14, 0x00030003u));
     }
   } else {
     const uint64_t lo = uint64_t(c.w[0]) | (uint64_t(c.w[1]) << 32);
@@ -127,30 +108,128 @@ __device__ __forceinline__ void cvt_codes(const Codes32<BITS>& c, u32x4 out[4]) 
 }
 
 __device__ __forceinline__ float h2f(uint16_t h) { return float(bitcast<_Float16>(h)); }
+__device__ __forceinline__ float h2f_lo(uint32_t w) { return h2f(uint16_t(w & 0xffffu)); }
+__device__ __forceinline__ float h2f_hi(uint32_t w) { return h2f(uint16_t(w >> 16)); }
+// element i of a packed run of 16-bit values held as dwords
+__device__ __forceinline__ uint32_t half16(const uint32_t* w, int i) { return (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu); }
+
+// 16 V codes (one channel, 16 consecutive tokens): 2*BITS bytes
+template <int BITS>
+struct VCodes16 {
+  uint32_t w[2];
+};
 
 template <int BITS>
-__global__ __launch_bounds__(256) void attn_quant_kernel(const QuantArgs args) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[ATT_KT * KS_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VT_PITCH];
-  __shared__ float vsc[ATT_KT][2];
-  __shared__ float vzr[ATT_KT][2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ VCodes16<BITS> ld_vcodes(const uint8_t* src) {
+  VCodes16<BITS> c;
+  if constexpr (BITS == 2) {
+    c.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
+    c.w[1] = 0;
+  } else if constexpr (BITS == 4) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+    c.w[0] = x.x;
+    c.w[1] = x.y;
+  } else {  // 6 bytes at a 2-byte boundary
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(src);
+    c.w[0] = uint32_t(p[0]) | (uint32_t(p[1]) << 16);
+    c.w[1] = p[2];
+  }
+  return c;
+}
+
+// -> 16 centred fp16 codes; output position i holds code perm_pos<BITS>(i)
+template <int BITS>
+__device__ __forceinline__ void cvt_vcodes(const VCodes16<BITS>& c, u32x4 out[2]) {
+  if constexpr (BITS == 2) {
+    const uint32_t x = c.w[0];
+    uint32_t r[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) r[k] = centre<BITS>(and_or_mag(x >> (2 * k), 0x00030003u));
+    out[0] = u32x4{r[0], r[1], r[2], r[3]};
+    out[1] = u32x4{r[4], r[5], r[6], r[7]};
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int w = 0; w < 2; w++) {
+      const uint32_t x = c.w[w];
+      out[w] = u32x4{centre<BITS>(and_or_mag(x, 0x000F000Fu)), centre<BITS>(and_or_mag(x >> 4, 0x000F000Fu)),
+                     centre<BITS>(and_or_mag(x >> 8, 0x000F000Fu)), centre<BITS>(and_or_mag(x >> 12, 0x000F000Fu))};
+    }
+  } else {
+    constexpr uint32_t MAG = 0x64006400u;
+    const uint64_t bits = uint64_t(c.w[0]) | (uint64_t(c.w[1]) << 32);
+    uint32_t r[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+      const uint32_t f = uint32_t(bits >> (6 * m));
+      r[m] = centre<BITS>(((f & 7u) | ((f & 0x38u) << 13)) | MAG);
+    }
+    out[0] = u32x4{r[0], r[1], r[2], r[3]};
+    out[1] = u32x4{r[4], r[5], r[6], r[7]};
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ Codes32<BITS> ld_kcodes(const uint8_t* src) {
+  Codes32<BITS> c;
+  if constexpr (BITS == 4) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+    c.w[0] = x.x; c.w[1] = x.y; c.w[2] = x.z; c.w[3] = x.w;
+  } else if constexpr (BITS == 2) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+    c.w[0] = x.x; c.w[1] = x.y;
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(src);
+    c.w[0] = __builtin_nontemporal_load(p);
+    c.w[1] = __builtin_nontemporal_load(p + 1);
+    c.w[2] = __builtin_nontemporal_load(p + 2);
+  }
+  return c;
+}
+
+template <int BITS>
+__device__ __forceinline__ void ld_ktile(Codes32<BITS> k[4], const uint8_t* kc, int t0, int r16, int g) {
+  constexpr int KROW = 16 * BITS;  // bytes per K code row (128 channels)
+#pragma unroll
+  for (int kt = 0; kt < 4; kt++) {
+    const int key = t0 + 16 * (r16 >> 2) + 4 * kt + (r16 & 3);
+    k[kt] = ld_kcodes<BITS>(kc + int64_t(key) * KROW + 4 * BITS * g);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void ld_vtile(VCodes16<BITS> v[8], const uint8_t* vc, int t0, int r16, int g) {
+  const uint8_t* vb = vc + int64_t(t0 >> 6) * D * (8 * BITS);
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) v[dt] = ld_vcodes<BITS>(vb + (16 * dt + r16) * (8 * BITS) + 2 * BITS * g);
+}
+
+constexpr int QWAVES = 4;
+constexpr int QRED = D + 4;  // floats per head in the merge buffer
+
+// NH: V channel groups per token (1 for group 128, 2 for group 64), a template parameter so
+// that every register index below is a compile-time constant
+template <int BITS, int NH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_quant_kernel(const QuantArgs args) {
+  __shared__ float red[QWAVES * 16 * QRED];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int z = blockIdx.z;
   if (z >= args.n_req) return;
   const QuantReq& R = args.r[z];
-  const int Hkv = args.Hkv, G = args.G, Hq = args.Hq;
+  const int G = args.G, Hq = args.Hq;
   const int j = blockIdx.x;
   const int s = blockIdx.y;
-  if (s >= R.n_splits) return;
+  if (s >= R.n_splits) return;  // uniform across the workgroup
   const int Tq = R.m.tq;
   const int grp_sz = args.group;
-  const int nh = D / grp_sz;      // V channel groups per token (1 or 2)
-  const bool two_groups = nh == 2;
-  const int ng = Tq / grp_sz;     // K token groups
+  constexpr bool two = NH == 2;
+  constexpr int nh = NH;
+  const int ng = Tq / grp_sz;
   const int nblk = Tq / 64;
   const int key_lo = s * args.split_len;
   const int key_hi = min(key_lo + args.split_len, Tq);
-  constexpr int RB = 4 * BITS;    // bytes of 32 codes
+  const int r16 = lane & 15, g = lane >> 4;
+  const bool head_ok = r16 < G;
+  const int hq = j * G + (head_ok ? r16 : 0);
 
   const uint8_t* kc = R.m.kc + int64_t(j) * Tq * (D * BITS / 8);
   const uint8_t* vc = R.m.vc + int64_t(j) * nblk * D * (8 * BITS);
@@ -159,21 +238,7 @@ __global__ __launch_bounds__(256) void attn_quant_kernel(const QuantArgs args) {
   const uint16_t* vs = R.m.vs + int64_t(j) * Tq * nh;
   const uint16_t* vz = R.m.vz + int64_t(j) * Tq * nh;
 
-  const int grp = lane >> 4;
-  const int qrow = lane & 15;
-  const bool row_ok = qrow < G;
-  const int hq = j * G + (row_ok ? qrow : 0);
-
-  // wave 0: the query row of this lane, at the permuted channel positions it feeds
-  float qv[4][8];
-  if (wave == 0) {
-    const uint16_t* qp = static_cast<const uint16_t*>(R.q) + int64_t(hq) * D;
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-#pragma unroll
-      for (int e = 0; e < 8; e++) qv[c][e] = row_ok ? bf2f(qp[perm_pos<BITS>(32 * c + 8 * grp + e)]) : 0.f;
-    }
-  }
+  const uint16_t* qp = static_cast<const uint16_t*>(R.q) + int64_t(hq) * D + 32 * g;  // this lane's 32 channels
   constexpr float C0 = float(1 << (BITS - 1));
   u32x4 qf[4], qlo[4];
   float kbias = 0.f;
@@ -181,68 +246,63 @@ __global__ __launch_bounds__(256) void attn_quant_kernel(const QuantArgs args) {
   f32x4 oacc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; dt++) oacc[dt] = f32x4{0, 0, 0, 0};
-  float vb[2] = {0.f, 0.f};
+  float vb0 = 0.f, vb1 = 0.f;
   float m_run = NEG_INF, l_run = 0.f;
   const float sl2 = args.scale_log2;
 
-  for (int t0 = key_lo; t0 < key_hi; t0 += ATT_KT) {
-    // ---- cooperative conversion of this tile
-    Codes32<BITS> kcw, vcw;
+  Codes32<BITS> kr[4];
+  VCodes16<BITS> vr[8];
+  int t0 = key_lo + ATT_KT * wave;
+  if (t0 < key_hi) {
+    ld_ktile<BITS>(kr, kc, t0, r16, g);
+    ld_vtile<BITS>(vr, vc, t0, r16, g);
+  }
+  for (; t0 < key_hi; t0 += QWAVES * ATT_KT) {
+    // ---- V scales and zeros of this lane's 16 keys [t0 + 16g, t0 + 16g + 16)
+    uint32_t vsw[16], vzw[16];
     {
-      const int key = tid >> 2, part = tid & 3;
-      kcw = ld_codes<BITS>(kc + int64_t(t0 + key) * (D * BITS / 8) + part * RB);
-      const int ch = tid >> 1, half = tid & 1;
-      vcw = ld_codes<BITS>(vc + (int64_t(t0 / 64) * D + ch) * (8 * BITS) + half * RB);
-    }
-    float vsv[2] = {0.f, 0.f}, vzv[2] = {0.f, 0.f};
-    if (tid < ATT_KT) {
-      const int t = t0 + perm_pos<BITS>(tid);
-      for (int h = 0; h < nh; h++) {
-        vsv[h] = h2f(vs[int64_t(t) * nh + h]);
-        vzv[h] = fmaf(vsv[h], float(1 << (BITS - 1)), h2f(vz[int64_t(t) * nh + h]));  // zero of the centred code
+      // 16 * nh fp16 values each, 32-byte aligned (sections are 256-byte aligned, Tq is a multiple of 64)
+      const u32x4* sp = reinterpret_cast<const u32x4*>(vs + int64_t(t0 + 16 * g) * nh);
+      const u32x4* zp = reinterpret_cast<const u32x4*>(vz + int64_t(t0 + 16 * g) * nh);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const u32x4 a = (i < 2 * nh) ? sp[i] : u32x4{0, 0, 0, 0};
+        const u32x4 b = (i < 2 * nh) ? zp[i] : u32x4{0, 0, 0, 0};
+        vsw[4 * i] = a.x; vsw[4 * i + 1] = a.y; vsw[4 * i + 2] = a.z; vsw[4 * i + 3] = a.w;
+        vzw[4 * i] = b.x; vzw[4 * i + 1] = b.y; vzw[4 * i + 2] = b.z; vzw[4 * i + 3] = b.w;
       }
     }
-    __syncthreads();  // previous tile fully consumed
-    {
-      u32x4 kout[4], vout[4];
-      cvt_codes<BITS>(kcw, kout);
-      cvt_codes<BITS>(vcw, vout);
-      const int key = tid >> 2, part = tid & 3;
-      const int row = inv_perm<BITS>(key);
+    // ---- Q' = q * s_g (fp16 hi/lo) and the key bias when the token group changes
+    const int tg = t0 / grp_sz;
+    if (tg != cur_group) {
+      cur_group = tg;
+      uint32_t sw[16], zw[16], qw[16];
+      const u32x4* sp = reinterpret_cast<const u32x4*>(ks + int64_t(tg) * D + 32 * g);
+      const u32x4* zp = reinterpret_cast<const u32x4*>(kz + int64_t(tg) * D + 32 * g);
+      const u32x4* qv = reinterpret_cast<const u32x4*>(qp);
 #pragma unroll
-      for (int q = 0; q < 4; q++) *reinterpret_cast<u32x4*>(Ks + row * KS_PITCH + 32 * part + 8 * q) = kout[q];
-      const int ch = tid >> 1, half = tid & 1;
-#pragma unroll
-      for (int q = 0; q < 4; q++) *reinterpret_cast<u32x4*>(Vt + ch * VT_PITCH + 32 * half + 8 * q) = vout[q];
-      if (tid < ATT_KT) {
-        vsc[tid][0] = vsv[0]; vsc[tid][1] = vsv[1];
-        vzr[tid][0] = vzv[0]; vzr[tid][1] = vzv[1];
+      for (int i = 0; i < 4; i++) {
+        const u32x4 a = sp[i], b = zp[i], c = head_ok ? qv[i] : u32x4{0, 0, 0, 0};
+        sw[4 * i] = a.x; sw[4 * i + 1] = a.y; sw[4 * i + 2] = a.z; sw[4 * i + 3] = a.w;
+        zw[4 * i] = b.x; zw[4 * i + 1] = b.y; zw[4 * i + 2] = b.z; zw[4 * i + 3] = b.w;
+        qw[4 * i] = c.x; qw[4 * i + 1] = c.y; qw[4 * i + 2] = c.z; qw[4 * i + 3] = c.w;
       }
-    }
-    __syncthreads();
-    if (wave != 0) continue;
-
-    // ---- Q' = q * s_g and the key bias of this token group
-    const int g = t0 / grp_sz;
-    if (g != cur_group) {
-      cur_group = g;
       float b = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; c++) {
         uint32_t w[4], wl[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; e2++) {
-          const int ch0 = perm_pos<BITS>(32 * c + 8 * grp + 2 * e2);
-          const int ch1 = perm_pos<BITS>(32 * c + 8 * grp + 2 * e2 + 1);
-          const float s0 = h2f(ks[int64_t(g) * D + ch0]), s1 = h2f(ks[int64_t(g) * D + ch1]);
-          const float z0 = h2f(kz[int64_t(g) * D + ch0]), z1 = h2f(kz[int64_t(g) * D + ch1]);
-          const float a0 = qv[c][2 * e2], a1 = qv[c][2 * e2 + 1];
-          b = fmaf(a0, fmaf(s0, C0, z0), b);
-          b = fmaf(a1, fmaf(s1, C0, z1), b);
-          const float p0 = a0 * s0, p1 = a1 * s1;
-          const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
-          w[e2] = bitcast<uint32_t>(f16x2{h0, h1});
-          wl[e2] = bitcast<uint32_t>(f16x2{(_Float16)(p0 - float(h0)), (_Float16)(p1 - float(h1))});
+          float pr[2];
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            const int ch = perm_pos<BITS>(8 * c + 2 * e2 + h);  // channel 32g + ch
+            const float qd = (ch & 1) ? hi_bf(qw[ch >> 1]) : lo_bf(qw[ch >> 1]);
+            const float sd = h2f(uint16_t(half16(sw, ch))), zd = h2f(uint16_t(half16(zw, ch)));
+            b = fmaf(qd, fmaf(sd, C0, zd), b);
+            pr[h] = qd * sd;
+          }
+          split_h2(pr[0], pr[1], w[e2], wl[e2]);
         }
         qf[c] = u32x4{w[0], w[1], w[2], w[3]};
         qlo[c] = u32x4{wl[0], wl[1], wl[2], wl[3]};
@@ -252,24 +312,30 @@ __global__ __launch_bounds__(256) void attn_quant_kernel(const QuantArgs args) {
       kbias = b;
     }
 
-    // ---- S^T = C_K Q'^T
+    // ---- S^T = C_K Q'^T: lane (g, head r) gets keys 16g + 4kt + jj
     f32x4 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
+      u32x4 ka[4];
+      cvt_codes<BITS>(kr[kt], ka);
       sacc[kt] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int c = 0; c < 4; c++) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (16 * kt + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
-        sacc[kt] = mfma_f16(ka, qf[c], sacc[kt]);
-        sacc[kt] = mfma_f16(ka, qlo[c], sacc[kt]);
+        sacc[kt] = mfma_f16(ka[c], qf[c], sacc[kt]);
+        sacc[kt] = mfma_f16(ka[c], qlo[c], sacc[kt]);
       }
     }
+    // the next tile's K codes are in flight during the softmax and P.V of this one
+    const int tn = t0 + QWAVES * ATT_KT;
+    if (tn < key_hi) ld_ktile<BITS>(kr, kc, tn, r16, g);
+
+    // ---- online softmax per head (every key of a tile is visible)
     float mx = NEG_INF;
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
-        const float v = row_ok ? (sacc[kt][jj] + kbias) * sl2 : NEG_INF;
+        const float v = (sacc[kt][jj] + kbias) * sl2;
         sacc[kt][jj] = v;
         mx = fmaxf(mx, v);
       }
@@ -277,14 +343,13 @@ __global__ __launch_bounds__(256) void attn_quant_kernel(const QuantArgs args) {
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const bool none = (m_new == NEG_INF);
-    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
-        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sacc[kt][jj] - m_new);
+        const float p = __builtin_amdgcn_exp2f(sacc[kt][jj] - m_new);
         sacc[kt][jj] = p;
         rs += p;
       }
@@ -293,70 +358,103 @@ __global__ __launch_bounds__(256) void attn_quant_kernel(const QuantArgs args) {
     rs += shfl_xor(rs, 32);
     l_run = l_run * alpha + rs;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {  // the running max rarely moves after the first tiles; x * 1 == x
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) oacc[dt] *= alpha;
-    vb[0] *= alpha;
-    vb[1] *= alpha;
+      for (int dt = 0; dt < 8; dt++) oacc[dt] *= alpha;
+      vb0 *= alpha;
+      vb1 *= alpha;
+    }
 
-    // ---- O^T += C_V^T P'^T, one P' per channel group of V
+    // ---- P' = p s (per V channel group) as fp16 hi/lo, in the V conversion order, and the V bias
+    u32x4 pb[2][2], pl[2][2];  // [32-key chunk][V channel group]
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; kc2++) {
-      float pv[8];
-      int pos[8];
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        pos[e] = 32 * kc2 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-        pv[e] = sacc[2 * kc2 + (e >> 2)][e & 3] * P_SCALE;
-      }
-      // P' for each channel group of V (group 1 only exists when the V group is 64 channels)
       uint32_t w0[4], w1[4], l0[4], l1[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; e2++) {
-        const int p0 = pos[2 * e2], p1 = pos[2 * e2 + 1];
-        const float x0 = pv[2 * e2], x1 = pv[2 * e2 + 1];
-        split_h2(x0 * vsc[p0][0], x1 * vsc[p1][0], w0[e2], l0[e2]);
-        split_h2(x0 * vsc[p0][1], x1 * vsc[p1][1], w1[e2], l1[e2]);
-        vb[0] = fmaf(x0, vzr[p0][0], vb[0]);
-        vb[0] = fmaf(x1, vzr[p1][0], vb[0]);
-        vb[1] = fmaf(x0, vzr[p0][1], vb[1]);
-        vb[1] = fmaf(x1, vzr[p1][1], vb[1]);
-      }
-      const u32x4 pb0 = u32x4{w0[0], w0[1], w0[2], w0[3]};
-      const u32x4 pb1 = two_groups ? u32x4{w1[0], w1[1], w1[2], w1[3]} : pb0;
-      const u32x4 pl0 = u32x4{l0[0], l0[1], l0[2], l0[3]};
-      const u32x4 pl1 = two_groups ? u32x4{l1[0], l1[1], l1[2], l1[3]} : pl0;
+        float x[2], s0[2], s1[2];
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) {
-        const uint16_t* vrow = Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc2 + 4 * grp;
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 16);
-        const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
-        oacc[dt] = mfma_f16(va, dt < 4 ? pb0 : pb1, oacc[dt]);
-        oacc[dt] = mfma_f16(va, dt < 4 ? pl0 : pl1, oacc[dt]);
+        for (int h = 0; h < 2; h++) {
+          const int k = perm_pos<BITS>(8 * kc2 + 2 * e2 + h);  // key 16g + k
+          x[h] = sacc[k >> 2][k & 3] * P_SCALE;
+          // fp16 scale and zero of key k: element k*nh + group
+          const float sa = h2f(uint16_t(half16(vsw, two ? 2 * k : k)));
+          const float za = h2f(uint16_t(half16(vzw, two ? 2 * k : k)));
+          s0[h] = sa;
+          vb0 = fmaf(x[h], fmaf(sa, C0, za), vb0);  // zero of the centred code
+          if (two) {
+            const float sb = h2f(uint16_t(half16(vsw, 2 * k + 1)));
+            const float zb = h2f(uint16_t(half16(vzw, 2 * k + 1)));
+            s1[h] = sb;
+            vb1 = fmaf(x[h], fmaf(sb, C0, zb), vb1);
+          } else {
+            s1[h] = sa;
+          }
+        }
+        split_h2(x[0] * s0[0], x[1] * s0[1], w0[e2], l0[e2]);
+        split_h2(x[0] * s1[0], x[1] * s1[1], w1[e2], l1[e2]);
+      }
+      pb[kc2][0] = u32x4{w0[0], w0[1], w0[2], w0[3]};
+      pl[kc2][0] = u32x4{l0[0], l0[1], l0[2], l0[3]};
+      pb[kc2][1] = u32x4{w1[0], w1[1], w1[2], w1[3]};
+      pl[kc2][1] = u32x4{l1[0], l1[1], l1[2], l1[3]};
+    }
+    // ---- O^T += C_V^T P'^T (channels 64..127 use the second V group's P' when the group is 64)
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+      u32x4 va[2];
+      cvt_vcodes<BITS>(vr[dt], va);
+      const int h = dt >> 2;
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; kc2++) {
+        oacc[dt] = mfma_f16(va[kc2], pb[kc2][h], oacc[dt]);
+        oacc[dt] = mfma_f16(va[kc2], pl[kc2][h], oacc[dt]);
       }
     }
+    if (tn < key_hi) ld_vtile<BITS>(vr, vc, tn, r16, g);
   }
-  if (wave != 0) return;
-  // the zero term of V is the same for every channel of a group: reduce over the key lanes
-  float vbt[2];
+
+  // ---- this wave's state -> LDS; lane holds o[16dt + 4g + jj] of head l % 16
+  vb0 += shfl_xor(vb0, 16);
+  vb0 += shfl_xor(vb0, 32);
+  vb1 += shfl_xor(vb1, 16);
+  vb1 += shfl_xor(vb1, 32);
+  if (!two) vb1 = vb0;
+  float* rw = red + wave * 16 * QRED;
+  if (head_ok) {
+    float* rh = rw + r16 * QRED;
+    if (g == 0) {
+      rh[0] = m_run;
+      rh[1] = l_run;
+    }
 #pragma unroll
-  for (int h = 0; h < 2; h++) {
-    float b = vb[h];
-    b += shfl_xor(b, 16);
-    b += shfl_xor(b, 32);
-    vbt[h] = b;
+    for (int dt = 0; dt < 8; dt++) {
+      const float vbias = dt >= 4 ? vb1 : vb0;
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) rh[2 + 16 * dt + 4 * g + jj] = (oacc[dt][jj] + vbias) * P_UNSCALE;
+    }
   }
-  if (!row_ok) return;
-  float* dst = R.part + (int64_t(hq) * R.s_total + s) * (D + 2);
-  if (grp == 0) {
-    dst[0] = m_run;
-    dst[1] = l_run;
-  }
+  __syncthreads();
+  for (int idx = tid; idx < G * (D + 2); idx += 256) {
+    const int n = idx / (D + 2), e = idx - n * (D + 2);
+    float mw[QWAVES];
+    float M = NEG_INF;
 #pragma unroll
-  for (int dt = 0; dt < 8; dt++) {
-    const int h = two_groups ? (dt >> 2) : 0;
+    for (int w = 0; w < QWAVES; w++) {
+      mw[w] = red[(w * 16 + n) * QRED];
+      M = fmaxf(M, mw[w]);
+    }
+    float acc = 0.f;
+    if (e == 0) {
+      acc = M;
+    } else {
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++) dst[2 + 16 * dt + 4 * grp + jj] = (oacc[dt][jj] + vbt[h]) * P_UNSCALE;
+      for (int w = 0; w < QWAVES; w++) {
+        const float wt = mw[w] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+        acc = fmaf(red[(w * 16 + n) * QRED + e], wt, acc);
+      }
+    }
+    R.part[(int64_t(j * G + n) * R.s_total + s) * (D + 2) + e] = acc;
   }
 }
 
@@ -366,12 +464,25 @@ vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s) {
   if (a.n_req <= 0 || a.max_splits <= 0) return VC_OK;
   VC_REQUIRE(a.group == 64 || a.group == 128, VC_ERR_UNSUPPORTED, "quant group must be 64 or 128");
   VC_REQUIRE(a.G <= 16, VC_ERR_UNSUPPORTED, "GQA group > 16");
-  VC_REQUIRE(a.split_len % a.group == 0 || a.group % a.split_len == 0, VC_ERR_ARG, "split/group mismatch");
+  VC_REQUIRE(a.split_len % (QWAVES * ATT_KT) == 0 && a.split_len % a.group == 0, VC_ERR_ARG,
+             "quantized decode: split %d must be a multiple of 256 and of the group", a.split_len);
+  for (int r = 0; r < a.n_req; r++)
+    VC_REQUIRE(a.r[r].m.tq % 64 == 0 && a.r[r].m.tq % a.group == 0, VC_ERR_ARG, "quantized rows not whole groups");
   dim3 grid(a.Hkv, a.max_splits, a.n_req);
+  const bool g64 = a.group == 64;
   switch (a.bits) {
-    case 2: hipLaunchKernelGGL(attn_quant_kernel<2>, grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(attn_quant_kernel<3>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(attn_quant_kernel<4>, grid, dim3(256), 0, s, a); break;
+    case 2:
+      if (g64) hipLaunchKernelGGL((attn_quant_kernel<2, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_quant_kernel<2, 1>), grid, dim3(256), 0, s, a);
+      break;
+    case 3:
+      if (g64) hipLaunchKernelGGL((attn_quant_kernel<3, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_quant_kernel<3, 1>), grid, dim3(256), 0, s, a);
+      break;
+    case 4:
+      if (g64) hipLaunchKernelGGL((attn_quant_kernel<4, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_quant_kernel<4, 1>), grid, dim3(256), 0, s, a);
+      break;
     default: VC_REQUIRE(false, VC_ERR_UNSUPPORTED, "bits must be 2, 3 or 4 (got %d)", a.bits);
   }
   VC_LAUNCH_CHECK();

@@ -19,6 +19,7 @@ buffers (torch allocations) and moves token ids it has already received.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
 import time
 from dataclasses import dataclass, field
@@ -85,6 +86,8 @@ class Request:
     full_k: object = None              # pinned host (HostBuffer)
     full_v: object = None
     n_host: int = 0                    # host rows per (layer, KV head)
+    pinned: bool = True                # host rows in pinned memory (else pageable)
+    stage_fut: object = None           # pageable staging in flight on the worker thread
     rows: torch.Tensor = None          # device int32 [x + 1]
     vtail_k: torch.Tensor = None
     vtail_v: torch.Tensor = None
@@ -104,7 +107,11 @@ class Request:
 class Engine:
     """Owns a vc_model, its workspaces and the per-request device/host buffers."""
 
-    def __init__(self, model: B.Model, spec, chunk: int = 1024, device="cuda"):
+    # the driver pins at most ~70 GiB of host memory per process; rows beyond the budget
+    # go to pageable memory (staged at roughly half the pinned PCIe rate)
+    PINNED_BUDGET = 69_000_000_000
+
+    def __init__(self, model: B.Model, spec, chunk: int = 1024, device="cuda", pinned_budget: int | None = None):
         self.m = model
         self.spec = spec
         self.shape = model.shape
@@ -117,6 +124,10 @@ class Engine:
         self.slot_free_ev = []
         self.ws_draft = None
         self.ws_verify = None
+        self.pinned_budget = self.PINNED_BUDGET if pinned_budget is None else pinned_budget
+        self.pinned_used = 0
+        self.pageable_stream = None
+        self.stager = None
 
     # ------------------------------------------------------------ setup (untimed)
     def add_request(self, prompt: torch.Tensor, x: int, n_tokens: int, keep_prefill_kv: bool = False):
@@ -137,8 +148,13 @@ class Engine:
         r.n_host = B.compress_layout(r.cd).n_host
         full_cap = max(r.n_host, 1)
         eb = 2 if self.dt == torch.bfloat16 else 4
-        r.full_k = B.HostBuffer(L * Hkv * full_cap * D * eb)
-        r.full_v = B.HostBuffer(L * Hkv * full_cap * D * eb)
+        nbytes = L * Hkv * full_cap * D * eb
+        r.pinned = self.pinned_used + 2 * nbytes <= self.pinned_budget
+        if r.pinned:
+            self.pinned_used += 2 * nbytes
+        buf = B.HostBuffer if r.pinned else B.PageableBuffer
+        r.full_k = buf(nbytes)
+        r.full_v = buf(nbytes)
         tail_cap = n_tokens + x + 2
         r.tail_k = torch.empty(L, Hkv, tail_cap, D, dtype=self.dt, device=self.device)
         r.tail_v = torch.empty_like(r.tail_k)
@@ -218,7 +234,7 @@ class Engine:
             if r.phase == WAIT_SLOT:
                 if r.slot < 0:
                     self._try_stage(r)
-                if r.slot >= 0 and r.stage_ev.query():
+                if r.slot >= 0 and self._staged(r):
                     self._verify(r, cs)
         if active:
             self.draft_steps += 1
@@ -269,12 +285,47 @@ class Engine:
                 self.slot_owner[i] = r.idx
                 r.slot = i
                 sk, sv = self.slots[i]
-                self.m.stage(r.req, sk, sv, 0, self.shape.n_layers, copy_stream=self.copy_stream)
-                ev = torch.cuda.Event()
-                ev.record(self.copy_stream)
-                r.stage_ev = ev
+                if r.pinned:
+                    self.m.stage(r.req, sk, sv, 0, self.shape.n_layers, copy_stream=self.copy_stream)
+                    ev = torch.cuda.Event()
+                    ev.record(self.copy_stream)
+                    r.stage_ev = ev
+                else:
+                    r.stage_ev = None
+                    r.stage_fut = self._stage_pageable(Req.from_buffer_copy(r.req), sk, sv)
                 return True
         return False
+
+    def _stage_pageable(self, req: Req, sk, sv):
+        """Copy from pageable memory on a worker thread (the call blocks until the
+        runtime has moved the data; ctypes releases the GIL meanwhile)."""
+        if self.stager is None:
+            self.stager = cf.ThreadPoolExecutor(max_workers=1)
+            self.pageable_stream = torch.cuda.Stream(device=self.device)
+        st = self.pageable_stream
+
+        def work():
+            self.m.stage(req, sk, sv, 0, self.shape.n_layers, copy_stream=st)
+            ev = torch.cuda.Event()
+            ev.record(st)
+            return ev
+
+        return self.stager.submit(work)
+
+    def _staged(self, r: Request) -> bool:
+        if r.stage_ev is None and r.stage_fut is not None and r.stage_fut.done():
+            r.stage_ev = r.stage_fut.result()
+            r.stage_fut = None
+        return r.stage_ev is not None and r.stage_ev.query()
+
+    def release_host(self):
+        """Free every request's host buffers (after decoding)."""
+        for r in self.reqs:
+            for b in (r.full_k, r.full_v):
+                if b is not None:
+                    b.free()
+            r.full_k = r.full_v = None
+        self.pinned_used = 0
 
     def _verify(self, r: Request, cs):
         sk, sv = self.slots[r.slot]

@@ -3,8 +3,9 @@
 
 Default workload: the 32-layer Llama-3-8B-shaped random-init decoder (bf16),
 8 requests with 65536-token prompts, a 4x token-dropped draft cache on the GPU,
-the full KV cache in pinned host memory staged over PCIe only to verify,
-x = 32, staggered verification.  A step is one scheduler round period: x
+the rest of the full KV cache (the dropped prompt rows; the kept rows and the
+committed tail are exact on the GPU) in pinned host memory, staged over PCIe
+only to verify, x = 32, staggered verification.  A step is one scheduler round period: x
 batched draft steps, during which every request is verified about once.
 
 Reported: emitted (lossless) tokens per second over exactly --steps steps,
@@ -25,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
 def log(*a):
@@ -87,17 +89,48 @@ def cpu_baseline(shape, ctx: int, keep: int, seed: int = 0) -> dict:
                        f"{s.n_layers} layers; {per_token:.2f} s per token; weight generation {t_gen:.1f} s excluded")}
 
 
+def pmc_traffic_ratio(workload: str):
+    """Measured HBM bytes over algorithmic bytes of the draft-attention launches, from the
+    committed counter profile of this workload (profiles/draft_attention_<workload>_pmc.json,
+    the workload name without its label), if the kernel sources are unchanged since.  The
+    counter passes serialise every dispatch, which changes how many requests draft together,
+    so the ratio (taken over the same launches on both sides) carries over to this run's
+    launches rather than the profiled run's bytes per launch."""
+    from lossless_speculative_decoding_amd.pmc_summary import sources_sha256
+    name = workload.split("_", 1)[1] if workload[:1] == "c" and "_" in workload else workload
+    path = os.path.join(ROOT, "profiles", f"draft_attention_{name}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("sources_sha256") != sources_sha256():
+        log(f"{path}: kernel sources changed since the counters were taken; traffic not reported")
+        return None
+    return rec.get("traffic_over_algorithmic")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4, help="timed scheduler round periods (x draft steps each)")
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16, help="timed scheduler round periods (x draft steps each)")
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c3", choices=["c3", "c4", "c5"])
     ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
     ap.add_argument("--baseline-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
+                         "the HBM byte counters of a profile)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(1 << 30, dtype=torch.int8, device="cuda")
+        for _ in range(5):
+            dst.copy_(src)  # uint8 -> int8: an elementwise kernel that reads and writes 1 GiB (not a DMA)
+        torch.cuda.synchronize()
+        log("copied 5 x 1 GiB")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (requests would be sharded across "
               "GPUs by request, each GPU running this same loop)", file=sys.stderr)
@@ -134,14 +167,17 @@ def main():
     t_setup = time.perf_counter() - t_setup
     log(f"setup {t_setup:.1f}s")
 
-    # warmup
-    eng.run_draft_steps(args.warmup * x_round)
-    eng.drain()
-    # timed region
+    # warmup (draft-attention launches recorded too, so that a counter profile of this command,
+    # which sees every launch, can be compared with the algorithmic bytes of the same launches)
     vc.profile_read()
     vc.profile_enable(True)
+    eng.run_draft_steps(args.warmup * x_round)
+    eng.drain()
+    warm = vc.profile_read()
+    # timed region
     torch.cuda.synchronize()
     e0 = eng.emitted_total()
+    sb0, sn0 = eng.staged_bytes, eng.stagings
     t0 = time.perf_counter()
     eng.run_draft_steps(args.steps * x_round)
     eng.drain()
@@ -150,12 +186,19 @@ def main():
     vc.profile_enable(False)
     prof = vc.profile_read()
     emitted = eng.emitted_total() - e0
+    staged, n_staged = eng.staged_bytes - sb0, eng.stagings - sn0
     tok_s = emitted / secs
     accepts = [a for r in eng.reqs for a in r.accepts]
     log(f"timed: {emitted} tokens in {secs:.2f}s = {tok_s:.2f} tok/s; mean accepted {sum(accepts)/max(len(accepts),1):.2f}")
 
     att_ms = prof["ms"] / max(prof["launches"], 1)
     att_gbs = prof["bytes"] / max(prof["ms"], 1e-9) / 1e6
+    all_launches = warm["launches"] + prof["launches"]
+    all_bytes = (warm["bytes"] + prof["bytes"]) / max(all_launches, 1)
+    traffic_ratio = pmc_traffic_ratio(w.name)
+    bpl = prof["bytes"] / max(prof["launches"], 1)
+    traffic = round(traffic_ratio * bpl) if traffic_ratio else None
+    pcie_gbs = staged / secs / 1e9
     # full-KV-from-host greedy comparator: request 0's prompt decoded again as a plain request
     # whose whole cache is on the host (after the timed region); its tokens must be the ones
     # VeriCache emitted for request 0
@@ -195,9 +238,16 @@ def main():
                               "verification"},
         "roofline": {"bound": "hbm", "kernel": "draft attention partials (all layers of a draft step)",
                      "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "traffic_over_algorithmic": traffic_ratio,
                      "avg_launch_ms": round(att_ms, 5), "launches": prof["launches"],
-                     "bytes_per_launch": round(prof["bytes"] / max(prof["launches"], 1))},
+                     "bytes_per_launch": round(prof["bytes"] / max(prof["launches"], 1)),
+                     "bytes_per_launch_incl_warmup": round(all_bytes), "launches_incl_warmup": all_launches},
+        "pcie": {"bound": "pcie", "achieved": round(pcie_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(pcie_gbs / PCIE_PEAK_GBS, 4), "stagings": n_staged,
+                 "bytes_per_staging": round(staged / max(n_staged, 1)),
+                 "note": "host rows staged for verification in the timed region / its wall time"},
         "full_kv_from_host_tok_s": round(base_tok_s, 3),
         "full_kv_from_host_tokens_match": base_match,
         "speedup_vs_full_kv_from_host": round(tok_s / base_tok_s, 3),

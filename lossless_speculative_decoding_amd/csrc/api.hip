@@ -349,11 +349,12 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     bytes += double(Hq) * row;                                       // query
     bytes += double(Hq) * (qs_n[r] + ts_n[r]) * (D + 2) * 4.0;        // partials written
   }
+  // live timing: the first partial launch's own start and the last one's own end
   ProfRec rec{nullptr, nullptr, bytes};
   if (g_prof_on) {
     rec.a = prof_event();
     rec.b = prof_event();
-    if (rec.a) VC_HIP(hipEventRecord(rec.a, s));
+    if (!rec.a || !rec.b) rec.a = rec.b = nullptr;
   }
   vc_status st;
   if (qa.n_req > 0) {
@@ -365,13 +366,17 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     qa.split_len = SPLIT_QUANT;
     qa.scale_log2 = sl2;
     VC_REQUIRE(D == 128 && dtype == VC_BF16, VC_ERR_UNSUPPORTED, "quantized draft needs bf16, head_dim 128");
-    if ((st = launch_attn_quant(qa, s))) return st;
+    if ((st = launch_attn_quant(qa, s, rec.a, nullptr))) return st;
   }
-  if ((st = decode ? launch_attn_decode(aa, s) : launch_attn(aa, dtype, s, true))) return st;
-  if (g_prof_on && rec.a && rec.b) {
-    VC_HIP(hipEventRecord(rec.b, s));
-    g_prof.push_back(rec);
+  hipEvent_t start = qa.n_req > 0 ? nullptr : rec.a;
+  if (decode) {
+    if ((st = launch_attn_decode(aa, s, start, rec.b))) return st;
+  } else {
+    if (start) VC_HIP(hipEventRecord(start, s));
+    if ((st = launch_attn(aa, dtype, s, true))) return st;
+    if (rec.b) VC_HIP(hipEventRecord(rec.b, s));
   }
+  if (rec.a && rec.b) g_prof.push_back(rec);
   CombineArgs c{};
   c.n_req = n;
   c.n_rows = 1;

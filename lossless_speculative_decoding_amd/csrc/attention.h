@@ -117,13 +117,18 @@ struct QuantArgs {
 
 // dtype: VC_BF16 (head_dim 128, MFMA) or VC_F32 (head_dim 64, VALU)
 vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, bool draft = false);
-vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s);
+// ev_start / ev_stop (may be null): HIP events that take the kernel's own start and end
+// time (hipExtLaunchKernelGGL), for live kernel timing without marker-packet gaps; when
+// nothing is launched they are recorded on the stream instead.
+vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_start = nullptr,
+                            hipEvent_t ev_stop = nullptr);
 
 // One-row decode (bf16, head_dim 128, G <= 16): segment a occupies logical keys
 // [0, align64(a.n)), segment b follows; lim0 is ignored (every key is visible) and
 // split_len must be a multiple of 256.  Logical key count for n_splits:
 inline int decode_keys(int a_n, int b_n) { return ((a_n + ATT_KT - 1) / ATT_KT) * ATT_KT + b_n; }
-vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s);
+vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start = nullptr,
+                             hipEvent_t ev_stop = nullptr);
 
 struct CombineArgs {
   const float* part[VC_MAX_BATCH];  // [rows][Hq][s_total][D+2]

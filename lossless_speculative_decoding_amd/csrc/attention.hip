@@ -589,8 +589,11 @@ __global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
 
 }  // namespace
 
-vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s) {
-  if (a.n_req <= 0 || a.max_splits <= 0) return VC_OK;
+vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (a.n_req <= 0 || a.max_splits <= 0) {
+    VC_EVENTS_IF_EMPTY(ev_start, ev_stop, s);
+    return VC_OK;
+  }
   VC_REQUIRE(a.head_dim == 128 && a.G >= 1 && a.G <= 16 && a.split_len % (DEC_WAVES * ATT_KT) == 0, VC_ERR_UNSUPPORTED,
              "decode attention needs head_dim 128, at most 16 query heads per KV head, split a multiple of 256");
   for (int r = 0; r < a.n_req; r++) {
@@ -601,7 +604,8 @@ vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s) {
     VC_REQUIRE(int64_t(q.n_splits) * a.split_len >= decode_keys(q.a.n, q.b.n), VC_ERR_ARG,
                "decode attention: %d splits do not cover the keys", q.n_splits);
   }
-  hipLaunchKernelGGL(attn_decode_bf16_kernel, dim3(a.Hkv, a.max_splits, a.n_req), dim3(256), 0, s, a);
+  hipExtLaunchKernelGGL(attn_decode_bf16_kernel, dim3(a.Hkv, a.max_splits, a.n_req), dim3(256), 0, s, ev_start,
+                        ev_stop, 0, a);
   VC_LAUNCH_CHECK();
   return VC_OK;
 }

@@ -460,8 +460,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s) {
-  if (a.n_req <= 0 || a.max_splits <= 0) return VC_OK;
+vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (a.n_req <= 0 || a.max_splits <= 0) {
+    VC_EVENTS_IF_EMPTY(ev_start, ev_stop, s);
+    return VC_OK;
+  }
   VC_REQUIRE(a.group == 64 || a.group == 128, VC_ERR_UNSUPPORTED, "quant group must be 64 or 128");
   VC_REQUIRE(a.G <= 16, VC_ERR_UNSUPPORTED, "GQA group > 16");
   VC_REQUIRE(a.split_len % (QWAVES * ATT_KT) == 0 && a.split_len % a.group == 0, VC_ERR_ARG,
@@ -472,16 +475,16 @@ vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s) {
   const bool g64 = a.group == 64;
   switch (a.bits) {
     case 2:
-      if (g64) hipLaunchKernelGGL((attn_quant_kernel<2, 2>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_quant_kernel<2, 1>), grid, dim3(256), 0, s, a);
+      if (g64) hipExtLaunchKernelGGL((attn_quant_kernel<2, 2>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
+      else hipExtLaunchKernelGGL((attn_quant_kernel<2, 1>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
       break;
     case 3:
-      if (g64) hipLaunchKernelGGL((attn_quant_kernel<3, 2>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_quant_kernel<3, 1>), grid, dim3(256), 0, s, a);
+      if (g64) hipExtLaunchKernelGGL((attn_quant_kernel<3, 2>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
+      else hipExtLaunchKernelGGL((attn_quant_kernel<3, 1>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
       break;
     case 4:
-      if (g64) hipLaunchKernelGGL((attn_quant_kernel<4, 2>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_quant_kernel<4, 1>), grid, dim3(256), 0, s, a);
+      if (g64) hipExtLaunchKernelGGL((attn_quant_kernel<4, 2>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
+      else hipExtLaunchKernelGGL((attn_quant_kernel<4, 1>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
       break;
     default: VC_REQUIRE(false, VC_ERR_UNSUPPORTED, "bits must be 2, 3 or 4 (got %d)", a.bits);
   }

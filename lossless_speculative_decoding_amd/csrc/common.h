@@ -1,6 +1,7 @@
 // Shared device/host helpers of the VeriCache HIP library (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,6 +30,12 @@ void set_error(const char* fmt, ...);
     }                                                                                              \
   } while (0)
 #define VC_LAUNCH_CHECK() VC_HIP(hipGetLastError())
+// a launcher that launches nothing still completes the events it was handed
+#define VC_EVENTS_IF_EMPTY(ev_start, ev_stop, s)     \
+  do {                                               \
+    if (ev_start) VC_HIP(hipEventRecord(ev_start, s)); \
+    if (ev_stop) VC_HIP(hipEventRecord(ev_stop, s));   \
+  } while (0)
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }

@@ -124,6 +124,8 @@ class Engine:
         self.slot_free_ev = []
         self.ws_draft = None
         self.ws_verify = None
+        self.staged_bytes = 0          # host rows copied to the device for verification (both K and V)
+        self.stagings = 0
         self.pinned_budget = self.PINNED_BUDGET if pinned_budget is None else pinned_budget
         self.pinned_used = 0
         self.pageable_stream = None
@@ -285,6 +287,8 @@ class Engine:
                 self.slot_owner[i] = r.idx
                 r.slot = i
                 sk, sv = self.slots[i]
+                self.staged_bytes += 2 * sk[:, :, :r.n_host].numel() * sk.element_size()
+                self.stagings += 1
                 if r.pinned:
                     self.m.stage(r.req, sk, sv, 0, self.shape.n_layers, copy_stream=self.copy_stream)
                     ev = torch.cuda.Event()

@@ -91,14 +91,13 @@ def cpu_baseline(shape, ctx: int, keep: int, seed: int = 0) -> dict:
 
 def pmc_traffic_ratio(workload: str):
     """Measured HBM bytes over algorithmic bytes of the draft-attention launches, from the
-    committed counter profile of this workload (profiles/draft_attention_<workload>_pmc.json,
-    the workload name without its label), if the kernel sources are unchanged since.  The
+    committed counter profile of this workload (profiles/draft_attention_<workload>_pmc.json),
+    if the kernel sources are unchanged since.  The
     counter passes serialise every dispatch, which changes how many requests draft together,
     so the ratio (taken over the same launches on both sides) carries over to this run's
     launches rather than the profiled run's bytes per launch."""
     from lossless_speculative_decoding_amd.pmc_summary import sources_sha256
-    name = workload.split("_", 1)[1] if workload[:1] == "c" and "_" in workload else workload
-    path = os.path.join(ROOT, "profiles", f"draft_attention_{name}_pmc.json")
+    path = os.path.join(ROOT, "profiles", f"draft_attention_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -113,7 +112,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16, help="timed scheduler round periods (x draft steps each)")
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c3", choices=["c3", "c4", "c5"])
+    ap.add_argument("--config", default="llama8b_tokdrop", choices=["llama8b_tokdrop", "llama8b_q2", "llama8b_mixed"])
     ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
     ap.add_argument("--baseline-steps", type=int, default=2)

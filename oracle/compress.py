@@ -5,7 +5,7 @@ ascending before gathering).
 Two families, run per layer l and per KV head j on the prefill's K (after
 RoPE) and V:
 
-Token drop by observed attention (SnapKV-like; workload C1/C3 rule)
+Token drop by observed attention (SnapKV-like; the rule of the token-drop workloads)
     W observation queries (the last W prompt positions), R recent rows, keep K rows.
     p[h,i,t] = softmax over t' <= i of q[h,i] . k[t'] / sqrt(D)  for h in the
                GQA group of j and i in [T-W, T)

@@ -8,7 +8,7 @@ import synth
 from gpu_helpers import TOL_F32, log, need_gpu, torch
 from oracle import decode as OD
 from oracle.model import Weights
-from synth.configs import c1
+from synth.configs import tiny as tiny_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -18,7 +18,7 @@ def setup():
     need_gpu()
     from lossless_speculative_decoding_amd import Model
     from lossless_speculative_decoding_amd.engine import make_weights
-    w = c1()
+    w = tiny_workload()
     s = w.model
     W = make_weights(s)
     m = Model(s, W, max_pos=w.ctx[0] + w.n_tokens + 64)

@@ -9,7 +9,8 @@ import pytest
 import synth
 from oracle import decode as D
 from oracle.model import Weights
-from synth.configs import ModelShape, c1
+from synth.configs import ModelShape
+from synth.configs import tiny as tiny_workload
 
 TINY = ModelShape(n_layers=2, d_model=32, n_q_heads=4, n_kv_heads=2, head_dim=8, ffn=48, vocab=16,
                   rope_theta=10000.0, dtype="fp32")
@@ -64,8 +65,8 @@ def test_bf16_model_vericache_equals_greedy():
 
 
 @pytest.mark.slow
-def test_c1_full_run():
-    w = c1()
+def test_tiny_workload_full_run():
+    w = tiny_workload()
     W = Weights(w.model)
     p = synth.prompt(0, w.ctx[0], w.model.vocab)
     pre = D.prefill(W, p)

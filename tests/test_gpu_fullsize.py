@@ -1,0 +1,160 @@
+"""GPU parity at full workload sizes, in the launch configurations the kernels run in,
+on sampled (request, KV head) slices the oracle evaluates one by one.
+
+Single GQA layer, 8B head shapes, 16 requests x 32768 tokens, 4-bit group 128 with
+4 outlier channels per head: the compressed bytes of the sampled heads (bit exact),
+the batched draft step over all 16 requests and the 32-row verification of all 16,
+each against the float64 oracle.  Token-drop decode at the 8B model's sizes
+(8 requests x 65536 prompt rows, 16384 kept, 100 tail rows) in one batched launch:
+the kept set of a sampled head against the oracle's selection (differences only at
+flagged ties), and the sampled heads' outputs against the oracle over the GPU's
+kept rows."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import TOL_BF16, dev_bf16, host_f64, log, need_gpu, row_rel_err, torch
+from oracle import attention as OA
+from oracle import compress as OC
+
+pytestmark = pytest.mark.gpu
+HQ, HKV, D, G = 32, 8, 128, 4
+
+
+def _gen(shape, stream, outl=None, scale=1.0):
+    from lossless_speculative_decoding_amd import synth_normal_heads
+    t = torch.empty(*shape, dtype=torch.bfloat16, device="cuda")
+    synth_normal_heads(t, stream, outl, scale)
+    return t
+
+
+def _outliers(B):
+    o = np.stack([synth.outlier_channels_for(b, j, HKV, D) for b in range(B) for j in range(HKV)]).astype(np.int32)
+    return torch.from_numpy(o).cuda()
+
+
+# ------------------------------------------------------------------ quantized single layer
+QB, QT, BITS, GROUP, ROWS = 16, 32768, 4, 128, 32
+Q_SAMPLE = [(0, 0), (6, 3), (15, 7)]
+
+
+@pytest.fixture(scope="module")
+def qlayer():
+    need_gpu()
+    from lossless_speculative_decoding_amd import VC_BF16, VC_QUANT, compress_desc, vc_compress
+    outl = _outliers(QB)
+    K = _gen((QB, HKV, QT, D), synth.S_ATT_K, outl, 10.0)
+    V = _gen((QB, HKV, QT, D), synth.S_ATT_V, outl, 10.0)
+    tK = _gen((QB, HKV, ROWS, D), synth.S_ATT_TK)
+    tV = _gen((QB, HKV, ROWS, D), synth.S_ATT_TV)
+    cds, blobs = [], []
+    for b in range(QB):
+        d = compress_desc(VC_QUANT, 1, HQ, HKV, D, QT, VC_BF16, bits=BITS, group=GROUP)
+        cds.append(d)
+        blobs.append(vc_compress(d, K[b:b + 1], V[b:b + 1]))
+    torch.cuda.synchronize()
+    log(f"generated and compressed {QB} x {QT} rows")
+    return dict(K=K, V=V, tK=tK, tV=tV, cds=cds, blobs=blobs)
+
+
+def test_quant_blob_sampled_heads_bit_exact(qlayer):
+    from lossless_speculative_decoding_amd import compress_layout
+    lay = compress_layout(qlayer["cds"][0])
+    Tq, ng, nb = QT, QT // GROUP, QT // 64
+    sizes = dict(kc=Tq * D * BITS // 8, vc=nb * D * 8 * BITS, ks=ng * D * 2, kz=ng * D * 2,
+                 vs=Tq * (D // GROUP) * 2, vz=Tq * (D // GROUP) * 2)
+    for b, j in Q_SAMPLE:
+        inp = OA.head_inputs(b, j, QT, HKV, HQ, D, ROWS)
+        q = OC.Quantized(inp["K"][None, None], inp["V"][None, None], BITS, GROUP)
+        want = dict(kc=OC.pack_bits(q.kcodes[0, 0], BITS).tobytes(),
+                    vc=OC.pack_bits(q.vcodes[0, 0].reshape(nb, 64, D).transpose(0, 2, 1), BITS).tobytes(),
+                    ks=q.ks[0, 0].astype("<f2").tobytes(), kz=q.kz[0, 0].astype("<f2").tobytes(),
+                    vs=q.vs[0, 0].astype("<f2").tobytes(), vz=q.vz[0, 0].astype("<f2").tobytes())
+        blob = qlayer["blobs"][b]
+        for name, n in sizes.items():
+            off = getattr(lay, name) + j * n
+            got = blob[off:off + n].cpu().numpy().tobytes()
+            assert got == want[name], f"request {b} head {j}: section {name} differs"
+        log(f"request {b} head {j}: all sections bit exact")
+
+
+def test_quant_draft_step_batched_sampled(qlayer):
+    from lossless_speculative_decoding_amd import VC_BF16, VC_F32, vc_attn_draft
+    from lossless_speculative_decoding_amd._vc import AttnDesc
+    qd = np.stack([synth.att_queries(synth.S_ATT_QD, b, 1, HQ, D)[0] for b in range(QB)])
+    out = vc_attn_draft(AttnDesc(HQ, HKV, D, VC_BF16, 0, VC_F32), qlayer["blobs"], qlayer["cds"],
+                        [qlayer["tK"][b] for b in range(QB)], [qlayer["tV"][b] for b in range(QB)], [1] * QB,
+                        dev_bf16(qd))
+    torch.cuda.synchronize()
+    for b, j in Q_SAMPLE:
+        ref = OA.draft_output(OA.head_inputs(b, j, QT, HKV, HQ, D, ROWS), BITS, GROUP)
+        err = row_rel_err(host_f64(out[b, j * G:(j + 1) * G]), ref)
+        log(f"draft request {b} head {j}: rel err {err:.2e}")
+        assert err <= TOL_BF16
+
+
+def test_verify_32_rows_batched_sampled(qlayer):
+    from lossless_speculative_decoding_amd import VC_BF16, VC_F32, vc_attn_verify
+    from lossless_speculative_decoding_amd._vc import AttnDesc
+    qv = np.stack([synth.att_queries(synth.S_ATT_QV, b, ROWS, HQ, D) for b in range(QB)])     # [B][rows][Hq][D]
+    out = vc_attn_verify(AttnDesc(HQ, HKV, D, VC_BF16, 0, VC_F32), dev_bf16(qv),
+                         [qlayer["K"][b] for b in range(QB)], [qlayer["V"][b] for b in range(QB)], [QT] * QB,
+                         [qlayer["tK"][b] for b in range(QB)], [qlayer["tV"][b] for b in range(QB)], ROWS)
+    torch.cuda.synchronize()
+    rows = [0, 13, ROWS - 1]
+    for b, j in Q_SAMPLE:
+        ref = OA.verify_output(OA.head_inputs(b, j, QT, HKV, HQ, D, ROWS), rows)
+        got = host_f64(out[b, rows, j * G:(j + 1) * G])
+        err = row_rel_err(got.reshape(-1, D), ref.reshape(-1, D))
+        log(f"verify request {b} head {j} rows {rows}: rel err {err:.2e}")
+        assert err <= TOL_BF16
+
+
+# ------------------------------------------------------------------ token drop at 8B sizes
+TB, TT, KEEP, REC, W, TAIL = 8, 65536, 16384, 64, 32, 100
+T_SAMPLE = [(0, 2), (7, 6)]
+
+
+def test_tokdrop_decode_at_8b_sizes_sampled():
+    need_gpu()
+    from lossless_speculative_decoding_amd import (VC_BF16, VC_F32, VC_TOKDROP, compress_desc, compress_layout,
+                                                   vc_attn_draft, vc_compress)
+    from lossless_speculative_decoding_amd._vc import AttnDesc
+    K = _gen((TB, HKV, TT, D), synth.S_ATT_K)
+    V = _gen((TB, HKV, TT, D), synth.S_ATT_V)
+    tK = _gen((TB, HKV, TAIL, D), synth.S_ATT_TK)
+    tV = _gen((TB, HKV, TAIL, D), synth.S_ATT_TV)
+    qo = np.stack([synth.att_queries(synth.S_ATT_QV, b, W, HQ, D) for b in range(TB)])       # [B][W][Hq][D]
+    cds, blobs = [], []
+    for b in range(TB):
+        d = compress_desc(VC_TOKDROP, 1, HQ, HKV, D, TT, VC_BF16, keep_total=KEEP, keep_recent=REC, obs_window=W)
+        cds.append(d)
+        blobs.append(vc_compress(d, K[b:b + 1], V[b:b + 1], dev_bf16(qo[b][None])))
+    qd = np.stack([synth.att_queries(synth.S_ATT_QD, b, 1, HQ, D)[0] for b in range(TB)])
+    out = vc_attn_draft(AttnDesc(HQ, HKV, D, VC_BF16, 0, VC_F32), blobs, cds, [tK[b] for b in range(TB)],
+                        [tV[b] for b in range(TB)], [TAIL] * TB, dev_bf16(qd))
+    torch.cuda.synchronize()
+    lay = compress_layout(cds[0])
+    f = lambda bits: synth.bf16_bits_to_f32(bits).astype(np.float64)
+    for n_check, (b, j) in enumerate(T_SAMPLE):
+        idx = blobs[b][lay.idx + j * KEEP * 4: lay.idx + (j + 1) * KEEP * 4].cpu().numpy().view(np.int32)
+        assert np.all(np.diff(idx) > 0) and idx[0] >= 0 and idx[-1] == TT - 1
+        assert np.array_equal(idx[-REC:], np.arange(TT - REC, TT))
+        Kh = f(synth.att_head(synth.S_ATT_K, b, j, TT, HKV, D))
+        Vh = f(synth.att_head(synth.S_ATT_V, b, j, TT, HKV, D))
+        if n_check == 0:
+            # the kept set against the oracle's selection (float64 scores; differences only at ties)
+            qh = f(qo[b])[:, j * G:(j + 1) * G].transpose(1, 0, 2)[None, None]        # [1][1][G][W][D]
+            widx, _, _, scores = OC.tokdrop(Kh[None, None], Vh[None, None], qh[0], KEEP, REC, G)
+            s = scores[0][0]
+            got, want = set(idx.tolist()), set(widx[0, 0].tolist())
+            kth = np.sort(s)[::-1][KEEP - REC - 1]
+            for t in got ^ want:
+                assert abs(s[t] - kth) <= 1e-4 * kth, (b, j, t, s[t], kth)
+            log(f"request {b} head {j}: kept set equal up to {len(got ^ want) // 2} flagged ties")
+        Kj = np.concatenate([Kh[idx], f(tK[b, j].cpu().view(torch.int16).numpy().view(np.uint16))])
+        Vj = np.concatenate([Vh[idx], f(tV[b, j].cpu().view(torch.int16).numpy().view(np.uint16))])
+        ref = np.stack([OA.attend(f(qd[b, j * G + g]), Kj, Vj) for g in range(G)])
+        err = row_rel_err(host_f64(out[b, j * G:(j + 1) * G]), ref)
+        log(f"token-drop decode request {b} head {j}: rel err {err:.2e}")
+        assert err <= TOL_BF16

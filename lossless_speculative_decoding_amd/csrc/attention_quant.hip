@@ -13,8 +13,8 @@
 // out of the fp16 subnormal range).  Codes are centred (c - 2^(b-1), the zero moves to
 // z + 2^(b-1) s) so the folded sums do not cancel against a large zero term (keeping the
 // 1024 of the conversion in the V codes instead costs ~5e-3 relative on outlier-heavy
-// heads), and Q' and P' are each carried as an fp16 hi/lo pair (two MFMAs), which leaves
-// about 22 significant bits in every score and weight.
+// heads).  Q' is carried as an fp16 hi/lo pair (two MFMAs, about 22 significant bits: a
+// score error moves every weight through the exponential); P' as one fp16 number.
 //
 // Operand assignment.  Lane l (g = l / 16, r = l % 16) holds for S^T = C_K Q'^T the
 // K codes of channels [32g, 32g + 32) of key 16 (r / 4) + 4 kt + r % 4 of the tile
@@ -208,9 +208,25 @@ constexpr int QRED = D + 4;  // floats per head in the merge buffer
 
 // NH: V channel groups per token (1 for group 128, 2 for group 64), a template parameter so
 // that every register index below is a compile-time constant
+constexpr int QSPLIT_MAX = 1024;  // keys per split (the LDS copies of the split's scales are sized for it)
+
+// LDS: the split's K scales and zeros (per token group and channel), V scales and zeros (per
+// token and channel group) and the G query rows, loaded once by the whole workgroup so that no
+// scale load is left in the loop; after the loop the same bytes hold the waves' merge buffer
+constexpr int QL_KS = 0, QL_KZ = QL_KS + QSPLIT_MAX / 64 * D * 2, QL_VS = QL_KZ + QSPLIT_MAX / 64 * D * 2,
+              QL_VZ = QL_VS + QSPLIT_MAX * 2 * 2, QL_Q = QL_VZ + QSPLIT_MAX * 2 * 2, QL_END = QL_Q + 16 * D * 2;
+constexpr int QL_BYTES = QL_END > QWAVES * 16 * QRED * 4 ? QL_END : QWAVES * 16 * QRED * 4;
+
 template <int BITS, int NH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_quant_kernel(const QuantArgs args) {
-  __shared__ float red[QWAVES * 16 * QRED];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3 : 2, NH == 1 ? 3 : 2))) void attn_quant_kernel(
+    const QuantArgs args) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[QL_BYTES];
+  uint16_t* const s_ks = reinterpret_cast<uint16_t*>(lds + QL_KS);
+  uint16_t* const s_kz = reinterpret_cast<uint16_t*>(lds + QL_KZ);
+  uint16_t* const s_vs = reinterpret_cast<uint16_t*>(lds + QL_VS);
+  uint16_t* const s_vz = reinterpret_cast<uint16_t*>(lds + QL_VZ);
+  uint16_t* const s_q = reinterpret_cast<uint16_t*>(lds + QL_Q);
+  float* const red = reinterpret_cast<float*>(lds);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int z = blockIdx.z;
   if (z >= args.n_req) return;
@@ -238,7 +254,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* vs = R.m.vs + int64_t(j) * Tq * nh;
   const uint16_t* vz = R.m.vz + int64_t(j) * Tq * nh;
 
-  const uint16_t* qp = static_cast<const uint16_t*>(R.q) + int64_t(hq) * D + 32 * g;  // this lane's 32 channels
+  {
+    const int g_lo = key_lo / grp_sz, n_grp = (key_hi - key_lo) / grp_sz;
+    const u32x4* a = reinterpret_cast<const u32x4*>(ks + int64_t(g_lo) * D);
+    const u32x4* b = reinterpret_cast<const u32x4*>(kz + int64_t(g_lo) * D);
+    for (int i = tid; i < n_grp * (D / 8); i += 256) {
+      reinterpret_cast<u32x4*>(s_ks)[i] = a[i];
+      reinterpret_cast<u32x4*>(s_kz)[i] = b[i];
+    }
+    const u32x4* c = reinterpret_cast<const u32x4*>(vs + int64_t(key_lo) * nh);
+    const u32x4* d = reinterpret_cast<const u32x4*>(vz + int64_t(key_lo) * nh);
+    for (int i = tid; i < (key_hi - key_lo) * nh / 8; i += 256) {
+      reinterpret_cast<u32x4*>(s_vs)[i] = c[i];
+      reinterpret_cast<u32x4*>(s_vz)[i] = d[i];
+    }
+    const u32x4* e = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(R.q) + int64_t(j) * G * D);
+    for (int i = tid; i < G * (D / 8); i += 256) reinterpret_cast<u32x4*>(s_q)[i] = e[i];
+  }
+  __syncthreads();
   constexpr float C0 = float(1 << (BITS - 1));
   u32x4 qf[4], qlo[4];
   float kbias = 0.f;
@@ -261,9 +294,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- V scales and zeros of this lane's 16 keys [t0 + 16g, t0 + 16g + 16)
     uint32_t vsw[16], vzw[16];
     {
-      // 16 * nh fp16 values each, 32-byte aligned (sections are 256-byte aligned, Tq is a multiple of 64)
-      const u32x4* sp = reinterpret_cast<const u32x4*>(vs + int64_t(t0 + 16 * g) * nh);
-      const u32x4* zp = reinterpret_cast<const u32x4*>(vz + int64_t(t0 + 16 * g) * nh);
+      const u32x4* sp = reinterpret_cast<const u32x4*>(s_vs + (t0 - key_lo + 16 * g) * nh);
+      const u32x4* zp = reinterpret_cast<const u32x4*>(s_vz + (t0 - key_lo + 16 * g) * nh);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const u32x4 a = (i < 2 * nh) ? sp[i] : u32x4{0, 0, 0, 0};
@@ -277,9 +309,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (tg != cur_group) {
       cur_group = tg;
       uint32_t sw[16], zw[16], qw[16];
-      const u32x4* sp = reinterpret_cast<const u32x4*>(ks + int64_t(tg) * D + 32 * g);
-      const u32x4* zp = reinterpret_cast<const u32x4*>(kz + int64_t(tg) * D + 32 * g);
-      const u32x4* qv = reinterpret_cast<const u32x4*>(qp);
+      const int gi = tg - key_lo / grp_sz;
+      const u32x4* sp = reinterpret_cast<const u32x4*>(s_ks + gi * D + 32 * g);
+      const u32x4* zp = reinterpret_cast<const u32x4*>(s_kz + gi * D + 32 * g);
+      const u32x4* qv = reinterpret_cast<const u32x4*>(s_q + r16 * D + 32 * g);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const u32x4 a = sp[i], b = zp[i], c = head_ok ? qv[i] : u32x4{0, 0, 0, 0};
@@ -365,55 +398,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       vb1 *= alpha;
     }
 
-    // ---- P' = p s (per V channel group) as fp16 hi/lo, in the V conversion order, and the V bias
-    u32x4 pb[2][2], pl[2][2];  // [32-key chunk][V channel group]
+    // ---- P' = p s (per V channel group) as one fp16 number, in the V conversion order, and the
+    // V bias.  One fp16 rounding of each weight (2^-12 relative, independent) costs up to ~6e-4
+    // relative in the output (measured; the exact V zero term partly cancels the coded sum),
+    // against ~1e-5 with an fp16 hi/lo pair, for half the P.V MFMAs and P' work.
+    u32x4 pb[2][NH];  // [32-key chunk][V channel group]
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; kc2++) {
-      uint32_t w0[4], w1[4], l0[4], l1[4];
+      uint32_t w[NH][4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; e2++) {
-        float x[2], s0[2], s1[2];
+        float pr[NH][2];
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int k = perm_pos<BITS>(8 * kc2 + 2 * e2 + h);  // key 16g + k
-          x[h] = sacc[k >> 2][k & 3] * P_SCALE;
-          // fp16 scale and zero of key k: element k*nh + group
-          const float sa = h2f(uint16_t(half16(vsw, two ? 2 * k : k)));
-          const float za = h2f(uint16_t(half16(vzw, two ? 2 * k : k)));
-          s0[h] = sa;
-          vb0 = fmaf(x[h], fmaf(sa, C0, za), vb0);  // zero of the centred code
-          if (two) {
-            const float sb = h2f(uint16_t(half16(vsw, 2 * k + 1)));
-            const float zb = h2f(uint16_t(half16(vzw, 2 * k + 1)));
-            s1[h] = sb;
-            vb1 = fmaf(x[h], fmaf(sb, C0, zb), vb1);
-          } else {
-            s1[h] = sa;
+          const float x = sacc[k >> 2][k & 3] * P_SCALE;
+          // fp16 scale and zero of key k, channel group v: element k*NH + v
+#pragma unroll
+          for (int v = 0; v < NH; v++) {
+            const float sv = h2f(uint16_t(half16(vsw, NH * k + v)));
+            const float zv = h2f(uint16_t(half16(vzw, NH * k + v)));
+            pr[v][h] = x * sv;
+            if (v == 0) vb0 = fmaf(x, fmaf(sv, C0, zv), vb0);  // zero of the centred code
+            else vb1 = fmaf(x, fmaf(sv, C0, zv), vb1);
           }
         }
-        split_h2(x[0] * s0[0], x[1] * s0[1], w0[e2], l0[e2]);
-        split_h2(x[0] * s1[0], x[1] * s1[1], w1[e2], l1[e2]);
+#pragma unroll
+        for (int v = 0; v < NH; v++) w[v][e2] = pack_h2(pr[v][0], pr[v][1]);
       }
-      pb[kc2][0] = u32x4{w0[0], w0[1], w0[2], w0[3]};
-      pl[kc2][0] = u32x4{l0[0], l0[1], l0[2], l0[3]};
-      pb[kc2][1] = u32x4{w1[0], w1[1], w1[2], w1[3]};
-      pl[kc2][1] = u32x4{l1[0], l1[1], l1[2], l1[3]};
+#pragma unroll
+      for (int v = 0; v < NH; v++) pb[kc2][v] = u32x4{w[v][0], w[v][1], w[v][2], w[v][3]};
     }
     // ---- O^T += C_V^T P'^T (channels 64..127 use the second V group's P' when the group is 64)
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
       u32x4 va[2];
       cvt_vcodes<BITS>(vr[dt], va);
-      const int h = dt >> 2;
+      const int v = NH == 2 ? (dt >> 2) : 0;
 #pragma unroll
-      for (int kc2 = 0; kc2 < 2; kc2++) {
-        oacc[dt] = mfma_f16(va[kc2], pb[kc2][h], oacc[dt]);
-        oacc[dt] = mfma_f16(va[kc2], pl[kc2][h], oacc[dt]);
-      }
+      for (int kc2 = 0; kc2 < 2; kc2++) oacc[dt] = mfma_f16(va[kc2], pb[kc2][v], oacc[dt]);
     }
     if (tn < key_hi) ld_vtile<BITS>(vr, vc, tn, r16, g);
   }
 
+  __syncthreads();  // every wave is done with the scale copies that the merge buffer overwrites
   // ---- this wave's state -> LDS; lane holds o[16dt + 4g + jj] of head l % 16
   vb0 += shfl_xor(vb0, 16);
   vb0 += shfl_xor(vb0, 32);
@@ -467,8 +495,9 @@ vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_sta
   }
   VC_REQUIRE(a.group == 64 || a.group == 128, VC_ERR_UNSUPPORTED, "quant group must be 64 or 128");
   VC_REQUIRE(a.G <= 16, VC_ERR_UNSUPPORTED, "GQA group > 16");
-  VC_REQUIRE(a.split_len % (QWAVES * ATT_KT) == 0 && a.split_len % a.group == 0, VC_ERR_ARG,
-             "quantized decode: split %d must be a multiple of 256 and of the group", a.split_len);
+  VC_REQUIRE(a.split_len % (QWAVES * ATT_KT) == 0 && a.split_len % a.group == 0 && a.split_len <= QSPLIT_MAX,
+             VC_ERR_ARG, "quantized decode: split %d must be a multiple of 256 and of the group, at most %d",
+             a.split_len, QSPLIT_MAX);
   for (int r = 0; r < a.n_req; r++)
     VC_REQUIRE(a.r[r].m.tq % 64 == 0 && a.r[r].m.tq % a.group == 0, VC_ERR_ARG, "quantized rows not whole groups");
   dim3 grid(a.Hkv, a.max_splits, a.n_req);

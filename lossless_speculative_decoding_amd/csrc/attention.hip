@@ -36,100 +36,134 @@ struct TileRegs {
   u32x4 v[4];
 };
 
-// K: thread (key = tid/4, q = tid%4) loads 16-byte chunks 4e+q (e = 0..3) of its row.
+// Base pointers of tile [t0, t0 + 64) when it lies inside one plain segment (no segment
+// boundary, not the kept/staged split of the prompt, not past the last key).
+__device__ __forceinline__ bool tile_plain(const AttnReq& R, int j, int t0, int n_keys, const uint16_t*& kb,
+                                           const uint16_t*& vb) {
+  if (t0 + ATT_KT > n_keys) return false;
+  const int an = R.a.n, bn = R.b.n;
+  const KVSeg* sg;
+  int off;
+  if (t0 + ATT_KT <= an) {
+    if (R.mix.mask != nullptr) return false;
+    sg = &R.a;
+    off = t0;
+  } else if (t0 >= an && t0 + ATT_KT <= an + bn) {
+    sg = &R.b;
+    off = t0 - an;
+  } else if (t0 >= an + bn) {
+    sg = &R.c;
+    off = t0 - an - bn;
+  } else {
+    return false;
+  }
+  const int64_t o = j * sg->hstride + int64_t(off) * D128;
+  kb = static_cast<const uint16_t*>(sg->k) + o;
+  vb = static_cast<const uint16_t*>(sg->v) + o;
+  return true;
+}
+
+// K: thread (kr = tid/16, ch = tid%16) loads 16-byte chunk ch of keys kr + 16e (e = 0..3):
+//    sixteen consecutive lanes move one whole 256-byte row (coalesced in HBM, and their LDS
+//    stores cover all banks once).
 // V: thread (dc = tid/16, kg = tid%16) loads channels 8dc..8dc+7 of keys 4kg..4kg+3.
 __device__ __forceinline__ void load_tile_bf16(TileRegs& r, const AttnReq& R, int j, int t0, int n_keys, int tid) {
-  {
-    const int key = tid >> 2, q = tid & 3, t = t0 + key;
-    if (t < n_keys) {
-      const uint16_t* row = key_row<uint16_t, D128>(R, j, t, false);
+  const int kr = tid >> 4, ch = tid & 15, dc = tid >> 4, kg = tid & 15;
+  const uint16_t* kb;
+  const uint16_t* vb;
+  if (tile_plain(R, j, t0, n_keys, kb, vb)) {  // uniform across the workgroup
 #pragma unroll
-      for (int e = 0; e < 4; e++) r.k[e] = *reinterpret_cast<const u32x4*>(row + 8 * (4 * e + q));
-    } else {
+    for (int e = 0; e < 4; e++) r.k[e] = *reinterpret_cast<const u32x4*>(kb + (kr + 16 * e) * D128 + 8 * ch);
 #pragma unroll
-      for (int e = 0; e < 4; e++) r.k[e] = u32x4{0, 0, 0, 0};
-    }
+    for (int e = 0; e < 4; e++) r.v[e] = *reinterpret_cast<const u32x4*>(vb + (4 * kg + e) * D128 + 8 * dc);
+    return;
   }
-  {
-    const int dc = tid >> 4, kg = tid & 15;
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const int t = t0 + 4 * kg + e;
-      if (t < n_keys) {
-        r.v[e] = *reinterpret_cast<const u32x4*>(key_row<uint16_t, D128>(R, j, t, true) + 8 * dc);
-      } else {
-        r.v[e] = u32x4{0, 0, 0, 0};
-      }
-    }
+  for (int e = 0; e < 4; e++) {
+    const int t = t0 + kr + 16 * e;
+    r.k[e] = t < n_keys ? *reinterpret_cast<const u32x4*>(key_row<uint16_t, D128>(R, j, t, false) + 8 * ch)
+                        : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int t = t0 + 4 * kg + e;
+    r.v[e] = t < n_keys ? *reinterpret_cast<const u32x4*>(key_row<uint16_t, D128>(R, j, t, true) + 8 * dc)
+                        : u32x4{0, 0, 0, 0};
   }
 }
 
+// V^T in LDS: row d holds the tile's 64 keys in fp16, key 32kc + 16h + 4g + jj at slot
+// 32kc + 8g + 4h + jj, so the eight keys of one lane's P^T fragment are contiguous.
 __device__ __forceinline__ void store_tile_bf16(const TileRegs& r, uint16_t* Ks, uint16_t* Vt, int tid) {
-  {
-    const int key = tid >> 2, q = tid & 3;
+  const int kr = tid >> 4, ch = tid & 15, dc = tid >> 4, kg = tid & 15;
 #pragma unroll
-    for (int e = 0; e < 4; e++) *reinterpret_cast<u32x4*>(Ks + key * KS_PITCH + 8 * (4 * e + q)) = r.k[e];
-  }
-  {
-    const int dc = tid >> 4, kg = tid & 15;
+  for (int e = 0; e < 4; e++) *reinterpret_cast<u32x4*>(Ks + (kr + 16 * e) * KS_PITCH + 8 * ch) = r.k[e];
+  const int slot = 32 * (kg >> 3) + 8 * (kg & 3) + 4 * ((kg >> 2) & 1);  // keys 4kg .. 4kg + 3
 #pragma unroll
-    for (int c = 0; c < 8; c++) {
-      const int w = c >> 1;
-      float x[4];
+  for (int c = 0; c < 8; c++) {
+    const int w = c >> 1;
+    float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; e++) x[e] = (c & 1) ? hi_bf(r.v[e][w]) : lo_bf(r.v[e][w]);
-      u32x2 out;
-      out.x = bitcast<uint32_t>(f16x2{(_Float16)x[0], (_Float16)x[1]});
-      out.y = bitcast<uint32_t>(f16x2{(_Float16)x[2], (_Float16)x[3]});
-      *reinterpret_cast<u32x2*>(Vt + (8 * dc + c) * VT_PITCH + 4 * kg) = out;
-    }
+    for (int e = 0; e < 4; e++) x[e] = (c & 1) ? hi_bf(r.v[e][w]) : lo_bf(r.v[e][w]);
+    u32x2 out;
+    out.x = bitcast<uint32_t>(f16x2{(_Float16)x[0], (_Float16)x[1]});
+    out.y = bitcast<uint32_t>(f16x2{(_Float16)x[2], (_Float16)x[3]});
+    *reinterpret_cast<u32x2*>(Vt + (8 * dc + c) * VT_PITCH + slot) = out;
   }
 }
 
-// DRAFT = 1 for decode over compressed caches (one query row per request), 0 for
-// verification / prefill rows; the code is identical, the symbol names differ so
-// profiles attribute the two uses separately.
-template <int DRAFT>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
+// Rows kernel (verification, prefill, observation scores): workgroup = 4 waves =
+// (request, KV head, group of up to 64 * RPW query rows, split); wave w owns the 16-row
+// blocks w, w + 4, ... (RPW of them), so every K/V tile staged in LDS serves all the
+// rows of the group: a 33-row verification of 4 GQA heads (132 query rows) reads the
+// keys once.  Each row's arithmetic is the same whatever block or group holds it.
+template <int RPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_rows_bf16_kernel(
+    const AttnArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[ATT_KT * KS_PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D128 * VT_PITCH];
+  constexpr int GROUP_ROWS = ATT_RB * RPW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int z = blockIdx.z;
   if (z >= args.n_req) return;
   const AttnReq& R = args.r[z];
   const int Hkv = args.Hkv, G = args.G, Hq = args.Hq;
-  const int j = blockIdx.x % Hkv, rb = blockIdx.x / Hkv;
+  const int j = blockIdx.x % Hkv, rg = blockIdx.x / Hkv;
   const int s = blockIdx.y;
   const int n_qrows = R.n_rows * G;
-  const int qr0 = rb * ATT_RB;
+  const int qr0 = rg * GROUP_ROWS;
   if (qr0 >= n_qrows || s >= R.n_splits) return;  // uniform across the workgroup
 
   const int n_keys = R.a.n + R.b.n + R.c.n;
   const int key_lo = s * args.split_len;
-  const int i_max = (min(qr0 + ATT_RB, n_qrows) - 1) / G;
+  const int i_max = (min(qr0 + GROUP_ROWS, n_qrows) - 1) / G;
   const int key_hi = min(min(key_lo + args.split_len, n_keys), R.lim0 + i_max + 1);
-
-  // this lane's query row
-  const int qr = qr0 + wave * 16 + (lane & 15);
-  const bool row_ok = qr < n_qrows;
-  const int qi = row_ok ? qr / G : 0;
-  const int hq = j * G + (row_ok ? qr % G : 0);
-  const bool wave_active = qr0 + wave * 16 < n_qrows;
-  const int lim = R.lim0 + qi;
   const int grp = lane >> 4;
 
-  u32x4 qf[4];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(R.q) + (int64_t(qi) * Hq + hq) * D128;
+  // per row block of this wave: the lane's query row, its query fragments and state
+  bool row_ok[RPW], blk_on[RPW];
+  int qi[RPW], hq[RPW], lim[RPW];
+  u32x4 qf[RPW][4];
+  f32x4 oacc[RPW][8];
+  float m_run[RPW], l_run[RPW];
+#pragma unroll
+  for (int b = 0; b < RPW; b++) {
+    const int blk0 = qr0 + 16 * (wave + 4 * b);
+    const int qr = blk0 + (lane & 15);
+    blk_on[b] = blk0 < n_qrows;
+    row_ok[b] = qr < n_qrows;
+    qi[b] = row_ok[b] ? qr / G : 0;
+    hq[b] = j * G + (row_ok[b] ? qr % G : 0);
+    lim[b] = R.lim0 + qi[b];
+    const uint16_t* qp = static_cast<const uint16_t*>(R.q) + (int64_t(qi[b]) * Hq + hq[b]) * D128;
 #pragma unroll
     for (int c = 0; c < 4; c++)
-      qf[c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * grp) : u32x4{0, 0, 0, 0};
-  }
-
-  f32x4 oacc[8];
+      qf[b][c] = row_ok[b] ? *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * grp) : u32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int dt = 0; dt < 8; dt++) oacc[dt] = f32x4{0, 0, 0, 0};
-  float m_run = NEG_INF, l_run = 0.f;
+    for (int dt = 0; dt < 8; dt++) oacc[b][dt] = f32x4{0, 0, 0, 0};
+    m_run[b] = NEG_INF;
+    l_run[b] = 0.f;
+  }
   const float sl2 = args.scale_log2;
 
   TileRegs regs;
@@ -139,87 +173,92 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs args) {
     store_tile_bf16(regs, Ks, Vt, tid);
     __syncthreads();
     if (t0 + ATT_KT < key_hi) load_tile_bf16(regs, R, j, t0 + ATT_KT, n_keys, tid);
-    if (!wave_active) continue;
 
-    // ---- S^T = K Q^T over 4 sub-tiles of 16 keys
-    f32x4 sacc[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
-      sacc[kt] = f32x4{0, 0, 0, 0};
+    for (int b = 0; b < RPW; b++) {
+      if (!blk_on[b]) continue;  // uniform across the wave
+      // ---- S^T = K Q^T over 4 sub-tiles of 16 keys
+      f32x4 sacc[4];
 #pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (16 * kt + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
-        sacc[kt] = mfma_bf16(ka, qf[c], sacc[kt]);
+      for (int kt = 0; kt < 4; kt++) {
+        sacc[kt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (16 * kt + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
+          sacc[kt] = mfma_bf16(ka, qf[b][c], sacc[kt]);
+        }
       }
-    }
-    // ---- scale, mask, online softmax (row q = lane % 16)
-    float mx = NEG_INF;
+      // ---- scale, mask, online softmax (row q = lane % 16)
+      float mx = NEG_INF;
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
+      for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int t = t0 + 16 * kt + 4 * grp + jj;
-        const bool vis = row_ok && t < n_keys && t <= lim;
-        const float v = vis ? sacc[kt][jj] * sl2 : NEG_INF;
-        sacc[kt][jj] = v;
-        mx = fmaxf(mx, v);
+        for (int jj = 0; jj < 4; jj++) {
+          const int t = t0 + 16 * kt + 4 * grp + jj;
+          const bool vis = row_ok[b] && t < n_keys && t <= lim[b];
+          const float v = vis ? sacc[kt][jj] * sl2 : NEG_INF;
+          sacc[kt][jj] = v;
+          mx = fmaxf(mx, v);
+        }
       }
-    }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const bool none = (m_new == NEG_INF);
-    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    float rs = 0.f;
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[b], mx);
+      const bool none = (m_new == NEG_INF);
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[b] - m_new);
+      float rs = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
+      for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sacc[kt][jj] - m_new);
-        sacc[kt][jj] = p;
-        rs += p;
+        for (int jj = 0; jj < 4; jj++) {
+          const float p = none ? 0.f : __builtin_amdgcn_exp2f(sacc[kt][jj] - m_new);
+          sacc[kt][jj] = p;
+          rs += p;
+        }
       }
-    }
-    rs += shfl_xor(rs, 16);
-    rs += shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+      rs += shfl_xor(rs, 16);
+      rs += shfl_xor(rs, 32);
+      l_run[b] = l_run[b] * alpha + rs;
+      m_run[b] = m_new;
+      if (__any(alpha != 1.f)) {  // x * 1 == x: skip the rescale when no running max moved
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) oacc[dt] *= alpha;
+        for (int dt = 0; dt < 8; dt++) oacc[b][dt] *= alpha;
+      }
 
-    // ---- O^T += V^T P^T over 2 chunks of 32 keys
+      // ---- O^T += V^T P^T over 2 chunks of 32 keys
 #pragma unroll
-    for (int kc = 0; kc < 2; kc++) {
-      uint32_t h[4], lw[4];
-      split_h2(sacc[2 * kc][0] * P_SCALE, sacc[2 * kc][1] * P_SCALE, h[0], lw[0]);
-      split_h2(sacc[2 * kc][2] * P_SCALE, sacc[2 * kc][3] * P_SCALE, h[1], lw[1]);
-      split_h2(sacc[2 * kc + 1][0] * P_SCALE, sacc[2 * kc + 1][1] * P_SCALE, h[2], lw[2]);
-      split_h2(sacc[2 * kc + 1][2] * P_SCALE, sacc[2 * kc + 1][3] * P_SCALE, h[3], lw[3]);
-      const u32x4 pb = u32x4{h[0], h[1], h[2], h[3]};
-      const u32x4 pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
+      for (int kc = 0; kc < 2; kc++) {
+        uint32_t h[4], lw[4];
+        split_h2(sacc[2 * kc][0] * P_SCALE, sacc[2 * kc][1] * P_SCALE, h[0], lw[0]);
+        split_h2(sacc[2 * kc][2] * P_SCALE, sacc[2 * kc][3] * P_SCALE, h[1], lw[1]);
+        split_h2(sacc[2 * kc + 1][0] * P_SCALE, sacc[2 * kc + 1][1] * P_SCALE, h[2], lw[2]);
+        split_h2(sacc[2 * kc + 1][2] * P_SCALE, sacc[2 * kc + 1][3] * P_SCALE, h[3], lw[3]);
+        const u32x4 pb = u32x4{h[0], h[1], h[2], h[3]};
+        const u32x4 pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) {
-        const uint16_t* vrow = Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 4 * grp;
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 16);
-        const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
-        oacc[dt] = mfma_f16(va, pb, oacc[dt]);
-        oacc[dt] = mfma_f16(va, pl, oacc[dt]);
+        for (int dt = 0; dt < 8; dt++) {
+          const u32x4 va = *reinterpret_cast<const u32x4*>(Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 8 * grp);
+          oacc[b][dt] = mfma_f16(va, pb, oacc[b][dt]);
+          oacc[b][dt] = mfma_f16(va, pl, oacc[b][dt]);
+        }
       }
     }
   }
 
-  // ---- partial (m, l, o) of this lane's row; lane holds o[16dt + 4g + jj]
-  if (!wave_active || !row_ok) return;
-  float* dst = R.part + ((int64_t(qi) * Hq + hq) * R.s_total + (R.s_off + s)) * (D128 + 2);
-  if (grp == 0) {
-    dst[0] = m_run;
-    dst[1] = l_run;
-  }
+  // ---- partial (m, l, o) of this lane's rows; lane holds o[16dt + 4g + jj]
 #pragma unroll
-  for (int dt = 0; dt < 8; dt++) {
+  for (int b = 0; b < RPW; b++) {
+    if (!blk_on[b] || !row_ok[b]) continue;
+    float* dst = R.part + ((int64_t(qi[b]) * Hq + hq[b]) * R.s_total + (R.s_off + s)) * (D128 + 2);
+    if (grp == 0) {
+      dst[0] = m_run[b];
+      dst[1] = l_run[b];
+    }
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++) dst[2 + 16 * dt + 4 * grp + jj] = oacc[dt][jj] * P_UNSCALE;
+    for (int dt = 0; dt < 8; dt++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) dst[2 + 16 * dt + 4 * grp + jj] = oacc[b][dt][jj] * P_UNSCALE;
+    }
   }
 }
 
@@ -614,12 +653,16 @@ vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, bool draft) {
   if (a.n_req <= 0 || a.max_splits <= 0) return VC_OK;
   if (dtype == VC_BF16) {
     VC_REQUIRE(a.head_dim == 128, VC_ERR_UNSUPPORTED, "bf16 attention needs head_dim 128 (got %d)", a.head_dim);
-    dim3 grid(a.Hkv * a.n_rowblocks, a.max_splits, a.n_req);
-    if (draft) {
-      hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(256), 0, s, a);
-    } else {
-      hipLaunchKernelGGL(attn_bf16_kernel<0>, grid, dim3(256), 0, s, a);
-    }
+    (void)draft;
+    int max_qrows = 0;
+    for (int i = 0; i < a.n_req; i++) max_qrows = max(max_qrows, a.r[i].n_rows * a.G);
+    // row blocks per wave: enough for the largest request up to 3 (a 192-row group)
+    const int rpw = max(1, min(3, int(cdiv(max_qrows, ATT_RB))));
+    const int n_groups = int(cdiv(max_qrows, ATT_RB * rpw));
+    dim3 grid(a.Hkv * n_groups, a.max_splits, a.n_req);
+    if (rpw == 1) hipLaunchKernelGGL(attn_rows_bf16_kernel<1>, grid, dim3(256), 0, s, a);
+    else if (rpw == 2) hipLaunchKernelGGL(attn_rows_bf16_kernel<2>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_rows_bf16_kernel<3>, grid, dim3(256), 0, s, a);
   } else {
     VC_REQUIRE(a.head_dim == 64, VC_ERR_UNSUPPORTED, "fp32 attention needs head_dim 64 (got %d)", a.head_dim);
     int max_qrows = 0;

@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
@@ -89,7 +90,7 @@ def cpu_baseline(shape, ctx: int, keep: int, seed: int = 0) -> dict:
                        f"{s.n_layers} layers; {per_token:.2f} s per token; weight generation {t_gen:.1f} s excluded")}
 
 
-def pmc_traffic_ratio(workload: str):
+def pmc_traffic_ratio(workload: str, kernel: str = "attn_decode_bf16"):
     """Measured HBM bytes over algorithmic bytes of the draft-attention launches, from the
     committed counter profile of this workload (profiles/draft_attention_<workload>_pmc.json),
     if the kernel sources are unchanged since.  The
@@ -101,10 +102,141 @@ def pmc_traffic_ratio(workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("sources_sha256") != sources_sha256():
+    if rec.get("kernel") != kernel or rec.get("sources_sha256") != sources_sha256(kernel):
         log(f"{path}: kernel sources changed since the counters were taken; traffic not reported")
         return None
     return rec.get("traffic_over_algorithmic")
+
+
+def cpu_baseline_layer(T: int, Hq: int, Hkv: int, D: int, rows: int, bits: int, group: int) -> dict:
+    """The oracle, as written, on one (request, KV head) slice of the single-layer workload:
+    the draft step's attention over the dequantized cache for the G query heads, and the
+    verification attention of all rows; reported as algorithmic bytes of that slice / time."""
+    import threadpoolctl
+
+    from oracle import attention as OA
+    from oracle import compress as OC
+    from oracle.model import attend
+    import numpy as np
+    inp = OA.head_inputs(0, 0, T, Hkv, Hq, D, rows)
+    q = OC.Quantized(inp["K"][None, None], inp["V"][None, None], bits, group)   # compression: not timed
+    with threadpoolctl.threadpool_limits(None) as _:
+        info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    t0 = time.perf_counter()
+    K = np.concatenate([q.rows_K()[0, 0], inp["tK"][:1]])
+    V = np.concatenate([q.rows_V()[0, 0], inp["tV"][:1]])
+    _ = [attend(qh, K, V) for qh in inp["qd"]]
+    t_draft = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    _ = OA.verify_output(inp)
+    t_verify = time.perf_counter() - t0
+    Tq = T // group * group
+    draft_bytes = 2 * Tq * D * bits / 8 + 2 * (Tq // group) * D * 2 + 2 * Tq * (D // group) * 2 + 2 * D * 2 \
+        + (Hq // Hkv) * D * 2
+    verify_bytes = 2 * (T + rows) * D * 2 + rows * (Hq // Hkv) * D * 2
+    return {"value": round(draft_bytes / t_draft / 1e9, 4), "unit": "GB/s (draft attention, algorithmic bytes)",
+            "cores": threads, "kind": "oracle",
+            "verify_gbs": round(verify_bytes / t_verify / 1e9, 4),
+            "sample": (f"request 0, KV head 0 of the workload: draft attention of its {Hq // Hkv} query heads over "
+                       f"the dequantized {T}-row cache ({t_draft:.2f} s) and verification attention of {rows} rows "
+                       f"({t_verify:.2f} s), float64 numpy; quantization excluded")}
+
+
+def bench_layer(args):
+    """Single GQA attention layer (Llama-3-8B head shapes): a step is one batched draft-step
+    attention of every request over its quantized cache plus one batched verification attention
+    of its rows over the full bf16 cache."""
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import configs
+    import lossless_speculative_decoding_amd as vc
+    from lossless_speculative_decoding_amd._vc import AttnDesc
+    w = configs.gqa_layer()
+    e = w.extra
+    Hq, Hkv, D, rows = e["n_q_heads"], e["n_kv_heads"], e["head_dim"], e["verify_rows"]
+    B, T, bits, group = w.batch, w.ctx[0], w.compress.bits, w.compress.group
+    torch.cuda.set_device(0)
+
+    def gen(shape, stream, outl=None, scale=1.0):
+        t = torch.empty(*shape, dtype=torch.bfloat16, device="cuda")
+        vc.synth_normal_heads(t, stream, outl, scale)
+        return t
+
+    outl = torch.from_numpy(np.stack([synth.outlier_channels_for(b, j, Hkv, D) for b in range(B)
+                                      for j in range(Hkv)]).astype(np.int32)).cuda()
+    K = gen((B, Hkv, T, D), synth.S_ATT_K, outl, e["outlier_scale"])
+    V = gen((B, Hkv, T, D), synth.S_ATT_V, outl, e["outlier_scale"])
+    tK = gen((B, Hkv, rows, D), synth.S_ATT_TK)
+    tV = gen((B, Hkv, rows, D), synth.S_ATT_TV)
+    qd = gen((1, B, Hq, D), synth.S_ATT_QD)[0]
+    qv = gen((1, B * rows, Hq, D), synth.S_ATT_QV)[0].view(B, rows, Hq, D)
+    cds, blobs = [], []
+    for b in range(B):
+        d = vc.compress_desc(vc.VC_QUANT, 1, Hq, Hkv, D, T, vc.VC_BF16, bits=bits, group=group)
+        cds.append(d)
+        blobs.append(vc.vc_compress(d, K[b:b + 1], V[b:b + 1]))
+    torch.cuda.synchronize()
+    desc = AttnDesc(Hq, Hkv, D, vc.VC_BF16, 0, vc.VC_BF16)
+    Ks, Vs = [K[b] for b in range(B)], [V[b] for b in range(B)]
+    tKs, tVs = [tK[b] for b in range(B)], [tV[b] for b in range(B)]
+
+    def step():
+        vc.vc_attn_draft(desc, blobs, cds, tKs, tVs, [1] * B, qd)
+        vc.vc_attn_verify(desc, qv, Ks, Vs, [T] * B, tKs, tVs, rows)
+
+    kinds = (vc.VC_PROF_DRAFT_ATTN, vc.VC_PROF_VERIFY_ATTN)
+    vc.profile_enable(kinds)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for k in kinds:
+        vc.profile_read(k)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    secs = time.perf_counter() - t0
+    vc.profile_enable(())
+    dp, vp = vc.profile_read(vc.VC_PROF_DRAFT_ATTN), vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
+    dr = _rate(dp, "hbm", f"quantized draft attention partials, {B} requests x {Hkv} KV heads x {T} keys, "
+                          f"{bits}-bit group {group}")
+    vr = _rate(vp, "hbm", f"verification attention partials, {B} requests x {rows} rows x {Hq} heads over "
+                          f"{T} + {rows} keys")
+    ratio = pmc_traffic_ratio(w.name, "attn_quant")
+    dr["traffic"] = round(ratio * dr["bytes_per_launch"]) if ratio else None
+    dr["traffic_over_algorithmic"] = ratio
+    cpu = None if args.no_cpu_baseline else cpu_baseline_layer(T, Hq, Hkv, D, rows, bits, group)
+    line = {
+        "metric": "draft-attn HBM GB/s vs peak (single GQA layer)",
+        "value": dr["achieved"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1000 * secs / args.steps, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V with 4 outlier channels x10)",
+        "config": {"workload": w.name, "batch": B, "ctx": T, "bits": bits, "group": group, "verify_rows": rows},
+        "roofline": dr, "verify_attention": vr, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _rate(st: dict, bound: str, what: str) -> dict | None:
+    """Live-timed kernel class against its roof: HBM bytes/s or bf16 MFMA flop/s."""
+    if not st or st["launches"] == 0 or st["ms"] <= 0:
+        return None
+    secs = st["ms"] * 1e-3
+    gbs = st["bytes"] / secs / 1e9
+    tflops = st["flops"] / secs / 1e12
+    if bound == "hbm":
+        out = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(gbs / HBM_PEAK_GBS, 4), "tflops": round(tflops, 2)}
+    else:
+        out = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+               "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "gbs": round(gbs, 1)}
+    out.update({"kernel": what, "launches": st["launches"], "avg_launch_ms": round(st["ms"] / st["launches"], 5),
+                "bytes_per_launch": round(st["bytes"] / st["launches"]),
+                "flops_per_launch": round(st["flops"] / st["launches"])})
+    return out
 
 
 def main():
@@ -112,7 +244,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16, help="timed scheduler round periods (x draft steps each)")
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="llama8b_tokdrop", choices=["llama8b_tokdrop", "llama8b_q2", "llama8b_mixed"])
+    ap.add_argument("--config", default="llama8b_tokdrop",
+                    choices=["llama8b_tokdrop", "llama8b_q2", "llama8b_mixed", "gqa_layer"])
     ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
     ap.add_argument("--baseline-steps", type=int, default=2)
@@ -135,6 +268,10 @@ def main():
               "GPUs by request, each GPU running this same loop)", file=sys.stderr)
         sys.exit(2)
 
+    if args.config == "gqa_layer":
+        bench_layer(args)
+        return
+
     import torch
 
     import synth
@@ -155,11 +292,18 @@ def main():
     W = make_weights(s)
     model = vc.Model(s, W, max_pos=max(ctx) + w.n_tokens + 64)
     eng = Engine(model, w.compress, chunk=2048)
+    prefill_prof = None
     for r, (T, x) in enumerate(zip(ctx, xs)):
         p = torch.empty(T, dtype=torch.int32, device="cuda")
         vc.synth_ids(p, synth.S_PROMPT + r, s.vocab)
         t0 = time.perf_counter()
+        if r == 0:  # request 0's prefill: live timing of its tiled GEMMs and causal attention
+            vc.profile_enable((vc.VC_PROF_GEMM_TILED, vc.VC_PROF_PREFILL_ATTN))
         eng.add_request(p, x, w.n_tokens, keep_prefill_kv=(r == 0))
+        if r == 0:
+            vc.profile_enable(())
+            prefill_prof = {"gemm": vc.profile_read(vc.VC_PROF_GEMM_TILED),
+                            "attention": vc.profile_read(vc.VC_PROF_PREFILL_ATTN), "tokens": T}
         log(f"request {r}: T={T} prefill+compress+offload {time.perf_counter() - t0:.1f}s")
     x_round = max(xs)
     eng.start()
@@ -168,11 +312,14 @@ def main():
 
     # warmup (draft-attention launches recorded too, so that a counter profile of this command,
     # which sees every launch, can be compared with the algorithmic bytes of the same launches)
-    vc.profile_read()
-    vc.profile_enable(True)
+    kinds = (vc.VC_PROF_DRAFT_ATTN, vc.VC_PROF_VERIFY_ATTN)
+    for k in kinds:
+        vc.profile_read(k)
+    vc.profile_enable(kinds)
     eng.run_draft_steps(args.warmup * x_round)
     eng.drain()
     warm = vc.profile_read()
+    vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
     # timed region
     torch.cuda.synchronize()
     e0 = eng.emitted_total()
@@ -183,8 +330,9 @@ def main():
     eng.drain()
     torch.cuda.synchronize()
     secs = time.perf_counter() - t0
-    vc.profile_enable(False)
+    vc.profile_enable(())
     prof = vc.profile_read()
+    vprof = vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
     emitted = eng.emitted_total() - e0
     staged, n_staged = eng.staged_bytes - sb0, eng.stagings - sn0
     tok_s = emitted / secs
@@ -212,6 +360,17 @@ def main():
             r.req.draft_idx = min(r.req.draft_idx + 1, r.x - 1)
     torch.cuda.synchronize()
     draft_only = len(live) * x_round / (time.perf_counter() - t_d)
+    # the same draft steps again with live timing of their weight-streaming GEMMs (separate
+    # pass: a per-GEMM event pair is not free at these kernel lengths)
+    vc.profile_read(vc.VC_PROF_GEMM_SKINNY)
+    vc.profile_enable((vc.VC_PROF_GEMM_SKINNY,))
+    for _ in range(x_round):
+        eng.m.draft_step([r.req for r in live], eng.ws_draft)
+        for r in live:
+            r.req.draft_idx = min(r.req.draft_idx + 1, r.x - 1)
+    torch.cuda.synchronize()
+    vc.profile_enable(())
+    gprof = vc.profile_read(vc.VC_PROF_GEMM_SKINNY)
     for r in live:
         r.req.draft_idx = 0
     log(f"compressed-only draft decoding (lossy): {draft_only:.1f} tok/s over {len(live)} requests")
@@ -261,6 +420,13 @@ def main():
                      "avg_launch_ms": round(att_ms, 5), "launches": prof["launches"],
                      "bytes_per_launch": round(prof["bytes"] / max(prof["launches"], 1)),
                      "bytes_per_launch_incl_warmup": round(all_bytes), "launches_incl_warmup": all_launches},
+        "verify_attention": _rate(vprof, "hbm", "verification attention partials (one layer of one request)"),
+        "gemm_decode": _rate(gprof, "hbm", f"projection and LM-head GEMMs of {len(live)}-request draft steps "
+                                           "(weight streaming)"),
+        "gemm_prefill": _rate(prefill_prof["gemm"], "mfma", f"projection GEMMs of request 0's prefill "
+                                                             f"({prefill_prof['tokens']} tokens, 2048-row chunks)"),
+        "attention_prefill": _rate(prefill_prof["attention"], "mfma", "causal attention of request 0's prefill "
+                                                                      "(2048-row chunks)"),
         "pcie": {"bound": "pcie", "achieved": round(pcie_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                  "frac": round(pcie_gbs / PCIE_PEAK_GBS, 4), "stagings": n_staged,
                  "bytes_per_staging": round(staged / max(n_staged, 1)),

@@ -307,22 +307,40 @@ vc_status vc_attn_verify(const vc_attn_desc* d, int32_t n, const void* q, const 
 vc_status vc_attn_ws_size(const vc_attn_desc* d, int32_t n, int32_t rows, int32_t max_keys, size_t* bytes);
 
 /* ------------------------------------------------------------------------
- * Live measurement of the draft-attention kernels (the decode attention over
- * compressed caches, the HBM-bound core of every draft step).  When enabled,
- * each vc_draft_step / vc_attn_draft records a HIP event pair on its stream
- * around the attention-partial launches of every layer, together with the
- * algorithmic bytes those launches must move (codes, scales and zeros, or
- * kept rows, plus exact tail rows, queries and split partials).
- * vc_profile_read synchronises the recorded events and returns the totals;
- * it clears the record.  Not thread-safe; intended for benchmarks.
+ * Live measurement of kernel classes, for benchmarks.  When the class's bit
+ * (1 << kind) is enabled, every launch of that class records a HIP event pair
+ * taken at the kernel's own start and end on its stream, together with the
+ * algorithmic bytes the launch must move and the flops it must compute:
+ *   VC_PROF_DRAFT_ATTN    draft-step attention partials of all requests of one
+ *                         layer (one pair spans the quantized and the exact-row
+ *                         launch): compressed main region (codes, scales and zeros,
+ *                         or kept rows), exact tail rows, queries, split partials;
+ *   VC_PROF_VERIFY_ATTN   verification attention of one layer: every key visible to
+ *                         the last row, K and V once per KV head, queries, partials;
+ *                         flops 4 D Hq per (row, visible key);
+ *   VC_PROF_GEMM_SKINNY   projection / LM-head GEMM with M <= 64 rows (weights, X,
+ *                         float32 partials; flops 2 M N K);
+ *   VC_PROF_GEMM_TILED    the same for larger M (prefill chunks);
+ *   VC_PROF_PREFILL_ATTN  causal prefill attention of one chunk (bytes as for
+ *                         verification; its keys are read once per row group).
+ * vc_profile_read synchronises the recorded events of one class, returns the
+ * totals and clears that class's record.  Not thread-safe.
  * ---------------------------------------------------------------------- */
+#define VC_PROF_DRAFT_ATTN 0
+#define VC_PROF_VERIFY_ATTN 1
+#define VC_PROF_GEMM_SKINNY 2
+#define VC_PROF_GEMM_TILED 3
+#define VC_PROF_PREFILL_ATTN 4
+#define VC_PROF_KINDS 5
 typedef struct {
-  int64_t launches;   /* attention-partial launch groups timed              */
+  int64_t launches;   /* timed launches (or launch groups)                  */
   double total_ms;    /* summed event time of those launches               */
   double bytes;       /* summed algorithmic bytes                          */
+  double flops;       /* summed algorithmic flops                          */
 } vc_profile_stats;
-vc_status vc_profile_enable(int32_t on);
-vc_status vc_profile_read(vc_profile_stats* out);
+/* mask: bit k enables class k (0 disables all). */
+vc_status vc_profile_enable(uint32_t mask);
+vc_status vc_profile_read(int32_t kind, vc_profile_stats* out);
 
 /* ------------------------------------------------------------------------
  * Seeded synthetic inputs (not part of the method): the counter-based

@@ -16,6 +16,8 @@ VC_OK, VC_ERR_ARG, VC_ERR_UNSUPPORTED, VC_ERR_CAPACITY, VC_ERR_HIP = 0, -1, -2, 
 VC_F32, VC_BF16 = 0, 1
 VC_TOKDROP, VC_QUANT = 1, 2
 VC_MAX_BATCH = 16
+(VC_PROF_DRAFT_ATTN, VC_PROF_VERIFY_ATTN, VC_PROF_GEMM_SKINNY, VC_PROF_GEMM_TILED,
+ VC_PROF_PREFILL_ATTN) = range(5)
 
 
 class VCError(RuntimeError):
@@ -60,7 +62,7 @@ class AttnDesc(C.Structure):
 
 
 class ProfileStats(C.Structure):
-    _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("bytes", C.c_double)]
+    _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("bytes", C.c_double), ("flops", C.c_double)]
 
 
 class AttnDraftReq(C.Structure):
@@ -94,11 +96,11 @@ _SIGS = {
     "vc_synth_normal_heads": (_I, [_P, _I, _I, _I, _I, C.c_uint32, C.c_uint32, _P, _I, C.c_float, _P]),
     "vc_synth_ids": (_I, [_P, C.c_int64, C.c_uint32, C.c_uint32, _I, _P]),
     "vc_synth_fill": (_I, [_P, _I, C.c_int64, C.c_float, _P]),
-    "vc_profile_enable": (_I, [_I]),
+    "vc_profile_enable": (_I, [C.c_uint32]),
     "vc_host_alloc": (_I, [_S, C.POINTER(_P)]),
     "vc_host_free": (_I, [_P]),
     "vc_offload": (_I, [_P, C.POINTER(Req), _P, _P, _I, _I, _P]),
-    "vc_profile_read": (_I, [C.POINTER(ProfileStats)]),
+    "vc_profile_read": (_I, [_I, C.POINTER(ProfileStats)]),
 }
 
 if not os.path.exists(LIB_PATH):

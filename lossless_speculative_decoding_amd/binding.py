@@ -11,13 +11,15 @@ import ctypes as C
 import torch
 
 from . import _vc
-from ._vc import (VC_BF16, VC_F32, VC_QUANT, VC_TOKDROP, AttnDesc, AttnDraftReq, CompressDesc, CompressLayout,
-                  ModelDesc, ProfileStats, Req, Weights, call)
+from ._vc import (VC_BF16, VC_F32, VC_PROF_DRAFT_ATTN, VC_PROF_GEMM_SKINNY, VC_PROF_GEMM_TILED,
+                  VC_PROF_PREFILL_ATTN, VC_PROF_VERIFY_ATTN, VC_QUANT, VC_TOKDROP, AttnDesc, AttnDraftReq,
+                  CompressDesc, CompressLayout, ModelDesc, ProfileStats, Req, Weights, call)
 
 __all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "CompressDesc", "Req", "Model", "compress_desc",
            "compress_layout", "vc_compress", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
            "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes",
-           "profile_enable", "profile_read", "HostBuffer", "PageableBuffer"]
+           "profile_enable", "profile_read", "HostBuffer", "PageableBuffer", "VC_PROF_DRAFT_ATTN",
+           "VC_PROF_VERIFY_ATTN", "VC_PROF_GEMM_SKINNY", "VC_PROF_GEMM_TILED", "VC_PROF_PREFILL_ATTN"]
 
 
 def stream_handle(s: torch.cuda.Stream | None = None) -> int:
@@ -213,14 +215,20 @@ class Model:
 
 
 # ---------------------------------------------------------------- live kernel timing
-def profile_enable(on: bool = True):
-    call("vc_profile_enable", 1 if on else 0)
+def profile_enable(kinds=(VC_PROF_DRAFT_ATTN,)):
+    """Time the given kernel classes (VC_PROF_*) from now on; an empty tuple stops."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << k
+    call("vc_profile_enable", mask)
 
 
-def profile_read() -> dict:
+def profile_read(kind: int = VC_PROF_DRAFT_ATTN) -> dict:
+    """Totals of one kernel class since its last read (launches, event ms, algorithmic bytes
+    and flops); clears that class's record."""
     st = ProfileStats()
-    call("vc_profile_read", C.byref(st))
-    return {"launches": st.launches, "ms": st.total_ms, "bytes": st.bytes}
+    call("vc_profile_read", kind, C.byref(st))
+    return {"launches": st.launches, "ms": st.total_ms, "bytes": st.bytes, "flops": st.flops}
 
 
 class PageableBuffer:

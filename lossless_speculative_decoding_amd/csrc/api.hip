@@ -30,13 +30,15 @@ void set_error(const char* fmt, ...) {
 using namespace vc;
 
 namespace {
-// draft-attention timing record (vc_profile_*)
+// live kernel timing (vc_profile_*): an event pair around a launch (or launch group) of one
+// kernel class, with the algorithmic bytes and flops that launch must move and compute
 struct ProfRec {
-  hipEvent_t a, b;
-  double bytes;
+  hipEvent_t a = nullptr, b = nullptr;
+  double bytes = 0, flops = 0;
+  int kind = 0;
 };
-bool g_prof_on = false;
-std::vector<ProfRec> g_prof;
+uint32_t g_prof_mask = 0;
+std::vector<ProfRec> g_prof[VC_PROF_KINDS];
 std::vector<hipEvent_t> g_prof_pool;
 
 hipEvent_t prof_event() {
@@ -45,9 +47,50 @@ hipEvent_t prof_event() {
     g_prof_pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence (cache writeback) when the event completes, which would
+  // otherwise lengthen the measured interval and the work after it
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
+}
+
+// events are null (and nothing is recorded) unless the kind is enabled
+ProfRec prof_begin(int kind, double bytes, double flops) {
+  ProfRec r;
+  r.kind = kind;
+  r.bytes = bytes;
+  r.flops = flops;
+  if (g_prof_mask & (1u << kind)) {
+    r.a = prof_event();
+    r.b = prof_event();
+    if (!r.a || !r.b) r.a = r.b = nullptr;
+  }
+  return r;
+}
+
+void prof_commit(const ProfRec& r) {
+  if (r.a && r.b) g_prof[r.kind].push_back(r);
+}
+
+// many-row attention launch: every key visible to the last row read once per KV head (K and V),
+// the queries read, the split partials written; flops of QK^T and PV over the causal rows
+ProfRec prof_rows(int kind, const AttnArgs& a, int eb) {
+  double bytes = 0, flops = 0;
+  for (int r = 0; r < a.n_req; r++) {
+    const AttnReq& q = a.r[r];
+    const double rows = q.n_rows, keys = double(q.lim0) + q.n_rows;
+    bytes += double(a.Hkv) * keys * a.head_dim * eb * 2 + rows * a.Hq * a.head_dim * eb +
+             rows * a.Hq * q.n_splits * (a.head_dim + 2) * 4.0;
+    flops += 4.0 * a.head_dim * a.Hq * (rows * q.lim0 + 0.5 * rows * (rows + 1));
+  }
+  return prof_begin(kind, bytes, flops);
+}
+
+// one projection GEMM: weights + activations read, float32 partials written once
+ProfRec prof_gemm(int M, int N, int K, int S, int dtype) {
+  const double eb = dtype == VC_BF16 ? 2 : 4;
+  const int kind = (dtype == VC_BF16 && M <= 64) ? VC_PROF_GEMM_SKINNY : VC_PROF_GEMM_TILED;
+  return prof_begin(kind, (double(N) * K + double(M) * K) * eb + double(S) * M * N * 4, 2.0 * M * N * K);
 }
 }  // namespace
 
@@ -120,8 +163,10 @@ WsLayout ws_layout(const vc_model* m, int R, int max_keys) {
 vc_status proj(const vc_model* m, const void* X, const void* W, int M, int N, int K, float* P, EpiArgs e,
                hipStream_t s) {
   const int S = gemm_splits(M, N, K, m->d.dtype);
-  vc_status st = gemm(X, W, P, M, N, K, S, m->d.dtype, s);
+  const ProfRec pr = prof_gemm(M, N, K, S, m->d.dtype);
+  vc_status st = gemm(X, W, P, M, N, K, S, m->d.dtype, s, pr.a, pr.b);
   if (st) return st;
+  prof_commit(pr);
   e.P = P;
   e.M = M;
   e.N = N;
@@ -199,7 +244,9 @@ vc_status head(const vc_model* m, int r0, int M, uint8_t* ws, const WsLayout& L,
   void* a = ws + L.a;
   float* P = reinterpret_cast<float*>(ws + L.y);
   if ((st = k_rmsnorm(hrow, m->w.norm_final, a, M, d.d_model, d.eps, d.dtype, s))) return st;
-  if ((st = gemm(a, m->w.lm_head, P, M, d.vocab, d.d_model, 1, d.dtype, s))) return st;
+  const ProfRec pr = prof_gemm(M, d.vocab, d.d_model, 1, d.dtype);
+  if ((st = gemm(a, m->w.lm_head, P, M, d.vocab, d.d_model, 1, d.dtype, s, pr.a, pr.b))) return st;
+  prof_commit(pr);
   if ((st = k_argmax(P, M, d.vocab, out_tok, s))) return st;
   if (logits_opt) VC_HIP(hipMemcpyAsync(logits_opt, P, size_t(M) * d.vocab * 4, hipMemcpyDeviceToDevice, s));
   return VC_OK;
@@ -335,7 +382,7 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     aa.max_splits = std::max(aa.max_splits, ts_n[r]);
   }
   // algorithmic bytes of the partial launches (for vc_profile_read)
-  double bytes = 0;
+  double bytes = 0, flops_keys = 0;  // flops_keys: query heads x keys attended
   for (int r = 0; r < n; r++) {
     const CompView& v = views[r];
     const double row = double(D) * (dtype == VC_BF16 ? 2 : 4);
@@ -343,19 +390,16 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
       const double ng = v.tq / v.group, nh = D / v.group;
       bytes += double(Hkv) * (2.0 * v.tq * D * v.bits / 8 + 2.0 * ng * D * 2 + 2.0 * v.tq * nh * 2);
       bytes += double(Hkv) * (v.n_resid + tail_n[r]) * row * 2;
+      flops_keys += double(Hq) * (v.tq + v.n_resid + tail_n[r]);
     } else {
       bytes += double(Hkv) * (v.kk + tail_n[r]) * row * 2;
+      flops_keys += double(Hq) * (v.kk + tail_n[r]);
     }
     bytes += double(Hq) * row;                                       // query
     bytes += double(Hq) * (qs_n[r] + ts_n[r]) * (D + 2) * 4.0;        // partials written
   }
   // live timing: the first partial launch's own start and the last one's own end
-  ProfRec rec{nullptr, nullptr, bytes};
-  if (g_prof_on) {
-    rec.a = prof_event();
-    rec.b = prof_event();
-    if (!rec.a || !rec.b) rec.a = rec.b = nullptr;
-  }
+  ProfRec rec = prof_begin(VC_PROF_DRAFT_ATTN, bytes, 4.0 * flops_keys * D);
   vc_status st;
   if (qa.n_req > 0) {
     qa.Hq = Hq;
@@ -372,11 +416,9 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
   if (decode) {
     if ((st = launch_attn_decode(aa, s, start, rec.b))) return st;
   } else {
-    if (start) VC_HIP(hipEventRecord(start, s));
-    if ((st = launch_attn(aa, dtype, s, true))) return st;
-    if (rec.b) VC_HIP(hipEventRecord(rec.b, s));
+    if ((st = launch_attn(aa, dtype, s, start, rec.b))) return st;
   }
-  if (rec.a && rec.b) g_prof.push_back(rec);
+  prof_commit(rec);
   CombineArgs c{};
   c.n_req = n;
   c.n_rows = 1;
@@ -399,27 +441,30 @@ extern "C" {
 
 const char* vc_last_error(void) { return g_err.c_str(); }
 
-vc_status vc_profile_enable(int32_t on) {
-  g_prof_on = on != 0;
+vc_status vc_profile_enable(uint32_t mask) {
+  g_prof_mask = mask & ((1u << VC_PROF_KINDS) - 1);
   return VC_OK;
 }
 
-vc_status vc_profile_read(vc_profile_stats* out) {
+vc_status vc_profile_read(int32_t kind, vc_profile_stats* out) {
   VC_REQUIRE(out != nullptr, VC_ERR_ARG, "vc_profile_read: null output");
-  *out = vc_profile_stats{0, 0.0, 0.0};
-  for (ProfRec& r : g_prof) {
+  VC_REQUIRE(kind >= 0 && kind < VC_PROF_KINDS, VC_ERR_ARG, "vc_profile_read: bad kind %d", kind);
+  *out = vc_profile_stats{0, 0.0, 0.0, 0.0};
+  for (ProfRec& r : g_prof[kind]) {
     VC_HIP(hipEventSynchronize(r.b));
     float ms = 0.f;
     VC_HIP(hipEventElapsedTime(&ms, r.a, r.b));
     out->launches += 1;
     out->total_ms += ms;
     out->bytes += r.bytes;
+    out->flops += r.flops;
     g_prof_pool.push_back(r.a);
     g_prof_pool.push_back(r.b);
   }
-  g_prof.clear();
+  g_prof[kind].clear();
   return VC_OK;
 }
+
 int32_t vc_abi_version(void) { return 1; }
 
 vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStream_t s, vc_model** out) {
@@ -658,8 +703,10 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
     r.s_off = 0;
     r.s_total = S;
     r.n_splits = S;
-    vc_status st2 = launch_attn(a, d.dtype, s);
+    const ProfRec pr = prof_rows(VC_PROF_VERIFY_ATTN, a, eb);
+    vc_status st2 = launch_attn(a, d.dtype, s, pr.a, pr.b);
     if (st2) return st2;
+    prof_commit(pr);
     CombineArgs c{};
     c.n_req = 1;
     c.n_rows = n_rows;
@@ -732,8 +779,10 @@ vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out,
       r.s_off = 0;
       r.s_total = 1;
       r.n_splits = 1;
-      vc_status st2 = launch_attn(a, d.dtype, s);
+      const ProfRec pr = prof_rows(VC_PROF_PREFILL_ATTN, a, eb);
+      vc_status st2 = launch_attn(a, d.dtype, s, pr.a, pr.b);
       if (st2) return st2;
+      prof_commit(pr);
       CombineArgs c{};
       c.n_req = 1;
       c.n_rows = C;
@@ -989,8 +1038,10 @@ vc_status vc_attn_verify(const vc_attn_desc* d, int32_t n, const void* q, const 
     c.out[r] = mptr(out, r * ostride);
     c.s_used[r] = ar.n_splits;
   }
-  vc_status st = launch_attn(a, d->dtype, s);
+  const ProfRec pr = prof_rows(VC_PROF_VERIFY_ATTN, a, eb);
+  vc_status st = launch_attn(a, d->dtype, s, pr.a, pr.b);
   if (st) return st;
+  prof_commit(pr);
   return launch_combine(c, s);
 }
 

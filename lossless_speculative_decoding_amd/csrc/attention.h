@@ -115,11 +115,13 @@ struct QuantArgs {
   float scale_log2;
 };
 
-// dtype: VC_BF16 (head_dim 128, MFMA) or VC_F32 (head_dim 64, VALU)
-vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, bool draft = false);
-// ev_start / ev_stop (may be null): HIP events that take the kernel's own start and end
-// time (hipExtLaunchKernelGGL), for live kernel timing without marker-packet gaps; when
-// nothing is launched they are recorded on the stream instead.
+// ev_start / ev_stop (may be null) in the launchers below: HIP events that take the
+// kernel's own start and end time (hipExtLaunchKernelGGL), for live kernel timing without
+// marker-packet gaps; when nothing is launched they are recorded on the stream instead.
+
+// Many-row attention. dtype: VC_BF16 (head_dim 128, MFMA) or VC_F32 (head_dim 64, VALU)
+vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start = nullptr,
+                      hipEvent_t ev_stop = nullptr);
 vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_start = nullptr,
                             hipEvent_t ev_stop = nullptr);
 

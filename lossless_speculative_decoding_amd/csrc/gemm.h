@@ -13,7 +13,9 @@ namespace vc {
 int gemm_splits(int M, int N, int K, int dtype);
 // Partials for M <= 64 (decode / verify): weight-streaming bf16 MFMA kernel or fp32 VALU kernel.
 // Larger M (prefill chunks) uses the tiled bf16 MFMA kernel with S = 1.
-vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int S, int dtype, hipStream_t s);
+// ev_start / ev_stop (optional) are recorded at the kernel's own start and end.
+vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int S, int dtype, hipStream_t s,
+               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 enum EpiMode { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_COPY = 3 };
 

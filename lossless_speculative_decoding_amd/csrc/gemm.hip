@@ -276,7 +276,8 @@ int gemm_splits(int M, int N, int K, int dtype) {
   return int(cdiv(K, kps));
 }
 
-vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int S, int dtype, hipStream_t s) {
+vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int S, int dtype, hipStream_t s,
+               hipEvent_t ev_start, hipEvent_t ev_stop) {
   VC_REQUIRE(M > 0 && N > 0 && K > 0, VC_ERR_ARG, "gemm: bad shape %d x %d x %d", M, N, K);
   if (dtype == VC_BF16) {
     VC_REQUIRE(K % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: K=%d not a multiple of 128", K);
@@ -285,18 +286,18 @@ vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int 
       const int want = S;
       const int kps = int(cdiv(cdiv(K, want), 128) * 128);
       VC_REQUIRE(cdiv(K, kps) == S, VC_ERR_ARG, "gemm: split count %d inconsistent", S);
-      hipLaunchKernelGGL(gemm_skinny_bf16, dim3(N / SK_NB, S), dim3(256), 0, s, static_cast<const uint16_t*>(X),
-                         static_cast<const uint16_t*>(W), P, M, N, K, kps);
+      hipExtLaunchKernelGGL(gemm_skinny_bf16, dim3(N / SK_NB, S), dim3(256), 0, s, ev_start, ev_stop, 0,
+                            static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K, kps);
     } else {
       VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: prefill tiles use one split");
       VC_REQUIRE(N % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: N=%d not a multiple of 128", N);
-      hipLaunchKernelGGL(gemm_big_bf16, dim3(N / 128, cdiv(M, 128)), dim3(256), 0, s, static_cast<const uint16_t*>(X),
-                         static_cast<const uint16_t*>(W), P, M, N, K);
+      hipExtLaunchKernelGGL(gemm_big_bf16, dim3(N / 128, cdiv(M, 128)), dim3(256), 0, s, ev_start, ev_stop, 0,
+                            static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K);
     }
   } else {
     VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: fp32 path uses one split");
-    hipLaunchKernelGGL(gemm_f32_tiled, dim3(cdiv(N, 16), cdiv(M, 16)), dim3(256), 0, s, static_cast<const float*>(X),
-                       static_cast<const float*>(W), P, M, N, K);
+    hipExtLaunchKernelGGL(gemm_f32_tiled, dim3(cdiv(N, 16), cdiv(M, 16)), dim3(256), 0, s, ev_start, ev_stop, 0,
+                          static_cast<const float*>(X), static_cast<const float*>(W), P, M, N, K);
   }
   VC_LAUNCH_CHECK();
   return VC_OK;

@@ -23,13 +23,17 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 COPY_KERNEL = "direct_copy_kernel"
-# sources that define the draft-attention kernels and their launch
-KERNEL_SOURCES = ["csrc/attention.hip", "csrc/attention.h", "csrc/common.h"]
+# sources that define each profiled kernel and its launch
+KERNEL_SOURCES = {
+    "attn_decode_bf16": ["csrc/attention.hip", "csrc/attention.h", "csrc/common.h"],
+    "attn_quant": ["csrc/attention_quant.hip", "csrc/attention.h", "csrc/common.h"],
+    "attn_rows_bf16": ["csrc/attention_rows.hip", "csrc/attention.h", "csrc/common.h"],
+}
 
 
-def sources_sha256() -> str:
+def sources_sha256(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -74,7 +78,7 @@ def main():
         "hbm_read_bytes_per_dispatch": read,
         "hbm_write_bytes_per_dispatch": written,
         "traffic_bytes_per_dispatch": read + written,
-        "sources_sha256": sources_sha256(),
+        "sources_sha256": sources_sha256(a.kernel),
     }
     if a.algorithmic_bytes:
         rec["algorithmic_bytes_per_dispatch"] = a.algorithmic_bytes

@@ -271,3 +271,53 @@ def test_bf16_output_is_rounded_fp32_output():
     torch.cuda.synchronize()
     want = synth.bf16_bits_from_f32(o32.cpu().numpy())
     assert np.array_equal(o16.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+def test_profile_records_verify_and_draft_launches():
+    """Live kernel timing (vc_profile_*): one record per launch group of the enabled class only,
+    carrying the algorithmic bytes and flops the header defines for it."""
+    need_gpu()
+    import lossless_speculative_decoding_amd as vc
+    from lossless_speculative_decoding_amd._vc import AttnDesc
+    ctxs, rows, split = (1500, 2100), 33, 512
+    cap = max(ctxs)  # one staged capacity for all requests
+    Ks = [torch.randn(HKV, cap, D, device="cuda").to(torch.bfloat16) for _ in ctxs]
+    Vs = [torch.randn(HKV, cap, D, device="cuda").to(torch.bfloat16) for _ in ctxs]
+    tK = [torch.randn(HKV, rows, D, device="cuda").to(torch.bfloat16) for _ in ctxs]
+    tV = [torch.randn(HKV, rows, D, device="cuda").to(torch.bfloat16) for _ in ctxs]
+    q = torch.randn(len(ctxs), rows, HQ, D, device="cuda").to(torch.bfloat16)
+    d = AttnDesc(HQ, HKV, D, vc.VC_BF16, 0, vc.VC_BF16)
+    for k in range(5):
+        vc.profile_read(k)
+    vc.profile_enable((vc.VC_PROF_VERIFY_ATTN,))
+    vc.vc_attn_verify(d, q, Ks, Vs, list(ctxs), tK, tV, rows, split_len=split)
+    # a draft step while only verification is enabled: not recorded
+    T, bits, group = 1000, 4, 128
+    cd = vc.compress_desc(vc.VC_QUANT, 1, HQ, HKV, D, T, vc.VC_BF16, bits=bits, group=group)
+    kq = torch.randn(1, HKV, T, D, device="cuda").to(torch.bfloat16)
+    blob = vc.vc_compress(cd, kq, kq)
+    qd = torch.randn(1, HQ, D, device="cuda").to(torch.bfloat16)
+    vc.vc_attn_draft(d, [blob], [cd], [tK[0]], [tV[0]], [3], qd)
+    vc.profile_enable((vc.VC_PROF_DRAFT_ATTN,))
+    vc.vc_attn_draft(d, [blob], [cd], [tK[0]], [tV[0]], [3], qd)
+    vc.profile_enable(())
+    torch.cuda.synchronize()
+    st = vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
+    want_b = want_f = 0.0
+    for c in ctxs:
+        S = -(-(c + rows) // split)
+        want_b += HKV * (c + rows) * D * 2 * 2 + rows * HQ * D * 2 + rows * HQ * S * (D + 2) * 4
+        want_f += 4 * D * HQ * (rows * c + rows * (rows + 1) / 2)
+    assert st["launches"] == 1 and st["ms"] > 0
+    assert st["bytes"] == want_b and st["flops"] == want_f
+    sd = vc.profile_read(vc.VC_PROF_DRAFT_ATTN)
+    Tq = T // group * group
+    n_resid, n_tail = T - Tq, 3
+    s_quant, s_exact = -(-Tq // 1024), -(-(64 * -(-n_resid // 64) + n_tail) // 512)
+    want = (HKV * (2 * Tq * D * bits / 8 + 2 * (Tq // group) * D * 2 + 2 * Tq * (D // group) * 2)
+            + HKV * (n_resid + n_tail) * D * 2 * 2 + HQ * D * 2 + HQ * (s_quant + s_exact) * (D + 2) * 4)
+    assert sd["launches"] == 1 and sd["ms"] > 0
+    assert sd["bytes"] == want, (sd["bytes"], want)
+    assert sd["flops"] == 4 * D * HQ * (T + n_tail)
+    for k in (vc.VC_PROF_GEMM_SKINNY, vc.VC_PROF_GEMM_TILED, vc.VC_PROF_PREFILL_ATTN):
+        assert vc.profile_read(k)["launches"] == 0

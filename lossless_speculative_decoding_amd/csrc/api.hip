@@ -105,7 +105,6 @@ namespace {
 
 constexpr int SPLIT_VERIFY = 1024;
 constexpr int SPLIT_DRAFT = 512;
-constexpr int SPLIT_QUANT = 1024;
 
 inline const uint8_t* cptr(const void* p, int64_t off) { return static_cast<const uint8_t*>(p) + off; }
 inline uint8_t* mptr(void* p, int64_t off) { return static_cast<uint8_t*>(p) + off; }
@@ -132,7 +131,9 @@ size_t gemm_part_bytes(const vc_model_desc& d, int R) {
 
 size_t att_part_bytes(const vc_model_desc& d, int R, int max_keys) {
   const int64_t D2 = d.head_dim + 2;
-  const int64_t draft = int64_t(VC_MAX_BATCH) * d.n_q_heads * (cdiv(max_keys, SPLIT_DRAFT) + cdiv(max_keys, SPLIT_QUANT) + 2) * D2 * 4;
+  // quantized splits are shortest for group 64
+  const int sq = quant_split_len(d.n_q_heads / d.n_kv_heads, 64);
+  const int64_t draft = int64_t(VC_MAX_BATCH) * d.n_q_heads * (cdiv(max_keys, SPLIT_DRAFT) + cdiv(max_keys, sq) + 2) * D2 * 4;
   const int64_t verify = int64_t(R) * d.n_q_heads * (cdiv(max_keys, SPLIT_VERIFY) + 1) * D2 * 4;
   return size_t(std::max(draft, verify));
 }
@@ -329,7 +330,7 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
   for (int r = 0; r < n; r++) {
     const CompView& v = views[r];
     const int a_n = v.kind == VC_QUANT ? v.n_resid : v.kk;
-    qs_n[r] = v.kind == VC_QUANT ? int(cdiv(v.tq, SPLIT_QUANT)) : 0;
+    qs_n[r] = v.kind == VC_QUANT ? int(cdiv(v.tq, quant_split_len(G, v.group))) : 0;
     ts_n[r] = int(cdiv(decode ? decode_keys(a_n, tail_n[r]) : a_n + tail_n[r], SPLIT_DRAFT));
     s_tot = std::max(s_tot, qs_n[r] + ts_n[r]);
   }
@@ -407,7 +408,7 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     qa.G = G;
     qa.bits = q_bits;
     qa.group = q_group;
-    qa.split_len = SPLIT_QUANT;
+    qa.split_len = quant_split_len(G, q_group);
     qa.scale_log2 = sl2;
     VC_REQUIRE(D == 128 && dtype == VC_BF16, VC_ERR_UNSUPPORTED, "quantized draft needs bf16, head_dim 128");
     if ((st = launch_attn_quant(qa, s, rec.a, nullptr))) return st;
@@ -943,7 +944,9 @@ vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const vo
 vc_status vc_attn_ws_size(const vc_attn_desc* d, int32_t n, int32_t rows, int32_t max_keys, size_t* bytes) {
   VC_REQUIRE(d && bytes && n > 0 && rows > 0 && max_keys > 0, VC_ERR_ARG, "vc_attn_ws_size: bad arguments");
   const int64_t D2 = d->head_dim + 2;
-  const int64_t S = cdiv(max_keys, SPLIT_DRAFT) + cdiv(max_keys, SPLIT_QUANT) + 2;
+  VC_REQUIRE(d->n_kv_heads > 0 && d->n_q_heads % d->n_kv_heads == 0, VC_ERR_ARG, "vc_attn_ws_size: bad heads");
+  const int sq = quant_split_len(d->n_q_heads / d->n_kv_heads, 64);  // quantized splits: shortest at group 64
+  const int64_t S = cdiv(max_keys, SPLIT_DRAFT) + cdiv(max_keys, sq) + 2;
   *bytes = align256(size_t(n) * rows * d->n_q_heads * S * D2 * 4);
   return VC_OK;
 }

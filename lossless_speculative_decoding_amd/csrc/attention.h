@@ -115,6 +115,18 @@ struct QuantArgs {
   float scale_log2;
 };
 
+// Keys per split of the quantized decode (split_len of QuantArgs, head_dim 128): at most 16
+// token groups (2048 keys at group 128, 1024 at group 64), a multiple of 256, and few enough
+// groups that the split's scaled query fragments (512 bytes per group per query head) fit in
+// QUANT_QP_BYTES of LDS.
+constexpr int QUANT_QP_BYTES = 32768;
+constexpr int QUANT_MAX_GROUPS = 16;
+inline int quant_split_len(int G, int group) {
+  int groups = QUANT_QP_BYTES / (512 * G);  // >= 4 for G <= 16
+  if (groups > QUANT_MAX_GROUPS) groups = QUANT_MAX_GROUPS;
+  return groups * group / 256 * 256;
+}
+
 // ev_start / ev_stop (may be null) in the launchers below: HIP events that take the
 // kernel's own start and end time (hipExtLaunchKernelGGL), for live kernel timing without
 // marker-packet gaps; when nothing is launched they are recorded on the stream instead.

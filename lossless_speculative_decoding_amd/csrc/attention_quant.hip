@@ -32,7 +32,7 @@ namespace vc {
 namespace {
 
 constexpr int D = 128;
-constexpr float P_SCALE = 1024.f;
+constexpr float P_LOG2 = 10.f;  // P' carries p * 2^10 (out of the fp16 subnormal range)
 constexpr float P_UNSCALE = 1.f / 1024.f;
 
 // 0x6400 | c is the fp16 number 1024 + c; subtracting 1024 + 2^(b-1) leaves the centred code exactly
@@ -207,25 +207,37 @@ constexpr int QWAVES = 4;
 constexpr int QRED = D + 4;  // floats per head in the merge buffer
 
 // NH: V channel groups per token (1 for group 128, 2 for group 64), a template parameter so
-// that every register index below is a compile-time constant
-constexpr int QSPLIT_MAX = 1024;  // keys per split (the LDS copies of the split's scales are sized for it)
+// that every register index below is a compile-time constant.  A split holds at most
+// QUANT_MAX_GROUPS token groups: 2048 / NH keys (the LDS tables of the split are sized for it).
+template <int NH>
+constexpr int qsplit_max() { return QUANT_MAX_GROUPS * D / NH; }
 
-// LDS: the split's K scales and zeros (per token group and channel), V scales and zeros (per
-// token and channel group) and the G query rows, loaded once by the whole workgroup so that no
-// scale load is left in the loop; after the loop the same bytes hold the waves' merge buffer
-constexpr int QL_KS = 0, QL_KZ = QL_KS + QSPLIT_MAX / 64 * D * 2, QL_VS = QL_KZ + QSPLIT_MAX / 64 * D * 2,
-              QL_VZ = QL_VS + QSPLIT_MAX * 2 * 2, QL_Q = QL_VZ + QSPLIT_MAX * 2 * 2, QL_END = QL_Q + 16 * D * 2;
-constexpr int QL_BYTES = QL_END > QWAVES * 16 * QRED * 4 ? QL_END : QWAVES * 16 * QRED * 4;
+// LDS tables of the split, built once by the whole workgroup before the key loop so that the
+// loop reads ready operands:
+//   QP  the scaled query Q' = q * s_K of every token group of the split and query head, as the
+//       fp16 hi / lo MFMA fragments lanes load directly: u32x4 index
+//       ((group * 4 + chunk) * 2 + hi_lo) * 4G + g * G + head (512 bytes per group and head);
+//   KB  the key bias sum_d q_d (2^(b-1) s_K + z_K) per token group and head (KBP: its four
+//       32-channel partial sums, merged in a fixed order);
+//   VF  per key and V channel group: (s_V, 2^(b-1) s_V + z_V) in float32.
+// After the loop the same bytes hold the waves' merge buffer.
+template <int NH>
+struct QLds {
+  static constexpr int QP = 0, KB = QP + QUANT_QP_BYTES, KBP = KB + QUANT_QP_BYTES / 512 * 4,
+                       VF = KBP + QUANT_QP_BYTES / 512 * 4 * 4, END = VF + qsplit_max<NH>() * NH * 8;
+  static constexpr int RED = QWAVES * 16 * QRED * 4;
+  static constexpr int BYTES = END > RED ? END : RED;
+};
 
 template <int BITS, int NH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3 : 2, NH == 1 ? 3 : 2))) void attn_quant_kernel(
     const QuantArgs args) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[QL_BYTES];
-  uint16_t* const s_ks = reinterpret_cast<uint16_t*>(lds + QL_KS);
-  uint16_t* const s_kz = reinterpret_cast<uint16_t*>(lds + QL_KZ);
-  uint16_t* const s_vs = reinterpret_cast<uint16_t*>(lds + QL_VS);
-  uint16_t* const s_vz = reinterpret_cast<uint16_t*>(lds + QL_VZ);
-  uint16_t* const s_q = reinterpret_cast<uint16_t*>(lds + QL_Q);
+  using L = QLds<NH>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::BYTES];
+  u32x4* const s_qp = reinterpret_cast<u32x4*>(lds + L::QP);
+  float* const s_kb = reinterpret_cast<float*>(lds + L::KB);
+  float* const s_kbp = reinterpret_cast<float*>(lds + L::KBP);
+  float* const s_vf = reinterpret_cast<float*>(lds + L::VF);
   float* const red = reinterpret_cast<float*>(lds);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int z = blockIdx.z;
@@ -245,7 +257,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
   const int key_hi = min(key_lo + args.split_len, Tq);
   const int r16 = lane & 15, g = lane >> 4;
   const bool head_ok = r16 < G;
-  const int hq = j * G + (head_ok ? r16 : 0);
+  // lanes past the group's heads compute a copy of the last head (finite, never written)
+  const int hc = min(r16, G - 1);
 
   const uint8_t* kc = R.m.kc + int64_t(j) * Tq * (D * BITS / 8);
   const uint8_t* vc = R.m.vc + int64_t(j) * nblk * D * (8 * BITS);
@@ -253,36 +266,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
   const uint16_t* kz = R.m.kz + int64_t(j) * ng * D;
   const uint16_t* vs = R.m.vs + int64_t(j) * Tq * nh;
   const uint16_t* vz = R.m.vz + int64_t(j) * Tq * nh;
-
-  {
-    const int g_lo = key_lo / grp_sz, n_grp = (key_hi - key_lo) / grp_sz;
-    const u32x4* a = reinterpret_cast<const u32x4*>(ks + int64_t(g_lo) * D);
-    const u32x4* b = reinterpret_cast<const u32x4*>(kz + int64_t(g_lo) * D);
-    for (int i = tid; i < n_grp * (D / 8); i += 256) {
-      reinterpret_cast<u32x4*>(s_ks)[i] = a[i];
-      reinterpret_cast<u32x4*>(s_kz)[i] = b[i];
-    }
-    const u32x4* c = reinterpret_cast<const u32x4*>(vs + int64_t(key_lo) * nh);
-    const u32x4* d = reinterpret_cast<const u32x4*>(vz + int64_t(key_lo) * nh);
-    for (int i = tid; i < (key_hi - key_lo) * nh / 8; i += 256) {
-      reinterpret_cast<u32x4*>(s_vs)[i] = c[i];
-      reinterpret_cast<u32x4*>(s_vz)[i] = d[i];
-    }
-    const u32x4* e = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(R.q) + int64_t(j) * G * D);
-    for (int i = tid; i < G * (D / 8); i += 256) reinterpret_cast<u32x4*>(s_q)[i] = e[i];
-  }
-  __syncthreads();
   constexpr float C0 = float(1 << (BITS - 1));
-  u32x4 qf[4], qlo[4];
-  float kbias = 0.f;
-  int cur_group = -1;
-  f32x4 oacc[8];
-#pragma unroll
-  for (int dt = 0; dt < 8; dt++) oacc[dt] = f32x4{0, 0, 0, 0};
-  float vb0 = 0.f, vb1 = 0.f;
-  float m_run = NEG_INF, l_run = 0.f;
-  const float sl2 = args.scale_log2;
+  const int g_lo = key_lo / grp_sz, n_grp = (key_hi - key_lo) / grp_sz;
 
+  // the first tile's codes are in flight while the tables are built
   Codes32<BITS> kr[4];
   VCodes16<BITS> vr[8];
   int t0 = key_lo + ATT_KT * wave;
@@ -290,60 +277,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
     ld_ktile<BITS>(kr, kc, t0, r16, g);
     ld_vtile<BITS>(vr, vc, t0, r16, g);
   }
-  for (; t0 < key_hi; t0 += QWAVES * ATT_KT) {
-    // ---- V scales and zeros of this lane's 16 keys [t0 + 16g, t0 + 16g + 16)
-    uint32_t vsw[16], vzw[16];
-    {
-      const u32x4* sp = reinterpret_cast<const u32x4*>(s_vs + (t0 - key_lo + 16 * g) * nh);
-      const u32x4* zp = reinterpret_cast<const u32x4*>(s_vz + (t0 - key_lo + 16 * g) * nh);
+
+  // ---- split tables.  Item (group, head, quarter): channels [32 quarter, +32) of Q' in the
+  // lane order of the MFMA fragments (position p -> channel 32 quarter + perm_pos(p)) and the
+  // quarter's key-bias partial, accumulated in that same order.
+  for (int it = tid; it < n_grp * G * 4; it += 256) {
+    const int gi = it / (4 * G), h = (it / 4) % G, qq = it % 4;
+    const u32x4* qv = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(R.q) + int64_t(j * G + h) * D + 32 * qq);
+    const u32x4* sp = reinterpret_cast<const u32x4*>(ks + int64_t(g_lo + gi) * D + 32 * qq);
+    const u32x4* zp = reinterpret_cast<const u32x4*>(kz + int64_t(g_lo + gi) * D + 32 * qq);
+    uint32_t sw[16], zw[16], qw[16];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const u32x4 a = (i < 2 * nh) ? sp[i] : u32x4{0, 0, 0, 0};
-        const u32x4 b = (i < 2 * nh) ? zp[i] : u32x4{0, 0, 0, 0};
-        vsw[4 * i] = a.x; vsw[4 * i + 1] = a.y; vsw[4 * i + 2] = a.z; vsw[4 * i + 3] = a.w;
-        vzw[4 * i] = b.x; vzw[4 * i + 1] = b.y; vzw[4 * i + 2] = b.z; vzw[4 * i + 3] = b.w;
-      }
+    for (int i = 0; i < 4; i++) {
+      const u32x4 a = sp[i], b = zp[i], c = qv[i];
+      sw[4 * i] = a.x; sw[4 * i + 1] = a.y; sw[4 * i + 2] = a.z; sw[4 * i + 3] = a.w;
+      zw[4 * i] = b.x; zw[4 * i + 1] = b.y; zw[4 * i + 2] = b.z; zw[4 * i + 3] = b.w;
+      qw[4 * i] = c.x; qw[4 * i + 1] = c.y; qw[4 * i + 2] = c.z; qw[4 * i + 3] = c.w;
     }
-    // ---- Q' = q * s_g (fp16 hi/lo) and the key bias when the token group changes
-    const int tg = t0 / grp_sz;
-    if (tg != cur_group) {
-      cur_group = tg;
-      uint32_t sw[16], zw[16], qw[16];
-      const int gi = tg - key_lo / grp_sz;
-      const u32x4* sp = reinterpret_cast<const u32x4*>(s_ks + gi * D + 32 * g);
-      const u32x4* zp = reinterpret_cast<const u32x4*>(s_kz + gi * D + 32 * g);
-      const u32x4* qv = reinterpret_cast<const u32x4*>(s_q + r16 * D + 32 * g);
+    float b = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const u32x4 a = sp[i], b = zp[i], c = head_ok ? qv[i] : u32x4{0, 0, 0, 0};
-        sw[4 * i] = a.x; sw[4 * i + 1] = a.y; sw[4 * i + 2] = a.z; sw[4 * i + 3] = a.w;
-        zw[4 * i] = b.x; zw[4 * i + 1] = b.y; zw[4 * i + 2] = b.z; zw[4 * i + 3] = b.w;
-        qw[4 * i] = c.x; qw[4 * i + 1] = c.y; qw[4 * i + 2] = c.z; qw[4 * i + 3] = c.w;
-      }
-      float b = 0.f;
+    for (int c = 0; c < 4; c++) {
+      uint32_t w[4], wl[4];
 #pragma unroll
-      for (int c = 0; c < 4; c++) {
-        uint32_t w[4], wl[4];
+      for (int e2 = 0; e2 < 4; e2++) {
+        float pr[2];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; e2++) {
-          float pr[2];
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-            const int ch = perm_pos<BITS>(8 * c + 2 * e2 + h);  // channel 32g + ch
-            const float qd = (ch & 1) ? hi_bf(qw[ch >> 1]) : lo_bf(qw[ch >> 1]);
-            const float sd = h2f(uint16_t(half16(sw, ch))), zd = h2f(uint16_t(half16(zw, ch)));
-            b = fmaf(qd, fmaf(sd, C0, zd), b);
-            pr[h] = qd * sd;
-          }
-          split_h2(pr[0], pr[1], w[e2], wl[e2]);
+        for (int h2 = 0; h2 < 2; h2++) {
+          const int ch = perm_pos<BITS>(8 * c + 2 * e2 + h2);  // channel 32 qq + ch
+          const float qd = (ch & 1) ? hi_bf(qw[ch >> 1]) : lo_bf(qw[ch >> 1]);
+          const float sd = h2f(uint16_t(half16(sw, ch))), zd = h2f(uint16_t(half16(zw, ch)));
+          b = fmaf(qd, fmaf(sd, C0, zd), b);
+          pr[h2] = qd * sd;
         }
-        qf[c] = u32x4{w[0], w[1], w[2], w[3]};
-        qlo[c] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+        split_h2(pr[0], pr[1], w[e2], wl[e2]);
       }
-      b += shfl_xor(b, 16);
-      b += shfl_xor(b, 32);
-      kbias = b;
+      s_qp[((gi * 4 + c) * 2 + 0) * 4 * G + qq * G + h] = u32x4{w[0], w[1], w[2], w[3]};
+      s_qp[((gi * 4 + c) * 2 + 1) * 4 * G + qq * G + h] = u32x4{wl[0], wl[1], wl[2], wl[3]};
     }
+    s_kbp[it] = b;
+  }
+  for (int i = tid; i < (key_hi - key_lo) * nh; i += 256) {
+    const float sv = h2f(vs[int64_t(key_lo) * nh + i]), zv = h2f(vz[int64_t(key_lo) * nh + i]);
+    s_vf[2 * i] = sv;
+    s_vf[2 * i + 1] = fmaf(sv, C0, zv);
+  }
+  __syncthreads();
+  // the four quarter sums of a (group, head) in the order ((0 + 1) + (2 + 3))
+  for (int it = tid; it < n_grp * G; it += 256) {
+    const float* p4 = s_kbp + 4 * it;
+    s_kb[it] = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+  }
+  __syncthreads();
+
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) oacc[dt] = f32x4{0, 0, 0, 0};
+  float vb0 = 0.f, vb1 = 0.f;
+  float m_run = NEG_INF, l_run = 0.f;
+  const float sl2 = args.scale_log2;
+
+  for (; t0 < key_hi; t0 += QWAVES * ATT_KT) {
+    // V scale and centred-code zero of this lane's keys [t0 + 16g, t0 + 16g + 16): (s, z') of
+    // key k, channel group v at vf[k * NH + v]
+    const float2* const vf = reinterpret_cast<const float2*>(s_vf) + (t0 - key_lo + 16 * g) * nh;
+    // ---- Q' fragments and key bias of the tile's token group, read for every tile (holding
+    // them across tiles would keep 32 registers live through the loop)
+    const int gi = t0 / grp_sz - g_lo;
+    u32x4 qf[4], qlo[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      qf[c] = s_qp[((gi * 4 + c) * 2 + 0) * 4 * G + g * G + hc];
+      qlo[c] = s_qp[((gi * 4 + c) * 2 + 1) * 4 * G + g * G + hc];
+    }
+    const float kbias = s_kb[gi * G + hc];
 
     // ---- S^T = C_K Q'^T: lane (g, head r) gets keys 16g + 4kt + jj
     f32x4 sacc[4];
@@ -362,27 +368,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
     const int tn = t0 + QWAVES * ATT_KT;
     if (tn < key_hi) ld_ktile<BITS>(kr, kc, tn, r16, g);
 
-    // ---- online softmax per head (every key of a tile is visible)
+    // ---- online softmax per head (every key of a tile is visible).  p' = 2^10 p comes out of
+    // one fma per key: 2^((s + bias) scale_log2 - m + 10), m and the sums in the scaled domain.
     float mx = NEG_INF;
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const float v = (sacc[kt][jj] + kbias) * sl2;
-        sacc[kt][jj] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
+    for (int kt = 0; kt < 4; kt++)
+      mx = fmaxf(mx, fmaxf(fmaxf(sacc[kt][0], sacc[kt][1]), fmaxf(sacc[kt][2], sacc[kt][3])));
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, (mx + kbias) * sl2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float nb = P_LOG2 - m_new;
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kt][jj] - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][jj] + kbias, sl2, nb));
         sacc[kt][jj] = p;
         rs += p;
       }
@@ -412,15 +414,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int k = perm_pos<BITS>(8 * kc2 + 2 * e2 + h);  // key 16g + k
-          const float x = sacc[k >> 2][k & 3] * P_SCALE;
-          // fp16 scale and zero of key k, channel group v: element k*NH + v
+          const float x = sacc[k >> 2][k & 3];                 // 2^10 p
 #pragma unroll
           for (int v = 0; v < NH; v++) {
-            const float sv = h2f(uint16_t(half16(vsw, NH * k + v)));
-            const float zv = h2f(uint16_t(half16(vzw, NH * k + v)));
-            pr[v][h] = x * sv;
-            if (v == 0) vb0 = fmaf(x, fmaf(sv, C0, zv), vb0);  // zero of the centred code
-            else vb1 = fmaf(x, fmaf(sv, C0, zv), vb1);
+            const float2 f = vf[k * NH + v];
+            pr[v][h] = x * f.x;
+            if (v == 0) vb0 = fmaf(x, f.y, vb0);  // zero of the centred code
+            else vb1 = fmaf(x, f.y, vb1);
           }
         }
 #pragma unroll
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
     float* rh = rw + r16 * QRED;
     if (g == 0) {
       rh[0] = m_run;
-      rh[1] = l_run;
+      rh[1] = l_run * P_UNSCALE;
     }
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
@@ -495,9 +495,11 @@ vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_sta
   }
   VC_REQUIRE(a.group == 64 || a.group == 128, VC_ERR_UNSUPPORTED, "quant group must be 64 or 128");
   VC_REQUIRE(a.G <= 16, VC_ERR_UNSUPPORTED, "GQA group > 16");
-  VC_REQUIRE(a.split_len % (QWAVES * ATT_KT) == 0 && a.split_len % a.group == 0 && a.split_len <= QSPLIT_MAX,
-             VC_ERR_ARG, "quantized decode: split %d must be a multiple of 256 and of the group, at most %d",
-             a.split_len, QSPLIT_MAX);
+  VC_REQUIRE(a.split_len % (QWAVES * ATT_KT) == 0 && a.split_len % a.group == 0 &&
+                 a.split_len / a.group <= QUANT_MAX_GROUPS && (a.split_len / a.group) * a.G * 512 <= QUANT_QP_BYTES,
+             VC_ERR_ARG, "quantized decode: split %d must be a multiple of 256 and of the group, hold at most %d "
+             "token groups and at most %d token groups x query heads", a.split_len, QUANT_MAX_GROUPS,
+             QUANT_QP_BYTES / 512);
   for (int r = 0; r < a.n_req; r++)
     VC_REQUIRE(a.r[r].m.tq % 64 == 0 && a.r[r].m.tq % a.group == 0, VC_ERR_ARG, "quantized rows not whole groups");
   dim3 grid(a.Hkv, a.max_splits, a.n_req);

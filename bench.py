@@ -90,7 +90,7 @@ def cpu_baseline(shape, ctx: int, keep: int, seed: int = 0) -> dict:
                        f"{s.n_layers} layers; {per_token:.2f} s per token; weight generation {t_gen:.1f} s excluded")}
 
 
-def pmc_traffic_ratio(workload: str, kernel: str = "attn_decode_bf16"):
+def pmc_traffic_ratio(workload: str, kernel: str = "attn_decode_bf16", what: str = "draft_attention"):
     """Measured HBM bytes over algorithmic bytes of the draft-attention launches, from the
     committed counter profile of this workload (profiles/draft_attention_<workload>_pmc.json),
     if the kernel sources are unchanged since.  The
@@ -98,7 +98,7 @@ def pmc_traffic_ratio(workload: str, kernel: str = "attn_decode_bf16"):
     so the ratio (taken over the same launches on both sides) carries over to this run's
     launches rather than the profiled run's bytes per launch."""
     from lossless_speculative_decoding_amd.pmc_summary import sources_sha256
-    path = os.path.join(ROOT, "profiles", f"draft_attention_{workload}_pmc.json")
+    path = os.path.join(ROOT, "profiles", f"{what}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -208,6 +208,9 @@ def bench_layer(args):
     ratio = pmc_traffic_ratio(w.name, "attn_quant")
     dr["traffic"] = round(ratio * dr["bytes_per_launch"]) if ratio else None
     dr["traffic_over_algorithmic"] = ratio
+    ratio = pmc_traffic_ratio(f"{w.name[:w.name.rindex('_')]}_r{rows}", "attn_rows_bf16", "verify_attention")
+    vr["traffic"] = round(ratio * vr["bytes_per_launch"]) if ratio else None
+    vr["traffic_over_algorithmic"] = ratio
     cpu = None if args.no_cpu_baseline else cpu_baseline_layer(T, Hq, Hkv, D, rows, bits, group)
     line = {
         "metric": "draft-attn HBM GB/s vs peak (single GQA layer)",

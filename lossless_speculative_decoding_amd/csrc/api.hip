@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "attention.h"
+#include "attention_quant.h"
 #include "compress.h"
 #include "elementwise.h"
 #include "gemm.h"
@@ -323,22 +324,28 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
   const int G = Hq / Hkv;
   const float sl2 = LOG2E / sqrtf(float(D));
   // bf16 head_dim 128: the one-row decode kernel, which numbers the exact-row segment's keys
-  // from a 64-aligned start (so its split count uses decode_keys)
+  // from a 64-aligned start (so its split count uses decode_keys).  A quantized request's
+  // exact rows (residual + tail) are one more workgroup of the quantized kernel (one slot).
   const bool decode = dtype == VC_BF16 && D == 128 && G <= 16;
   int s_tot = 0;
   int qs_n[VC_MAX_BATCH], ts_n[VC_MAX_BATCH];
   for (int r = 0; r < n; r++) {
     const CompView& v = views[r];
-    const int a_n = v.kind == VC_QUANT ? v.n_resid : v.kk;
-    qs_n[r] = v.kind == VC_QUANT ? int(cdiv(v.tq, quant_split_len(G, v.group))) : 0;
-    ts_n[r] = int(cdiv(decode ? decode_keys(a_n, tail_n[r]) : a_n + tail_n[r], SPLIT_DRAFT));
+    if (v.kind == VC_QUANT) {
+      VC_REQUIRE(D == 128 && dtype == VC_BF16, VC_ERR_UNSUPPORTED, "quantized draft needs bf16, head_dim 128");
+      qs_n[r] = int(cdiv(v.tq, quant_split_len(G, v.group)));
+      ts_n[r] = 1;
+    } else {
+      qs_n[r] = 0;
+      ts_n[r] = int(cdiv(decode ? decode_keys(v.kk, tail_n[r]) : v.kk + tail_n[r], SPLIT_DRAFT));
+    }
     s_tot = std::max(s_tot, qs_n[r] + ts_n[r]);
   }
   const int64_t per_req = int64_t(Hq) * s_tot * (D + 2);
   QuantArgs qa{};
   qa.n_req = 0;
   AttnArgs aa{};
-  aa.n_req = n;
+  aa.n_req = 0;
   aa.Hq = Hq;
   aa.Hkv = Hkv;
   aa.G = G;
@@ -350,37 +357,36 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
   int q_bits = 0, q_group = 0;
   for (int r = 0; r < n; r++) {
     const CompView& v = views[r];
-    AttnReq& ar = aa.r[r];
-    ar.q = cptr(q, r * q_req_stride_bytes);
-    ar.part = part + r * per_req;
-    ar.n_rows = 1;
-    ar.s_total = s_tot;
+    const void* qr_ptr = cptr(q, r * q_req_stride_bytes);
+    KVSeg tail = tails[r];
+    tail.n = tail_n[r];
     if (v.kind == VC_QUANT) {
       VC_REQUIRE(q_bits == 0 || (q_bits == v.bits && q_group == v.group), VC_ERR_UNSUPPORTED,
                  "one draft batch must share the quantizer settings");
       q_bits = v.bits;
       q_group = v.group;
       QuantReq& qr = qa.r[qa.n_req++];
-      qr.q = ar.q;
+      qr.q = qr_ptr;
       qr.m = v.quant(l);
-      qr.part = ar.part;
+      qr.a = v.resid(l);
+      qr.b = tail;
+      qr.part = part + r * per_req;
       qr.s_total = s_tot;
       qr.n_splits = qs_n[r];
       qa.max_splits = std::max(qa.max_splits, qs_n[r]);
-      ar.a = v.resid(l);
-      ar.b = tails[r];
-      ar.b.n = tail_n[r];
-      ar.lim0 = v.n_resid + tail_n[r] - 1;
-      ar.s_off = qs_n[r];
     } else {
+      AttnReq& ar = aa.r[aa.n_req++];
+      ar.q = qr_ptr;
+      ar.part = part + r * per_req;
+      ar.n_rows = 1;
+      ar.s_total = s_tot;
       ar.a = v.main_bf16(l);
-      ar.b = tails[r];
-      ar.b.n = tail_n[r];
+      ar.b = tail;
       ar.lim0 = v.kk + tail_n[r] - 1;
       ar.s_off = 0;
+      ar.n_splits = ts_n[r];
+      aa.max_splits = std::max(aa.max_splits, ts_n[r]);
     }
-    ar.n_splits = ts_n[r];
-    aa.max_splits = std::max(aa.max_splits, ts_n[r]);
   }
   // algorithmic bytes of the partial launches (for vc_profile_read)
   double bytes = 0, flops_keys = 0;  // flops_keys: query heads x keys attended
@@ -402,6 +408,7 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
   // live timing: the first partial launch's own start and the last one's own end
   ProfRec rec = prof_begin(VC_PROF_DRAFT_ATTN, bytes, 4.0 * flops_keys * D);
   vc_status st;
+  const bool both = qa.n_req > 0 && aa.n_req > 0;
   if (qa.n_req > 0) {
     qa.Hq = Hq;
     qa.Hkv = Hkv;
@@ -410,14 +417,15 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     qa.group = q_group;
     qa.split_len = quant_split_len(G, q_group);
     qa.scale_log2 = sl2;
-    VC_REQUIRE(D == 128 && dtype == VC_BF16, VC_ERR_UNSUPPORTED, "quantized draft needs bf16, head_dim 128");
-    if ((st = launch_attn_quant(qa, s, rec.a, nullptr))) return st;
+    if ((st = launch_attn_quant(qa, s, rec.a, both ? nullptr : rec.b))) return st;
   }
-  hipEvent_t start = qa.n_req > 0 ? nullptr : rec.a;
-  if (decode) {
-    if ((st = launch_attn_decode(aa, s, start, rec.b))) return st;
-  } else {
-    if ((st = launch_attn(aa, dtype, s, start, rec.b))) return st;
+  if (aa.n_req > 0) {
+    hipEvent_t start = both ? nullptr : rec.a;
+    if (decode) {
+      if ((st = launch_attn_decode(aa, s, start, rec.b))) return st;
+    } else {
+      if ((st = launch_attn(aa, dtype, s, start, rec.b))) return st;
+    }
   }
   prof_commit(rec);
   CombineArgs c{};

@@ -4,18 +4,19 @@
 // query head, then attn_combine merges them in ascending split order:
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s o_s 2^(m_s - M) / L
 // (m is kept in log2 units: scores are pre-multiplied by log2(e) / sqrt(D)).
-// Keys are addressed by a logical index t over up to two segments (a then b);
-// splits and 64-key tiles are aligned to t = 0, and query row i (position
-// index within the call) sees keys t <= lim0 + i.  For verification the
-// logical index is the absolute position (a = staged full cache, b = verify
-// tail), which makes each row's arithmetic independent of the row count.
+// Keys are addressed by a logical index t over up to three segments (a, then b,
+// then c); splits and 64-key tiles are aligned to t = 0, and query row i (position
+// index within the call) sees keys t <= lim0 + i.  For verification the logical
+// index is the absolute position (a = the prompt positions, b = the committed
+// tail, c = the rows under verification), which makes each row's arithmetic
+// independent of the row count.
 #pragma once
 #include "common.h"
 
 namespace vc {
 
 constexpr int ATT_KT = 64;   // keys per tile
-constexpr int ATT_RB = 64;   // query rows (row x GQA head) per workgroup
+constexpr int ATT_RB = 64;   // query rows (row x GQA head) of one 16-row block in each of a workgroup's 4 waves
 
 struct KVSeg {
   const void* k;
@@ -89,44 +90,6 @@ __device__ __forceinline__ const E* key_row(const AttnReq& R, int j, int t, bool
   return base + j * R.c.hstride + int64_t(t) * D;
 }
 
-// Quantized main region of one request (one layer), plus the per-request
-// view of the draft query.
-struct QuantSeg {
-  const uint8_t* kc;   // [Hkv][Tq][D*b/8]
-  const uint8_t* vc;   // [Hkv][Tq/64][D][64*b/8]
-  const uint16_t* ks;  // [Hkv][Tq/G][D] fp16
-  const uint16_t* kz;
-  const uint16_t* vs;  // [Hkv][Tq][D/G] fp16
-  const uint16_t* vz;
-  int32_t tq;          // quantized rows
-  int32_t pad_;
-};
-
-struct QuantReq {
-  const void* q;       // [1][Hq][D] bf16
-  QuantSeg m;
-  float* part;         // [1][Hq][s_total][D + 2]
-  int32_t s_total, n_splits;
-};
-
-struct QuantArgs {
-  QuantReq r[VC_MAX_BATCH];
-  int32_t n_req, Hq, Hkv, G, bits, group, split_len, max_splits;
-  float scale_log2;
-};
-
-// Keys per split of the quantized decode (split_len of QuantArgs, head_dim 128): at most 16
-// token groups (2048 keys at group 128, 1024 at group 64), a multiple of 256, and few enough
-// groups that the split's scaled query fragments (512 bytes per group per query head) fit in
-// QUANT_QP_BYTES of LDS.
-constexpr int QUANT_QP_BYTES = 32768;
-constexpr int QUANT_MAX_GROUPS = 16;
-inline int quant_split_len(int G, int group) {
-  int groups = QUANT_QP_BYTES / (512 * G);  // >= 4 for G <= 16
-  if (groups > QUANT_MAX_GROUPS) groups = QUANT_MAX_GROUPS;
-  return groups * group / 256 * 256;
-}
-
 // ev_start / ev_stop (may be null) in the launchers below: HIP events that take the
 // kernel's own start and end time (hipExtLaunchKernelGGL), for live kernel timing without
 // marker-packet gaps; when nothing is launched they are recorded on the stream instead.
@@ -134,8 +97,6 @@ inline int quant_split_len(int G, int group) {
 // Many-row attention. dtype: VC_BF16 (head_dim 128, MFMA) or VC_F32 (head_dim 64, VALU)
 vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start = nullptr,
                       hipEvent_t ev_stop = nullptr);
-vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_start = nullptr,
-                            hipEvent_t ev_stop = nullptr);
 
 // One-row decode (bf16, head_dim 128, G <= 16): segment a occupies logical keys
 // [0, align64(a.n)), segment b follows; lim0 is ignored (every key is visible) and

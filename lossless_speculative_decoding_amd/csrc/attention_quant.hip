@@ -25,7 +25,9 @@
 // contiguous 2*BITS-byte piece of a per-channel code row).  Within a conversion group
 // of 8 (4-bit) or 16 (2-bit) codes the conversion yields the order [0,4,1,5,2,6,3,7]
 // (resp. [0,8,1,9,...,7,15]); Q' and P' are built in that same order.
-#include "attention.h"
+#include <type_traits>
+
+#include "attention_quant.h"
 
 namespace vc {
 
@@ -104,6 +106,33 @@ __device__ __forceinline__ void cvt_codes(const Codes32<BITS>& c, u32x4 out[4]) 
     }
 #pragma unroll
     for (int q = 0; q < 4; q++) out[q] = u32x4{r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]};
+  }
+}
+
+// Chunk ch (channels 8ch..8ch+7 of the lane's 32, in conversion order) of cvt_codes: the
+// same words and operations, so that a chunk's operand is built just before its MFMAs.
+template <int BITS, int CH>
+__device__ __forceinline__ u32x4 cvt_codes_chunk(const Codes32<BITS>& c) {
+  constexpr uint32_t MAG = 0x64006400u;
+  if constexpr (BITS == 4) {
+    const uint32_t x = c.w[CH];
+    return u32x4{centre<BITS>(and_or_mag(x, 0x000F000Fu)), centre<BITS>(and_or_mag(x >> 4, 0x000F000Fu)),
+                 centre<BITS>(and_or_mag(x >> 8, 0x000F000Fu)), centre<BITS>(and_or_mag(x >> 12, 0x000F000Fu))};
+  } else if constexpr (BITS == 2) {
+    const uint32_t x = c.w[CH >> 1] >> (8 * (CH & 1));
+    return u32x4{centre<BITS>(and_or_mag(x, 0x00030003u)), centre<BITS>(and_or_mag(x >> 2, 0x00030003u)),
+                 centre<BITS>(and_or_mag(x >> 4, 0x00030003u)), centre<BITS>(and_or_mag(x >> 6, 0x00030003u))};
+  } else {
+    const uint64_t lo = uint64_t(c.w[0]) | (uint64_t(c.w[1]) << 32);
+    const uint64_t hi = uint64_t(c.w[1]) | (uint64_t(c.w[2]) << 32);
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int off = 6 * (4 * CH + i);
+      const uint32_t f = off < 32 ? uint32_t(lo >> off) : uint32_t(hi >> (off - 32));
+      r[i] = centre<BITS>(((f & 7u) | ((f & 0x38u) << 13)) | MAG);
+    }
+    return u32x4{r[0], r[1], r[2], r[3]};
   }
 }
 
@@ -225,12 +254,152 @@ template <int NH>
 struct QLds {
   static constexpr int QP = 0, KB = QP + QUANT_QP_BYTES, KBP = KB + QUANT_QP_BYTES / 512 * 4,
                        VF = KBP + QUANT_QP_BYTES / 512 * 4 * 4, END = VF + qsplit_max<NH>() * NH * 8;
-  static constexpr int RED = QWAVES * 16 * QRED * 4;
+  static constexpr int RED = QWAVES * 16 * QRED * 4;  // also covers the exact rows' 4 * 16 * (D + 2) floats
+  static_assert(QWAVES * 16 * (D + 2) * 4 <= RED, "exact-row merge buffer");
+  static_assert((16 * D + 4 * 64 * 16) * 4 <= RED, "exact-row query rows and weights");
   static constexpr int BYTES = END > RED ? END : RED;
 };
 
+// ---------------------------------------------------------------- exact rows of a request
+// The residual and tail rows (bf16, at most a few hundred) of one KV head, for the G query
+// heads, on the VALU: wave w takes keys w*64 + lane, w*64 + 256 + lane, ...; the lane of a key
+// computes its G scores (query rows from LDS), the wave keeps an online softmax per head, and
+// lane l accumulates channels 2l and 2l + 1 of every head.  The four wave states are merged in
+// wave order into partial slot `slot`.  lds: at least 4 * G * (D + 2) * 4 bytes (the merge
+// buffer, which reuses the query rows' and weights' space).
+constexpr int XMAXG = 16;
+constexpr int XVB = 16;  // V words loaded together
+
+__device__ __forceinline__ const uint16_t* exact_row(const QuantReq& R, int j, int t, bool is_v) {
+  const KVSeg& sg = t < R.a.n ? R.a : R.b;
+  const int tt = t < R.a.n ? t : t - R.a.n;
+  return static_cast<const uint16_t*>(is_v ? sg.v : sg.k) + j * sg.hstride + int64_t(tt) * D;
+}
+
+__device__ void quant_exact_rows(const QuantReq& R, int j, int G, int Hq, float sl2, int slot, uint8_t* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = R.a.n + R.b.n;
+  float* qs = reinterpret_cast<float*>(lds);                  // [G][D] query rows, float32
+  float* ps = qs + G * D + wave * 64 * G;                       // [64 keys][G] this wave's weights
+  float* red = reinterpret_cast<float*>(lds);                   // [4 waves][G][D + 2], after the loop
+  for (int i = tid; i < G * D; i += 256)
+    qs[i] = bf2f(static_cast<const uint16_t*>(R.q)[int64_t(j * G) * D + i]);
+  __syncthreads();
+  float m_run[XMAXG], l_run[XMAXG], o0[XMAXG], o1[XMAXG];
+#pragma unroll
+  for (int h = 0; h < XMAXG; h++) {
+    m_run[h] = NEG_INF;
+    l_run[h] = 0.f;
+    o0[h] = 0.f;
+    o1[h] = 0.f;
+  }
+  for (int t0 = wave * 64; t0 < n; t0 += 256) {
+    const int t = t0 + lane;
+    const bool ok = t < n;
+    // ---- this lane's key: G scores (log2 units)
+    float sc[XMAXG];
+#pragma unroll
+    for (int h = 0; h < XMAXG; h++) sc[h] = 0.f;
+    const uint16_t* kr = exact_row(R, j, ok ? t : 0, false);
+#pragma unroll 4
+    for (int c = 0; c < D / 8; c++) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(kr + 8 * c);
+      const float k8[8] = {lo_bf(w.x), hi_bf(w.x), lo_bf(w.y), hi_bf(w.y), lo_bf(w.z), hi_bf(w.z), lo_bf(w.w), hi_bf(w.w)};
+#pragma unroll
+      for (int h = 0; h < XMAXG; h++) {
+        if (h < G) {
+#pragma unroll
+          for (int e = 0; e < 8; e++) sc[h] = fmaf(qs[h * D + 8 * c + e], k8[e], sc[h]);
+        }
+      }
+    }
+    // ---- online softmax per head over the wave's 64 keys
+#pragma unroll
+    for (int h = 0; h < XMAXG; h++) {
+      if (h >= G) continue;  // uniform; keeps the loop fully unrolled (register arrays)
+      const float v = ok ? sc[h] * sl2 : NEG_INF;
+      float mx = v;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+      const float m_new = fmaxf(m_run[h], mx);      // finite: lane 0's key of a processed chunk exists
+      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+      const float pk = __builtin_amdgcn_exp2f(v - m_new);
+      float rs = pk;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) rs += shfl_xor(rs, o);
+      l_run[h] = l_run[h] * alpha + rs;
+      m_run[h] = m_new;
+      o0[h] *= alpha;
+      o1[h] *= alpha;
+      ps[lane * G + h] = pk;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // ---- P.V: lane l accumulates channels 2l, 2l + 1 over the wave's keys, in key order; the
+    // V words of XVB keys are loaded together so that their latencies overlap
+    const int nk = min(64, n - t0);
+    for (int kb = 0; kb < nk; kb += XVB) {
+      uint32_t vv[XVB];
+#pragma unroll
+      for (int k = 0; k < XVB; k++) {
+        const int t = t0 + kb + min(k, nk - 1 - kb);  // in range; the excess keys are skipped below
+        vv[k] = *reinterpret_cast<const uint32_t*>(exact_row(R, j, t, true) + 2 * lane);
+      }
+#pragma unroll
+      for (int k = 0; k < XVB; k++) {
+        if (kb + k < nk) {
+          const float v0 = lo_bf(vv[k]), v1 = hi_bf(vv[k]);
+#pragma unroll
+          for (int h = 0; h < XMAXG; h++) {
+            if (h < G) {
+              const float p = ps[(kb + k) * G + h];
+              o0[h] = fmaf(p, v0, o0[h]);
+              o1[h] = fmaf(p, v1, o1[h]);
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+  // ---- merge the four wave states in wave order
+  __syncthreads();  // every wave is done with the query rows and weights the merge buffer reuses
+  float* rw = red + wave * G * (D + 2);
+#pragma unroll
+  for (int h = 0; h < XMAXG; h++) {
+    if (h >= G) continue;
+    if (lane == 0) {
+      rw[h * (D + 2)] = m_run[h];
+      rw[h * (D + 2) + 1] = l_run[h];
+    }
+    rw[h * (D + 2) + 2 + 2 * lane] = o0[h];
+    rw[h * (D + 2) + 2 + 2 * lane + 1] = o1[h];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * (D + 2); idx += 256) {
+    const int h = idx / (D + 2), e = idx - h * (D + 2);
+    float mw[4];
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      mw[w] = red[(w * G + h) * (D + 2)];
+      M = fmaxf(M, mw[w]);
+    }
+    float acc = 0.f;
+    if (e == 0) {
+      acc = M;
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const float wt = mw[w] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+        acc = fmaf(red[(w * G + h) * (D + 2) + e], wt, acc);
+      }
+    }
+    R.part[(int64_t(j * G + h) * R.s_total + slot) * (D + 2) + e] = acc;
+  }
+}
+
 template <int BITS, int NH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3 : 2, NH == 1 ? 3 : 2))) void attn_quant_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 || BITS == 2) ? 3 : 2, (NH == 1 || BITS == 2) ? 3 : 2))) void attn_quant_kernel(
     const QuantArgs args) {
   using L = QLds<NH>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::BYTES];
@@ -245,7 +414,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
   const QuantReq& R = args.r[z];
   const int G = args.G, Hq = args.Hq;
   const int j = blockIdx.x;
-  const int s = blockIdx.y;
+  if (blockIdx.y == 0) {  // the request's exact rows, first in the grid so that they finish early
+    quant_exact_rows(R, j, G, Hq, args.scale_log2, R.n_splits, lds);
+    return;
+  }
+  const int s = blockIdx.y - 1;
   if (s >= R.n_splits) return;  // uniform across the workgroup
   const int Tq = R.m.tq;
   const int grp_sz = args.group;
@@ -340,30 +513,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
     // V scale and centred-code zero of this lane's keys [t0 + 16g, t0 + 16g + 16): (s, z') of
     // key k, channel group v at vf[k * NH + v]
     const float2* const vf = reinterpret_cast<const float2*>(s_vf) + (t0 - key_lo + 16 * g) * nh;
-    // ---- Q' fragments and key bias of the tile's token group, read for every tile (holding
-    // them across tiles would keep 32 registers live through the loop)
+    // ---- key bias of the tile's token group; its Q' fragments are read per 32-channel chunk
+    // (holding them across tiles, or all four chunks at once, would keep registers live)
     const int gi = t0 / grp_sz - g_lo;
-    u32x4 qf[4], qlo[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      qf[c] = s_qp[((gi * 4 + c) * 2 + 0) * 4 * G + g * G + hc];
-      qlo[c] = s_qp[((gi * 4 + c) * 2 + 1) * 4 * G + g * G + hc];
-    }
     const float kbias = s_kb[gi * G + hc];
+    const u32x4* const qp = s_qp + (gi * 4 * 2) * 4 * G + g * G + hc;
 
-    // ---- S^T = C_K Q'^T: lane (g, head r) gets keys 16g + 4kt + jj
+    // ---- S^T = C_K Q'^T: lane (g, head r) gets keys 16g + 4kt + jj; chunk-outer, so the four
+    // 16-key blocks are independent MFMA chains
     f32x4 sacc[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
-      u32x4 ka[4];
-      cvt_codes<BITS>(kr[kt], ka);
-      sacc[kt] = f32x4{0, 0, 0, 0};
+    for (int kt = 0; kt < 4; kt++) sacc[kt] = f32x4{0, 0, 0, 0};
+    auto s_chunk = [&](auto chv) {
+      constexpr int c = decltype(chv)::value;
+      const u32x4 qh = qp[(c * 2 + 0) * 4 * G], ql = qp[(c * 2 + 1) * 4 * G];
 #pragma unroll
-      for (int c = 0; c < 4; c++) {
-        sacc[kt] = mfma_f16(ka[c], qf[c], sacc[kt]);
-        sacc[kt] = mfma_f16(ka[c], qlo[c], sacc[kt]);
+      for (int kt = 0; kt < 4; kt++) {
+        const u32x4 ka = cvt_codes_chunk<BITS, c>(kr[kt]);
+        sacc[kt] = mfma_f16(ka, qh, sacc[kt]);
+        sacc[kt] = mfma_f16(ka, ql, sacc[kt]);
       }
-    }
+    };
+    s_chunk(std::integral_constant<int, 0>{});
+    s_chunk(std::integral_constant<int, 1>{});
+    s_chunk(std::integral_constant<int, 2>{});
+    s_chunk(std::integral_constant<int, 3>{});
     // the next tile's K codes are in flight during the softmax and P.V of this one
     const int tn = t0 + QWAVES * ATT_KT;
     if (tn < key_hi) ld_ktile<BITS>(kr, kc, tn, r16, g);
@@ -489,12 +663,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
 }  // namespace
 
 vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  if (a.n_req <= 0 || a.max_splits <= 0) {
+  if (a.n_req <= 0) {
     VC_EVENTS_IF_EMPTY(ev_start, ev_stop, s);
     return VC_OK;
   }
   VC_REQUIRE(a.group == 64 || a.group == 128, VC_ERR_UNSUPPORTED, "quant group must be 64 or 128");
-  VC_REQUIRE(a.G <= 16, VC_ERR_UNSUPPORTED, "GQA group > 16");
+  VC_REQUIRE(a.G <= XMAXG, VC_ERR_UNSUPPORTED, "GQA group > %d", XMAXG);
   VC_REQUIRE(a.split_len % (QWAVES * ATT_KT) == 0 && a.split_len % a.group == 0 &&
                  a.split_len / a.group <= QUANT_MAX_GROUPS && (a.split_len / a.group) * a.G * 512 <= QUANT_QP_BYTES,
              VC_ERR_ARG, "quantized decode: split %d must be a multiple of 256 and of the group, hold at most %d "
@@ -502,7 +676,7 @@ vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_sta
              QUANT_QP_BYTES / 512);
   for (int r = 0; r < a.n_req; r++)
     VC_REQUIRE(a.r[r].m.tq % 64 == 0 && a.r[r].m.tq % a.group == 0, VC_ERR_ARG, "quantized rows not whole groups");
-  dim3 grid(a.Hkv, a.max_splits, a.n_req);
+  dim3 grid(a.Hkv, a.max_splits + 1, a.n_req);
   const bool g64 = a.group == 64;
   switch (a.bits) {
     case 2:

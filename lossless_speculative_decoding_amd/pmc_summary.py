@@ -26,7 +26,7 @@ COPY_KERNEL = "direct_copy_kernel"
 # sources that define each profiled kernel and its launch
 KERNEL_SOURCES = {
     "attn_decode_bf16": ["csrc/attention.hip", "csrc/attention.h", "csrc/common.h"],
-    "attn_quant": ["csrc/attention_quant.hip", "csrc/attention.h", "csrc/common.h"],
+    "attn_quant": ["csrc/attention_quant.hip", "csrc/attention_quant.h", "csrc/attention.h", "csrc/common.h"],
     "attn_rows_bf16": ["csrc/attention_rows.hip", "csrc/attention.h", "csrc/common.h"],
 }
 

@@ -313,7 +313,8 @@ def test_profile_records_verify_and_draft_launches():
     sd = vc.profile_read(vc.VC_PROF_DRAFT_ATTN)
     Tq = T // group * group
     n_resid, n_tail = T - Tq, 3
-    s_quant, s_exact = -(-Tq // 1024), -(-(64 * -(-n_resid // 64) + n_tail) // 512)
+    # quantized splits of 16 groups (2048 keys at group 128, G = 4); the exact rows are one slot
+    s_quant, s_exact = -(-Tq // 2048), 1
     want = (HKV * (2 * Tq * D * bits / 8 + 2 * (Tq // group) * D * 2 + 2 * Tq * (D // group) * 2)
             + HKV * (n_resid + n_tail) * D * 2 * 2 + HQ * D * 2 + HQ * (s_quant + s_exact) * (D + 2) * 4)
     assert sd["launches"] == 1 and sd["ms"] > 0

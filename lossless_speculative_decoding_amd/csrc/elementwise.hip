@@ -22,25 +22,71 @@ __global__ void embed_kernel(const void* E, const int32_t* tok, void* h, int d, 
   else static_cast<float*>(h)[int64_t(r) * d + c] = static_cast<const float*>(E)[t * d + c];
 }
 
-// y = x / sqrt(mean(x^2) + eps) * g, one workgroup of 256 threads per row; the
-// sum of squares is reduced in a fixed tree so every row is computed identically.
+// y = x / sqrt(mean(x^2) + eps) * g, one workgroup of 256 threads per row.  bf16 rows with
+// d a multiple of 2048 (up to 8192): every thread holds its 16-byte chunks c = tid + 256 i in
+// registers, so the row is read once; the sum of squares is reduced in a fixed order (each
+// thread's chunks in order, then a butterfly within each wave, then the four waves in order),
+// identically for every row.  Other rows: the same reduction over single elements.
+constexpr int RMS_MAXC = 4;  // 16-byte chunks per thread (d <= 8192)
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void* g, void* y, int d, float eps, int dt) {
-  __shared__ float red[256];
-  const int r = blockIdx.x, tid = threadIdx.x;
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t base = int64_t(r) * d;
+  const bool vec = dt == VC_BF16 && d % 2048 == 0 && d <= 2048 * RMS_MAXC;  // uniform
   float ss = 0.f;
-  for (int c = tid; c < d; c += 256) {
-    const float v = ld(x, base + c, dt);
-    ss = fmaf(v, v, ss);
+  u32x4 xv[RMS_MAXC];
+  if (vec) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + base);
+#pragma unroll
+    for (int i = 0; i < RMS_MAXC; i++)
+      if (i < d / 2048) xv[i] = xr[tid + 256 * i];
+#pragma unroll
+    for (int i = 0; i < RMS_MAXC; i++) {
+      if (i < d / 2048) {
+        const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float a = lo_bf(w[e]), b = hi_bf(w[e]);
+          ss = fmaf(a, a, ss);
+          ss = fmaf(b, b, ss);
+        }
+      }
+    }
+  } else {
+    for (int c = tid; c < d; c += 256) {
+      const float v = ld(x, base + c, dt);
+      ss = fmaf(v, v, ss);
+    }
   }
-  red[tid] = ss;
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.f / sqrtf(tot / float(d) + eps);
+  if (vec) {
+    const u32x4* gr = reinterpret_cast<const u32x4*>(g);
+    u32x4* yr = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base);
+#pragma unroll
+    for (int i = 0; i < RMS_MAXC; i++) {
+      if (i < d / 2048) {
+        const u32x4 gv = gr[tid + 256 * i];
+        const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = pack_bf2(lo_bf(w[e]) * inv * lo_bf(gw[e]), hi_bf(w[e]) * inv * hi_bf(gw[e]));
+        yr[tid + 256 * i] = u32x4{o[0], o[1], o[2], o[3]};
+      }
+    }
+  } else {
+    for (int c = tid; c < d; c += 256) st(y, base + c, ld(x, base + c, dt) * inv * ld(g, c, dt), dt);
   }
-  const float inv = 1.f / sqrtf(red[0] / float(d) + eps);
-  for (int c = tid; c < d; c += 256) st(y, base + c, ld(x, base + c, dt) * inv * ld(g, c, dt), dt);
 }
 
 // Greedy choice per row: the largest logit, ties to the lowest index.

@@ -20,6 +20,8 @@
 // Attention outputs then agree with a float64 evaluation to ~1e-6, so the
 // bf16 rounding of the output (and of everything downstream) almost never
 // lands on the other side of a rounding boundary than the exact value does.
+#include <type_traits>
+
 #include "attention.h"
 
 namespace vc {
@@ -195,6 +197,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // recomputed where needed rather than held in registers
   const int qr_lane = qr0 + 16 * wave + (lane & 15);
   auto blk_on = [&](int b) { return qr0 + 16 * (wave + 4 * b) < n_qrows; };  // uniform per wave
+  int n_act = 0;  // active blocks 0 .. n_act - 1 of this wave
+#pragma unroll
+  for (int b = 0; b < RPW; b++) n_act += blk_on(b) ? 1 : 0;
   u32x4 qf[RPW][4];
   f32x4 oacc[RPW][8];
   float m_run[RPW], l_run[RPW];
@@ -231,84 +236,108 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const bool full = t0 + ATT_KT - 1 <= lim_all;  // uniform
 
-#pragma unroll
-    for (int b = 0; b < RPW; b++) {
-      if (!blk_on(b)) continue;  // uniform across the wave
+    // Row blocks [B0, B0 + NB) of this wave (NB <= 2): each K and V^T fragment read from LDS
+    // feeds the MFMAs of all NB blocks.  Per block, the MFMA sequence and the softmax arithmetic
+    // are the same whichever blocks share the pass.
+    auto blocks = [&](auto b0v, auto nbv) {
+      constexpr int B0 = decltype(b0v)::value, NB = decltype(nbv)::value;
       // ---- S^T = K Q^T over 4 sub-tiles of 16 keys
-      f32x4 sacc[4];
+      f32x4 sacc[NB][4];
+#pragma unroll
+      for (int b = 0; b < NB; b++)
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++) sacc[b][kt] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int kt = 0; kt < 4; kt++) {
-        sacc[kt] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < 4; c++) {
           const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (16 * kt + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
-          sacc[kt] = mfma_bf16(ka, qf[b][c], sacc[kt]);
+#pragma unroll
+          for (int b = 0; b < NB; b++) sacc[b][kt] = mfma_bf16(ka, qf[B0 + b][c], sacc[b][kt]);
         }
       }
       // ---- mask, online softmax (row q = lane % 16).  Scores stay unscaled until the
       // exponent: p' = 2^(s * scale_log2 - m + 10) = 2^10 p in one fma per key, m and the
       // running sum in the scaled domain (the 2^10 is removed when the partial is written)
-      float mx = NEG_INF;
-      if (full) {
 #pragma unroll
-        for (int kt = 0; kt < 4; kt++) mx = fmaxf(mx, fmaxf(fmaxf(sacc[kt][0], sacc[kt][1]), fmaxf(sacc[kt][2], sacc[kt][3])));
-      } else {
-        const int qr = qr_lane + 64 * b;
-        const int lim = qr < n_qrows ? min(R.lim0 + qr / G, n_keys - 1) : -1;
+      for (int b = 0; b < NB; b++) {
+        float mx = NEG_INF;
+        if (full) {
+#pragma unroll
+          for (int kt = 0; kt < 4; kt++)
+            mx = fmaxf(mx, fmaxf(fmaxf(sacc[b][kt][0], sacc[b][kt][1]), fmaxf(sacc[b][kt][2], sacc[b][kt][3])));
+        } else {
+          const int qr = qr_lane + 64 * (B0 + b);
+          const int lim = qr < n_qrows ? min(R.lim0 + qr / G, n_keys - 1) : -1;
+#pragma unroll
+          for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              const int t = t0 + 16 * kt + 4 * grp + jj;
+              const bool vis = t <= lim;
+              sacc[b][kt][jj] = vis ? sacc[b][kt][jj] : NEG_INF;
+              mx = fmaxf(mx, sacc[b][kt][jj]);
+            }
+          }
+        }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[B0 + b], mx * sl2);
+        // no visible key yet (masked tiles only): nothing to add, state unchanged
+        const bool none = !full && m_new == NEG_INF;
+        const float nb = none ? 0.f : P_LOG2 - m_new;
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[B0 + b] - m_new);
+        float rs = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
           for (int jj = 0; jj < 4; jj++) {
-            const int t = t0 + 16 * kt + 4 * grp + jj;
-            const bool vis = t <= lim;
-            sacc[kt][jj] = vis ? sacc[kt][jj] : NEG_INF;
-            mx = fmaxf(mx, sacc[kt][jj]);
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][kt][jj], sl2, nb));
+            sacc[b][kt][jj] = p;
+            rs += p;
           }
         }
-      }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[b], mx * sl2);
-      // no visible key yet (masked tiles only): nothing to add, state unchanged
-      const bool none = !full && m_new == NEG_INF;
-      const float nb = none ? 0.f : P_LOG2 - m_new;
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[b] - m_new);
-      float rs = 0.f;
+        rs += shfl_xor(rs, 16);
+        rs += shfl_xor(rs, 32);
+        l_run[B0 + b] = l_run[B0 + b] * alpha + rs;
+        m_run[B0 + b] = m_new;
+        if (__any(alpha != 1.f)) {  // x * 1 == x: skip the rescale when no running max moved
 #pragma unroll
-      for (int kt = 0; kt < 4; kt++) {
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][jj], sl2, nb));
-          sacc[kt][jj] = p;
-          rs += p;
+          for (int dt = 0; dt < 8; dt++) oacc[B0 + b][dt] *= alpha;
         }
       }
-      rs += shfl_xor(rs, 16);
-      rs += shfl_xor(rs, 32);
-      l_run[b] = l_run[b] * alpha + rs;
-      m_run[b] = m_new;
-      if (__any(alpha != 1.f)) {  // x * 1 == x: skip the rescale when no running max moved
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) oacc[b][dt] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T over 2 chunks of 32 keys
+      // ---- O^T += V^T P^T over 2 chunks of 32 keys, P as an fp16 hi/lo pair
 #pragma unroll
       for (int kc = 0; kc < 2; kc++) {
-        uint32_t h[4], lw[4];
-        split_h2(sacc[2 * kc][0], sacc[2 * kc][1], h[0], lw[0]);
-        split_h2(sacc[2 * kc][2], sacc[2 * kc][3], h[1], lw[1]);
-        split_h2(sacc[2 * kc + 1][0], sacc[2 * kc + 1][1], h[2], lw[2]);
-        split_h2(sacc[2 * kc + 1][2], sacc[2 * kc + 1][3], h[3], lw[3]);
-        const u32x4 pb = u32x4{h[0], h[1], h[2], h[3]};
-        const u32x4 pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        u32x4 pb[NB], pl[NB];
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+          uint32_t h[4], lw[4];
+          split_h2(sacc[b][2 * kc][0], sacc[b][2 * kc][1], h[0], lw[0]);
+          split_h2(sacc[b][2 * kc][2], sacc[b][2 * kc][3], h[1], lw[1]);
+          split_h2(sacc[b][2 * kc + 1][0], sacc[b][2 * kc + 1][1], h[2], lw[2]);
+          split_h2(sacc[b][2 * kc + 1][2], sacc[b][2 * kc + 1][3], h[3], lw[3]);
+          pb[b] = u32x4{h[0], h[1], h[2], h[3]};
+          pl[b] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        }
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
           const u32x4 va = *reinterpret_cast<const u32x4*>(Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 8 * grp);
-          oacc[b][dt] = mfma_f16(va, pb, oacc[b][dt]);
-          oacc[b][dt] = mfma_f16(va, pl, oacc[b][dt]);
+#pragma unroll
+          for (int b = 0; b < NB; b++) {
+            oacc[B0 + b][dt] = mfma_f16(va, pb[b], oacc[B0 + b][dt]);
+            oacc[B0 + b][dt] = mfma_f16(va, pl[b], oacc[B0 + b][dt]);
+          }
         }
       }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (n_act >= 2) blocks(I0{}, I2{});
+    else if (n_act == 1) blocks(I0{}, I1{});
+    if constexpr (RPW == 3) {
+      if (n_act == 3) blocks(I2{}, I1{});
     }
   }
 

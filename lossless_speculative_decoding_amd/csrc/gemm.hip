@@ -5,10 +5,17 @@
 // wave) and one K range; the activations of that range are staged in LDS
 // 256 columns at a time and every wave runs 16x16x32 bf16 MFMAs over all
 // M rows (padded to 16) while its next weight fragments are in flight.
-// Prefill chunks (M > 64) use gemm_big_bf16, a 128x128x32 LDS double-buffered
-// MFMA tile.  The fp32 model uses a 16x16 tiled VALU kernel whose outputs are
-// single fma chains in ascending k.
+// Prefill chunks (M > 64) are plain bf16 GEMMs with float32 output and go to hipBLASLt
+// (one handle, a 32 MiB workspace and one algorithm per shape, kept per device for the
+// life of the process); gemm_big_bf16, a 128x128x32 LDS double-buffered MFMA tile, remains
+// for bf16 shapes the library does not serve.  The fp32 model uses a 16x16 tiled VALU
+// kernel whose outputs are single fma chains in ascending k.
+#include <hipblaslt/hipblaslt.h>
+
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "gemm.h"
 
@@ -265,6 +272,89 @@ __global__ void epilogue_kernel(const EpiArgs a) {
 
 }  // namespace
 
+namespace {
+
+// hipBLASLt for the prefill projections: P[M][N] = X[M][K] W[N][K]^T in float32.  In its
+// column-major view this is C (N x M) = W^T-as-stored (op T of a K x N matrix) times X (K x M).
+// A shape's descriptors and the first algorithm of the heuristic are made once and kept, so a
+// shape's result does not change between calls and a call does no host-side set-up.
+struct LtShape {
+  hipblasLtMatmulDesc_t md = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+  bool served = false;
+};
+struct LtDevice {
+  hipblasLtHandle_t h = nullptr;
+  void* ws = nullptr;
+  std::map<std::tuple<int, int, int>, LtShape> shape;
+};
+constexpr size_t LT_WS_BYTES = size_t(32) << 20;
+std::mutex g_lt_mu;
+std::map<int, LtDevice> g_lt;
+
+#define VC_LT(x)                                                                        \
+  do {                                                                                  \
+    const hipblasStatus_t st_ = (x);                                                    \
+    VC_REQUIRE(st_ == HIPBLAS_STATUS_SUCCESS, VC_ERR_HIP, "%s failed: status %d", #x, int(st_)); \
+  } while (0)
+
+// Descriptors and algorithm of one shape; leaves sh.served false when the library offers none.
+vc_status lt_shape_init(LtDevice& L, LtShape& sh, int M, int N, int K) {
+  VC_LT(hipblasLtMatmulDescCreate(&sh.md, HIPBLAS_COMPUTE_32F, HIP_R_32F));
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  VC_LT(hipblasLtMatmulDescSetAttribute(sh.md, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)));
+  VC_LT(hipblasLtMatmulDescSetAttribute(sh.md, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)));
+  VC_LT(hipblasLtMatrixLayoutCreate(&sh.la, HIP_R_16BF, K, N, K));
+  VC_LT(hipblasLtMatrixLayoutCreate(&sh.lb, HIP_R_16BF, K, M, K));
+  VC_LT(hipblasLtMatrixLayoutCreate(&sh.lc, HIP_R_32F, N, M, N));
+  hipblasLtMatmulPreference_t pref = nullptr;
+  VC_LT(hipblasLtMatmulPreferenceCreate(&pref));
+  size_t wsb = LT_WS_BYTES;
+  hipblasLtMatmulHeuristicResult_t res[1];
+  int nres = 0;
+  const hipblasStatus_t st1 =
+      hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb));
+  const hipblasStatus_t st2 = st1 == HIPBLAS_STATUS_SUCCESS
+                                  ? hipblasLtMatmulAlgoGetHeuristic(L.h, sh.md, sh.la, sh.lb, sh.lc, sh.lc, pref, 1, res, &nres)
+                                  : st1;
+  hipblasLtMatmulPreferenceDestroy(pref);
+  if (st2 == HIPBLAS_STATUS_SUCCESS && nres >= 1) {
+    sh.algo = res[0].algo;
+    sh.served = true;
+  }
+  return VC_OK;
+}
+
+vc_status lt_gemm(const void* X, const void* W, float* P, int M, int N, int K, hipStream_t s, bool* served) {
+  *served = false;
+  int dev = 0;
+  VC_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_lt_mu);
+  LtDevice& L = g_lt[dev];
+  if (!L.h) {
+    VC_LT(hipblasLtCreate(&L.h));
+    VC_HIP(hipMalloc(&L.ws, LT_WS_BYTES));
+  }
+  const auto key = std::make_tuple(M, N, K);
+  auto it = L.shape.find(key);
+  if (it == L.shape.end()) {
+    LtShape sh;
+    const vc_status st = lt_shape_init(L, sh, M, N, K);
+    if (st) return st;
+    it = L.shape.emplace(key, sh).first;
+  }
+  const LtShape& sh = it->second;
+  if (!sh.served) return VC_OK;  // the caller uses its own kernel
+  const float alpha = 1.f, beta = 0.f;
+  VC_LT(hipblasLtMatmul(L.h, sh.md, &alpha, W, sh.la, X, sh.lb, &beta, P, sh.lc, P, sh.lc, &sh.algo, L.ws,
+                        LT_WS_BYTES, s));
+  *served = true;
+  return VC_OK;
+}
+
+}  // namespace
+
 int gemm_splits(int M, int N, int K, int dtype) {
   if (dtype != VC_BF16 || M > 64) return 1;
   const int col_blocks = N / SK_NB;
@@ -290,6 +380,15 @@ vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int 
                             static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K, kps);
     } else {
       VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: prefill tiles use one split");
+      bool served = false;
+      if (ev_start) VC_HIP(hipEventRecord(ev_start, s));
+      vc_status st = lt_gemm(X, W, P, M, N, K, s, &served);
+      if (st) return st;
+      if (served) {
+        if (ev_stop) VC_HIP(hipEventRecord(ev_stop, s));
+        return VC_OK;
+      }
+      ev_start = nullptr;  // recorded above; the kernel below takes only the stop event
       VC_REQUIRE(N % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: N=%d not a multiple of 128", N);
       hipExtLaunchKernelGGL(gemm_big_bf16, dim3(N / 128, cdiv(M, 128)), dim3(256), 0, s, ev_start, ev_stop, 0,
                             static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K);

@@ -205,3 +205,15 @@ def test_one_layer_stage_by_stage():
     err = (np.abs(lg.cpu().numpy() - l_c).max(axis=1) / np.abs(l_c).max(axis=1)).max()
     log(f"stage logits (GPU normed input): max row rel err {err:.2e}")
     assert err <= TOL_BF16
+
+
+def test_prefill_is_repeatable_bitwise(setup):
+    """Two prefills of the same prompt give the same K/V bit for bit (the projection GEMMs of
+    prefill chunks use one fixed library algorithm per shape)."""
+    from lossless_speculative_decoding_amd.engine import greedy_resident
+    T = setup["prompt"].numel()  # rows past the prompt are capacity, not written by prefill
+    _, _, (k1, v1) = greedy_resident(setup["m"], setup["prompt"], 1, chunk=256)
+    _, _, (k2, v2) = greedy_resident(setup["m"], setup["prompt"], 1, chunk=256)
+    kd, vd = setup["kv"]
+    for a, b in ((k1, k2), (v1, v2), (k1, kd), (v1, vd)):
+        assert torch.equal(a[:, :, :T], b[:, :, :T])

@@ -34,106 +34,124 @@ namespace vc {
 namespace {
 
 constexpr int D = 128;
-constexpr float P_LOG2 = 10.f;  // P' carries p * 2^10 (out of the fp16 subnormal range)
-constexpr float P_UNSCALE = 1.f / 1024.f;
+// ---------------------------------------------------------------- codes -> fp16 MFMA operands
+// An output word carries two codes of a lane's run as fp16 numbers 1 + c 2^(o - 10): the b code
+// bits sit at mantissa bits [o, o + b) under the exponent of 1.0 (0x3C00), one code per 16-bit
+// half.  Word m of a run takes the run's little-endian bit stream from bit s (nothing, one shift
+// or one funnel shift of two packed words), keeps the two fields and ors in the exponents: one
+// v_and_or_b32 plus at most one shift per word, and words with the same s share the shift.
+// Position p = 2m + h of a run's fp16 sequence (h = 0 the low half) holds code lo (h = 0) or
+// hi (h = 1) of word m.  The factor 2^(10 - o) of each position goes into the other operand
+// (Q' on the K side, the V scale on the V side), and the offset 1 into a bias, so the codes are
+// never centred by arithmetic.  The fp32 accumulators then also carry the offsets, 2^(10 - o)
+// times the code part at most, and for a diffuse attention row the output is far smaller than
+// the weighted sum of offsets: positions keep o >= 4 (3-bit V: o >= 3), which holds the extra
+// accumulation error to ~1e-4 of the output (o = 0 measured ~3e-3 at 2k keys).
+struct ConvWord {
+  int s;         // stream bit that lands at bit 0 (negative: shifted left)
+  int lo, olo;   // code index in the run and mantissa offset, low half
+  int hi, ohi;   // same, high half
+};
 
-// 0x6400 | c is the fp16 number 1024 + c; subtracting 1024 + 2^(b-1) leaves the centred code exactly
-template <int BITS>
-__device__ __forceinline__ uint32_t centre(uint32_t x) {
-  constexpr float off = 1024.f + float(1 << (BITS - 1));
-  return bitcast<uint32_t>(bitcast<f16x2>(x) - f16x2{(_Float16)off, (_Float16)off});
+template <int BITS> struct KConv;  // K runs: 32 codes (one key, 32 channels), 16 words
+template <int BITS> struct VConv;  // V runs: 16 codes (one channel, 16 tokens), 8 words
+
+#define RUN4(w) ConvWord{32 * w - 4, 8 * w, 4, 8 * w + 4, 4}, ConvWord{32 * w, 8 * w + 1, 4, 8 * w + 5, 4}, \
+               ConvWord{32 * w + 4, 8 * w + 2, 4, 8 * w + 6, 4}, ConvWord{32 * w + 8, 8 * w + 3, 4, 8 * w + 7, 4}
+template <> struct KConv<4> { static constexpr ConvWord w[16] = {RUN4(0), RUN4(1), RUN4(2), RUN4(3)}; };
+template <> struct VConv<4> { static constexpr ConvWord w[8] = {RUN4(0), RUN4(1)}; };
+#define RUN2(w) ConvWord{32 * w - 4, 16 * w, 4, 16 * w + 8, 4}, ConvWord{32 * w - 4, 16 * w + 1, 6, 16 * w + 9, 6},       \
+               ConvWord{32 * w, 16 * w + 2, 4, 16 * w + 10, 4}, ConvWord{32 * w, 16 * w + 3, 6, 16 * w + 11, 6},        \
+               ConvWord{32 * w, 16 * w + 4, 8, 16 * w + 12, 8}, ConvWord{32 * w + 6, 16 * w + 5, 4, 16 * w + 13, 4}, \
+               ConvWord{32 * w + 6, 16 * w + 6, 6, 16 * w + 14, 6}, ConvWord{32 * w + 6, 16 * w + 7, 8, 16 * w + 15, 8}
+template <> struct KConv<2> { static constexpr ConvWord w[16] = {RUN2(0), RUN2(1)}; };
+template <> struct VConv<2> { static constexpr ConvWord w[8] = {RUN2(0)}; };
+#undef RUN2
+#undef RUN4
+// 3-bit fields sit at multiples of 3, so the two codes of a word are 5 or 6 apart in the run and
+// most words need their own (funnel) shift
+template <> struct KConv<3> {
+  static constexpr ConvWord w[16] = {{-7, 0, 7, 5, 6},   {-4, 1, 7, 6, 6},   {0, 2, 6, 7, 5},    {2, 3, 7, 8, 6},
+                                     {5, 4, 7, 9, 6},    {23, 10, 7, 15, 6}, {26, 11, 7, 16, 6}, {29, 12, 7, 17, 6},
+                                     {32, 13, 7, 18, 6}, {35, 14, 7, 19, 6}, {53, 20, 7, 25, 6}, {58, 21, 5, 27, 7},
+                                     {61, 22, 5, 28, 7}, {64, 23, 5, 29, 7}, {67, 24, 5, 30, 7}, {71, 26, 7, 31, 6}};
+};
+// (no pairing of 16 3-bit codes keeps every offset >= 4; five positions use o = 3)
+template <> struct VConv<3> {
+  static constexpr ConvWord w[8] = {{-7, 0, 7, 4, 3}, {-4, 1, 7, 5, 3},  {0, 2, 6, 7, 5},   {2, 3, 7, 8, 6},
+                                    {13, 6, 5, 12, 7}, {20, 9, 7, 13, 3}, {23, 10, 7, 14, 3}, {26, 11, 7, 15, 3}};
+};
+
+// every code of the run exactly once, each field where the word's shift puts it
+template <int BITS, int N, int OMIN>
+constexpr bool conv_table_ok(const ConvWord (&t)[N]) {
+  int seen[2 * N] = {};
+  for (int m = 0; m < N; m++) {
+    const ConvWord& c = t[m];
+    if (c.lo < 0 || c.hi < 0 || c.lo >= 2 * N || c.hi >= 2 * N) return false;
+    seen[c.lo]++;
+    seen[c.hi]++;
+    if (BITS * c.lo - c.s != c.olo || BITS * c.hi - c.s - 16 != c.ohi) return false;
+    if (c.olo < OMIN || c.ohi < OMIN || c.olo + BITS > 10 || c.ohi + BITS > 10) return false;
+  }
+  for (int i = 0; i < 2 * N; i++)
+    if (seen[i] != 1) return false;
+  return true;
+}
+static_assert(conv_table_ok<4, 16, 4>(KConv<4>::w) && conv_table_ok<2, 16, 4>(KConv<2>::w) &&
+                  conv_table_ok<3, 16, 4>(KConv<3>::w), "K conversion tables");
+static_assert(conv_table_ok<4, 8, 4>(VConv<4>::w) && conv_table_ok<2, 8, 4>(VConv<2>::w) &&
+                  conv_table_ok<3, 8, 3>(VConv<3>::w), "V conversion tables");
+
+// the stream bits of word CW's two fields, shifted so that stream bit CW.s is bit 0
+template <int BITS, ConvWord CW, int NW>
+__device__ __forceinline__ uint32_t run_bits(const uint32_t (&w)[NW]) {
+  constexpr int b0 = BITS * CW.lo, b1 = BITS * CW.hi + BITS - 1;  // first and last bit of the fields
+  constexpr int k0 = b0 / 32, k1 = b1 / 32;
+  static_assert(k1 < NW, "field past the packed words");
+  if constexpr (k0 == k1) {
+    constexpr int r = CW.s - 32 * k0;
+    if constexpr (r >= 0) return w[k0] >> r;
+    else return w[k0] << (-r);
+  } else {
+    static_assert(k1 == k0 + 1 && CW.s >= 32 * k0 && CW.s < 32 * k0 + 32, "funnel window");
+    return __builtin_amdgcn_alignbit(w[k0 + 1], w[k0], CW.s - 32 * k0);
+  }
 }
 
-// (x & mask) | 0x64006400 (two codes -> two fp16 numbers 1024 + c) as one VALU operation
-__device__ __forceinline__ uint32_t and_or_mag(uint32_t x, uint32_t mask) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(0x64006400u));
+template <int BITS, ConvWord CW, int NW>
+__device__ __forceinline__ uint32_t conv_word(const uint32_t (&w)[NW]) {
+  constexpr uint32_t f = (1u << BITS) - 1;
+  constexpr uint32_t mask = (f << CW.olo) | (f << (16 + CW.ohi));
+  // (x & mask) | 0x3C003C00 as one v_bitop3_b32 (truth table 0xEA = (a & b) | c); a builtin rather
+  // than inline asm, so that the compiler sees the write and keeps the MFMA operand hazards
+  return __builtin_amdgcn_bitop3_b32(run_bits<BITS, CW>(w), mask, 0x3C003C00u, 0xEA);
+}
+
+// fp16 position p of a run: the code index and mantissa offset it carries
+template <typename T>
+constexpr int conv_code(int p) { return (p & 1) ? T::w[p >> 1].hi : T::w[p >> 1].lo; }
+template <typename T>
+constexpr int conv_off(int p) { return (p & 1) ? T::w[p >> 1].ohi : T::w[p >> 1].olo; }
+// mantissa offsets of the positions that carry codes 0..15 of a V run, 4 bits each
+template <typename T>
+constexpr uint64_t conv_offs_by_code() {
+  uint64_t r = 0;
+  for (int p = 0; p < 16; p++) r |= uint64_t(conv_off<T>(p)) << (4 * conv_code<T>(p));
   return r;
 }
 
-// position -> code index within a conversion group
-template <int BITS>
-__device__ __forceinline__ int perm_pos(int p) {
-  if constexpr (BITS == 4) {
-    const int k = p & 7;
-    return (p & ~7) | ((k & 1) ? 4 + (k >> 1) : (k >> 1));
-  } else if constexpr (BITS == 2) {
-    const int k = p & 15;
-    return (p & ~15) | ((k & 1) ? 8 + (k >> 1) : (k >> 1));
-  } else {
-    return p;
-  }
-}
 template <int BITS>
 struct Codes32 {
   uint32_t w[BITS];  // 32 * BITS bits
 };
 
-template <int BITS>
-__device__ __forceinline__ void cvt_codes(const Codes32<BITS>& c, u32x4 out[4]) {
-  constexpr uint32_t MAG = 0x64006400u;
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-      const uint32_t x = c.w[w];
-      out[w].x = centre<BITS>(and_or_mag(x, 0x000F000Fu));
-      out[w].y = centre<BITS>(and_or_mag(x >> 4, 0x000F000Fu));
-      out[w].z = centre<BITS>(and_or_mag(x >> 8, 0x000F000Fu));
-      out[w].w = centre<BITS>(and_or_mag(x >> 12, 0x000F000Fu));
-    }
-  } else if constexpr (BITS == 2) {
-#pragma unroll
-    for (int w = 0; w < 2; w++) {
-      const uint32_t x = c.w[w];
-      out[2 * w].x = centre<BITS>(and_or_mag(x, 0x00030003u));
-      out[2 * w].y = centre<BITS>(and_or_mag(x >> 2, 0x00030003u));
-      out[2 * w].z = centre<BITS>(and_or_mag(x >> 4, 0x00030003u));
-      out[2 * w].w = centre<BITS>(and_or_mag(x >> 6, 0x00030003u));
-      out[2 * w + 1].x = centre<BITS>(and_or_mag(x >> 8, 0x00030003u));
-      out[2 * w + 1].y = centre<BITS>(and_or_mag(x >> 10, 0x00030003u));
-      out[2 * w + 1].z = centre<BITS>(and_or_mag(x >> 12, 0x00030003u));
-      out[2 * w + 1].w = centre<BITS>(and_or_mag(x >> 14, 0x00030003u));
-    }
-  } else {
-    const uint64_t lo = uint64_t(c.w[0]) | (uint64_t(c.w[1]) << 32);
-    const uint64_t hi = uint64_t(c.w[1]) | (uint64_t(c.w[2]) << 32);
-    uint32_t r[16];
-#pragma unroll
-    for (int m = 0; m < 16; m++) {
-      const int off = 6 * m;
-      const uint32_t f = off < 32 ? uint32_t(lo >> off) : uint32_t(hi >> (off - 32));
-      r[m] = centre<BITS>(((f & 7u) | ((f & 0x38u) << 13)) | MAG);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; q++) out[q] = u32x4{r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]};
-  }
-}
-
-// Chunk ch (channels 8ch..8ch+7 of the lane's 32, in conversion order) of cvt_codes: the
-// same words and operations, so that a chunk's operand is built just before its MFMAs.
+// chunk CH (fp16 positions 8CH .. 8CH + 7) of a K run, built just before its MFMAs
 template <int BITS, int CH>
-__device__ __forceinline__ u32x4 cvt_codes_chunk(const Codes32<BITS>& c) {
-  constexpr uint32_t MAG = 0x64006400u;
-  if constexpr (BITS == 4) {
-    const uint32_t x = c.w[CH];
-    return u32x4{centre<BITS>(and_or_mag(x, 0x000F000Fu)), centre<BITS>(and_or_mag(x >> 4, 0x000F000Fu)),
-                 centre<BITS>(and_or_mag(x >> 8, 0x000F000Fu)), centre<BITS>(and_or_mag(x >> 12, 0x000F000Fu))};
-  } else if constexpr (BITS == 2) {
-    const uint32_t x = c.w[CH >> 1] >> (8 * (CH & 1));
-    return u32x4{centre<BITS>(and_or_mag(x, 0x00030003u)), centre<BITS>(and_or_mag(x >> 2, 0x00030003u)),
-                 centre<BITS>(and_or_mag(x >> 4, 0x00030003u)), centre<BITS>(and_or_mag(x >> 6, 0x00030003u))};
-  } else {
-    const uint64_t lo = uint64_t(c.w[0]) | (uint64_t(c.w[1]) << 32);
-    const uint64_t hi = uint64_t(c.w[1]) | (uint64_t(c.w[2]) << 32);
-    uint32_t r[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int off = 6 * (4 * CH + i);
-      const uint32_t f = off < 32 ? uint32_t(lo >> off) : uint32_t(hi >> (off - 32));
-      r[i] = centre<BITS>(((f & 7u) | ((f & 0x38u) << 13)) | MAG);
-    }
-    return u32x4{r[0], r[1], r[2], r[3]};
-  }
+__device__ __forceinline__ u32x4 cvt_k_chunk(const Codes32<BITS>& c) {
+  using T = KConv<BITS>;
+  return u32x4{conv_word<BITS, T::w[4 * CH]>(c.w), conv_word<BITS, T::w[4 * CH + 1]>(c.w),
+               conv_word<BITS, T::w[4 * CH + 2]>(c.w), conv_word<BITS, T::w[4 * CH + 3]>(c.w)};
 }
 
 __device__ __forceinline__ float h2f(uint16_t h) { return float(bitcast<_Float16>(h)); }
@@ -166,35 +184,26 @@ __device__ __forceinline__ VCodes16<BITS> ld_vcodes(const uint8_t* src) {
   return c;
 }
 
-// -> 16 centred fp16 codes; output position i holds code perm_pos<BITS>(i)
+// the two chunks (fp16 positions 0..7, 8..15) of a V run
 template <int BITS>
-__device__ __forceinline__ void cvt_vcodes(const VCodes16<BITS>& c, u32x4 out[2]) {
-  if constexpr (BITS == 2) {
-    const uint32_t x = c.w[0];
-    uint32_t r[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) r[k] = centre<BITS>(and_or_mag(x >> (2 * k), 0x00030003u));
-    out[0] = u32x4{r[0], r[1], r[2], r[3]};
-    out[1] = u32x4{r[4], r[5], r[6], r[7]};
-  } else if constexpr (BITS == 4) {
-#pragma unroll
-    for (int w = 0; w < 2; w++) {
-      const uint32_t x = c.w[w];
-      out[w] = u32x4{centre<BITS>(and_or_mag(x, 0x000F000Fu)), centre<BITS>(and_or_mag(x >> 4, 0x000F000Fu)),
-                     centre<BITS>(and_or_mag(x >> 8, 0x000F000Fu)), centre<BITS>(and_or_mag(x >> 12, 0x000F000Fu))};
-    }
-  } else {
-    constexpr uint32_t MAG = 0x64006400u;
-    const uint64_t bits = uint64_t(c.w[0]) | (uint64_t(c.w[1]) << 32);
-    uint32_t r[8];
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-      const uint32_t f = uint32_t(bits >> (6 * m));
-      r[m] = centre<BITS>(((f & 7u) | ((f & 0x38u) << 13)) | MAG);
-    }
-    out[0] = u32x4{r[0], r[1], r[2], r[3]};
-    out[1] = u32x4{r[4], r[5], r[6], r[7]};
-  }
+__device__ __forceinline__ void cvt_v(const VCodes16<BITS>& c, u32x4 out[2]) {
+  using T = VConv<BITS>;
+  out[0] = u32x4{conv_word<BITS, T::w[0]>(c.w), conv_word<BITS, T::w[1]>(c.w), conv_word<BITS, T::w[2]>(c.w),
+                 conv_word<BITS, T::w[3]>(c.w)};
+  out[1] = u32x4{conv_word<BITS, T::w[4]>(c.w), conv_word<BITS, T::w[5]>(c.w), conv_word<BITS, T::w[6]>(c.w),
+                 conv_word<BITS, T::w[7]>(c.w)};
+}
+
+// The constant "centre row" of the V side, negated: position p holds -W_p with
+// W_p = 1 + 2^(b-1) 2^(o_p - 10), so that u - W_p = (c - 2^(b-1)) 2^(o_p - 10) for the code u of
+// that position; its fp16 bits are 0xBC00 | 2^(b - 1 + o_p) (exact).  An MFMA of this row with P'
+// right after each code MFMA subtracts sum_t P'_t W_t, from the same rounded P', in the same
+// accumulator: the accumulators never carry more than one chunk's offsets (the MFMA accumulation
+// of large offsets measured ~3e-3 of the output at o = 4 when they were removed only at the end).
+template <int BITS>
+constexpr uint32_t centre_word(int m) {
+  const ConvWord& c = VConv<BITS>::w[m];
+  return (0xBC00u | (1u << (BITS - 1 + c.olo))) | ((0xBC00u | (1u << (BITS - 1 + c.ohi))) << 16);
 }
 
 template <int BITS>
@@ -399,7 +408,7 @@ __device__ void quant_exact_rows(const QuantReq& R, int j, int G, int Hq, float 
 }
 
 template <int BITS, int NH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 || BITS == 2) ? 3 : 2, (NH == 1 || BITS == 2) ? 3 : 2))) void attn_quant_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3 : 2, NH == 1 ? 3 : 2))) void attn_quant_kernel(
     const QuantArgs args) {
   using L = QLds<NH>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::BYTES];
@@ -452,8 +461,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
   }
 
   // ---- split tables.  Item (group, head, quarter): channels [32 quarter, +32) of Q' in the
-  // lane order of the MFMA fragments (position p -> channel 32 quarter + perm_pos(p)) and the
-  // quarter's key-bias partial, accumulated in that same order.
+  // lane order of the MFMA fragments (position p carries channel 32 quarter + conv_code(p)),
+  //     Q'_p = q s_K 2^(10 - o_p) scale_log2   (scores come out in log2 units),
+  // split into fp16 hi + lo, and the quarter's key-bias partial
+  //     scale_log2 sum q z_K - sum_p (hi_p + lo_p),
+  // which removes the offset 1 of every code from the score using exactly the Q' the MFMAs use.
+  using KT = KConv<BITS>;
+  const float sl2 = args.scale_log2;
   for (int it = tid; it < n_grp * G * 4; it += 256) {
     const int gi = it / (4 * G), h = (it / 4) % G, qq = it % 4;
     const u32x4* qv = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(R.q) + int64_t(j * G + h) * D + 32 * qq);
@@ -467,7 +481,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
       zw[4 * i] = b.x; zw[4 * i + 1] = b.y; zw[4 * i + 2] = b.z; zw[4 * i + 3] = b.w;
       qw[4 * i] = c.x; qw[4 * i + 1] = c.y; qw[4 * i + 2] = c.z; qw[4 * i + 3] = c.w;
     }
-    float b = 0.f;
+    float bqz = 0.f, boff = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       uint32_t w[4], wl[4];
@@ -476,22 +490,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
         float pr[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; h2++) {
-          const int ch = perm_pos<BITS>(8 * c + 2 * e2 + h2);  // channel 32 qq + ch
+          const int pos = 8 * c + 2 * e2 + h2;
+          const int ch = conv_code<KT>(pos);  // channel 32 qq + ch
           const float qd = (ch & 1) ? hi_bf(qw[ch >> 1]) : lo_bf(qw[ch >> 1]);
           const float sd = h2f(uint16_t(half16(sw, ch))), zd = h2f(uint16_t(half16(zw, ch)));
-          b = fmaf(qd, fmaf(sd, C0, zd), b);
-          pr[h2] = qd * sd;
+          bqz = fmaf(qd, zd, bqz);
+          pr[h2] = (qd * sd) * (sl2 * float(1 << (10 - conv_off<KT>(pos))));
         }
+        // Left to itself the compiler may round the same product to fp16 in two ways (a fused
+        // v_fma_mixlo_f16 for one use, the product rounded to fp32 and then converted for
+        // another): the hi of the stored word and the hi that lo is taken against could then
+        // differ by one ulp, and so could the bias's hi and the MFMAs' (~1e-2 in a score).  Empty
+        // asm statements (no instruction) make the fp32 product and the stored words opaque, so
+        // hi + lo is the product to 2^-22 and the bias is taken from the very bits the MFMAs read.
+        asm volatile("" : "+v"(pr[0]), "+v"(pr[1]));
         split_h2(pr[0], pr[1], w[e2], wl[e2]);
+        asm volatile("" : "+v"(w[e2]), "+v"(wl[e2]));
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+          const float hi = h2f(uint16_t(w[e2] >> (16 * h2))), lo = h2f(uint16_t(wl[e2] >> (16 * h2)));
+          boff += hi + lo;
+        }
       }
       s_qp[((gi * 4 + c) * 2 + 0) * 4 * G + qq * G + h] = u32x4{w[0], w[1], w[2], w[3]};
       s_qp[((gi * 4 + c) * 2 + 1) * 4 * G + qq * G + h] = u32x4{wl[0], wl[1], wl[2], wl[3]};
     }
-    s_kbp[it] = b;
+    s_kbp[it] = fmaf(bqz, sl2, -boff);
   }
+  // V scale of key t with the factor 2^(10 - o) of the position that carries it (its index in
+  // its 16-token run), and the V bias weight 2^(b-1) s_V + z_V
+  using VT = VConv<BITS>;
   for (int i = tid; i < (key_hi - key_lo) * nh; i += 256) {
     const float sv = h2f(vs[int64_t(key_lo) * nh + i]), zv = h2f(vz[int64_t(key_lo) * nh + i]);
-    s_vf[2 * i] = sv;
+    constexpr uint64_t offs = conv_offs_by_code<VT>();
+    const int o = int((offs >> (4 * ((i / nh) & 15))) & 15);
+    s_vf[2 * i] = sv * float(1 << (10 - o));
     s_vf[2 * i + 1] = fmaf(sv, C0, zv);
   }
   __syncthreads();
@@ -505,13 +538,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
   f32x4 oacc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; dt++) oacc[dt] = f32x4{0, 0, 0, 0};
+  // the negated centre row as an MFMA operand: the same fp16 positions in every lane
+  const u32x4 wcen[2] = {u32x4{centre_word<BITS>(0), centre_word<BITS>(1), centre_word<BITS>(2), centre_word<BITS>(3)},
+                         u32x4{centre_word<BITS>(4), centre_word<BITS>(5), centre_word<BITS>(6), centre_word<BITS>(7)}};
   float vb0 = 0.f, vb1 = 0.f;
   float m_run = NEG_INF, l_run = 0.f;
-  const float sl2 = args.scale_log2;
 
   for (; t0 < key_hi; t0 += QWAVES * ATT_KT) {
-    // V scale and centred-code zero of this lane's keys [t0 + 16g, t0 + 16g + 16): (s, z') of
-    // key k, channel group v at vf[k * NH + v]
+    // V scale (times the factor of the key's position) and bias weight of this lane's keys
+    // [t0 + 16g, t0 + 16g + 16): key k, channel group v at vf[k * NH + v]
     const float2* const vf = reinterpret_cast<const float2*>(s_vf) + (t0 - key_lo + 16 * g) * nh;
     // ---- key bias of the tile's token group; its Q' fragments are read per 32-channel chunk
     // (holding them across tiles, or all four chunks at once, would keep registers live)
@@ -529,7 +564,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
       const u32x4 qh = qp[(c * 2 + 0) * 4 * G], ql = qp[(c * 2 + 1) * 4 * G];
 #pragma unroll
       for (int kt = 0; kt < 4; kt++) {
-        const u32x4 ka = cvt_codes_chunk<BITS, c>(kr[kt]);
+        const u32x4 ka = cvt_k_chunk<BITS, c>(kr[kt]);
         sacc[kt] = mfma_f16(ka, qh, sacc[kt]);
         sacc[kt] = mfma_f16(ka, ql, sacc[kt]);
       }
@@ -542,23 +577,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
     const int tn = t0 + QWAVES * ATT_KT;
     if (tn < key_hi) ld_ktile<BITS>(kr, kc, tn, r16, g);
 
-    // ---- online softmax per head (every key of a tile is visible).  p' = 2^10 p comes out of
-    // one fma per key: 2^((s + bias) scale_log2 - m + 10), m and the sums in the scaled domain.
+    // ---- online softmax per head (every key of a tile is visible), in log2 units: the score of a
+    // key is its MFMA sum plus the group's key bias, p = 2^(score - m).
     float mx = NEG_INF;
 #pragma unroll
     for (int kt = 0; kt < 4; kt++)
       mx = fmaxf(mx, fmaxf(fmaxf(sacc[kt][0], sacc[kt][1]), fmaxf(sacc[kt][2], sacc[kt][3])));
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, (mx + kbias) * sl2);
+    const float m_new = fmaxf(m_run, mx + kbias);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float nb = P_LOG2 - m_new;
+    const float nb = kbias - m_new;
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][jj] + kbias, sl2, nb));
+        const float p = __builtin_amdgcn_exp2f(sacc[kt][jj] + nb);
         sacc[kt][jj] = p;
         rs += p;
       }
@@ -574,10 +609,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
       vb1 *= alpha;
     }
 
-    // ---- P' = p s (per V channel group) as one fp16 number, in the V conversion order, and the
-    // V bias.  One fp16 rounding of each weight (2^-12 relative, independent) costs up to ~6e-4
-    // relative in the output (measured; the exact V zero term partly cancels the coded sum),
-    // against ~1e-5 with an fp16 hi/lo pair, for half the P.V MFMAs and P' work.
+    // ---- P' = p s_V 2^(10 - o) (per V channel group) as one fp16 number, in the V conversion
+    // order, and the V bias sum p (2^(b-1) s_V + z_V).  With the centre row, the output is
+    //     sum_t P'_t (u_t - W_t) + bias = sum_t P'_t (c_t - 2^(b-1)) 2^(o-10) + bias,
+    // so one fp16 rounding of each weight (2^-12 relative, independent) meets the centred code,
+    // as if the codes had been centred: up to ~6e-4 relative in the output (measured), against
+    // ~1e-5 with an fp16 hi/lo pair, for half the P.V MFMAs and P' work.
     u32x4 pb[2][NH];  // [32-key chunk][V channel group]
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; kc2++) {
@@ -587,13 +624,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
         float pr[NH][2];
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-          const int k = perm_pos<BITS>(8 * kc2 + 2 * e2 + h);  // key 16g + k
-          const float x = sacc[k >> 2][k & 3];                 // 2^10 p
+          const int k = conv_code<VT>(8 * kc2 + 2 * e2 + h);  // key 16g + k
+          const float x = sacc[k >> 2][k & 3];                // p
 #pragma unroll
           for (int v = 0; v < NH; v++) {
             const float2 f = vf[k * NH + v];
             pr[v][h] = x * f.x;
-            if (v == 0) vb0 = fmaf(x, f.y, vb0);  // zero of the centred code
+            if (v == 0) vb0 = fmaf(x, f.y, vb0);
             else vb1 = fmaf(x, f.y, vb1);
           }
         }
@@ -607,10 +644,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
       u32x4 va[2];
-      cvt_vcodes<BITS>(vr[dt], va);
+      cvt_v<BITS>(vr[dt], va);
       const int v = NH == 2 ? (dt >> 2) : 0;
 #pragma unroll
-      for (int kc2 = 0; kc2 < 2; kc2++) oacc[dt] = mfma_f16(va[kc2], pb[kc2][v], oacc[dt]);
+      for (int kc2 = 0; kc2 < 2; kc2++) {
+        oacc[dt] = mfma_f16(va[kc2], pb[kc2][v], oacc[dt]);
+        oacc[dt] = mfma_f16(wcen[kc2], pb[kc2][v], oacc[dt]);
+      }
     }
     if (tn < key_hi) ld_vtile<BITS>(vr, vc, tn, r16, g);
   }
@@ -627,13 +667,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((NH == 1 ||
     float* rh = rw + r16 * QRED;
     if (g == 0) {
       rh[0] = m_run;
-      rh[1] = l_run * P_UNSCALE;
+      rh[1] = l_run;
     }
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
       const float vbias = dt >= 4 ? vb1 : vb0;
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) rh[2 + 16 * dt + 4 * g + jj] = (oacc[dt][jj] + vbias) * P_UNSCALE;
+      for (int jj = 0; jj < 4; jj++) rh[2 + 16 * dt + 4 * g + jj] = oacc[dt][jj] + vbias;
     }
   }
   __syncthreads();

@@ -242,6 +242,14 @@ def _rate(st: dict, bound: str, what: str) -> dict | None:
     return out
 
 
+# Workloads switched off until the cause of a failure is shown (their code paths are otherwise unchanged).
+DISABLED = {
+    "llama8b_q2": "a run of it (with the 8 x 65536 token-drop and the mixed workloads in the same command) left the "
+                  "GPU faulted without output; the faulting kernel is not identified yet",
+    "llama8b_mixed": "see llama8b_q2: the same command, the faulting kernel is not identified yet",
+}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +260,10 @@ def main():
     ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
     ap.add_argument("--baseline-steps", type=int, default=2)
+    ap.add_argument("--draft-batch", type=int, default=0,
+                    help="requests yet to draft wait for a batch this large while --queue-min drafted requests are "
+                         "queued for verification (0: half the requests; 1: draft as soon as possible)")
+    ap.add_argument("--queue-min", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
@@ -282,6 +294,8 @@ def main():
     import lossless_speculative_decoding_amd as vc
     from lossless_speculative_decoding_amd.engine import Engine, greedy_from_host, make_weights
 
+    if args.config in DISABLED:
+        sys.exit(f"bench.py: workload {args.config} is disabled: {DISABLED[args.config]}")
     w = configs.ALL[args.config]()
     s = w.model
     ctx = list(w.ctx)
@@ -309,7 +323,7 @@ def main():
                             "attention": vc.profile_read(vc.VC_PROF_PREFILL_ATTN), "tokens": T}
         log(f"request {r}: T={T} prefill+compress+offload {time.perf_counter() - t0:.1f}s")
     x_round = max(xs)
-    eng.start()
+    eng.start(draft_batch=args.draft_batch or None, queue_min=args.queue_min)
     t_setup = time.perf_counter() - t_setup
     log(f"setup {t_setup:.1f}s")
 
@@ -328,6 +342,7 @@ def main():
     e0 = eng.emitted_total()
     sb0, sn0 = eng.staged_bytes, eng.stagings
     a0 = [len(r.accepts) for r in eng.reqs]
+    d0, ds0 = eng.drafted, eng.draft_steps
     t0 = time.perf_counter()
     eng.run_draft_steps(args.steps * x_round)
     eng.drain()
@@ -337,6 +352,7 @@ def main():
     prof = vc.profile_read()
     vprof = vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
     emitted = eng.emitted_total() - e0
+    mean_draft_batch = (eng.drafted - d0) / max(eng.draft_steps - ds0, 1)
     staged, n_staged = eng.staged_bytes - sb0, eng.stagings - sn0
     tok_s = emitted / secs
     accepts = [a for r, n0 in zip(eng.reqs, a0) for a in r.accepts[n0:]]
@@ -437,6 +453,8 @@ def main():
         "full_kv_from_host_tok_s": round(base_tok_s, 3),
         "full_kv_from_host_tokens_match": base_match,
         "speedup_vs_full_kv_from_host": round(tok_s / base_tok_s, 3),
+        "scheduler": {"draft_batch": eng.draft_batch, "queue_min": eng.queue_min,
+                      "mean_requests_per_draft_step": round(mean_draft_batch, 2)},
         "mean_accepted_per_round": round(sum(accepts) / max(len(accepts), 1), 3),
         "accept_hist": {str(k): hist[k] for k in sorted(hist)},
         "compressed_only_draft_tok_s": round(draft_only, 2),

@@ -198,16 +198,28 @@ class Engine:
             self.slot_owner = [None] * n_slots
 
     # ------------------------------------------------------------ the VeriCache loop
-    def start(self, lead: int = 2, stagger: bool = True):
-        """Allocate slots/workspaces and set the staggered start ticks."""
+    def start(self, lead: int = 2, stagger: bool = True, draft_batch: int | None = None, queue_min: int = 2):
+        """Allocate slots/workspaces and set the staggered start ticks.
+
+        draft_batch / queue_min: a request that has not begun its x drafts waits while at least
+        queue_min drafted requests are queued for verification and fewer than draft_batch
+        requests would draft together; drafting is then done in larger batches (fuller draft
+        kernels) while the host link, which sets the pace, still always has a drafted request to
+        stage.  draft_batch=1 drafts every request as soon as it can (default: five eighths of them,
+        at most n - queue_min - 1)."""
         self._alloc()
         n = len(self.reqs)
         for r in self.reqs:
             r.start_tick = (r.idx * r.x) // n if stagger else 0
             r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
         self.lead = lead
+        # at most n - queue_min - 1 requests can wait together (queue_min queued, one staging)
+        auto = max(1, min(n // 2 + n // 8, n - queue_min - 1))
+        self.draft_batch = auto if draft_batch is None else max(1, draft_batch)
+        self.queue_min = queue_min
         self.tick = 0
         self.draft_steps = 0
+        self.drafted = 0  # request-tokens drafted (sum of the batch over draft steps)
 
     def step(self) -> bool:
         """One scheduler iteration: finish accepts, issue staging, one batched
@@ -222,11 +234,18 @@ class Engine:
         for r in reqs:
             if r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= r.x - self.lead and self.tick >= r.start_tick:
                 self._try_stage(r)
-        # 3. one batched draft step for every drafting request
-        active = [r for r in reqs if r.phase == DRAFT and self.tick >= r.start_tick and r.req.draft_idx < r.x]
+        # 3. one batched draft step for every drafting request; requests yet to begin wait for a
+        # fuller batch while enough drafted requests are queued for the host link
+        ready = [r for r in reqs if r.phase == DRAFT and self.tick >= r.start_tick and r.req.draft_idx < r.x]
+        active = [r for r in ready if r.req.draft_idx > 0]
+        fresh = [r for r in ready if r.req.draft_idx == 0]
+        queued = sum(1 for r in reqs if r.phase == WAIT_SLOT)
+        if fresh and (len(active) + len(fresh) >= self.draft_batch or queued < self.queue_min):
+            active += fresh
         for k in range(0, len(active), 16):
             grp = active[k:k + 16]
             self.m.draft_step([r.req for r in grp], self.ws_draft)
+            self.drafted += len(grp)
             for r in grp:
                 r.req.draft_idx += 1
                 if r.req.draft_idx == r.x:

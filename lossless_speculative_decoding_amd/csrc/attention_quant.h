@@ -34,6 +34,7 @@ struct QuantArgs {
   int32_t n_req, Hq, Hkv, G, bits, group, split_len, max_splits;
   float scale_log2;
 };
+static_assert(sizeof(QuantArgs) <= 4096, "kernel argument block too large");
 
 // Keys per split of the quantized decode (split_len of QuantArgs, head_dim 128): at most 16
 // token groups (2048 keys at group 128, 1024 at group 64), a multiple of 256, and few enough

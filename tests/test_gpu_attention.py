@@ -119,7 +119,9 @@ def _verify_case(n_req, ctxs, n_rows, cap):
     return Kst, Vst, tks, tvs, q, np.stack(refs)
 
 
-@pytest.mark.parametrize("ctxs,n_rows", [((1500, 2100), 33), ((64, 1), 17), ((0, 130), 3), ((2048,), 1)])
+@pytest.mark.parametrize("ctxs,n_rows", [((1500, 2100), 33), ((64, 1), 17), ((0, 130), 3), ((2048,), 1),
+                                         ((700, 1250), 64),   # 256 query rows: two row groups, the most rows per call
+                                         ((900,), 48)])       # 192 query rows: one full group of 12 row blocks
 def test_verify_attention(ctxs, n_rows):
     need_gpu()
     from lossless_speculative_decoding_amd import VC_BF16, VC_F32, vc_attn_verify
@@ -214,6 +216,7 @@ def test_tokdrop_blob_and_draft_attention():
     [(700, 200, 64, 70)],                                  # kept count off the 64-key grid, tail > 1 tile
     [(1536, 384, 64, 1), (900, 130, 32, 300), (2000, 777, 64, 65)],   # batch with mixed shapes
     [(640, 64, 64, 0), (512, 100, 64, 256)],               # kept = recent only, empty tail; 4-tile tail
+    [(300 + 61 * b, 70 + 13 * b, 64, 9 * b) for b in range(16)],     # the largest batch one call takes
 ])
 def test_draft_decode_ragged_batch(reqs):
     """One-row decode over (kept rows, tail) for a batch of requests of different sizes:

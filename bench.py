@@ -5,8 +5,9 @@ Default workload: the 32-layer Llama-3-8B-shaped random-init decoder (bf16),
 8 requests with 65536-token prompts, a 4x token-dropped draft cache on the GPU,
 the rest of the full KV cache (the dropped prompt rows; the kept rows and the
 committed tail are exact on the GPU) in pinned host memory, staged over PCIe
-only to verify, x = 32, staggered verification.  A step is one scheduler round period: x
-batched draft steps, during which every request is verified about once.
+only to verify, x = 32, staggered verification.  A step is one verification round per
+request: the timed region ends once steps x n verifications have been issued (and then
+completes them), a fixed amount of decoding work whatever the draft batching.
 
 Reported: emitted (lossless) tokens per second over exactly --steps steps,
 the live HIP-event time and algorithmic bytes of the draft-attention kernels
@@ -262,8 +263,11 @@ def main():
     ap.add_argument("--baseline-steps", type=int, default=2)
     ap.add_argument("--draft-batch", type=int, default=0,
                     help="requests yet to draft wait for a batch this large while --queue-min drafted requests are "
-                         "queued for verification (0: half the requests; 1: draft as soon as possible)")
+                         "queued for verification (0: all the requests; 1: draft as soon as possible)")
     ap.add_argument("--queue-min", type=int, default=2)
+    ap.add_argument("--lead", type=int, default=0, help="draft steps before a request's last draft at which its "
+                    "host rows start to stage (0: as soon as its drafting has begun)")
+    ap.add_argument("--slots", type=int, default=2, help="device staging slots")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
@@ -323,7 +327,7 @@ def main():
                             "attention": vc.profile_read(vc.VC_PROF_PREFILL_ATTN), "tokens": T}
         log(f"request {r}: T={T} prefill+compress+offload {time.perf_counter() - t0:.1f}s")
     x_round = max(xs)
-    eng.start(draft_batch=args.draft_batch or None, queue_min=args.queue_min)
+    eng.start(lead=args.lead or None, draft_batch=args.draft_batch or None, queue_min=args.queue_min, n_slots=args.slots)
     t_setup = time.perf_counter() - t_setup
     log(f"setup {t_setup:.1f}s")
 
@@ -333,7 +337,8 @@ def main():
     for k in kinds:
         vc.profile_read(k)
     vc.profile_enable(kinds)
-    eng.run_draft_steps(args.warmup * x_round)
+    n_req = len(eng.reqs)
+    eng.run_rounds(args.warmup * n_req)
     eng.drain()
     warm = vc.profile_read()
     vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
@@ -344,7 +349,7 @@ def main():
     a0 = [len(r.accepts) for r in eng.reqs]
     d0, ds0 = eng.drafted, eng.draft_steps
     t0 = time.perf_counter()
-    eng.run_draft_steps(args.steps * x_round)
+    eng.run_rounds(args.steps * n_req)
     eng.drain()
     torch.cuda.synchronize()
     secs = time.perf_counter() - t0
@@ -453,9 +458,12 @@ def main():
         "full_kv_from_host_tok_s": round(base_tok_s, 3),
         "full_kv_from_host_tokens_match": base_match,
         "speedup_vs_full_kv_from_host": round(tok_s / base_tok_s, 3),
-        "scheduler": {"draft_batch": eng.draft_batch, "queue_min": eng.queue_min,
+        "scheduler": {"draft_batch": eng.draft_batch, "queue_min": eng.queue_min, "lead": eng.lead,
+                      "slots": len(eng.slots),
                       "mean_requests_per_draft_step": round(mean_draft_batch, 2)},
         "mean_accepted_per_round": round(sum(accepts) / max(len(accepts), 1), 3),
+        "rounds": len(accepts),
+        "rounds_per_s": round(len(accepts) / secs, 3),
         "accept_hist": {str(k): hist[k] for k in sorted(hist)},
         "compressed_only_draft_tok_s": round(draft_only, 2),
         "cpu_baseline": cpu,

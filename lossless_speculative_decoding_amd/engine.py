@@ -10,7 +10,8 @@ start drafting at staggered ticks (request r joins after floor(r * x / B)
 ticks, the study note's "10 requests, x = 30: one verification every 3 draft
 rounds"), so one request's transfer and verification overlap the others'
 drafting.  A request's staging is issued `lead` ticks before its draft ends,
-lead = ceil(t_copy / t_tick) (the guide's drafting-horizon sizing rule);
+lead = ceil(t_copy / t_tick) (the guide's drafting-horizon sizing rule; by default
+as soon as its drafting has begun, since one copy outlasts a round of drafts here);
 verification never blocks the compute stream on a copy: the host polls the
 copy event and keeps drafting other requests until the slot is ready.
 
@@ -188,7 +189,7 @@ class Engine:
         self.ws_draft = self.m.workspace(min(n, 16), max_ctx)
         self.ws_verify = self.m.workspace(max_x + 1, max_ctx)
         L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
-        n_slots = min(2, n)
+        n_slots = min(getattr(self, 'n_slots', 2), n)
         slot_rows = max(max(r.n_host for r in self.reqs), 1)
         if not self.slots:
             self.slots = [(torch.empty(L, Hkv, slot_rows, D, dtype=self.dt, device=self.device),
@@ -198,28 +199,34 @@ class Engine:
             self.slot_owner = [None] * n_slots
 
     # ------------------------------------------------------------ the VeriCache loop
-    def start(self, lead: int = 2, stagger: bool = True, draft_batch: int | None = None, queue_min: int = 2):
+    def start(self, lead: int | None = None, stagger: bool = True, draft_batch: int | None = None,
+              queue_min: int = 2, n_slots: int = 2):
         """Allocate slots/workspaces and set the staggered start ticks.
 
+        lead: a request's host rows start to stage once it has begun drafting and is within
+        `lead` draft steps of its last draft.  None (default) stages as soon as drafting has
+        begun: the sizing rule lead = ceil(t_copy / t_tick) gives more than x steps when one
+        request's host rows take longer to copy than x draft steps take to run.
         draft_batch / queue_min: a request that has not begun its x drafts waits while at least
         queue_min drafted requests are queued for verification and fewer than draft_batch
         requests would draft together; drafting is then done in larger batches (fuller draft
         kernels) while the host link, which sets the pace, still always has a drafted request to
-        stage.  draft_batch=1 drafts every request as soon as it can (default: five eighths of them,
-        at most n - queue_min - 1)."""
+        stage.  draft_batch=1 drafts every request as soon as it can (default: all requests).
+        A waiting request holds no slot, so the wait always ends: slot holders are drafting or
+        drafted, and each verification returns a request to the waiting ones."""
+        self.n_slots = max(1, n_slots)
         self._alloc()
         n = len(self.reqs)
         for r in self.reqs:
             r.start_tick = (r.idx * r.x) // n if stagger else 0
             r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
-        self.lead = lead
-        # at most n - queue_min - 1 requests can wait together (queue_min queued, one staging)
-        auto = max(1, min(n // 2 + n // 8, n - queue_min - 1))
-        self.draft_batch = auto if draft_batch is None else max(1, draft_batch)
+        self.lead = max(r.x for r in self.reqs) if lead is None else lead
+        self.draft_batch = n if draft_batch is None else max(1, draft_batch)
         self.queue_min = queue_min
         self.tick = 0
         self.draft_steps = 0
         self.drafted = 0  # request-tokens drafted (sum of the batch over draft steps)
+        self.verifications = 0
 
     def step(self) -> bool:
         """One scheduler iteration: finish accepts, issue staging, one batched
@@ -230,9 +237,11 @@ class Engine:
         for r in reqs:
             if r.phase == ACCEPTING and r.acc_ev.query():
                 self._finish_accept(r)
-        # 2. stage full KV for requests close to the end of their draft
+        # 2. stage full KV for requests close to the end of their draft (only once drafting has
+        # begun: a request still waiting for a fuller draft batch must not hold a slot)
         for r in reqs:
-            if r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= r.x - self.lead and self.tick >= r.start_tick:
+            if (r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= max(1, r.x - self.lead)
+                    and self.tick >= r.start_tick):
                 self._try_stage(r)
         # 3. one batched draft step for every drafting request; requests yet to begin wait for a
         # fuller batch while enough drafted requests are queued for the host link
@@ -281,7 +290,7 @@ class Engine:
     def emitted_total(self) -> int:
         return sum(len(r.emitted) for r in self.reqs)
 
-    def run(self, lead: int = 2, stagger: bool = True, trace: list | None = None):
+    def run(self, lead: int | None = None, stagger: bool = True, trace: list | None = None):
         """Decode every request to its n_tokens; returns wall seconds of the decode phase."""
         self.start(lead, stagger)
         t0 = time.perf_counter()
@@ -298,6 +307,13 @@ class Engine:
         """Run scheduler iterations until n more batched draft steps have executed."""
         target = self.draft_steps + n
         while self.draft_steps < target and any(r.phase != DONE for r in self.reqs):
+            self.step()
+
+    def run_rounds(self, n: int):
+        """Run scheduler iterations until n more verifications have been issued (a fixed
+        amount of decoding work whatever the draft batching; drain() completes them)."""
+        target = self.verifications + n
+        while self.verifications < target and any(r.phase != DONE for r in self.reqs):
             self.step()
 
     def _try_stage(self, r: Request):
@@ -351,6 +367,7 @@ class Engine:
         self.pinned_used = 0
 
     def _verify(self, r: Request, cs):
+        self.verifications += 1
         sk, sv = self.slots[r.slot]
         self.m.verify(r.req, sk, sv, r.rows, r.x + 1, r.verified, r.vtail_k, r.vtail_v, self.ws_verify)
         ev_free = torch.cuda.Event()

@@ -17,7 +17,7 @@ VeriCache round ([VC1] "The Core Idea", pseudocode and worked example;
     commit  : the verifier's exact K/V rows 0..a (pending, draft[0..a-1]) are
               appended to the full KV and to the draft cache's exact tail;
               draft rows are discarded; pending = ver[a]; pos += a + 1
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
     - the verifier's rows, not the draft's, are what the caches keep for accepted tokens;
     - generated rows are never re-compressed: the tail stays in the model dtype;
     - every round drafts a full x, and the output is cut to N at the end;

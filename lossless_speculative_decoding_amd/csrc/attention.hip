@@ -41,7 +41,37 @@ struct DecV {
   u32x4 v[4][4];  // [16-key group a][key 4g + jj within it: jj]
 };
 
-__device__ __forceinline__ int dec_sw(int d) { return (d ^ (d >> 3)) & 7; }
+constexpr int dec_sw(int d) { return (d ^ (d >> 3)) & 7; }
+
+// The kernel forms V^T store and fragment-read addresses as (lane base) ^ (compile-time XOR) +
+// (compile-time offset); this checks that against the layout's definition for every lane and
+// access, and that the lane bases stay inside the wave's 16 KB tile.
+constexpr bool dec_xor_addressing_ok() {
+  for (int r16 = 0; r16 < 16; r16++) {
+    for (int g = 0; g < 4; g++) {
+      const int st_lane = 1024 * r16 + 16 * (g ^ (r16 & 7));
+      const int rd_lane = 128 * r16 + 16 * (g ^ (r16 & 7) ^ (r16 >> 3));
+      for (int q = 0; q < 4; q++) {
+        for (int c = 0; c < 8; c++) {
+          const int d = 8 * r16 + c;
+          const int ref = 2 * (d * ATT_KT + 8 * ((4 * (q >> 1) + g) ^ dec_sw(d)) + 4 * (q & 1));
+          const int got = (st_lane ^ (16 * ((4 * (q >> 1)) ^ c))) + 128 * c + 8 * (q & 1);
+          if (ref != got || (st_lane ^ 112) >= 2 * DEC_TILE) return false;
+        }
+      }
+      for (int kc = 0; kc < 2; kc++) {
+        for (int dt = 0; dt < 8; dt++) {
+          const int d = 16 * dt + r16;
+          const int ref = 2 * (d * ATT_KT + 8 * ((4 * kc + g) ^ dec_sw(d)));
+          const int got = (rd_lane ^ (16 * ((4 * kc) ^ (2 * dt & 6)))) + 2048 * dt;
+          if (ref != got || (rd_lane ^ 112) + 2048 * dt >= 2 * DEC_TILE) return false;
+        }
+      }
+    }
+  }
+  return true;
+}
+static_assert(dec_xor_addressing_ok(), "decode V^T addressing does not match the tile layout");
 
 // The decode kernel numbers keys per tile-aligned segment: segment a occupies logical
 // keys [0, a_al) with a_al = a.n rounded up to 64 (keys a.n .. a_al - 1 are invisible),
@@ -112,18 +142,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = NEG_INF, l_run = 0.f;
   const float sl2 = args.scale_log2;
 
+  // LDS byte offsets of this lane's V^T stores and fragment reads (see the tile layout above):
+  // the swizzle is an XOR, (lane part) ^ (compile-time part), and the tile row a store or read
+  // touches is the lane part plus a compile-time multiple of the row pitch, so each access is
+  // one XOR of a lane base and an immediate offset.  The wave's tile starts on a 16 KB boundary
+  // and the lane bases stay below 16 KB with bits 4-6 clear, so the XOR never carries.
+  //   store (channel d = 8 r16 + c, keys of group 4 (q >> 1) + g, half q & 1):
+  //     1024 r16 + 128 c + 16 ((4 (q >> 1) ^ c) ^ (g ^ (r16 & 7))) + 8 (q & 1)
+  //   read (channel d = 16 dt + r16, 16-byte group 4 kc + g):
+  //     2048 dt + 128 r16 + 16 ((4 kc ^ (2 dt & 6)) ^ (g ^ (r16 & 7) ^ (r16 >> 3)))
+  uint8_t* const lds8 = reinterpret_cast<uint8_t*>(lds);
+  const uint32_t tile_base = uint32_t(wave) * (DEC_TILE * 2);
+  const uint32_t st_lane = tile_base + 1024 * r16 + 16 * (g ^ (r16 & 7));
+  const uint32_t rd_lane = tile_base + 128 * r16 + 16 * (g ^ (r16 & 7) ^ (r16 >> 3));
+  // a tile is wholly visible when it ends at or before key_hi and lies in the visible part of
+  // its segment (segment a's keys below a_n, or segment b)
+  const int a_vis_end = min(a_n, key_hi);
+
   DecK kr;
   DecV vr;
   int t0 = key_lo + ATT_KT * wave;
   if (t0 < key_hi) dec_load(kr, vr, R.a, R.b, a_al, j, t0, off);
   for (; t0 < key_hi; t0 += DEC_WAVES * ATT_KT) {
-    // The LDS addresses below are loop invariant; hoisted out of the loop they would not fit
-    // in registers next to two tiles, and their spill reloads would serialise every tile.
-    // Offsetting the tile base by an opaque zero makes the compiler recompute them (a few
-    // VALU operations per tile).
-    int zero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-    uint16_t* const Vw = Vt + zero;
+    // The lane bases are loop invariant; the twelve XORed addresses hoisted out of the loop would
+    // not fit in registers next to two tiles (their spill reloads would serialise every tile), so
+    // an opaque copy per tile makes the compiler form them again (twelve VALU operations).
+    uint32_t st = st_lane, rd = rd_lane;
+    asm volatile("" : "+v"(st), "+v"(rd));
     // ---- S^T = K Q^T (16 keys x 16 heads per group)
     f32x4 sacc[4];
 #pragma unroll
@@ -135,17 +180,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- V -> fp16, transposed into this wave's LDS tile
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const int grp = 4 * (q >> 1) + g, half = q & 1;
+      const int half = q & 1;
 #pragma unroll
       for (int c = 0; c < 8; c++) {
-        const int d = 8 * r16 + c;
         float x[4];
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) x[jj] = (c & 1) ? hi_bf(vr.v[q][jj][c >> 1]) : lo_bf(vr.v[q][jj][c >> 1]);
         u32x2 w;
         w.x = pack_h2(x[0], x[1]);
         w.y = pack_h2(x[2], x[3]);
-        *reinterpret_cast<u32x2*>(Vw + d * ATT_KT + 8 * (grp ^ dec_sw(d)) + 4 * half) = w;
+        const uint32_t k16 = 16u * uint32_t((4 * (q >> 1)) ^ c);
+        *reinterpret_cast<u32x2*>(lds8 + (st ^ k16) + (128 * c + 8 * half)) = w;
       }
     }
     // ---- next tile in flight while this one finishes (the scheduling barrier keeps the
@@ -154,30 +199,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tn = t0 + DEC_WAVES * ATT_KT;
     if (tn < key_hi) dec_load(kr, vr, R.a, R.b, a_al, j, tn, off);
 
-    // ---- scale, mask, online softmax per head (column l % 16)
-    float mx = NEG_INF;
+    // ---- mask, online softmax per head (column l % 16).  Scores stay unscaled until the
+    // exponent: p = 2^(s * scale_log2 - m), one fma per key; m is kept in scaled (log2) units
+    const bool full = t0 + ATT_KT <= key_hi && (t0 + ATT_KT <= a_vis_end || t0 >= a_al);  // uniform
+    if (!full) {
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
+      for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int t = t0 + 16 * kt + 4 * g + jj;
-        const bool vis = (t < key_hi) & ((t < a_n) | (t >= a_al));
-        const float v = vis ? sacc[kt][jj] * sl2 : NEG_INF;
-        sacc[kt][jj] = v;
-        mx = fmaxf(mx, v);
+        for (int jj = 0; jj < 4; jj++) {
+          const int t = t0 + 16 * kt + 4 * g + jj;
+          const bool vis = (t < key_hi) & ((t < a_n) | (t >= a_al));
+          sacc[kt][jj] = vis ? sacc[kt][jj] : NEG_INF;
+        }
       }
     }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++)
+      mx = fmaxf(mx, fmaxf(fmaxf(sacc[kt][0], sacc[kt][1]), fmaxf(sacc[kt][2], sacc[kt][3])));
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
     // finite: key t0 of a processed tile is always visible (t0 < a_n or a_al <= t0 < key_hi)
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx * sl2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float nb = -m_new;
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kt][jj] - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][jj], sl2, nb));
         sacc[kt][jj] = p;
         rs += p;
       }
@@ -206,8 +257,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const u32x4 pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
-        const int d = 16 * dt + r16;
-        const u32x4 va = *reinterpret_cast<const u32x4*>(Vw + d * ATT_KT + 8 * ((4 * kc + g) ^ dec_sw(d)));
+        const uint32_t c16 = 16u * uint32_t((4 * kc) ^ (2 * dt & 6));
+        const u32x4 va = *reinterpret_cast<const u32x4*>(lds8 + (rd ^ c16) + 2048 * dt);
         oacc[dt] = mfma_f16(va, pb, oacc[dt]);
         oacc[dt] = mfma_f16(va, pl, oacc[dt]);
       }

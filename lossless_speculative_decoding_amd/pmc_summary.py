@@ -39,9 +39,12 @@ def sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def counter_avg(path: str, kernel: str, counter: str) -> tuple[float, int]:
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
+def counter_avg(path: str, kernel: str, counter: str, first: int | None = None) -> tuple[float, int]:
+    """Average of the counter over the kernel's dispatches (the first `first` of them in
+    dispatch order when given)."""
+    rows = sorted((r for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter),
+                  key=lambda r: int(r["Dispatch_Id"]))
+    vals = [float(r["Counter_Value"]) for r in rows[:first]]
     if not vals:
         raise SystemExit(f"no {counter} rows for a kernel named like {kernel!r} in {path}")
     return sum(vals) / len(vals), len(vals)
@@ -56,6 +59,8 @@ def main():
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--algorithmic-bytes", type=float, default=None,
                     help="algorithmic bytes per dispatch over the same dispatches, for the ratio")
+    ap.add_argument("--first", type=int, default=None,
+                    help="only the kernel's first N dispatches (those the algorithmic bytes describe)")
     ap.add_argument("--command", required=True)
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
@@ -63,8 +68,8 @@ def main():
     cw, _ = counter_avg(a.copy_write, COPY_KERNEL, "WRITE_SIZE")
     f_scale = COPY_BYTES / (cf * 1024)
     w_scale = COPY_BYTES / (cw * 1024)
-    kf, nf = counter_avg(a.fetch, a.kernel, "FETCH_SIZE")
-    kw, nw = counter_avg(a.write, a.kernel, "WRITE_SIZE")
+    kf, nf = counter_avg(a.fetch, a.kernel, "FETCH_SIZE", a.first)
+    kw, nw = counter_avg(a.write, a.kernel, "WRITE_SIZE", a.first)
     read = kf * 1024 * f_scale
     written = kw * 1024 * w_scale
     rec = {

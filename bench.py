@@ -6,8 +6,10 @@ Default workload: the 32-layer Llama-3-8B-shaped random-init decoder (bf16),
 the rest of the full KV cache (the dropped prompt rows; the kept rows and the
 committed tail are exact on the GPU) in pinned host memory, staged over PCIe
 only to verify, x = 32, staggered verification.  A step is one verification round per
-request: the timed region ends once steps x n verifications have been issued (and then
-completes them), a fixed amount of decoding work whatever the draft batching.
+request: in the timed region every request issues exactly --steps verifications (rounds
+warmup + 1 .. warmup + steps of each request; a request that is done with them waits),
+and the region ends when they have completed: the same decoding work, and the same
+emitted tokens, whatever the draft batching.
 
 Reported: emitted (lossless) tokens per second over exactly --steps steps,
 the live HIP-event time and algorithmic bytes of the draft-attention kernels
@@ -254,7 +256,7 @@ DISABLED = {
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=16, help="timed scheduler round periods (x draft steps each)")
+    ap.add_argument("--steps", type=int, default=16, help="timed verification rounds per request")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="llama8b_tokdrop",
                     choices=["llama8b_tokdrop", "llama8b_q2", "llama8b_mixed", "gqa_layer"])
@@ -264,10 +266,10 @@ def main():
     ap.add_argument("--draft-batch", type=int, default=0,
                     help="requests yet to draft wait for a batch this large while --queue-min drafted requests are "
                          "queued for verification (0: all the requests; 1: draft as soon as possible)")
-    ap.add_argument("--queue-min", type=int, default=2)
+    ap.add_argument("--queue-min", type=int, default=1)
     ap.add_argument("--lead", type=int, default=0, help="draft steps before a request's last draft at which its "
                     "host rows start to stage (0: as soon as its drafting has begun)")
-    ap.add_argument("--slots", type=int, default=2, help="device staging slots")
+    ap.add_argument("--slots", type=int, default=3, help="device staging slots")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
@@ -338,7 +340,7 @@ def main():
         vc.profile_read(k)
     vc.profile_enable(kinds)
     n_req = len(eng.reqs)
-    eng.run_rounds(args.warmup * n_req)
+    eng.run_rounds_each(args.warmup)
     eng.drain()
     warm = vc.profile_read()
     vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
@@ -349,7 +351,7 @@ def main():
     a0 = [len(r.accepts) for r in eng.reqs]
     d0, ds0 = eng.drafted, eng.draft_steps
     t0 = time.perf_counter()
-    eng.run_rounds(args.steps * n_req)
+    eng.run_rounds_each(args.steps)
     eng.drain()
     torch.cuda.synchronize()
     secs = time.perf_counter() - t0

@@ -103,6 +103,7 @@ class Request:
     slot: int = -1
     stage_ev: object = None
     acc_ev: object = None
+    budget: int = -1                   # verifications it may still issue (-1: unlimited; 0: parked)
 
 
 class Engine:
@@ -200,7 +201,7 @@ class Engine:
 
     # ------------------------------------------------------------ the VeriCache loop
     def start(self, lead: int | None = None, stagger: bool = True, draft_batch: int | None = None,
-              queue_min: int = 2, n_slots: int = 2):
+              queue_min: int = 1, n_slots: int = 3):
         """Allocate slots/workspaces and set the staggered start ticks.
 
         lead: a request's host rows start to stage once it has begun drafting and is within
@@ -211,15 +212,20 @@ class Engine:
         queue_min drafted requests are queued for verification and fewer than draft_batch
         requests would draft together; drafting is then done in larger batches (fuller draft
         kernels) while the host link, which sets the pace, still always has a drafted request to
-        stage.  draft_batch=1 drafts every request as soon as it can (default: all requests).
-        A waiting request holds no slot, so the wait always ends: slot holders are drafting or
-        drafted, and each verification returns a request to the waiting ones."""
+        stage.  draft_batch=1 drafts every request as soon as it can (default: all requests,
+        counting only those not yet done).  A waiting request holds no slot, so the wait always
+        ends: slot holders are drafting or drafted, and each verification returns a request to
+        the waiting ones.
+        n_slots: device staging buffers.  With fuller draft batches several requests finish
+        drafting together; a third slot lets the link stage the next one while two staged
+        requests wait for their verification."""
         self.n_slots = max(1, n_slots)
         self._alloc()
         n = len(self.reqs)
         for r in self.reqs:
             r.start_tick = (r.idx * r.x) // n if stagger else 0
             r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
+            r.budget = -1
         self.lead = max(r.x for r in self.reqs) if lead is None else lead
         self.draft_batch = n if draft_batch is None else max(1, draft_batch)
         self.queue_min = queue_min
@@ -245,11 +251,14 @@ class Engine:
                 self._try_stage(r)
         # 3. one batched draft step for every drafting request; requests yet to begin wait for a
         # fuller batch while enough drafted requests are queued for the host link
-        ready = [r for r in reqs if r.phase == DRAFT and self.tick >= r.start_tick and r.req.draft_idx < r.x]
+        ready = [r for r in reqs
+                 if r.phase == DRAFT and r.budget != 0 and self.tick >= r.start_tick and r.req.draft_idx < r.x]
         active = [r for r in ready if r.req.draft_idx > 0]
         fresh = [r for r in ready if r.req.draft_idx == 0]
         queued = sum(1 for r in reqs if r.phase == WAIT_SLOT)
-        if fresh and (len(active) + len(fresh) >= self.draft_batch or queued < self.queue_min):
+        # requests that will draft again (finished or parked ones never join a batch)
+        live = sum(1 for r in reqs if r.phase != DONE and r.budget != 0)
+        if fresh and (len(active) + len(fresh) >= min(self.draft_batch, live) or queued < self.queue_min):
             active += fresh
         for k in range(0, len(active), 16):
             grp = active[k:k + 16]
@@ -316,6 +325,16 @@ class Engine:
         while self.verifications < target and any(r.phase != DONE for r in self.reqs):
             self.step()
 
+    def run_rounds_each(self, n: int):
+        """Let every unfinished request issue exactly n more verifications (a request that has
+        issued them parks: it neither drafts nor stages); returns once all are issued, and
+        drain() completes them.  Drafts and verifications do not depend on which requests
+        share a draft step, so the tokens these rounds emit do not depend on the schedule."""
+        for r in self.reqs:
+            r.budget = n if r.phase != DONE else 0
+        while any(r.phase != DONE and r.budget > 0 for r in self.reqs):
+            self.step()
+
     def _try_stage(self, r: Request):
         for i in range(len(self.slots)):
             if self.slot_owner[i] is None and (self.slot_free_ev[i] is None or self.slot_free_ev[i].query()):
@@ -368,6 +387,8 @@ class Engine:
 
     def _verify(self, r: Request, cs):
         self.verifications += 1
+        if r.budget > 0:
+            r.budget -= 1
         sk, sv = self.slots[r.slot]
         self.m.verify(r.req, sk, sv, r.rows, r.x + 1, r.verified, r.vtail_k, r.vtail_v, self.ws_verify)
         ev_free = torch.cuda.Event()

@@ -1,0 +1,202 @@
+"""The staggered draft/verify scheduler's host logic, on the CPU.
+
+A fake model stands in for the library (no kernel runs: draft steps, staging,
+verification and accept only record what they were asked to do, and the accept
+count of each round is a fixed function of the request and its round index) and
+fake events complete after a set number of polls, so the scheduling decisions of
+Engine.step run exactly as on the GPU.  Checked for several policies (draft batch,
+queue threshold, slot count, event latency): every request drafts exactly x tokens
+per round, one staging per verification, a slot holds one request at a time, a
+fixed per-request round count ends and gives the same tokens whatever the policy,
+and decoding to the end terminates when requests finish at different times."""
+import pytest
+import torch
+
+from lossless_speculative_decoding_amd import engine as E
+from lossless_speculative_decoding_amd._vc import Req
+from synth.configs import ModelShape
+
+SHAPE = ModelShape(n_layers=1, d_model=128, n_q_heads=1, n_kv_heads=1, head_dim=1, ffn=128, vocab=1 << 20,
+                   rope_theta=10000.0, dtype="fp32")
+
+
+class FakeEvent:
+    lag = 0
+
+    def __init__(self):
+        self.left = FakeEvent.lag
+
+    def record(self, stream=None):
+        self.left = FakeEvent.lag
+
+    def query(self):
+        if self.left > 0:
+            self.left -= 1
+            return False
+        return True
+
+    def synchronize(self):
+        self.left = 0
+
+
+class FakeStream:
+    def synchronize(self):
+        pass
+
+
+def accept_count(idx: int, rnd: int, x: int) -> int:
+    return (3 * idx + 5 * rnd + rnd * rnd) % (x + 1)
+
+
+class FakeModel:
+    shape = SHAPE
+
+    def __init__(self, engine_reqs):
+        self.reqs = engine_reqs        # Request objects, to map a Req back to its request
+        self.batches = []
+        self.log = []                  # (event, request index)
+        self.rounds = {}
+
+    def _idx(self, req):
+        return next(r.idx for r in self.reqs if r.req is req)
+
+    def workspace(self, rows, keys):
+        return None
+
+    def draft_step(self, reqs, ws):
+        assert 1 <= len(reqs) <= 16
+        self.batches.append(len(reqs))
+        for q in reqs:
+            i = self._idx(q)
+            r = self.reqs[i]
+            assert 0 <= q.draft_idx < r.x
+            self.log.append(("draft", i))
+
+    def stage(self, req, sk, sv, l0, l1, copy_stream=None):
+        self.log.append(("stage", self._idx(req)))
+
+    def verify(self, req, sk, sv, rows, n_rows, out, vk, vv, ws):
+        i = self._idx(req)
+        assert req.draft_idx == self.reqs[i].x and n_rows == self.reqs[i].x + 1
+        self.log.append(("verify", i))
+
+    def accept(self, req, verified, x, vk, vv, result):
+        i = self._idx(req)
+        rnd = self.rounds.get(i, 0)
+        self.rounds[i] = rnd + 1
+        a = accept_count(i, rnd, x)
+        result[0] = a
+        result[1:a + 2] = torch.arange(a + 1, dtype=torch.int32) + 1000 * i + 100 * rnd
+
+    def commit(self, req, a, vk, vv, after_event=None, copy_stream=None):
+        req.ctx_len += a + 1
+        req.n_tail += a + 1
+        req.draft_idx = 0
+
+
+def make_engine(monkeypatch, n_req=5, x=4, n_tokens=10_000, lag=0):
+    monkeypatch.setattr(E.torch.cuda, "Event", FakeEvent)
+    monkeypatch.setattr(E.torch.cuda, "current_stream", lambda *a, **k: FakeStream())
+    monkeypatch.setattr(E.torch.cuda, "synchronize", lambda *a, **k: None)
+    FakeEvent.lag = lag
+    eng = E.Engine.__new__(E.Engine)
+    eng.reqs = []
+    eng.m = FakeModel(eng.reqs)
+    eng.spec, eng.shape, eng.dt, eng.chunk, eng.device = None, SHAPE, torch.float32, 1, "cpu"
+    eng.copy_stream = FakeStream()
+    eng.slots, eng.slot_free_ev = [], []
+    eng.ws_draft = eng.ws_verify = None
+    eng.staged_bytes = eng.stagings = 0
+    eng.pinned_budget, eng.pinned_used = 1 << 40, 0
+    eng.pageable_stream = eng.stager = None
+    nt = n_tokens if isinstance(n_tokens, list) else [n_tokens] * n_req
+    for i in range(n_req):
+        r = E.Request(idx=i, T=100 + i, x=x, n_tokens=nt[i])
+        r.n_host = 8
+        r.rows = torch.zeros(x + 1, dtype=torch.int32)
+        r.verified = torch.zeros(x + 1, dtype=torch.int32)
+        r.result = torch.zeros(x + 2, dtype=torch.int32)
+        r.result_host = torch.zeros(x + 2, dtype=torch.int32)
+        r.req = Req(ctx_len=r.T)
+        r.emitted = [7]
+        eng.reqs.append(r)
+    return eng
+
+
+def guard(monkeypatch, eng, limit=20_000):
+    """Fail instead of spinning: at most `limit` scheduler iterations, each checking the slots."""
+    orig = E.Engine.step
+    count = [0]
+
+    def step(self):
+        count[0] += 1
+        assert count[0] < limit, "scheduler made no progress"
+        out = orig(self)
+        owners = [o for o in self.slot_owner if o is not None]
+        assert len(owners) == len(set(owners))
+        for i, o in enumerate(self.slot_owner):
+            if o is not None:
+                assert self.reqs[o].slot == i
+        for r in self.reqs:
+            assert r.slot < 0 or self.slot_owner[r.slot] == r.idx
+        return out
+
+    monkeypatch.setattr(E.Engine, "step", step)
+
+
+POLICIES = [dict(draft_batch=None, queue_min=1, n_slots=3), dict(draft_batch=None, queue_min=2, n_slots=2),
+            dict(draft_batch=None, queue_min=0, n_slots=3), dict(draft_batch=1, queue_min=1, n_slots=1),
+            dict(draft_batch=3, queue_min=1, n_slots=2)]
+
+
+def tokens_of_rounds(monkeypatch, policy, lag, warm=2, rounds=3):
+    eng = make_engine(monkeypatch, lag=lag)
+    guard(monkeypatch, eng)
+    eng.start(**policy)
+    eng.run_rounds_each(warm)
+    eng.drain()
+    assert all(len(r.accepts) == warm for r in eng.reqs)
+    e0 = [len(r.emitted) for r in eng.reqs]
+    eng.run_rounds_each(rounds)
+    eng.drain()
+    assert all(len(r.accepts) == warm + rounds for r in eng.reqs)
+    # every round: x drafts, then one staging and one verification, in that order per request
+    for r in eng.reqs:
+        ev = [e for e, i in eng.m.log if i == r.idx]
+        drafts = 0
+        for e in ev:
+            if e == "draft":
+                drafts += 1
+            elif e == "verify":
+                assert drafts == r.x
+                drafts = 0
+        assert ev.count("verify") == ev.count("stage") == warm + rounds
+    return [r.emitted[n0:] for r, n0 in zip(eng.reqs, e0)], eng.m.batches
+
+
+@pytest.mark.parametrize("lag", [0, 1, 3])
+def test_rounds_each_same_tokens_for_every_policy(monkeypatch, lag):
+    ref = None
+    for p in POLICIES:
+        toks, _ = tokens_of_rounds(monkeypatch, p, lag)
+        ref = ref or toks
+        assert toks == ref, p
+
+
+def test_full_batch_policy_drafts_all_requests_together(monkeypatch):
+    _, batches = tokens_of_rounds(monkeypatch, dict(draft_batch=None, queue_min=0, n_slots=3), lag=1)
+    assert min(batches) == 5  # once every request has started, fresh requests wait for the whole batch
+
+
+@pytest.mark.parametrize("policy", POLICIES)
+def test_run_to_the_end_with_requests_finishing_at_different_times(monkeypatch, policy):
+    eng = make_engine(monkeypatch, n_tokens=[12, 40, 25, 60, 33], lag=1)
+    guard(monkeypatch, eng)
+    eng.start(**policy)
+    while any(r.phase != E.DONE for r in eng.reqs):
+        eng.step()
+    eng.drain()
+    for r in eng.reqs:
+        assert len(r.emitted) >= r.n_tokens
+        assert all(0 <= a <= r.x for a in r.accepts)
+        assert r.emitted[1:] == [1000 * r.idx + 100 * k + i for k, a in enumerate(r.accepts) for i in range(a + 1)]

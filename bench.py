@@ -312,8 +312,12 @@ def main():
     xs = list(w.x)[: len(ctx)]
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
+    # token capacity per request: the workload's count, or more where the measured rounds could
+    # emit more (every round accepting all x drafts), so that no request finishes inside the
+    # timed window and each one runs exactly --steps timed rounds
+    n_cap = max(w.n_tokens, (args.warmup + args.steps) * (max(xs) + 1) + 1)
     W = make_weights(s)
-    model = vc.Model(s, W, max_pos=max(ctx) + w.n_tokens + 64)
+    model = vc.Model(s, W, max_pos=max(ctx) + n_cap + 64)
     eng = Engine(model, w.compress, chunk=2048)
     prefill_prof = None
     for r, (T, x) in enumerate(zip(ctx, xs)):
@@ -322,7 +326,7 @@ def main():
         t0 = time.perf_counter()
         if r == 0:  # request 0's prefill: live timing of its tiled GEMMs and causal attention
             vc.profile_enable((vc.VC_PROF_GEMM_TILED, vc.VC_PROF_PREFILL_ATTN))
-        eng.add_request(p, x, w.n_tokens, keep_prefill_kv=(r == 0))
+        eng.add_request(p, x, n_cap, keep_prefill_kv=(r == 0))
         if r == 0:
             vc.profile_enable(())
             prefill_prof = {"gemm": vc.profile_read(vc.VC_PROF_GEMM_TILED),
@@ -437,7 +441,8 @@ def main():
         "config": {"workload": w.name, "batch": len(ctx), "ctx": ctx if len(set(ctx)) > 1 else ctx[0],
                    "x": xs if len(set(xs)) > 1 else xs[0], "compress": w.compress.kind,
                    "full_kv": "pinned host for the rows the GPU does not hold exactly, staged over PCIe per "
-                              "verification"},
+                              "verification",
+                   "timed_rounds": f"verification rounds {args.warmup + 1}..{args.warmup + args.steps} of every request"},
         "roofline": {"bound": "hbm", "kernel": "draft attention partials (all layers of a draft step)",
                      "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,

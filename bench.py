@@ -6,10 +6,10 @@ Default workload: the 32-layer Llama-3-8B-shaped random-init decoder (bf16),
 the rest of the full KV cache (the dropped prompt rows; the kept rows and the
 committed tail are exact on the GPU) in pinned host memory, staged over PCIe
 only to verify, x = 32, staggered verification.  A step is one verification round per
-request: in the timed region every request issues exactly --steps verifications (rounds
-warmup + 1 .. warmup + steps of each request; a request that is done with them waits),
-and the region ends when they have completed: the same decoding work, and the same
-emitted tokens, whatever the draft batching.
+request: in the timed region every request issues its verification rounds warmup + 1 ..
+warmup + steps (fewer if it reaches the workload's token count first; a request that is
+done with them waits), and the region ends when they have completed: the same decoding
+work, and the same emitted tokens, whatever the draft batching.
 
 Reported: emitted (lossless) tokens per second over exactly --steps steps,
 the live HIP-event time and algorithmic bytes of the draft-attention kernels
@@ -312,10 +312,7 @@ def main():
     xs = list(w.x)[: len(ctx)]
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    # token capacity per request: the workload's count, or more where the measured rounds could
-    # emit more (every round accepting all x drafts), so that no request finishes inside the
-    # timed window and each one runs exactly --steps timed rounds
-    n_cap = max(w.n_tokens, (args.warmup + args.steps) * (max(xs) + 1) + 1)
+    n_cap = w.n_tokens
     W = make_weights(s)
     model = vc.Model(s, W, max_pos=max(ctx) + n_cap + 64)
     eng = Engine(model, w.compress, chunk=2048)
@@ -442,7 +439,8 @@ def main():
                    "x": xs if len(set(xs)) > 1 else xs[0], "compress": w.compress.kind,
                    "full_kv": "pinned host for the rows the GPU does not hold exactly, staged over PCIe per "
                               "verification",
-                   "timed_rounds": f"verification rounds {args.warmup + 1}..{args.warmup + args.steps} of every request"},
+                   "timed_rounds": f"verification rounds {args.warmup + 1}..{args.warmup + args.steps} of every "
+                                   f"request, up to its {w.n_tokens}th token"},
         "roofline": {"bound": "hbm", "kernel": "draft attention partials (all layers of a draft step)",
                      "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,

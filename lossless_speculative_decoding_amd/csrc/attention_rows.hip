@@ -95,13 +95,13 @@ __device__ __forceinline__ TileMix tile_mix(const AttnReq& R, int j, int t0) {
 
 __device__ __forceinline__ const uint16_t* mixed_row(const AttnReq& R, int j, int t0, int o, const TileMix& x,
                                                      bool is_v) {
+  // lanes of one load take rows from both buffers: select the address (no divergent branch)
   const int below = __popcll(x.m & ((uint64_t(1) << o) - 1));
-  if ((x.m >> o) & 1) {
-    const uint16_t* base = static_cast<const uint16_t*>(is_v ? R.mix.v : R.mix.k);
-    return base + j * R.mix.hstride + int64_t(x.c + below) * D128;
-  }
-  const uint16_t* base = static_cast<const uint16_t*>(is_v ? R.a.v : R.a.k);
-  return base + j * R.a.hstride + int64_t(t0 - x.c + o - below) * D128;
+  const bool kept = (x.m >> o) & 1;
+  const uint16_t* kb = static_cast<const uint16_t*>(is_v ? R.mix.v : R.mix.k) + j * R.mix.hstride;
+  const uint16_t* sb = static_cast<const uint16_t*>(is_v ? R.a.v : R.a.k) + j * R.a.hstride;
+  const int row = kept ? x.c + below : t0 - x.c + o - below;
+  return (kept ? kb : sb) + int64_t(row) * D128;
 }
 
 // K: thread (kr = tid/16, ch = tid%16) loads 16-byte chunk ch of keys kr + 16e (e = 0..3):

@@ -13,6 +13,12 @@ Token drop by observed attention (SnapKV-like; the rule of the token-drop worklo
     keep     = top-(K - R) candidates by s (ties: smaller t), plus [T-R, T), ascending.
     If every candidate fits, nothing is dropped.
 
+Token drop by key norm ([VC2] "The Uniform Compressor Interface": its example
+compressor ranks tokens by key energy)
+    per layer l: e[t] = mean over the KV heads j of ||k[l,j,t]||_2 (one ranking shared by
+    every head of the layer); keep = the max(32, T // ratio) tokens of largest e (ties:
+    smaller t), ascending; no recent window.  If every token fits, nothing is dropped.
+
 Per-group asymmetric quantization (KIVI-style: K per channel, V per token)
     b in {2,3,4}, group G, Tq = floor(T/G)*G; rows [Tq, T) stay unquantized.
     For each group, in IEEE float32:
@@ -37,7 +43,9 @@ Bitstreams are little-endian: stream bit n is bit (n mod 8) of byte floor(n/8).
 Pins (tests/test_oracle_compress.py): constant groups, exactly representable
 ramps, the reconstruction bound, brute-force nearest-code search, a literal
 packed-byte fixture, T <= K keeping everything, one-hot crafted attention
-giving a known keep set, and a brute-force full sort for the top-k.
+giving a known keep set, and a brute-force full sort for the top-k; for the
+key-norm ranking, keys of known norms, heads that disagree (the mean decides),
+a per-token norm recomputed by a plain loop, and the shared per-layer set.
 """
 from __future__ import annotations
 
@@ -102,6 +110,29 @@ def tokdrop(Kf: np.ndarray, Vf: np.ndarray, q_obs: np.ndarray, keep_total: int, 
     Kk = np.take_along_axis(Kf, idx[..., None].astype(np.int64), axis=2)
     Vk = np.take_along_axis(Vf, idx[..., None].astype(np.int64), axis=2)
     return idx, Kk, Vk, scores
+
+
+def keynorm_scores(K: np.ndarray) -> np.ndarray:
+    """K [Hkv][T][D] of one layer.  e[t] = mean over heads of the L2 norm of key t."""
+    K = np.asarray(K, dtype=np.float64)
+    return np.sqrt((K * K).sum(axis=-1)).mean(axis=0)
+
+
+def tokdrop_keynorm(Kf: np.ndarray, Vf: np.ndarray, keep_total: int):
+    """Kf, Vf [L][Hkv][T][D].  Returns (idx [L][Hkv][Kk], Kk, Vk, scores [L][T]): per layer
+    the top-keep_total tokens by key norm (ties to the smaller index), ascending, the same
+    positions for every KV head of the layer."""
+    L, H, T, D = Kf.shape
+    idx, scores = [], []
+    for l in range(L):
+        e = keynorm_scores(Kf[l])
+        sel = tokdrop_select(e, T, keep_total, 0)
+        idx.append([sel] * H)
+        scores.append(e)
+    idx = np.asarray(idx, dtype=np.int32)
+    Kk = np.take_along_axis(Kf, idx[..., None].astype(np.int64), axis=2)
+    Vk = np.take_along_axis(Vf, idx[..., None].astype(np.int64), axis=2)
+    return idx, Kk, Vk, np.asarray(scores)
 
 
 # --------------------------------------------------------------------------

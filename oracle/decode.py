@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .compress import Quantized, tokdrop
+from .compress import Quantized, tokdrop, tokdrop_keynorm
 from .kvcache import FixedRows, RowStore, chain
 from .model import Weights, argmax, row_forward
 
@@ -109,6 +109,16 @@ def draft_cache_tokdrop(pre: Prefill, W: Weights, keep_total: int, keep_recent: 
     Kf = pre.full.K[:, :, :n]
     Vf = pre.full.V[:, :, :n]
     idx, Kk, Vk, _scores = tokdrop(Kf, Vf, pre.q_obs, keep_total, keep_recent, W.shape.group)
+    return FixedRows([[Kk[l, j] for j in range(H)] for l in range(L)],
+                     [[Vk[l, j] for j in range(H)] for l in range(L)])
+
+
+def draft_cache_keynorm(pre: Prefill, W: Weights, keep_total: int, **_):
+    """Token drop ranked by key norm: per layer, the keep_total prompt rows of largest mean key
+    norm over the KV heads ([VC2] "The Uniform Compressor Interface")."""
+    L, H = W.shape.n_layers, W.shape.n_kv_heads
+    n = pre.full.n
+    idx, Kk, Vk, _scores = tokdrop_keynorm(pre.full.K[:, :, :n], pre.full.V[:, :, :n], keep_total)
     return FixedRows([[Kk[l, j] for j in range(H)] for l in range(L)],
                      [[Vk[l, j] for j in range(H)] for l in range(L)])
 

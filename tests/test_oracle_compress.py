@@ -151,3 +151,49 @@ def test_tokdrop_gather():
         assert np.all(np.diff(idx[0, j]) > 0)
         assert np.array_equal(Kk[0, j], K[0, j, idx[0, j]])
         assert idx[0, j, -8:].tolist() == list(range(56, 64))
+
+
+# ------------------------------------------------------------------ token drop by key norm
+def test_keynorm_known_norms_and_shared_set():
+    """Every head's key t has norm 1 + t mod 7 (in a different channel per head): the largest
+    norms are known, ties go to the smaller position, and every head keeps the same set."""
+    from oracle.compress import tokdrop_keynorm
+    L, H, T, D = 2, 3, 40, 4
+    K = np.zeros((L, H, T, D))
+    for t in range(T):
+        for j in range(H):
+            K[:, j, t, j] = 1 + t % 7
+    V = np.arange(L * H * T * D, dtype=float).reshape(L, H, T, D)
+    idx, Kk, Vk, e = tokdrop_keynorm(K, V, keep_total=8)
+    # norm 7 at t = 6, 13, 20, 27, 34 (five tokens), then norm 6 at t = 5, 12, 19, 26, 33: the
+    # three smallest positions of those take the remaining places
+    assert idx[0, 0].tolist() == [5, 6, 12, 13, 19, 20, 27, 34]
+    assert all(idx[l, j].tolist() == idx[0, 0].tolist() for l in range(L) for j in range(H))
+    assert np.array_equal(Vk[1, 2], V[1, 2, idx[1, 2]])
+    assert np.allclose(e[0], 1 + np.arange(T) % 7)
+
+
+def test_keynorm_mean_over_heads_decides():
+    """Head 0 prefers token 0, head 1 prefers token 1; token 1's mean norm is larger."""
+    from oracle.compress import keynorm_scores, tokdrop_keynorm
+    K = np.zeros((1, 2, 3, 2))
+    K[0, 0, 0] = [3.0, 4.0]     # norm 5
+    K[0, 1, 0] = [0.0, 1.0]     # norm 1   -> mean 3
+    K[0, 0, 1] = [0.0, 2.0]     # norm 2
+    K[0, 1, 1] = [6.0, 0.0]     # norm 6   -> mean 4
+    K[0, :, 2] = [1.0, 0.0]     #          -> mean 1
+    assert keynorm_scores(K[0]).tolist() == [3.0, 4.0, 1.0]
+    idx, _, _, _ = tokdrop_keynorm(K, K, keep_total=1)
+    assert idx[0, 0].tolist() == [1] and idx[0, 1].tolist() == [1]
+
+
+def test_keynorm_plain_loop_and_keep_all():
+    from oracle.compress import keynorm_scores, tokdrop_keynorm
+    rng = np.random.default_rng(5)
+    K = rng.normal(size=(3, 17, 6))
+    e = keynorm_scores(K)
+    for t in range(17):
+        norms = [math.sqrt(sum(K[j, t, d] ** 2 for d in range(6))) for j in range(3)]
+        assert abs(e[t] - sum(norms) / 3) < 1e-12
+    idx, _, _, _ = tokdrop_keynorm(K[None], K[None], keep_total=40)
+    assert idx[0, 1].tolist() == list(range(17))

@@ -26,11 +26,12 @@ def tiny():
 
 
 @pytest.mark.parametrize("x", range(1, 9))
-@pytest.mark.parametrize("kind", ["tokdrop", "quant2", "quant4", "identity"])
+@pytest.mark.parametrize("kind", ["tokdrop", "keynorm", "quant2", "quant4", "identity"])
 def test_vericache_equals_greedy(tiny, x, kind):
     W, p, pre, ref = tiny
     mk = {
         "tokdrop": lambda pr: D.draft_cache_tokdrop(pr, W, keep_total=12, keep_recent=4),
+        "keynorm": lambda pr: D.draft_cache_keynorm(pr, W, keep_total=10),
         "quant2": lambda pr: D.draft_cache_quant(pr, W, bits=2, group=8),
         "quant4": lambda pr: D.draft_cache_quant(pr, W, bits=4, group=8),
         "identity": D.draft_cache_identity,

@@ -270,6 +270,10 @@ def main():
     ap.add_argument("--lead", type=int, default=0, help="draft steps before a request's last draft at which its "
                     "host rows start to stage (0: as soon as its drafting has begun)")
     ap.add_argument("--slots", type=int, default=3, help="device staging slots")
+    ap.add_argument("--score", choices=["attn", "keynorm"], default="attn",
+                    help="token-drop ranking: observed attention (the workload's) or key norm (the pages' example "
+                         "compressor: no recent window)")
+    ap.add_argument("--ratio", type=int, default=0, help="token-drop compression ratio (0: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
@@ -303,6 +307,14 @@ def main():
     if args.config in DISABLED:
         sys.exit(f"bench.py: workload {args.config} is disabled: {DISABLED[args.config]}")
     w = configs.ALL[args.config]()
+    if w.compress.kind == "tokdrop" and (args.score != "attn" or args.ratio):
+        import dataclasses
+        ratio = args.ratio or w.compress.ratio
+        spec = dataclasses.replace(w.compress, score=args.score, ratio=ratio,
+                                   keep_recent=0 if args.score == "keynorm" else w.compress.keep_recent)
+        name = w.name.replace(f"tokdrop{w.compress.ratio}x", f"tokdrop{ratio}x" + ("_keynorm" if args.score ==
+                                                                                       "keynorm" else ""))
+        w = dataclasses.replace(w, compress=spec, name=name)
     s = w.model
     ctx = list(w.ctx)
     if args.ctx:
@@ -414,7 +426,33 @@ def main():
     n_cmp = min(len(toks), len(r0.emitted) - 1)
     base_match = toks[:n_cmp] == r0.emitted[1:1 + n_cmp]
     log(f"full-KV-from-host greedy: {base_tok_s:.2f} tok/s; its {n_cmp} tokens match VeriCache's: {base_match}")
+    # resident full-KV greedy (context only: the workload keeps the full cache on the host): request
+    # 0 alone with its whole cache in HBM, one vc_verify row per token appended in place
+    from lossless_speculative_decoding_amd._vc import Req
+    n_res = 16
+    cap = r0.T + n_res + 1
+    kd = torch.empty(s.n_layers, s.n_kv_heads, cap, s.head_dim, dtype=r0.prefill_kv[0].dtype, device="cuda")
+    vd = torch.empty_like(kd)
+    kd[:, :, :r0.T].copy_(r0.prefill_kv[0][:, :, :r0.T])
+    vd[:, :, :r0.T].copy_(r0.prefill_kv[1][:, :, :r0.T])
     del r0.prefill_kv
+    res_rows = torch.empty(n_res + 1, dtype=torch.int32, device="cuda")
+    res_rows[:1].copy_(first)
+    rreq = Req(ctx_len=r0.T)
+    row_b = s.head_dim * kd.element_size()
+    torch.cuda.synchronize()
+    t_r = time.perf_counter()
+    for i in range(n_res):
+        rreq.ctx_len = r0.T + i
+        off = rreq.ctx_len * row_b
+        model.verify_raw(rreq, kd.data_ptr(), vd.data_ptr(), cap, res_rows.data_ptr() + 4 * i, 1,
+                         res_rows.data_ptr() + 4 * (i + 1), kd.data_ptr() + off, vd.data_ptr() + off, cap, eng.ws_verify)
+    torch.cuda.synchronize()
+    res_tok_s = n_res / (time.perf_counter() - t_r)
+    n_rc = min(n_res, len(r0.emitted) - 1)
+    res_match = res_rows[1:1 + n_rc].tolist() == r0.emitted[1:1 + n_rc]
+    del kd, vd
+    log(f"resident full-KV greedy (one request, context): {res_tok_s:.1f} tok/s; tokens match VeriCache's: {res_match}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -436,7 +474,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded random-init weights and uniform prompt ids)",
         "config": {"workload": w.name, "batch": len(ctx), "ctx": ctx if len(set(ctx)) > 1 else ctx[0],
-                   "x": xs if len(set(xs)) > 1 else xs[0], "compress": w.compress.kind,
+                   "x": xs if len(set(xs)) > 1 else xs[0],
+                   "compress": w.compress.kind + ("" if w.compress.kind != "tokdrop" else
+                                                  f" {w.compress.ratio}x by {w.compress.score}"),
                    "full_kv": "pinned host for the rows the GPU does not hold exactly, staged over PCIe per "
                               "verification",
                    "timed_rounds": f"verification rounds {args.warmup + 1}..{args.warmup + args.steps} of every "
@@ -462,6 +502,9 @@ def main():
                  "note": "host rows staged for verification in the timed region / its wall time"},
         "full_kv_from_host_tok_s": round(base_tok_s, 3),
         "full_kv_from_host_tokens_match": base_match,
+        "resident_full_kv_greedy_tok_s": round(res_tok_s, 2),
+        "resident_full_kv_note": "context only: request 0 alone with its whole cache in HBM (the workload keeps it "
+                                 "on the host); tokens match VeriCache's: " + str(res_match),
         "speedup_vs_full_kv_from_host": round(tok_s / base_tok_s, 3),
         "scheduler": {"draft_batch": eng.draft_batch, "queue_min": eng.queue_min, "lead": eng.lead,
                       "slots": len(eng.slots),

@@ -63,6 +63,9 @@ typedef int32_t vc_status;
 
 #define VC_TOKDROP 1
 #define VC_QUANT 2
+/* token-drop ranking (vc_compress_desc.score) */
+#define VC_SCORE_ATTN 0    /* observed attention of the last obs_window prompt queries */
+#define VC_SCORE_KEYNORM 1 /* key norm ("The Uniform Compressor Interface" example)     */
 
 #define VC_MAX_BATCH 16 /* requests per vc_draft_step / vc_attn_* call */
 
@@ -124,6 +127,13 @@ vc_status vc_ws_size(const vc_model* m, int32_t max_rows, int32_t max_keys, size
  *   cnt + (kept below it in the tile) when kept, else dropped row
  *   t - cnt - (kept below it): the compacted order in which the host holds the
  *   dropped rows (vc_offload) and verification stages them.
+ *   score = VC_SCORE_KEYNORM ranks by key norm instead ([VC2] "The Uniform
+ *   Compressor Interface", its example compressor): per layer, e[t] = mean over
+ *   the KV heads of ||k_t||_2 in float32 (channels summed in order, heads in
+ *   order), one ranking shared by every head of the layer; the top
+ *   keep_total - R rows by e (ties to the smaller index) plus the last R rows
+ *   (R = keep_recent, 0 for the pages' rule), same blob; q_obs is not read and
+ *   obs_window is ignored.
  * VC_QUANT: b in {2,3,4} bits, group G in {64,128}, Tq = floor(T/G)*G.
  *   K per channel (groups of G tokens), V per token (groups of G channels):
  *   zero = fp16(min), scale = fp16((max - min) / (2^b - 1)),
@@ -143,6 +153,7 @@ typedef struct {
   int32_t keep_total, keep_recent, obs_window; /* VC_TOKDROP                       */
   int32_t n_layers, n_q_heads, n_kv_heads, head_dim, seq_len, dtype;
   int32_t src_cap; /* row pitch (rows) of the input K/V per (layer, head) */
+  int32_t score;   /* VC_TOKDROP ranking: VC_SCORE_ATTN | VC_SCORE_KEYNORM */
 } vc_compress_desc;
 
 /* Byte offsets of the sections of a compressed blob. */

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvc.so")
 VC_OK, VC_ERR_ARG, VC_ERR_UNSUPPORTED, VC_ERR_CAPACITY, VC_ERR_HIP = 0, -1, -2, -3, -4
 VC_F32, VC_BF16 = 0, 1
 VC_TOKDROP, VC_QUANT = 1, 2
+VC_SCORE_ATTN, VC_SCORE_KEYNORM = 0, 1
 VC_MAX_BATCH = 16
 (VC_PROF_DRAFT_ATTN, VC_PROF_VERIFY_ATTN, VC_PROF_GEMM_SKINNY, VC_PROF_GEMM_TILED,
  VC_PROF_PREFILL_ATTN) = range(5)
@@ -40,7 +41,7 @@ class Weights(C.Structure):
 class CompressDesc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("kind", "bits", "group", "keep_total", "keep_recent", "obs_window",
                                          "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "seq_len", "dtype",
-                                         "src_cap")]
+                                         "src_cap", "score")]
 
 
 class CompressLayout(C.Structure):

@@ -12,10 +12,11 @@ import torch
 
 from . import _vc
 from ._vc import (VC_BF16, VC_F32, VC_PROF_DRAFT_ATTN, VC_PROF_GEMM_SKINNY, VC_PROF_GEMM_TILED,
-                  VC_PROF_PREFILL_ATTN, VC_PROF_VERIFY_ATTN, VC_QUANT, VC_TOKDROP, AttnDesc, AttnDraftReq,
+                  VC_PROF_PREFILL_ATTN, VC_PROF_VERIFY_ATTN, VC_QUANT, VC_SCORE_ATTN, VC_SCORE_KEYNORM, VC_TOKDROP,
+                  AttnDesc, AttnDraftReq,
                   CompressDesc, CompressLayout, ModelDesc, ProfileStats, Req, Weights, call)
 
-__all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "CompressDesc", "Req", "Model", "compress_desc",
+__all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "VC_SCORE_ATTN", "VC_SCORE_KEYNORM", "CompressDesc", "Req", "Model", "compress_desc",
            "compress_layout", "vc_compress", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
            "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes",
            "profile_enable", "profile_read", "HostBuffer", "PageableBuffer", "VC_PROF_DRAFT_ATTN",
@@ -46,10 +47,10 @@ def elem_bytes(vc_dtype: int) -> int:
 # ---------------------------------------------------------------- compression
 def compress_desc(kind: int, n_layers: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
                   dtype: int, src_cap: int | None = None, bits: int = 0, group: int = 0, keep_total: int = 0,
-                  keep_recent: int = 64, obs_window: int = 32) -> CompressDesc:
+                  keep_recent: int = 64, obs_window: int = 32, score: int = 0) -> CompressDesc:
     return CompressDesc(kind=kind, bits=bits, group=group, keep_total=keep_total, keep_recent=keep_recent,
                         obs_window=obs_window, n_layers=n_layers, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
-                        head_dim=head_dim, seq_len=seq_len, dtype=dtype, src_cap=src_cap or seq_len)
+                        head_dim=head_dim, seq_len=seq_len, dtype=dtype, src_cap=src_cap or seq_len, score=score)
 
 
 def compress_layout(d: CompressDesc) -> CompressLayout:

@@ -1,5 +1,5 @@
 // Compressors ("The Uniform Compressor Interface", VeriCache Guide): per-group
-// quantization with bit packing, and token dropping by observed attention.
+// quantization with bit packing, and token dropping by observed attention or by key norm.
 //
 // Quantization arithmetic is IEEE float32 step by step (no contraction) so
 // that codes, scales and zeros are bit-identical to the reference definition:
@@ -317,6 +317,28 @@ __global__ void gather_rows_kernel(const uint8_t* src, int src_cap, int row_byte
 
 // Per (layer*head, 64-position tile): bit o of mask = position 64*tile + o is kept;
 // cnt = kept positions before the tile (idx is ascending, so a binary search finds it).
+// Key-norm ranking: thread t of layer blockIdx.y sums k^2 over the channels of each KV head
+// in order, takes the square root and averages over the heads in order; the score is written
+// to every head's row so that each head's selection is the layer's one.
+__global__ void keynorm_scores_kernel(const void* k, int dtype, int src_cap, int D, int Hkv, int n_cand,
+                                      float* scores) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int l = blockIdx.y;
+  if (t >= n_cand) return;
+  float e = 0.f;
+  for (int j = 0; j < Hkv; j++) {
+    const int64_t base = (int64_t(l * Hkv + j) * src_cap + t) * D;
+    float ss = 0.f;
+    for (int d = 0; d < D; d++) {
+      const float x = load_elem(k, base + d, dtype);
+      ss = __fmaf_rn(x, x, ss);
+    }
+    e += __fsqrt_rn(ss);
+  }
+  e = __fdiv_rn(e, float(Hkv));
+  for (int j = 0; j < Hkv; j++) scores[int64_t(l * Hkv + j) * n_cand + t] = e;
+}
+
 __global__ void keep_tiles_kernel(const int32_t* idx, int kk, int n_lh, int n_tiles, uint64_t* mask, int32_t* cnt) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= int64_t(n_lh) * n_tiles) return;
@@ -372,7 +394,10 @@ vc_status compress_layout(const vc_compress_desc* d, vc_compress_layout* L) {
     return o;
   };
   if (d->kind == VC_TOKDROP) {
-    VC_REQUIRE(d->keep_recent >= 0 && d->keep_total > 0 && d->obs_window > 0, VC_ERR_ARG, "tokdrop: bad knobs");
+    VC_REQUIRE(d->score == VC_SCORE_ATTN || d->score == VC_SCORE_KEYNORM, VC_ERR_ARG, "tokdrop: bad score %d",
+               d->score);
+    VC_REQUIRE(d->keep_recent >= 0 && d->keep_total > 0 && (d->obs_window > 0 || d->score == VC_SCORE_KEYNORM),
+               VC_ERR_ARG, "tokdrop: bad knobs");
     const int64_t nrec = std::min<int64_t>(d->keep_recent, T);
     const int64_t kk = std::min<int64_t>(T, std::max<int64_t>(d->keep_total, nrec));
     L->n_main = int32_t(kk);
@@ -413,6 +438,10 @@ vc_status compress_ws_bytes(const vc_compress_desc* d, size_t* ws) {
   if (d->kind != VC_TOKDROP) return VC_OK;
   const int64_t LH = int64_t(d->n_layers) * d->n_kv_heads;
   const int64_t T = d->seq_len, D = d->head_dim;
+  if (d->score == VC_SCORE_KEYNORM) {
+    *ws = align256(LH * T * 4);  // scores only
+    return VC_OK;
+  }
   const int64_t W = std::min<int64_t>(d->obs_window, T);
   const int64_t split = 1024;
   const int64_t S = cdiv(T, split);
@@ -479,6 +508,15 @@ vc_status compress_run(const vc_compress_desc* d, const void* k, const void* v, 
     // everything fits: keep all rows
     const int64_t n = int64_t(n_lh) * kk;
     hipLaunchKernelGGL(iota_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, idx, n_lh, kk);
+    VC_LAUNCH_CHECK();
+  } else if (d->score == VC_SCORE_KEYNORM) {
+    VC_REQUIRE(ws != nullptr && ws_bytes >= need, VC_ERR_CAPACITY, "vc_compress: workspace %zu < %zu", ws_bytes, need);
+    float* scores = static_cast<float*>(ws);
+    hipLaunchKernelGGL(keynorm_scores_kernel, dim3(cdiv(n_cand, 256), d->n_layers), dim3(256), 0, s, k, d->dtype,
+                       d->src_cap, D, d->n_kv_heads, n_cand, scores);
+    VC_LAUNCH_CHECK();
+    hipLaunchKernelGGL(topk_select_kernel, dim3(n_lh), dim3(SEL_THREADS), 0, s, scores, n_cand, n_top, n_recent, kk,
+                       idx);
     VC_LAUNCH_CHECK();
   } else {
     VC_REQUIRE(q_obs != nullptr, VC_ERR_ARG, "vc_compress: token drop needs q_obs");

@@ -64,6 +64,11 @@ def make_weights(shape, device="cuda", seed: int = 0) -> dict:
 
 def compress_spec_desc(spec, shape, T: int, src_cap: int):
     dt = B.VC_BF16 if shape.dtype == "bf16" else B.VC_F32
+    if spec.kind == "tokdrop" and spec.score == "keynorm":
+        # the pages' example compressor: keep max(32, T // ratio) tokens, no recent window of its own
+        return B.compress_desc(B.VC_TOKDROP, shape.n_layers, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, T, dt,
+                               src_cap=src_cap, keep_total=max(32, T // spec.ratio), keep_recent=spec.keep_recent,
+                               obs_window=0, score=B.VC_SCORE_KEYNORM)
     if spec.kind == "tokdrop":
         return B.compress_desc(B.VC_TOKDROP, shape.n_layers, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, T, dt,
                                src_cap=src_cap, keep_total=T // spec.ratio, keep_recent=spec.keep_recent,

@@ -45,6 +45,7 @@ class CompressSpec:
     keep_recent: int = 64
     ratio: int = 4        # token drop keeps T // ratio rows
     obs_window: int = 32
+    score: str = "attn"   # token-drop ranking: "attn" (observed attention) | "keynorm"
 
 
 @dataclass(frozen=True)

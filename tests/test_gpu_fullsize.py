@@ -158,3 +158,48 @@ def test_tokdrop_decode_at_8b_sizes_sampled():
         err = row_rel_err(host_f64(out[b, j * G:(j + 1) * G]), ref)
         log(f"token-drop decode request {b} head {j}: rel err {err:.2e}")
         assert err <= TOL_BF16
+
+
+def test_keynorm_kept_set_at_8b_sizes():
+    """Key-norm token drop of one 8B-shaped layer (8 KV heads, a ragged 65499-row prompt, keep a
+    quarter): the kept set against the float64 oracle (differences only where the float32 and
+    float64 rankings meet at a near-tie), the same set for every head, the kept rows gathered,
+    and the tile map consistent with the indices."""
+    need_gpu()
+    from lossless_speculative_decoding_amd import (VC_BF16, VC_SCORE_KEYNORM, VC_TOKDROP, compress_desc,
+                                                   compress_layout, vc_compress)
+    T = 65499
+    keep = T // 4
+    K = _gen((1, HKV, T, D), synth.S_ATT_K)
+    V = _gen((1, HKV, T, D), synth.S_ATT_V)
+    d = compress_desc(VC_TOKDROP, 1, HQ, HKV, D, T, VC_BF16, keep_total=keep, keep_recent=0, obs_window=0,
+                      score=VC_SCORE_KEYNORM)
+    blob = vc_compress(d, K, V)
+    torch.cuda.synchronize()
+    lay = compress_layout(d)
+    assert lay.n_main == keep and lay.n_host == T - keep
+    idx = blob[lay.idx: lay.idx + HKV * keep * 4].cpu().numpy().view(np.int32).reshape(HKV, keep)
+    assert all(np.array_equal(idx[j], idx[0]) for j in range(HKV))
+    assert np.all(np.diff(idx[0]) > 0) and idx[0, 0] >= 0 and idx[0, -1] < T
+    f = lambda bits: synth.bf16_bits_to_f32(bits).astype(np.float64)
+    Kh = np.stack([f(synth.att_head(synth.S_ATT_K, 0, j, T, HKV, D)) for j in range(HKV)])
+    widx, _, _, e = OC.tokdrop_keynorm(Kh[None], Kh[None], keep)
+    e = e[0]
+    kth = np.sort(e)[::-1][keep - 1]
+    got, want = set(idx[0].tolist()), set(widx[0, 0].tolist())
+    for t in got ^ want:
+        assert abs(e[t] - kth) <= 1e-5 * kth, (t, e[t], kth)
+    log(f"key-norm kept set equal to the oracle's up to {len(got ^ want) // 2} near-ties")
+    j = 5
+    kk = blob[lay.k_main + j * keep * D * 2: lay.k_main + (j + 1) * keep * D * 2].cpu().numpy().view(np.uint16)
+    assert np.array_equal(kk.reshape(keep, D), K[0, j].cpu().view(torch.int16).numpy().view(np.uint16)[idx[j]])
+    nt = lay.n_tiles
+    mask = blob[lay.keep_mask: lay.keep_mask + HKV * nt * 8].cpu().numpy().view(np.uint64).reshape(HKV, nt)
+    cnt = blob[lay.keep_cnt: lay.keep_cnt + HKV * nt * 4].cpu().numpy().view(np.int32).reshape(HKV, nt)
+    kept = np.zeros(T, dtype=bool)
+    kept[idx[3]] = True
+    for tile in (0, 17, nt - 1):
+        bits = [(int(mask[3, tile]) >> o) & 1 for o in range(64)]
+        pos = [64 * tile + o for o in range(64) if 64 * tile + o < T]
+        assert [bool(bits[p - 64 * tile]) for p in pos] == kept[pos].tolist()
+        assert cnt[3, tile] == kept[: 64 * tile].sum()

@@ -87,8 +87,10 @@ def test_greedy_tokens_and_logits(setup):
 
 
 @pytest.mark.parametrize("spec", [CompressSpec("tokdrop", keep_recent=64, ratio=4, obs_window=32),
+                                  CompressSpec("tokdrop", keep_recent=0, ratio=4, score="keynorm"),
                                   CompressSpec("quant", bits=2, group=64), CompressSpec("quant", bits=3, group=128),
-                                  CompressSpec("quant", bits=4, group=128)], ids=["tokdrop", "q2g64", "q3g128", "q4g128"])
+                                  CompressSpec("quant", bits=4, group=128)],
+                         ids=["tokdrop", "keynorm", "q2g64", "q3g128", "q4g128"])
 def test_vericache_equals_gpu_greedy(setup, spec):
     from lossless_speculative_decoding_amd.engine import Engine
     eng = Engine(setup["m"], spec, chunk=256)
@@ -100,7 +102,8 @@ def test_vericache_equals_gpu_greedy(setup, spec):
 
 
 @pytest.mark.parametrize("spec", [CompressSpec("tokdrop", keep_recent=64, ratio=4, obs_window=32),
-                                  CompressSpec("quant", bits=3, group=128)], ids=["tokdrop", "q3g128"])
+                                  CompressSpec("tokdrop", keep_recent=0, ratio=4, score="keynorm"),
+                                  CompressSpec("quant", bits=3, group=128)], ids=["tokdrop", "keynorm", "q3g128"])
 def test_split_full_kv_verify_is_bitwise_plain(setup, spec):
     """A request with a compressed cache verifies over its full KV split between the
     host rows (staged), the kept prompt rows (token drop) and the committed tail;

@@ -3,7 +3,7 @@
 Per request ("Verifying Without Giving Back the Speedup", VeriCache: Making
 Lossy KV Compression Exact): the compressed cache and a tail of exact rows
 stay on the GPU; the rest of the full cache lives in pinned host memory and is
-staged into one of two device slots on a copy stream only for verification.
+staged into one of the device slots (three by default) on a copy stream only for verification.
 Rows the GPU already holds exactly (the committed tail, and the kept prompt
 rows of a token-drop cache) are not kept on the host and never cross PCIe.  Requests
 start drafting at staggered ticks (request r joins after floor(r * x / B)

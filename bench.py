@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
-PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
+PCIE_PEAK_GBS = 63.0
+PCIE_PINNED_GBS = 57.6  # pinned host-to-device rate measured on the box (4 GiB copy)  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
 def log(*a):
@@ -274,6 +275,9 @@ def main():
                     help="token-drop ranking: observed attention (the workload's) or key norm (the pages' example "
                          "compressor: no recent window)")
     ap.add_argument("--ratio", type=int, default=0, help="token-drop compression ratio (0: the workload's)")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="per-request draft length between L_min = ceil(t_copy / t_step) (measured in the warmup) "
+                         "and the workload's x: doubled after an all-accepted round, a + 1 after a rejection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
@@ -342,7 +346,8 @@ def main():
                             "attention": vc.profile_read(vc.VC_PROF_PREFILL_ATTN), "tokens": T}
         log(f"request {r}: T={T} prefill+compress+offload {time.perf_counter() - t0:.1f}s")
     x_round = max(xs)
-    eng.start(lead=args.lead or None, draft_batch=args.draft_batch or None, queue_min=args.queue_min, n_slots=args.slots)
+    eng.start(lead=args.lead or None, draft_batch=args.draft_batch or None, queue_min=args.queue_min, n_slots=args.slots,
+              adaptive=args.adaptive, x_min=max(xs))
     t_setup = time.perf_counter() - t_setup
     log(f"setup {t_setup:.1f}s")
 
@@ -354,6 +359,28 @@ def main():
     vc.profile_enable(kinds)
     n_req = len(eng.reqs)
     eng.run_rounds_each(args.warmup)
+    if args.adaptive:
+        # the drafting horizon that still hides one request's host-row copy: L_min = ceil(t_copy / t_step),
+        # t_copy at the measured pinned host-to-device rate, t_step = one batched draft step of every request
+        # (timed here; the drafts it writes are overwritten by the real ones)
+        import math
+        eng.drain()
+        from lossless_speculative_decoding_amd.engine import DONE
+        live_w = [r for r in eng.reqs if r.phase != DONE]
+        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        for _ in range(4):
+            eng.m.draft_step([r.req for r in live_w], eng.ws_draft)
+            for r in live_w:
+                r.req.draft_idx += 1
+        torch.cuda.synchronize()
+        t_step = (time.perf_counter() - t_w) / 4
+        for r in live_w:
+            r.req.draft_idx = 0
+        n_host_bytes = 2 * max(r.n_host for r in eng.reqs) * s.n_layers * s.n_kv_heads * s.head_dim * 2
+        t_copy = n_host_bytes / (PCIE_PINNED_GBS * 1e9)
+        eng.x_min = max(1, min(max(xs), math.ceil(t_copy / t_step)))
+        log(f"adaptive draft length: L_min = {eng.x_min} (t_copy {t_copy * 1e3:.1f} ms, t_step {t_step * 1e3:.2f} ms)")
     eng.drain()
     warm = vc.profile_read()
     vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
@@ -507,7 +534,9 @@ def main():
                                  "on the host); tokens match VeriCache's: " + str(res_match),
         "speedup_vs_full_kv_from_host": round(tok_s / base_tok_s, 3),
         "scheduler": {"draft_batch": eng.draft_batch, "queue_min": eng.queue_min, "lead": eng.lead,
-                      "slots": len(eng.slots),
+                      "slots": len(eng.slots), "adaptive": args.adaptive,
+                      "x_min": eng.x_min if args.adaptive else None,
+                      "drafts_per_round": round((eng.drafted - d0) / max(len(accepts), 1), 2),
                       "mean_requests_per_draft_step": round(mean_draft_batch, 2)},
         "mean_accepted_per_round": round(sum(accepts) / max(len(accepts), 1), 3),
         "rounds": len(accepts),

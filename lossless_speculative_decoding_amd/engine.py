@@ -109,6 +109,7 @@ class Request:
     stage_ev: object = None
     acc_ev: object = None
     budget: int = -1                   # verifications it may still issue (-1: unlimited; 0: parked)
+    x_cur: int = 0                     # this round's draft length (x unless adaptive)
 
 
 class Engine:
@@ -206,7 +207,7 @@ class Engine:
 
     # ------------------------------------------------------------ the VeriCache loop
     def start(self, lead: int | None = None, stagger: bool = True, draft_batch: int | None = None,
-              queue_min: int = 1, n_slots: int = 3):
+              queue_min: int = 1, n_slots: int = 3, adaptive: bool = False, x_min: int = 1):
         """Allocate slots/workspaces and set the staggered start ticks.
 
         lead: a request's host rows start to stage once it has begun drafting and is within
@@ -223,7 +224,14 @@ class Engine:
         the waiting ones.
         n_slots: device staging buffers.  With fuller draft batches several requests finish
         drafting together; a third slot lets the link stage the next one while two staged
-        requests wait for their verification."""
+        requests wait for their verification.
+        adaptive / x_min: per-request draft length ("Tuning and Scaling", VeriCache Guide: the
+        drafting horizon is sized so that the full-KV copy overlaps drafting, L_min =
+        ceil(t_copy / t_step); KV Cache and Speculative Decoding: a falling acceptance rate is the
+        sign that speculation costs more than it saves).  A request starts at its x; after a
+        round that accepts every draft its length doubles (at most x), after a rejection at a it
+        becomes max(x_min, a + 1).  The emitted tokens do not change, only how many are drafted
+        per verification."""
         self.n_slots = max(1, n_slots)
         self._alloc()
         n = len(self.reqs)
@@ -231,6 +239,9 @@ class Engine:
             r.start_tick = (r.idx * r.x) // n if stagger else 0
             r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
             r.budget = -1
+            r.x_cur = r.x
+        self.adaptive = adaptive
+        self.x_min = max(1, x_min)
         self.lead = max(r.x for r in self.reqs) if lead is None else lead
         self.draft_batch = n if draft_batch is None else max(1, draft_batch)
         self.queue_min = queue_min
@@ -251,13 +262,13 @@ class Engine:
         # 2. stage full KV for requests close to the end of their draft (only once drafting has
         # begun: a request still waiting for a fuller draft batch must not hold a slot)
         for r in reqs:
-            if (r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= max(1, r.x - self.lead)
+            if (r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= max(1, r.x_cur - self.lead)
                     and self.tick >= r.start_tick):
                 self._try_stage(r)
         # 3. one batched draft step for every drafting request; requests yet to begin wait for a
         # fuller batch while enough drafted requests are queued for the host link
         ready = [r for r in reqs
-                 if r.phase == DRAFT and r.budget != 0 and self.tick >= r.start_tick and r.req.draft_idx < r.x]
+                 if r.phase == DRAFT and r.budget != 0 and self.tick >= r.start_tick and r.req.draft_idx < r.x_cur]
         active = [r for r in ready if r.req.draft_idx > 0]
         fresh = [r for r in ready if r.req.draft_idx == 0]
         queued = sum(1 for r in reqs if r.phase == WAIT_SLOT)
@@ -271,7 +282,7 @@ class Engine:
             self.drafted += len(grp)
             for r in grp:
                 r.req.draft_idx += 1
-                if r.req.draft_idx == r.x:
+                if r.req.draft_idx == r.x_cur:
                     r.phase = WAIT_SLOT
         # 4. verify requests whose drafts are complete and whose slot is staged
         for r in reqs:
@@ -289,6 +300,8 @@ class Engine:
         a = int(r.result_host[0])
         r.emitted += r.result_host[1:a + 2].tolist()
         r.accepts.append(a)
+        if self.adaptive:
+            r.x_cur = min(r.x, 2 * r.x_cur) if a == r.x_cur else max(min(self.x_min, r.x), a + 1)
         self.m.commit(r.req, a, r.vtail_k, r.vtail_v, after_event=r.acc_ev, copy_stream=self.copy_stream)
         r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
 
@@ -304,9 +317,10 @@ class Engine:
     def emitted_total(self) -> int:
         return sum(len(r.emitted) for r in self.reqs)
 
-    def run(self, lead: int | None = None, stagger: bool = True, trace: list | None = None):
+    def run(self, lead: int | None = None, stagger: bool = True, trace: list | None = None, adaptive: bool = False,
+            x_min: int = 1):
         """Decode every request to its n_tokens; returns wall seconds of the decode phase."""
-        self.start(lead, stagger)
+        self.start(lead, stagger, adaptive=adaptive, x_min=x_min)
         t0 = time.perf_counter()
         while any(r.phase != DONE for r in self.reqs):
             self.step()
@@ -395,13 +409,13 @@ class Engine:
         if r.budget > 0:
             r.budget -= 1
         sk, sv = self.slots[r.slot]
-        self.m.verify(r.req, sk, sv, r.rows, r.x + 1, r.verified, r.vtail_k, r.vtail_v, self.ws_verify)
+        self.m.verify(r.req, sk, sv, r.rows, r.x_cur + 1, r.verified, r.vtail_k, r.vtail_v, self.ws_verify)
         ev_free = torch.cuda.Event()
         ev_free.record(cs)
         self.slot_free_ev[r.slot] = ev_free
         self.slot_owner[r.slot] = None
         r.slot = -1
-        self.m.accept(r.req, r.verified, r.x, r.vtail_k, r.vtail_v, r.result)
+        self.m.accept(r.req, r.verified, r.x_cur, r.vtail_k, r.vtail_v, r.result)
         r.result_host.copy_(r.result, non_blocking=True)
         ev = torch.cuda.Event()
         ev.record(cs)

@@ -220,3 +220,14 @@ def test_prefill_is_repeatable_bitwise(setup):
     kd, vd = setup["kv"]
     for a, b in ((k1, k2), (v1, v2), (k1, kd), (v1, vd)):
         assert torch.equal(a[:, :, :T], b[:, :, :T])
+
+
+def test_adaptive_draft_length_equals_gpu_greedy(setup):
+    """Per-request draft lengths that change from round to round (adaptive horizon) leave the
+    tokens those of full-KV greedy decoding."""
+    from lossless_speculative_decoding_amd.engine import Engine
+    eng = Engine(setup["m"], CompressSpec("tokdrop", keep_recent=64, ratio=4, obs_window=32), chunk=256)
+    r = eng.add_request(setup["prompt"], X, N)
+    eng.run(adaptive=True, x_min=2)
+    log("adaptive accepts", r.accepts)
+    assert r.emitted == setup["g_toks"]

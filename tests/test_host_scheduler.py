@@ -56,6 +56,7 @@ class FakeModel:
         self.batches = []
         self.log = []                  # (event, request index)
         self.rounds = {}
+        self.x_log = []                # (request index, draft length) per verification
 
     def _idx(self, req):
         return next(r.idx for r in self.reqs if r.req is req)
@@ -69,7 +70,7 @@ class FakeModel:
         for q in reqs:
             i = self._idx(q)
             r = self.reqs[i]
-            assert 0 <= q.draft_idx < r.x
+            assert 0 <= q.draft_idx < r.x_cur <= r.x
             self.log.append(("draft", i))
 
     def stage(self, req, sk, sv, l0, l1, copy_stream=None):
@@ -77,7 +78,9 @@ class FakeModel:
 
     def verify(self, req, sk, sv, rows, n_rows, out, vk, vv, ws):
         i = self._idx(req)
-        assert req.draft_idx == self.reqs[i].x and n_rows == self.reqs[i].x + 1
+        r = self.reqs[i]
+        assert req.draft_idx == r.x_cur and n_rows == r.x_cur + 1
+        self.x_log.append((i, r.x_cur))
         self.log.append(("verify", i))
 
     def accept(self, req, verified, x, vk, vv, result):
@@ -199,4 +202,31 @@ def test_run_to_the_end_with_requests_finishing_at_different_times(monkeypatch, 
     for r in eng.reqs:
         assert len(r.emitted) >= r.n_tokens
         assert all(0 <= a <= r.x for a in r.accepts)
+        assert r.emitted[1:] == [1000 * r.idx + 100 * k + i for k, a in enumerate(r.accepts) for i in range(a + 1)]
+
+
+@pytest.mark.parametrize("x_min", [1, 3])
+def test_adaptive_draft_length(monkeypatch, x_min):
+    """Each round drafts exactly its length; the length doubles after an all-accepted round (at
+    most x) and drops to max(x_min, a + 1) after a rejection at a."""
+    eng = make_engine(monkeypatch, n_req=4, x=8, n_tokens=[40, 70, 55, 90], lag=1)
+    guard(monkeypatch, eng)
+    eng.start(adaptive=True, x_min=x_min)
+    while any(r.phase != E.DONE for r in eng.reqs):
+        eng.step()
+    eng.drain()
+    for r in eng.reqs:
+        xs = [x for i, x in eng.m.x_log if i == r.idx]
+        assert xs[0] == r.x and len(xs) == len(r.accepts)
+        for k in range(1, len(xs)):
+            a, prev = r.accepts[k - 1], xs[k - 1]
+            assert xs[k] == (min(r.x, 2 * prev) if a == prev else max(x_min, a + 1))
+        ev = [e for e, i in eng.m.log if i == r.idx]
+        drafts, k = 0, 0
+        for e in ev:
+            if e == "draft":
+                drafts += 1
+            elif e == "verify":
+                assert drafts == xs[k]
+                drafts, k = 0, k + 1
         assert r.emitted[1:] == [1000 * r.idx + 100 * k + i for k, a in enumerate(r.accepts) for i in range(a + 1)]

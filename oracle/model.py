@@ -25,10 +25,14 @@ position are the same computation.  That is the property [KV4] "Autoregressive
 Decoding and the KV Cache" states: past rows' K/V do not depend on later
 tokens, so caching them is exact.
 
-Pins: tests/test_oracle_model.py checks RMSNorm against its closed form, RoPE
-at position 0 (identity), norm preservation and relative-position dependence,
-and the cached row-by-row greedy decode against a brute-force recomputation
-of the whole sequence in matrix form with no cache (``sequence_logits``).
+Pins: tests/test_oracle_model.py checks RMSNorm against its closed form; RoPE
+at position 0 (identity), norm preservation, relative-position dependence, the
+rotate-half pairing and the frequencies theta**(-2i/D) on unit vectors at D = 8,
+and the equivalence with complex multiplication by exp(i pos theta_i); silu at
+closed-form points (sigma(ln 3) = 3/4) and its odd-part identity; the SwiGLU
+gate/up assignment on a crafted one-layer model; and the cached row-by-row
+greedy decode against a brute-force recomputation of the whole sequence in
+matrix form with no cache (``sequence_logits``).
 """
 from __future__ import annotations
 

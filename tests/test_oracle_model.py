@@ -7,7 +7,7 @@ import pytest
 
 import synth
 from oracle import decode as D
-from oracle.model import Weights, argmax, attend, rmsnorm, rope, sequence_logits
+from oracle.model import Weights, argmax, attend, rmsnorm, rope, row_forward, sequence_logits, silu
 from oracle.rounding import to_bf16, to_f16
 from synth.configs import ModelShape
 
@@ -41,6 +41,82 @@ def test_rope_pairing_is_rotate_half():
     # D = 2: a single pair (x0, x1) rotated by pos * theta**0 = pos radians
     x = np.array([1.0, 0.0])
     np.testing.assert_allclose(rope(x, 1, 10000.0), [math.cos(1.0), math.sin(1.0)], rtol=1e-15)
+
+
+def test_rope_frequencies_and_pairing_at_d8():
+    """Rotate-half pairing and the frequency exponent at D = 8: unit vector e_i (i < D/2) turns
+    towards e_{i + D/2} by the angle pos * theta**(-2i/D); e_{i + D/2} turns towards -e_i."""
+    D, theta, pos = 8, 10000.0, 3
+    for i in range(D // 2):
+        ang = pos * theta ** (-2.0 * i / D)
+        e = np.zeros(D)
+        e[i] = 1.0
+        want = np.zeros(D)
+        want[i], want[i + D // 2] = math.cos(ang), math.sin(ang)
+        np.testing.assert_allclose(rope(e, pos, theta), want, rtol=1e-14, atol=1e-15)
+        e = np.zeros(D)
+        e[i + D // 2] = 1.0
+        want = np.zeros(D)
+        want[i], want[i + D // 2] = -math.sin(ang), math.cos(ang)
+        np.testing.assert_allclose(rope(e, pos, theta), want, rtol=1e-14, atol=1e-15)
+    # the angles themselves: pos 1 gives 1, theta**-0.25, theta**-0.5, theta**-0.75 radians
+    e = np.zeros(D)
+    e[1] = 1.0
+    np.testing.assert_allclose(rope(e, 1, theta)[[1, 5]], [math.cos(0.1), math.sin(0.1)], rtol=1e-14)
+
+
+def test_rope_is_complex_multiplication():
+    """Rotate-half RoPE equals multiplying z_i = x_i + i x_{i+D/2} by exp(i pos theta_i)."""
+    rng = np.random.default_rng(4)
+    D, theta, pos = 16, 500000.0, 12345
+    x = rng.normal(size=D)
+    z = (x[: D // 2] + 1j * x[D // 2:]) * np.exp(1j * pos * theta ** (-np.arange(D // 2) * 2.0 / D))
+    np.testing.assert_allclose(rope(x, pos, theta), np.concatenate([z.real, z.imag]), rtol=1e-12, atol=1e-12)
+
+
+def test_silu_closed_forms():
+    """silu(x) = x sigma(x): sigma(ln 3) = 3/4, sigma(-ln 3) = 1/4, silu(0) = 0, and
+    silu(x) - silu(-x) = x for every x."""
+    l3 = math.log(3.0)
+    np.testing.assert_allclose(silu(np.array([l3, -l3, 0.0])), [0.75 * l3, -0.25 * l3, 0.0], rtol=1e-15, atol=0)
+    x = np.linspace(-6, 6, 25)
+    np.testing.assert_allclose(silu(x) - silu(-x), x, rtol=1e-14, atol=1e-14)
+    assert abs(silu(np.array([40.0]))[0] - 40.0) < 1e-15 * 40 * 1e3
+
+
+def _crafted_ffn_model():
+    """One layer, d = 4, one head of 4, ffn 2, vocab 4, eps 0: attention weights zero (the
+    attention output is then exactly zero), the embedding row of token 0 is [1, 1, 1, 1],
+    the gate projection W1 reads 2 * x0 into unit 0, the up projection W3 reads 3 * x0 into
+    unit 0, W2 writes unit 0 back to channel 0, and the LM head is the identity."""
+    s = ModelShape(n_layers=1, d_model=4, n_q_heads=1, n_kv_heads=1, head_dim=4, ffn=2, vocab=4,
+                   rope_theta=10000.0, dtype="fp64", eps=0.0)
+    W = Weights.__new__(Weights)
+    W.shape, W.dtype = s, "fp64"
+    W.E = np.ones((4, 4))
+    W.Wlm = np.eye(4)
+    z4 = np.zeros((4, 4))
+    W.Wq, W.Wk, W.Wv, W.Wo = [z4], [z4], [z4], [z4]
+    W.W1 = [np.array([[2.0, 0, 0, 0], [0, 0, 0, 0]])]
+    W.W3 = [np.array([[3.0, 0, 0, 0], [0, 0, 0, 0]])]
+    W.W2 = [np.array([[1.0, 0], [0, 0], [0, 0], [0, 0]])]
+    W.g1, W.g2, W.gF = [np.ones(4)], [np.ones(4)], np.ones(4)
+    return W
+
+
+def test_swiglu_gate_and_up_assignment():
+    """SwiGLU is silu(W1 f) * (W3 f): with gate 2 and up 3 the residual gains 3 * silu(2) =
+    6 sigma(2) on channel 0 (with the roles swapped it would gain 2 * silu(3) = 6 sigma(3))."""
+    W = _crafted_ffn_model()
+    h0 = 1.0 + 6.0 / (1.0 + math.exp(-2.0))
+    h = np.array([h0, 1.0, 1.0, 1.0])
+    want = h / math.sqrt(np.mean(h * h))
+    none = lambda l, j: (np.zeros((0, 4)), np.zeros((0, 4)))
+    got = row_forward(W, 0, 5, none).logits
+    np.testing.assert_allclose(got, want, rtol=1e-14)
+    np.testing.assert_allclose(sequence_logits(W, [0])[-1], want, rtol=1e-14)
+    hs = np.array([1.0 + 6.0 / (1.0 + math.exp(-3.0)), 1.0, 1.0, 1.0])
+    assert np.max(np.abs(got - hs / math.sqrt(np.mean(hs * hs)))) > 1e-3
 
 
 def test_attend_special_cases():

@@ -93,7 +93,7 @@ typedef struct {
   const void* norm_attn;  /* [L][d]                                            */
   const void* norm_ffn;   /* [L][d]                                            */
   const void* w_qkv;      /* [L][(Hq + 2 Hkv) D][d]: rows of Wq, then Wk, then Wv */
-  const void* w_o;        /* [L][d][Hq D]                                      */
+  const void* w_o;        /* [L][d][Hq D] (Hq D need not equal d)              */
   const void* w_gu;       /* [L][2 ffn][d]: rows of W1 (gate), then W3 (up)    */
   const void* w_down;     /* [L][d][ffn]                                       */
 } vc_weights;

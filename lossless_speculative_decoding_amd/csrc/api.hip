@@ -484,7 +484,6 @@ vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStr
              VC_ERR_ARG, "vc_model_create: bad shape");
   VC_REQUIRE((d.dtype == VC_BF16 && d.head_dim == 128) || (d.dtype == VC_F32 && d.head_dim == 64),
              VC_ERR_UNSUPPORTED, "vc_model_create: supported are bf16 with head_dim 128 and fp32 with head_dim 64");
-  VC_REQUIRE(d.n_q_heads * d.head_dim == d.d_model, VC_ERR_UNSUPPORTED, "vc_model_create: Hq * D must equal d_model");
   VC_REQUIRE(d.n_q_heads / d.n_kv_heads <= 16, VC_ERR_UNSUPPORTED, "vc_model_create: GQA group > 16");
   VC_REQUIRE(w->embed && w->lm_head && w->norm_final && w->norm_attn && w->norm_ffn && w->w_qkv && w->w_o && w->w_gu &&
                  w->w_down,

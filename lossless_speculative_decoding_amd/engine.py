@@ -110,17 +110,25 @@ class Request:
     acc_ev: object = None
     budget: int = -1                   # verifications it may still issue (-1: unlimited; 0: parked)
     x_cur: int = 0                     # this round's draft length (x unless adaptive)
+    rounds: list = field(default_factory=list)  # per-round record (Engine(record=True))
+    rec_host: torch.Tensor = None      # pinned [2][x + 1]: this round's rows and verified tokens
 
 
 class Engine:
     """Owns a vc_model, its workspaces and the per-request device/host buffers."""
 
+    record = False
+
     # the driver pins at most ~70 GiB of host memory per process; rows beyond the budget
     # go to pageable memory (staged at roughly half the pinned PCIe rate)
     PINNED_BUDGET = 69_000_000_000
 
-    def __init__(self, model: B.Model, spec, chunk: int = 1024, device="cuda", pinned_budget: int | None = None):
+    def __init__(self, model: B.Model, spec, chunk: int = 1024, device="cuda", pinned_budget: int | None = None,
+                 record: bool = False):
+        """record: keep, per request and round, the position, the pending token, the drafts, the
+        verifier's tokens and the accept count (host copies of device values; for parity tests)."""
         self.m = model
+        self.record = record
         self.spec = spec
         self.shape = model.shape
         self.dt = torch.bfloat16 if self.shape.dtype == "bf16" else torch.float32
@@ -175,6 +183,8 @@ class Engine:
         r.verified = torch.empty(x + 1, dtype=torch.int32, device=self.device)
         r.result = torch.empty(x + 2, dtype=torch.int32, device=self.device)
         r.result_host = torch.empty(x + 2, dtype=torch.int32, pin_memory=True)
+        if self.record:
+            r.rec_host = torch.empty(2, x + 1, dtype=torch.int32, pin_memory=True)
         r.req = Req(comp=r.comp.data_ptr(), cd=None, tail_k=r.tail_k.data_ptr(), tail_v=r.tail_v.data_ptr(),
                     tail_cap=tail_cap, n_tail=0, ctx_len=T, draft_idx=0, full_k_host=r.full_k.data_ptr(),
                     full_v_host=r.full_v.data_ptr(), full_cap=full_cap, rows=r.rows.data_ptr())
@@ -185,6 +195,7 @@ class Engine:
         r.emitted = [int(g0.item())]
         if keep_prefill_kv:
             r.prefill_kv = (kd, vd)
+            r.q_obs = q_obs
         self.reqs.append(r)
         return r
 
@@ -298,6 +309,11 @@ class Engine:
 
     def _finish_accept(self, r: Request):
         a = int(r.result_host[0])
+        if self.record:
+            n = r.x_cur + 1
+            rows, ver = r.rec_host[0, :n].tolist(), r.rec_host[1, :n].tolist()
+            r.rounds.append({"pos": r.req.ctx_len, "n_tail": r.req.n_tail, "pending": rows[0], "draft": rows[1:],
+                             "verified": ver, "a": a})
         r.emitted += r.result_host[1:a + 2].tolist()
         r.accepts.append(a)
         if self.adaptive:
@@ -410,6 +426,10 @@ class Engine:
             r.budget -= 1
         sk, sv = self.slots[r.slot]
         self.m.verify(r.req, sk, sv, r.rows, r.x_cur + 1, r.verified, r.vtail_k, r.vtail_v, self.ws_verify)
+        if self.record:  # before vc_accept overwrites rows[0] with the next pending token
+            n = r.x_cur + 1
+            r.rec_host[0, :n].copy_(r.rows[:n], non_blocking=True)
+            r.rec_host[1, :n].copy_(r.verified[:n], non_blocking=True)
         ev_free = torch.cuda.Event()
         ev_free.record(cs)
         self.slot_free_ev[r.slot] = ev_free

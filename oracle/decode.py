@@ -132,11 +132,21 @@ def draft_cache_quant(pre: Prefill, W: Weights, bits: int, group: int, **_):
                      [[Vd[l, j] for j in range(H)] for l in range(L)])
 
 
-class RoundLog:
-    __slots__ = ("pos", "draft", "verified", "a", "emitted")
+def rel_gap(logits: np.ndarray) -> float:
+    """(top-1 - top-2) / max |logit|: how far a greedy choice is from a tie, relative to the
+    logits' scale (positions below a comparison tolerance are near-ties)."""
+    srt = np.sort(np.asarray(logits))[::-1]
+    return float((srt[0] - srt[1]) / max(np.abs(srt).max(), 1e-300))
 
-    def __init__(self, pos, draft, verified, a, emitted):
+
+class RoundLog:
+    """One round: position of the pending token, drafts, verifier's predictions, accept count,
+    emitted tokens, and the relative top-2 gaps of every draft and verify row."""
+    __slots__ = ("pos", "draft", "verified", "a", "emitted", "draft_gap", "verify_gap")
+
+    def __init__(self, pos, draft, verified, a, emitted, draft_gap=None, verify_gap=None):
         self.pos, self.draft, self.verified, self.a, self.emitted = pos, draft, verified, a, emitted
+        self.draft_gap, self.verify_gap = draft_gap, verify_gap
 
 
 def vericache(W: Weights, prompt, n_tokens: int, x: int, make_draft_cache, pre: Prefill | None = None,
@@ -160,27 +170,29 @@ def vericache(W: Weights, prompt, n_tokens: int, x: int, make_draft_cache, pre: 
         # ---- draft x tokens with the compressed cache
         dtail = RowStore(s.n_layers, s.n_kv_heads, s.head_dim)
         past = chain(comp, tail, dtail)
-        draft, t = [], pending
+        draft, t, dgap = [], pending, []
         for i in range(x):
             o = row_forward(W, t, pos + i, past)
             dtail.append(o.k, o.v)
             t = argmax(o.logits)
             draft.append(t)
+            dgap.append(rel_gap(o.logits))
         if drafter is not None:
             draft = [int(v) for v in drafter(len(rounds), pending, draft)]
         # ---- verify x + 1 rows against the full KV
         rows = [pending] + draft
         vrows = RowStore(s.n_layers, s.n_kv_heads, s.head_dim)
         vpast = chain(full, vrows)
-        ver, kv = [], []
+        ver, kv, vgap = [], [], []
         for i, tok in enumerate(rows):
             o = row_forward(W, tok, pos + i, vpast)
             vrows.append(o.k, o.v)
             kv.append((o.k, o.v))
             ver.append(argmax(o.logits))
+            vgap.append(rel_gap(o.logits))
         # ---- accept and commit
         a, emitted = accept(draft, ver)
-        rounds.append(RoundLog(pos, draft, ver, a, emitted))
+        rounds.append(RoundLog(pos, draft, ver, a, emitted, dgap, vgap))
         out += emitted
         for i in range(a + 1):
             full.append(*kv[i])

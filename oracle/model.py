@@ -126,6 +126,38 @@ class RowOut:
         self.logits, self.k, self.v, self.q = logits, k, v, q
 
 
+def layer_forward(W: Weights, l: int, h: np.ndarray, pos: int, past, rdtype: str | None = None):
+    """Layer l on one row: residual stream h [d] (as stored) at position pos.
+
+    past(j) -> (K [n][D], V [n][D]): the rows of layer l, KV head j visible to this
+    row, in absolute-position order (this row's own K/V is appended after them).
+    Returns (h_out [d], k [Hkv][D], v [Hkv][D], q [Hq][D], o [Hq][D]), each as stored."""
+    s = W.shape
+    R = storage_round(rdtype or W.dtype)
+    D, G, Hq, Hkv = s.head_dim, s.group, s.n_q_heads, s.n_kv_heads
+    a = R(rmsnorm(h, W.g1[l], s.eps))
+    q = R(rope((W.Wq[l] @ a).reshape(Hq, D), pos, s.rope_theta))
+    k = R(rope((W.Wk[l] @ a).reshape(Hkv, D), pos, s.rope_theta))
+    v = R((W.Wv[l] @ a).reshape(Hkv, D))
+    o = np.empty((Hq, D))
+    for hq in range(Hq):
+        j = hq // G
+        Kp, Vp = past(j)
+        o[hq] = attend(q[hq], np.concatenate([Kp, k[j][None]]), np.concatenate([Vp, v[j][None]]))
+    o = R(o)
+    h = R(h + W.Wo[l] @ o.reshape(-1))
+    f = R(rmsnorm(h, W.g2[l], s.eps))
+    m = R(silu(W.W1[l] @ f) * (W.W3[l] @ f))
+    h = R(h + W.W2[l] @ m)
+    return h, k, v, q, o
+
+
+def head_forward(W: Weights, h: np.ndarray, rdtype: str | None = None) -> np.ndarray:
+    """Final norm and LM head of one row: float64 logits [V]."""
+    R = storage_round(rdtype or W.dtype)
+    return W.Wlm @ R(rmsnorm(h, W.gF, W.shape.eps))
+
+
 def row_forward(W: Weights, tok: int, pos: int, past, rdtype: str | None = None) -> RowOut:
     """One token through the whole model.
 
@@ -136,30 +168,14 @@ def row_forward(W: Weights, tok: int, pos: int, past, rdtype: str | None = None)
     """
     s = W.shape
     R = storage_round(rdtype or W.dtype)
-    D, G = s.head_dim, s.group
-    L, Hq, Hkv = s.n_layers, s.n_q_heads, s.n_kv_heads
+    L, Hq, Hkv, D = s.n_layers, s.n_q_heads, s.n_kv_heads, s.head_dim
     ks = np.empty((L, Hkv, D))
     vs = np.empty((L, Hkv, D))
     qs = np.empty((L, Hq, D))
     h = R(W.E[tok])
     for l in range(L):
-        a = R(rmsnorm(h, W.g1[l], s.eps))
-        q = R(rope((W.Wq[l] @ a).reshape(Hq, D), pos, s.rope_theta))
-        k = R(rope((W.Wk[l] @ a).reshape(Hkv, D), pos, s.rope_theta))
-        v = R((W.Wv[l] @ a).reshape(Hkv, D))
-        ks[l], vs[l], qs[l] = k, v, q
-        o = np.empty((Hq, D))
-        for hq in range(Hq):
-            j = hq // G
-            Kp, Vp = past(l, j)
-            o[hq] = attend(q[hq], np.concatenate([Kp, k[j][None]]), np.concatenate([Vp, v[j][None]]))
-        o = R(o)
-        h = R(h + W.Wo[l] @ o.reshape(-1))
-        f = R(rmsnorm(h, W.g2[l], s.eps))
-        m = R(silu(W.W1[l] @ f) * (W.W3[l] @ f))
-        h = R(h + W.W2[l] @ m)
-    z = R(rmsnorm(h, W.gF, s.eps))
-    return RowOut(W.Wlm @ z, ks, vs, qs)
+        h, ks[l], vs[l], qs[l], _ = layer_forward(W, l, h, pos, lambda j, l=l: past(l, j), rdtype)
+    return RowOut(head_forward(W, h, rdtype), ks, vs, qs)
 
 
 def argmax(logits: np.ndarray) -> int:

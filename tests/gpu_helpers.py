@@ -47,3 +47,26 @@ def row_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 TOL_BF16 = 2e-3
 TOL_F32 = 1e-5
+
+
+def compare_rounds(name, gpu_rounds, ref_a, ref_draft, ref_ver, ref_dgap, ref_vgap, tol):
+    """GPU rounds (Engine(record=True)) against an oracle run, round by round, up to the first
+    draft or verify token that differs, which must be one the oracle flags as a near-tie (its
+    relative top-2 gap below tol).  Equal drafts and verifier tokens give equal accept counts;
+    with no divergence at all the number of rounds must be equal too.  Returns the rounds
+    compared."""
+    for k, rd in enumerate(gpu_rounds):
+        if k >= len(ref_a):
+            break
+        for what, g, r, gap in (("draft", rd["draft"], ref_draft[k], ref_dgap[k]),
+                                ("verify row", rd["verified"], ref_ver[k], ref_vgap[k])):
+            for i, (a_, b_) in enumerate(zip(g, r)):
+                if int(a_) != int(b_):
+                    log(f"{name}: round {k} {what} {i} differs (oracle top-2 gap {gap[i]:.2e}); "
+                        f"{k} rounds compared before it")
+                    assert gap[i] < tol, f"{name}: round {k} {what} {i}: unflagged divergence from the oracle"
+                    return k
+        assert rd["a"] == int(ref_a[k]), f"{name}: round {k}: same drafts and verifier tokens, other accept count"
+    assert len(gpu_rounds) == len(ref_a), f"{name}: same rounds, but {len(gpu_rounds)} against {len(ref_a)}"
+    log(f"{name}: all {len(ref_a)} rounds equal the oracle's (accepts {[int(a) for a in ref_a]})")
+    return len(ref_a)

@@ -216,6 +216,20 @@ typedef struct {
 vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, void* ws, size_t ws_bytes,
                         hipStream_t s);
 
+/* vc_draft_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same step, with its
+ * workspace in a library-owned static device array of VC_STATIC_SCRATCH_BYTES per GPU (each
+ * GPU that runs the library holds its own copy until the process ends) instead of a caller
+ * buffer; its outputs equal vc_draft_step's bit for bit.  Returns VC_ERR_CAPACITY when the step
+ * needs more workspace than that (vc_ws_size(m, n, max keys visible to a request) bytes;
+ * 16 requests of the 8B-shaped model at 131072 keys need about 120 MiB).  Every call on one
+ * GPU uses that GPU's one array, which keeps the previous call's contents (the step writes
+ * every byte it reads): calls that overlap on one GPU, from several streams or threads, race.
+ * Allocates nothing. */
+#define VC_STATIC_SCRATCH_BYTES (160u << 20)
+#define VC_MAX_DEVICES 64
+vc_status vc_draft_step_static(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, hipStream_t s);
+
 /* Verification forward of ONE request ("The Core Idea": predictions for every
  * drafted position plus one bonus, in a single pass against the full cache).
  * Rows tok[0..n_rows) (the pending token then the x drafts) sit at positions

@@ -84,6 +84,7 @@ _SIGS = {
     "vc_compress_size": (_I, [C.POINTER(CompressDesc), C.POINTER(_S), C.POINTER(_S)]),
     "vc_compress": (_I, [C.POINTER(CompressDesc), _P, _P, _P, _P, _S, _P, _S, _P]),
     "vc_draft_step": (_I, [_P, C.POINTER(Req), _I, _P, _P, _S, _P]),
+    "vc_draft_step_static": (_I, [_P, C.POINTER(Req), _I, _P, _P]),
     "vc_verify": (_I, [_P, C.POINTER(Req), _P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
     "vc_accept": (_I, [_P, C.POINTER(Req), _P, _I, _P, _P, _I, _P, _P]),
     "vc_commit": (_I, [_P, C.POINTER(Req), _I, _P, _P, _I, _P, _P]),

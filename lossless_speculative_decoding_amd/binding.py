@@ -187,6 +187,13 @@ class Model:
         call("vc_draft_step", self.h, arr, n, ptr(logits), ptr(ws), ws.numel(), stream_handle())
         return arr
 
+    def draft_step_static(self, reqs, logits=None):
+        """vc_draft_step with the library's static workspace (no allocation)."""
+        n = len(reqs)
+        arr = (Req * n)(*reqs)
+        call("vc_draft_step_static", self.h, arr, n, ptr(logits), stream_handle())
+        return arr
+
     def verify_raw(self, req: Req, staged_k: int, staged_v: int, staged_cap: int, tok: int, n_rows: int, out: int,
                    vtail_k: int, vtail_v: int, vtail_cap: int, ws: torch.Tensor, logits: int | None = None):
         call("vc_verify", self.h, C.byref(req), staged_k, staged_v, staged_cap, tok, n_rows, out, logits, vtail_k,

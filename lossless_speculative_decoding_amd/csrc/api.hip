@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <vector>
 
 #include "attention.h"
@@ -94,6 +95,9 @@ ProfRec prof_gemm(int M, int N, int K, int S, int dtype) {
   return prof_begin(kind, (double(N) * K + double(M) * K) * eb + double(S) * M * N * 4, 2.0 * M * N * K);
 }
 }  // namespace
+
+// File-scope device array behind vc_draft_step_static (see scratch_of_current_device).
+static __device__ __align__(256) uint8_t vc_static_scratch[VC_STATIC_SCRATCH_BYTES];
 
 struct vc_model {
   vc_model_desc d;
@@ -542,8 +546,13 @@ vc_status vc_compress(const vc_compress_desc* d, const void* k, const void* v, c
   return compress_run(d, k, v, q_obs, out, out_bytes, ws, ws_bytes, s);
 }
 
-vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, void* ws, size_t ws_bytes,
-                        hipStream_t s) {
+}  // extern "C"
+
+namespace {
+// The batched draft step over a workspace of ws_bytes bytes at ws (a caller's buffer, or the
+// static scratch of vc_draft_step_static).
+vc_status draft_step_impl(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, void* ws, size_t ws_bytes,
+                          hipStream_t s) {
   if (vc_status st = check_model(m)) return st;
   VC_REQUIRE(reqs && ws, VC_ERR_ARG, "vc_draft_step: null argument");
   VC_REQUIRE(n > 0 && n <= VC_MAX_BATCH, VC_ERR_ARG, "vc_draft_step: batch %d not in [1, %d]", n, VC_MAX_BATCH);
@@ -605,6 +614,56 @@ vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logit
   if ((st = forward_layers(m, n, w8, L, tmpl, set_kv, attend, s))) return st;
   if ((st = head(m, 0, n, w8, L, tok_out, logits_opt, s))) return st;
   return k_scatter_tok(dst, n, tok_out, s);
+}
+
+// Workspace of vc_draft_step_static: one array per GPU the library runs on, held until the process
+// ends.  Host code never uses the symbol itself as an address (on the host it is a stand-in, not
+// device memory): each device's address is taken once with that device current and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_dev[VC_MAX_DEVICES] = {};
+
+vc_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  VC_HIP(hipGetDevice(&dev));
+  VC_REQUIRE(dev >= 0 && dev < VC_MAX_DEVICES, VC_ERR_UNSUPPORTED, "static scratch: device %d beyond %d", dev,
+             VC_MAX_DEVICES);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    VC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(vc_static_scratch)));
+    VC_REQUIRE(p != nullptr, VC_ERR_HIP, "static scratch: no device address");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return VC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, void* ws, size_t ws_bytes,
+                        hipStream_t s) {
+  return draft_step_impl(m, reqs, n, logits_opt, ws, ws_bytes, s);
+}
+
+vc_status vc_draft_step_static(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, hipStream_t s) {
+  if (vc_status st = check_model(m)) return st;
+  VC_REQUIRE(reqs != nullptr && n > 0 && n <= VC_MAX_BATCH, VC_ERR_ARG, "vc_draft_step_static: bad batch");
+  void* ws = nullptr;
+  if (vc_status st = scratch_of_current_device(&ws)) return st;
+  // the workspace this step needs, against the array's fixed size (draft_step_impl checks the
+  // requests themselves)
+  int max_keys = 1;
+  for (int r = 0; r < n; r++) {
+    CompView v;
+    if (vc_status st = comp_view(reqs[r].comp, reqs[r].cd, v)) return st;
+    max_keys = std::max(max_keys, v.lay.n_main + v.n_resid + reqs[r].n_tail + reqs[r].draft_idx + 1);
+  }
+  const size_t need = ws_layout(m, n, max_keys).total;
+  VC_REQUIRE(need <= VC_STATIC_SCRATCH_BYTES, VC_ERR_CAPACITY,
+             "vc_draft_step_static: the step needs %zu bytes of workspace, above the static maximum of %zu", need,
+             size_t(VC_STATIC_SCRATCH_BYTES));
+  return draft_step_impl(m, reqs, n, logits_opt, ws, VC_STATIC_SCRATCH_BYTES, s);
 }
 
 // Where a request's full cache lives.  A VeriCache request (comp != NULL) keeps exact rows on

@@ -32,6 +32,15 @@
  *   key sits in the staged cache or in the verify tail (row invariance), so
  *   vc_verify with n_rows = 1 is full-KV greedy decoding with exactly the
  *   tokens VeriCache emits.
+ *   Token ids: every argmax the library writes (drafts, verified tokens, g0) is
+ *   the lowest index of the largest logit, or -1 when the row's logits have no
+ *   finite maximum (all NaN, or all -inf).  An input token outside [0, vocab)
+ *   (such a -1 included) reads no memory: its embedding row is quiet NaN, so
+ *   that row's outputs are NaN and its argmax is -1 again (NaN keys or values
+ *   reach every row that shares their 64-key attention tile, the rows before
+ *   them included: the masked weights are zero and 0 x NaN is NaN).  A caller
+ *   that sees -1 has non-finite activations upstream and should stop decoding
+ *   that request.
  *
  * Errors: every call returns vc_status; 0 is success.  Negative values:
  *   VC_ERR_ARG (null pointer, bad shape or size), VC_ERR_UNSUPPORTED (e.g. a

@@ -587,7 +587,7 @@ vc_status draft_step_impl(vc_model* m, const vc_req* reqs, int32_t n, float* log
     dst[r] = reqs[r].rows + reqs[r].draft_idx + 1;
   }
   if ((st = k_gather_tok(src, n, tok_in, s))) return st;
-  if ((st = k_embed(m->w.embed, tok_in, w8 + L.h, n, d.d_model, d.dtype, s))) return st;
+  if ((st = k_embed(m->w.embed, tok_in, w8 + L.h, n, d.d_model, d.vocab, d.dtype, s))) return st;
   EpiArgs tmpl{};
   tmpl.batched = 1;
   for (int r = 0; r < n; r++) tmpl.pos[r] = reqs[r].ctx_len + reqs[r].draft_idx;
@@ -719,7 +719,7 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
   VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_verify: workspace %zu < %zu bytes", ws_bytes, L.total);
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   vc_status st;
-  if ((st = k_embed(m->w.embed, tok, w8 + L.h, n_rows, d.d_model, d.dtype, s))) return st;
+  if ((st = k_embed(m->w.embed, tok, w8 + L.h, n_rows, d.d_model, d.vocab, d.dtype, s))) return st;
   EpiArgs tmpl{};
   tmpl.batched = 0;
   tmpl.pos0 = ctx;
@@ -806,7 +806,7 @@ vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out,
   vc_status st;
   for (int c0 = 0; c0 < T; c0 += chunk) {
     const int C = std::min(chunk, T - c0);
-    if ((st = k_embed(m->w.embed, tokens + c0, w8 + L.h, C, d.d_model, d.dtype, s))) return st;
+    if ((st = k_embed(m->w.embed, tokens + c0, w8 + L.h, C, d.d_model, d.vocab, d.dtype, s))) return st;
     EpiArgs tmpl{};
     tmpl.batched = 0;
     tmpl.pos0 = c0;

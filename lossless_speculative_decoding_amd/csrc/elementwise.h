@@ -4,7 +4,7 @@
 
 namespace vc {
 
-vc_status k_embed(const void* E, const int32_t* tok, void* h, int M, int d, int dt, hipStream_t s);
+vc_status k_embed(const void* E, const int32_t* tok, void* h, int M, int d, int V, int dt, hipStream_t s);
 vc_status k_rmsnorm(const void* x, const void* g, void* y, int M, int d, float eps, int dt, hipStream_t s);
 vc_status k_argmax(const float* logits, int M, int V, int32_t* out, hipStream_t s);
 vc_status k_accept(int32_t* rows, const int32_t* verified, int x, int32_t* result, hipStream_t s);

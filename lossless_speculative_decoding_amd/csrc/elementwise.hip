@@ -13,13 +13,22 @@ __device__ __forceinline__ void st(void* p, int64_t i, float v, int dt) {
   else static_cast<float*>(p)[i] = v;
 }
 
-__global__ void embed_kernel(const void* E, const int32_t* tok, void* h, int d, int dt) {
+// Row r of h = row tok[r] of E.  A token outside [0, V) (the -1 that argmax writes for a row with
+// no finite logit, or any other invalid id) reads nothing: its row becomes quiet NaN, which the
+// rest of the forward carries into that row's logits and so into another -1.
+__global__ void embed_kernel(const void* E, const int32_t* tok, void* h, int d, int V, int dt) {
   const int r = blockIdx.y;
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= d) return;
   const int64_t t = tok[r];
-  if (dt == VC_BF16) static_cast<uint16_t*>(h)[int64_t(r) * d + c] = static_cast<const uint16_t*>(E)[t * d + c];
-  else static_cast<float*>(h)[int64_t(r) * d + c] = static_cast<const float*>(E)[t * d + c];
+  const int64_t o = int64_t(r) * d + c;
+  if (t < 0 || t >= V) {  // the table is not touched
+    if (dt == VC_BF16) static_cast<uint16_t*>(h)[o] = uint16_t(0x7fc0);
+    else static_cast<float*>(h)[o] = __builtin_nanf("");
+    return;
+  }
+  if (dt == VC_BF16) static_cast<uint16_t*>(h)[o] = static_cast<const uint16_t*>(E)[t * d + c];
+  else static_cast<float*>(h)[o] = static_cast<const float*>(E)[t * d + c];
 }
 
 // y = x / sqrt(mean(x^2) + eps) * g, one workgroup of 256 threads per row.  bf16 rows with
@@ -89,7 +98,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
   }
 }
 
-// Greedy choice per row: the largest logit, ties to the lowest index.
+// Greedy choice per row: the largest logit, ties to the lowest index; -1 when the row has no
+// finite maximum (every logit NaN, or all of them -inf), which no embedding row answers to.
 __global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V, int32_t* out) {
   __shared__ float bv[1024];
   __shared__ int bi[1024];
@@ -118,7 +128,7 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V
     }
     __syncthreads();
   }
-  if (tid == 0) out[r] = bi[0];
+  if (tid == 0) out[r] = (bi[0] < V && bv[0] > -__builtin_huge_valf()) ? bi[0] : -1;
 }
 
 // a = first i < x with draft[i] != verified[i] (else x); result = [a, draft[0..a), verified[a]];
@@ -190,8 +200,8 @@ __global__ void copy_words_kernel(const uint32_t* src, uint32_t* dst, int64_t n)
 
 }  // namespace
 
-vc_status k_embed(const void* E, const int32_t* tok, void* h, int M, int d, int dt, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(cdiv(d, 256), M), dim3(256), 0, s, E, tok, h, d, dt);
+vc_status k_embed(const void* E, const int32_t* tok, void* h, int M, int d, int V, int dt, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(cdiv(d, 256), M), dim3(256), 0, s, E, tok, h, d, V, dt);
   VC_LAUNCH_CHECK();
   return VC_OK;
 }

@@ -35,6 +35,10 @@ from ._vc import Req
 DRAFT, WAIT_SLOT, ACCEPTING, DONE = range(4)
 
 
+class NonFiniteLogits(RuntimeError):
+    """The library wrote token -1: some row's logits had no finite maximum."""
+
+
 def make_weights(shape, device="cuda", seed: int = 0) -> dict:
     """Random-init weights in the library layout, generated on the GPU from the
     seeded recipe (Xavier-uniform; norm gains 1)."""
@@ -193,6 +197,8 @@ class Engine:
         self.m.offload(r.req, kd, vd, T)
         torch.cuda.synchronize()
         r.emitted = [int(g0.item())]
+        if r.emitted[0] < 0:
+            raise NonFiniteLogits(f"request {r.idx}: the prefill's last row has no finite logit")
         if keep_prefill_kv:
             r.prefill_kv = (kd, vd)
             r.q_obs = q_obs
@@ -314,7 +320,11 @@ class Engine:
             rows, ver = r.rec_host[0, :n].tolist(), r.rec_host[1, :n].tolist()
             r.rounds.append({"pos": r.req.ctx_len, "n_tail": r.req.n_tail, "pending": rows[0], "draft": rows[1:],
                              "verified": ver, "a": a})
-        r.emitted += r.result_host[1:a + 2].tolist()
+        new = r.result_host[1:a + 2].tolist()
+        if min(new) < 0:
+            raise NonFiniteLogits(f"request {r.idx}: a row of its round {len(r.accepts)} (position "
+                                  f"{r.req.ctx_len} onwards) has no finite logit; emitted {new}")
+        r.emitted += new
         r.accepts.append(a)
         if self.adaptive:
             r.x_cur = min(r.x, 2 * r.x_cur) if a == r.x_cur else max(min(self.x_min, r.x), a + 1)
@@ -469,7 +479,10 @@ def greedy_resident(model: B.Model, prompt: torch.Tensor, n_tokens: int, chunk: 
         model.verify_raw(req, kd.data_ptr(), vd.data_ptr(), cap, out.data_ptr() + 4 * (i - 1), 1,
                          out.data_ptr() + 4 * i, kd.data_ptr() + off, vd.data_ptr() + off, cap, ws)
     torch.cuda.synchronize()
-    return out.tolist(), time.perf_counter() - t0, (kd, vd)
+    toks = out.tolist()
+    if min(toks) < 0:
+        raise NonFiniteLogits(f"greedy decoding: token -1 at step {toks.index(-1)}")
+    return toks, time.perf_counter() - t0, (kd, vd)
 
 
 def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tensor, n_steps: int, ws: torch.Tensor,
@@ -516,4 +529,7 @@ def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tenso
     del sk, sv
     hk.free()
     hv.free()
-    return [int(t.item()) for t in toks], secs
+    toks = [int(t.item()) for t in toks]
+    if toks and min(toks) < 0:
+        raise NonFiniteLogits(f"full-KV-from-host decoding: token -1 at step {toks.index(-1)}")
+    return toks, secs

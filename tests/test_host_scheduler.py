@@ -230,3 +230,20 @@ def test_adaptive_draft_length(monkeypatch, x_min):
                 assert drafts == xs[k]
                 drafts, k = 0, k + 1
         assert r.emitted[1:] == [1000 * r.idx + 100 * k + i for k, a in enumerate(r.accepts) for i in range(a + 1)]
+
+
+def test_token_minus_one_stops_the_request_loudly(monkeypatch):
+    """A -1 token (a row with no finite logit) in an accept result raises instead of being
+    emitted, so a non-finite row can never be decoded further."""
+    eng = make_engine(monkeypatch, n_req=2, x=4)
+    orig = eng.m.accept
+
+    def accept(req, verified, x, vk, vv, result):
+        orig(req, verified, x, vk, vv, result)
+        if eng.m.rounds[eng.m._idx(req)] == 3:
+            result[1 + int(result[0])] = -1
+    eng.m.accept = accept
+    eng.start()
+    with pytest.raises(E.NonFiniteLogits):
+        for _ in range(10_000):
+            eng.step()

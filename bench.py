@@ -254,62 +254,21 @@ DISABLED = {
 }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=16, help="timed verification rounds per request")
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="llama8b_tokdrop",
-                    choices=["llama8b_tokdrop", "llama8b_q2", "llama8b_mixed", "gqa_layer"])
-    ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
-    ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
-    ap.add_argument("--baseline-steps", type=int, default=2)
-    ap.add_argument("--draft-batch", type=int, default=0,
-                    help="requests yet to draft wait for a batch this large while --queue-min drafted requests are "
-                         "queued for verification (0: all the requests; 1: draft as soon as possible)")
-    ap.add_argument("--queue-min", type=int, default=1)
-    ap.add_argument("--lead", type=int, default=0, help="draft steps before a request's last draft at which its "
-                    "host rows start to stage (0: as soon as its drafting has begun)")
-    ap.add_argument("--slots", type=int, default=3, help="device staging slots")
-    ap.add_argument("--score", choices=["attn", "keynorm"], default="attn",
-                    help="token-drop ranking: observed attention (the workload's) or key norm (the pages' example "
-                         "compressor: no recent window)")
-    ap.add_argument("--ratio", type=int, default=0, help="token-drop compression ratio (0: the workload's)")
-    ap.add_argument("--adaptive", action="store_true",
-                    help="per-request draft length between L_min = ceil(t_copy / t_step) (measured in the warmup) "
-                         "and the workload's x: doubled after an all-accepted round, a + 1 after a rejection")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
-                         "the HBM byte counters of a profile)")
-    args = ap.parse_args()
-    if args.calibrate_copy:
-        import torch
-        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty(1 << 30, dtype=torch.int8, device="cuda")
-        for _ in range(5):
-            dst.copy_(src)  # uint8 -> int8: an elementwise kernel that reads and writes 1 GiB (not a DMA)
-        torch.cuda.synchronize()
-        log("copied 5 x 1 GiB")
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (requests would be sharded across "
-              "GPUs by request, each GPU running this same loop)", file=sys.stderr)
-        sys.exit(2)
-
-    if args.config == "gqa_layer":
-        bench_layer(args)
-        return
-
+def run_model_workload(args) -> dict:
+    """The model workloads: setup (weights, prefill, compression, offload of every request),
+    warmup and timed verification rounds, the compressed-only and comparator passes.  Runs on
+    the selected runtime: the GPU, or a dry run of the library's address-range checks."""
     import torch
 
     import synth
     from synth import configs
     import lossless_speculative_decoding_amd as vc
+    from lossless_speculative_decoding_amd import runtime
     from lossless_speculative_decoding_amd.engine import Engine, greedy_from_host, make_weights
 
-    if args.config in DISABLED:
-        sys.exit(f"bench.py: workload {args.config} is disabled: {DISABLED[args.config]}")
+    dry = runtime.RT.dry
+    device = runtime.RT.device
+    sync = runtime.RT.synchronize
     w = configs.ALL[args.config]()
     if w.compress.kind == "tokdrop" and (args.score != "attn" or args.ratio):
         import dataclasses
@@ -326,15 +285,16 @@ def main():
     if args.batch:
         ctx = ctx[: args.batch]
     xs = list(w.x)[: len(ctx)]
-    torch.cuda.set_device(0)
+    if not dry:
+        torch.cuda.set_device(0)
     t_setup = time.perf_counter()
     n_cap = w.n_tokens
-    W = make_weights(s)
+    W = make_weights(s, device=device)
     model = vc.Model(s, W, max_pos=max(ctx) + n_cap + 64)
-    eng = Engine(model, w.compress, chunk=2048)
+    eng = Engine(model, w.compress, chunk=2048, device=device)
     prefill_prof = None
     for r, (T, x) in enumerate(zip(ctx, xs)):
-        p = torch.empty(T, dtype=torch.int32, device="cuda")
+        p = torch.empty(T, dtype=torch.int32, device=device)
         vc.synth_ids(p, synth.S_PROMPT + r, s.vocab)
         t0 = time.perf_counter()
         if r == 0:  # request 0's prefill: live timing of its tiled GEMMs and causal attention
@@ -367,13 +327,13 @@ def main():
         eng.drain()
         from lossless_speculative_decoding_amd.engine import DONE
         live_w = [r for r in eng.reqs if r.phase != DONE]
-        torch.cuda.synchronize()
+        sync()
         t_w = time.perf_counter()
         for _ in range(4):
             eng.m.draft_step([r.req for r in live_w], eng.ws_draft)
             for r in live_w:
                 r.req.draft_idx += 1
-        torch.cuda.synchronize()
+        sync()
         t_step = (time.perf_counter() - t_w) / 4
         for r in live_w:
             r.req.draft_idx = 0
@@ -385,7 +345,7 @@ def main():
     warm = vc.profile_read()
     vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
     # timed region
-    torch.cuda.synchronize()
+    sync()
     e0 = eng.emitted_total()
     sb0, sn0 = eng.staged_bytes, eng.stagings
     a0 = [len(r.accepts) for r in eng.reqs]
@@ -393,7 +353,7 @@ def main():
     t0 = time.perf_counter()
     eng.run_rounds_each(args.steps)
     eng.drain()
-    torch.cuda.synchronize()
+    sync()
     secs = time.perf_counter() - t0
     vc.profile_enable(())
     prof = vc.profile_read()
@@ -417,14 +377,20 @@ def main():
     traffic = round(traffic_ratio * bpl) if traffic_ratio else None
     pcie_gbs = staged / secs / 1e9
     # compressed-only decoding (lossy; context): x batched draft steps of every request, no verification
-    live = [r for r in eng.reqs if r.req.n_tail + r.x + 1 <= r.tail_k.shape[2]]
-    torch.cuda.synchronize()
+    # (requests whose tail has no room for x more rows are rolled back to the last position that
+    # has: this pass follows the timed region and only its rate is kept)
+    live = list(eng.reqs)
+    for r in live:
+        r.req.n_tail = min(r.req.n_tail, r.tail_k.shape[2] - r.x - 1)
+        r.req.ctx_len = r.T + r.req.n_tail
+        r.req.draft_idx = 0
+    sync()
     t_d = time.perf_counter()
     for _ in range(x_round):
         eng.m.draft_step([r.req for r in live], eng.ws_draft)
         for r in live:
             r.req.draft_idx = min(r.req.draft_idx + 1, r.x - 1)
-    torch.cuda.synchronize()
+    sync()
     draft_only = len(live) * x_round / (time.perf_counter() - t_d)
     # the same draft steps again with live timing of their weight-streaming GEMMs (separate
     # pass: a per-GEMM event pair is not free at these kernel lengths)
@@ -434,7 +400,7 @@ def main():
         eng.m.draft_step([r.req for r in live], eng.ws_draft)
         for r in live:
             r.req.draft_idx = min(r.req.draft_idx + 1, r.x - 1)
-    torch.cuda.synchronize()
+    sync()
     vc.profile_enable(())
     gprof = vc.profile_read(vc.VC_PROF_GEMM_SKINNY)
     for r in live:
@@ -446,7 +412,7 @@ def main():
     # VeriCache emitted for request 0
     r0 = eng.reqs[0]
     eng.release_host()  # the comparator needs host memory for a whole full KV
-    first = torch.tensor([r0.emitted[0]], dtype=torch.int32, device="cuda")
+    first = torch.tensor([r0.emitted[0]], dtype=torch.int32, device=device)
     toks, bsecs = greedy_from_host(model, r0.prefill_kv, r0.T, first, args.baseline_steps, eng.ws_verify,
                                    eng.copy_stream)
     base_tok_s = args.baseline_steps / bsecs
@@ -458,23 +424,25 @@ def main():
     from lossless_speculative_decoding_amd._vc import Req
     n_res = 16
     cap = r0.T + n_res + 1
-    kd = torch.empty(s.n_layers, s.n_kv_heads, cap, s.head_dim, dtype=r0.prefill_kv[0].dtype, device="cuda")
+    kd = torch.empty(s.n_layers, s.n_kv_heads, cap, s.head_dim, dtype=r0.prefill_kv[0].dtype, device=device)
     vd = torch.empty_like(kd)
-    kd[:, :, :r0.T].copy_(r0.prefill_kv[0][:, :, :r0.T])
-    vd[:, :, :r0.T].copy_(r0.prefill_kv[1][:, :, :r0.T])
+    if not dry:  # data only (a dry run computes nothing)
+        kd[:, :, :r0.T].copy_(r0.prefill_kv[0][:, :, :r0.T])
+        vd[:, :, :r0.T].copy_(r0.prefill_kv[1][:, :, :r0.T])
     del r0.prefill_kv
-    res_rows = torch.empty(n_res + 1, dtype=torch.int32, device="cuda")
+    res_rows = torch.empty(n_res + 1, dtype=torch.int32, device=device)
     res_rows[:1].copy_(first)
+    vc.debug_register(kd, vd, res_rows, eng.ws_verify)
     rreq = Req(ctx_len=r0.T)
     row_b = s.head_dim * kd.element_size()
-    torch.cuda.synchronize()
+    sync()
     t_r = time.perf_counter()
     for i in range(n_res):
         rreq.ctx_len = r0.T + i
         off = rreq.ctx_len * row_b
         model.verify_raw(rreq, kd.data_ptr(), vd.data_ptr(), cap, res_rows.data_ptr() + 4 * i, 1,
                          res_rows.data_ptr() + 4 * (i + 1), kd.data_ptr() + off, vd.data_ptr() + off, cap, eng.ws_verify)
-    torch.cuda.synchronize()
+    sync()
     res_tok_s = n_res / (time.perf_counter() - t_r)
     n_rc = min(n_res, len(r0.emitted) - 1)
     res_match = res_rows[1:1 + n_rc].tolist() == r0.emitted[1:1 + n_rc]
@@ -482,12 +450,12 @@ def main():
     log(f"resident full-KV greedy (one request, context): {res_tok_s:.1f} tok/s; tokens match VeriCache's: {res_match}")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not dry:
         keep = ctx[0] // w.compress.ratio if w.compress.kind == "tokdrop" else ctx[0]
         cpu = cpu_baseline(s, ctx[0], keep)
         log(f"cpu baseline {cpu['value']:.4f} {cpu['unit']}")
 
-    line = {
+    return {
         "metric": "lossless decode tokens/s at 1 GPU; draft-attn HBM GB/s vs peak",
         "value": round(tok_s, 3),
         "unit": "tokens/s",
@@ -545,6 +513,98 @@ def main():
         "compressed_only_draft_tok_s": round(draft_only, 2),
         "cpu_baseline": cpu,
     }
+
+
+def bounds_replay(args):
+    """Replay the workload's exact sequence of library calls on the CPU with the library's
+    address-range checks (vc_debug_mode VC_DEBUG_DRY): every launch and copy states the byte
+    ranges it can touch, each must lie inside a buffer the caller or the library allocated (host
+    memory stands in for device memory, mapped lazily), and nothing runs.  Accept counts come
+    from a seeded policy that accepts every draft in every other round (the fastest-growing
+    tails).  Prints the checks made; exits non-zero at the first range outside every buffer."""
+    import lossless_speculative_decoding_amd as vc
+    from lossless_speculative_decoding_amd import runtime
+    runtime.use(runtime.DryRT(seed=0))
+    vc.debug_mode(vc.VC_DEBUG_DRY)
+    args.no_cpu_baseline = True
+    t0 = time.perf_counter()
+    try:
+        run_model_workload(args)
+    except vc._vc.VCError as e:
+        st = vc.debug_stats()
+        print(json.dumps({"bounds_replay": args.config, "ok": False, "error": str(e), **st}), flush=True)
+        sys.exit(1)
+    st = vc.debug_stats()
+    print(json.dumps({"bounds_replay": args.config, "ok": st["violations"] == 0, "seconds": round(time.perf_counter()
+                                                                                                 - t0, 1), **st}),
+          flush=True)
+    sys.exit(0 if st["violations"] == 0 else 1)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16, help="timed verification rounds per request")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="llama8b_tokdrop",
+                    choices=["llama8b_tokdrop", "llama8b_q2", "llama8b_mixed", "gqa_layer"])
+    ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
+    ap.add_argument("--baseline-steps", type=int, default=2)
+    ap.add_argument("--draft-batch", type=int, default=0,
+                    help="requests yet to draft wait for a batch this large while --queue-min drafted requests are "
+                         "queued for verification (0: all the requests; 1: draft as soon as possible)")
+    ap.add_argument("--queue-min", type=int, default=1)
+    ap.add_argument("--lead", type=int, default=0, help="draft steps before a request's last draft at which its "
+                    "host rows start to stage (0: as soon as its drafting has begun)")
+    ap.add_argument("--slots", type=int, default=3, help="device staging slots")
+    ap.add_argument("--score", choices=["attn", "keynorm"], default="attn",
+                    help="token-drop ranking: observed attention (the workload's) or key norm (the pages' example "
+                         "compressor: no recent window)")
+    ap.add_argument("--ratio", type=int, default=0, help="token-drop compression ratio (0: the workload's)")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="per-request draft length between L_min = ceil(t_copy / t_step) (measured in the warmup) "
+                         "and the workload's x: doubled after an all-accepted round, a + 1 after a rejection")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--check-bounds", action="store_true",
+                    help="check every launch's and copy's byte ranges against the buffers allocated for it before "
+                         "it runs on the GPU (an error instead of a launch outside them)")
+    ap.add_argument("--bounds-replay", action="store_true",
+                    help="no GPU work: replay the workload's sequence of library calls on the CPU with every "
+                         "launch's byte ranges checked against the buffers allocated for it")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
+                         "the HBM byte counters of a profile)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(1 << 30, dtype=torch.int8, device="cuda")
+        for _ in range(5):
+            dst.copy_(src)  # uint8 -> int8: an elementwise kernel that reads and writes 1 GiB (not a DMA)
+        torch.cuda.synchronize()
+        log("copied 5 x 1 GiB")
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (requests would be sharded across "
+              "GPUs by request, each GPU running this same loop)", file=sys.stderr)
+        sys.exit(2)
+
+    if args.config == "gqa_layer":
+        bench_layer(args)
+        return
+
+    if args.config in DISABLED and not args.bounds_replay:
+        sys.exit(f"bench.py: workload {args.config} is disabled: {DISABLED[args.config]}")
+    if args.bounds_replay:
+        bounds_replay(args)
+        return
+    if args.check_bounds:
+        import lossless_speculative_decoding_amd as vc
+        vc.debug_mode(vc.VC_DEBUG_CHECK)
+    line = run_model_workload(args)
+    if args.check_bounds:
+        line["bounds_checks"] = vc.debug_stats()
     print(json.dumps(line), flush=True)
 
 

@@ -377,6 +377,41 @@ vc_status vc_profile_enable(uint32_t mask);
 vc_status vc_profile_read(int32_t kind, vc_profile_stats* out);
 
 /* ------------------------------------------------------------------------
+ * Address-range checking (debugging, not for the hot path).
+ *   VC_DEBUG_CHECK: before every kernel launch and copy the library states
+ *     each byte range it will touch, from the call's arguments and the
+ *     kernel's own loop bounds, and checks that each lies inside one buffer
+ *     registered with vc_debug_register (device or host memory; the library
+ *     registers what it allocates itself: the RoPE table, pinned buffers of
+ *     vc_host_alloc, temporaries, the static scratch).  A range outside every
+ *     buffer fails the call with VC_ERR_ARG before anything is launched;
+ *     vc_last_error() names the kernel, the operand and the range.
+ *   VC_DEBUG_DRY: the same checks, and then no HIP call at all (no launch,
+ *     copy, event, synchronisation or device allocation; vc_host_alloc and
+ *     the library's temporaries become lazily mapped host memory, and
+ *     host_alloc bytes are counted as pinned).  A caller passes host memory
+ *     where device buffers would be, and replays a workload's exact sequence
+ *     of calls on a machine without a GPU.  Results are not computed: device
+ *     outputs keep whatever the caller's buffers held.
+ *   Not thread-safe with respect to mode changes.
+ * ---------------------------------------------------------------------- */
+#define VC_DEBUG_OFF 0
+#define VC_DEBUG_CHECK 1
+#define VC_DEBUG_DRY 2
+typedef struct {
+  int64_t launches;    /* launches and copies checked            */
+  int64_t ranges;      /* byte ranges checked                    */
+  int64_t violations;  /* checks that failed                     */
+  double pinned_bytes; /* vc_host_alloc bytes live (dry mode)    */
+  double pinned_peak;  /* their peak                             */
+} vc_debug_stats;
+vc_status vc_debug_mode(int32_t mode);
+vc_status vc_debug_register(const void* p, size_t bytes);
+vc_status vc_debug_forget(const void* p);
+/* Counters since the last reset; reset != 0 clears them (the live pinned bytes are kept). */
+vc_status vc_debug_stats_read(vc_debug_stats* out, int32_t reset);
+
+/* ------------------------------------------------------------------------
  * Seeded synthetic inputs (not part of the method): the counter-based
  * SplitMix64 generator of the input recipe, evaluated on the GPU so that
  * large workloads need not be generated on the host.  Counter

@@ -66,6 +66,14 @@ class ProfileStats(C.Structure):
     _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("bytes", C.c_double), ("flops", C.c_double)]
 
 
+class DebugStats(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("ranges", C.c_int64), ("violations", C.c_int64),
+                ("pinned_bytes", C.c_double), ("pinned_peak", C.c_double)]
+
+
+VC_DEBUG_OFF, VC_DEBUG_CHECK, VC_DEBUG_DRY = 0, 1, 2
+
+
 class AttnDraftReq(C.Structure):
     _fields_ = [("comp", C.c_void_p), ("cd", C.POINTER(CompressDesc)), ("tail_k", C.c_void_p),
                 ("tail_v", C.c_void_p), ("tail_cap", C.c_int32), ("n_tail", C.c_int32)]
@@ -103,6 +111,10 @@ _SIGS = {
     "vc_host_free": (_I, [_P]),
     "vc_offload": (_I, [_P, C.POINTER(Req), _P, _P, _I, _I, _P]),
     "vc_profile_read": (_I, [_I, C.POINTER(ProfileStats)]),
+    "vc_debug_mode": (_I, [_I]),
+    "vc_debug_register": (_I, [_P, _S]),
+    "vc_debug_forget": (_I, [_P]),
+    "vc_debug_stats_read": (_I, [C.POINTER(DebugStats), _I]),
 }
 
 if not os.path.exists(LIB_PATH):

@@ -10,29 +10,60 @@ import ctypes as C
 
 import torch
 
-from . import _vc
+from . import _vc, runtime
 from ._vc import (VC_BF16, VC_F32, VC_PROF_DRAFT_ATTN, VC_PROF_GEMM_SKINNY, VC_PROF_GEMM_TILED,
                   VC_PROF_PREFILL_ATTN, VC_PROF_VERIFY_ATTN, VC_QUANT, VC_SCORE_ATTN, VC_SCORE_KEYNORM, VC_TOKDROP,
-                  AttnDesc, AttnDraftReq,
+                  VC_DEBUG_CHECK, VC_DEBUG_DRY, VC_DEBUG_OFF, AttnDesc, AttnDraftReq, DebugStats,
                   CompressDesc, CompressLayout, ModelDesc, ProfileStats, Req, Weights, call)
 
 __all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "VC_SCORE_ATTN", "VC_SCORE_KEYNORM", "CompressDesc", "Req", "Model", "compress_desc",
            "compress_layout", "vc_compress", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
            "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes",
            "profile_enable", "profile_read", "HostBuffer", "PageableBuffer", "VC_PROF_DRAFT_ATTN",
-           "VC_PROF_VERIFY_ATTN", "VC_PROF_GEMM_SKINNY", "VC_PROF_GEMM_TILED", "VC_PROF_PREFILL_ATTN"]
+           "VC_PROF_VERIFY_ATTN", "VC_PROF_GEMM_SKINNY", "VC_PROF_GEMM_TILED", "VC_PROF_PREFILL_ATTN",
+           "VC_DEBUG_OFF", "VC_DEBUG_CHECK", "VC_DEBUG_DRY", "debug_mode", "debug_register", "debug_stats"]
+
+_DBG = False   # address-range checks on: every tensor handed to the library is registered
+_DRY = False   # dry run: host tensors stand in for device tensors
 
 
-def stream_handle(s: torch.cuda.Stream | None = None) -> int:
-    s = s or torch.cuda.current_stream()
+def stream_handle(s=None) -> int:
+    s = s or runtime.RT.current_stream()
     return s.cuda_stream
+
+
+def debug_register(*tensors) -> None:
+    """Register the storage of each tensor as a buffer the library may touch (range checks)."""
+    if not _DBG:
+        return
+    for t in tensors:
+        if t is not None:
+            st = t.untyped_storage()
+            call("vc_debug_register", st.data_ptr(), st.nbytes())
+
+
+def debug_mode(mode: int) -> None:
+    """VC_DEBUG_OFF, VC_DEBUG_CHECK (every launch's byte ranges checked against registered
+    buffers first) or VC_DEBUG_DRY (checked, then nothing launched; host tensors stand in for
+    device tensors).  In dry mode select runtime.DryRT() as well."""
+    global _DBG, _DRY
+    call("vc_debug_mode", mode)
+    _DBG, _DRY = mode != VC_DEBUG_OFF, mode == VC_DEBUG_DRY
+
+
+def debug_stats(reset: bool = False) -> dict:
+    st = DebugStats()
+    call("vc_debug_stats_read", C.byref(st), int(reset))
+    return {"launches": st.launches, "ranges": st.ranges, "violations": st.violations,
+            "pinned_bytes": st.pinned_bytes, "pinned_peak": st.pinned_peak}
 
 
 def ptr(t: torch.Tensor | None) -> int | None:
     if t is None:
         return None
-    if not t.is_cuda:
+    if not t.is_cuda and not _DRY:
         raise ValueError("expected a device tensor")
+    debug_register(t)
     return t.data_ptr()
 
 
@@ -63,8 +94,8 @@ def vc_compress(d: CompressDesc, k: torch.Tensor, v: torch.Tensor, q_obs: torch.
                 out: torch.Tensor | None = None) -> torch.Tensor:
     ob, wb = C.c_size_t(), C.c_size_t()
     call("vc_compress_size", C.byref(d), C.byref(ob), C.byref(wb))
-    if out is None:
-        out = torch.zeros(ob.value, dtype=torch.uint8, device=k.device)
+    if out is None:  # zeroed so that the bytes between sections are defined (not in a dry run)
+        out = (torch.empty if _DRY else torch.zeros)(ob.value, dtype=torch.uint8, device=k.device)
     ws = torch.empty(max(wb.value, 256), dtype=torch.uint8, device=k.device)
     call("vc_compress", C.byref(d), ptr(k), ptr(v), ptr(q_obs), ptr(out), out.numel(), ptr(ws), ws.numel(),
          stream_handle())
@@ -247,6 +278,7 @@ class PageableBuffer:
     def __init__(self, nbytes: int):
         self.t = torch.empty(nbytes, dtype=torch.uint8)
         self.nbytes = nbytes
+        debug_register(self.t)
 
     def data_ptr(self) -> int:
         return self.t.data_ptr()

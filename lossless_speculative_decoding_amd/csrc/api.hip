@@ -10,6 +10,7 @@
 
 #include "attention.h"
 #include "attention_quant.h"
+#include "bounds.h"
 #include "compress.h"
 #include "elementwise.h"
 #include "gemm.h"
@@ -62,7 +63,7 @@ ProfRec prof_begin(int kind, double bytes, double flops) {
   r.kind = kind;
   r.bytes = bytes;
   r.flops = flops;
-  if (g_prof_mask & (1u << kind)) {
+  if ((g_prof_mask & (1u << kind)) && !dbg_dry()) {
     r.a = prof_event();
     r.b = prof_event();
     if (!r.a || !r.b) r.a = r.b = nullptr;
@@ -113,6 +114,41 @@ constexpr int SPLIT_DRAFT = 512;
 
 inline const uint8_t* cptr(const void* p, int64_t off) { return static_cast<const uint8_t*>(p) + off; }
 inline uint8_t* mptr(void* p, int64_t off) { return static_cast<uint8_t*>(p) + off; }
+
+// A 2D asynchronous copy, its ranges checked (debug mode) and skipped in dry mode.
+vc_status copy2d(const char* what, void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
+                 size_t height, hipMemcpyKind kind, hipStream_t s) {
+  if (dbg_on()) {
+    if (vc_status st = dbg_check(what, {dbg_2d("destination", dst, dpitch, width, height),
+                                        dbg_2d("source", src, spitch, width, height)}))
+      return st;
+    if (dbg_dry()) return VC_OK;
+  }
+  VC_HIP(hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, kind, s));
+  return VC_OK;
+}
+
+// Device memory the library owns (the RoPE table, temporaries): registered for the range
+// checks; lazily mapped host memory in dry mode.
+vc_status dev_alloc(void** p, size_t bytes) {
+  if (dbg_dry()) {
+    *p = dbg_alloc(bytes, false);
+    VC_REQUIRE(*p != nullptr, VC_ERR_HIP, "dry run: host allocation of %zu bytes failed", bytes);
+    return VC_OK;
+  }
+  VC_HIP(hipMalloc(p, bytes));
+  dbg_register(*p, bytes);
+  return VC_OK;
+}
+void dev_free(void* p) {
+  if (!p) return;
+  if (dbg_dry()) {
+    dbg_free(p, false);
+    return;
+  }
+  dbg_forget(p);
+  (void)hipFree(p);
+}
 
 struct WsLayout {
   size_t h, a, q, o, m, y, att, tok, total;
@@ -254,7 +290,14 @@ vc_status head(const vc_model* m, int r0, int M, uint8_t* ws, const WsLayout& L,
   if ((st = gemm(a, m->w.lm_head, P, M, d.vocab, d.d_model, 1, d.dtype, s, pr.a, pr.b))) return st;
   prof_commit(pr);
   if ((st = k_argmax(P, M, d.vocab, out_tok, s))) return st;
-  if (logits_opt) VC_HIP(hipMemcpyAsync(logits_opt, P, size_t(M) * d.vocab * 4, hipMemcpyDeviceToDevice, s));
+  if (logits_opt) {
+    const int64_t bytes = int64_t(M) * d.vocab * 4;
+    if (dbg_on()) {
+      if ((st = dbg_check("logits copy", {{"destination", logits_opt, bytes}, {"source", P, bytes}}))) return st;
+      if (dbg_dry()) return VC_OK;
+    }
+    VC_HIP(hipMemcpyAsync(logits_opt, P, size_t(bytes), hipMemcpyDeviceToDevice, s));
+  }
   return VC_OK;
 }
 
@@ -318,6 +361,27 @@ vc_status comp_view(const void* comp, const vc_compress_desc* cd, CompView& v) {
   v.eb = cd->dtype == VC_BF16 ? 2 : 4;
   v.base = static_cast<const uint8_t*>(comp);
   return VC_OK;
+}
+
+// Debug mode: the whole buffers a request claims (tails of tail_cap rows per (layer, head), the
+// host rows, the token slots, the compressed blob), each measured from its own base pointer so
+// that a capacity larger than the allocation is caught even where a neighbouring buffer follows.
+vc_status dbg_request(const char* where, const vc_model* m, const vc_req& q, bool host_rows, int token_rows = 1) {
+  if (!dbg_on()) return VC_OK;
+  const vc_model_desc& d = m->d;
+  const int64_t per = int64_t(d.n_layers) * d.n_kv_heads * d.head_dim * m->eb;
+  vc_status st = dbg_check(where, {{"request tail K", q.tail_k, q.tail_k ? per * q.tail_cap : 0},
+                                   {"request tail V", q.tail_v, q.tail_v ? per * q.tail_cap : 0},
+                                   {"request token rows", q.rows, q.rows ? int64_t(token_rows) * 4 : 0}});
+  if (!st && host_rows)
+    st = dbg_check(where, {{"request host K rows", q.full_k_host, q.full_k_host ? per * q.full_cap : 0},
+                           {"request host V rows", q.full_v_host, q.full_v_host ? per * q.full_cap : 0}});
+  if (!st && q.comp && q.cd) {
+    vc_compress_layout lay;
+    if ((st = compress_layout(q.cd, &lay))) return st;
+    st = dbg_check(where, {{"compressed blob", q.comp, int64_t(lay.total)}});
+  }
+  return st;
 }
 
 // Draft attention for a batch of requests over (compressed main region, exact tail), one layer.
@@ -500,16 +564,16 @@ vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStr
   m->d = d;
   m->w = *w;
   m->eb = d.dtype == VC_BF16 ? 2 : 4;
-  hipError_t e = hipMalloc(&m->rope, size_t(d.max_pos) * d.head_dim * 4);
-  if (e != hipSuccess) {
+  void* rope = nullptr;
+  if (vc_status st = dev_alloc(&rope, size_t(d.max_pos) * d.head_dim * 4)) {
     delete m;
-    set_error("vc_model_create: hipMalloc of the RoPE table failed: %s", hipGetErrorString(e));
-    return VC_ERR_HIP;
+    return st;
   }
+  m->rope = static_cast<float*>(rope);
   vc_status st = k_rope_table(m->rope, d.max_pos, d.head_dim, double(d.rope_theta), s);
-  if (st == VC_OK && hipStreamSynchronize(s) != hipSuccess) st = VC_ERR_HIP;
+  if (st == VC_OK && !dbg_dry() && hipStreamSynchronize(s) != hipSuccess) st = VC_ERR_HIP;
   if (st) {
-    hipFree(m->rope);
+    dev_free(m->rope);
     delete m;
     return st;
   }
@@ -519,7 +583,7 @@ vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStr
 
 vc_status vc_model_destroy(vc_model* m) {
   if (!m) return VC_OK;
-  hipFree(m->rope);
+  dev_free(m->rope);
   delete m;
   return VC_OK;
 }
@@ -573,9 +637,11 @@ vc_status draft_step_impl(vc_model* m, const vc_req* reqs, int32_t n, float* log
     VC_REQUIRE(q.ctx_len + q.draft_idx < d.max_pos, VC_ERR_CAPACITY, "vc_draft_step: position beyond the RoPE table");
     tail_n[r] = q.n_tail + q.draft_idx + 1;
     max_keys = std::max(max_keys, views[r].lay.n_main + views[r].n_resid + tail_n[r]);
+    if (vc_status st = dbg_request("vc_draft_step", m, q, false, q.draft_idx + 2)) return st;
   }
   const WsLayout L = ws_layout(m, n, max_keys);
   VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_draft_step: workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (vc_status st = dbg_check("vc_draft_step", {{"workspace", ws, int64_t(ws_bytes)}})) return st;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   vc_status st;
   int32_t* tok_in = reinterpret_cast<int32_t*>(w8 + L.tok);
@@ -623,14 +689,19 @@ std::mutex g_scratch_mu;
 void* g_scratch_dev[VC_MAX_DEVICES] = {};
 
 vc_status scratch_of_current_device(void** out) {
-  int dev = -1;
-  VC_HIP(hipGetDevice(&dev));
+  int dev = 0;
+  if (!dbg_dry()) VC_HIP(hipGetDevice(&dev));
   VC_REQUIRE(dev >= 0 && dev < VC_MAX_DEVICES, VC_ERR_UNSUPPORTED, "static scratch: device %d beyond %d", dev,
              VC_MAX_DEVICES);
   std::lock_guard<std::mutex> lk(g_scratch_mu);
   if (!g_scratch_dev[dev]) {
     void* p = nullptr;
-    VC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(vc_static_scratch)));
+    if (dbg_dry()) {  // a host stand-in of the array's size
+      p = dbg_alloc(VC_STATIC_SCRATCH_BYTES, false);
+    } else {
+      VC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(vc_static_scratch)));
+      dbg_register(p, VC_STATIC_SCRATCH_BYTES);
+    }
     VC_REQUIRE(p != nullptr, VC_ERR_HIP, "static scratch: no device address");
     g_scratch_dev[dev] = p;
   }
@@ -717,6 +788,20 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
   VC_REQUIRE(ctx + n_rows <= d.max_pos, VC_ERR_CAPACITY, "vc_verify: position beyond the RoPE table");
   const WsLayout L = ws_layout(m, n_rows, ctx + n_rows);
   VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_verify: workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (dbg_on()) {
+    // the rows touched in each (layer, head) at the buffers' pitches (a caller may pass windows of
+    // a larger cache, as full-KV greedy decoding does)
+    const int64_t row = int64_t(d.head_dim) * m->eb, lh = int64_t(d.n_layers) * d.n_kv_heads;
+    if (vc_status st = dbg_request("vc_verify", m, *req, false)) return st;
+    if (vc_status st = dbg_check("vc_verify", {{"workspace", ws, int64_t(ws_bytes)},
+                                               dbg_2d("staged K", staged_k, staged_cap * row, hp.rows * row, lh),
+                                               dbg_2d("staged V", staged_v, staged_cap * row, hp.rows * row, lh),
+                                               dbg_2d("verify K rows", vtail_k, vtail_cap * row, n_rows * row, lh),
+                                               dbg_2d("verify V rows", vtail_v, vtail_cap * row, n_rows * row, lh),
+                                               {"tokens", tok, int64_t(n_rows) * 4},
+                                               {"argmax", out_argmax, int64_t(n_rows) * 4}}))
+      return st;
+  }
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   vc_status st;
   if ((st = k_embed(m->w.embed, tok, w8 + L.h, n_rows, d.d_model, d.vocab, d.dtype, s))) return st;
@@ -901,14 +986,17 @@ vc_status vc_commit(vc_model* m, vc_req* req, int32_t a, const void* vtail_k, co
     return VC_OK;
   }
   VC_REQUIRE(req->ctx_len + a + 1 <= req->full_cap, VC_ERR_CAPACITY, "vc_commit: full KV capacity");
-  if (after) VC_HIP(hipStreamWaitEvent(copy, after, 0));
+  if (after && !dbg_dry()) VC_HIP(hipStreamWaitEvent(copy, after, 0));
   if (req->full_k_host && req->full_v_host) {
-    VC_HIP(hipMemcpy2DAsync(mptr(req->full_k_host, int64_t(req->ctx_len) * row), size_t(req->full_cap) * row, vtail_k,
-                            size_t(vtail_cap) * row, size_t(a + 1) * row, size_t(d.n_layers) * d.n_kv_heads,
-                            hipMemcpyDeviceToHost, copy));
-    VC_HIP(hipMemcpy2DAsync(mptr(req->full_v_host, int64_t(req->ctx_len) * row), size_t(req->full_cap) * row, vtail_v,
-                            size_t(vtail_cap) * row, size_t(a + 1) * row, size_t(d.n_layers) * d.n_kv_heads,
-                            hipMemcpyDeviceToHost, copy));
+    const size_t h = size_t(d.n_layers) * d.n_kv_heads;
+    if (vc_status st = copy2d("commit K rows to the host", mptr(req->full_k_host, int64_t(req->ctx_len) * row),
+                              size_t(req->full_cap) * row, vtail_k, size_t(vtail_cap) * row, size_t(a + 1) * row, h,
+                              hipMemcpyDeviceToHost, copy))
+      return st;
+    if (vc_status st = copy2d("commit V rows to the host", mptr(req->full_v_host, int64_t(req->ctx_len) * row),
+                              size_t(req->full_cap) * row, vtail_v, size_t(vtail_cap) * row, size_t(a + 1) * row, h,
+                              hipMemcpyDeviceToHost, copy))
+      return st;
   }
   req->ctx_len += a + 1;
   req->n_tail += a + 1;
@@ -927,27 +1015,45 @@ vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, i
   const int rows = hp.rows;
   VC_REQUIRE(slot_cap >= rows && req->full_cap >= rows, VC_ERR_CAPACITY, "vc_stage: slot %d / host %d < %d rows",
              slot_cap, req->full_cap, rows);
+  if (dbg_on()) {
+    const int64_t per = int64_t(d.n_layers) * d.n_kv_heads * d.head_dim * m->eb;
+    if (vc_status st = dbg_request("vc_stage", m, *req, true)) return st;
+    if (vc_status st = dbg_check("vc_stage", {{"slot K", slot_k, per * slot_cap}, {"slot V", slot_v, per * slot_cap}}))
+      return st;
+  }
   if (l0 == l1 || rows == 0) return VC_OK;
   const size_t row = size_t(d.head_dim) * m->eb;
   const int64_t lo_src = int64_t(l0) * d.n_kv_heads * req->full_cap * row;
   const int64_t lo_dst = int64_t(l0) * d.n_kv_heads * slot_cap * row;
   const size_t height = size_t(l1 - l0) * d.n_kv_heads;
-  VC_HIP(hipMemcpy2DAsync(mptr(slot_k, lo_dst), size_t(slot_cap) * row, cptr(req->full_k_host, lo_src),
-                          size_t(req->full_cap) * row, size_t(rows) * row, height, hipMemcpyHostToDevice, copy));
-  VC_HIP(hipMemcpy2DAsync(mptr(slot_v, lo_dst), size_t(slot_cap) * row, cptr(req->full_v_host, lo_src),
-                          size_t(req->full_cap) * row, size_t(rows) * row, height, hipMemcpyHostToDevice, copy));
-  return VC_OK;
+  if (vc_status st = copy2d("stage K rows", mptr(slot_k, lo_dst), size_t(slot_cap) * row, cptr(req->full_k_host, lo_src),
+                            size_t(req->full_cap) * row, size_t(rows) * row, height, hipMemcpyHostToDevice, copy))
+    return st;
+  return copy2d("stage V rows", mptr(slot_v, lo_dst), size_t(slot_cap) * row, cptr(req->full_v_host, lo_src),
+                size_t(req->full_cap) * row, size_t(rows) * row, height, hipMemcpyHostToDevice, copy);
 }
 
 vc_status vc_host_alloc(size_t bytes, void** out_host) {
   VC_REQUIRE(out_host != nullptr && bytes > 0, VC_ERR_ARG, "vc_host_alloc: bad arguments");
   *out_host = nullptr;
+  if (dbg_dry()) {
+    *out_host = dbg_alloc(bytes, true);
+    VC_REQUIRE(*out_host != nullptr, VC_ERR_HIP, "dry run: host allocation of %zu bytes failed", bytes);
+    return VC_OK;
+  }
   VC_HIP(hipHostMalloc(out_host, bytes, hipHostMallocDefault));
+  dbg_register(*out_host, bytes);
   return VC_OK;
 }
 
 vc_status vc_host_free(void* host) {
-  if (host) VC_HIP(hipHostFree(host));
+  if (!host) return VC_OK;
+  if (dbg_dry()) {
+    dbg_free(host, true);
+    return VC_OK;
+  }
+  dbg_forget(host);
+  VC_HIP(hipHostFree(host));
   return VC_OK;
 }
 
@@ -972,7 +1078,7 @@ vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const vo
       if (hp.rows == 0) return VC_OK;
       const size_t lbytes = size_t(d.n_kv_heads) * hp.rows * row;
       void* tmp = nullptr;
-      VC_HIP(hipMalloc(&tmp, 2 * lbytes));
+      if (vc_status st0 = dev_alloc(&tmp, 2 * lbytes)) return st0;
       vc_status st = VC_OK;
       for (int l = 0; l < d.n_layers && st == VC_OK; l++) {
         for (int kv = 0; kv < 2 && st == VC_OK; kv++) {
@@ -981,29 +1087,24 @@ vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const vo
                               hp.rows, s);
           if (st) break;
           void* host = kv ? req->full_v_host : req->full_k_host;
-          const hipError_t e = hipMemcpy2DAsync(mptr(host, int64_t(l) * d.n_kv_heads * req->full_cap * row),
-                                                size_t(req->full_cap) * row, dst, size_t(hp.rows) * row,
-                                                size_t(hp.rows) * row, d.n_kv_heads, hipMemcpyDeviceToHost, s);
-          if (e != hipSuccess) {
-            set_error("vc_offload: copy failed: %s", hipGetErrorString(e));
-            st = VC_ERR_HIP;
-          }
+          st = copy2d("offload dropped rows", mptr(host, int64_t(l) * d.n_kv_heads * req->full_cap * row),
+                      size_t(req->full_cap) * row, dst, size_t(hp.rows) * row, size_t(hp.rows) * row, d.n_kv_heads,
+                      hipMemcpyDeviceToHost, s);
         }
       }
-      const hipError_t e1 = hipStreamSynchronize(s);
-      const hipError_t e2 = hipFree(tmp);
+      const hipError_t e1 = dbg_dry() ? hipSuccess : hipStreamSynchronize(s);
+      dev_free(tmp);
       if (st) return st;
       VC_HIP(e1);
-      VC_HIP(e2);
       return VC_OK;
     }
   }
   VC_REQUIRE(T <= req->full_cap, VC_ERR_CAPACITY, "vc_offload: host capacity %d < %d rows", req->full_cap, T);
-  VC_HIP(hipMemcpy2DAsync(req->full_k_host, size_t(req->full_cap) * row, k_dev, size_t(src_cap) * row, size_t(T) * row,
-                          height, hipMemcpyDeviceToHost, s));
-  VC_HIP(hipMemcpy2DAsync(req->full_v_host, size_t(req->full_cap) * row, v_dev, size_t(src_cap) * row, size_t(T) * row,
-                          height, hipMemcpyDeviceToHost, s));
-  return VC_OK;
+  if (vc_status st = copy2d("offload K rows", req->full_k_host, size_t(req->full_cap) * row, k_dev, size_t(src_cap) * row,
+                            size_t(T) * row, height, hipMemcpyDeviceToHost, s))
+    return st;
+  return copy2d("offload V rows", req->full_v_host, size_t(req->full_cap) * row, v_dev, size_t(src_cap) * row,
+                size_t(T) * row, height, hipMemcpyDeviceToHost, s);
 }
 
 // ---------------------------------------------------------------- single-layer attention

@@ -90,6 +90,11 @@ __device__ __forceinline__ const E* key_row(const AttnReq& R, int j, int t, bool
   return base + j * R.c.hstride + int64_t(t) * D;
 }
 
+// Address-range check (debug mode) of the rows [0, rows) of every KV head of a segment.
+vc_status dbg_kv_seg(const char* kernel, const char* what, const KVSeg& g, int Hkv, int D, int eb, int64_t rows);
+// Of one many-row or decode request: queries, segments (with a token-drop split), partials.
+vc_status dbg_attn_req(const char* kernel, const AttnReq& R, int Hq, int Hkv, int D, int eb);
+
 // ev_start / ev_stop (may be null) in the launchers below: HIP events that take the
 // kernel's own start and end time (hipExtLaunchKernelGGL), for live kernel timing without
 // marker-packet gaps; when nothing is launched they are recorded on the stream instead.

@@ -6,6 +6,7 @@
 // (two MFMAs), which keeps about 22 significant bits of every weight; QK^T is bf16 x
 // bf16 with exact products.
 #include "attention.h"
+#include "bounds.h"
 
 namespace vc {
 
@@ -358,6 +359,40 @@ __global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
 
 }  // namespace
 
+vc_status dbg_kv_seg(const char* kernel, const char* what, const KVSeg& g, int Hkv, int D, int eb, int64_t rows) {
+  if (rows <= 0) return VC_OK;
+  char wk[96], wv[96];
+  snprintf(wk, sizeof(wk), "%s K rows", what);
+  snprintf(wv, sizeof(wv), "%s V rows", what);
+  return dbg_check(kernel, {dbg_2d(wk, g.k, g.hstride * eb, rows * D * eb, Hkv),
+                            dbg_2d(wv, g.v, g.hstride * eb, rows * D * eb, Hkv)});
+}
+
+vc_status dbg_attn_req(const char* kernel, const AttnReq& R, int Hq, int Hkv, int D, int eb) {
+  if (R.s_off < 0 || R.s_off + R.n_splits > R.s_total)
+    return dbg_fail("%s: partial slots %d..%d beyond the %d per row", kernel, R.s_off, R.s_off + R.n_splits - 1,
+                    R.s_total);
+  vc_status st = dbg_check(kernel, {{"queries", R.q, int64_t(R.n_rows) * Hq * D * eb},
+                                    {"partials", R.part, int64_t(R.n_rows) * Hq * R.s_total * (D + 2) * 4}});
+  if (st) return st;
+  if (R.mix.mask) {
+    // token-drop split of segment a: kept rows [0, kk) on the device, the other a.n - kk staged
+    const int64_t kk = R.mix.hstride / D;
+    if (int64_t(R.mix.nt) * 64 < R.a.n) return dbg_fail("%s: tile map of %d tiles for %d positions", kernel, R.mix.nt, R.a.n);
+    if (kk > R.a.n) return dbg_fail("%s: %lld kept rows for %d positions", kernel, (long long)kk, R.a.n);
+    const KVSeg kept{R.mix.k, R.mix.v, R.mix.hstride, 0, 0};
+    if ((st = dbg_kv_seg(kernel, "kept prompt", kept, Hkv, D, eb, kk))) return st;
+    if ((st = dbg_kv_seg(kernel, "staged prompt", R.a, Hkv, D, eb, R.a.n - kk))) return st;
+    if ((st = dbg_check(kernel, {{"kept-tile masks", R.mix.mask, int64_t(Hkv) * R.mix.nt * 8},
+                                 {"kept-tile counts", R.mix.cnt, int64_t(Hkv) * R.mix.nt * 4}})))
+      return st;
+  } else if ((st = dbg_kv_seg(kernel, "segment a", R.a, Hkv, D, eb, R.a.n))) {
+    return st;
+  }
+  if ((st = dbg_kv_seg(kernel, "segment b", R.b, Hkv, D, eb, R.b.n))) return st;
+  return dbg_kv_seg(kernel, "segment c", R.c, Hkv, D, eb, R.c.n);
+}
+
 vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (a.n_req <= 0 || a.max_splits <= 0) {
     VC_EVENTS_IF_EMPTY(ev_start, ev_stop, s);
@@ -372,7 +407,14 @@ vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s, hipEvent_t ev_sta
                VC_ERR_UNSUPPORTED, "decode attention: segment above 2 GiB per head");
     VC_REQUIRE(int64_t(q.n_splits) * a.split_len >= decode_keys(q.a.n, q.b.n), VC_ERR_ARG,
                "decode attention: %d splits do not cover the keys", q.n_splits);
+    if (dbg_on()) {
+      AttnReq d = q;
+      d.c.n = 0;  // the decode kernel reads segments a and b only
+      d.mix.mask = nullptr;
+      if (vc_status st = dbg_attn_req("attn_decode_bf16", d, a.Hq, a.Hkv, 128, 2)) return st;
+    }
   }
+  if (dbg_dry()) return VC_OK;
   hipExtLaunchKernelGGL(attn_decode_bf16_kernel, dim3(a.Hkv, a.max_splits, a.n_req), dim3(256), 0, s, ev_start,
                         ev_stop, 0, a);
   VC_LAUNCH_CHECK();
@@ -382,6 +424,16 @@ vc_status launch_attn_decode(const AttnArgs& a, hipStream_t s, hipEvent_t ev_sta
 
 vc_status launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.n_req <= 0) return VC_OK;
+  if (dbg_on()) {
+    const int64_t rows = int64_t(a.n_rows) * a.Hq, ob = a.out_dtype == VC_BF16 ? 2 : 4;
+    for (int r = 0; r < a.n_req; r++) {
+      if (a.s_used[r] > a.s_total) return dbg_fail("combine: %d slots used of %d", a.s_used[r], a.s_total);
+      if (vc_status st = dbg_check("combine", {{"partials", a.part[r], rows * a.s_total * (a.head_dim + 2) * 4},
+                                               {"output", a.out[r], rows * a.head_dim * ob}}))
+        return st;
+    }
+    if (dbg_dry()) return VC_OK;
+  }
   dim3 grid(a.n_rows * a.Hq, a.n_req);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(128), 0, s, a);
   VC_LAUNCH_CHECK();

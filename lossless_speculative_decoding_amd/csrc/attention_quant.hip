@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "attention_quant.h"
+#include "bounds.h"
 
 namespace vc {
 
@@ -716,6 +717,27 @@ vc_status launch_attn_quant(const QuantArgs& a, hipStream_t s, hipEvent_t ev_sta
              QUANT_QP_BYTES / 512);
   for (int r = 0; r < a.n_req; r++)
     VC_REQUIRE(a.r[r].m.tq % 64 == 0 && a.r[r].m.tq % a.group == 0, VC_ERR_ARG, "quantized rows not whole groups");
+  if (dbg_on()) {
+    for (int r = 0; r < a.n_req; r++) {
+      const QuantReq& q = a.r[r];
+      const int64_t tq = q.m.tq, cb = int64_t(a.Hkv) * tq * D * a.bits / 8;
+      const int64_t kzb = int64_t(a.Hkv) * (tq / a.group) * D * 2, vzb = int64_t(a.Hkv) * tq * (D / a.group) * 2;
+      // quantized splits s < n_splits cover keys [s split_len, min((s + 1) split_len, tq)); the exact
+      // rows go to slot n_splits
+      if (int64_t(q.n_splits) * a.split_len < tq || q.n_splits + 1 > q.s_total || q.n_splits > a.max_splits)
+        return dbg_fail("attn_quant: request %d has %d splits of %d keys for %lld rows, %d slots", r, q.n_splits,
+                        a.split_len, (long long)tq, q.s_total);
+      if (vc_status st = dbg_check("attn_quant", {{"query", q.q, int64_t(a.Hq) * D * 2},
+                                                  {"K codes", q.m.kc, cb}, {"V codes", q.m.vc, cb},
+                                                  {"K scales", q.m.ks, kzb}, {"K zeros", q.m.kz, kzb},
+                                                  {"V scales", q.m.vs, vzb}, {"V zeros", q.m.vz, vzb},
+                                                  {"partials", q.part, int64_t(a.Hq) * q.s_total * (D + 2) * 4}}))
+        return st;
+      if (vc_status st = dbg_kv_seg("attn_quant", "residual", q.a, a.Hkv, D, 2, q.a.n)) return st;
+      if (vc_status st = dbg_kv_seg("attn_quant", "tail", q.b, a.Hkv, D, 2, q.b.n)) return st;
+    }
+    if (dbg_dry()) return VC_OK;
+  }
   dim3 grid(a.Hkv, a.max_splits + 1, a.n_req);
   const bool g64 = a.group == 64;
   switch (a.bits) {

@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "attention.h"
+#include "bounds.h"
 
 namespace vc {
 
@@ -443,6 +444,12 @@ vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, hipEvent_t ev
   }
   int max_qrows = 0;
   for (int i = 0; i < a.n_req; i++) max_qrows = max(max_qrows, a.r[i].n_rows * a.G);
+  if (dbg_on()) {
+    const int eb = dtype == VC_BF16 ? 2 : 4;
+    for (int i = 0; i < a.n_req; i++)
+      if (vc_status st = dbg_attn_req("attn_rows", a.r[i], a.Hq, a.Hkv, a.head_dim, eb)) return st;
+    if (dbg_dry()) return VC_OK;
+  }
   if (dtype == VC_BF16) {
     VC_REQUIRE(a.head_dim == 128, VC_ERR_UNSUPPORTED, "bf16 attention needs head_dim 128 (got %d)", a.head_dim);
     // row blocks per wave: enough for the largest request up to 3 (a 192-row group)

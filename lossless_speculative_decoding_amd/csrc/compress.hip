@@ -6,6 +6,7 @@
 //   zero = fp16(min); scale = fp16((max - min) / (2^b - 1));
 //   code = scale == 0 ? 0 : clamp(rint((x - zero) / scale), 0, 2^b - 1).
 #include "attention.h"
+#include "bounds.h"
 #include "compress.h"
 
 namespace vc {
@@ -465,6 +466,25 @@ vc_status compress_run(const vc_compress_desc* d, const void* k, const void* v, 
   const int D = d->head_dim, T = d->seq_len;
   const int eb = d->dtype == VC_BF16 ? 2 : 4;
   uint8_t* o = static_cast<uint8_t*>(out);
+  if (dbg_on()) {
+    // prompt rows [0, T) of every (layer, head), the blob, and (token drop) the observation
+    // queries and the workspace; the observation attention checks its own launch below
+    const int64_t row = int64_t(D) * eb, pitch = int64_t(d->src_cap) * row;
+    size_t need = 0;
+    compress_ws_bytes(d, &need);
+    const bool obs = d->kind == VC_TOKDROP && d->score == VC_SCORE_ATTN;
+    const int64_t W = std::min(d->obs_window, T);
+    if (vc_status st = dbg_check("compress", {dbg_2d("prompt K", k, pitch, T * row, n_lh),
+                                              dbg_2d("prompt V", v, pitch, T * row, n_lh),
+                                              {"blob", out, int64_t(L.total)},
+                                              {"workspace", ws, int64_t(need)},
+                                              {"observation queries", q_obs,
+                                               obs ? int64_t(d->n_layers) * W * d->n_q_heads * row : 0}}))
+      return st;
+  }
+  if (dbg_dry() && !(d->kind == VC_TOKDROP && d->score == VC_SCORE_ATTN && L.n_main - std::min(d->keep_recent, T) <
+                                                                              T - std::min(d->keep_recent, T)))
+    return VC_OK;
   if (d->kind == VC_QUANT) {
     const int tq = L.n_main, ng = tq / d->group, b = d->bits;
     uint16_t* ks = reinterpret_cast<uint16_t*>(o + L.ks);
@@ -560,6 +580,7 @@ vc_status compress_run(const vc_compress_desc* d, const void* k, const void* v, 
       st = launch_attn(a, d->dtype, s);
       if (st) return st;
     }
+    if (dbg_dry()) return VC_OK;
     {
       const int n = int(int64_t(d->n_layers) * rows_heads);
       hipLaunchKernelGGL(merge_ml_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, part, n, S, S, D, ml);
@@ -602,6 +623,15 @@ vc_status gather_dropped(const vc_compress_desc* d, const void* comp, const void
   if (L.n_host == 0) return VC_OK;
   const int eb = d->dtype == VC_BF16 ? 2 : 4;
   const uint8_t* o = static_cast<const uint8_t*>(comp);
+  {
+    const int64_t row = int64_t(d->head_dim) * eb, nt = L.n_tiles;
+    const int64_t lh_all = int64_t(d->n_layers) * d->n_kv_heads;
+    VC_DBG_LAUNCH("gather_dropped",
+                  dbg_2d("prompt rows", static_cast<const uint8_t*>(src) + lh0 * int64_t(src_cap) * row,
+                         int64_t(src_cap) * row, d->seq_len * row, n_lh),
+                  dbg_2d("dropped rows", dst, int64_t(dst_cap) * row, int64_t(dst_cap) * row, n_lh),
+                  {"kept-tile masks", o + L.keep_mask, lh_all * nt * 8}, {"kept-tile counts", o + L.keep_cnt, lh_all * nt * 4});
+  }
   hipLaunchKernelGGL(gather_dropped_kernel, dim3(d->seq_len, n_lh), dim3(64), 0, s, static_cast<const uint8_t*>(src),
                      src_cap, d->seq_len, d->head_dim * eb, reinterpret_cast<const uint64_t*>(o + L.keep_mask),
                      reinterpret_cast<const int32_t*>(o + L.keep_cnt), L.n_tiles, lh0, static_cast<uint8_t*>(dst),

@@ -1,4 +1,5 @@
 // Row-wise kernels of the forward pass and the accept / commit steps.
+#include "bounds.h"
 #include "elementwise.h"
 
 namespace vc {
@@ -200,27 +201,41 @@ __global__ void copy_words_kernel(const uint32_t* src, uint32_t* dst, int64_t n)
 
 }  // namespace
 
+static inline int64_t ebytes(int dt) { return dt == VC_BF16 ? 2 : 4; }
+
 vc_status k_embed(const void* E, const int32_t* tok, void* h, int M, int d, int V, int dt, hipStream_t s) {
+  VC_DBG_LAUNCH("embed", {"embedding table", E, int64_t(V) * d * ebytes(dt)}, {"tokens", tok, int64_t(M) * 4},
+                {"rows", h, int64_t(M) * d * ebytes(dt)});
   hipLaunchKernelGGL(embed_kernel, dim3(cdiv(d, 256), M), dim3(256), 0, s, E, tok, h, d, V, dt);
   VC_LAUNCH_CHECK();
   return VC_OK;
 }
 vc_status k_rmsnorm(const void* x, const void* g, void* y, int M, int d, float eps, int dt, hipStream_t s) {
+  VC_DBG_LAUNCH("rmsnorm", {"input", x, int64_t(M) * d * ebytes(dt)}, {"gain", g, int64_t(d) * ebytes(dt)},
+                {"output", y, int64_t(M) * d * ebytes(dt)});
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, g, y, d, eps, dt);
   VC_LAUNCH_CHECK();
   return VC_OK;
 }
 vc_status k_argmax(const float* logits, int M, int V, int32_t* out, hipStream_t s) {
+  VC_DBG_LAUNCH("argmax", {"logits", logits, int64_t(M) * V * 4}, {"tokens", out, int64_t(M) * 4});
   hipLaunchKernelGGL(argmax_kernel, dim3(M), dim3(1024), 0, s, logits, V, out);
   VC_LAUNCH_CHECK();
   return VC_OK;
 }
 vc_status k_accept(int32_t* rows, const int32_t* verified, int x, int32_t* result, hipStream_t s) {
+  VC_DBG_LAUNCH("accept", {"rows", rows, int64_t(x + 1) * 4}, {"verified", verified, int64_t(x + 1) * 4},
+                {"result", result, int64_t(x + 2) * 4});
   hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, s, rows, verified, x, result);
   VC_LAUNCH_CHECK();
   return VC_OK;
 }
 vc_status k_gather_tok(const int32_t* const* src, int n, int32_t* tok, hipStream_t s) {
+  if (dbg_on()) {
+    for (int r = 0; r < n; r++)
+      if (vc_status st = dbg_check_one("gather_tok", {"request token slot", src[r], 4})) return st;
+  }
+  VC_DBG_LAUNCH("gather_tok", {"tokens", tok, int64_t(n) * 4});
   TokPtrs p{};
   p.n = n;
   for (int r = 0; r < n; r++) p.src[r] = src[r];
@@ -229,6 +244,11 @@ vc_status k_gather_tok(const int32_t* const* src, int n, int32_t* tok, hipStream
   return VC_OK;
 }
 vc_status k_scatter_tok(int32_t* const* dst, int n, const int32_t* out, hipStream_t s) {
+  if (dbg_on()) {
+    for (int r = 0; r < n; r++)
+      if (vc_status st = dbg_check_one("scatter_tok", {"request token slot", dst[r], 4})) return st;
+  }
+  VC_DBG_LAUNCH("scatter_tok", {"tokens", out, int64_t(n) * 4});
   TokPtrs p{};
   p.n = n;
   for (int r = 0; r < n; r++) p.dst[r] = dst[r];
@@ -238,6 +258,13 @@ vc_status k_scatter_tok(int32_t* const* dst, int n, const int32_t* out, hipStrea
 }
 vc_status k_commit_rows(const void* vk, const void* vv, int vcap, void* tk, void* tv, int tcap, int n_tail,
                         int row_bytes, int n_lh, int max_rows, const int32_t* result, hipStream_t s) {
+  // rows 0..result[0] (at most max_rows) of every (layer, head)
+  const int64_t rb = row_bytes;
+  VC_DBG_LAUNCH("commit_rows", dbg_2d("verified K rows", vk, vcap * rb, max_rows * rb, n_lh),
+                dbg_2d("verified V rows", vv, vcap * rb, max_rows * rb, n_lh),
+                dbg_2d("tail K rows", static_cast<uint8_t*>(tk) + n_tail * rb, tcap * rb, max_rows * rb, n_lh),
+                dbg_2d("tail V rows", static_cast<uint8_t*>(tv) + n_tail * rb, tcap * rb, max_rows * rb, n_lh),
+                {"accept result", result, 4});
   hipLaunchKernelGGL(commit_rows_kernel, dim3(1, max_rows, n_lh), dim3(64), 0, s, static_cast<const uint8_t*>(vk),
                      static_cast<const uint8_t*>(vv), vcap, static_cast<uint8_t*>(tk), static_cast<uint8_t*>(tv), tcap,
                      n_tail, row_bytes, n_lh, result);
@@ -245,6 +272,7 @@ vc_status k_commit_rows(const void* vk, const void* vv, int vcap, void* tk, void
   return VC_OK;
 }
 vc_status k_rope_table(float* tab, int max_pos, int D, double theta, hipStream_t s) {
+  VC_DBG_LAUNCH("rope_table", {"table", tab, int64_t(max_pos) * D * 4});
   const int64_t n = int64_t(max_pos) * (D / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, tab, max_pos, D, theta);
   VC_LAUNCH_CHECK();
@@ -253,6 +281,7 @@ vc_status k_rope_table(float* tab, int max_pos, int D, double theta, hipStream_t
 vc_status k_copy_words(const void* src, void* dst, int64_t bytes, hipStream_t s) {
   const int64_t n = bytes / 4;
   if (n == 0) return VC_OK;
+  VC_DBG_LAUNCH("copy_words", {"source", src, n * 4}, {"destination", dst, n * 4});
   hipLaunchKernelGGL(copy_words_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, static_cast<const uint32_t*>(src),
                      static_cast<uint32_t*>(dst), n);
   VC_LAUNCH_CHECK();

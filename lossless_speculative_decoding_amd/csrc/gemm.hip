@@ -17,6 +17,7 @@
 #include <mutex>
 #include <tuple>
 
+#include "bounds.h"
 #include "gemm.h"
 
 namespace vc {
@@ -335,6 +336,7 @@ vc_status lt_gemm(const void* X, const void* W, float* P, int M, int N, int K, h
   if (!L.h) {
     VC_LT(hipblasLtCreate(&L.h));
     VC_HIP(hipMalloc(&L.ws, LT_WS_BYTES));
+    dbg_register(L.ws, LT_WS_BYTES);
   }
   const auto key = std::make_tuple(M, N, K);
   auto it = L.shape.find(key);
@@ -369,6 +371,12 @@ int gemm_splits(int M, int N, int K, int dtype) {
 vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int S, int dtype, hipStream_t s,
                hipEvent_t ev_start, hipEvent_t ev_stop) {
   VC_REQUIRE(M > 0 && N > 0 && K > 0, VC_ERR_ARG, "gemm: bad shape %d x %d x %d", M, N, K);
+  {
+    const int64_t eb = dtype == VC_BF16 ? 2 : 4;
+    const int64_t parts = (dtype == VC_BF16 && M <= 64) ? S : 1;  // split-K partials of the skinny kernel
+    VC_DBG_LAUNCH("gemm", {"activations", X, int64_t(M) * K * eb}, {"weights", W, int64_t(N) * K * eb},
+                  {"partials", P, parts * M * N * 4});
+  }
   if (dtype == VC_BF16) {
     VC_REQUIRE(K % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: K=%d not a multiple of 128", K);
     if (M <= 64) {
@@ -410,6 +418,35 @@ vc_status epilogue(const EpiArgs& a, hipStream_t s) {
     default: units = a.N; break;
   }
   VC_REQUIRE(!a.batched || a.M <= EPI_MAX_ROWS, VC_ERR_ARG, "epilogue: too many batched rows");
+  if (dbg_on()) {
+    const int64_t eb = a.dtype == VC_BF16 ? 2 : 4;
+    const int64_t M = a.M, N = a.N;
+    if (vc_status st = dbg_check_one("epilogue", {"partials", a.P, int64_t(a.S) * M * N * 4})) return st;
+    vc_status st = VC_OK;
+    if (a.mode == EPI_RESID) st = dbg_check("epilogue", {{"residual", a.out, M * N * eb}});
+    else if (a.mode == EPI_SWIGLU) st = dbg_check("epilogue", {{"ffn activations", a.out, M * (N / 2) * eb}});
+    else if (a.mode == EPI_COPY) st = dbg_check("epilogue", {{"output", a.out, M * N * 4}});
+    else {
+      const int64_t D = a.D, row = D * eb;
+      int max_pos = a.pos0 + a.M - 1;
+      if (a.batched)
+        for (int r = 0; r < a.M; r++) max_pos = r ? std::max(max_pos, a.pos[r]) : a.pos[r];
+      st = dbg_check("epilogue", {{"queries", a.q_out, M * a.Hq * row}, {"RoPE table", a.rope, (max_pos + 1) * D * 4}});
+      for (int r = 0; r < a.M && !st && a.batched; r++) {
+        st = dbg_check_one("epilogue", dbg_2d("new K row", a.krow[r], int64_t(a.rpitch[r]) * row, row, a.Hkv));
+        if (!st) st = dbg_check_one("epilogue", dbg_2d("new V row", a.vrow[r], int64_t(a.rpitch[r]) * row, row, a.Hkv));
+      }
+      if (!st && !a.batched) {
+        st = dbg_check_one("epilogue", dbg_2d("new K rows", static_cast<uint8_t*>(a.kbase) + a.row0 * row,
+                                              int64_t(a.pitch) * row, M * row, a.Hkv));
+        if (!st)
+          st = dbg_check_one("epilogue", dbg_2d("new V rows", static_cast<uint8_t*>(a.vbase) + a.row0 * row,
+                                                int64_t(a.pitch) * row, M * row, a.Hkv));
+      }
+    }
+    if (st) return st;
+    if (dbg_dry()) return VC_OK;
+  }
   hipLaunchKernelGGL(epilogue_kernel, dim3(cdiv(units, 256), a.M), dim3(256), 0, s, a);
   VC_LAUNCH_CHECK();
   return VC_OK;

@@ -6,6 +6,7 @@
 // Draws are evaluated in float64 and rounded float64 -> float32 -> bf16
 // (round to nearest even at each step), the same recipe as the host-side
 // generator used by the tests, which compare the two bit for bit.
+#include "bounds.h"
 #include "common.h"
 
 namespace vc {
@@ -75,6 +76,7 @@ extern "C" vc_status vc_synth_xavier(void* dst, int32_t dtype, int64_t n, uint32
   VC_REQUIRE(seed < 256 && stream < (1u << 24) && start >= 0 && start + n <= (int64_t(1) << 32), VC_ERR_ARG,
              "vc_synth_xavier: counter out of range");
   if (n == 0) return VC_OK;
+  VC_DBG_LAUNCH("synth_xavier", {"output", dst, n * (dtype == VC_BF16 ? 2 : 4)});
   const double a = sqrt(6.0 / double(fan_in + fan_out));
   hipLaunchKernelGGL(xavier_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, dst, dtype, n, stream, seed, start, a);
   VC_LAUNCH_CHECK();
@@ -88,6 +90,8 @@ extern "C" vc_status vc_synth_normal_heads(void* dst, int32_t B, int32_t H, int3
   const int64_t n = int64_t(B) * H * rows * D;
   VC_REQUIRE(2 * n <= (int64_t(1) << 32) && seed < 256 && stream < (1u << 24), VC_ERR_ARG,
              "vc_synth_normal_heads: counter out of range");
+  VC_DBG_LAUNCH("synth_normal_heads", {"output", dst, n * 2},
+                {"outlier channels", outl, outl ? int64_t(B) * H * n_outl * 4 : 0});
   hipLaunchKernelGGL(normal_heads_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, static_cast<uint16_t*>(dst), n, H,
                      rows, D, stream, seed, outl, n_outl, double(outl_scale));
   VC_LAUNCH_CHECK();
@@ -99,6 +103,7 @@ extern "C" vc_status vc_synth_ids(int32_t* dst, int64_t n, uint32_t stream, uint
   VC_REQUIRE(dst != nullptr && n >= 0 && vocab > 0, VC_ERR_ARG, "vc_synth_ids: bad arguments");
   VC_REQUIRE(n <= (int64_t(1) << 32) && seed < 256 && stream < (1u << 24), VC_ERR_ARG, "vc_synth_ids: counter range");
   if (n == 0) return VC_OK;
+  VC_DBG_LAUNCH("synth_ids", {"output", dst, n * 4});
   hipLaunchKernelGGL(ids_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, dst, n, stream, seed, uint32_t(vocab));
   VC_LAUNCH_CHECK();
   return VC_OK;
@@ -107,6 +112,7 @@ extern "C" vc_status vc_synth_ids(int32_t* dst, int64_t n, uint32_t stream, uint
 extern "C" vc_status vc_synth_fill(void* dst, int32_t dtype, int64_t n, float value, hipStream_t s) {
   VC_REQUIRE(dst != nullptr && n >= 0, VC_ERR_ARG, "vc_synth_fill: bad arguments");
   if (n == 0) return VC_OK;
+  VC_DBG_LAUNCH("synth_fill", {"output", dst, n * (dtype == VC_BF16 ? 2 : 4)});
   hipLaunchKernelGGL(fill_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, dst, dtype, n, value);
   VC_LAUNCH_CHECK();
   return VC_OK;

@@ -30,6 +30,7 @@ import torch
 import synth
 
 from . import binding as B
+from . import runtime
 from ._vc import Req
 
 DRAFT, WAIT_SLOT, ACCEPTING, DONE = range(4)
@@ -114,6 +115,7 @@ class Request:
     acc_ev: object = None
     budget: int = -1                   # verifications it may still issue (-1: unlimited; 0: parked)
     x_cur: int = 0                     # this round's draft length (x unless adaptive)
+    n_verified: int = 0                # verifications issued
     rounds: list = field(default_factory=list)  # per-round record (Engine(record=True))
     rec_host: torch.Tensor = None      # pinned [2][x + 1]: this round's rows and verified tokens
 
@@ -139,7 +141,7 @@ class Engine:
         self.chunk = chunk
         self.device = device
         self.reqs: list[Request] = []
-        self.copy_stream = torch.cuda.Stream(device=device)
+        self.copy_stream = runtime.RT.Stream(device=device)
         self.slots = []
         self.slot_free_ev = []
         self.ws_draft = None
@@ -162,8 +164,10 @@ class Engine:
         W = min(self.spec.obs_window, T)
         q_obs = torch.empty(L, W, Hq, D, dtype=self.dt, device=self.device)
         g0 = torch.empty(1, dtype=torch.int32, device=self.device)
-        ws = self.m.workspace(min(self.chunk, T), T)
+        ws = self.m.workspace(min(self.chunk, T), T, device=self.device)
         self.m.prefill(prompt, kd, vd, q_obs, W, g0, ws, min(self.chunk, T))
+        if runtime.RT.dry:  # the first token the prefill would have written
+            g0.fill_(1)
         del ws
         r.cd = compress_spec_desc(self.spec, s, T, T)
         r.comp = B.vc_compress(r.cd, kd, vd, q_obs)
@@ -186,16 +190,17 @@ class Engine:
         r.vtail_v = torch.empty_like(r.vtail_k)
         r.verified = torch.empty(x + 1, dtype=torch.int32, device=self.device)
         r.result = torch.empty(x + 2, dtype=torch.int32, device=self.device)
-        r.result_host = torch.empty(x + 2, dtype=torch.int32, pin_memory=True)
+        r.result_host = torch.empty(x + 2, dtype=torch.int32, pin_memory=runtime.RT.pin)
         if self.record:
-            r.rec_host = torch.empty(2, x + 1, dtype=torch.int32, pin_memory=True)
+            r.rec_host = torch.empty(2, x + 1, dtype=torch.int32, pin_memory=runtime.RT.pin)
+        B.debug_register(r.rows, r.tail_k, r.tail_v, r.vtail_k, r.vtail_v, r.verified, r.result)
         r.req = Req(comp=r.comp.data_ptr(), cd=None, tail_k=r.tail_k.data_ptr(), tail_v=r.tail_v.data_ptr(),
                     tail_cap=tail_cap, n_tail=0, ctx_len=T, draft_idx=0, full_k_host=r.full_k.data_ptr(),
                     full_v_host=r.full_v.data_ptr(), full_cap=full_cap, rows=r.rows.data_ptr())
         import ctypes as C
         r.req.cd = C.pointer(r.cd)
         self.m.offload(r.req, kd, vd, T)
-        torch.cuda.synchronize()
+        runtime.RT.synchronize()
         r.emitted = [int(g0.item())]
         if r.emitted[0] < 0:
             raise NonFiniteLogits(f"request {r.idx}: the prefill's last row has no finite logit")
@@ -210,8 +215,8 @@ class Engine:
         n = len(self.reqs)
         max_ctx = max(r.T + r.n_tokens + r.x + 2 for r in self.reqs)
         max_x = max(r.x for r in self.reqs)
-        self.ws_draft = self.m.workspace(min(n, 16), max_ctx)
-        self.ws_verify = self.m.workspace(max_x + 1, max_ctx)
+        self.ws_draft = self.m.workspace(min(n, 16), max_ctx, device=self.device)
+        self.ws_verify = self.m.workspace(max_x + 1, max_ctx, device=self.device)
         L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
         n_slots = min(getattr(self, 'n_slots', 2), n)
         slot_rows = max(max(r.n_host for r in self.reqs), 1)
@@ -271,7 +276,7 @@ class Engine:
         """One scheduler iteration: finish accepts, issue staging, one batched
         draft step, issue ready verifications.  Returns True if a draft step ran."""
         reqs = self.reqs
-        cs = torch.cuda.current_stream()
+        cs = runtime.RT.current_stream()
         # 1. finish accepts whose result reached the host
         for r in reqs:
             if r.phase == ACCEPTING and r.acc_ev.query():
@@ -333,7 +338,7 @@ class Engine:
 
     def drain(self):
         """Wait for every in-flight verification and fold its accepted tokens in."""
-        torch.cuda.synchronize()
+        runtime.RT.synchronize()
         for r in self.reqs:
             if r.phase == ACCEPTING:
                 r.acc_ev.synchronize()
@@ -390,7 +395,7 @@ class Engine:
                 self.stagings += 1
                 if r.pinned:
                     self.m.stage(r.req, sk, sv, 0, self.shape.n_layers, copy_stream=self.copy_stream)
-                    ev = torch.cuda.Event()
+                    ev = runtime.RT.Event()
                     ev.record(self.copy_stream)
                     r.stage_ev = ev
                 else:
@@ -404,12 +409,12 @@ class Engine:
         runtime has moved the data; ctypes releases the GIL meanwhile)."""
         if self.stager is None:
             self.stager = cf.ThreadPoolExecutor(max_workers=1)
-            self.pageable_stream = torch.cuda.Stream(device=self.device)
+            self.pageable_stream = runtime.RT.Stream(device=self.device)
         st = self.pageable_stream
 
         def work():
             self.m.stage(req, sk, sv, 0, self.shape.n_layers, copy_stream=st)
-            ev = torch.cuda.Event()
+            ev = runtime.RT.Event()
             ev.record(st)
             return ev
 
@@ -440,14 +445,17 @@ class Engine:
             n = r.x_cur + 1
             r.rec_host[0, :n].copy_(r.rows[:n], non_blocking=True)
             r.rec_host[1, :n].copy_(r.verified[:n], non_blocking=True)
-        ev_free = torch.cuda.Event()
+        ev_free = runtime.RT.Event()
         ev_free.record(cs)
         self.slot_free_ev[r.slot] = ev_free
         self.slot_owner[r.slot] = None
         r.slot = -1
         self.m.accept(r.req, r.verified, r.x_cur, r.vtail_k, r.vtail_v, r.result)
+        if runtime.RT.dry:  # the accept result the library would have written
+            runtime.RT.fill_accept(r.idx, r.n_verified, r.x_cur, r.result)
+        r.n_verified += 1
         r.result_host.copy_(r.result, non_blocking=True)
-        ev = torch.cuda.Event()
+        ev = runtime.RT.Event()
         ev.record(cs)
         r.acc_ev = ev
         r.phase = ACCEPTING
@@ -464,21 +472,22 @@ def greedy_resident(model: B.Model, prompt: torch.Tensor, n_tokens: int, chunk: 
     L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
     kd = torch.empty(L, Hkv, cap, D, dtype=dt, device=device)
     vd = torch.empty_like(kd)
-    out = torch.empty(n_tokens, dtype=torch.int32, device=device)
-    ws = model.workspace(min(chunk, T), cap)
+    out = (torch.ones if runtime.RT.dry else torch.empty)(n_tokens, dtype=torch.int32, device=device)
+    ws = model.workspace(min(chunk, T), cap, device=device)
+    B.debug_register(kd, vd, out, ws)
     model.prefill(prompt, kd, vd, None, 0, out[:1], ws, min(chunk, T))
     req = Req(ctx_len=T)
     eb = 2 if s.dtype == "bf16" else 4
     row = D * eb
     t0 = None
-    torch.cuda.synchronize()
+    runtime.RT.synchronize()
     t0 = time.perf_counter()
     for i in range(1, n_tokens):
         req.ctx_len = T + i - 1
         off = req.ctx_len * row
         model.verify_raw(req, kd.data_ptr(), vd.data_ptr(), cap, out.data_ptr() + 4 * (i - 1), 1,
                          out.data_ptr() + 4 * i, kd.data_ptr() + off, vd.data_ptr() + off, cap, ws)
-    torch.cuda.synchronize()
+    runtime.RT.synchronize()
     toks = out.tolist()
     if min(toks) < 0:
         raise NonFiniteLogits(f"greedy decoding: token -1 at step {toks.index(-1)}")
@@ -506,24 +515,25 @@ def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tenso
     vk = torch.empty(L, Hkv, 1, D, dtype=dt, device=sk.device)
     vv = torch.empty_like(vk)
     rows = first_token.clone()
+    B.debug_register(sk, sv, vk, vv, rows, ws)
     req = Req(ctx_len=T, full_k_host=hk.data_ptr(), full_v_host=hv.data_ptr(), full_cap=cap, rows=rows.data_ptr())
     model.offload(req, prompt_kv[0], prompt_kv[1], T)
-    cs = torch.cuda.current_stream()
+    cs = runtime.RT.current_stream()
     toks = []
-    torch.cuda.synchronize()
+    runtime.RT.synchronize()
     t0 = time.perf_counter()
     for _ in range(n_steps):
         model.stage(req, sk, sv, 0, L, copy_stream=copy_stream)
-        ev = torch.cuda.Event()
+        ev = runtime.RT.Event()
         ev.record(copy_stream)
         cs.wait_event(ev)
         model.verify_raw(req, sk.data_ptr(), sv.data_ptr(), cap, rows.data_ptr(), 1, rows.data_ptr(),
                          vk.data_ptr(), vv.data_ptr(), 1, ws)
-        done = torch.cuda.Event()
+        done = runtime.RT.Event()
         done.record(cs)
         model.commit(req, 0, vk, vv, after_event=done, copy_stream=copy_stream)
         toks.append(rows.clone())
-    torch.cuda.synchronize()
+    runtime.RT.synchronize()
     copy_stream.synchronize()
     secs = time.perf_counter() - t0
     del sk, sv

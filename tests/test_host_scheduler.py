@@ -61,7 +61,7 @@ class FakeModel:
     def _idx(self, req):
         return next(r.idx for r in self.reqs if r.req is req)
 
-    def workspace(self, rows, keys):
+    def workspace(self, rows, keys, device=None):
         return None
 
     def draft_step(self, reqs, ws):

@@ -10,6 +10,12 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+# PyTorch ships its own HIP runtime and asks for it as libamdhip64.so; libvc.so asks for
+# libamdhip64.so.7.  Loaded in that order, the library binds to torch's runtime (same soname), so
+# both share one runtime, its device and its streams.  Loaded the other way round the process
+# would hold two runtimes, and the library's would see no device: torch is imported first.
+import torch  # noqa: F401
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvc.so")
 
 VC_OK, VC_ERR_ARG, VC_ERR_UNSUPPORTED, VC_ERR_CAPACITY, VC_ERR_HIP = 0, -1, -2, -3, -4

@@ -91,7 +91,50 @@ def cpu_baseline(shape, ctx: int, keep: int, seed: int = 0) -> dict:
     return {"value": 1.0 / per_token, "unit": "draft tokens/s (one request)", "cores": threads, "kind": "oracle",
             "sample": (f"{reps} evaluations of layer 0 of one draft step (attention over {keep} kept rows per KV "
                        f"head at position {ctx}) + LM head on 1/8 of the vocabulary, scaled to "
-                       f"{s.n_layers} layers; {per_token:.2f} s per token; weight generation {t_gen:.1f} s excluded")}
+                       f"{s.n_layers} layers; {per_token:.2f} s per token; weight generation {t_gen:.1f} s excluded"),
+            "host": host_info(), "tiny_workload_full_run": cpu_oracle_tiny()}
+
+
+def host_info() -> dict:
+    """The host the oracle ran on: cores, affinity, the BLAS library behind numpy and its threads."""
+    import numpy  # noqa: F401  (loads the BLAS library threadpoolctl reports)
+    import threadpoolctl
+    info = threadpoolctl.threadpool_info()
+    blas = [{"api": i.get("internal_api"), "version": i.get("version"), "threads": i.get("num_threads")}
+            for i in info if i.get("user_api") == "blas"]
+    return {"os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "blas": blas}
+
+
+def cpu_oracle_tiny() -> dict:
+    """The oracle's whole run of the tiny fp32 decoder workload (1024-token prompt, token drop 4x,
+    x = 8, 64 tokens): prefill, full-KV greedy decoding and the VeriCache loop, all threads and one
+    thread; tokens/s of each decode (the first token from the prefill excluded)."""
+    import threadpoolctl
+
+    import synth
+    from oracle import decode as OD
+    from oracle.model import Weights
+    from synth.configs import tiny
+    w = tiny()
+    s = w.model
+    W = Weights(s)
+    p = synth.prompt(0, w.ctx[0], s.vocab)
+    out = {}
+    for label, limit in (("all_threads", None), ("one_thread", 1)):
+        with threadpoolctl.threadpool_limits(limit):
+            t0 = time.perf_counter()
+            pre = OD.prefill(W, p)
+            t1 = time.perf_counter()
+            g, _ = OD.greedy(W, p, w.n_tokens, pre=pre)
+            t2 = time.perf_counter()
+            v, rounds = OD.vericache(W, p, w.n_tokens, w.x[0],
+                                     lambda pr: OD.draft_cache_tokdrop(pr, W, keep_total=w.ctx[0] // 4, keep_recent=64),
+                                     pre=pre)
+            t3 = time.perf_counter()
+        assert v == g, "oracle VeriCache differs from oracle greedy"
+        out[label] = {"prefill_s": round(t1 - t0, 3), "greedy_tok_s": round((w.n_tokens - 1) / (t2 - t1), 2),
+                      "vericache_tok_s": round((w.n_tokens - 1) / (t3 - t2), 2), "rounds": len(rounds)}
+    return out
 
 
 def pmc_traffic_ratio(workload: str, kernel: str = "attn_decode_bf16", what: str = "draft_attention"):
@@ -127,14 +170,19 @@ def cpu_baseline_layer(T: int, Hq: int, Hkv: int, D: int, rows: int, bits: int, 
     with threadpoolctl.threadpool_limits(None) as _:
         info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] + [1])
-    t0 = time.perf_counter()
-    K = np.concatenate([q.rows_K()[0, 0], inp["tK"][:1]])
-    V = np.concatenate([q.rows_V()[0, 0], inp["tV"][:1]])
-    _ = [attend(qh, K, V) for qh in inp["qd"]]
-    t_draft = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    _ = OA.verify_output(inp)
-    t_verify = time.perf_counter() - t0
+    times = {}
+    for label, limit in (("all", None), ("one", 1)):
+        with threadpoolctl.threadpool_limits(limit):
+            t0 = time.perf_counter()
+            K = np.concatenate([q.rows_K()[0, 0], inp["tK"][:1]])
+            V = np.concatenate([q.rows_V()[0, 0], inp["tV"][:1]])
+            _ = [attend(qh, K, V) for qh in inp["qd"]]
+            t_draft = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            _ = OA.verify_output(inp)
+            t_verify = time.perf_counter() - t0
+        times[label] = (t_draft, t_verify)
+    t_draft, t_verify = times["all"]
     Tq = T // group * group
     draft_bytes = 2 * Tq * D * bits / 8 + 2 * (Tq // group) * D * 2 + 2 * Tq * (D // group) * 2 + 2 * D * 2 \
         + (Hq // Hkv) * D * 2
@@ -142,6 +190,9 @@ def cpu_baseline_layer(T: int, Hq: int, Hkv: int, D: int, rows: int, bits: int, 
     return {"value": round(draft_bytes / t_draft / 1e9, 4), "unit": "GB/s (draft attention, algorithmic bytes)",
             "cores": threads, "kind": "oracle",
             "verify_gbs": round(verify_bytes / t_verify / 1e9, 4),
+            "one_thread": {"draft_gbs": round(draft_bytes / times["one"][0] / 1e9, 4),
+                           "verify_gbs": round(verify_bytes / times["one"][1] / 1e9, 4)},
+            "host": host_info(),
             "sample": (f"request 0, KV head 0 of the workload: draft attention of its {Hq // Hkv} query heads over "
                        f"the dequantized {T}-row cache ({t_draft:.2f} s) and verification attention of {rows} rows "
                        f"({t_verify:.2f} s), float64 numpy; quantization excluded")}
@@ -242,6 +293,7 @@ def _rate(st: dict, bound: str, what: str) -> dict | None:
                "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "gbs": round(gbs, 1)}
     out.update({"kernel": what, "launches": st["launches"], "avg_launch_ms": round(st["ms"] / st["launches"], 5),
                 "bytes_per_launch": round(st["bytes"] / st["launches"]),
+                "partial_bytes_per_launch": round(st.get("aux_bytes", 0) / st["launches"]),
                 "flops_per_launch": round(st["flops"] / st["launches"])})
     return out
 
@@ -319,6 +371,10 @@ def run_model_workload(args) -> dict:
         vc.profile_read(k)
     vc.profile_enable(kinds)
     n_req = len(eng.reqs)
+    # whole-decode window: from the first decoding round to every request's last token
+    sync()
+    t_dec0 = time.perf_counter()
+    g_dec0 = sum(len(r.emitted) for r in eng.reqs)   # the prefills' first tokens
     eng.run_rounds_each(args.warmup)
     if args.adaptive:
         # the drafting horizon that still hides one request's host-row copy: L_min = ceil(t_copy / t_step),
@@ -368,6 +424,16 @@ def run_model_workload(args) -> dict:
     for a in accepts:
         hist[a] = hist.get(a, 0) + 1
     log(f"timed: {emitted} tokens in {secs:.2f}s = {tok_s:.2f} tok/s; mean accepted {sum(accepts)/max(len(accepts),1):.2f}")
+    # the rest of the decode, to every request's token count: whole-decode tokens/s = every generated token
+    # of every request / wall time from the first round to the last
+    if not args.no_whole_decode:
+        eng.run_to_end(progress=lambda n, t: log(f"  whole decode: {n} tokens after {t:.0f}s"))
+    sync()
+    dec_secs = time.perf_counter() - t_dec0
+    dec_tokens = sum(min(len(r.emitted), r.n_tokens) for r in eng.reqs) - g_dec0
+    dec_accepts = [a for r in eng.reqs for a in r.accepts]
+    log(f"whole decode: {dec_tokens} tokens in {dec_secs:.2f}s = {dec_tokens / dec_secs:.2f} tok/s over "
+        f"{len(dec_accepts)} rounds")
 
     att_ms = prof["ms"] / max(prof["launches"], 1)
     att_gbs = prof["bytes"] / max(prof["ms"], 1e-9) / 1e6
@@ -423,7 +489,7 @@ def run_model_workload(args) -> dict:
     # resident full-KV greedy (context only: the workload keeps the full cache on the host): request
     # 0 alone with its whole cache in HBM, one vc_verify row per token appended in place
     from lossless_speculative_decoding_amd._vc import Req
-    n_res = 16
+    n_res = min(len(r0.emitted), r0.n_tokens) - 1   # every token request 0 emitted after its first
     cap = r0.T + n_res + 1
     kd = torch.empty(s.n_layers, s.n_kv_heads, cap, s.head_dim, dtype=r0.prefill_kv[0].dtype, device=device)
     vd = torch.empty_like(kd)
@@ -484,6 +550,7 @@ def run_model_workload(args) -> dict:
                      "traffic_over_algorithmic": traffic_ratio,
                      "avg_launch_ms": round(att_ms, 5), "launches": prof["launches"],
                      "bytes_per_launch": round(prof["bytes"] / max(prof["launches"], 1)),
+                     "partial_bytes_per_launch": round(prof["aux_bytes"] / max(prof["launches"], 1)),
                      "bytes_per_launch_incl_warmup": round(all_bytes), "launches_incl_warmup": all_launches},
         "verify_attention": _rate(vprof, "hbm", "verification attention partials (one layer of one request)"),
         "gemm_decode": _rate(gprof, "hbm", f"projection and LM-head GEMMs of {len(live)}-request draft steps "
@@ -507,6 +574,12 @@ def run_model_workload(args) -> dict:
                       "x_min": eng.x_min if args.adaptive else None,
                       "drafts_per_round": round((eng.drafted - d0) / max(len(accepts), 1), 2),
                       "mean_requests_per_draft_step": round(mean_draft_batch, 2)},
+        "whole_decode": None if args.no_whole_decode else {"tokens_per_s": round(dec_tokens / dec_secs, 3), "tokens": dec_tokens,
+                         "seconds": round(dec_secs, 2), "rounds": len(dec_accepts),
+                         "mean_accepted_per_round": round(sum(dec_accepts) / max(len(dec_accepts), 1), 3),
+                         "note": f"every generated token of every request ({w.n_tokens} per request, the first "
+                                 "from the prefill excluded) over the wall time of the whole decode, warmup and "
+                                 "timed rounds included"},
         "mean_accepted_per_round": round(sum(accepts) / max(len(accepts), 1), 3),
         "rounds": len(accepts),
         "rounds_per_s": round(len(accepts) / secs, 3),
@@ -551,7 +624,7 @@ def main():
                     choices=["llama8b_tokdrop", "llama8b_q2", "llama8b_mixed", "gqa_layer"])
     ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
-    ap.add_argument("--baseline-steps", type=int, default=2)
+    ap.add_argument("--baseline-steps", type=int, default=16)
     ap.add_argument("--draft-batch", type=int, default=0,
                     help="requests yet to draft wait for a batch this large while --queue-min drafted requests are "
                          "queued for verification (0: all the requests; 1: draft as soon as possible)")
@@ -567,6 +640,8 @@ def main():
                     help="per-request draft length between L_min = ceil(t_copy / t_step) (measured in the warmup) "
                          "and the workload's x: doubled after an all-accepted round, a + 1 after a rejection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-whole-decode", action="store_true",
+                    help="skip decoding the rest of every request after the timed rounds (the whole-decode rate)")
     ap.add_argument("--check-bounds", action="store_true",
                     help="check every launch's and copy's byte ranges against the buffers allocated for it before "
                          "it runs on the GPU (an error instead of a launch outside them)")

@@ -348,12 +348,13 @@ vc_status vc_attn_ws_size(const vc_attn_desc* d, int32_t n, int32_t rows, int32_
  *   VC_PROF_DRAFT_ATTN    draft-step attention partials of all requests of one
  *                         layer (one pair spans the quantized and the exact-row
  *                         launch): compressed main region (codes, scales and zeros,
- *                         or kept rows), exact tail rows, queries, split partials;
+ *                         or kept rows), exact tail rows, queries (split partials
+ *                         in aux_bytes);
  *   VC_PROF_VERIFY_ATTN   verification attention of one layer: every key visible to
- *                         the last row, K and V once per KV head, queries, partials;
- *                         flops 4 D Hq per (row, visible key);
- *   VC_PROF_GEMM_SKINNY   projection / LM-head GEMM with M <= 64 rows (weights, X,
- *                         float32 partials; flops 2 M N K);
+ *                         the last row, K and V once per KV head, queries (partials
+ *                         in aux_bytes); flops 4 D Hq per (row, visible key);
+ *   VC_PROF_GEMM_SKINNY   projection / LM-head GEMM with M <= 64 rows (weights and X;
+ *                         float32 partials in aux_bytes; flops 2 M N K);
  *   VC_PROF_GEMM_TILED    the same for larger M (prefill chunks);
  *   VC_PROF_PREFILL_ATTN  causal prefill attention of one chunk (bytes as for
  *                         verification; its keys are read once per row group).
@@ -371,6 +372,9 @@ typedef struct {
   double total_ms;    /* summed event time of those launches               */
   double bytes;       /* summed algorithmic bytes                          */
   double flops;       /* summed algorithmic flops                          */
+  double aux_bytes;   /* bytes beyond the algorithmic ones: the launches'
+                         own split-K partials (written, and read back by
+                         the combine or the epilogue)                      */
 } vc_profile_stats;
 /* mask: bit k enables class k (0 disables all). */
 vc_status vc_profile_enable(uint32_t mask);

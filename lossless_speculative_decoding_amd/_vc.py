@@ -69,7 +69,8 @@ class AttnDesc(C.Structure):
 
 
 class ProfileStats(C.Structure):
-    _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("bytes", C.c_double), ("flops", C.c_double)]
+    _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("bytes", C.c_double), ("flops", C.c_double),
+                ("aux_bytes", C.c_double)]
 
 
 class DebugStats(C.Structure):

@@ -267,7 +267,8 @@ def profile_read(kind: int = VC_PROF_DRAFT_ATTN) -> dict:
     and flops); clears that class's record."""
     st = ProfileStats()
     call("vc_profile_read", kind, C.byref(st))
-    return {"launches": st.launches, "ms": st.total_ms, "bytes": st.bytes, "flops": st.flops}
+    return {"launches": st.launches, "ms": st.total_ms, "bytes": st.bytes, "flops": st.flops,
+            "aux_bytes": st.aux_bytes}
 
 
 class PageableBuffer:

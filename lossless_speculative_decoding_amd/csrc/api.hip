@@ -38,6 +38,7 @@ namespace {
 struct ProfRec {
   hipEvent_t a = nullptr, b = nullptr;
   double bytes = 0, flops = 0;
+  double aux = 0;  // bytes the launch moves beyond the algorithmic ones (its own split partials)
   int kind = 0;
 };
 uint32_t g_prof_mask = 0;
@@ -58,11 +59,12 @@ hipEvent_t prof_event() {
 }
 
 // events are null (and nothing is recorded) unless the kind is enabled
-ProfRec prof_begin(int kind, double bytes, double flops) {
+ProfRec prof_begin(int kind, double bytes, double flops, double aux = 0) {
   ProfRec r;
   r.kind = kind;
   r.bytes = bytes;
   r.flops = flops;
+  r.aux = aux;
   if ((g_prof_mask & (1u << kind)) && !dbg_dry()) {
     r.a = prof_event();
     r.b = prof_event();
@@ -78,22 +80,22 @@ void prof_commit(const ProfRec& r) {
 // many-row attention launch: every key visible to the last row read once per KV head (K and V),
 // the queries read, the split partials written; flops of QK^T and PV over the causal rows
 ProfRec prof_rows(int kind, const AttnArgs& a, int eb) {
-  double bytes = 0, flops = 0;
+  double bytes = 0, flops = 0, aux = 0;
   for (int r = 0; r < a.n_req; r++) {
     const AttnReq& q = a.r[r];
     const double rows = q.n_rows, keys = double(q.lim0) + q.n_rows;
-    bytes += double(a.Hkv) * keys * a.head_dim * eb * 2 + rows * a.Hq * a.head_dim * eb +
-             rows * a.Hq * q.n_splits * (a.head_dim + 2) * 4.0;
+    bytes += double(a.Hkv) * keys * a.head_dim * eb * 2 + rows * a.Hq * a.head_dim * eb;
+    aux += rows * a.Hq * q.n_splits * (a.head_dim + 2) * 4.0;
     flops += 4.0 * a.head_dim * a.Hq * (rows * q.lim0 + 0.5 * rows * (rows + 1));
   }
-  return prof_begin(kind, bytes, flops);
+  return prof_begin(kind, bytes, flops, aux);
 }
 
 // one projection GEMM: weights + activations read, float32 partials written once
 ProfRec prof_gemm(int M, int N, int K, int S, int dtype) {
   const double eb = dtype == VC_BF16 ? 2 : 4;
   const int kind = (dtype == VC_BF16 && M <= 64) ? VC_PROF_GEMM_SKINNY : VC_PROF_GEMM_TILED;
-  return prof_begin(kind, (double(N) * K + double(M) * K) * eb + double(S) * M * N * 4, 2.0 * M * N * K);
+  return prof_begin(kind, (double(N) * K + double(M) * K) * eb, 2.0 * M * N * K, double(S) * M * N * 4);
 }
 }  // namespace
 
@@ -457,7 +459,7 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
     }
   }
   // algorithmic bytes of the partial launches (for vc_profile_read)
-  double bytes = 0, flops_keys = 0;  // flops_keys: query heads x keys attended
+  double bytes = 0, flops_keys = 0, aux = 0;  // flops_keys: query heads x keys attended
   for (int r = 0; r < n; r++) {
     const CompView& v = views[r];
     const double row = double(D) * (dtype == VC_BF16 ? 2 : 4);
@@ -471,10 +473,10 @@ vc_status draft_attention(int Hq, int Hkv, int D, int dtype, int out_dtype, int 
       flops_keys += double(Hq) * (v.kk + tail_n[r]);
     }
     bytes += double(Hq) * row;                                       // query
-    bytes += double(Hq) * (qs_n[r] + ts_n[r]) * (D + 2) * 4.0;        // partials written
+    aux += double(Hq) * (qs_n[r] + ts_n[r]) * (D + 2) * 4.0;          // partials written
   }
   // live timing: the first partial launch's own start and the last one's own end
-  ProfRec rec = prof_begin(VC_PROF_DRAFT_ATTN, bytes, 4.0 * flops_keys * D);
+  ProfRec rec = prof_begin(VC_PROF_DRAFT_ATTN, bytes, 4.0 * flops_keys * D, aux);
   vc_status st;
   const bool both = qa.n_req > 0 && aa.n_req > 0;
   if (qa.n_req > 0) {
@@ -526,7 +528,7 @@ vc_status vc_profile_enable(uint32_t mask) {
 vc_status vc_profile_read(int32_t kind, vc_profile_stats* out) {
   VC_REQUIRE(out != nullptr, VC_ERR_ARG, "vc_profile_read: null output");
   VC_REQUIRE(kind >= 0 && kind < VC_PROF_KINDS, VC_ERR_ARG, "vc_profile_read: bad kind %d", kind);
-  *out = vc_profile_stats{0, 0.0, 0.0, 0.0};
+  *out = vc_profile_stats{0, 0.0, 0.0, 0.0, 0.0};
   for (ProfRec& r : g_prof[kind]) {
     VC_HIP(hipEventSynchronize(r.b));
     float ms = 0.f;
@@ -534,6 +536,7 @@ vc_status vc_profile_read(int32_t kind, vc_profile_stats* out) {
     out->launches += 1;
     out->total_ms += ms;
     out->bytes += r.bytes;
+    out->aux_bytes += r.aux;
     out->flops += r.flops;
     g_prof_pool.push_back(r.a);
     g_prof_pool.push_back(r.b);
@@ -641,7 +644,8 @@ vc_status draft_step_impl(vc_model* m, const vc_req* reqs, int32_t n, float* log
   }
   const WsLayout L = ws_layout(m, n, max_keys);
   VC_REQUIRE(ws_bytes >= L.total, VC_ERR_CAPACITY, "vc_draft_step: workspace %zu < %zu bytes", ws_bytes, L.total);
-  if (vc_status st = dbg_check("vc_draft_step", {{"workspace", ws, int64_t(ws_bytes)}})) return st;
+  if (dbg_on())
+    if (vc_status st = dbg_check("vc_draft_step", {{"workspace", ws, int64_t(ws_bytes)}})) return st;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   vc_status st;
   int32_t* tok_in = reinterpret_cast<int32_t*>(w8 + L.tok);

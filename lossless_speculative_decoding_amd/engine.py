@@ -385,6 +385,20 @@ class Engine:
         while any(r.phase != DONE and r.budget > 0 for r in self.reqs):
             self.step()
 
+    def run_to_end(self, progress=None, every: float = 20.0):
+        """Lift every request's round budget and decode until all have their token count;
+        progress(emitted tokens, seconds) is called about every `every` seconds."""
+        for r in self.reqs:
+            if r.phase != DONE:
+                r.budget = -1
+        t0 = t_last = time.perf_counter()
+        while any(r.phase != DONE for r in self.reqs):
+            self.step()
+            if progress is not None and time.perf_counter() - t_last >= every:
+                t_last = time.perf_counter()
+                progress(sum(min(len(r.emitted), r.n_tokens) for r in self.reqs), t_last - t0)
+        self.drain()
+
     def _try_stage(self, r: Request):
         for i in range(len(self.slots)):
             if self.slot_owner[i] is None and (self.slot_free_ev[i] is None or self.slot_free_ev[i].query()):

@@ -306,22 +306,24 @@ def test_profile_records_verify_and_draft_launches():
     vc.profile_enable(())
     torch.cuda.synchronize()
     st = vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
-    want_b = want_f = 0.0
+    want_b = want_f = want_a = 0.0
     for c in ctxs:
         S = -(-(c + rows) // split)
-        want_b += HKV * (c + rows) * D * 2 * 2 + rows * HQ * D * 2 + rows * HQ * S * (D + 2) * 4
+        want_b += HKV * (c + rows) * D * 2 * 2 + rows * HQ * D * 2
+        want_a += rows * HQ * S * (D + 2) * 4          # the launch's own split partials, reported apart
         want_f += 4 * D * HQ * (rows * c + rows * (rows + 1) / 2)
     assert st["launches"] == 1 and st["ms"] > 0
-    assert st["bytes"] == want_b and st["flops"] == want_f
+    assert st["bytes"] == want_b and st["flops"] == want_f and st["aux_bytes"] == want_a
     sd = vc.profile_read(vc.VC_PROF_DRAFT_ATTN)
     Tq = T // group * group
     n_resid, n_tail = T - Tq, 3
     # quantized splits of 16 groups (2048 keys at group 128, G = 4); the exact rows are one slot
     s_quant, s_exact = -(-Tq // 2048), 1
     want = (HKV * (2 * Tq * D * bits / 8 + 2 * (Tq // group) * D * 2 + 2 * Tq * (D // group) * 2)
-            + HKV * (n_resid + n_tail) * D * 2 * 2 + HQ * D * 2 + HQ * (s_quant + s_exact) * (D + 2) * 4)
+            + HKV * (n_resid + n_tail) * D * 2 * 2 + HQ * D * 2)
     assert sd["launches"] == 1 and sd["ms"] > 0
     assert sd["bytes"] == want, (sd["bytes"], want)
+    assert sd["aux_bytes"] == HQ * (s_quant + s_exact) * (D + 2) * 4
     assert sd["flops"] == 4 * D * HQ * (T + n_tail)
     for k in (vc.VC_PROF_GEMM_SKINNY, vc.VC_PROF_GEMM_TILED, vc.VC_PROF_PREFILL_ATTN):
         assert vc.profile_read(k)["launches"] == 0

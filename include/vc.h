@@ -263,7 +263,12 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
  * verifier's rows 0..a are copied from vtail into the request's tail at n_tail
  * (overwriting this round's draft rows).  verified: device int32 [x+1];
  * result: device int32 [x+2].  Does not block and does not change *req:
- * after result[0] is visible on the host, call vc_commit. */
+ * after result[0] is visible on the host, call vc_commit.
+ * This splits the single accept-and-commit call of the four-call interface
+ * sketched for the method: accepting runs on the device and returns no host
+ * count, and the host copy of the accepted rows (for a plain request only;
+ * a compressed request keeps them exact in its device tail) moves to
+ * vc_commit, so nothing here waits on the host. */
 vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* verified, int32_t x, const void* vtail_k,
                     const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s);
 
@@ -307,6 +312,16 @@ vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out,
 /* ------------------------------------------------------------------------
  * Attention cores of one layer (the single-layer workload and tests).
  * Query rows are [rows][Hq][D] bf16 (post-RoPE); outputs [rows][Hq][D] in out_dtype.
+ *
+ * Value range (every bf16 attention path, draft and verification, and so the
+ * model calls built on them): P.V runs on fp16 MFMAs, so each bf16 V element
+ * is converted to fp16.  The contract is |v| <= 65504.  Inside it the
+ * conversion is exact for |v| >= 2^-14 and off by at most 2^-25 (absolute)
+ * below.  An element beyond it becomes +-inf and makes the output channels it
+ * feeds non-finite (never a finite wrong value); through a model this reaches
+ * the logits, and the argmax then writes -1 (see the token-id conventions).
+ * The quantized compressor stores fp16 scales and zeros, so the same bound
+ * holds for the range max - min of every quantization group.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t n_q_heads, n_kv_heads, head_dim, dtype;

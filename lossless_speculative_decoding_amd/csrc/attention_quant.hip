@@ -2,19 +2,21 @@
 //
 // One workgroup = 4 waves = (request, KV head, split); wave w streams the 64-key tiles
 // w, w + 4, ... of the split with its own online softmax, and the four states are merged
-// in wave order at the end.  Nothing goes through LDS on the way: every lane loads
-// exactly the packed codes its MFMA fragments need and turns them into exact small
-// integers in fp16 (magic-number trick: 0x6400 | c is 1024 + c, then subtract).  The
+// in wave order at the end.  The codes are not staged through LDS: every lane loads
+// exactly the packed codes its MFMA fragments need and turns them into fp16 operands
+// 1 + c 2^(o - 10) by bit placement under the exponent of 1.0 (see "codes -> fp16 MFMA
+// operands" below for the offsets o and where the factors and the offset 1 go).  The
 // quantization scale and zero are never applied to the codes; they are folded into
 // the other operand instead:
 //     q . k_t       = sum_d (q_d s_gd) c_td + sum_d q_d z_gd        (K: scale/zero per channel and token group)
 //     sum_t p_t v_t = sum_t (p_t s_t) c_t  + sum_t p_t z_t          (V: scale/zero per token and channel group)
 // so the MFMA operands are Q' = q*s, the codes, and P' = p*s (scaled by 2^10 to stay
-// out of the fp16 subnormal range).  Codes are centred (c - 2^(b-1), the zero moves to
-// z + 2^(b-1) s) so the folded sums do not cancel against a large zero term (keeping the
-// 1024 of the conversion in the V codes instead costs ~5e-3 relative on outlier-heavy
-// heads).  Q' is carried as an fp16 hi/lo pair (two MFMAs, about 22 significant bits: a
-// score error moves every weight through the exponential); P' as one fp16 number.
+// out of the fp16 subnormal range).  Codes count as centred (c - 2^(b-1); the zero moves
+// to z + 2^(b-1) s) so that the folded sums do not cancel against a large zero term; the
+// centring and the conversion's offset 1 are removed by bias terms (K) and by a constant
+// "centre row" MFMA after each code MFMA (V), never by arithmetic on the codes.  Q' is
+// carried as an fp16 hi/lo pair (two MFMAs, about 22 significant bits: a score error
+// moves every weight through the exponential); P' as one fp16 number.
 //
 // Operand assignment.  Lane l (g = l / 16, r = l % 16) holds for S^T = C_K Q'^T the
 // K codes of channels [32g, 32g + 32) of key 16 (r / 4) + 4 kt + r % 4 of the tile
@@ -22,9 +24,9 @@
 // whole rows.  The score accumulator of lane (g, head r) then holds keys
 // [16g, 16g + 16), which are exactly the keys whose V codes the lane loads for
 // O^T += C_V^T P'^T: the 16-code run of channel 16 dt + r starting at token 16g (one
-// contiguous 2*BITS-byte piece of a per-channel code row).  Within a conversion group
-// of 8 (4-bit) or 16 (2-bit) codes the conversion yields the order [0,4,1,5,2,6,3,7]
-// (resp. [0,8,1,9,...,7,15]); Q' and P' are built in that same order.
+// contiguous 2*BITS-byte piece of a per-channel code row).  The conversion tables below
+// fix which code each fp16 position carries (4-bit: [0,4,1,5,2,6,3,7] per 8 codes; 2-bit:
+// [0,8,1,9,...,7,15] per 16; 3-bit: its own table); Q' and P' are built in that order.
 #include <type_traits>
 
 #include "attention_quant.h"

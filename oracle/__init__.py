@@ -4,7 +4,8 @@ Plain, slow, float64 numpy implementation of what the path computes:
 full-KV greedy decoding of a pre-norm Llama-style decoder, the two compressor
 families (token dropping by observed attention, per-group low-bit
 quantization), compressed-KV drafting, full-KV verification and the
-accept-until-first-mismatch rule.
+accept-until-first-mismatch rule, and sampled decoding with speculative
+rejection sampling.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
 leg may import this package.  It shares no code with the HIP library or its
@@ -23,6 +24,10 @@ Sources (the pages are cited by title and section):
   [VC3] "VeriCache: Turning Lossy KV Cache into Lossless LLM Inference"
         (estelledc study note), section "实践案例" case 1 (draft / verify /
         accept_prefix_until_first_mismatch / resume loop).
+  [VC2] also "Mathematical Guarantee of Lossless Correctness" (speculative
+        rejection sampling; ``sampling.py``, whose uniforms come from
+        Philox4x64-10, Salmon et al., "Parallel Random Numbers: As Easy as
+        1, 2, 3", SC 2011).
   [KV4] "KV Cache and Speculative Decoding" (corecocept), section
         "Autoregressive Decoding and the KV Cache" (cached K/V are legal
         because causal attention never changes past rows).

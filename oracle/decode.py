@@ -21,7 +21,8 @@ Readings where the pages are silent:
     - the verifier's rows, not the draft's, are what the caches keep for accepted tokens;
     - generated rows are never re-compressed: the tail stays in the model dtype;
     - every round drafts a full x, and the output is cut to N at the end;
-    - the acceptance rule is greedy exact match (not rejection sampling).
+    - the acceptance rule here is greedy exact match; sampled decoding with
+      speculative rejection sampling is in sampling.py.
 """
 from __future__ import annotations
 

@@ -327,3 +327,57 @@ def test_profile_records_verify_and_draft_launches():
     assert sd["flops"] == 4 * D * HQ * (T + n_tail)
     for k in (vc.VC_PROF_GEMM_SKINNY, vc.VC_PROF_GEMM_TILED, vc.VC_PROF_PREFILL_ATTN):
         assert vc.profile_read(k)["launches"] == 0
+
+
+def test_v_beyond_fp16_range_is_non_finite_not_wrong():
+    """A V element beyond fp16's range (the documented bound |v| <= 65504)
+    makes exactly the output channels it feeds non-finite, on the verification
+    kernel (staged row) and on the draft kernel (tail row); every other output
+    still matches the oracle."""
+    need_gpu()
+    from lossless_speculative_decoding_amd import VC_BF16, VC_F32, VC_TOKDROP, compress_desc, compress_layout
+    from lossless_speculative_decoding_amd import vc_attn_draft, vc_attn_verify, vc_compress
+    from lossless_speculative_decoding_amd._vc import AttnDesc
+    big = np.uint16(0x47C3)                                     # bf16 99840
+    ctx, n_rows, ch, key = 300, 3, 7, 5
+    Kst, Vst, tks, tvs, q, ref = _verify_case(1, (ctx,), n_rows, ctx)
+    vb = Vst[0].cpu().view(torch.int16).numpy().view(np.uint16).copy()
+    vb[0, key, ch] = big
+    out = vc_attn_verify(AttnDesc(HQ, HKV, D, VC_BF16, 0, VC_F32), dev_bf16(q), Kst, [dev_bf16(vb)], [ctx], tks, tvs,
+                         n_rows, split_len=256)
+    torch.cuda.synchronize()
+    o = host_f64(out)[0]                                        # [rows][Hq][D]
+    bad = ~np.isfinite(o)
+    assert bad[:, 0:4, ch].all()                                # the four query heads of KV head 0, channel ch
+    bad[:, 0:4, ch] = False
+    assert not bad.any()
+    keep = np.ones(o.shape, bool)
+    keep[:, 0:4, ch] = False
+    assert np.abs(o - ref[0])[keep].max() <= TOL_BF16 * np.abs(ref[0]).max()
+    # draft kernel: the large element sits in the bf16 tail of KV head 3
+    T, W, R, kt, n_tail = 640, 32, 64, 192, 5
+    kb, vb2 = _head_bits(synth.S_ATT_K, 0, T, outl=False)[0], _head_bits(synth.S_ATT_V, 0, T, outl=False)[0]
+    qo = synth.att_queries(synth.S_ATT_QV, 1, W, HQ, D)
+    d = compress_desc(VC_TOKDROP, 1, HQ, HKV, D, T, VC_BF16, keep_total=kt, keep_recent=R, obs_window=W)
+    blob = vc_compress(d, dev_bf16(kb[None]), dev_bf16(vb2[None]), dev_bf16(qo[None]))
+    tk = _head_bits(synth.S_ATT_TK, 0, n_tail, outl=False)[0]
+    tv = _head_bits(synth.S_ATT_TV, 0, n_tail, outl=False)[0]
+    tv[3, 2, ch] = big
+    qd = synth.att_queries(synth.S_ATT_QD, 0, 1, HQ, D)
+    out = vc_attn_draft(AttnDesc(HQ, HKV, D, VC_BF16, 0, VC_F32), [blob], [d], [dev_bf16(tk)], [dev_bf16(tv)],
+                        [n_tail], dev_bf16(qd))
+    torch.cuda.synchronize()
+    o = host_f64(out[0])
+    bad = ~np.isfinite(o)
+    assert bad[12:16, ch].all()
+    bad[12:16, ch] = False
+    assert not bad.any()
+    raw = blob.cpu().numpy()
+    idx = raw[compress_layout(d).idx: compress_layout(d).idx + HKV * kt * 4].view(np.int32).reshape(HKV, kt)
+    for j in (0, 3):
+        Kj = np.concatenate([_f(kb[j, idx[j]]), _f(tk[j])])
+        Vj = np.concatenate([_f(vb2[j, idx[j]]), _f(tv[j])])
+        for g in range(4):
+            r = OA.attend(_f(qd[0, j * 4 + g]), Kj, Vj)
+            m = np.isfinite(r)
+            assert np.abs(o[j * 4 + g][m] - r[m]).max() <= TOL_BF16 * np.abs(r[m]).max()

@@ -304,10 +304,74 @@ vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, i
  * chunks of `chunk` rows, each through the verification path with the rows
  * before it as the staged cache.  Writes K/V into k_out/v_out
  * [L][Hkv][cap][D], the post-RoPE queries of the last W rows into q_obs
- * [L][W][Hq][D] (NULL to skip), and g0 = argmax of row T-1 into g0_out[0]. */
+ * [L][W][Hq][D] (NULL to skip), g0 = argmax of row T-1 into g0_out[0], and
+ * row T-1's logits into last_logits_opt [V] (NULL to skip; sampled decoding
+ * draws g0 from them with vc_sample). */
 vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out, void* v_out, int32_t cap,
-                     void* q_obs, int32_t W, int32_t* g0_out, int32_t chunk, void* ws, size_t ws_bytes,
-                     hipStream_t s);
+                     void* q_obs, int32_t W, int32_t* g0_out, float* last_logits_opt, int32_t chunk, void* ws,
+                     size_t ws_bytes, hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * Sampled decoding ("VeriCache Guide: Lossless Inference with Lossy KV
+ * Caches", "Mathematical Guarantee of Lossless Correctness"): drafts are drawn
+ * from the compressed-cache distribution, and a draft x is kept with
+ * probability min(1, p_target(x) / p_draft(x)), where p_target is the full-KV
+ * verification row's distribution; at the first rejection the token is drawn
+ * from max(0, p_target - p_draft) renormalised, and after x kept drafts the
+ * bonus token from verify row x.  Every emitted token is then distributed as
+ * full-KV sampling would draw it.
+ *   Distribution of a logits row: softmax(logits / temperature); temperature 0
+ *   is the one-hot row at the greedy argmax (the whole path then emits the
+ *   greedy tokens).  A row holding NaN or +inf, or nothing finite, draws -1.
+ *   Draws: inverse CDF, the lowest index i of positive weight whose running
+ *   sum (a fixed-order fp32 scan) exceeds u * (total).  u comes from
+ *   Philox4x64-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2,
+ *   3", SC 2011) with key (seed, 0) and counter (position, purpose, stream, 0):
+ *   (first output word >> 40) * 2^-24.  position is the absolute position of
+ *   the token being chosen; purpose is one of VC_DRAW_*.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float temperature; /* finite, >= 0 */
+  uint64_t seed;     /* generator key word 0                        */
+  uint64_t stream;   /* counter word 2: one stream per request      */
+} vc_sampler;
+#define VC_DRAW_DRAFT 0  /* a draft token                                       */
+#define VC_DRAW_ACCEPT 1 /* the acceptance test of a draft                      */
+#define VC_DRAW_TARGET 2 /* a token drawn from the target: g0, plain sampling, the
+                            token after a rejection, the bonus token            */
+
+/* One token per logits row: row r (logits + r * vocab, device fp32) with
+ * sampler smp[r] (host array) at position pos[r] (host array) and draw
+ * `purpose`; writes out_tok[r] (device) and, when probs_opt is not NULL, the
+ * row's distribution to probs_opt + r * vocab (device fp32). */
+vc_status vc_sample(const float* logits, int32_t n_rows, int32_t vocab, const vc_sampler* smp, const int64_t* pos,
+                    int32_t purpose, int32_t* out_tok, float* probs_opt, hipStream_t s);
+
+/* vc_draft_step with the draft token drawn instead of the argmax: request r
+ * draws rows[draft_idx + 1] at position ctx_len + draft_idx + 1 with smp[r]
+ * (VC_DRAW_DRAFT) and writes the draft distribution to probs[r] + draft_idx *
+ * vocab (probs: host array of n device pointers, each to [>= x][vocab] fp32,
+ * which vc_spec_sample reads after the round's x steps). */
+vc_status vc_draft_step_sampled(vc_model* m, const vc_req* reqs, int32_t n, const vc_sampler* smp,
+                                float* const* probs, float* logits_opt, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Speculative rejection sampling of one verified round of one request: the
+ * step that replaces the greedy comparison before vc_accept.  logits_t: the
+ * x + 1 verify rows' logits (vc_verify's logits_opt, device fp32
+ * [x + 1][vocab]); probs_d: the draft distributions [x][vocab] (from
+ * vc_draft_step_sampled); draft: the x drafts (req->rows + 1); pos0: the
+ * pending token's position (req->ctx_len), so draft i sits at pos0 + 1 + i.
+ * Draft i is kept when u_accept * p_d(draft i) < p_t(draft i); with a the
+ * first rejection (else x), writes verified[0..a) = the kept drafts and
+ * verified[a] = the token drawn with the TARGET draw of its position from the
+ * residual of row a (from row x when a = x; from row a without the rejected
+ * draft if rounding left the residual no mass), which always differs from a
+ * rejected draft, so that vc_accept then finds the same a and emits it.
+ * verified[i > a] is not written.  ws: device, vc_spec_ws_size bytes. */
+vc_status vc_spec_ws_size(int32_t x, size_t* bytes);
+vc_status vc_spec_sample(int32_t vocab, const float* logits_t, const float* probs_d, const int32_t* draft, int32_t x,
+                         const vc_sampler* smp, int64_t pos0, int32_t* verified, void* ws, size_t ws_bytes,
+                         hipStream_t s);
 
 /* ------------------------------------------------------------------------
  * Attention cores of one layer (the single-layer workload and tests).

@@ -81,6 +81,13 @@ class DebugStats(C.Structure):
 VC_DEBUG_OFF, VC_DEBUG_CHECK, VC_DEBUG_DRY = 0, 1, 2
 
 
+class Sampler(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("seed", C.c_uint64), ("stream", C.c_uint64)]
+
+
+VC_DRAW_DRAFT, VC_DRAW_ACCEPT, VC_DRAW_TARGET = 0, 1, 2
+
+
 class AttnDraftReq(C.Structure):
     _fields_ = [("comp", C.c_void_p), ("cd", C.POINTER(CompressDesc)), ("tail_k", C.c_void_p),
                 ("tail_v", C.c_void_p), ("tail_cap", C.c_int32), ("n_tail", C.c_int32)]
@@ -104,7 +111,11 @@ _SIGS = {
     "vc_accept": (_I, [_P, C.POINTER(Req), _P, _I, _P, _P, _I, _P, _P]),
     "vc_commit": (_I, [_P, C.POINTER(Req), _I, _P, _P, _I, _P, _P]),
     "vc_stage": (_I, [_P, C.POINTER(Req), _P, _P, _I, _I, _I, _P]),
-    "vc_prefill": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _P, _I, _P, _S, _P]),
+    "vc_prefill": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _P, _P, _I, _P, _S, _P]),
+    "vc_sample": (_I, [_P, _I, _I, C.POINTER(Sampler), C.POINTER(C.c_int64), _I, _P, _P, _P]),
+    "vc_draft_step_sampled": (_I, [_P, C.POINTER(Req), _I, C.POINTER(Sampler), C.POINTER(_P), _P, _P, _S, _P]),
+    "vc_spec_ws_size": (_I, [_I, C.POINTER(_S)]),
+    "vc_spec_sample": (_I, [_I, _P, _P, _P, _I, C.POINTER(Sampler), C.c_int64, _P, _P, _S, _P]),
     "vc_attn_ws_size": (_I, [C.POINTER(AttnDesc), _I, _I, _I, C.POINTER(_S)]),
     "vc_attn_draft": (_I, [C.POINTER(AttnDesc), C.POINTER(AttnDraftReq), _I, _P, _P, _P, _S, _P]),
     "vc_attn_verify": (_I, [C.POINTER(AttnDesc), _I, _P, C.POINTER(_P), C.POINTER(_P), _I, C.POINTER(_I),

@@ -14,14 +14,17 @@ from . import _vc, runtime
 from ._vc import (VC_BF16, VC_F32, VC_PROF_DRAFT_ATTN, VC_PROF_GEMM_SKINNY, VC_PROF_GEMM_TILED,
                   VC_PROF_PREFILL_ATTN, VC_PROF_VERIFY_ATTN, VC_QUANT, VC_SCORE_ATTN, VC_SCORE_KEYNORM, VC_TOKDROP,
                   VC_DEBUG_CHECK, VC_DEBUG_DRY, VC_DEBUG_OFF, AttnDesc, AttnDraftReq, DebugStats,
-                  CompressDesc, CompressLayout, ModelDesc, ProfileStats, Req, Weights, call)
+                  CompressDesc, CompressLayout, ModelDesc, ProfileStats, Req, Sampler, Weights, call,
+                  VC_DRAW_ACCEPT, VC_DRAW_DRAFT, VC_DRAW_TARGET)
 
 __all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "VC_SCORE_ATTN", "VC_SCORE_KEYNORM", "CompressDesc", "Req", "Model", "compress_desc",
            "compress_layout", "vc_compress", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
            "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes",
            "profile_enable", "profile_read", "HostBuffer", "PageableBuffer", "VC_PROF_DRAFT_ATTN",
            "VC_PROF_VERIFY_ATTN", "VC_PROF_GEMM_SKINNY", "VC_PROF_GEMM_TILED", "VC_PROF_PREFILL_ATTN",
-           "VC_DEBUG_OFF", "VC_DEBUG_CHECK", "VC_DEBUG_DRY", "debug_mode", "debug_register", "debug_stats"]
+           "VC_DEBUG_OFF", "VC_DEBUG_CHECK", "VC_DEBUG_DRY", "debug_mode", "debug_register", "debug_stats",
+           "Sampler", "VC_DRAW_DRAFT", "VC_DRAW_ACCEPT", "VC_DRAW_TARGET", "vc_sample", "spec_ws_size",
+           "vc_spec_sample"]
 
 _DBG = False   # address-range checks on: every tensor handed to the library is registered
 _DRY = False   # dry run: host tensors stand in for device tensors
@@ -208,14 +211,24 @@ class Model:
         return torch.empty(self.ws_size(max_rows, max_keys), dtype=torch.uint8, device=device)
 
     def prefill(self, tokens: torch.Tensor, k_out, v_out, q_obs, W: int, g0: torch.Tensor, ws: torch.Tensor,
-                chunk: int):
+                chunk: int, last_logits=None):
         call("vc_prefill", self.h, ptr(tokens), tokens.numel(), ptr(k_out), ptr(v_out), k_out.shape[-2],
-             ptr(q_obs), W, ptr(g0), chunk, ptr(ws), ws.numel(), stream_handle())
+             ptr(q_obs), W, ptr(g0), ptr(last_logits), chunk, ptr(ws), ws.numel(), stream_handle())
 
     def draft_step(self, reqs, ws: torch.Tensor, logits=None):
         n = len(reqs)
         arr = (Req * n)(*reqs)
         call("vc_draft_step", self.h, arr, n, ptr(logits), ptr(ws), ws.numel(), stream_handle())
+        return arr
+
+    def draft_step_sampled(self, reqs, samplers, probs, ws: torch.Tensor, logits=None):
+        """vc_draft_step_sampled: samplers, one _vc.Sampler per request; probs, one fp32
+        device tensor [>= x][vocab] per request (row draft_idx is written)."""
+        n = len(reqs)
+        arr = (Req * n)(*reqs)
+        sm = (Sampler * n)(*samplers)
+        pp = (C.c_void_p * n)(*[ptr(p) for p in probs])
+        call("vc_draft_step_sampled", self.h, arr, n, sm, pp, ptr(logits), ptr(ws), ws.numel(), stream_handle())
         return arr
 
     def draft_step_static(self, reqs, logits=None):
@@ -251,6 +264,36 @@ class Model:
     def stage(self, req: Req, slot_k, slot_v, l0: int, l1: int, copy_stream=None):
         call("vc_stage", self.h, C.byref(req), ptr(slot_k), ptr(slot_v), slot_k.shape[-2], l0, l1,
              stream_handle(copy_stream))
+
+
+# ---------------------------------------------------------------- sampled decoding
+def vc_sample(logits: torch.Tensor, samplers, pos, purpose: int, out: torch.Tensor | None = None,
+              probs: torch.Tensor | None = None) -> torch.Tensor:
+    """One draw per row of logits [n][vocab] (fp32, device); samplers: one Sampler per row;
+    pos: the position of each row's token.  Returns the int32 tokens."""
+    n, V = logits.shape
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=logits.device)
+    sm = (Sampler * n)(*samplers)
+    ps = (C.c_int64 * n)(*[int(p) for p in pos])
+    call("vc_sample", ptr(logits), n, V, sm, ps, purpose, ptr(out), ptr(probs), stream_handle())
+    return out
+
+
+def spec_ws_size(x: int) -> int:
+    b = C.c_size_t()
+    call("vc_spec_ws_size", x, C.byref(b))
+    return b.value
+
+
+def vc_spec_sample(logits_t: torch.Tensor, probs_d: torch.Tensor | None, draft: torch.Tensor | int, x: int,
+                   sampler, pos0: int, verified: torch.Tensor, ws: torch.Tensor) -> None:
+    """Speculative rejection sampling of one round: logits_t [x + 1][vocab], probs_d [x][vocab]
+    (fp32, device), draft: the x drafts (a tensor or a device address)."""
+    V = logits_t.shape[-1]
+    d = draft if isinstance(draft, int) else ptr(draft)
+    call("vc_spec_sample", V, ptr(logits_t), ptr(probs_d), d, x, C.byref(sampler), pos0, ptr(verified), ptr(ws),
+         ws.numel(), stream_handle())
 
 
 # ---------------------------------------------------------------- live kernel timing

@@ -14,6 +14,7 @@
 #include "compress.h"
 #include "elementwise.h"
 #include "gemm.h"
+#include "sampling.h"
 
 namespace vc {
 
@@ -279,9 +280,10 @@ vc_status forward_layers(const vc_model* m, int M, uint8_t* ws, const WsLayout& 
   return VC_OK;
 }
 
-// Final norm + LM head + argmax of rows [r0, r0 + M) of ws.h.
+// Final norm + LM head of rows [r0, r0 + M) of ws.h, then the argmax of each row or, with smp
+// (M rows; their logits and out fields are set here), a draw of the given purpose.
 vc_status head(const vc_model* m, int r0, int M, uint8_t* ws, const WsLayout& L, int32_t* out_tok, float* logits_opt,
-               hipStream_t s) {
+               hipStream_t s, const SampleRow* smp = nullptr, int purpose = VC_DRAW_TARGET) {
   const vc_model_desc& d = m->d;
   vc_status st;
   const void* hrow = ws + L.h + size_t(r0) * d.d_model * m->eb;
@@ -291,7 +293,18 @@ vc_status head(const vc_model* m, int r0, int M, uint8_t* ws, const WsLayout& L,
   const ProfRec pr = prof_gemm(M, d.vocab, d.d_model, 1, d.dtype);
   if ((st = gemm(a, m->w.lm_head, P, M, d.vocab, d.d_model, 1, d.dtype, s, pr.a, pr.b))) return st;
   prof_commit(pr);
-  if ((st = k_argmax(P, M, d.vocab, out_tok, s))) return st;
+  if (smp) {
+    SampleRow rows[SAMPLE_MAX_ROWS];
+    VC_REQUIRE(M <= SAMPLE_MAX_ROWS, VC_ERR_ARG, "sampled head: %d rows", M);
+    for (int r = 0; r < M; r++) {
+      rows[r] = smp[r];
+      rows[r].logits = P + int64_t(r) * d.vocab;
+      rows[r].out = out_tok + r;
+    }
+    if ((st = k_sample(rows, M, d.vocab, purpose, s))) return st;
+  } else if ((st = k_argmax(P, M, d.vocab, out_tok, s))) {
+    return st;
+  }
   if (logits_opt) {
     const int64_t bytes = int64_t(M) * d.vocab * 4;
     if (dbg_on()) {
@@ -545,7 +558,7 @@ vc_status vc_profile_read(int32_t kind, vc_profile_stats* out) {
   return VC_OK;
 }
 
-int32_t vc_abi_version(void) { return 1; }
+int32_t vc_abi_version(void) { return 2; }
 
 vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStream_t s, vc_model** out) {
   VC_REQUIRE(desc && w && out, VC_ERR_ARG, "vc_model_create: null argument");
@@ -619,7 +632,7 @@ namespace {
 // The batched draft step over a workspace of ws_bytes bytes at ws (a caller's buffer, or the
 // static scratch of vc_draft_step_static).
 vc_status draft_step_impl(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, void* ws, size_t ws_bytes,
-                          hipStream_t s) {
+                          hipStream_t s, const vc_sampler* smp = nullptr, float* const* probs = nullptr) {
   if (vc_status st = check_model(m)) return st;
   VC_REQUIRE(reqs && ws, VC_ERR_ARG, "vc_draft_step: null argument");
   VC_REQUIRE(n > 0 && n <= VC_MAX_BATCH, VC_ERR_ARG, "vc_draft_step: batch %d not in [1, %d]", n, VC_MAX_BATCH);
@@ -682,7 +695,17 @@ vc_status draft_step_impl(vc_model* m, const vc_req* reqs, int32_t n, float* log
                            qstride, ob, qstride, part, s);
   };
   if ((st = forward_layers(m, n, w8, L, tmpl, set_kv, attend, s))) return st;
-  if ((st = head(m, 0, n, w8, L, tok_out, logits_opt, s))) return st;
+  if (smp) {
+    SampleRow rows[VC_MAX_BATCH];
+    for (int r = 0; r < n; r++) {
+      const vc_req& q = reqs[r];
+      rows[r] = SampleRow{nullptr, probs[r] + int64_t(q.draft_idx) * d.vocab, nullptr, smp[r].seed, smp[r].stream,
+                          int64_t(q.ctx_len) + q.draft_idx + 1, smp[r].temperature};
+    }
+    if ((st = head(m, 0, n, w8, L, tok_out, logits_opt, s, rows, VC_DRAW_DRAFT))) return st;
+  } else if ((st = head(m, 0, n, w8, L, tok_out, logits_opt, s))) {
+    return st;
+  }
   return k_scatter_tok(dst, n, tok_out, s);
 }
 
@@ -719,6 +742,62 @@ extern "C" {
 vc_status vc_draft_step(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, void* ws, size_t ws_bytes,
                         hipStream_t s) {
   return draft_step_impl(m, reqs, n, logits_opt, ws, ws_bytes, s);
+}
+
+vc_status vc_draft_step_sampled(vc_model* m, const vc_req* reqs, int32_t n, const vc_sampler* smp,
+                                float* const* probs, float* logits_opt, void* ws, size_t ws_bytes, hipStream_t s) {
+  VC_REQUIRE(smp && probs && reqs && n > 0 && n <= VC_MAX_BATCH, VC_ERR_ARG, "vc_draft_step_sampled: null argument");
+  for (int r = 0; r < n; r++) {
+    VC_REQUIRE(probs[r], VC_ERR_ARG, "vc_draft_step_sampled: null probabilities of request %d", r);
+    VC_REQUIRE(smp[r].temperature >= 0.f && smp[r].temperature < __builtin_huge_valf(), VC_ERR_ARG,
+               "vc_draft_step_sampled: temperature of request %d not finite and >= 0", r);
+  }
+  return draft_step_impl(m, reqs, n, logits_opt, ws, ws_bytes, s, smp, probs);
+}
+
+vc_status vc_sample(const float* logits, int32_t n_rows, int32_t vocab, const vc_sampler* smp, const int64_t* pos,
+                    int32_t purpose, int32_t* out_tok, float* probs_opt, hipStream_t s) {
+  VC_REQUIRE(n_rows >= 0 && vocab > 0, VC_ERR_ARG, "vc_sample: %d rows of %d", n_rows, vocab);
+  if (n_rows == 0) return VC_OK;
+  VC_REQUIRE(logits && smp && pos && out_tok, VC_ERR_ARG, "vc_sample: null argument");
+  VC_REQUIRE(purpose >= VC_DRAW_DRAFT && purpose <= VC_DRAW_TARGET, VC_ERR_ARG, "vc_sample: purpose %d", purpose);
+  for (int32_t r0 = 0; r0 < n_rows; r0 += SAMPLE_MAX_ROWS) {
+    const int n = std::min<int32_t>(SAMPLE_MAX_ROWS, n_rows - r0);
+    SampleRow rows[SAMPLE_MAX_ROWS];
+    for (int r = 0; r < n; r++) {
+      const vc_sampler& q = smp[r0 + r];
+      VC_REQUIRE(q.temperature >= 0.f && q.temperature < __builtin_huge_valf(), VC_ERR_ARG,
+                 "vc_sample: temperature of row %d not finite and >= 0", r0 + r);
+      rows[r] = SampleRow{logits + int64_t(r0 + r) * vocab,
+                          probs_opt ? probs_opt + int64_t(r0 + r) * vocab : nullptr,
+                          out_tok + r0 + r,
+                          q.seed,
+                          q.stream,
+                          pos[r0 + r],
+                          q.temperature};
+    }
+    if (vc_status st = k_sample(rows, n, vocab, purpose, s)) return st;
+  }
+  return VC_OK;
+}
+
+vc_status vc_spec_ws_size(int32_t x, size_t* bytes) {
+  VC_REQUIRE(x >= 0 && bytes, VC_ERR_ARG, "vc_spec_ws_size: bad argument");
+  *bytes = spec_ws_bytes(x);
+  return VC_OK;
+}
+
+vc_status vc_spec_sample(int32_t vocab, const float* logits_t, const float* probs_d, const int32_t* draft, int32_t x,
+                         const vc_sampler* smp, int64_t pos0, int32_t* verified, void* ws, size_t ws_bytes,
+                         hipStream_t s) {
+  VC_REQUIRE(vocab > 0 && x >= 0, VC_ERR_ARG, "vc_spec_sample: vocab %d, x %d", vocab, x);
+  VC_REQUIRE(logits_t && smp && verified && ws && (x == 0 || (probs_d && draft)), VC_ERR_ARG,
+             "vc_spec_sample: null argument");
+  VC_REQUIRE(smp->temperature >= 0.f && smp->temperature < __builtin_huge_valf(), VC_ERR_ARG,
+             "vc_spec_sample: temperature not finite and >= 0");
+  VC_REQUIRE(ws_bytes >= spec_ws_bytes(x), VC_ERR_CAPACITY, "vc_spec_sample: workspace %zu < %zu bytes", ws_bytes,
+             spec_ws_bytes(x));
+  return k_spec(logits_t, probs_d, draft, x, vocab, smp->temperature, smp->seed, smp->stream, pos0, verified, ws, s);
 }
 
 vc_status vc_draft_step_static(vc_model* m, const vc_req* reqs, int32_t n, float* logits_opt, hipStream_t s) {
@@ -880,7 +959,8 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
 }
 
 vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out, void* v_out, int32_t cap, void* q_obs,
-                     int32_t W, int32_t* g0_out, int32_t chunk, void* ws, size_t ws_bytes, hipStream_t s) {
+                     int32_t W, int32_t* g0_out, float* last_logits_opt, int32_t chunk, void* ws, size_t ws_bytes,
+                     hipStream_t s) {
   if (vc_status st = check_model(m)) return st;
   VC_REQUIRE(tokens && k_out && v_out && g0_out && ws, VC_ERR_ARG, "vc_prefill: null argument");
   VC_REQUIRE(T > 0 && cap >= T && chunk > 0, VC_ERR_ARG, "vc_prefill: bad sizes");
@@ -953,7 +1033,7 @@ vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out,
     };
     if ((st = forward_layers(m, C, w8, L, tmpl, set_kv, attend, s))) return st;
     if (c0 + C == T) {
-      if ((st = head(m, C - 1, 1, w8, L, g0_out, nullptr, s))) return st;
+      if ((st = head(m, C - 1, 1, w8, L, g0_out, last_logits_opt, s))) return st;
     }
   }
   return VC_OK;

@@ -11,7 +11,7 @@ PKG = os.path.dirname(HERE)
 OUT = os.path.join(PKG, "libvc.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "attention.hip", "attention_rows.hip", "attention_quant.hip", "gemm.hip", "elementwise.hip",
-           "compress.hip", "synth.hip", "bounds.hip"]
+           "compress.hip", "synth.hip", "bounds.hip", "sampling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++20", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-result", "-I" + os.path.join(PKG, "..", "include")]

@@ -118,23 +118,36 @@ class Request:
     n_verified: int = 0                # verifications issued
     rounds: list = field(default_factory=list)  # per-round record (Engine(record=True))
     rec_host: torch.Tensor = None      # pinned [2][x + 1]: this round's rows and verified tokens
+    sampler: object = None             # _vc.Sampler (sampled decoding), else None (greedy)
+    probs: torch.Tensor = None         # fp32 [x][vocab]: this round's draft distributions
 
 
 class Engine:
     """Owns a vc_model, its workspaces and the per-request device/host buffers."""
 
     record = False
+    temperature = None  # greedy unless a temperature is given
 
     # the driver pins at most ~70 GiB of host memory per process; rows beyond the budget
     # go to pageable memory (staged at roughly half the pinned PCIe rate)
     PINNED_BUDGET = 69_000_000_000
 
     def __init__(self, model: B.Model, spec, chunk: int = 1024, device="cuda", pinned_budget: int | None = None,
-                 record: bool = False):
+                 record: bool = False, temperature: float | None = None, seed: int = 0):
         """record: keep, per request and round, the position, the pending token, the drafts, the
-        verifier's tokens and the accept count (host copies of device values; for parity tests)."""
+        verifier's tokens and the accept count (host copies of device values; for parity tests).
+        temperature: None decodes greedily (exact-match acceptance); a value >= 0 samples
+        ("Mathematical Guarantee of Lossless Correctness", VeriCache Guide): drafts are drawn
+        from the compressed cache's distribution and kept by speculative rejection sampling
+        against the full-KV distribution, with the draws of request r taken from stream r of
+        the generator keyed by seed."""
         self.m = model
         self.record = record
+        self.temperature = temperature
+        self.seed = seed
+        self.vlogits = None
+        self.ws_spec = None
+        self.vargmax = None
         self.spec = spec
         self.shape = model.shape
         self.dt = torch.bfloat16 if self.shape.dtype == "bf16" else torch.float32
@@ -165,7 +178,14 @@ class Engine:
         q_obs = torch.empty(L, W, Hq, D, dtype=self.dt, device=self.device)
         g0 = torch.empty(1, dtype=torch.int32, device=self.device)
         ws = self.m.workspace(min(self.chunk, T), T, device=self.device)
-        self.m.prefill(prompt, kd, vd, q_obs, W, g0, ws, min(self.chunk, T))
+        last = None
+        if self.temperature is not None:
+            r.sampler = B.Sampler(self.temperature, self.seed, r.idx)
+            last = torch.empty(1, s.vocab, dtype=torch.float32, device=self.device)
+            B.debug_register(last, g0)
+        self.m.prefill(prompt, kd, vd, q_obs, W, g0, ws, min(self.chunk, T), last_logits=last)
+        if last is not None:  # g0 drawn from the prompt's last row at position T
+            B.vc_sample(last, [r.sampler], [T], B.VC_DRAW_TARGET, out=g0)
         if runtime.RT.dry:  # the first token the prefill would have written
             g0.fill_(1)
         del ws
@@ -193,6 +213,9 @@ class Engine:
         r.result_host = torch.empty(x + 2, dtype=torch.int32, pin_memory=runtime.RT.pin)
         if self.record:
             r.rec_host = torch.empty(2, x + 1, dtype=torch.int32, pin_memory=runtime.RT.pin)
+        if r.sampler is not None:
+            r.probs = torch.empty(x, s.vocab, dtype=torch.float32, device=self.device)
+            B.debug_register(r.probs)
         B.debug_register(r.rows, r.tail_k, r.tail_v, r.vtail_k, r.vtail_v, r.verified, r.result)
         r.req = Req(comp=r.comp.data_ptr(), cd=None, tail_k=r.tail_k.data_ptr(), tail_v=r.tail_v.data_ptr(),
                     tail_cap=tail_cap, n_tail=0, ctx_len=T, draft_idx=0, full_k_host=r.full_k.data_ptr(),
@@ -217,6 +240,11 @@ class Engine:
         max_x = max(r.x for r in self.reqs)
         self.ws_draft = self.m.workspace(min(n, 16), max_ctx, device=self.device)
         self.ws_verify = self.m.workspace(max_x + 1, max_ctx, device=self.device)
+        if self.temperature is not None:
+            self.vlogits = torch.empty(max_x + 1, s.vocab, dtype=torch.float32, device=self.device)
+            self.ws_spec = torch.empty(B.spec_ws_size(max_x), dtype=torch.uint8, device=self.device)
+            self.vargmax = torch.empty(max_x + 1, dtype=torch.int32, device=self.device)  # greedy picks, unused
+            B.debug_register(self.vlogits, self.ws_spec, self.vargmax)
         L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
         n_slots = min(getattr(self, 'n_slots', 2), n)
         slot_rows = max(max(r.n_host for r in self.reqs), 1)
@@ -300,7 +328,11 @@ class Engine:
             active += fresh
         for k in range(0, len(active), 16):
             grp = active[k:k + 16]
-            self.m.draft_step([r.req for r in grp], self.ws_draft)
+            if self.temperature is None:
+                self.m.draft_step([r.req for r in grp], self.ws_draft)
+            else:
+                self.m.draft_step_sampled([r.req for r in grp], [r.sampler for r in grp], [r.probs for r in grp],
+                                          self.ws_draft)
             self.drafted += len(grp)
             for r in grp:
                 r.req.draft_idx += 1
@@ -323,6 +355,8 @@ class Engine:
         if self.record:
             n = r.x_cur + 1
             rows, ver = r.rec_host[0, :n].tolist(), r.rec_host[1, :n].tolist()
+            if self.temperature is not None:  # the verifier's tokens after a are not written
+                ver = ver[:a + 1]
             r.rounds.append({"pos": r.req.ctx_len, "n_tail": r.req.n_tail, "pending": rows[0], "draft": rows[1:],
                              "verified": ver, "a": a})
         new = r.result_host[1:a + 2].tolist()
@@ -454,7 +488,13 @@ class Engine:
         if r.budget > 0:
             r.budget -= 1
         sk, sv = self.slots[r.slot]
-        self.m.verify(r.req, sk, sv, r.rows, r.x_cur + 1, r.verified, r.vtail_k, r.vtail_v, self.ws_verify)
+        if self.temperature is None:
+            self.m.verify(r.req, sk, sv, r.rows, r.x_cur + 1, r.verified, r.vtail_k, r.vtail_v, self.ws_verify)
+        else:  # the verify rows' logits, then rejection sampling writes the tokens vc_accept compares
+            self.m.verify(r.req, sk, sv, r.rows, r.x_cur + 1, self.vargmax, r.vtail_k, r.vtail_v, self.ws_verify,
+                          logits=self.vlogits)
+            B.vc_spec_sample(self.vlogits[:r.x_cur + 1], r.probs, r.rows.data_ptr() + 4, r.x_cur, r.sampler,
+                             r.req.ctx_len, r.verified, self.ws_spec)
         if self.record:  # before vc_accept overwrites rows[0] with the next pending token
             n = r.x_cur + 1
             r.rec_host[0, :n].copy_(r.rows[:n], non_blocking=True)
@@ -506,6 +546,39 @@ def greedy_resident(model: B.Model, prompt: torch.Tensor, n_tokens: int, chunk: 
     if min(toks) < 0:
         raise NonFiniteLogits(f"greedy decoding: token -1 at step {toks.index(-1)}")
     return toks, time.perf_counter() - t0, (kd, vd)
+
+
+def sample_resident(model: B.Model, prompt: torch.Tensor, n_tokens: int, sampler, chunk: int = 1024, device="cuda"):
+    """Full-KV sampled decoding with the cache resident in HBM (the distribution sampled
+    VeriCache must reproduce): the token at position p is drawn from the row before it with
+    the TARGET draw of p (g0 from the prompt's last row at position T)."""
+    s = model.shape
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    T = int(prompt.numel())
+    cap = T + n_tokens
+    L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
+    kd = torch.empty(L, Hkv, cap, D, dtype=dt, device=device)
+    vd = torch.empty_like(kd)
+    out = torch.empty(n_tokens, dtype=torch.int32, device=device)
+    logits = torch.empty(1, s.vocab, dtype=torch.float32, device=device)
+    pick = torch.empty(1, dtype=torch.int32, device=device)
+    ws = model.workspace(min(chunk, T), cap, device=device)
+    B.debug_register(kd, vd, out, logits, pick, ws)
+    model.prefill(prompt, kd, vd, None, 0, pick, ws, min(chunk, T), last_logits=logits)
+    B.vc_sample(logits, [sampler], [T], B.VC_DRAW_TARGET, out=out[:1])
+    req = Req(ctx_len=T)
+    row = D * (2 if s.dtype == "bf16" else 4)
+    for i in range(1, n_tokens):
+        req.ctx_len = T + i - 1
+        off = req.ctx_len * row
+        model.verify_raw(req, kd.data_ptr(), vd.data_ptr(), cap, out.data_ptr() + 4 * (i - 1), 1, pick.data_ptr(),
+                         kd.data_ptr() + off, vd.data_ptr() + off, cap, ws, logits=logits.data_ptr())
+        B.vc_sample(logits, [sampler], [T + i], B.VC_DRAW_TARGET, out=out[i:i + 1])
+    runtime.RT.synchronize()
+    toks = out.tolist()
+    if min(toks) < 0:
+        raise NonFiniteLogits(f"sampled decoding: token -1 at step {toks.index(-1)}")
+    return toks
 
 
 def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tensor, n_steps: int, ws: torch.Tensor,

@@ -28,7 +28,8 @@ Readings where the pages are silent:
     running sum exceeds u * (total weight); if none does (only through
     rounding), the last index of positive weight.
   - A rejection whose residual has no positive mass (only through rounding)
-    draws from p_target instead.
+    draws from p_target with the rejected candidate's weight set to zero, so
+    that the emitted token always differs from the rejected draft.
   - A row whose logits hold NaN or +inf, or nothing finite, yields token -1.
   - Uniforms: key (seed, 0), counter (position, purpose, stream, 0), where
     position is the absolute position of the token being chosen and purpose
@@ -151,7 +152,10 @@ def speculative_accept(pt_rows, pd_rows, draft, u_acc, u_res):
         if lhs < rhs:
             continue
         r = residual_weights(pt, pd)
-        k, m = sample_index(r if r.sum() > 0 else pt, u_res[i])
+        if not r.sum() > 0:
+            r = np.array(pt, dtype=np.float64)
+            r[d] = 0.0
+        k, m = sample_index(r, u_res[i])
         margins.append(m)
         return i, k, margins
     k, m = sample_index(pt_rows[x], u_res[x])

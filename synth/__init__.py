@@ -49,6 +49,7 @@ S_ATT_TV = 205
 S_ATT_OUTL = 206
 S_CTXLEN = 300          # mixed-batch context lengths
 S_XDRAW = 301           # mixed-batch draft horizons
+S_LOGITS = 400          # synthetic logits rows (sampling tests): + case index
 S_LAYER0 = 1000         # + 16 * layer + tensor id
 T_WQ, T_WK, T_WV, T_WO, T_W1, T_W3, T_W2 = range(7)
 

@@ -30,5 +30,5 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_loads_and_covers_every_symbol():
     import lossless_speculative_decoding_amd._vc as vc
-    assert vc.raw("vc_abi_version")() == 1
+    assert vc.raw("vc_abi_version")() == 2
     assert sorted(vc.exported_symbols()) == declared()

@@ -379,5 +379,7 @@ def test_v_beyond_fp16_range_is_non_finite_not_wrong():
         Vj = np.concatenate([_f(vb2[j, idx[j]]), _f(tv[j])])
         for g in range(4):
             r = OA.attend(_f(qd[0, j * 4 + g]), Kj, Vj)
-            m = np.isfinite(r)
+            m = np.ones(D, bool)
+            if j == 3:
+                m[ch] = False                           # the channel the large element feeds
             assert np.abs(o[j * 4 + g][m] - r[m]).max() <= TOL_BF16 * np.abs(r[m]).max()

@@ -344,7 +344,8 @@ def run_model_workload(args) -> dict:
     n_cap = w.n_tokens
     W = make_weights(s, device=device)
     model = vc.Model(s, W, max_pos=max(ctx) + n_cap + 64)
-    eng = Engine(model, w.compress, chunk=2048, device=device)
+    sampled = args.temperature is not None
+    eng = Engine(model, w.compress, chunk=2048, device=device, temperature=args.temperature, seed=args.seed)
     prefill_prof = None
     for r, (T, x) in enumerate(zip(ctx, xs)):
         p = torch.empty(T, dtype=torch.int32, device=device)
@@ -360,7 +361,7 @@ def run_model_workload(args) -> dict:
         log(f"request {r}: T={T} prefill+compress+offload {time.perf_counter() - t0:.1f}s")
     x_round = max(xs)
     eng.start(lead=args.lead or None, draft_batch=args.draft_batch or None, queue_min=args.queue_min, n_slots=args.slots,
-              adaptive=args.adaptive, x_min=max(xs))
+              adaptive=args.adaptive, x_min=max(xs), fallback_after=args.fallback_after, plain_rounds=args.plain_rounds)
     t_setup = time.perf_counter() - t_setup
     log(f"setup {t_setup:.1f}s")
 
@@ -484,7 +485,8 @@ def run_model_workload(args) -> dict:
                                    eng.copy_stream)
     base_tok_s = args.baseline_steps / bsecs
     n_cmp = min(len(toks), len(r0.emitted) - 1)
-    base_match = toks[:n_cmp] == r0.emitted[1:1 + n_cmp]
+    # sampled decoding emits another draw of the same distribution: tokens are not comparable
+    base_match = None if sampled else toks[:n_cmp] == r0.emitted[1:1 + n_cmp]
     log(f"full-KV-from-host greedy: {base_tok_s:.2f} tok/s; its {n_cmp} tokens match VeriCache's: {base_match}")
     # resident full-KV greedy (context only: the workload keeps the full cache on the host): request
     # 0 alone with its whole cache in HBM, one vc_verify row per token appended in place
@@ -512,7 +514,7 @@ def run_model_workload(args) -> dict:
     sync()
     res_tok_s = n_res / (time.perf_counter() - t_r)
     n_rc = min(n_res, len(r0.emitted) - 1)
-    res_match = res_rows[1:1 + n_rc].tolist() == r0.emitted[1:1 + n_rc]
+    res_match = None if sampled else res_rows[1:1 + n_rc].tolist() == r0.emitted[1:1 + n_rc]
     del kd, vd
     log(f"resident full-KV greedy (one request, context): {res_tok_s:.1f} tok/s; tokens match VeriCache's: {res_match}")
 
@@ -535,6 +537,8 @@ def run_model_workload(args) -> dict:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded random-init weights and uniform prompt ids)",
+        "decoding": "greedy" if not sampled else f"sampled, temperature {args.temperature}, seed {args.seed} "
+                                                 "(speculative rejection sampling)",
         "config": {"workload": w.name, "batch": len(ctx), "ctx": ctx if len(set(ctx)) > 1 else ctx[0],
                    "x": xs if len(set(xs)) > 1 else xs[0],
                    "compress": w.compress.kind + ("" if w.compress.kind != "tokdrop" else
@@ -572,6 +576,10 @@ def run_model_workload(args) -> dict:
         "scheduler": {"draft_batch": eng.draft_batch, "queue_min": eng.queue_min, "lead": eng.lead,
                       "slots": len(eng.slots), "adaptive": args.adaptive,
                       "x_min": eng.x_min if args.adaptive else None,
+                      "fallback_after": args.fallback_after if args.adaptive else None,
+                      "plain_rounds": args.plain_rounds if args.adaptive and args.fallback_after else None,
+                      "plain_round_share": round(sum(1 for r in eng.reqs for g in r.x_hist if g == 0) /
+                                                 max(sum(len(r.x_hist) for r in eng.reqs), 1), 4),
                       "drafts_per_round": round((eng.drafted - d0) / max(len(accepts), 1), 2),
                       "mean_requests_per_draft_step": round(mean_draft_batch, 2)},
         "whole_decode": None if args.no_whole_decode else {"tokens_per_s": round(dec_tokens / dec_secs, 3), "tokens": dec_tokens,
@@ -598,20 +606,23 @@ def bounds_replay(args):
     tails).  Prints the checks made; exits non-zero at the first range outside every buffer."""
     import lossless_speculative_decoding_amd as vc
     from lossless_speculative_decoding_amd import runtime
-    runtime.use(runtime.DryRT(seed=0))
+    # "collapse": runs of rounds that keep no draft between runs that keep all (plain rounds then occur
+    # under --adaptive --fallback-after); default: every other round keeps all, the others a seeded count
+    policy = (lambda idx, rnd, x: 0 if (rnd // 5) % 2 else x) if args.replay_policy == "collapse" else None
+    runtime.use(runtime.DryRT(seed=0, accept_policy=policy))
     vc.debug_mode(vc.VC_DEBUG_DRY)
     args.no_cpu_baseline = True
     t0 = time.perf_counter()
     try:
-        run_model_workload(args)
+        res = run_model_workload(args)
     except vc._vc.VCError as e:
         st = vc.debug_stats()
         print(json.dumps({"bounds_replay": args.config, "ok": False, "error": str(e), **st}), flush=True)
         sys.exit(1)
     st = vc.debug_stats()
     print(json.dumps({"bounds_replay": args.config, "ok": st["violations"] == 0, "seconds": round(time.perf_counter()
-                                                                                                 - t0, 1), **st}),
-          flush=True)
+                                                                                                 - t0, 1),
+                      "plain_round_share": res["scheduler"]["plain_round_share"], **st}), flush=True)
     sys.exit(0 if st["violations"] == 0 else 1)
 
 
@@ -639,6 +650,13 @@ def main():
     ap.add_argument("--adaptive", action="store_true",
                     help="per-request draft length between L_min = ceil(t_copy / t_step) (measured in the warmup) "
                          "and the workload's x: doubled after an all-accepted round, a + 1 after a rejection")
+    ap.add_argument("--fallback-after", type=int, default=0,
+                    help="with --adaptive: after this many consecutive rounds that keep no draft, decode plainly "
+                         "(no drafts) for --plain-rounds rounds (0: never)")
+    ap.add_argument("--plain-rounds", type=int, default=8)
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="sampled decoding at this temperature with speculative rejection sampling (default: greedy)")
+    ap.add_argument("--seed", type=int, default=0, help="generator key of sampled decoding")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-whole-decode", action="store_true",
                     help="skip decoding the rest of every request after the timed rounds (the whole-decode rate)")
@@ -648,6 +666,8 @@ def main():
     ap.add_argument("--bounds-replay", action="store_true",
                     help="no GPU work: replay the workload's sequence of library calls on the CPU with every "
                          "launch's byte ranges checked against the buffers allocated for it")
+    ap.add_argument("--replay-policy", choices=["grow", "collapse"], default="grow",
+                    help="accept counts a bounds replay assumes (collapse: runs of rounds that keep no draft)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that scales "
                          "the HBM byte counters of a profile)")

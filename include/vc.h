@@ -262,7 +262,8 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
  * a == x); req->rows[0] = verified[a] (the next pending token); then the
  * verifier's rows 0..a are copied from vtail into the request's tail at n_tail
  * (overwriting this round's draft rows).  verified: device int32 [x+1];
- * result: device int32 [x+2].  Does not block and does not change *req:
+ * result: device int32 [x+2].  x = 0 is a plain round (no drafts: the pending
+ * token alone was verified, and its successor is emitted).  Does not block and does not change *req:
  * after result[0] is visible on the host, call vc_commit.
  * This splits the single accept-and-commit call of the four-call interface
  * sketched for the method: accepting runs on the device and returns no host

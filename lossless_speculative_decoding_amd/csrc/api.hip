@@ -1043,7 +1043,7 @@ vc_status vc_accept(vc_model* m, const vc_req* req, const int32_t* verified, int
                     const void* vtail_v, int32_t vtail_cap, int32_t* result, hipStream_t s) {
   if (vc_status st = check_model(m)) return st;
   VC_REQUIRE(req && req->rows && verified && vtail_k && vtail_v && result, VC_ERR_ARG, "vc_accept: null argument");
-  VC_REQUIRE(x >= 1 && vtail_cap >= x + 1, VC_ERR_ARG, "vc_accept: bad draft length %d", x);
+  VC_REQUIRE(x >= 0 && vtail_cap >= x + 1, VC_ERR_ARG, "vc_accept: bad draft length %d", x);
   VC_REQUIRE(req->tail_k && req->tail_v, VC_ERR_ARG, "vc_accept: request without tail");
   VC_REQUIRE(req->n_tail + x + 1 <= req->tail_cap, VC_ERR_CAPACITY, "vc_accept: tail capacity");
   const vc_model_desc& d = m->d;

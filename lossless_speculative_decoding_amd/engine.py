@@ -114,7 +114,10 @@ class Request:
     stage_ev: object = None
     acc_ev: object = None
     budget: int = -1                   # verifications it may still issue (-1: unlimited; 0: parked)
-    x_cur: int = 0                     # this round's draft length (x unless adaptive)
+    x_cur: int = 0                     # this round's draft length (x unless adaptive; 0: a plain round)
+    x_hist: list = field(default_factory=list)  # draft length of every verification issued
+    zero_run: int = 0                  # consecutive rounds that kept no draft
+    plain_left: int = 0                # plain rounds left before drafting is tried again
     n_verified: int = 0                # verifications issued
     rounds: list = field(default_factory=list)  # per-round record (Engine(record=True))
     rec_host: torch.Tensor = None      # pinned [2][x + 1]: this round's rows and verified tokens
@@ -257,7 +260,8 @@ class Engine:
 
     # ------------------------------------------------------------ the VeriCache loop
     def start(self, lead: int | None = None, stagger: bool = True, draft_batch: int | None = None,
-              queue_min: int = 1, n_slots: int = 3, adaptive: bool = False, x_min: int = 1):
+              queue_min: int = 1, n_slots: int = 3, adaptive: bool = False, x_min: int = 1,
+              fallback_after: int = 0, plain_rounds: int = 8):
         """Allocate slots/workspaces and set the staggered start ticks.
 
         lead: a request's host rows start to stage once it has begun drafting and is within
@@ -281,7 +285,12 @@ class Engine:
         sign that speculation costs more than it saves).  A request starts at its x; after a
         round that accepts every draft its length doubles (at most x), after a rejection at a it
         becomes max(x_min, a + 1).  The emitted tokens do not change, only how many are drafted
-        per verification."""
+        per verification.
+        fallback_after / plain_rounds (adaptive only): after fallback_after consecutive rounds
+        that keep no draft, the request decodes plainly for plain_rounds rounds (no drafts: each
+        round verifies the pending token alone against the full KV and emits one token; "When
+        the Serving Stack Breaks Down", KV Cache and Speculative Decoding), then drafts again at
+        x_min.  0 never falls back."""
         self.n_slots = max(1, n_slots)
         self._alloc()
         n = len(self.reqs)
@@ -292,6 +301,10 @@ class Engine:
             r.x_cur = r.x
         self.adaptive = adaptive
         self.x_min = max(1, x_min)
+        self.fallback_after = fallback_after
+        self.plain_rounds = plain_rounds
+        for r in self.reqs:
+            r.zero_run = r.plain_left = 0
         self.lead = max(r.x for r in self.reqs) if lead is None else lead
         self.draft_batch = n if draft_batch is None else max(1, draft_batch)
         self.queue_min = queue_min
@@ -315,6 +328,10 @@ class Engine:
             if (r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= max(1, r.x_cur - self.lead)
                     and self.tick >= r.start_tick):
                 self._try_stage(r)
+        # a request in a plain round (draft length 0) has nothing to draft
+        for r in reqs:
+            if r.phase == DRAFT and r.x_cur == 0 and r.budget != 0 and self.tick >= r.start_tick:
+                r.phase = WAIT_SLOT
         # 3. one batched draft step for every drafting request; requests yet to begin wait for a
         # fuller batch while enough drafted requests are queued for the host link
         ready = [r for r in reqs
@@ -366,9 +383,24 @@ class Engine:
         r.emitted += new
         r.accepts.append(a)
         if self.adaptive:
-            r.x_cur = min(r.x, 2 * r.x_cur) if a == r.x_cur else max(min(self.x_min, r.x), a + 1)
+            self._next_x(r, a)
         self.m.commit(r.req, a, r.vtail_k, r.vtail_v, after_event=r.acc_ev, copy_stream=self.copy_stream)
         r.phase = DRAFT if len(r.emitted) < r.n_tokens else DONE
+
+    def _next_x(self, r: Request, a: int):
+        """The next round's draft length after a round that kept a drafts (see start)."""
+        if r.x_cur == 0:
+            r.plain_left -= 1
+            if r.plain_left <= 0:
+                r.x_cur, r.zero_run = min(self.x_min, r.x), 0
+            return
+        r.zero_run = r.zero_run + 1 if a == 0 else 0
+        if self.fallback_after and r.zero_run >= self.fallback_after:
+            r.x_cur, r.plain_left = 0, self.plain_rounds
+        elif a == r.x_cur:
+            r.x_cur = min(r.x, 2 * r.x_cur)
+        else:
+            r.x_cur = max(min(self.x_min, r.x), a + 1)
 
     def drain(self):
         """Wait for every in-flight verification and fold its accepted tokens in."""
@@ -383,9 +415,10 @@ class Engine:
         return sum(len(r.emitted) for r in self.reqs)
 
     def run(self, lead: int | None = None, stagger: bool = True, trace: list | None = None, adaptive: bool = False,
-            x_min: int = 1):
+            x_min: int = 1, fallback_after: int = 0, plain_rounds: int = 8):
         """Decode every request to its n_tokens; returns wall seconds of the decode phase."""
-        self.start(lead, stagger, adaptive=adaptive, x_min=x_min)
+        self.start(lead, stagger, adaptive=adaptive, x_min=x_min, fallback_after=fallback_after,
+                   plain_rounds=plain_rounds)
         t0 = time.perf_counter()
         while any(r.phase != DONE for r in self.reqs):
             self.step()
@@ -485,6 +518,7 @@ class Engine:
 
     def _verify(self, r: Request, cs):
         self.verifications += 1
+        r.x_hist.append(r.x_cur)
         if r.budget > 0:
             r.budget -= 1
         sk, sv = self.slots[r.slot]

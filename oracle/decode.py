@@ -150,13 +150,52 @@ class RoundLog:
         self.draft_gap, self.verify_gap = draft_gap, verify_gap
 
 
+class DraftLength:
+    """Draft length per round, with a fall back to plain decoding.
+
+    [VC3] "踩过的坑": a short verification cycle wastes the long accepted runs,
+    so x should grow with the acceptance; [KV4] "When the Serving Stack Breaks
+    Down": when drafts stop matching, speculation costs a draft pass and a
+    verification pass for the one token plain decoding would give, so fall
+    back to plain decoding.  Reading (the pages give no numbers): start at
+    x_max; after a round that keeps all x drafts, double x (at most x_max);
+    after a rejection at a, x = max(x_min, a + 1); after fallback_after
+    consecutive rounds that keep no draft (0: never), decode plainly (x = 0:
+    the round verifies the pending token alone and emits one token) for
+    plain_rounds rounds, then probe again at x_min.  The tokens do not depend
+    on any of this (every x gives the greedy tokens), only the work per token.
+    """
+
+    def __init__(self, x_max: int, x_min: int = 1, fallback_after: int = 0, plain_rounds: int = 8):
+        self.x_max, self.x_min = x_max, max(1, min(x_min, x_max))
+        self.fallback_after, self.plain_rounds = fallback_after, plain_rounds
+        self.x = x_max
+        self.zero_run = 0
+        self.plain_left = 0
+
+    def after(self, a: int) -> None:
+        if self.x == 0:
+            self.plain_left -= 1
+            if self.plain_left <= 0:
+                self.x, self.zero_run = self.x_min, 0
+            return
+        self.zero_run = self.zero_run + 1 if a == 0 else 0
+        if self.fallback_after and self.zero_run >= self.fallback_after:
+            self.x, self.plain_left = 0, self.plain_rounds
+        elif a == self.x:
+            self.x = min(self.x_max, 2 * self.x)
+        else:
+            self.x = max(self.x_min, a + 1)
+
+
 def vericache(W: Weights, prompt, n_tokens: int, x: int, make_draft_cache, pre: Prefill | None = None,
-              drafter=None):
+              drafter=None, policy: DraftLength | None = None):
     """The VeriCache loop.  Returns (tokens, rounds).
 
     make_draft_cache(pre) -> segment with rows(l, j) (the compressed cache).
     drafter(round_index, pending, own_draft) -> replacement draft list (to test
         that any drafter still yields the greedy output); None keeps the model's drafts.
+    policy: a DraftLength choosing each round's x (None: x every round).
     """
     s = W.shape
     pre = pre or prefill(W, prompt)
@@ -171,8 +210,9 @@ def vericache(W: Weights, prompt, n_tokens: int, x: int, make_draft_cache, pre: 
         # ---- draft x tokens with the compressed cache
         dtail = RowStore(s.n_layers, s.n_kv_heads, s.head_dim)
         past = chain(comp, tail, dtail)
+        xr = x if policy is None else policy.x
         draft, t, dgap = [], pending, []
-        for i in range(x):
+        for i in range(xr):
             o = row_forward(W, t, pos + i, past)
             dtail.append(o.k, o.v)
             t = argmax(o.logits)
@@ -194,6 +234,8 @@ def vericache(W: Weights, prompt, n_tokens: int, x: int, make_draft_cache, pre: 
         # ---- accept and commit
         a, emitted = accept(draft, ver)
         rounds.append(RoundLog(pos, draft, ver, a, emitted, dgap, vgap))
+        if policy is not None:
+            policy.after(a)
         out += emitted
         for i in range(a + 1):
             full.append(*kv[i])

@@ -58,6 +58,7 @@ def compare_rounds(name, gpu_rounds, ref_a, ref_draft, ref_ver, ref_dgap, ref_vg
     for k, rd in enumerate(gpu_rounds):
         if k >= len(ref_a):
             break
+        assert len(rd["draft"]) == len(ref_draft[k]), f"{name}: round {k}: draft length differs from the oracle's"
         for what, g, r, gap in (("draft", rd["draft"], ref_draft[k], ref_dgap[k]),
                                 ("verify row", rd["verified"], ref_ver[k], ref_vgap[k])):
             for i, (a_, b_) in enumerate(zip(g, r)):

@@ -35,6 +35,22 @@ def test_full_size_workload_replay_stays_in_bounds(config):
     assert out["pinned_peak"] <= 69e9
 
 
+@pytest.mark.parametrize("config,extra", [("llama8b_tokdrop", ("--temperature", "0.8")),
+                                          ("llama8b_q2", ("--temperature", "0.8", "--adaptive", "--fallback-after",
+                                                          "2", "--plain-rounds", "3", "--replay-policy", "collapse")),
+                                          ("llama8b_tokdrop", ("--adaptive", "--fallback-after", "2",
+                                                               "--replay-policy", "collapse"))])
+def test_sampled_and_fallback_replay_stays_in_bounds(config, extra):
+    """Sampled decoding (draft distributions, verify logits, rejection sampling) and plain rounds
+    (x = 0) add launches and buffers of their own: the same replay, with them."""
+    out = _replay(config, "--no-whole-decode", *extra)
+    print(out)
+    assert out["rc"] == 0 and out["ok"] and out["violations"] == 0
+    assert out["launches"] > 100_000
+    if "--fallback-after" in extra:
+        assert out["plain_round_share"] > 0.05          # plain rounds (x = 0) were replayed
+
+
 def _dry_model():
     """A 1-layer bf16 model on host memory under the dry mode, and a quantized request."""
     import torch

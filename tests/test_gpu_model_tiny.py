@@ -101,3 +101,28 @@ def test_vericache_equals_gpu_greedy_and_oracle(setup):
     rr = setup["ref_rounds"]
     compare_rounds("tiny token drop", r.rounds, [d.a for d in rr], [d.draft for d in rr], [d.verified for d in rr],
                    [d.draft_gap for d in rr], [d.verify_gap for d in rr], TOL_F32)
+
+
+@pytest.mark.parametrize("fallback_after,plain_rounds", [(2, 3), (0, 0)])
+def test_adaptive_and_fallback_rounds_match_oracle(setup, fallback_after, plain_rounds):
+    """Adaptive draft length with the fall back to plain rounds (x = 0) when acceptance
+    collapses: the GPU engine's rounds (position, drafts, verifier tokens, accept count) equal
+    the oracle's loop run with the same policy, and the tokens are the oracle's greedy tokens."""
+    from lossless_speculative_decoding_amd.engine import Engine
+    m, prompt, w, ow = setup["m"], setup["prompt"], setup["w"], setup["ow"]
+    eng = Engine(m, w.compress, record=True)
+    r = eng.add_request(prompt, w.x[0], w.n_tokens)
+    eng.run(adaptive=True, x_min=2, fallback_after=fallback_after, plain_rounds=plain_rounds)
+    pol = OD.DraftLength(w.x[0], x_min=2, fallback_after=fallback_after, plain_rounds=plain_rounds)
+    ref, rr = OD.vericache(ow, setup["prompt_np"], w.n_tokens, w.x[0],
+                           lambda pr: OD.draft_cache_tokdrop(pr, ow, keep_total=w.ctx[0] // 4, keep_recent=64),
+                           pre=setup["pre"], policy=pol)
+    xs = [len(g["draft"]) for g in r.rounds]
+    log(f"fallback_after={fallback_after}: draft lengths {xs}")
+    if fallback_after:
+        assert 0 in xs
+    compare_rounds("tiny adaptive", r.rounds, [d.a for d in rr], [d.draft for d in rr], [d.verified for d in rr],
+                   [d.draft_gap for d in rr], [d.verify_gap for d in rr], TOL_F32)
+    i = next((i for i in range(w.n_tokens) if r.emitted[i] != ref[i]), None)
+    if i is not None:
+        assert _flagged(setup["ref_logits"][i], TOL_F32), f"unflagged divergence from the oracle at {i}"

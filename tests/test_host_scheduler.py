@@ -247,3 +247,36 @@ def test_token_minus_one_stops_the_request_loudly(monkeypatch):
     with pytest.raises(E.NonFiniteLogits):
         for _ in range(10_000):
             eng.step()
+
+
+@pytest.mark.parametrize("fallback_after,plain_rounds", [(2, 3), (1, 1), (4, 6)])
+def test_fallback_to_plain_rounds_follows_the_oracle_policy(monkeypatch, fallback_after, plain_rounds):
+    """With acceptance collapsing (long runs of a = 0), the engine's per-round draft lengths equal
+    those of the oracle's DraftLength fed the same accept counts: plain rounds (x = 0) draft
+    nothing and verify the pending token alone, then drafting is probed again at x_min."""
+    from oracle.decode import DraftLength
+    pattern = lambda idx, rnd, x: 0 if (rnd // 7 + idx) % 3 else min(x, rnd % 5)
+    monkeypatch.setitem(globals(), "accept_count", pattern)
+    eng = make_engine(monkeypatch, n_req=3, x=6, n_tokens=[60, 45, 80], lag=1)
+    guard(monkeypatch, eng)
+    eng.start(adaptive=True, x_min=2, fallback_after=fallback_after, plain_rounds=plain_rounds)
+    while any(r.phase != E.DONE for r in eng.reqs):
+        eng.step()
+    eng.drain()
+    for r in eng.reqs:
+        xs = [x for i, x in eng.m.x_log if i == r.idx]
+        pol = DraftLength(r.x, x_min=2, fallback_after=fallback_after, plain_rounds=plain_rounds)
+        want = []
+        for a in r.accepts:
+            want.append(pol.x)
+            pol.after(a)
+        assert xs == want
+        assert 0 in xs
+        ev = [e for e, i in eng.m.log if i == r.idx]
+        drafts, k = 0, 0
+        for e in ev:
+            if e == "draft":
+                drafts += 1
+            elif e == "verify":
+                assert drafts == xs[k]
+                drafts, k = 0, k + 1

@@ -76,3 +76,32 @@ def test_tiny_workload_full_run():
                               lambda pr: D.draft_cache_tokdrop(pr, W, keep_total=256, keep_recent=64), pre=pre)
     assert out == ref and len(out) == 64
     assert 1 + sum(len(r.emitted) for r in rounds) >= 64      # g0 comes from the prefill
+
+
+def test_draft_length_policy_rules():
+    """Growth on a fully kept round, a + 1 after a rejection, the fall back to
+    plain rounds after consecutive empty rounds, and the probe afterwards."""
+    p = D.DraftLength(8, x_min=2, fallback_after=3, plain_rounds=2)
+    seq = []
+    for a in [8, 3, 4, 0, 0, 0, 0, 0, 1, 2, 0]:
+        seq.append(p.x)
+        p.after(a)
+    # x: 8 -> (kept all) 8 -> (a=3) 4 -> (kept all) 8 -> 2,2,2 (zeros) -> plain 0,0 -> probe 2 ...
+    assert seq == [8, 8, 4, 8, 2, 2, 0, 0, 2, 2, 4]
+    q = D.DraftLength(4, fallback_after=0)
+    for _ in range(10):
+        q.after(0)
+    assert q.x == 1                                     # no fall back when it is off
+
+
+@pytest.mark.parametrize("fallback_after", [0, 1, 2])
+def test_adaptive_and_fallback_stay_lossless(tiny, fallback_after):
+    W, p, pre, ref = tiny
+    pol = D.DraftLength(6, x_min=1, fallback_after=fallback_after, plain_rounds=3)
+    out, rounds = D.vericache(W, p, 30, 6, lambda pr: D.draft_cache_tokdrop(pr, W, keep_total=12, keep_recent=4),
+                              pre=pre, policy=pol)
+    assert out == ref
+    xs = [len(r.draft) for r in rounds]
+    if fallback_after:
+        assert 0 in xs                                  # some rounds decoded plainly
+        assert all(len(r.emitted) == 1 for r in rounds if not r.draft)

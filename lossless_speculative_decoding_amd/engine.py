@@ -121,6 +121,9 @@ class Request:
     n_verified: int = 0                # verifications issued
     rounds: list = field(default_factory=list)  # per-round record (Engine(record=True))
     rec_host: torch.Tensor = None      # pinned [2][x + 1]: this round's rows and verified tokens
+    ready: object = None               # threading.Event: set once the compressed cache is on the device
+                                       # (remote prefix shipping); None: it is there from the start
+    t_first: float = None              # wall time at which the first round's tokens were known
     sampler: object = None             # _vc.Sampler (sampled decoding), else None (greedy)
     probs: torch.Tensor = None         # fp32 [x][vocab]: this round's draft distributions
 
@@ -326,16 +329,17 @@ class Engine:
         # begun: a request still waiting for a fuller draft batch must not hold a slot)
         for r in reqs:
             if (r.phase == DRAFT and r.slot < 0 and r.req.draft_idx >= max(1, r.x_cur - self.lead)
-                    and self.tick >= r.start_tick):
+                    and self.tick >= r.start_tick and self._ready(r)):
                 self._try_stage(r)
         # a request in a plain round (draft length 0) has nothing to draft
         for r in reqs:
-            if r.phase == DRAFT and r.x_cur == 0 and r.budget != 0 and self.tick >= r.start_tick:
+            if r.phase == DRAFT and r.x_cur == 0 and r.budget != 0 and self.tick >= r.start_tick and self._ready(r):
                 r.phase = WAIT_SLOT
         # 3. one batched draft step for every drafting request; requests yet to begin wait for a
         # fuller batch while enough drafted requests are queued for the host link
         ready = [r for r in reqs
-                 if r.phase == DRAFT and r.budget != 0 and self.tick >= r.start_tick and r.req.draft_idx < r.x_cur]
+                 if r.phase == DRAFT and r.budget != 0 and self.tick >= r.start_tick and r.req.draft_idx < r.x_cur
+                 and self._ready(r)]
         active = [r for r in ready if r.req.draft_idx > 0]
         fresh = [r for r in ready if r.req.draft_idx == 0]
         queued = sum(1 for r in reqs if r.phase == WAIT_SLOT)
@@ -367,8 +371,14 @@ class Engine:
         self.tick += 1
         return bool(active)
 
+    @staticmethod
+    def _ready(r: Request) -> bool:
+        return r.ready is None or r.ready.is_set()
+
     def _finish_accept(self, r: Request):
         a = int(r.result_host[0])
+        if r.t_first is None:
+            r.t_first = time.perf_counter()
         if self.record:
             n = r.x_cur + 1
             rows, ver = r.rec_host[0, :n].tolist(), r.rec_host[1, :n].tolist()
@@ -460,7 +470,8 @@ class Engine:
                 r.budget = -1
         t0 = t_last = time.perf_counter()
         while any(r.phase != DONE for r in self.reqs):
-            self.step()
+            if not self.step() and any(not self._ready(r) for r in self.reqs):
+                time.sleep(0.0005)  # waiting on a cache in flight: leave the interpreter to the link's thread
             if progress is not None and time.perf_counter() - t_last >= every:
                 t_last = time.perf_counter()
                 progress(sum(min(len(r.emitted), r.n_tokens) for r in self.reqs), t_last - t0)

@@ -17,6 +17,7 @@ namespace vc {
 
 constexpr int ATT_KT = 64;   // keys per tile
 constexpr int ATT_RB = 64;   // query rows (row x GQA head) of one 16-row block in each of a workgroup's 4 waves
+constexpr int ATT_MB = 16;   // query rows of one MFMA row block
 
 struct KVSeg {
   const void* k;

@@ -94,17 +94,6 @@ __device__ __forceinline__ TileMix tile_mix(const AttnReq& R, int j, int t0) {
   return x;
 }
 
-__device__ __forceinline__ const uint16_t* mixed_row(const AttnReq& R, int j, int t0, int o, const TileMix& x,
-                                                     bool is_v) {
-  // lanes of one load take rows from both buffers: select the address (no divergent branch)
-  const int below = __popcll(x.m & ((uint64_t(1) << o) - 1));
-  const bool kept = (x.m >> o) & 1;
-  const uint16_t* kb = static_cast<const uint16_t*>(is_v ? R.mix.v : R.mix.k) + j * R.mix.hstride;
-  const uint16_t* sb = static_cast<const uint16_t*>(is_v ? R.a.v : R.a.k) + j * R.a.hstride;
-  const int row = kept ? x.c + below : t0 - x.c + o - below;
-  return (kept ? kb : sb) + int64_t(row) * D128;
-}
-
 // K: thread (kr = tid/16, ch = tid%16) loads 16-byte chunk ch of keys kr + 16e (e = 0..3):
 //    sixteen consecutive lanes move one whole 256-byte row (coalesced in HBM, and their LDS
 //    stores cover all banks once).
@@ -123,12 +112,28 @@ __device__ __forceinline__ void load_tile_bf16(TileRegs& r, const AttnReq& R, in
     return;
   }
   if (mix.valid) {  // uniform: every row in the kept / staged mix of segment a
+    // lane o of each wave locates key t0 + o (one popcount); each thread then takes the rows of
+    // its eight loads from the lanes that located them (the top bit marks a kept row)
+    const int o = tid & 63;
+    const int below = __popcll(mix.m & ((uint64_t(1) << o) - 1));
+    const bool kept = (mix.m >> o) & 1;
+    const uint32_t handle = kept ? (uint32_t(mix.c + below) | 0x80000000u) : uint32_t(t0 - mix.c + o - below);
+    const uint16_t* kk = static_cast<const uint16_t*>(R.mix.k) + j * R.mix.hstride;
+    const uint16_t* sk = static_cast<const uint16_t*>(R.a.k) + j * R.a.hstride;
+    const uint16_t* kv = static_cast<const uint16_t*>(R.mix.v) + j * R.mix.hstride;
+    const uint16_t* sv = static_cast<const uint16_t*>(R.a.v) + j * R.a.hstride;
 #pragma unroll
-    for (int e = 0; e < 4; e++)
-      r.k[e] = *reinterpret_cast<const u32x4*>(mixed_row(R, j, t0, kr + 16 * e, mix, false) + 8 * ch);
+    for (int e = 0; e < 4; e++) {
+      const uint32_t h = uint32_t(__shfl(int(handle), kr + 16 * e, 64));
+      const uint16_t* base = (h & 0x80000000u) ? kk : sk;
+      r.k[e] = *reinterpret_cast<const u32x4*>(base + int64_t(h & 0x7fffffffu) * D128 + 8 * ch);
+    }
 #pragma unroll
-    for (int e = 0; e < 4; e++)
-      r.v[e] = *reinterpret_cast<const u32x4*>(mixed_row(R, j, t0, 4 * kg + e, mix, true) + 8 * dc);
+    for (int e = 0; e < 4; e++) {
+      const uint32_t h = uint32_t(__shfl(int(handle), 4 * kg + e, 64));
+      const uint16_t* base = (h & 0x80000000u) ? kv : sv;
+      r.v[e] = *reinterpret_cast<const u32x4*>(base + int64_t(h & 0x7fffffffu) * D128 + 8 * dc);
+    }
     return;
   }
 #pragma unroll
@@ -166,16 +171,25 @@ __device__ __forceinline__ void store_tile_bf16(const TileRegs& r, uint16_t* Ks,
 }
 
 // Rows kernel (verification, prefill, observation scores): workgroup = 4 waves =
-// (request, KV head, group of up to 64 * RPW query rows, split); wave w owns the 16-row
-// blocks w, w + 4, ... (RPW of them), so every K/V tile staged in LDS serves all the
-// rows of the group: a 33-row verification of 4 GQA heads (132 query rows) reads the
-// keys once.  Each row's arithmetic is the same whatever block or group holds it.
-template <int RPW>
+// (request, KV head, group of query rows, split).  A group holds up to 4 RPW "own" row blocks
+// of 16 rows -- wave w keeps the state of blocks w and w + 4 in registers -- followed by up to
+// JMAX "shared" blocks that the four waves compute together: for the block's scores wave w takes
+// keys 16w .. 16w + 15 of each tile, the waves exchange the scores through LDS, each then runs
+// the block's online softmax on the whole tile (all four identically) and accumulates the
+// output channels 32w .. 32w + 31.  A 33-row verification of 4 GQA heads (132 rows) is eight
+// own blocks and one shared block, so the four waves issue the same MFMA work; every K/V tile
+// staged in LDS serves all the rows of the group.  A row's arithmetic is the same whichever
+// kind of block or group holds it: the same MFMAs in the same order for its scores and for
+// each output channel, the same softmax sequence.
+template <int RPW, int JMAX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_rows_bf16_kernel(
     const AttnArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[ATT_KT * KS_PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D128 * VT_PITCH];
-  constexpr int GROUP_ROWS = ATT_RB * RPW;
+  __shared__ __attribute__((aligned(16))) uint16_t Qj[JMAX > 0 ? JMAX * ATT_MB * KS_PITCH : 1];  // shared blocks' queries
+  __shared__ __attribute__((aligned(16))) f32x4 Sx[JMAX > 0 ? JMAX * 4 * 64 : 1];  // [block][16-key slice][lane]
+  constexpr int OWN_ROWS = ATT_RB * RPW;
+  constexpr int GROUP_ROWS = OWN_ROWS + ATT_MB * JMAX;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int z = blockIdx.z;
   if (z >= args.n_req) return;
@@ -192,13 +206,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int i_max = (min(qr0 + GROUP_ROWS, n_qrows) - 1) / G;
   const int key_hi = min(min(key_lo + args.split_len, n_keys), R.lim0 + i_max + 1);
   const int grp = lane >> 4;
+  // shared blocks in use (uniform): those holding at least one row
+  const int nj = JMAX > 0 ? min(JMAX, max(0, (n_qrows - (qr0 + OWN_ROWS) + ATT_MB - 1) / ATT_MB)) : 0;
 
-  // per row block b of this wave: the lane's query row qr0 + 16 (wave + 4b) + lane % 16 (query
-  // qr / G, head j G + qr % G), its query fragments and softmax state; the row indices are
-  // recomputed where needed rather than held in registers
-  const int qr_lane = qr0 + 16 * wave + (lane & 15);
-  auto blk_on = [&](int b) { return qr0 + 16 * (wave + 4 * b) < n_qrows; };  // uniform per wave
-  int n_act = 0;  // active blocks 0 .. n_act - 1 of this wave
+  auto q_row = [&](int qr) -> const uint16_t* {  // query row qr (row qr / G, head j G + qr % G)
+    const int qi = qr / G, hq = j * G + qr % G;
+    return static_cast<const uint16_t*>(R.q) + (int64_t(qi) * Hq + hq) * D128;
+  };
+
+  // per own row block b of this wave: the lane's query row qr0 + 16 (wave + 4b) + lane % 16, its
+  // query fragments and softmax state; the row indices are recomputed where needed
+  const int qr_lane = qr0 + ATT_MB * wave + (lane & 15);
+  auto blk_on = [&](int b) { return qr0 + ATT_MB * (wave + 4 * b) < n_qrows; };  // uniform per wave
+  int n_act = 0;  // active own blocks 0 .. n_act - 1 of this wave
 #pragma unroll
   for (int b = 0; b < RPW; b++) n_act += blk_on(b) ? 1 : 0;
   u32x4 qf[RPW][4];
@@ -206,10 +226,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run[RPW], l_run[RPW];
 #pragma unroll
   for (int b = 0; b < RPW; b++) {
-    const int qr = qr_lane + 64 * b;
+    const int qr = qr_lane + ATT_RB * b;
     const bool row_ok = qr < n_qrows;
-    const int qi = row_ok ? qr / G : 0, hq = j * G + (row_ok ? qr % G : 0);
-    const uint16_t* qp = static_cast<const uint16_t*>(R.q) + (int64_t(qi) * Hq + hq) * D128;
+    const uint16_t* qp = q_row(row_ok ? qr : 0);
 #pragma unroll
     for (int c = 0; c < 4; c++)
       qf[b][c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * grp) : u32x4{0, 0, 0, 0};
@@ -218,11 +237,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     m_run[b] = NEG_INF;
     l_run[b] = 0.f;
   }
+  // shared blocks: queries into LDS (thread = one 16-byte chunk of one row), and per block this
+  // wave's two output channel tiles and the block's softmax state (the same in every wave)
+  f32x4 oj[JMAX > 0 ? JMAX : 1][2];
+  float mj[JMAX > 0 ? JMAX : 1], lj[JMAX > 0 ? JMAX : 1];
+#pragma unroll
+  for (int jb = 0; jb < JMAX; jb++) {
+    if (jb < nj) {
+      const int r = tid >> 4, ch = tid & 15;
+      const int qr = qr0 + OWN_ROWS + ATT_MB * jb + r;
+      *reinterpret_cast<u32x4*>(Qj + (jb * ATT_MB + r) * KS_PITCH + 8 * ch) =
+          qr < n_qrows ? *reinterpret_cast<const u32x4*>(q_row(qr) + 8 * ch) : u32x4{0, 0, 0, 0};
+    }
+    oj[jb][0] = oj[jb][1] = f32x4{0, 0, 0, 0};
+    mj[jb] = NEG_INF;
+    lj[jb] = 0.f;
+  }
   const float sl2 = args.scale_log2;
 
   // a tile at or below lim_all is visible to every row of the group (and holds no key past
   // the last); padding rows (past n_qrows) compute on zero queries and are never written
   const int lim_all = min(R.lim0 + qr0 / G, n_keys - 1);
+
+  // Online softmax of one block's 64-key tile held in the MFMA output layout (row qr = the lane's
+  // row, keys 16kt + 4 grp + jj): masks, the running max and sum, and P' = 2^10 p in place.
+  // Scores stay unscaled until the exponent: p' = 2^(s * scale_log2 - m + 10) in one fma per key,
+  // m and the running sum in the scaled domain (the 2^10 is removed when the partial is written).
+  // Returns the factor the block's accumulators take.
+  auto softmax = [&](f32x4 (&sa)[4], float& m_run_, float& l_run_, int qr, int t0, bool full) -> float {
+    float mx = NEG_INF;
+    if (full) {
+#pragma unroll
+      for (int kt = 0; kt < 4; kt++) mx = fmaxf(mx, fmaxf(fmaxf(sa[kt][0], sa[kt][1]), fmaxf(sa[kt][2], sa[kt][3])));
+    } else {
+      const int lim = qr < n_qrows ? min(R.lim0 + qr / G, n_keys - 1) : -1;
+#pragma unroll
+      for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int t = t0 + 16 * kt + 4 * grp + jj;
+          const bool vis = t <= lim;
+          sa[kt][jj] = vis ? sa[kt][jj] : NEG_INF;
+          mx = fmaxf(mx, sa[kt][jj]);
+        }
+      }
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run_, mx * sl2);
+    // no visible key yet (masked tiles only): nothing to add, state unchanged
+    const bool none = !full && m_new == NEG_INF;
+    const float nb = none ? 0.f : P_LOG2 - m_new;
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run_ - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sa[kt][jj], sl2, nb));
+        sa[kt][jj] = p;
+        rs += p;
+      }
+    }
+    rs += shfl_xor(rs, 16);
+    rs += shfl_xor(rs, 32);
+    l_run_ = l_run_ * alpha + rs;
+    m_run_ = m_new;
+    return alpha;
+  };
+  // P' of 32 keys (chunk kc of the tile) as fp16 hi / lo MFMA B fragments
+  auto p_frags = [&](const f32x4 (&sa)[4], int kc, u32x4& pb, u32x4& pl) {
+    uint32_t h[4], lw[4];
+    split_h2(sa[2 * kc][0], sa[2 * kc][1], h[0], lw[0]);
+    split_h2(sa[2 * kc][2], sa[2 * kc][3], h[1], lw[1]);
+    split_h2(sa[2 * kc + 1][0], sa[2 * kc + 1][1], h[2], lw[2]);
+    split_h2(sa[2 * kc + 1][2], sa[2 * kc + 1][3], h[3], lw[3]);
+    pb = u32x4{h[0], h[1], h[2], h[3]};
+    pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
+  };
 
   TileRegs regs;
   TileMix mix_next = tile_mix(R, j, key_lo + ATT_KT);
@@ -237,7 +329,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const bool full = t0 + ATT_KT - 1 <= lim_all;  // uniform
 
-    // Row blocks [B0, B0 + NB) of this wave (NB <= 2): each K and V^T fragment read from LDS
+    // Own row blocks [B0, B0 + NB) of this wave (NB <= 2): each K and V^T fragment read from LDS
     // feeds the MFMAs of all NB blocks.  Per block, the MFMA sequence and the softmax arithmetic
     // are the same whichever blocks share the pass.
     auto blocks = [&](auto b0v, auto nbv) {
@@ -257,51 +349,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int b = 0; b < NB; b++) sacc[b][kt] = mfma_bf16(ka, qf[B0 + b][c], sacc[b][kt]);
         }
       }
-      // ---- mask, online softmax (row q = lane % 16).  Scores stay unscaled until the
-      // exponent: p' = 2^(s * scale_log2 - m + 10) = 2^10 p in one fma per key, m and the
-      // running sum in the scaled domain (the 2^10 is removed when the partial is written)
 #pragma unroll
       for (int b = 0; b < NB; b++) {
-        float mx = NEG_INF;
-        if (full) {
-#pragma unroll
-          for (int kt = 0; kt < 4; kt++)
-            mx = fmaxf(mx, fmaxf(fmaxf(sacc[b][kt][0], sacc[b][kt][1]), fmaxf(sacc[b][kt][2], sacc[b][kt][3])));
-        } else {
-          const int qr = qr_lane + 64 * (B0 + b);
-          const int lim = qr < n_qrows ? min(R.lim0 + qr / G, n_keys - 1) : -1;
-#pragma unroll
-          for (int kt = 0; kt < 4; kt++) {
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              const int t = t0 + 16 * kt + 4 * grp + jj;
-              const bool vis = t <= lim;
-              sacc[b][kt][jj] = vis ? sacc[b][kt][jj] : NEG_INF;
-              mx = fmaxf(mx, sacc[b][kt][jj]);
-            }
-          }
-        }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[B0 + b], mx * sl2);
-        // no visible key yet (masked tiles only): nothing to add, state unchanged
-        const bool none = !full && m_new == NEG_INF;
-        const float nb = none ? 0.f : P_LOG2 - m_new;
-        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[B0 + b] - m_new);
-        float rs = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; kt++) {
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][kt][jj], sl2, nb));
-            sacc[b][kt][jj] = p;
-            rs += p;
-          }
-        }
-        rs += shfl_xor(rs, 16);
-        rs += shfl_xor(rs, 32);
-        l_run[B0 + b] = l_run[B0 + b] * alpha + rs;
-        m_run[B0 + b] = m_new;
+        const float alpha = softmax(sacc[b], m_run[B0 + b], l_run[B0 + b], qr_lane + ATT_RB * (B0 + b), t0, full);
         if (__any(alpha != 1.f)) {  // x * 1 == x: skip the rescale when no running max moved
 #pragma unroll
           for (int dt = 0; dt < 8; dt++) oacc[B0 + b][dt] *= alpha;
@@ -312,15 +362,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int kc = 0; kc < 2; kc++) {
         u32x4 pb[NB], pl[NB];
 #pragma unroll
-        for (int b = 0; b < NB; b++) {
-          uint32_t h[4], lw[4];
-          split_h2(sacc[b][2 * kc][0], sacc[b][2 * kc][1], h[0], lw[0]);
-          split_h2(sacc[b][2 * kc][2], sacc[b][2 * kc][3], h[1], lw[1]);
-          split_h2(sacc[b][2 * kc + 1][0], sacc[b][2 * kc + 1][1], h[2], lw[2]);
-          split_h2(sacc[b][2 * kc + 1][2], sacc[b][2 * kc + 1][3], h[3], lw[3]);
-          pb[b] = u32x4{h[0], h[1], h[2], h[3]};
-          pl[b] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-        }
+        for (int b = 0; b < NB; b++) p_frags(sacc[b], kc, pb[b], pl[b]);
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
           const u32x4 va = *reinterpret_cast<const u32x4*>(Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 8 * grp);
@@ -335,20 +377,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    if (n_act >= 2) blocks(I0{}, I2{});
-    else if (n_act == 1) blocks(I0{}, I1{});
-    if constexpr (RPW == 3) {
-      if (n_act == 3) blocks(I2{}, I1{});
+    if constexpr (RPW >= 2) {
+      if (n_act >= 2) blocks(I0{}, I2{});
+      else if (n_act == 1) blocks(I0{}, I1{});
+    } else {
+      if (n_act == 1) blocks(I0{}, I1{});
+    }
+
+    // ---- shared blocks, scores (after the own blocks, whose registers are then free): this
+    // wave's 16 keys (sub-tile kt = wave), the same MFMAs an own block runs for that sub-tile,
+    // out to LDS
+#pragma unroll
+    for (int jb = 0; jb < JMAX; jb++) {
+      if (jb < nj) {
+        f32x4 sj = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (16 * wave + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
+          const u32x4 qb = *reinterpret_cast<const u32x4*>(Qj + (jb * ATT_MB + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
+          sj = mfma_bf16(ka, qb, sj);
+        }
+        Sx[(jb * 4 + wave) * 64 + lane] = sj;
+      }
+    }
+
+    // ---- shared blocks: the whole tile's scores from the four waves, softmax, this wave's
+    // output channel tiles 2 wave and 2 wave + 1
+    if (nj > 0) {  // uniform
+      __syncthreads();
+#pragma unroll
+      for (int jb = 0; jb < JMAX; jb++) {
+        if (jb < nj) {
+          f32x4 sa[4];
+#pragma unroll
+          for (int kt = 0; kt < 4; kt++) sa[kt] = Sx[(jb * 4 + kt) * 64 + lane];
+          const float alpha = softmax(sa, mj[jb], lj[jb], qr0 + OWN_ROWS + ATT_MB * jb + (lane & 15), t0, full);
+          if (__any(alpha != 1.f)) {
+            oj[jb][0] *= alpha;
+            oj[jb][1] *= alpha;
+          }
+#pragma unroll
+          for (int kc = 0; kc < 2; kc++) {
+            u32x4 pb, pl;
+            p_frags(sa, kc, pb, pl);
+#pragma unroll
+            for (int dd = 0; dd < 2; dd++) {
+              const int dt = 2 * wave + dd;
+              const u32x4 va = *reinterpret_cast<const u32x4*>(Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 8 * grp);
+              oj[jb][dd] = mfma_f16(va, pb, oj[jb][dd]);
+              oj[jb][dd] = mfma_f16(va, pl, oj[jb][dd]);
+            }
+          }
+        }
+      }
     }
   }
 
-  // ---- partial (m, l, o) of this lane's rows; lane holds o[16dt + 4g + jj]
+  // ---- partials (m, l, o): own blocks, lane holds o[16dt + 4g + jj]
+  auto part_of = [&](int qr) -> float* {
+    const int qi = qr / G, hq = j * G + qr % G;
+    return R.part + ((int64_t(qi) * Hq + hq) * R.s_total + (R.s_off + s)) * (D128 + 2);
+  };
 #pragma unroll
   for (int b = 0; b < RPW; b++) {
-    const int qr = qr_lane + 64 * b;
+    const int qr = qr_lane + ATT_RB * b;
     if (!blk_on(b) || qr >= n_qrows) continue;
-    const int qi = qr / G, hq = j * G + qr % G;
-    float* dst = R.part + ((int64_t(qi) * Hq + hq) * R.s_total + (R.s_off + s)) * (D128 + 2);
+    float* dst = part_of(qr);
     if (grp == 0) {
       dst[0] = m_run[b];
       dst[1] = l_run[b] * P_UNSCALE;
@@ -357,6 +451,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int dt = 0; dt < 8; dt++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) dst[2 + 16 * dt + 4 * grp + jj] = oacc[b][dt][jj] * P_UNSCALE;
+    }
+  }
+  // shared blocks: each wave its two channel tiles, wave 0 the row's (m, l)
+#pragma unroll
+  for (int jb = 0; jb < JMAX; jb++) {
+    const int qr = qr0 + OWN_ROWS + ATT_MB * jb + (lane & 15);
+    if (jb >= nj || qr >= n_qrows) continue;
+    float* dst = part_of(qr);
+    if (wave == 0 && grp == 0) {
+      dst[0] = mj[jb];
+      dst[1] = lj[jb] * P_UNSCALE;
+    }
+#pragma unroll
+    for (int dd = 0; dd < 2; dd++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) dst[2 + 16 * (2 * wave + dd) + 4 * grp + jj] = oj[jb][dd][jj] * P_UNSCALE;
     }
   }
 }
@@ -452,13 +562,19 @@ vc_status launch_attn(const AttnArgs& a, int dtype, hipStream_t s, hipEvent_t ev
   }
   if (dtype == VC_BF16) {
     VC_REQUIRE(a.head_dim == 128, VC_ERR_UNSUPPORTED, "bf16 attention needs head_dim 128 (got %d)", a.head_dim);
-    // row blocks per wave: enough for the largest request up to 3 (a 192-row group)
-    const int rpw = max(1, min(3, int(cdiv(max_qrows, ATT_RB))));
-    const int n_groups = int(cdiv(max_qrows, ATT_RB * rpw));
-    dim3 grid(a.Hkv * n_groups, a.max_splits, a.n_req);
-    if (rpw == 1) hipExtLaunchKernelGGL(attn_rows_bf16_kernel<1>, grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
-    else if (rpw == 2) hipExtLaunchKernelGGL(attn_rows_bf16_kernel<2>, grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
-    else hipExtLaunchKernelGGL(attn_rows_bf16_kernel<3>, grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
+    // row groups: up to 64 rows (one own block per wave); up to 144 (two own blocks per wave and
+    // one shared block: a verification of up to 36 rows of 4 GQA heads in one group); beyond,
+    // 128-row groups (prefill)
+    if (max_qrows <= ATT_RB) {
+      dim3 grid(a.Hkv, a.max_splits, a.n_req);
+      hipExtLaunchKernelGGL((attn_rows_bf16_kernel<1, 0>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
+    } else if (max_qrows <= 2 * ATT_RB + ATT_MB) {
+      dim3 grid(a.Hkv, a.max_splits, a.n_req);
+      hipExtLaunchKernelGGL((attn_rows_bf16_kernel<2, 1>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
+    } else {
+      dim3 grid(a.Hkv * int(cdiv(max_qrows, 2 * ATT_RB)), a.max_splits, a.n_req);
+      hipExtLaunchKernelGGL((attn_rows_bf16_kernel<2, 0>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, a);
+    }
   } else {
     VC_REQUIRE(a.head_dim == 64, VC_ERR_UNSUPPORTED, "fp32 attention needs head_dim 64 (got %d)", a.head_dim);
     dim3 grid(a.Hkv * max_qrows, a.max_splits, a.n_req);

@@ -65,12 +65,17 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
 }
-// two floats -> fp16 hi pair and fp16 lo pair with a ~= hi + lo (about 22 significant bits)
+// two floats -> fp16 hi pair and fp16 lo pair with a ~= hi + lo (about 22 significant bits).
+// a - hi is exact in fp32 (hi is a rounded to fp16), so it is taken in one mixed-precision fma
+// per value straight from the packed hi word (v_fma_mix_f32: fp16 source half, fp32 rest)
+// instead of converting hi back first.  The results feed a conversion, not an MFMA.
 __device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_t& lo) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-  hi = __builtin_bit_cast(uint32_t, h2{ha, hb});
-  lo = __builtin_bit_cast(uint32_t, h2{(_Float16)(a - float(ha)), (_Float16)(b - float(hb))});
+  hi = __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+  float ra, rb;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(hi), "v"(a));
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(hi), "v"(b));
+  lo = __builtin_bit_cast(uint32_t, h2{(_Float16)ra, (_Float16)rb});
 }
 
 template <typename T>

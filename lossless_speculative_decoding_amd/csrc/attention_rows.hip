@@ -106,9 +106,9 @@ __device__ __forceinline__ void load_tile_bf16(TileRegs& r, const AttnReq& R, in
   const uint16_t* vb;
   if (tile_plain(R, j, t0, n_keys, kb, vb)) {  // uniform across the workgroup
 #pragma unroll
-    for (int e = 0; e < 4; e++) r.k[e] = *reinterpret_cast<const u32x4*>(kb + (kr + 16 * e) * D128 + 8 * ch);
+    for (int e = 0; e < 4; e++) r.k[e] = ld_nt(kb + (kr + 16 * e) * D128 + 8 * ch);
 #pragma unroll
-    for (int e = 0; e < 4; e++) r.v[e] = *reinterpret_cast<const u32x4*>(vb + (4 * kg + e) * D128 + 8 * dc);
+    for (int e = 0; e < 4; e++) r.v[e] = ld_nt(vb + (4 * kg + e) * D128 + 8 * dc);
     return;
   }
   if (mix.valid) {  // uniform: every row in the kept / staged mix of segment a
@@ -126,13 +126,13 @@ __device__ __forceinline__ void load_tile_bf16(TileRegs& r, const AttnReq& R, in
     for (int e = 0; e < 4; e++) {
       const uint32_t h = uint32_t(__shfl(int(handle), kr + 16 * e, 64));
       const uint16_t* base = (h & 0x80000000u) ? kk : sk;
-      r.k[e] = *reinterpret_cast<const u32x4*>(base + int64_t(h & 0x7fffffffu) * D128 + 8 * ch);
+      r.k[e] = ld_nt(base + int64_t(h & 0x7fffffffu) * D128 + 8 * ch);
     }
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       const uint32_t h = uint32_t(__shfl(int(handle), 4 * kg + e, 64));
       const uint16_t* base = (h & 0x80000000u) ? kv : sv;
-      r.v[e] = *reinterpret_cast<const u32x4*>(base + int64_t(h & 0x7fffffffu) * D128 + 8 * dc);
+      r.v[e] = ld_nt(base + int64_t(h & 0x7fffffffu) * D128 + 8 * dc);
     }
     return;
   }

@@ -26,11 +26,13 @@ Readings where the pages are silent:
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from .compress import Quantized, tokdrop, tokdrop_keynorm
 from .kvcache import FixedRows, RowStore, chain
-from .model import Weights, argmax, row_forward
+from .model import Weights, argmax, head_forward, rmsnorm, rope, row_forward, silu, storage_round
 
 
 def accept(draft, verified):
@@ -73,6 +75,44 @@ def prefill(W: Weights, prompt, obs_window: int = 32) -> Prefill:
         if p >= T - wn:
             q_obs[:, :, p - (T - wn)] = out.q
     return Prefill(full, argmax(out.logits), q_obs, out.logits)
+
+
+def prefill_matrix(W: Weights, prompt, obs_window: int = 32) -> Prefill:
+    """prefill() in matrix form: each layer over all prompt rows at once (causal mask), with the
+    rounding points of layer_forward, for long prompts at large widths.  The stored values equal
+    the row-at-a-time prefill's up to float64 summation order (pinned against it)."""
+    s = W.shape
+    R = storage_round(W.dtype)
+    L, Hq, Hkv, D, G = s.n_layers, s.n_q_heads, s.n_kv_heads, s.head_dim, s.group
+    toks = np.asarray(prompt, dtype=np.int64)
+    n = len(toks)
+    wn = min(obs_window, n)
+    full = RowStore(L, Hkv, D, max(n, 1))
+    q_obs = np.zeros((L, Hq, wn, D))
+    mask = np.tril(np.ones((n, n), dtype=bool))
+    H = R(W.E[toks])
+    for l in range(L):
+        A = R(rmsnorm(H, W.g1[l], s.eps))
+        Q = R(np.stack([rope(q, p, s.rope_theta) for p, q in enumerate((A @ W.Wq[l].T).reshape(n, Hq, D))]))
+        K = R(np.stack([rope(k, p, s.rope_theta) for p, k in enumerate((A @ W.Wk[l].T).reshape(n, Hkv, D))]))
+        V = R((A @ W.Wv[l].T).reshape(n, Hkv, D))
+        O = np.empty((n, Hq, D))
+        for hq in range(Hq):
+            j = hq // G
+            S = np.where(mask, (Q[:, hq] @ K[:, j].T) / math.sqrt(D), -np.inf)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            O[:, hq] = (P / P.sum(axis=1, keepdims=True)) @ V[:, j]
+        O = R(O)
+        H = R(H + O.reshape(n, -1) @ W.Wo[l].T)
+        F = R(rmsnorm(H, W.g2[l], s.eps))
+        M = R(silu(F @ W.W1[l].T) * (F @ W.W3[l].T))
+        H = R(H + M @ W.W2[l].T)
+        full.K[l, :, :n] = K.transpose(1, 0, 2)
+        full.V[l, :, :n] = V.transpose(1, 0, 2)
+        q_obs[l] = Q[n - wn:].transpose(1, 0, 2)
+    full.n = n
+    last = head_forward(W, H[-1])
+    return Prefill(full, argmax(last), q_obs, last)
 
 
 def greedy(W: Weights, prompt, n_tokens: int, pre: Prefill | None = None, force=None):

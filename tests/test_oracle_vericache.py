@@ -105,3 +105,17 @@ def test_adaptive_and_fallback_stay_lossless(tiny, fallback_after):
     if fallback_after:
         assert 0 in xs                                  # some rounds decoded plainly
         assert all(len(r.emitted) == 1 for r in rounds if not r.draft)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_matrix_prefill_equals_row_prefill(dtype):
+    """The matrix-form prefill stores the same K/V, observation queries, last logits and first
+    token as the row-at-a-time prefill (only the float64 summation order differs)."""
+    W = Weights(TINY, dtype=dtype)
+    p = synth.prompt(4, 40, TINY.vocab)
+    a, b = D.prefill(W, p, obs_window=8), D.prefill_matrix(W, p, obs_window=8)
+    assert a.full.n == b.full.n == 40 and a.g0 == b.g0
+    for x, y in ((a.full.K[:, :, :40], b.full.K[:, :, :40]), (a.full.V[:, :, :40], b.full.V[:, :, :40]),
+                 (a.q_obs, b.q_obs)):
+        assert np.allclose(x, y, rtol=1e-6, atol=0)
+    assert np.allclose(a.last_logits, b.last_logits, rtol=1e-9, atol=1e-12)

@@ -207,6 +207,88 @@ __global__ __launch_bounds__(256) void tokdrop_scores_kernel(const void* k, cons
   }
 }
 
+// The same scores for bf16 caches with head_dim 128, on MFMAs.  Workgroup = 4 waves =
+// (layer*head, 256 candidates); wave w takes candidates 64w .. 64w + 63 of the chunk as four
+// 16-key sub-tiles.  Per 16-row block of the observation rows (staged in LDS, 128 at a time)
+// S = Q K^T runs as 16x16x32 bf16 MFMAs: A = Q rows from LDS, B = K^T fragments held in
+// registers for the whole kernel (lane l: candidate l % 16 of each sub-tile, channels
+// 8 (l / 16) .. + 8 of each 32-channel chunk), read straight from HBM once.  Lane l then holds
+// the scores of rows 4 (l / 16) + jj of the block for its candidate; it adds
+// 2^(s sl2 - M_row) / L_row over its rows (1 / L_row taken once per row), and the four lane
+// groups are added in fixed order.
+constexpr int SC_ROWS = 128;            // observation rows staged per pass
+constexpr int SC_PITCH = 128 + 8;       // bf16 per staged row (pad breaks bank aliasing)
+
+__global__ __launch_bounds__(256) void tokdrop_scores_bf16_kernel(const uint16_t* k, const uint16_t* q_obs,
+                                                                  const float* ml, int src_cap, int Hq, int Hkv,
+                                                                  int W, int n_cand, float sl2, float* scores) {
+  __shared__ __attribute__((aligned(16))) uint16_t qs[SC_ROWS * SC_PITCH];
+  __shared__ float2 mls[SC_ROWS];  // (-M, 1 / L) per staged row
+  constexpr int D = 128;
+  const int G = Hq / Hkv;
+  const int lh = blockIdx.y;
+  const int l = lh / Hkv, j = lh % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g = lane >> 4;
+  const int n_q = G * W;
+  const int t_base = blockIdx.x * 256 + 64 * wave;
+  u32x4 kf[4][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; kt++) {
+    const int t = t_base + 16 * kt + r16;
+    const uint16_t* kp = k + (int64_t(lh) * src_cap + (t < n_cand ? t : 0)) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < 4; c++) kf[kt][c] = t < n_cand ? ld_nt(kp + 32 * c) : u32x4{0, 0, 0, 0};
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < n_q; r0 += SC_ROWS) {
+    const int nr = min(SC_ROWS, n_q - r0);
+    __syncthreads();
+    for (int e = tid; e < SC_ROWS * 16; e += 256) {
+      const int rr = e >> 4, ch = e & 15;
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (rr < nr) {
+        const int r = r0 + rr, h = r / W, w = r % W;
+        x = *reinterpret_cast<const u32x4*>(q_obs + ((int64_t(l) * W + w) * Hq + j * G + h) * D + 8 * ch);
+      }
+      *reinterpret_cast<u32x4*>(qs + rr * SC_PITCH + 8 * ch) = x;
+    }
+    for (int rr = tid; rr < SC_ROWS; rr += 256) {
+      float2 m = float2{NEG_INF, 0.f};  // padding rows add exp2(-inf) * 0 = 0
+      if (rr < nr) {
+        const int r = r0 + rr, h = r / W, w = r % W;
+        const int64_t mi = ((int64_t(l) * W + w) * Hq + j * G + h) * 2;
+        m = float2{-ml[mi], 1.f / ml[mi + 1]};
+      }
+      mls[rr] = m;
+    }
+    __syncthreads();
+    const int nb = (nr + 15) >> 4;
+    for (int rb = 0; rb < nb; rb++) {
+      u32x4 qa[4];
+#pragma unroll
+      for (int c = 0; c < 4; c++) qa[c] = *reinterpret_cast<const u32x4*>(qs + (16 * rb + r16) * SC_PITCH + 32 * c + 8 * g);
+      float2 m[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) m[jj] = mls[16 * rb + 4 * g + jj];
+#pragma unroll
+      for (int kt = 0; kt < 4; kt++) {
+        f32x4 sv = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < 4; c++) sv = mfma_bf16(qa[c], kf[kt][c], sv);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) acc[kt] += __builtin_amdgcn_exp2f(fmaf(sv[jj], sl2, m[jj].x)) * m[jj].y;
+      }
+    }
+  }
+#pragma unroll
+  for (int kt = 0; kt < 4; kt++) {
+    acc[kt] += shfl_xor(acc[kt], 16);
+    acc[kt] += shfl_xor(acc[kt], 32);
+    const int t = t_base + 16 * kt + r16;
+    if (g == 0 && t < n_cand) scores[int64_t(lh) * n_cand + t] = acc[kt] / float(n_q);
+  }
+}
+
 // Deterministic top-k per (layer*head): radix select on the float bits (scores are >= 0, so the
 // unsigned bit pattern orders them), ties resolved towards the smaller index; output ascending.
 constexpr int SEL_THREADS = 1024;
@@ -587,8 +669,14 @@ vc_status compress_run(const vc_compress_desc* d, const void* k, const void* v, 
       VC_LAUNCH_CHECK();
     }
     // pass 2: scores of the candidates
-    hipLaunchKernelGGL(tokdrop_scores_kernel, dim3(cdiv(n_cand, 64), n_lh), dim3(256), 0, s, k, q_obs, ml, d->dtype,
-                       d->src_cap, D, d->n_q_heads, d->n_kv_heads, W, n_cand, sl2, scores);
+    if (d->dtype == VC_BF16 && D == 128) {
+      hipLaunchKernelGGL(tokdrop_scores_bf16_kernel, dim3(cdiv(n_cand, 256), n_lh), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(q_obs), ml, d->src_cap,
+                         d->n_q_heads, d->n_kv_heads, W, n_cand, sl2, scores);
+    } else {
+      hipLaunchKernelGGL(tokdrop_scores_kernel, dim3(cdiv(n_cand, 64), n_lh), dim3(256), 0, s, k, q_obs, ml, d->dtype,
+                         d->src_cap, D, d->n_q_heads, d->n_kv_heads, W, n_cand, sl2, scores);
+    }
     VC_LAUNCH_CHECK();
     hipLaunchKernelGGL(topk_select_kernel, dim3(n_lh), dim3(SEL_THREADS), 0, s, scores, n_cand, n_top, n_recent, kk,
                        idx);

@@ -378,9 +378,11 @@ vc_status vc_spec_sample(int32_t vocab, const float* logits_t, const float* prob
  * Attention cores of one layer (the single-layer workload and tests).
  * Query rows are [rows][Hq][D] bf16 (post-RoPE); outputs [rows][Hq][D] in out_dtype.
  *
- * Value range (every bf16 attention path, draft and verification, and so the
- * model calls built on them): P.V runs on fp16 MFMAs, so each bf16 V element
- * is converted to fp16.  The contract is |v| <= 65504.  Inside it the
+ * Value range.  Draft attention over a bf16 token-drop cache keeps V in bf16
+ * (P.V on bf16 MFMAs with P as a bf16 hi/lo pair): any finite bf16 V.
+ * Verification (and prefill) attention runs P.V on fp16 MFMAs, so each bf16 V
+ * element is converted to fp16 there: the contract is |v| <= 65504, and it
+ * binds every model call, since each one verifies or prefills.  Inside it the
  * conversion is exact for |v| >= 2^-14 and off by at most 2^-25 (absolute)
  * below.  An element beyond it becomes +-inf and makes the output channels it
  * feeds non-finite (never a finite wrong value); through a model this reaches

@@ -1,10 +1,9 @@
 // Draft-step attention over bf16 key segments (one query row per request) and the
 // fixed-order combine of split-K partials; the many-row kernels are in
 // attention_rows.hip, the quantized-cache decode in attention_quant.hip.
-// The P.V product runs in fp16: V is converted from bf16 as it is loaded (exact for
-// |v| in [2^-14, 65504]) and P * 2^10 (P <= 1) is carried as an fp16 hi/lo pair
-// (two MFMAs), which keeps about 22 significant bits of every weight; QK^T is bf16 x
-// bf16 with exact products.
+// QK^T is bf16 x bf16 with exact products.  In P.V the draft kernel keeps V in bf16 (any
+// finite bf16 value) and carries P as a bf16 hi/lo pair (two MFMAs): hi = P rounded to bf16,
+// lo = the remainder rounded to bf16, so each weight keeps about 17 significant bits.
 #include "attention.h"
 #include "bounds.h"
 
@@ -13,8 +12,6 @@ namespace vc {
 namespace {
 
 constexpr int D128 = 128;
-constexpr float P_SCALE = 1024.f;      // P is rounded to fp16 as P * 2^10
-constexpr float P_UNSCALE = 1.f / 1024.f;
 
 // ---------------------------------------------------------------- bf16 decode, one query row
 // Draft steps attend with a single query row per request, so a 64-row block would leave
@@ -27,52 +24,62 @@ constexpr float P_UNSCALE = 1.f / 1024.f;
 // through a 16 KB LDS tile per wave.  A wave issues the next tile's loads as soon as the
 // current tile's registers are consumed, so its softmax and P.V overlap the next fetch;
 // KV loads are non-temporal (every byte is read once).
-// V^T tile layout: row d (channel) holds 64 fp16 slots; key 32kc + 16h + 4g + jj of the tile
-// sits in slot 32kc + 8g + 4h + jj, so the eight keys one lane's P^T fragment covers are
-// contiguous; 16-byte groups are XOR-swizzled by dec_sw(d) to spread the fragment reads of
-// 16 consecutive channels over all banks.
+// V tile layout: the wave's 64 keys as rows of 256 bytes (bf16, as in the cache); the eight
+// 32-byte chunks of row t (16 channels each) sit in the order chunk ^ (t & 7), so eight
+// consecutive rows put one channel chunk on eight different bank groups.  Lane (r16, g)
+// stores its 16-byte pieces (key 16q + 4g + jj, channels 8 r16 .. + 8) with one ds_write_b128
+// each.  The V^T fragments come back with the gfx950 LDS transpose read (ds_read_b64_tr_b16):
+// in each 16-lane group, lane i of the result holds element i & 3 of the 8-byte pieces that
+// lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 addressed.  Lane s of group g therefore
+// addresses channels 16 dt + 4 (s & 3) .. + 4 of key row 4g + s / 4 (plus the 16-key half h of
+// 32-key chunk kc), and lane m of the group receives channel 16 dt + m of keys 4g + 0..3: the
+// four keys its P^T fragment holds in that half.
 constexpr int DEC_WAVES = 4;
-constexpr int DEC_TILE = D128 * ATT_KT;  // fp16 per wave LDS tile
+constexpr int DEC_TILE = D128 * ATT_KT;  // bf16 per wave LDS tile
 constexpr int DEC_RED = D128 + 4;        // floats per head in the merge buffer
 
 struct DecK {
   u32x4 k[4][4];  // [16-key group kt][32-channel chunk c]
 };
 struct DecV {
-  u32x4 v[4][4];  // [16-key group a][key 4g + jj within it: jj]
+  u32x4 v[4][4];  // [16-key group q][key 4g + jj within it: jj]
 };
 
-constexpr int dec_sw(int d) { return (d ^ (d >> 3)) & 7; }
+// byte offset of (key row t, channel c) in a wave's V tile
+constexpr int dec_v_addr(int t, int c) { return 256 * t + 32 * ((c >> 4) ^ (t & 7)) + 2 * (c & 15); }
 
-// The kernel forms V^T store and fragment-read addresses as (lane base) ^ (compile-time XOR) +
-// (compile-time offset); this checks that against the layout's definition for every lane and
-// access, and that the lane bases stay inside the wave's 16 KB tile.
-constexpr bool dec_xor_addressing_ok() {
-  for (int r16 = 0; r16 < 16; r16++) {
-    for (int g = 0; g < 4; g++) {
-      const int st_lane = 1024 * r16 + 16 * (g ^ (r16 & 7));
-      const int rd_lane = 128 * r16 + 16 * (g ^ (r16 & 7) ^ (r16 >> 3));
-      for (int q = 0; q < 4; q++) {
-        for (int c = 0; c < 8; c++) {
-          const int d = 8 * r16 + c;
-          const int ref = 2 * (d * ATT_KT + 8 * ((4 * (q >> 1) + g) ^ dec_sw(d)) + 4 * (q & 1));
-          const int got = (st_lane ^ (16 * ((4 * (q >> 1)) ^ c))) + 128 * c + 8 * (q & 1);
-          if (ref != got || (st_lane ^ 112) >= 2 * DEC_TILE) return false;
-        }
+// The kernel forms the tile's store and transpose-read addresses as (lane base) ^ (compile-time
+// XOR) + (compile-time offset).  This checks, for every lane and access, that the stores put
+// each piece where the layout says, and that the transpose reads (with the result lane mapping
+// above) deliver to lane (m, g) channel 16 dt + m of keys 32 kc + 16 h + 4 g + e, e = 0..3, all
+// inside the wave's 16 KB tile.
+constexpr bool dec_tr_addressing_ok() {
+  for (int lane = 0; lane < 64; lane++) {
+    const int r16 = lane & 15, g = lane >> 4;
+    const int st_lane = 1024 * g + 32 * ((r16 >> 1) ^ (4 * (g & 1))) + 16 * (r16 & 1);
+    for (int q = 0; q < 4; q++) {
+      for (int jj = 0; jj < 4; jj++) {
+        const int got = (st_lane ^ (32 * jj)) + 4096 * q + 256 * jj;
+        if (got != dec_v_addr(16 * q + 4 * g + jj, 8 * r16) || got + 16 > 2 * DEC_TILE) return false;
       }
-      for (int kc = 0; kc < 2; kc++) {
+    }
+    for (int kc = 0; kc < 2; kc++) {
+      for (int h = 0; h < 2; h++) {
         for (int dt = 0; dt < 8; dt++) {
-          const int d = 16 * dt + r16;
-          const int ref = 2 * (d * ATT_KT + 8 * ((4 * kc + g) ^ dec_sw(d)));
-          const int got = (rd_lane ^ (16 * ((4 * kc) ^ (2 * dt & 6)))) + 2048 * dt;
-          if (ref != got || (rd_lane ^ 112) + 2048 * dt >= 2 * DEC_TILE) return false;
+          for (int e = 0; e < 4; e++) {
+            const int src = 16 * g + (r16 >> 2) + 4 * e;  // the lane whose piece element e comes from
+            const int rd_src = 256 * (src >> 2) + 32 * ((src >> 2) & 7) + 8 * (src & 3);
+            const int addr = (rd_src ^ (32 * dt)) + 8192 * kc + 4096 * h;
+            if (addr + 8 > 2 * DEC_TILE) return false;
+            if (addr + 2 * (r16 & 3) != dec_v_addr(32 * kc + 16 * h + 4 * g + e, 16 * dt + r16)) return false;
+          }
         }
       }
     }
   }
   return true;
 }
-static_assert(dec_xor_addressing_ok(), "decode V^T addressing does not match the tile layout");
+static_assert(dec_tr_addressing_ok(), "decode V tile addressing does not match the layout");
 
 // The decode kernel numbers keys per tile-aligned segment: segment a occupies logical
 // keys [0, a_al) with a_al = a.n rounded up to 64 (keys a.n .. a_al - 1 are invisible),
@@ -143,19 +150,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = NEG_INF, l_run = 0.f;
   const float sl2 = args.scale_log2;
 
-  // LDS byte offsets of this lane's V^T stores and fragment reads (see the tile layout above):
-  // the swizzle is an XOR, (lane part) ^ (compile-time part), and the tile row a store or read
-  // touches is the lane part plus a compile-time multiple of the row pitch, so each access is
-  // one XOR of a lane base and an immediate offset.  The wave's tile starts on a 16 KB boundary
-  // and the lane bases stay below 16 KB with bits 4-6 clear, so the XOR never carries.
-  //   store (channel d = 8 r16 + c, keys of group 4 (q >> 1) + g, half q & 1):
-  //     1024 r16 + 128 c + 16 ((4 (q >> 1) ^ c) ^ (g ^ (r16 & 7))) + 8 (q & 1)
-  //   read (channel d = 16 dt + r16, 16-byte group 4 kc + g):
-  //     2048 dt + 128 r16 + 16 ((4 kc ^ (2 dt & 6)) ^ (g ^ (r16 & 7) ^ (r16 >> 3)))
+  // LDS byte offsets of this lane's V stores and transpose reads (see the tile layout above):
+  // the chunk swizzle is an XOR, (lane part) ^ (compile-time part), and the row an access touches
+  // is the lane part plus a compile-time multiple of the row pitch, so each access is one XOR of
+  // a lane base and an immediate offset.  The wave's tile starts on a 16 KB boundary and the
+  // XORed bits (5-6 for stores, 5-7 for reads) are the chunk field, so the XOR never carries.
+  //   store (key 16 q + 4 g + jj, channels 8 r16 .. + 8): (st_lane ^ 32 jj) + 4096 q + 256 jj
+  //   read (half h of 32-key chunk kc, channels of 16-block dt): (rd_lane ^ 32 dt) + 8192 kc + 4096 h
   uint8_t* const lds8 = reinterpret_cast<uint8_t*>(lds);
   const uint32_t tile_base = uint32_t(wave) * (DEC_TILE * 2);
-  const uint32_t st_lane = tile_base + 1024 * r16 + 16 * (g ^ (r16 & 7));
-  const uint32_t rd_lane = tile_base + 128 * r16 + 16 * (g ^ (r16 & 7) ^ (r16 >> 3));
+  const uint32_t st_lane = tile_base + 1024 * g + 32 * ((r16 >> 1) ^ (4 * (g & 1))) + 16 * (r16 & 1);
+  const uint32_t rd_lane = tile_base + 256 * (lane >> 2) + 32 * ((lane >> 2) & 7) + 8 * (lane & 3);
   // a tile is wholly visible when it ends at or before key_hi and lies in the visible part of
   // its segment (segment a's keys below a_n, or segment b)
   const int a_vis_end = min(a_n, key_hi);
@@ -178,21 +183,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int c = 0; c < 4; c++) sacc[kt] = mfma_bf16(kr.k[kt][c], qf[c], sacc[kt]);
     }
-    // ---- V -> fp16, transposed into this wave's LDS tile
+    // ---- V rows into this wave's LDS tile as they are
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const int half = q & 1;
 #pragma unroll
-      for (int c = 0; c < 8; c++) {
-        float x[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) x[jj] = (c & 1) ? hi_bf(vr.v[q][jj][c >> 1]) : lo_bf(vr.v[q][jj][c >> 1]);
-        u32x2 w;
-        w.x = pack_h2(x[0], x[1]);
-        w.y = pack_h2(x[2], x[3]);
-        const uint32_t k16 = 16u * uint32_t((4 * (q >> 1)) ^ c);
-        *reinterpret_cast<u32x2*>(lds8 + (st ^ k16) + (128 * c + 8 * half)) = w;
-      }
+      for (int jj = 0; jj < 4; jj++)
+        *reinterpret_cast<u32x4*>(lds8 + (st ^ (32u * jj)) + (4096 * q + 256 * jj)) = vr.v[q][jj];
     }
     // ---- next tile in flight while this one finishes (the scheduling barrier keeps the
     // loads from being hoisted above the last uses of the registers they overwrite)
@@ -246,22 +242,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // LDS operations of one wave complete in issue order; the fence keeps the compiler
     // from moving the fragment reads above the tile stores (and later stores above them).
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    // ---- O^T += V^T P^T over 2 chunks of 32 keys, P as an fp16 hi/lo pair
+    // ---- O^T += V^T P^T over 2 chunks of 32 keys, P as a bf16 hi/lo pair
 #pragma unroll
     for (int kc = 0; kc < 2; kc++) {
       uint32_t h[4], lw[4];
-      split_h2(sacc[2 * kc][0] * P_SCALE, sacc[2 * kc][1] * P_SCALE, h[0], lw[0]);
-      split_h2(sacc[2 * kc][2] * P_SCALE, sacc[2 * kc][3] * P_SCALE, h[1], lw[1]);
-      split_h2(sacc[2 * kc + 1][0] * P_SCALE, sacc[2 * kc + 1][1] * P_SCALE, h[2], lw[2]);
-      split_h2(sacc[2 * kc + 1][2] * P_SCALE, sacc[2 * kc + 1][3] * P_SCALE, h[3], lw[3]);
+      split_bf2(sacc[2 * kc][0], sacc[2 * kc][1], h[0], lw[0]);
+      split_bf2(sacc[2 * kc][2], sacc[2 * kc][3], h[1], lw[1]);
+      split_bf2(sacc[2 * kc + 1][0], sacc[2 * kc + 1][1], h[2], lw[2]);
+      split_bf2(sacc[2 * kc + 1][2], sacc[2 * kc + 1][3], h[3], lw[3]);
       const u32x4 pb = u32x4{h[0], h[1], h[2], h[3]};
       const u32x4 pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
-        const uint32_t c16 = 16u * uint32_t((4 * kc) ^ (2 * dt & 6));
-        const u32x4 va = *reinterpret_cast<const u32x4*>(lds8 + (rd ^ c16) + 2048 * dt);
-        oacc[dt] = mfma_f16(va, pb, oacc[dt]);
-        oacc[dt] = mfma_f16(va, pl, oacc[dt]);
+        const uint32_t a0 = (rd ^ (32u * dt)) + 8192 * kc;
+        const u32x2 v0 = lds_read_tr16(lds8 + a0), v1 = lds_read_tr16(lds8 + a0 + 4096);
+        const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
+        oacc[dt] = mfma_bf16(va, pb, oacc[dt]);
+        oacc[dt] = mfma_bf16(va, pl, oacc[dt]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -278,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) rh[2 + 16 * dt + 4 * g + jj] = oacc[dt][jj] * P_UNSCALE;
+      for (int jj = 0; jj < 4; jj++) rh[2 + 16 * dt + 4 * g + jj] = oacc[dt][jj];
     }
   }
   __syncthreads();

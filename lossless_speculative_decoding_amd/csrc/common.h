@@ -78,6 +78,17 @@ __device__ __forceinline__ void split_h2(float a, float b, uint32_t& hi, uint32_
   lo = __builtin_bit_cast(uint32_t, h2{(_Float16)ra, (_Float16)rb});
 }
 
+// two floats -> bf16 hi pair and bf16 lo pair with a ~= hi + lo (about 17 significant bits):
+// hi rounds a to bf16 (nearest even), a - hi is exact in fp32 and lo rounds it.  The empty asm
+// keeps the compiler from converting a a second time to rebuild hi's low half.
+__device__ __forceinline__ void split_bf2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(uint32_t, b2{(__bf16)a, (__bf16)b});
+  asm volatile("" : "+v"(hi));
+  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, b2{(__bf16)ra, (__bf16)rb});
+}
+
 template <typename T>
 __device__ __forceinline__ T bitcast(const auto& x) {
   static_assert(sizeof(T) == sizeof(x), "size mismatch");
@@ -96,6 +107,17 @@ __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, f32x4
 }
 __device__ __forceinline__ f32x4 mfma_f16(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8>(a), bitcast<f16x8>(b), c, 0, 0, 0);
+}
+
+// gfx950 LDS transpose read of 16-bit elements (ds_read_b64_tr_b16): every lane addresses an
+// 8-byte piece (4 elements); in each group of 16 lanes, lane i receives element i & 3 of the
+// pieces of lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 of its group, in that order.
+// p must point into LDS and be 8-byte aligned.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const lds_s4* q = (const lds_s4*)((const __attribute__((address_space(3))) uint8_t*)p);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s4*>(q)));
 }
 
 // 16-byte load marked non-temporal (streamed once, not kept in the caches)

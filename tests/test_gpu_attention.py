@@ -330,10 +330,11 @@ def test_profile_records_verify_and_draft_launches():
 
 
 def test_v_beyond_fp16_range_is_non_finite_not_wrong():
-    """A V element beyond fp16's range (the documented bound |v| <= 65504)
-    makes exactly the output channels it feeds non-finite, on the verification
-    kernel (staged row) and on the draft kernel (tail row); every other output
-    still matches the oracle."""
+    """A V element beyond fp16's range (the documented bound |v| <= 65504 of
+    the verification kernel, which runs P.V on fp16) makes exactly the output
+    channels it feeds non-finite there (staged row), and every other output
+    still matches the oracle.  The draft kernel keeps V in bf16, so the same
+    element in its tail row gives finite outputs that all match the oracle."""
     need_gpu()
     from lossless_speculative_decoding_amd import VC_BF16, VC_F32, VC_TOKDROP, compress_desc, compress_layout
     from lossless_speculative_decoding_amd import vc_attn_draft, vc_attn_verify, vc_compress
@@ -368,10 +369,7 @@ def test_v_beyond_fp16_range_is_non_finite_not_wrong():
                         [n_tail], dev_bf16(qd))
     torch.cuda.synchronize()
     o = host_f64(out[0])
-    bad = ~np.isfinite(o)
-    assert bad[12:16, ch].all()
-    bad[12:16, ch] = False
-    assert not bad.any()
+    assert np.isfinite(o).all()
     raw = blob.cpu().numpy()
     idx = raw[compress_layout(d).idx: compress_layout(d).idx + HKV * kt * 4].view(np.int32).reshape(HKV, kt)
     for j in (0, 3):
@@ -379,7 +377,4 @@ def test_v_beyond_fp16_range_is_non_finite_not_wrong():
         Vj = np.concatenate([_f(vb2[j, idx[j]]), _f(tv[j])])
         for g in range(4):
             r = OA.attend(_f(qd[0, j * 4 + g]), Kj, Vj)
-            m = np.ones(D, bool)
-            if j == 3:
-                m[ch] = False                           # the channel the large element feeds
-            assert np.abs(o[j * 4 + g][m] - r[m]).max() <= TOL_BF16 * np.abs(r[m]).max()
+            assert np.abs(o[j * 4 + g] - r).max() <= TOL_BF16 * np.abs(r).max()

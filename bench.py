@@ -138,8 +138,8 @@ def cpu_oracle_tiny() -> dict:
 
 
 def pmc_traffic_ratio(workload: str, kernel: str = "attn_decode_bf16", what: str = "draft_attention"):
-    """Measured HBM bytes over algorithmic bytes of the draft-attention launches, from the
-    committed counter profile of this workload (profiles/draft_attention_<workload>_pmc.json),
+    """Measured HBM bytes over algorithmic bytes of one kernel class's launches, from the
+    committed counter profile of this workload (profiles/<what>_<workload>_pmc.json),
     if the kernel sources are unchanged since.  The
     counter passes serialise every dispatch, which changes how many requests draft together,
     so the ratio (taken over the same launches on both sides) carries over to this run's
@@ -444,6 +444,11 @@ def run_model_workload(args) -> dict:
     bpl = prof["bytes"] / max(prof["launches"], 1)
     traffic = round(traffic_ratio * bpl) if traffic_ratio else None
     pcie_gbs = staged / secs / 1e9
+    verify_rate = _rate(vprof, "hbm", "verification attention partials (one layer of one request)")
+    if verify_rate:
+        v_ratio = pmc_traffic_ratio(w.name, "attn_rows_bf16", "verify_attention")
+        verify_rate["traffic"] = round(v_ratio * verify_rate["bytes_per_launch"]) if v_ratio else None
+        verify_rate["traffic_over_algorithmic"] = v_ratio
     # compressed-only decoding (lossy; context): x batched draft steps of every request, no verification
     # (requests whose tail has no room for x more rows are rolled back to the last position that
     # has: this pass follows the timed region and only its rate is kept)
@@ -556,7 +561,7 @@ def run_model_workload(args) -> dict:
                      "bytes_per_launch": round(prof["bytes"] / max(prof["launches"], 1)),
                      "partial_bytes_per_launch": round(prof["aux_bytes"] / max(prof["launches"], 1)),
                      "bytes_per_launch_incl_warmup": round(all_bytes), "launches_incl_warmup": all_launches},
-        "verify_attention": _rate(vprof, "hbm", "verification attention partials (one layer of one request)"),
+        "verify_attention": verify_rate,
         "gemm_decode": _rate(gprof, "hbm", f"projection and LM-head GEMMs of {len(live)}-request draft steps "
                                            "(weight streaming)"),
         "gemm_prefill": _rate(prefill_prof["gemm"], "mfma", f"projection GEMMs of request 0's prefill "

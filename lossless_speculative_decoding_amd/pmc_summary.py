@@ -39,11 +39,14 @@ def sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def counter_avg(path: str, kernel: str, counter: str, first: int | None = None) -> tuple[float, int]:
-    """Average of the counter over the kernel's dispatches (the first `first` of them in
-    dispatch order when given)."""
+def counter_avg(path: str, kernel: str, counter: str, first: int | None = None,
+                last: int | None = None) -> tuple[float, int]:
+    """Average of the counter over the dispatches of kernels whose name contains `kernel` (the
+    first `first` or the last `last` of them in dispatch order when given)."""
     rows = sorted((r for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter),
                   key=lambda r: int(r["Dispatch_Id"]))
+    if last is not None:
+        rows = rows[-last:]
     vals = [float(r["Counter_Value"]) for r in rows[:first]]
     if not vals:
         raise SystemExit(f"no {counter} rows for a kernel named like {kernel!r} in {path}")
@@ -61,6 +64,12 @@ def main():
                     help="algorithmic bytes per dispatch over the same dispatches, for the ratio")
     ap.add_argument("--first", type=int, default=None,
                     help="only the kernel's first N dispatches (those the algorithmic bytes describe)")
+    ap.add_argument("--last", type=int, default=None,
+                    help="only the kernel's last N dispatches (e.g. a timed region followed by no other "
+                         "dispatch of the same kernel)")
+    ap.add_argument("--match", default=None,
+                    help="select dispatches whose kernel name contains this text (default: --kernel), e.g. "
+                         "one template instance")
     ap.add_argument("--command", required=True)
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
@@ -68,12 +77,14 @@ def main():
     cw, _ = counter_avg(a.copy_write, COPY_KERNEL, "WRITE_SIZE")
     f_scale = COPY_BYTES / (cf * 1024)
     w_scale = COPY_BYTES / (cw * 1024)
-    kf, nf = counter_avg(a.fetch, a.kernel, "FETCH_SIZE", a.first)
-    kw, nw = counter_avg(a.write, a.kernel, "WRITE_SIZE", a.first)
+    sel = a.match or a.kernel
+    kf, nf = counter_avg(a.fetch, sel, "FETCH_SIZE", a.first, a.last)
+    kw, nw = counter_avg(a.write, sel, "WRITE_SIZE", a.first, a.last)
     read = kf * 1024 * f_scale
     written = kw * 1024 * w_scale
     rec = {
         "kernel": a.kernel,
+        "match": sel,
         "command": a.command,
         "dispatches": {"fetch_pass": nf, "write_pass": nw},
         "fetch_kib_per_dispatch": kf,

@@ -487,7 +487,7 @@ def run_model_workload(args) -> dict:
     eng.release_host()  # the comparator needs host memory for a whole full KV
     first = torch.tensor([r0.emitted[0]], dtype=torch.int32, device=device)
     toks, bsecs = greedy_from_host(model, r0.prefill_kv, r0.T, first, args.baseline_steps, eng.ws_verify,
-                                   eng.copy_stream)
+                                   eng.copy_stream, layered=args.comparator_staging == "layered")
     base_tok_s = args.baseline_steps / bsecs
     n_cmp = min(len(toks), len(r0.emitted) - 1)
     # sampled decoding emits another draw of the same distribution: tokens are not comparable
@@ -574,6 +574,7 @@ def run_model_workload(args) -> dict:
                  "note": "host rows staged for verification in the timed region / its wall time"},
         "full_kv_from_host_tok_s": round(base_tok_s, 3),
         "full_kv_from_host_tokens_match": base_match,
+        "full_kv_from_host_staging": args.comparator_staging,
         "resident_full_kv_greedy_tok_s": round(res_tok_s, 2),
         "resident_full_kv_note": "context only: request 0 alone with its whole cache in HBM (the workload keeps it "
                                  "on the host); tokens match VeriCache's: " + str(res_match),
@@ -792,6 +793,9 @@ def main():
     ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
     ap.add_argument("--baseline-steps", type=int, default=16)
+    ap.add_argument("--comparator-staging", choices=["layered", "whole"], default="layered",
+                    help="full-KV-from-host comparator: stage layer by layer with each layer's attention waiting "
+                         "only for its own layer (default), or stage all layers before each verification")
     ap.add_argument("--draft-batch", type=int, default=0,
                     help="requests yet to draft wait for a batch this large while --queue-min drafted requests are "
                          "queued for verification (0: all the requests; 1: draft as soon as possible)")

@@ -255,6 +255,20 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
                     const int32_t* tok, int32_t n_rows, int32_t* out_argmax, float* logits_opt, void* vtail_k,
                     void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* vc_verify with the staged rows arriving layer by layer (the swap cost of
+ * bringing the full KV back, "The VeriCache Architecture", VeriCache Guide):
+ * layer_ready holds n_layers events (host array of handles); before layer l's
+ * attention reads the staged rows, `s` waits for layer_ready[l], which the
+ * caller records on its copy stream once layer l is staged (vc_stage with
+ * l0 = l, l1 = l + 1).  Each layer's projections run before that wait, and
+ * layer l's compute overlaps the copies of the later layers.  Results are
+ * those of vc_verify.  The events are not retained after the call returns
+ * (the waits are enqueued). */
+vc_status vc_verify_layered(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v,
+                            int32_t staged_cap, const int32_t* tok, int32_t n_rows, int32_t* out_argmax,
+                            float* logits_opt, void* vtail_k, void* vtail_v, int32_t vtail_cap, void* ws,
+                            size_t ws_bytes, const hipEvent_t* layer_ready, hipStream_t s);
+
 /* Accept until the first mismatch ("The Core Idea", pseudocode and worked
  * example).  On `s`: with draft = req->rows + 1, a = first i < x with
  * draft[i] != verified[i] (else x); result[0] = a, result[1 .. a+1] =

@@ -108,6 +108,7 @@ _SIGS = {
     "vc_draft_step": (_I, [_P, C.POINTER(Req), _I, _P, _P, _S, _P]),
     "vc_draft_step_static": (_I, [_P, C.POINTER(Req), _I, _P, _P]),
     "vc_verify": (_I, [_P, C.POINTER(Req), _P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P]),
+    "vc_verify_layered": (_I, [_P, C.POINTER(Req), _P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _P, _S, _P, _P]),
     "vc_accept": (_I, [_P, C.POINTER(Req), _P, _I, _P, _P, _I, _P, _P]),
     "vc_commit": (_I, [_P, C.POINTER(Req), _I, _P, _P, _I, _P, _P]),
     "vc_stage": (_I, [_P, C.POINTER(Req), _P, _P, _I, _I, _I, _P]),

@@ -243,6 +243,14 @@ class Model:
         call("vc_verify", self.h, C.byref(req), staged_k, staged_v, staged_cap, tok, n_rows, out, logits, vtail_k,
              vtail_v, vtail_cap, ptr(ws), ws.numel(), stream_handle())
 
+    def verify_layered_raw(self, req: Req, staged_k: int, staged_v: int, staged_cap: int, tok: int, n_rows: int,
+                           out: int, vtail_k: int, vtail_v: int, vtail_cap: int, ws: torch.Tensor, layer_ready,
+                           logits: int | None = None):
+        """vc_verify_layered: layer l's attention waits for layer_ready[l] (one event per layer)."""
+        evs = (C.c_void_p * len(layer_ready))(*[e.cuda_event for e in layer_ready])
+        call("vc_verify_layered", self.h, C.byref(req), staged_k, staged_v, staged_cap, tok, n_rows, out, logits,
+             vtail_k, vtail_v, vtail_cap, ptr(ws), ws.numel(), evs, stream_handle())
+
     def verify(self, req: Req, staged_k, staged_v, tok: torch.Tensor, n_rows: int, out: torch.Tensor, vtail_k,
                vtail_v, ws: torch.Tensor, logits=None):
         scap = staged_k.shape[-2] if staged_k is not None else 0

@@ -855,9 +855,14 @@ vc_status host_part(const vc_model* m, const vc_req* req, HostPart& hp) {
   return VC_OK;
 }
 
-vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v, int32_t staged_cap,
-                    const int32_t* tok, int32_t n_rows, int32_t* out_argmax, float* logits_opt, void* vtail_k,
-                    void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, hipStream_t s) {
+}  // extern "C"
+
+namespace {
+// vc_verify; with layer_ready, layer l's attention waits on the stream for layer_ready[l] first.
+vc_status verify_impl(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v, int32_t staged_cap,
+                      const int32_t* tok, int32_t n_rows, int32_t* out_argmax, float* logits_opt, void* vtail_k,
+                      void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, const hipEvent_t* layer_ready,
+                      hipStream_t s) {
   if (vc_status st = check_model(m)) return st;
   VC_REQUIRE(req && tok && out_argmax && vtail_k && vtail_v && ws, VC_ERR_ARG, "vc_verify: null argument");
   VC_REQUIRE(n_rows > 0 && n_rows <= 64, VC_ERR_ARG, "vc_verify: n_rows %d not in [1, 64]", n_rows);
@@ -900,6 +905,7 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
     return VC_OK;
   };
   auto attend = [&](int l, const void* qb, void* ob, float* part) -> vc_status {
+    if (layer_ready && !dbg_dry()) VC_HIP(hipStreamWaitEvent(s, layer_ready[l], 0));
     AttnArgs a{};
     a.n_req = 1;
     a.Hq = d.n_q_heads;
@@ -956,6 +962,25 @@ vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const 
   };
   if ((st = forward_layers(m, n_rows, w8, L, tmpl, set_kv, attend, s))) return st;
   return head(m, 0, n_rows, w8, L, out_argmax, logits_opt, s);
+}
+}  // namespace
+
+extern "C" {
+
+vc_status vc_verify(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v, int32_t staged_cap,
+                    const int32_t* tok, int32_t n_rows, int32_t* out_argmax, float* logits_opt, void* vtail_k,
+                    void* vtail_v, int32_t vtail_cap, void* ws, size_t ws_bytes, hipStream_t s) {
+  return verify_impl(m, req, staged_k, staged_v, staged_cap, tok, n_rows, out_argmax, logits_opt, vtail_k, vtail_v,
+                     vtail_cap, ws, ws_bytes, nullptr, s);
+}
+
+vc_status vc_verify_layered(vc_model* m, const vc_req* req, const void* staged_k, const void* staged_v,
+                            int32_t staged_cap, const int32_t* tok, int32_t n_rows, int32_t* out_argmax,
+                            float* logits_opt, void* vtail_k, void* vtail_v, int32_t vtail_cap, void* ws,
+                            size_t ws_bytes, const hipEvent_t* layer_ready, hipStream_t s) {
+  VC_REQUIRE(layer_ready != nullptr, VC_ERR_ARG, "vc_verify_layered: null event array");
+  return verify_impl(m, req, staged_k, staged_v, staged_cap, tok, n_rows, out_argmax, logits_opt, vtail_k, vtail_v,
+                     vtail_cap, ws, ws_bytes, layer_ready, s);
 }
 
 vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out, void* v_out, int32_t cap, void* q_obs,

@@ -627,11 +627,15 @@ def sample_resident(model: B.Model, prompt: torch.Tensor, n_tokens: int, sampler
 
 
 def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tensor, n_steps: int, ws: torch.Tensor,
-                     copy_stream):
+                     copy_stream, layered: bool = True):
     """Full-KV greedy decoding with the cache in pinned host memory, the
     comparator VeriCache is measured against: a plain request (no compressed
     cache) whose whole context lives on the host; every token stages it over
-    PCIe, runs one vc_verify row, and appends the new row to the host copy.
+    PCIe, runs one verification row, and appends the new row to the host copy.
+    layered: the context is staged one layer at a time and layer l's attention
+    waits only for layer l (vc_verify_layered), so each layer's compute overlaps
+    the copies of the layers after it; otherwise all layers are staged before
+    vc_verify starts.
     prompt_kv: device (K, V) [L][Hkv][cap][D] holding prompt rows [0, T);
     first_token: device int32 [1], the token at position T.
     Returns (tokens after first_token, seconds)."""
@@ -654,13 +658,21 @@ def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tenso
     toks = []
     runtime.RT.synchronize()
     t0 = time.perf_counter()
+    layer_ev = [runtime.RT.Event() for _ in range(L)]
     for _ in range(n_steps):
-        model.stage(req, sk, sv, 0, L, copy_stream=copy_stream)
-        ev = runtime.RT.Event()
-        ev.record(copy_stream)
-        cs.wait_event(ev)
-        model.verify_raw(req, sk.data_ptr(), sv.data_ptr(), cap, rows.data_ptr(), 1, rows.data_ptr(),
-                         vk.data_ptr(), vv.data_ptr(), 1, ws)
+        if layered:
+            for l in range(L):
+                model.stage(req, sk, sv, l, l + 1, copy_stream=copy_stream)
+                layer_ev[l].record(copy_stream)
+            model.verify_layered_raw(req, sk.data_ptr(), sv.data_ptr(), cap, rows.data_ptr(), 1, rows.data_ptr(),
+                                     vk.data_ptr(), vv.data_ptr(), 1, ws, layer_ev)
+        else:
+            model.stage(req, sk, sv, 0, L, copy_stream=copy_stream)
+            ev = runtime.RT.Event()
+            ev.record(copy_stream)
+            cs.wait_event(ev)
+            model.verify_raw(req, sk.data_ptr(), sv.data_ptr(), cap, rows.data_ptr(), 1, rows.data_ptr(),
+                             vk.data_ptr(), vv.data_ptr(), 1, ws)
         done = runtime.RT.Event()
         done.record(cs)
         model.commit(req, 0, vk, vv, after_event=done, copy_stream=copy_stream)

@@ -231,3 +231,18 @@ def test_adaptive_draft_length_equals_gpu_greedy(setup):
     eng.run(adaptive=True, x_min=2)
     log("adaptive accepts", r.accepts)
     assert r.emitted == setup["g_toks"]
+
+
+@pytest.mark.parametrize("layered", [True, False], ids=["layered", "whole"])
+def test_full_kv_from_host_equals_resident_greedy(setup, layered):
+    """The full-KV-from-host comparator: the prompt's cache offloaded to pinned host memory, every
+    token stages it (layer by layer, each layer's attention waiting only for its own layer, or all
+    layers before the verification) and verifies one row, then appends that row to the host copy;
+    its tokens equal resident greedy decoding's (the same rows through the same kernels)."""
+    from lossless_speculative_decoding_amd.engine import greedy_from_host
+    m, (kd, vd) = setup["m"], setup["kv"]
+    first = torch.tensor([setup["g_toks"][0]], dtype=torch.int32, device="cuda")
+    ws = m.workspace(1, T + N + 1)
+    toks, secs = greedy_from_host(m, (kd, vd), T, first, 16, ws, torch.cuda.Stream(), layered=layered)
+    log(f"full KV from host ({'layered' if layered else 'whole'} staging): 16 tokens in {secs * 1e3:.1f} ms")
+    assert toks == setup["g_toks"][1:17]

@@ -300,10 +300,10 @@ def _rate(st: dict, bound: str, what: str) -> dict | None:
 
 # Workloads refused by bench.py until the cause of a failure is shown.
 DISABLED = {
-    "llama8b_mixed": "its run faulted the GPU although every launch and copy was range-checked first (bench "
-                     "--check-bounds); what only this workload runs: host rows beyond the pinned budget copied "
-                     "from pageable memory on a worker stream, partial prefill chunks through the GEMM library at "
-                     "the 8B shapes, 16-request draft batches with per-request draft lengths; no cause shown yet",
+    "llama8b_mixed": "its one run faulted the GPU although every launch and copy was range-checked first; the cause "
+                     "found since (host rows beyond the pinned budget handed to the copy engines in pageable "
+                     "memory) is fixed (they now move through a pinned pair of one-layer buffers), but the "
+                     "workload has not run again yet",
 }
 
 

@@ -307,11 +307,19 @@ vc_status vc_host_free(void* host);
  * the call then synchronises `s`), all T rows otherwise. */
 vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const void* v_dev, int32_t src_cap, int32_t T,
                      hipStream_t s);
+/* vc_offload of layers [l0, l1) only.  Like vc_stage, it touches only those
+ * layers of the host arrays (bytes [l0, l1) x Hkv x full_cap x D x elem of
+ * full_k_host / full_v_host), so a caller that keeps host rows in ordinary
+ * (pageable) memory can move them one layer at a time through a pinned buffer
+ * of one layer, passing full_k_host = buffer - l0 x (that layer size): the
+ * library never hands pageable memory to a copy engine. */
+vc_status vc_offload_layers(vc_model* m, const vc_req* req, const void* k_dev, const void* v_dev, int32_t src_cap,
+                            int32_t T, int32_t l0, int32_t l1, hipStream_t s);
 
 /* Stage the request's host rows (n_host per (layer, head) with a compressed
  * cache, ctx_len for a plain request) from pinned host memory into a device
  * slot [L][Hkv][slot_cap][D] on `copy` (SDMA, hipMemcpy2DAsync), layers
- * [l0, l1). */
+ * [l0, l1); only those layers of the host arrays and the slot are touched. */
 vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, int32_t slot_cap, int32_t l0, int32_t l1,
                    hipStream_t copy);
 

@@ -129,6 +129,7 @@ _SIGS = {
     "vc_host_alloc": (_I, [_S, C.POINTER(_P)]),
     "vc_host_free": (_I, [_P]),
     "vc_offload": (_I, [_P, C.POINTER(Req), _P, _P, _I, _I, _P]),
+    "vc_offload_layers": (_I, [_P, C.POINTER(Req), _P, _P, _I, _I, _I, _I, _P]),
     "vc_profile_read": (_I, [_I, C.POINTER(ProfileStats)]),
     "vc_debug_mode": (_I, [_I]),
     "vc_debug_register": (_I, [_P, _S]),

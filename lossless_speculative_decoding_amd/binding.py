@@ -266,8 +266,12 @@ class Model:
         call("vc_commit", self.h, C.byref(req), a, ptr(vtail_k), ptr(vtail_v), vtail_k.shape[-2], ev,
              stream_handle(copy_stream))
 
-    def offload(self, req: Req, k_dev, v_dev, T: int):
-        call("vc_offload", self.h, C.byref(req), ptr(k_dev), ptr(v_dev), k_dev.shape[-2], T, stream_handle())
+    def offload(self, req: Req, k_dev, v_dev, T: int, l0: int | None = None, l1: int | None = None):
+        if l0 is None:
+            call("vc_offload", self.h, C.byref(req), ptr(k_dev), ptr(v_dev), k_dev.shape[-2], T, stream_handle())
+        else:
+            call("vc_offload_layers", self.h, C.byref(req), ptr(k_dev), ptr(v_dev), k_dev.shape[-2], T, l0, l1,
+                 stream_handle())
 
     def stage(self, req: Req, slot_k, slot_v, l0: int, l1: int, copy_stream=None):
         call("vc_stage", self.h, C.byref(req), ptr(slot_k), ptr(slot_v), slot_k.shape[-2], l0, l1,
@@ -323,14 +327,14 @@ def profile_read(kind: int = VC_PROF_DRAFT_ATTN) -> dict:
 
 
 class PageableBuffer:
-    """Ordinary (pageable) host memory for host rows beyond the pinned budget.  Copies
-    from it block the calling thread (the runtime stages them through its own pinned
-    buffers), so the scheduler issues them from a worker thread."""
+    """Ordinary (pageable) host memory for host rows beyond the pinned budget.  No copy
+    engine ever reads or writes it: the engine moves its rows one layer at a time through
+    pinned buffers with host memcpy (see Engine._offload_pageable / _stage_pageable).
+    Never pass its address to a library call."""
 
     def __init__(self, nbytes: int):
         self.t = torch.empty(nbytes, dtype=torch.uint8)
         self.nbytes = nbytes
-        debug_register(self.t)
 
     def data_ptr(self) -> int:
         return self.t.data_ptr()
@@ -347,11 +351,19 @@ class HostBuffer:
         call("vc_host_alloc", nbytes, C.byref(p))
         self.ptr = p.value
         self.nbytes = nbytes
+        self._view = None
 
     def data_ptr(self) -> int:
         return self.ptr
 
+    def tensor(self) -> torch.Tensor:
+        """A uint8 CPU tensor over the buffer (no copy; valid until free())."""
+        if self._view is None:
+            self._view = torch.frombuffer((C.c_uint8 * self.nbytes).from_address(self.ptr), dtype=torch.uint8)
+        return self._view
+
     def free(self):
+        self._view = None
         if self.ptr:
             call("vc_host_free", self.ptr)
             self.ptr = None

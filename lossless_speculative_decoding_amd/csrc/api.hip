@@ -381,16 +381,24 @@ vc_status comp_view(const void* comp, const vc_compress_desc* cd, CompView& v) {
 // Debug mode: the whole buffers a request claims (tails of tail_cap rows per (layer, head), the
 // host rows, the token slots, the compressed blob), each measured from its own base pointer so
 // that a capacity larger than the allocation is caught even where a neighbouring buffer follows.
-vc_status dbg_request(const char* where, const vc_model* m, const vc_req& q, bool host_rows, int token_rows = 1) {
+// host_rows: also the host arrays, layers [l0, l1) of them (l1 < 0: all layers)
+vc_status dbg_request(const char* where, const vc_model* m, const vc_req& q, bool host_rows, int token_rows = 1,
+                      int l0 = 0, int l1 = -1) {
   if (!dbg_on()) return VC_OK;
   const vc_model_desc& d = m->d;
   const int64_t per = int64_t(d.n_layers) * d.n_kv_heads * d.head_dim * m->eb;
   vc_status st = dbg_check(where, {{"request tail K", q.tail_k, q.tail_k ? per * q.tail_cap : 0},
                                    {"request tail V", q.tail_v, q.tail_v ? per * q.tail_cap : 0},
                                    {"request token rows", q.rows, q.rows ? int64_t(token_rows) * 4 : 0}});
-  if (!st && host_rows)
-    st = dbg_check(where, {{"request host K rows", q.full_k_host, q.full_k_host ? per * q.full_cap : 0},
-                           {"request host V rows", q.full_v_host, q.full_v_host ? per * q.full_cap : 0}});
+  if (!st && host_rows) {
+    if (l1 < 0) l1 = d.n_layers;
+    const int64_t lay = int64_t(d.n_kv_heads) * d.head_dim * m->eb * q.full_cap;  // one layer of a host array
+    const int64_t off = int64_t(l0) * lay, len = int64_t(l1 - l0) * lay;
+    st = dbg_check(where, {{"request host K rows", q.full_k_host ? cptr(q.full_k_host, off) : nullptr,
+                            q.full_k_host ? len : 0},
+                           {"request host V rows", q.full_v_host ? cptr(q.full_v_host, off) : nullptr,
+                            q.full_v_host ? len : 0}});
+  }
   if (!st && q.comp && q.cd) {
     vc_compress_layout lay;
     if ((st = compress_layout(q.cd, &lay))) return st;
@@ -1125,9 +1133,10 @@ vc_status vc_stage(vc_model* m, const vc_req* req, void* slot_k, void* slot_v, i
   VC_REQUIRE(slot_cap >= rows && req->full_cap >= rows, VC_ERR_CAPACITY, "vc_stage: slot %d / host %d < %d rows",
              slot_cap, req->full_cap, rows);
   if (dbg_on()) {
-    const int64_t per = int64_t(d.n_layers) * d.n_kv_heads * d.head_dim * m->eb;
-    if (vc_status st = dbg_request("vc_stage", m, *req, true)) return st;
-    if (vc_status st = dbg_check("vc_stage", {{"slot K", slot_k, per * slot_cap}, {"slot V", slot_v, per * slot_cap}}))
+    const int64_t lay = int64_t(d.n_kv_heads) * d.head_dim * m->eb * slot_cap;  // one layer of the slot
+    if (vc_status st = dbg_request("vc_stage", m, *req, true, 1, l0, l1)) return st;
+    if (vc_status st = dbg_check("vc_stage", {{"slot K", mptr(slot_k, l0 * lay), (l1 - l0) * lay},
+                                              {"slot V", mptr(slot_v, l0 * lay), (l1 - l0) * lay}}))
       return st;
   }
   if (l0 == l1 || rows == 0) return VC_OK;
@@ -1169,11 +1178,19 @@ vc_status vc_host_free(void* host) {
 vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const void* v_dev, int32_t src_cap, int32_t T,
                      hipStream_t s) {
   if (vc_status st = check_model(m)) return st;
+  return vc_offload_layers(m, req, k_dev, v_dev, src_cap, T, 0, m->d.n_layers, s);
+}
+
+vc_status vc_offload_layers(vc_model* m, const vc_req* req, const void* k_dev, const void* v_dev, int32_t src_cap,
+                            int32_t T, int32_t l0, int32_t l1, hipStream_t s) {
+  if (vc_status st = check_model(m)) return st;
   VC_REQUIRE(req && k_dev && v_dev && req->full_k_host && req->full_v_host, VC_ERR_ARG, "vc_offload: null argument");
   VC_REQUIRE(T > 0 && T <= src_cap, VC_ERR_CAPACITY, "vc_offload: bad row counts");
   const vc_model_desc& d = m->d;
+  VC_REQUIRE(0 <= l0 && l0 <= l1 && l1 <= d.n_layers, VC_ERR_ARG, "vc_offload: bad layer range");
+  if (l0 == l1) return VC_OK;
   const size_t row = size_t(d.head_dim) * m->eb;
-  const size_t height = size_t(d.n_layers) * d.n_kv_heads;
+  const size_t height = size_t(l1 - l0) * d.n_kv_heads;
   if (req->comp != nullptr) {
     HostPart hp;
     vc_req probe = *req;
@@ -1189,7 +1206,7 @@ vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const vo
       void* tmp = nullptr;
       if (vc_status st0 = dev_alloc(&tmp, 2 * lbytes)) return st0;
       vc_status st = VC_OK;
-      for (int l = 0; l < d.n_layers && st == VC_OK; l++) {
+      for (int l = l0; l < l1 && st == VC_OK; l++) {
         for (int kv = 0; kv < 2 && st == VC_OK; kv++) {
           void* dst = mptr(tmp, kv * lbytes);
           st = gather_dropped(req->cd, req->comp, kv ? v_dev : k_dev, src_cap, l * d.n_kv_heads, d.n_kv_heads, dst,
@@ -1209,11 +1226,12 @@ vc_status vc_offload(vc_model* m, const vc_req* req, const void* k_dev, const vo
     }
   }
   VC_REQUIRE(T <= req->full_cap, VC_ERR_CAPACITY, "vc_offload: host capacity %d < %d rows", req->full_cap, T);
-  if (vc_status st = copy2d("offload K rows", req->full_k_host, size_t(req->full_cap) * row, k_dev, size_t(src_cap) * row,
-                            size_t(T) * row, height, hipMemcpyDeviceToHost, s))
+  const int64_t h0 = int64_t(l0) * d.n_kv_heads * req->full_cap * row, d0 = int64_t(l0) * d.n_kv_heads * src_cap * row;
+  if (vc_status st = copy2d("offload K rows", mptr(req->full_k_host, h0), size_t(req->full_cap) * row, cptr(k_dev, d0),
+                            size_t(src_cap) * row, size_t(T) * row, height, hipMemcpyDeviceToHost, s))
     return st;
-  return copy2d("offload V rows", req->full_v_host, size_t(req->full_cap) * row, v_dev, size_t(src_cap) * row,
-                size_t(T) * row, height, hipMemcpyDeviceToHost, s);
+  return copy2d("offload V rows", mptr(req->full_v_host, h0), size_t(req->full_cap) * row, cptr(v_dev, d0),
+                size_t(src_cap) * row, size_t(T) * row, height, hipMemcpyDeviceToHost, s);
 }
 
 // ---------------------------------------------------------------- single-layer attention

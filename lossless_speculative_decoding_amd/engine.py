@@ -135,8 +135,11 @@ class Engine:
     temperature = None  # greedy unless a temperature is given
 
     # the driver pins at most ~70 GiB of host memory per process; rows beyond the budget
-    # go to pageable memory (staged at roughly half the pinned PCIe rate)
+    # go to pageable memory, which no copy engine touches: they move one layer at a time
+    # through a pinned pair of one-layer buffers (host memcpy on one side, a pinned copy on
+    # the other), outside the budget and at most BOUNCE_MAX bytes
     PINNED_BUDGET = 69_000_000_000
+    BOUNCE_MAX = 1_200_000_000
 
     def __init__(self, model: B.Model, spec, chunk: int = 1024, device="cuda", pinned_budget: int | None = None,
                  record: bool = False, temperature: float | None = None, seed: int = 0):
@@ -171,6 +174,7 @@ class Engine:
         self.pinned_used = 0
         self.pageable_stream = None
         self.stager = None
+        self.bounce = None             # (K, V) pinned one-layer buffers for pageable host rows
 
     # ------------------------------------------------------------ setup (untimed)
     def add_request(self, prompt: torch.Tensor, x: int, n_tokens: int, keep_prefill_kv: bool = False):
@@ -207,6 +211,8 @@ class Engine:
         buf = B.HostBuffer if r.pinned else B.PageableBuffer
         r.full_k = buf(nbytes)
         r.full_v = buf(nbytes)
+        if not r.pinned:
+            self._bounce(nbytes // L)
         tail_cap = n_tokens + x + 2
         r.tail_k = torch.empty(L, Hkv, tail_cap, D, dtype=self.dt, device=self.device)
         r.tail_v = torch.empty_like(r.tail_k)
@@ -224,11 +230,16 @@ class Engine:
             B.debug_register(r.probs)
         B.debug_register(r.rows, r.tail_k, r.tail_v, r.vtail_k, r.vtail_v, r.verified, r.result)
         r.req = Req(comp=r.comp.data_ptr(), cd=None, tail_k=r.tail_k.data_ptr(), tail_v=r.tail_v.data_ptr(),
-                    tail_cap=tail_cap, n_tail=0, ctx_len=T, draft_idx=0, full_k_host=r.full_k.data_ptr(),
-                    full_v_host=r.full_v.data_ptr(), full_cap=full_cap, rows=r.rows.data_ptr())
+                    tail_cap=tail_cap, n_tail=0, ctx_len=T, draft_idx=0,
+                    full_k_host=r.full_k.data_ptr() if r.pinned else None,
+                    full_v_host=r.full_v.data_ptr() if r.pinned else None, full_cap=full_cap,
+                    rows=r.rows.data_ptr())
         import ctypes as C
         r.req.cd = C.pointer(r.cd)
-        self.m.offload(r.req, kd, vd, T)
+        if r.pinned:
+            self.m.offload(r.req, kd, vd, T)
+        else:
+            self._offload_pageable(r, kd, vd, T)
         runtime.RT.synchronize()
         r.emitted = [int(g0.item())]
         if r.emitted[0] < 0:
@@ -492,22 +503,70 @@ class Engine:
                     r.stage_ev = ev
                 else:
                     r.stage_ev = None
-                    r.stage_fut = self._stage_pageable(Req.from_buffer_copy(r.req), sk, sv)
+                    r.stage_fut = self._stage_pageable(r, sk, sv)
                 return True
         return False
 
-    def _stage_pageable(self, req: Req, sk, sv):
-        """Copy from pageable memory on a worker thread (the call blocks until the
-        runtime has moved the data; ctypes releases the GIL meanwhile)."""
+    # ------------------------------------------------------------ pageable host rows
+    def _bounce(self, layer_bytes: int):
+        """The pinned (K, V) pair of one-layer buffers, grown to layer_bytes if needed."""
+        if self.bounce is not None and self.bounce[0].nbytes >= layer_bytes:
+            return self.bounce
+        if 2 * layer_bytes > self.BOUNCE_MAX:
+            raise ValueError(f"a layer of host rows ({layer_bytes} B) exceeds the pinned staging pair")
+        if self.bounce is not None:
+            runtime.RT.synchronize()
+            if self.pageable_stream is not None:
+                self.pageable_stream.synchronize()
+            for b in self.bounce:
+                b.free()
+        self.bounce = (B.HostBuffer(layer_bytes), B.HostBuffer(layer_bytes))
+        return self.bounce
+
+    @staticmethod
+    def _layer_req(r: Request, bk, bv, l: int, lb: int) -> Req:
+        """r's request with host arrays placed so that layer l lies in the pinned pair (the
+        library touches only the layers it is given)."""
+        q = Req.from_buffer_copy(r.req)
+        q.full_k_host = bk.data_ptr() - l * lb
+        q.full_v_host = bv.data_ptr() - l * lb
+        return q
+
+    def _offload_pageable(self, r: Request, kd, vd, T: int):
+        """Offload into pageable memory one layer at a time: the library copies layer l into
+        the pinned pair, the host copies it on into the pageable store."""
+        L = self.shape.n_layers
+        lb = r.full_k.nbytes // L
+        bk, bv = self.bounce
+        for l in range(L):
+            self.m.offload(self._layer_req(r, bk, bv, l, lb), kd, vd, T, l, l + 1)
+            runtime.RT.synchronize()
+            if not runtime.RT.dry:
+                r.full_k.t[l * lb:(l + 1) * lb].copy_(bk.tensor()[:lb])
+                r.full_v.t[l * lb:(l + 1) * lb].copy_(bv.tensor()[:lb])
+
+    def _stage_pageable(self, r: Request, sk, sv):
+        """Stage from pageable memory on a worker thread: per layer, a host copy into the
+        pinned pair, then the library's pinned copy into the slot; the pair is reused once
+        that copy has completed."""
         if self.stager is None:
             self.stager = cf.ThreadPoolExecutor(max_workers=1)
             self.pageable_stream = runtime.RT.Stream(device=self.device)
         st = self.pageable_stream
+        L = self.shape.n_layers
+        lb = r.full_k.nbytes // L
+        bk, bv = self.bounce
 
         def work():
-            self.m.stage(req, sk, sv, 0, self.shape.n_layers, copy_stream=st)
             ev = runtime.RT.Event()
-            ev.record(st)
+            for l in range(L):
+                if not runtime.RT.dry:
+                    bk.tensor()[:lb].copy_(r.full_k.t[l * lb:(l + 1) * lb])
+                    bv.tensor()[:lb].copy_(r.full_v.t[l * lb:(l + 1) * lb])
+                self.m.stage(self._layer_req(r, bk, bv, l, lb), sk, sv, l, l + 1, copy_stream=st)
+                ev = runtime.RT.Event()
+                ev.record(st)
+                ev.synchronize()
             return ev
 
         return self.stager.submit(work)
@@ -520,11 +579,20 @@ class Engine:
 
     def release_host(self):
         """Free every request's host buffers (after decoding)."""
+        if self.stager is not None:
+            self.stager.shutdown(wait=True)
+            self.stager = None
+        if self.pageable_stream is not None:
+            self.pageable_stream.synchronize()
         for r in self.reqs:
             for b in (r.full_k, r.full_v):
                 if b is not None:
                     b.free()
             r.full_k = r.full_v = None
+        if self.bounce is not None:
+            for b in self.bounce:
+                b.free()
+            self.bounce = None
         self.pinned_used = 0
 
     def _verify(self, r: Request, cs):
@@ -659,11 +727,17 @@ def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tenso
     runtime.RT.synchronize()
     t0 = time.perf_counter()
     layer_ev = [runtime.RT.Event() for _ in range(L)]
+    committed = None
     for _ in range(n_steps):
         if layered:
             for l in range(L):
                 model.stage(req, sk, sv, l, l + 1, copy_stream=copy_stream)
                 layer_ev[l].record(copy_stream)
+            # the verification writes its new rows into vk / vv in each layer's projections,
+            # before that layer waits for its staged rows: it must not start while the previous
+            # step's commit still copies them out
+            if committed is not None:
+                cs.wait_event(committed)
             model.verify_layered_raw(req, sk.data_ptr(), sv.data_ptr(), cap, rows.data_ptr(), 1, rows.data_ptr(),
                                      vk.data_ptr(), vv.data_ptr(), 1, ws, layer_ev)
         else:
@@ -676,6 +750,8 @@ def greedy_from_host(model: B.Model, prompt_kv, T: int, first_token: torch.Tenso
         done = runtime.RT.Event()
         done.record(cs)
         model.commit(req, 0, vk, vv, after_event=done, copy_stream=copy_stream)
+        committed = runtime.RT.Event()
+        committed.record(copy_stream)
         toks.append(rows.clone())
     runtime.RT.synchronize()
     copy_stream.synchronize()

@@ -246,3 +246,24 @@ def test_full_kv_from_host_equals_resident_greedy(setup, layered):
     toks, secs = greedy_from_host(m, (kd, vd), T, first, 16, ws, torch.cuda.Stream(), layered=layered)
     log(f"full KV from host ({'layered' if layered else 'whole'} staging): 16 tokens in {secs * 1e3:.1f} ms")
     assert toks == setup["g_toks"][1:17]
+
+
+@pytest.mark.parametrize("spec", [CompressSpec("tokdrop", keep_recent=64, ratio=4, obs_window=32),
+                                  CompressSpec("quant", bits=3, group=128)], ids=["tokdrop", "q3g128"])
+def test_pageable_host_rows_equal_pinned(setup, spec):
+    """Host rows beyond the pinned budget stay in pageable memory, which no copy engine touches:
+    the offload and every staging move them one layer at a time through a pinned pair of
+    one-layer buffers.  A run with the request's rows there emits the same tokens and accept
+    counts as a run with them pinned, and its tokens equal greedy decoding's."""
+    from lossless_speculative_decoding_amd.engine import Engine
+    res = []
+    for budget in (None, 0):
+        eng = Engine(setup["m"], spec, chunk=256, pinned_budget=budget)
+        r = eng.add_request(setup["prompt"], X, N)
+        assert r.pinned == (budget is None)
+        eng.run()
+        res.append((list(r.emitted), list(r.accepts)))
+        eng.release_host()
+    log(spec.kind, "pageable host rows: accepts", res[1][1])
+    assert res[0] == res[1]
+    assert res[1][0] == setup["g_toks"]

@@ -110,7 +110,12 @@ typedef struct {
 typedef struct vc_model vc_model;
 
 /* Validates shapes, copies the descriptor and pointers, and builds the RoPE
- * cos/sin table (angles in float64, stored float32).  Synchronises `s`. */
+ * cos/sin table (angles in float64, stored float32).  For bf16 models it also
+ * keeps a copy of w_qkv, w_o, w_gu, w_down and lm_head in a fragment-major
+ * layout (1 KB tiles of 16 rows x 32 columns in the order the weight-streaming
+ * GEMMs of draft steps and verification read them; as much device memory as
+ * those weights), so those weights must hold their final values when the model
+ * is created; prefill reads the caller's row-major weights.  Synchronises `s`. */
 vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStream_t s, vc_model** out);
 vc_status vc_model_destroy(vc_model* m);
 

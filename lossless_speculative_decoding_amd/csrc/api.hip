@@ -108,6 +108,10 @@ struct vc_model {
   vc_weights w;
   float* rope;  // [max_pos][D/2][2]
   int eb;       // bytes per activation / weight element
+  // bf16: fragment-major copies of the projection and LM-head weights for the skinny GEMMs
+  // (pack_weights), in one allocation; null for fp32 models
+  void* wp_mem;
+  const void *wp_qkv, *wp_o, *wp_gu, *wp_down, *wp_lm;
 };
 
 namespace {
@@ -205,11 +209,11 @@ WsLayout ws_layout(const vc_model* m, int R, int max_keys) {
 }
 
 // One projection + epilogue.
-vc_status proj(const vc_model* m, const void* X, const void* W, int M, int N, int K, float* P, EpiArgs e,
-               hipStream_t s) {
+vc_status proj(const vc_model* m, const void* X, const void* W, const void* Wp, int M, int N, int K, float* P,
+               EpiArgs e, hipStream_t s) {
   const int S = gemm_splits(M, N, K, m->d.dtype);
   const ProfRec pr = prof_gemm(M, N, K, S, m->d.dtype);
-  vc_status st = gemm(X, W, P, M, N, K, S, m->d.dtype, s, pr.a, pr.b);
+  vc_status st = gemm(X, W, P, M, N, K, S, m->d.dtype, s, pr.a, pr.b, Wp);
   if (st) return st;
   prof_commit(pr);
   e.P = P;
@@ -222,6 +226,7 @@ vc_status proj(const vc_model* m, const void* X, const void* W, int M, int N, in
 
 struct LayerPtrs {
   const uint8_t *wqkv, *wo, *wgu, *wdown, *g1, *g2;
+  const uint8_t *pqkv, *po, *pgu, *pdown;  // packed copies (null for fp32 models)
 };
 LayerPtrs layer_ptrs(const vc_model* m, int l) {
   const vc_model_desc& d = m->d;
@@ -234,6 +239,11 @@ LayerPtrs layer_ptrs(const vc_model* m, int l) {
   p.wdown = cptr(m->w.w_down, l * dm * d.ffn * eb);
   p.g1 = cptr(m->w.norm_attn, l * dm * eb);
   p.g2 = cptr(m->w.norm_ffn, l * dm * eb);
+  const bool pk = m->wp_mem != nullptr;
+  p.pqkv = pk ? cptr(m->wp_qkv, l * n_qkv(d) * dm * eb) : nullptr;
+  p.po = pk ? cptr(m->wp_o, l * dm * hd * eb) : nullptr;
+  p.pgu = pk ? cptr(m->wp_gu, l * 2 * int64_t(d.ffn) * dm * eb) : nullptr;
+  p.pdown = pk ? cptr(m->wp_down, l * dm * d.ffn * eb) : nullptr;
   return p;
 }
 
@@ -261,21 +271,21 @@ vc_status forward_layers(const vc_model* m, int M, uint8_t* ws, const WsLayout& 
     e.Hkv = d.n_kv_heads;
     e.D = d.head_dim;
     if ((st = set_kv(l, e))) return st;
-    if ((st = proj(m, a, lp.wqkv, M, int(n_qkv(d)), d.d_model, P, e, s))) return st;
+    if ((st = proj(m, a, lp.wqkv, lp.pqkv, M, int(n_qkv(d)), d.d_model, P, e, s))) return st;
     if ((st = attend(l, q, o, reinterpret_cast<float*>(ws + L.att)))) return st;
     EpiArgs r{};
     r.mode = EPI_RESID;
     r.out = h;
-    if ((st = proj(m, o, lp.wo, M, d.d_model, hd, P, r, s))) return st;
+    if ((st = proj(m, o, lp.wo, lp.po, M, d.d_model, hd, P, r, s))) return st;
     if ((st = k_rmsnorm(h, lp.g2, a, M, d.d_model, d.eps, d.dtype, s))) return st;
     EpiArgs g{};
     g.mode = EPI_SWIGLU;
     g.out = mb;
-    if ((st = proj(m, a, lp.wgu, M, 2 * d.ffn, d.d_model, P, g, s))) return st;
+    if ((st = proj(m, a, lp.wgu, lp.pgu, M, 2 * d.ffn, d.d_model, P, g, s))) return st;
     EpiArgs r2{};
     r2.mode = EPI_RESID;
     r2.out = h;
-    if ((st = proj(m, mb, lp.wdown, M, d.d_model, d.ffn, P, r2, s))) return st;
+    if ((st = proj(m, mb, lp.wdown, lp.pdown, M, d.d_model, d.ffn, P, r2, s))) return st;
   }
   return VC_OK;
 }
@@ -291,7 +301,7 @@ vc_status head(const vc_model* m, int r0, int M, uint8_t* ws, const WsLayout& L,
   float* P = reinterpret_cast<float*>(ws + L.y);
   if ((st = k_rmsnorm(hrow, m->w.norm_final, a, M, d.d_model, d.eps, d.dtype, s))) return st;
   const ProfRec pr = prof_gemm(M, d.vocab, d.d_model, 1, d.dtype);
-  if ((st = gemm(a, m->w.lm_head, P, M, d.vocab, d.d_model, 1, d.dtype, s, pr.a, pr.b))) return st;
+  if ((st = gemm(a, m->w.lm_head, P, M, d.vocab, d.d_model, 1, d.dtype, s, pr.a, pr.b, m->wp_lm))) return st;
   prof_commit(pr);
   if (smp) {
     SampleRow rows[SAMPLE_MAX_ROWS];
@@ -594,10 +604,32 @@ vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStr
     return st;
   }
   m->rope = static_cast<float*>(rope);
+  m->wp_mem = nullptr;
+  m->wp_qkv = m->wp_o = m->wp_gu = m->wp_down = m->wp_lm = nullptr;
   vc_status st = k_rope_table(m->rope, d.max_pos, d.head_dim, double(d.rope_theta), s);
+  if (st == VC_OK && d.dtype == VC_BF16) {
+    // fragment-major copies for the skinny GEMMs (decode and verification); prefill chunks read
+    // the caller's row-major weights through the GEMM library
+    const int64_t L = d.n_layers, dm = d.d_model, hd = int64_t(d.n_q_heads) * d.head_dim;
+    const int64_t rows[5] = {L * n_qkv(d), L * dm, L * 2 * int64_t(d.ffn), L * dm, d.vocab};
+    const int64_t cols[5] = {dm, hd, dm, d.ffn, dm};
+    const void* src[5] = {w->w_qkv, w->w_o, w->w_gu, w->w_down, w->lm_head};
+    int64_t total = 0;
+    for (int i = 0; i < 5; i++) total += rows[i] * cols[i] * 2;
+    st = dev_alloc(&m->wp_mem, size_t(total));
+    const void** dst[5] = {&m->wp_qkv, &m->wp_o, &m->wp_gu, &m->wp_down, &m->wp_lm};
+    int64_t off = 0;
+    for (int i = 0; i < 5 && st == VC_OK; i++) {
+      void* p = mptr(m->wp_mem, off);
+      st = pack_weights(src[i], p, rows[i], int(cols[i]), s);
+      *dst[i] = p;
+      off += rows[i] * cols[i] * 2;
+    }
+  }
   if (st == VC_OK && !dbg_dry() && hipStreamSynchronize(s) != hipSuccess) st = VC_ERR_HIP;
   if (st) {
     dev_free(m->rope);
+    if (m->wp_mem) dev_free(m->wp_mem);
     delete m;
     return st;
   }
@@ -608,6 +640,7 @@ vc_status vc_model_create(const vc_model_desc* desc, const vc_weights* w, hipStr
 vc_status vc_model_destroy(vc_model* m) {
   if (!m) return VC_OK;
   dev_free(m->rope);
+  if (m->wp_mem) dev_free(m->wp_mem);
   delete m;
   return VC_OK;
 }

@@ -14,8 +14,12 @@ int gemm_splits(int M, int N, int K, int dtype);
 // Partials for M <= 64 (decode / verify): weight-streaming bf16 MFMA kernel or fp32 VALU kernel.
 // Larger M (prefill chunks) uses the tiled bf16 MFMA kernel with S = 1.
 // ev_start / ev_stop (optional) are recorded at the kernel's own start and end.
+// Wp (optional): W in the fragment-major layout of pack_weights, used by the skinny bf16 kernel.
 vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int S, int dtype, hipStream_t s,
-               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr, const void* Wp = nullptr);
+// Fragment-major copy of the bf16 matrix (or stack of matrices) W [N][K] into Wp (same size):
+// 1 KB tiles of 16 rows x 32 columns, each in the lane order of the skinny kernel's loads.
+vc_status pack_weights(const void* W, void* Wp, int64_t N, int K, hipStream_t s);
 
 enum EpiMode { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_COPY = 3 };
 

@@ -28,6 +28,9 @@ constexpr int SK_NB = 64;
 constexpr int SK_KC = 256;
 constexpr int SK_XP = SK_KC + 8;
 
+// PACKED: W in the fragment-major layout of pack_weights (each wave's 16 B per lane weight loads
+// read one contiguous 1 KB tile); otherwise row-major [N][K].  Same MFMAs in the same order.
+template <bool PACKED>
 __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                         float* __restrict__ P, int M, int N, int K, int kps) {
   __shared__ __attribute__((aligned(16))) uint16_t Xs[64 * SK_XP];
@@ -40,7 +43,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restri
   f32x4 acc[4];
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4{0, 0, 0, 0};
-  const uint16_t* wrow = W + int64_t(n0 + r) * K;
+  const uint16_t* wrow = PACKED ? W + int64_t(n0 >> 4) * (K >> 5) * 512 + 8 * lane : W + int64_t(n0 + r) * K;
 
   u32x4 wf[2][4];
   auto load_w = [&](int kc) {
@@ -49,8 +52,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restri
     for (int h = 0; h < 2; h++) {
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        wf[h][e] = (128 * h < klen) ? *reinterpret_cast<const u32x4*>(wrow + kc + 128 * h + 32 * e + 8 * g)
-                                    : u32x4{0, 0, 0, 0};
+        const uint16_t* src = PACKED ? wrow + int64_t((kc + 128 * h + 32 * e) >> 5) * 512
+                                     : wrow + kc + 128 * h + 32 * e + 8 * g;
+        wf[h][e] = (128 * h < klen) ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -95,6 +99,23 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restri
       if (m < M) P[(int64_t(s) * M + m) * N + n0 + r] = acc[mt][jj];
     }
   }
+}
+
+// Fragment-major copy of a row-major bf16 matrix [N][K] (N % 16 == 0, K % 32 == 0): the 16 x 32
+// block (16-row block nb, 32-column block kb) is 1 KB at element (nb (K / 32) + kb) 512, in the
+// order the skinny kernel's lanes read it: lane l = r + 16 g holds row 16 nb + r, columns
+// 32 kb + 8 g .. + 8.  Thread = one 16-byte chunk of the output.
+__global__ void pack_weights_kernel(const uint16_t* __restrict__ W, uint16_t* __restrict__ Wp, int64_t n_chunks,
+                                    int K) {
+  const int64_t o = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (o >= n_chunks) return;
+  const int64_t kbs = K >> 5;
+  const int lane = int(o & 63);
+  const int64_t t = o >> 6;  // tile index nb * kbs + kb
+  const int64_t nb = t / kbs, kb = t - nb * kbs;
+  const int r = lane & 15, g = lane >> 4;
+  *reinterpret_cast<u32x4*>(Wp + 8 * o) =
+      *reinterpret_cast<const u32x4*>(W + (16 * nb + r) * int64_t(K) + 32 * kb + 8 * g);
 }
 
 constexpr int BG_P = 40;  // LDS pitch (bf16) of a 32-wide k slice
@@ -368,13 +389,24 @@ int gemm_splits(int M, int N, int K, int dtype) {
   return int(cdiv(K, kps));
 }
 
+vc_status pack_weights(const void* W, void* Wp, int64_t N, int K, hipStream_t s) {
+  VC_REQUIRE(N % 16 == 0 && K % 32 == 0, VC_ERR_ARG, "pack_weights: %lld x %d not 16 x 32 blocks", (long long)N, K);
+  const int64_t n_chunks = N * K / 8;
+  VC_DBG_LAUNCH("pack_weights", {"weights", W, N * K * 2}, {"packed weights", Wp, N * K * 2});
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(unsigned(cdiv(n_chunks, 256))), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(Wp), n_chunks, K);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+
 vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int S, int dtype, hipStream_t s,
-               hipEvent_t ev_start, hipEvent_t ev_stop) {
+               hipEvent_t ev_start, hipEvent_t ev_stop, const void* Wp) {
   VC_REQUIRE(M > 0 && N > 0 && K > 0, VC_ERR_ARG, "gemm: bad shape %d x %d x %d", M, N, K);
+  const bool packed = Wp != nullptr && dtype == VC_BF16 && M <= 64;
   {
     const int64_t eb = dtype == VC_BF16 ? 2 : 4;
     const int64_t parts = (dtype == VC_BF16 && M <= 64) ? S : 1;  // split-K partials of the skinny kernel
-    VC_DBG_LAUNCH("gemm", {"activations", X, int64_t(M) * K * eb}, {"weights", W, int64_t(N) * K * eb},
+    VC_DBG_LAUNCH("gemm", {"activations", X, int64_t(M) * K * eb}, {"weights", packed ? Wp : W, int64_t(N) * K * eb},
                   {"partials", P, parts * M * N * 4});
   }
   if (dtype == VC_BF16) {
@@ -384,8 +416,12 @@ vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int 
       const int want = S;
       const int kps = int(cdiv(cdiv(K, want), 128) * 128);
       VC_REQUIRE(cdiv(K, kps) == S, VC_ERR_ARG, "gemm: split count %d inconsistent", S);
-      hipExtLaunchKernelGGL(gemm_skinny_bf16, dim3(N / SK_NB, S), dim3(256), 0, s, ev_start, ev_stop, 0,
-                            static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K, kps);
+      if (packed)
+        hipExtLaunchKernelGGL(gemm_skinny_bf16<true>, dim3(N / SK_NB, S), dim3(256), 0, s, ev_start, ev_stop, 0,
+                              static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wp), P, M, N, K, kps);
+      else
+        hipExtLaunchKernelGGL(gemm_skinny_bf16<false>, dim3(N / SK_NB, S), dim3(256), 0, s, ev_start, ev_stop, 0,
+                              static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K, kps);
     } else {
       VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: prefill tiles use one split");
       bool served = false;

@@ -418,6 +418,7 @@ def run_model_workload(args) -> dict:
     vprof = vc.profile_read(vc.VC_PROF_VERIFY_ATTN)
     emitted = eng.emitted_total() - e0
     mean_draft_batch = (eng.drafted - d0) / max(eng.draft_steps - ds0, 1)
+    drafted_timed = eng.drafted - d0
     staged, n_staged = eng.staged_bytes - sb0, eng.stagings - sn0
     tok_s = emitted / secs
     accepts = [a for r, n0 in zip(eng.reqs, a0) for a in r.accepts[n0:]]
@@ -586,7 +587,7 @@ def run_model_workload(args) -> dict:
                       "plain_rounds": args.plain_rounds if args.adaptive and args.fallback_after else None,
                       "plain_round_share": round(sum(1 for r in eng.reqs for g in r.x_hist if g == 0) /
                                                  max(sum(len(r.x_hist) for r in eng.reqs), 1), 4),
-                      "drafts_per_round": round((eng.drafted - d0) / max(len(accepts), 1), 2),
+                      "drafts_per_round": round(drafted_timed / max(len(accepts), 1), 2),
                       "mean_requests_per_draft_step": round(mean_draft_batch, 2)},
         "whole_decode": None if args.no_whole_decode else {"tokens_per_s": round(dec_tokens / dec_secs, 3), "tokens": dec_tokens,
                          "seconds": round(dec_secs, 2), "rounds": len(dec_accepts),

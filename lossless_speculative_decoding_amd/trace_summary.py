@@ -22,6 +22,22 @@ import glob
 import json
 
 
+def short_name(name: str) -> str:
+    """The kernel's name without namespaces, return type and argument list (template arguments
+    kept); library kernels from other projects cut to 90 characters."""
+    n = name.replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    depth = 0
+    for i, ch in enumerate(n):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            n = n[:i]
+            break
+    return n.replace("vc::", "")[:90]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("trace_dir")
@@ -40,7 +56,7 @@ def main():
     rows.sort()
     tot = collections.defaultdict(lambda: [0, 0])
     for _, name, dur in rows:
-        t = tot[name.split("(")[0].replace("void ", "")[:90]]
+        t = tot[short_name(name)]
         t[0] += 1
         t[1] += dur
     all_ns = sum(v[1] for v in tot.values())

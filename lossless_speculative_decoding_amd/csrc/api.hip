@@ -259,10 +259,22 @@ vc_status forward_layers(const vc_model* m, int M, uint8_t* ws, const WsLayout& 
   void* o = ws + L.o;
   void* mb = ws + L.m;
   const int hd = d.n_q_heads * d.head_dim;
+  // weight-streaming rows: a residual projection and the RMSNorm after it run as the GEMM plus one
+  // fused residual-and-norm launch (bitwise the epilogue and rmsnorm kernels' results)
+  const bool fuse_norm = d.dtype == VC_BF16 && M <= 64 && resid_rmsnorm_ok(d.d_model, d.dtype);
+  auto resid_norm = [&](const void* X, const void* W, const void* Wp, int K, const void* gain) -> vc_status {
+    const int S = gemm_splits(M, d.d_model, K, d.dtype);
+    const ProfRec pr = prof_gemm(M, d.d_model, K, S, d.dtype);
+    if (vc_status st1 = gemm(X, W, P, M, d.d_model, K, S, d.dtype, s, pr.a, pr.b, Wp)) return st1;
+    prof_commit(pr);
+    return k_resid_rmsnorm(P, S, h, gain, a, M, d.d_model, d.eps, d.dtype, s);
+  };
   vc_status st;
   for (int l = 0; l < d.n_layers; l++) {
     const LayerPtrs lp = layer_ptrs(m, l);
-    if ((st = k_rmsnorm(h, lp.g1, a, M, d.d_model, d.eps, d.dtype, s))) return st;
+    if (l == 0 || !fuse_norm) {  // otherwise the previous layer's last projection normalised h already
+      if ((st = k_rmsnorm(h, lp.g1, a, M, d.d_model, d.eps, d.dtype, s))) return st;
+    }
     EpiArgs e = qkv_tmpl;
     e.mode = EPI_QKV;
     e.q_out = q;
@@ -273,19 +285,27 @@ vc_status forward_layers(const vc_model* m, int M, uint8_t* ws, const WsLayout& 
     if ((st = set_kv(l, e))) return st;
     if ((st = proj(m, a, lp.wqkv, lp.pqkv, M, int(n_qkv(d)), d.d_model, P, e, s))) return st;
     if ((st = attend(l, q, o, reinterpret_cast<float*>(ws + L.att)))) return st;
-    EpiArgs r{};
-    r.mode = EPI_RESID;
-    r.out = h;
-    if ((st = proj(m, o, lp.wo, lp.po, M, d.d_model, hd, P, r, s))) return st;
-    if ((st = k_rmsnorm(h, lp.g2, a, M, d.d_model, d.eps, d.dtype, s))) return st;
+    if (fuse_norm) {
+      if ((st = resid_norm(o, lp.wo, lp.po, hd, lp.g2))) return st;
+    } else {
+      EpiArgs r{};
+      r.mode = EPI_RESID;
+      r.out = h;
+      if ((st = proj(m, o, lp.wo, lp.po, M, d.d_model, hd, P, r, s))) return st;
+      if ((st = k_rmsnorm(h, lp.g2, a, M, d.d_model, d.eps, d.dtype, s))) return st;
+    }
     EpiArgs g{};
     g.mode = EPI_SWIGLU;
     g.out = mb;
     if ((st = proj(m, a, lp.wgu, lp.pgu, M, 2 * d.ffn, d.d_model, P, g, s))) return st;
-    EpiArgs r2{};
-    r2.mode = EPI_RESID;
-    r2.out = h;
-    if ((st = proj(m, mb, lp.wdown, lp.pdown, M, d.d_model, d.ffn, P, r2, s))) return st;
+    if (fuse_norm && l + 1 < d.n_layers) {  // the next layer's input norm
+      if ((st = resid_norm(mb, lp.wdown, lp.pdown, d.ffn, layer_ptrs(m, l + 1).g1))) return st;
+    } else {
+      EpiArgs r2{};
+      r2.mode = EPI_RESID;
+      r2.out = h;
+      if ((st = proj(m, mb, lp.wdown, lp.pdown, M, d.d_model, d.ffn, P, r2, s))) return st;
+    }
   }
   return VC_OK;
 }

@@ -99,6 +99,81 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
   }
 }
 
+// The residual step of a projection and the RMSNorm that follows it, one workgroup per row (bf16,
+// d a multiple of 2048): h[r] += sum over the S split-K partials P[s][r] (summed in ascending s,
+// then added and rounded to bf16, as the projection's residual epilogue does), then
+// y[r] = rmsnorm(h[r]) * g with the reduction of rmsnorm_kernel.  Both results equal the two
+// kernels' bit for bit; the new row is stored and normalised from registers.
+__global__ __launch_bounds__(256) void resid_rmsnorm_kernel(const float* __restrict__ P, int S, int M, void* h,
+                                                            const void* g, void* y, int d, float eps) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t base = int64_t(r) * d;
+  const int64_t pst = int64_t(M) * d;  // between the partials of consecutive splits
+  u32x4* hr = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(h) + base);
+  u32x4 xv[RMS_MAXC];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < RMS_MAXC; i++) {
+    if (i < d / 2048) {
+      const int c0 = 8 * (tid + 256 * i);
+      const f32x4* p = reinterpret_cast<const f32x4*>(P + base + c0);
+      f32x4 a = p[0], b = p[1];
+      // the partials of up to eight splits are loaded together, then added in ascending order
+      for (int s0 = 1; s0 < S; s0 += 8) {
+        f32x4 ta[8], tb[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          if (s0 + k < S) {
+            const f32x4* q = reinterpret_cast<const f32x4*>(P + (s0 + k) * pst + base + c0);
+            ta[k] = q[0];
+            tb[k] = q[1];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          if (s0 + k < S) {
+            a += ta[k];
+            b += tb[k];
+          }
+        }
+      }
+      const u32x4 hv = hr[tid + 256 * i];
+      const uint32_t w[4] = {hv.x, hv.y, hv.z, hv.w};
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[e] = pack_bf2(lo_bf(w[e]) + v[2 * e], hi_bf(w[e]) + v[2 * e + 1]);
+      xv[i] = u32x4{o[0], o[1], o[2], o[3]};
+      hr[tid + 256 * i] = xv[i];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float x0 = lo_bf(o[e]), x1 = hi_bf(o[e]);
+        ss = fmaf(x0, x0, ss);
+        ss = fmaf(x1, x1, ss);
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.f / sqrtf(tot / float(d) + eps);
+  const u32x4* gr = reinterpret_cast<const u32x4*>(g);
+  u32x4* yr = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base);
+#pragma unroll
+  for (int i = 0; i < RMS_MAXC; i++) {
+    if (i < d / 2048) {
+      const u32x4 gv = gr[tid + 256 * i];
+      const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[e] = pack_bf2(lo_bf(w[e]) * inv * lo_bf(gw[e]), hi_bf(w[e]) * inv * hi_bf(gw[e]));
+      yr[tid + 256 * i] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+}
+
 // Greedy choice per row: the largest logit, ties to the lowest index; -1 when the row has no
 // finite maximum (every logit NaN, or all of them -inf), which no embedding row answers to.
 __global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V, int32_t* out) {
@@ -214,6 +289,16 @@ vc_status k_rmsnorm(const void* x, const void* g, void* y, int M, int d, float e
   VC_DBG_LAUNCH("rmsnorm", {"input", x, int64_t(M) * d * ebytes(dt)}, {"gain", g, int64_t(d) * ebytes(dt)},
                 {"output", y, int64_t(M) * d * ebytes(dt)});
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, g, y, d, eps, dt);
+  VC_LAUNCH_CHECK();
+  return VC_OK;
+}
+bool resid_rmsnorm_ok(int d, int dt) { return dt == VC_BF16 && d % 2048 == 0 && d <= 2048 * RMS_MAXC; }
+vc_status k_resid_rmsnorm(const float* P, int S, void* h, const void* g, void* y, int M, int d, float eps, int dt,
+                          hipStream_t s) {
+  VC_REQUIRE(resid_rmsnorm_ok(d, dt) && S >= 1, VC_ERR_UNSUPPORTED, "resid_rmsnorm: d=%d", d);
+  VC_DBG_LAUNCH("resid_rmsnorm", {"partials", P, int64_t(S) * M * d * 4}, {"residual", h, int64_t(M) * d * 2},
+                {"gain", g, int64_t(d) * 2}, {"output", y, int64_t(M) * d * 2});
+  hipLaunchKernelGGL(resid_rmsnorm_kernel, dim3(M), dim3(256), 0, s, P, S, M, h, g, y, d, eps);
   VC_LAUNCH_CHECK();
   return VC_OK;
 }

@@ -20,10 +20,10 @@ constexpr int D128 = 128;
 // online softmax; the four states are merged in wave order at the end (fixed order, so the
 // result does not depend on timing).  The G query heads of the KV head are the 16 MFMA
 // columns.  K goes from HBM straight into A fragments (lane l: key l%16 of a 16-key group,
-// channels 8(l/16)..+8 of a 32-channel chunk); V is converted to fp16 and transposed
-// through a 16 KB LDS tile per wave.  A wave issues the next tile's loads as soon as the
-// current tile's registers are consumed, so its softmax and P.V overlap the next fetch;
-// KV loads are non-temporal (every byte is read once).
+// channels 8(l/16)..+8 of a 32-channel chunk); V passes through a 16 KB LDS tile per wave,
+// stored as loaded and read back transposed (below).  A wave issues the next tile's loads as
+// soon as the current tile's registers are consumed, so its softmax and P.V overlap the next
+// fetch; KV loads are non-temporal (every byte is read once).
 // V tile layout: the wave's 64 keys as rows of 256 bytes (bf16, as in the cache); the eight
 // 32-byte chunks of row t (16 channels each) sit in the order chunk ^ (t & 7), so eight
 // consecutive rows put one channel chunk on eight different bank groups.  Lane (r16, g)

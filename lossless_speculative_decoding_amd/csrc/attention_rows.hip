@@ -349,6 +349,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int b = 0; b < NB; b++) sacc[b][kt] = mfma_bf16(ka, qf[B0 + b][c], sacc[b][kt]);
         }
       }
+      // the softmax phase at a raised wave priority, the MFMA phases at the normal one, so the two
+      // waves of a SIMD tend to alternate between them instead of meeting in the same phase
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int b = 0; b < NB; b++) {
         const float alpha = softmax(sacc[b], m_run[B0 + b], l_run[B0 + b], qr_lane + ATT_RB * (B0 + b), t0, full);
@@ -358,6 +361,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
       // ---- O^T += V^T P^T over 2 chunks of 32 keys, P as an fp16 hi/lo pair
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int kc = 0; kc < 2; kc++) {
         u32x4 pb[NB], pl[NB];

@@ -196,6 +196,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tn = t0 + DEC_WAVES * ATT_KT;
     if (tn < key_hi) dec_load(kr, vr, R.a, R.b, a_al, j, tn, off);
 
+    // softmax at a raised wave priority, P.V at the normal one: the two waves of a SIMD tend to
+    // alternate between the VALU and the MFMA phase
+    __builtin_amdgcn_s_setprio(1);
     // ---- mask, online softmax per head (column l % 16).  Scores stay unscaled until the
     // exponent: p = 2^(s * scale_log2 - m), one fma per key; m is kept in scaled (log2) units
     const bool full = t0 + ATT_KT <= key_hi && (t0 + ATT_KT <= a_vis_end || t0 >= a_al);  // uniform
@@ -242,6 +245,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // LDS operations of one wave complete in issue order; the fence keeps the compiler
     // from moving the fragment reads above the tile stores (and later stores above them).
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_s_setprio(0);
     // ---- O^T += V^T P^T over 2 chunks of 32 keys, P as a bf16 hi/lo pair
 #pragma unroll
     for (int kc = 0; kc < 2; kc++) {

@@ -31,6 +31,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 PCIE_PEAK_GBS = 63.0
+# prompt rows per prefill chunk: 8192 rows give every 8B projection a whole number of rounds of
+# 256 x 256 GEMM tiles over the 256 compute units (2048 rows leave half the GPU idle on 4096 columns)
+PREFILL_CHUNK = 8192
 PCIE_PINNED_GBS = 57.6  # pinned host-to-device rate measured on the box (4 GiB copy)  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
@@ -345,7 +348,7 @@ def run_model_workload(args) -> dict:
     W = make_weights(s, device=device)
     model = vc.Model(s, W, max_pos=max(ctx) + n_cap + 64)
     sampled = args.temperature is not None
-    eng = Engine(model, w.compress, chunk=2048, device=device, temperature=args.temperature, seed=args.seed)
+    eng = Engine(model, w.compress, chunk=PREFILL_CHUNK, device=device, temperature=args.temperature, seed=args.seed)
     prefill_prof = None
     for r, (T, x) in enumerate(zip(ctx, xs)):
         p = torch.empty(T, dtype=torch.int32, device=device)
@@ -566,9 +569,9 @@ def run_model_workload(args) -> dict:
         "gemm_decode": _rate(gprof, "hbm", f"projection and LM-head GEMMs of {len(live)}-request draft steps "
                                            "(weight streaming)"),
         "gemm_prefill": _rate(prefill_prof["gemm"], "mfma", f"projection GEMMs of request 0's prefill "
-                                                             f"({prefill_prof['tokens']} tokens, 2048-row chunks)"),
+                                                             f"({prefill_prof['tokens']} tokens, {PREFILL_CHUNK}-row chunks)"),
         "attention_prefill": _rate(prefill_prof["attention"], "mfma", "causal attention of request 0's prefill "
-                                                                      "(2048-row chunks)"),
+                                                                      f"({PREFILL_CHUNK}-row chunks)"),
         "pcie": {"bound": "pcie", "achieved": round(pcie_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                  "frac": round(pcie_gbs / PCIE_PEAK_GBS, 4), "stagings": n_staged,
                  "bytes_per_staging": round(staged / max(n_staged, 1)),
@@ -634,7 +637,7 @@ def run_remote_prefix(args) -> dict:
     torch.cuda.set_device(0)
     W = make_weights(s)
     model = vc.Model(s, W, max_pos=max(ctx) + n_tok + 64)
-    eng = Engine(model, w.compress, chunk=2048)
+    eng = Engine(model, w.compress, chunk=PREFILL_CHUNK)
     for r, (T, x) in enumerate(zip(ctx, xs)):
         p = torch.empty(T, dtype=torch.int32, device="cuda")
         vc.synth_ids(p, synth.S_PROMPT + r, s.vocab)

@@ -339,6 +339,19 @@ vc_status vc_prefill(vc_model* m, const int32_t* tokens, int32_t T, void* k_out,
                      void* q_obs, int32_t W, int32_t* g0_out, float* last_logits_opt, int32_t chunk, void* ws,
                      size_t ws_bytes, hipStream_t s);
 
+/* One projection of the model's linear layers (every GEMM of prefill, draft
+ * and verification; the model itself is the pre-norm decoder of the
+ * configurations, since the pages fix no architecture), in a single K range:
+ * y[M][N] (float32) = x[M][K] w[N][K]^T, the products of dtype elements summed
+ * in float32.  M > 64 runs the prefill kernel (256 x 256 MFMA tiles when N is a
+ * multiple of 256, else 128 x 128), M <= 64 the weight-streaming kernel of the
+ * decode steps.  dtype VC_BF16 needs K % 128 == 0 and N % 64 == 0 (M <= 64) or
+ * N % 128 == 0 (M > 64); VC_F32 takes any shape.  Row-major device buffers,
+ * caller-owned; y is overwritten.  VC_ERR_ARG for a non-positive size, a null
+ * pointer or another dtype, VC_ERR_UNSUPPORTED for a shape outside the above. */
+vc_status vc_linear(const void* x, const void* w, float* y, int32_t M, int32_t N, int32_t K, int32_t dtype,
+                    hipStream_t s);
+
 /* ------------------------------------------------------------------------
  * Sampled decoding ("VeriCache Guide: Lossless Inference with Lossy KV
  * Caches", "Mathematical Guarantee of Lossless Correctness"): drafts are drawn

@@ -117,6 +117,7 @@ _SIGS = {
     "vc_draft_step_sampled": (_I, [_P, C.POINTER(Req), _I, C.POINTER(Sampler), C.POINTER(_P), _P, _P, _S, _P]),
     "vc_spec_ws_size": (_I, [_I, C.POINTER(_S)]),
     "vc_spec_sample": (_I, [_I, _P, _P, _P, _I, C.POINTER(Sampler), C.c_int64, _P, _P, _S, _P]),
+    "vc_linear": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "vc_attn_ws_size": (_I, [C.POINTER(AttnDesc), _I, _I, _I, C.POINTER(_S)]),
     "vc_attn_draft": (_I, [C.POINTER(AttnDesc), C.POINTER(AttnDraftReq), _I, _P, _P, _P, _S, _P]),
     "vc_attn_verify": (_I, [C.POINTER(AttnDesc), _I, _P, C.POINTER(_P), C.POINTER(_P), _I, C.POINTER(_I),

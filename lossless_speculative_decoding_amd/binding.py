@@ -18,7 +18,7 @@ from ._vc import (VC_BF16, VC_F32, VC_PROF_DRAFT_ATTN, VC_PROF_GEMM_SKINNY, VC_P
                   VC_DRAW_ACCEPT, VC_DRAW_DRAFT, VC_DRAW_TARGET)
 
 __all__ = ["VC_BF16", "VC_F32", "VC_QUANT", "VC_TOKDROP", "VC_SCORE_ATTN", "VC_SCORE_KEYNORM", "CompressDesc", "Req", "Model", "compress_desc",
-           "compress_layout", "vc_compress", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
+           "compress_layout", "vc_compress", "vc_linear", "vc_attn_draft", "vc_attn_verify", "synth_xavier",
            "synth_normal_heads", "synth_ids", "synth_fill", "stream_handle", "torch_dtype", "elem_bytes",
            "profile_enable", "profile_read", "HostBuffer", "PageableBuffer", "VC_PROF_DRAFT_ATTN",
            "VC_PROF_VERIFY_ATTN", "VC_PROF_GEMM_SKINNY", "VC_PROF_GEMM_TILED", "VC_PROF_PREFILL_ATTN",
@@ -103,6 +103,18 @@ def vc_compress(d: CompressDesc, k: torch.Tensor, v: torch.Tensor, q_obs: torch.
     call("vc_compress", C.byref(d), ptr(k), ptr(v), ptr(q_obs), ptr(out), out.numel(), ptr(ws), ws.numel(),
          stream_handle())
     return out
+
+
+# ---------------------------------------------------------------- one projection GEMM
+def vc_linear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """y[M][N] float32 = x[M][K] w[N][K]^T (bf16 or float32 operands, float32 sums)."""
+    M, K = x.shape
+    N = w.shape[0]
+    assert w.shape == (N, K) and w.dtype == x.dtype and x.is_contiguous() and w.is_contiguous()
+    y = torch.empty(M, N, dtype=torch.float32, device=x.device)
+    dt = VC_BF16 if x.dtype == torch.bfloat16 else VC_F32
+    call("vc_linear", ptr(x), ptr(w), ptr(y), M, N, K, dt, stream_handle())
+    return y
 
 
 # ---------------------------------------------------------------- single-layer attention

@@ -1288,6 +1288,14 @@ vc_status vc_offload_layers(vc_model* m, const vc_req* req, const void* k_dev, c
 }
 
 // ---------------------------------------------------------------- single-layer attention
+vc_status vc_linear(const void* x, const void* w, float* y, int32_t M, int32_t N, int32_t K, int32_t dtype,
+                    hipStream_t s) {
+  VC_REQUIRE(x && w && y, VC_ERR_ARG, "vc_linear: null argument");
+  VC_REQUIRE(M > 0 && N > 0 && K > 0, VC_ERR_ARG, "vc_linear: bad shape %d x %d x %d", M, N, K);
+  VC_REQUIRE(dtype == VC_BF16 || dtype == VC_F32, VC_ERR_ARG, "vc_linear: bad dtype %d", dtype);
+  return gemm(x, w, y, M, N, K, 1, dtype, s);
+}
+
 vc_status vc_attn_ws_size(const vc_attn_desc* d, int32_t n, int32_t rows, int32_t max_keys, size_t* bytes) {
   VC_REQUIRE(d && bytes && n > 0 && rows > 0 && max_keys > 0, VC_ERR_ARG, "vc_attn_ws_size: bad arguments");
   const int64_t D2 = d->head_dim + 2;

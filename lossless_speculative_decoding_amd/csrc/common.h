@@ -42,6 +42,7 @@ static inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- vector types
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -104,6 +105,11 @@ __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m
 //           D lane l holds D[4*(l/16)+j][l%16].
 __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0, 0);
+}
+// 32x32x16: A lane l holds A[l%32][8*(l/32)+e]; B lane l holds B[8*(l/32)+e][l%32];
+//           D lane l holds D[8*(e/4)+4*(l/32)+e%4][l%32], e = 0..15.
+__device__ __forceinline__ f32x16 mfma32_bf16(const u32x4& a, const u32x4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_f16(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8>(a), bitcast<f16x8>(b), c, 0, 0, 0);

@@ -5,17 +5,11 @@
 // wave) and one K range; the activations of that range are staged in LDS
 // 256 columns at a time and every wave runs 16x16x32 bf16 MFMAs over all
 // M rows (padded to 16) while its next weight fragments are in flight.
-// Prefill chunks (M > 64) are plain bf16 GEMMs with float32 output and go to hipBLASLt
-// (one handle, a 32 MiB workspace and one algorithm per shape, kept per device for the
-// life of the process); gemm_big_bf16, a 128x128x32 LDS double-buffered MFMA tile, remains
-// for bf16 shapes the library does not serve.  The fp32 model uses a 16x16 tiled VALU
-// kernel whose outputs are single fma chains in ascending k.
-#include <hipblaslt/hipblaslt.h>
-
+// Prefill chunks (M > 64) are plain bf16 GEMMs with float32 output: gemm_tile256_bf16 (256 x 256
+// tiles, one wave per SIMD holding a 128 x 128 block) where N is a multiple of 256, else
+// gemm_big_bf16 (128 x 128 x 32 tiles).  The fp32 model uses a 16x16 tiled VALU kernel whose
+// outputs are single fma chains in ascending k.
 #include <algorithm>
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "bounds.h"
 #include "gemm.h"
@@ -186,6 +180,156 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(const uint16_t* __restrict_
   }
 }
 
+// Prefill tile: a 256 x 256 block of P from 4 waves in 2 x 2, each wave 128 x 128 (4 x 4
+// 32x32x16 MFMA tiles, 256 float accumulators per lane, one wave per SIMD).  k advances KS at a
+// time through a ring of NST LDS stages, each A [256][KS] and B [256][KS] bf16 (NST KS 1 KB in
+// all), filled by direct-to-LDS buffer loads (each wave instruction writes 1 KB of whole rows),
+// so the staging holds no registers; loads run NST - 1 stages ahead of the multiplies.  Per
+// stage one barrier, preceded by a wait for this wave's loads of the stage (the barrier then
+// publishes every wave's); the barrier carries no memory fence, which would wait for all loads
+// in flight.  In each LDS row the 16-byte chunks are XOR-swizzled by the row (each lane loads
+// the global chunk that belongs at its LDS slot) so that the rows one fragment read touches
+// fall in distinct banks.  X is read through a buffer resource that ends at row M, so rows of
+// the last tile past M load as zero and are never stored.
+constexpr int PT = 256;
+#ifndef GEMM_KS
+#define GEMM_KS 64  // k per LDS stage
+#define GEMM_NST 2  // stages in the ring
+#endif
+
+template <int KS>
+__device__ __forceinline__ int pt_swz(int row) {
+  if constexpr (KS == 64) return (row & 7) ^ ((row >> 3) & 1);
+  else return (row >> 2) & 3;
+}
+
+template <int KS, int NST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile256_bf16(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, float* __restrict__ P, int M, int N, int K) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int CPR = KS / 8;      // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CPR;    // rows one wave instruction fills
+  constexpr int NI = PT / RPI / 4; // instructions per wave, operand and stage
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NST][2][PT * KS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int MT = (M + PT - 1) / PT, NT = N / PT;
+  // XCD x (blocks x, x + 8, ...) takes an eighth of the tile grid, split along the longer side
+  // when that side divides by eight; inside it, bands of up to 8 row tiles, rows fastest, so
+  // the ~32 tiles resident on one XCD form a compact block that shares its A and B slabs.
+  int u = blockIdx.x, mt0 = 0, mt = MT, nt0 = 0, nt = NT;
+  if (MT % 8 == 0 && MT >= NT) {
+    mt = MT / 8; mt0 = (u & 7) * mt; u >>= 3;
+  } else if (NT % 8 == 0) {
+    nt = NT / 8; nt0 = (u & 7) * nt; u >>= 3;
+  }
+  const int g = min(mt, 8), band = u / (g * nt), bs = min(g, mt - band * g), rr = u - band * g * nt;
+  const int m0 = (mt0 + band * g + rr % bs) * PT, n0 = (nt0 + rr / bs) * PT;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X + int64_t(m0) * K), 0, min(M - m0, PT) * K * 2, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W + int64_t(n0) * K), 0, PT * K * 2, BUF_DWORD3);
+  // wave instruction i fills tile rows RPI (4 i + wave) .. + RPI; lane: row + lane / CPR, LDS chunk lane % CPR
+  const int lrow = RPI * wave + lane / CPR;
+  const int voff = lrow * K * 2 + 16 * ((lane % CPR) ^ pt_swz<KS>(lrow));
+  const int rstep = 4 * RPI * K * 2;
+  auto issue = [&](int k0, int buf) {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&lds[buf][0][RPI * (4 * i + wave) * KS], 16,
+                                               voff + i * rstep + 2 * k0, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&lds[buf][1][RPI * (4 * i + wave) * KS], 16,
+                                               voff + i * rstep + 2 * k0, 0, 0, 0);
+    }
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = f32x16{};
+  const int nk = K / KS;
+  const int lr32 = lane & 31, lh = lane >> 5;
+  u32x4 af[2][4], bf[2][4];
+  auto frags = [&](int buf, int s, int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int ra_ = 128 * wm + 32 * i + lr32, rb_ = 128 * wn + 32 * i + lr32;
+      af[slot][i] = *reinterpret_cast<const u32x4*>(&lds[buf][0][ra_ * KS + 8 * ((2 * s + lh) ^ pt_swz<KS>(ra_))]);
+      bf[slot][i] = *reinterpret_cast<const u32x4*>(&lds[buf][1][rb_ * KS + 8 * ((2 * s + lh) ^ pt_swz<KS>(rb_))]);
+    }
+  };
+  // MFMAs number e0 .. e1 - 1 of a step (e = 4 i + j: A block i, B block j)
+  auto mfmas = [&](int slot, int e0, int e1) {
+#pragma unroll
+    for (int e = e0; e < e1; e++) acc[e >> 2][e & 3] = mfma32_bf16(af[slot][e >> 2], bf[slot][e & 3], acc[e >> 2][e & 3]);
+  };
+  auto issue_one = [&](int k0, int buf, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&lds[buf][0][RPI * (4 * i + wave) * KS], 16,
+                                             voff + i * rstep + 2 * k0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&lds[buf][1][RPI * (4 * i + wave) * KS], 16,
+                                             voff + i * rstep + 2 * k0, 0, 0, 0);
+  };
+  constexpr int S = KS / 16;  // 32x32x16 steps per stage
+  static_assert(S % 2 == 0, "a stage's first step must use fragment slot 0");
+  // The ring holds NST stages.  At the barrier of stage kt every wave has its fragments of
+  // stage kt in registers (LDS reads waited for), so the buffer of stage kt is free and is
+  // refilled with stage kt + NST, its loads interleaved with the stage's last MFMAs.  Each
+  // step issues two MFMAs, then the LDS reads of the next step (the next stage's first step
+  // after the barrier), then its other fourteen MFMAs, so every fragment is read fourteen
+  // MFMAs before its first use; scheduling fences keep the compiler from pulling uses closer.
+  // Stages past the last reload the last one: every load is unconditional and in range, and
+  // each wave always has the same number in flight.
+#pragma unroll
+  for (int st = 0; st < NST; st++) issue(KS * min(st, nk - 1), st);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NST - 1)) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  frags(0, 0, 0);
+  for (int kt = 0; kt < nk; kt++) {
+    const int buf = kt % NST;
+#pragma unroll
+    for (int s = 0; s + 1 < S; s++) {
+      mfmas(s & 1, 0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      frags(buf, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s & 1, 2, 16);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * NI * (NST - 2)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    constexpr int L = (S - 1) & 1;
+    mfmas(L, 0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    frags((kt + 1) % NST, 0, S & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kn = KS * min(kt + NST, nk - 1);
+    // the other fourteen MFMAs with the NI load pairs spread over them
+#pragma unroll
+    for (int q = 0; q < NI; q++) {
+      issue_one(kn, buf, q);
+      mfmas(L, 2 + 14 * q / NI, 2 + 14 * (q + 1) / NI);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // no load may still be writing this workgroup's LDS when it ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // D element e of lane l: row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+      const int m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+      if (m >= M) continue;
+      float* prow = P + int64_t(m) * N + n0 + 128 * wn + lr32;
+#pragma unroll
+      for (int j = 0; j < 4; j++) prow[32 * j] = acc[i][j][e];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void gemm_f32_tiled(const float* __restrict__ X, const float* __restrict__ W,
                                                       float* __restrict__ P, int M, int N, int K) {
   __shared__ float Xs[16][17];
@@ -294,90 +438,6 @@ __global__ void epilogue_kernel(const EpiArgs a) {
 
 }  // namespace
 
-namespace {
-
-// hipBLASLt for the prefill projections: P[M][N] = X[M][K] W[N][K]^T in float32.  In its
-// column-major view this is C (N x M) = W^T-as-stored (op T of a K x N matrix) times X (K x M).
-// A shape's descriptors and the first algorithm of the heuristic are made once and kept, so a
-// shape's result does not change between calls and a call does no host-side set-up.
-struct LtShape {
-  hipblasLtMatmulDesc_t md = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
-  hipblasLtMatmulAlgo_t algo{};
-  bool served = false;
-};
-struct LtDevice {
-  hipblasLtHandle_t h = nullptr;
-  void* ws = nullptr;
-  std::map<std::tuple<int, int, int>, LtShape> shape;
-};
-constexpr size_t LT_WS_BYTES = size_t(32) << 20;
-std::mutex g_lt_mu;
-std::map<int, LtDevice> g_lt;
-
-#define VC_LT(x)                                                                        \
-  do {                                                                                  \
-    const hipblasStatus_t st_ = (x);                                                    \
-    VC_REQUIRE(st_ == HIPBLAS_STATUS_SUCCESS, VC_ERR_HIP, "%s failed: status %d", #x, int(st_)); \
-  } while (0)
-
-// Descriptors and algorithm of one shape; leaves sh.served false when the library offers none.
-vc_status lt_shape_init(LtDevice& L, LtShape& sh, int M, int N, int K) {
-  VC_LT(hipblasLtMatmulDescCreate(&sh.md, HIPBLAS_COMPUTE_32F, HIP_R_32F));
-  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-  VC_LT(hipblasLtMatmulDescSetAttribute(sh.md, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)));
-  VC_LT(hipblasLtMatmulDescSetAttribute(sh.md, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)));
-  VC_LT(hipblasLtMatrixLayoutCreate(&sh.la, HIP_R_16BF, K, N, K));
-  VC_LT(hipblasLtMatrixLayoutCreate(&sh.lb, HIP_R_16BF, K, M, K));
-  VC_LT(hipblasLtMatrixLayoutCreate(&sh.lc, HIP_R_32F, N, M, N));
-  hipblasLtMatmulPreference_t pref = nullptr;
-  VC_LT(hipblasLtMatmulPreferenceCreate(&pref));
-  size_t wsb = LT_WS_BYTES;
-  hipblasLtMatmulHeuristicResult_t res[1];
-  int nres = 0;
-  const hipblasStatus_t st1 =
-      hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb));
-  const hipblasStatus_t st2 = st1 == HIPBLAS_STATUS_SUCCESS
-                                  ? hipblasLtMatmulAlgoGetHeuristic(L.h, sh.md, sh.la, sh.lb, sh.lc, sh.lc, pref, 1, res, &nres)
-                                  : st1;
-  hipblasLtMatmulPreferenceDestroy(pref);
-  if (st2 == HIPBLAS_STATUS_SUCCESS && nres >= 1) {
-    sh.algo = res[0].algo;
-    sh.served = true;
-  }
-  return VC_OK;
-}
-
-vc_status lt_gemm(const void* X, const void* W, float* P, int M, int N, int K, hipStream_t s, bool* served) {
-  *served = false;
-  int dev = 0;
-  VC_HIP(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lk(g_lt_mu);
-  LtDevice& L = g_lt[dev];
-  if (!L.h) {
-    VC_LT(hipblasLtCreate(&L.h));
-    VC_HIP(hipMalloc(&L.ws, LT_WS_BYTES));
-    dbg_register(L.ws, LT_WS_BYTES);
-  }
-  const auto key = std::make_tuple(M, N, K);
-  auto it = L.shape.find(key);
-  if (it == L.shape.end()) {
-    LtShape sh;
-    const vc_status st = lt_shape_init(L, sh, M, N, K);
-    if (st) return st;
-    it = L.shape.emplace(key, sh).first;
-  }
-  const LtShape& sh = it->second;
-  if (!sh.served) return VC_OK;  // the caller uses its own kernel
-  const float alpha = 1.f, beta = 0.f;
-  VC_LT(hipblasLtMatmul(L.h, sh.md, &alpha, W, sh.la, X, sh.lb, &beta, P, sh.lc, P, sh.lc, &sh.algo, L.ws,
-                        LT_WS_BYTES, s));
-  *served = true;
-  return VC_OK;
-}
-
-}  // namespace
-
 int gemm_splits(int M, int N, int K, int dtype) {
   if (dtype != VC_BF16 || M > 64) return 1;
   const int col_blocks = N / SK_NB;
@@ -424,18 +484,15 @@ vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int 
                               static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K, kps);
     } else {
       VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: prefill tiles use one split");
-      bool served = false;
-      if (ev_start) VC_HIP(hipEventRecord(ev_start, s));
-      vc_status st = lt_gemm(X, W, P, M, N, K, s, &served);
-      if (st) return st;
-      if (served) {
-        if (ev_stop) VC_HIP(hipEventRecord(ev_stop, s));
-        return VC_OK;
+      if (N % PT == 0 && K <= (1 << 20)) {  // tile offsets (256 K 2 bytes) stay within 32 bits
+        const int T = int(cdiv(M, PT)) * (N / PT);
+        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(gemm_tile256_bf16<GEMM_KS, GEMM_NST>), dim3(T), dim3(256), 0, s, ev_start, ev_stop, 0,
+                              static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K);
+      } else {
+        VC_REQUIRE(N % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: N=%d not a multiple of 128", N);
+        hipExtLaunchKernelGGL(gemm_big_bf16, dim3(N / 128, cdiv(M, 128)), dim3(256), 0, s, ev_start, ev_stop, 0,
+                              static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K);
       }
-      ev_start = nullptr;  // recorded above; the kernel below takes only the stop event
-      VC_REQUIRE(N % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: N=%d not a multiple of 128", N);
-      hipExtLaunchKernelGGL(gemm_big_bf16, dim3(N / 128, cdiv(M, 128)), dim3(256), 0, s, ev_start, ev_stop, 0,
-                            static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K);
     }
   } else {
     VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: fp32 path uses one split");

@@ -211,8 +211,8 @@ def test_one_layer_stage_by_stage():
 
 
 def test_prefill_is_repeatable_bitwise(setup):
-    """Two prefills of the same prompt give the same K/V bit for bit (the projection GEMMs of
-    prefill chunks use one fixed library algorithm per shape)."""
+    """Two prefills of the same prompt give the same K/V bit for bit (every kernel of a prefill
+    chunk sums in a fixed order)."""
     from lossless_speculative_decoding_amd.engine import greedy_resident
     T = setup["prompt"].numel()  # rows past the prompt are capacity, not written by prefill
     _, _, (k1, v1) = greedy_resident(setup["m"], setup["prompt"], 1, chunk=256)

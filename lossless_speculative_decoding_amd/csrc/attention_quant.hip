@@ -260,12 +260,16 @@ constexpr int qsplit_max() { return QUANT_MAX_GROUPS * D / NH; }
 //       ((group * 4 + chunk) * 2 + hi_lo) * 4G + g * G + head (512 bytes per group and head);
 //   KB  the key bias sum_d q_d (2^(b-1) s_K + z_K) per token group and head (KBP: its four
 //       32-channel partial sums, merged in a fixed order);
-//   VF  per key and V channel group: (s_V, 2^(b-1) s_V + z_V) in float32.
+//   VF  per key and V channel group: (s_V, 2^(b-1) s_V + z_V) in float32, entry (k, v) at float2
+//       k NH + v + k / 16: one 8-byte pad per 16 keys, so that the four 16-key runs the lane
+//       groups of a wave read at once fall in different LDS banks (without it they are 128 NH
+//       bytes apart: the same banks for NH = 2).
 // After the loop the same bytes hold the waves' merge buffer.
 template <int NH>
 struct QLds {
   static constexpr int QP = 0, KB = QP + QUANT_QP_BYTES, KBP = KB + QUANT_QP_BYTES / 512 * 4,
-                       VF = KBP + QUANT_QP_BYTES / 512 * 4 * 4, END = VF + qsplit_max<NH>() * NH * 8;
+                       VF = KBP + QUANT_QP_BYTES / 512 * 4 * 4,
+                       END = VF + (qsplit_max<NH>() * NH + qsplit_max<NH>() / 16) * 8;
   static constexpr int RED = QWAVES * 16 * QRED * 4;  // also covers the exact rows' 4 * 16 * (D + 2) floats
   static_assert(QWAVES * 16 * (D + 2) * 4 <= RED, "exact-row merge buffer");
   static_assert((16 * D + 4 * 64 * 16) * 4 <= RED, "exact-row query rows and weights");
@@ -410,8 +414,11 @@ __device__ void quant_exact_rows(const QuantReq& R, int j, int G, int Hq, float 
   }
 }
 
+#ifndef QUANT_WPE2
+#define QUANT_WPE2 2
+#endif
 template <int BITS, int NH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3 : 2, NH == 1 ? 3 : 2))) void attn_quant_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3 : QUANT_WPE2, NH == 1 ? 3 : QUANT_WPE2))) void attn_quant_kernel(
     const QuantArgs args) {
   using L = QLds<NH>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::BYTES];
@@ -527,8 +534,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
     const float sv = h2f(vs[int64_t(key_lo) * nh + i]), zv = h2f(vz[int64_t(key_lo) * nh + i]);
     constexpr uint64_t offs = conv_offs_by_code<VT>();
     const int o = int((offs >> (4 * ((i / nh) & 15))) & 15);
-    s_vf[2 * i] = sv * float(1 << (10 - o));
-    s_vf[2 * i + 1] = fmaf(sv, C0, zv);
+    const int e = i + (i / nh >> 4);
+    s_vf[2 * e] = sv * float(1 << (10 - o));
+    s_vf[2 * e + 1] = fmaf(sv, C0, zv);
   }
   __syncthreads();
   // the four quarter sums of a (group, head) in the order ((0 + 1) + (2 + 3))
@@ -550,7 +558,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3
   for (; t0 < key_hi; t0 += QWAVES * ATT_KT) {
     // V scale (times the factor of the key's position) and bias weight of this lane's keys
     // [t0 + 16g, t0 + 16g + 16): key k, channel group v at vf[k * NH + v]
-    const float2* const vf = reinterpret_cast<const float2*>(s_vf) + (t0 - key_lo + 16 * g) * nh;
+    const int run0 = t0 - key_lo + 16 * g;
+    const float2* const vf = reinterpret_cast<const float2*>(s_vf) + run0 * nh + (run0 >> 4);
     // ---- key bias of the tile's token group; its Q' fragments are read per 32-channel chunk
     // (holding them across tiles, or all four chunks at once, would keep registers live)
     const int gi = t0 / grp_sz - g_lo;

@@ -30,8 +30,19 @@ namespace vc {
 namespace {
 
 constexpr int D128 = 128;
-constexpr int KS_PITCH = D128 + 8;     // bf16 per K row in LDS (pad breaks bank aliasing)
-constexpr int VT_PITCH = ATT_KT + 8;   // fp16 per V^T row in LDS
+// LDS tiles, 16-byte chunks XOR-swizzled within each row.  A ds_read_b128 is served in four
+// passes of 16 lanes: per half-wave, the quads (4 lanes) whose index has even bit parity
+// (lanes 0-3, 12-15, 20-23, 24-27) and those with odd parity (measured with the bank-conflict
+// counter).  A fragment read takes row r = lane % 16 and chunk q + lane / 16, so a pass holds
+// rows {0-3, 12-15} at one chunk and rows {4-11} at the next (or the reverse):
+//   K (and the shared blocks' queries): 256-byte rows, chunk q stored at q ^ (r % 16), so each
+//     pass covers the 16 chunk positions of the 256 bytes (all 64 banks) once;
+//   V^T: 128-byte rows (two per 256 bytes), chunk q at q ^ ((r / 2) % 8), so each pass's rows of
+//     either parity take eight different chunk positions.
+constexpr int KS_PITCH = D128;   // bf16 per K row
+constexpr int VT_PITCH = ATT_KT; // fp16 per V^T row
+__device__ __forceinline__ int ks_off(int row, int chunk) { return row * KS_PITCH + 8 * (chunk ^ (row & 15)); }
+__device__ __forceinline__ int vt_off(int row, int chunk) { return row * VT_PITCH + 8 * (chunk ^ ((row >> 1) & 7)); }
 constexpr float P_SCALE = 1024.f;      // P is rounded to fp16 as P * 2^10
 constexpr float P_LOG2 = 10.f;         // log2 of P_SCALE
 constexpr float P_UNSCALE = 1.f / 1024.f;
@@ -155,7 +166,7 @@ __device__ __forceinline__ void load_tile_bf16(TileRegs& r, const AttnReq& R, in
 __device__ __forceinline__ void store_tile_bf16(const TileRegs& r, uint16_t* Ks, uint16_t* Vt, int tid) {
   const int kr = tid >> 4, ch = tid & 15, dc = tid >> 4, kg = tid & 15;
 #pragma unroll
-  for (int e = 0; e < 4; e++) *reinterpret_cast<u32x4*>(Ks + (kr + 16 * e) * KS_PITCH + 8 * ch) = r.k[e];
+  for (int e = 0; e < 4; e++) *reinterpret_cast<u32x4*>(Ks + ks_off(kr + 16 * e, ch)) = r.k[e];
   const int slot = 32 * (kg >> 3) + 8 * (kg & 3) + 4 * ((kg >> 2) & 1);  // keys 4kg .. 4kg + 3
 #pragma unroll
   for (int c = 0; c < 8; c++) {
@@ -166,7 +177,7 @@ __device__ __forceinline__ void store_tile_bf16(const TileRegs& r, uint16_t* Ks,
     u32x2 out;
     out.x = bitcast<uint32_t>(f16x2{(_Float16)x[0], (_Float16)x[1]});
     out.y = bitcast<uint32_t>(f16x2{(_Float16)x[2], (_Float16)x[3]});
-    *reinterpret_cast<u32x2*>(Vt + (8 * dc + c) * VT_PITCH + slot) = out;
+    *reinterpret_cast<u32x2*>(Vt + vt_off(8 * dc + c, slot >> 3) + (slot & 7)) = out;
   }
 }
 
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (jb < nj) {
       const int r = tid >> 4, ch = tid & 15;
       const int qr = qr0 + OWN_ROWS + ATT_MB * jb + r;
-      *reinterpret_cast<u32x4*>(Qj + (jb * ATT_MB + r) * KS_PITCH + 8 * ch) =
+      *reinterpret_cast<u32x4*>(Qj + ks_off(jb * ATT_MB + r, ch)) =
           qr < n_qrows ? *reinterpret_cast<const u32x4*>(q_row(qr) + 8 * ch) : u32x4{0, 0, 0, 0};
     }
     oj[jb][0] = oj[jb][1] = f32x4{0, 0, 0, 0};
@@ -344,7 +355,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int kt = 0; kt < 4; kt++) {
 #pragma unroll
         for (int c = 0; c < 4; c++) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (16 * kt + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + ks_off(16 * kt + (lane & 15), 4 * c + grp));
 #pragma unroll
           for (int b = 0; b < NB; b++) sacc[b][kt] = mfma_bf16(ka, qf[B0 + b][c], sacc[b][kt]);
         }
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int b = 0; b < NB; b++) p_frags(sacc[b], kc, pb[b], pl[b]);
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
-          const u32x4 va = *reinterpret_cast<const u32x4*>(Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 8 * grp);
+          const u32x4 va = *reinterpret_cast<const u32x4*>(Vt + vt_off(16 * dt + (lane & 15), 4 * kc + grp));
 #pragma unroll
           for (int b = 0; b < NB; b++) {
             oacc[B0 + b][dt] = mfma_f16(va, pb[b], oacc[B0 + b][dt]);
@@ -397,8 +408,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         f32x4 sj = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < 4; c++) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (16 * wave + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
-          const u32x4 qb = *reinterpret_cast<const u32x4*>(Qj + (jb * ATT_MB + (lane & 15)) * KS_PITCH + 32 * c + 8 * grp);
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + ks_off(16 * wave + (lane & 15), 4 * c + grp));
+          const u32x4 qb = *reinterpret_cast<const u32x4*>(Qj + ks_off(jb * ATT_MB + (lane & 15), 4 * c + grp));
           sj = mfma_bf16(ka, qb, sj);
         }
         Sx[(jb * 4 + wave) * 64 + lane] = sj;
@@ -427,7 +438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int dd = 0; dd < 2; dd++) {
               const int dt = 2 * wave + dd;
-              const u32x4 va = *reinterpret_cast<const u32x4*>(Vt + (16 * dt + (lane & 15)) * VT_PITCH + 32 * kc + 8 * grp);
+              const u32x4 va = *reinterpret_cast<const u32x4*>(Vt + vt_off(16 * dt + (lane & 15), 4 * kc + grp));
               oj[jb][dd] = mfma_f16(va, pb, oj[jb][dd]);
               oj[jb][dd] = mfma_f16(va, pl, oj[jb][dd]);
             }

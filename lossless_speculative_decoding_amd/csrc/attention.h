@@ -70,7 +70,9 @@ __device__ __forceinline__ const E* key_row(const AttnReq& R, int j, int t, bool
       const int o = t & 63;
       const uint64_t m = R.mix.mask[tl];
       const int c = R.mix.cnt[tl];
-      const int below = __popcll(m & ((uint64_t(1) << o) - 1));
+      // set bits of m below bit o, shifting m itself (a mask (1 << o) - 1 would be loop invariant
+      // per lane and get hoisted: one 64-bit register pair per call site)
+      const int below = o ? __popcll(m << (64 - o)) : 0;
       if ((m >> o) & 1) {
         const E* base = static_cast<const E*>(is_v ? R.mix.v : R.mix.k);
         return base + j * R.mix.hstride + int64_t(c + below) * D;

@@ -125,9 +125,11 @@ __device__ __forceinline__ void load_tile_bf16(TileRegs& r, const AttnReq& R, in
   if (mix.valid) {  // uniform: every row in the kept / staged mix of segment a
     // lane o of each wave locates key t0 + o (one popcount); each thread then takes the rows of
     // its eight loads from the lanes that located them (the top bit marks a kept row)
+    // (set bits of m below this lane: v_mbcnt, so no per-lane 64-bit mask is kept in registers)
     const int o = tid & 63;
-    const int below = __popcll(mix.m & ((uint64_t(1) << o) - 1));
-    const bool kept = (mix.m >> o) & 1;
+    const uint32_t m_lo = uint32_t(mix.m), m_hi = uint32_t(mix.m >> 32);
+    const int below = int(__builtin_amdgcn_mbcnt_hi(m_hi, __builtin_amdgcn_mbcnt_lo(m_lo, 0u)));
+    const bool kept = ((o < 32 ? m_lo >> o : m_hi >> (o - 32)) & 1u) != 0;
     const uint32_t handle = kept ? (uint32_t(mix.c + below) | 0x80000000u) : uint32_t(t0 - mix.c + o - below);
     const uint16_t* kk = static_cast<const uint16_t*>(R.mix.k) + j * R.mix.hstride;
     const uint16_t* sk = static_cast<const uint16_t*>(R.a.k) + j * R.a.hstride;

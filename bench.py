@@ -216,6 +216,12 @@ def bench_layer(args):
     e = w.extra
     Hq, Hkv, D, rows = e["n_q_heads"], e["n_kv_heads"], e["head_dim"], e["verify_rows"]
     B, T, bits, group = w.batch, w.ctx[0], w.compress.bits, w.compress.group
+    # other cache shapes of the same layer (the quantized caches of the 8B-shaped workloads: 2-bit
+    # group 64 at 4 x 131072, 3-bit group 128 at 16 requests); the workload name records them
+    B, T = args.batch or B, args.ctx or T
+    bits, group = args.bits or bits, args.group or group
+    name = w.name if (B, T, bits, group) == (w.batch, w.ctx[0], w.compress.bits, w.compress.group) else \
+        f"gqa_layer_bf16_b{B}_t{T}_q{bits}g{group}"
     torch.cuda.set_device(0)
 
     def gen(shape, stream, outl=None, scale=1.0):
@@ -263,10 +269,10 @@ def bench_layer(args):
                           f"{bits}-bit group {group}")
     vr = _rate(vp, "hbm", f"verification attention partials, {B} requests x {rows} rows x {Hq} heads over "
                           f"{T} + {rows} keys")
-    ratio = pmc_traffic_ratio(w.name, "attn_quant")
+    ratio = pmc_traffic_ratio(name, "attn_quant")
     dr["traffic"] = round(ratio * dr["bytes_per_launch"]) if ratio else None
     dr["traffic_over_algorithmic"] = ratio
-    ratio = pmc_traffic_ratio(f"{w.name[:w.name.rindex('_')]}_r{rows}", "attn_rows_bf16", "verify_attention")
+    ratio = pmc_traffic_ratio(f"{name[:name.rindex('_')]}_r{rows}", "attn_rows_bf16", "verify_attention")
     vr["traffic"] = round(ratio * vr["bytes_per_launch"]) if ratio else None
     vr["traffic_over_algorithmic"] = ratio
     cpu = None if args.no_cpu_baseline else cpu_baseline_layer(T, Hq, Hkv, D, rows, bits, group)
@@ -275,7 +281,7 @@ def bench_layer(args):
         "value": dr["achieved"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(1000 * secs / args.steps, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V with 4 outlier channels x10)",
-        "config": {"workload": w.name, "batch": B, "ctx": T, "bits": bits, "group": group, "verify_rows": rows},
+        "config": {"workload": name, "batch": B, "ctx": T, "bits": bits, "group": group, "verify_rows": rows},
         "roofline": dr, "verify_attention": vr, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -795,6 +801,8 @@ def main():
     ap.add_argument("--config", default="llama8b_tokdrop",
                     choices=["llama8b_tokdrop", "llama8b_q2", "llama8b_mixed", "gqa_layer"])
     ap.add_argument("--ctx", type=int, default=0, help="override the prompt length (diagnostics only)")
+    ap.add_argument("--bits", type=int, default=0, help="gqa_layer: code width of the quantized cache (2, 3, 4)")
+    ap.add_argument("--group", type=int, default=0, help="gqa_layer: quantization group (64, 128)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (diagnostics only)")
     ap.add_argument("--baseline-steps", type=int, default=16)
     ap.add_argument("--comparator-staging", choices=["layered", "whole"], default="layered",

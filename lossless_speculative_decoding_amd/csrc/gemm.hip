@@ -6,7 +6,7 @@
 // 256 columns at a time and every wave runs 16x16x32 bf16 MFMAs over all
 // M rows (padded to 16) while its next weight fragments are in flight.
 // Prefill chunks (M > 64) are plain bf16 GEMMs with float32 output: gemm_tile256_bf16 (256 x 256
-// tiles, one wave per SIMD holding a 128 x 128 block) where N is a multiple of 256, else
+// tiles, eight waves of 128 x 64, two per SIMD) where N is a multiple of 256, else
 // gemm_big_bf16 (128 x 128 x 32 tiles).  The fp32 model uses a 16x16 tiled VALU kernel whose
 // outputs are single fma chains in ascending k.
 #include <algorithm>
@@ -180,8 +180,10 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(const uint16_t* __restrict_
   }
 }
 
-// Prefill tile: a 256 x 256 block of P from 4 waves in 2 x 2, each wave 128 x 128 (4 x 4
-// 32x32x16 MFMA tiles, 256 float accumulators per lane, one wave per SIMD).  k advances KS at a
+// Prefill tile: a 256 x 256 block of P from NW waves in 2 x NW/2, each wave 128 x 512/NW (32x32x16
+// MFMA tiles; NW = 8: 128 x 64, 128 float accumulators per lane, two waves per SIMD, so one
+// wave's MFMAs run while the other waits at a barrier or for LDS; NW = 4: 128 x 128, one wave
+// per SIMD, measured 5% slower).  k advances KS at a
 // time through a ring of NST LDS stages, each A [256][KS] and B [256][KS] bf16 (NST KS 1 KB in
 // all), filled by direct-to-LDS buffer loads (each wave instruction writes 1 KB of whole rows),
 // so the staging holds no registers; loads run NST - 1 stages ahead of the multiplies.  Per
@@ -195,6 +197,7 @@ constexpr int PT = 256;
 #ifndef GEMM_KS
 #define GEMM_KS 64  // k per LDS stage
 #define GEMM_NST 2  // stages in the ring
+#define GEMM_NW 8   // waves per workgroup: 4 (128 x 128 each, one per SIMD) or 8 (128 x 64, two per SIMD)
 #endif
 
 template <int KS>
@@ -203,17 +206,20 @@ __device__ __forceinline__ int pt_swz(int row) {
   else return (row >> 2) & 3;
 }
 
-template <int KS, int NST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile256_bf16(
+template <int KS, int NST, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_tile256_bf16(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, float* __restrict__ P, int M, int N, int K) {
   typedef __attribute__((address_space(3))) void lds_void;
-  constexpr int CPR = KS / 8;      // 16-byte chunks per LDS row
-  constexpr int RPI = 64 / CPR;    // rows one wave instruction fills
-  constexpr int NI = PT / RPI / 4; // instructions per wave, operand and stage
+  constexpr int CPR = KS / 8;       // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CPR;     // rows one wave instruction fills
+  constexpr int NI = PT / RPI / NW; // instructions per wave, operand and stage
+  constexpr int WN = NW / 2;        // waves along N (two along M)
+  constexpr int JN = PT / WN / 32;  // 32-column MFMA blocks per wave
+  constexpr int TOT = 4 * JN;       // MFMAs per wave and 16-deep step
   __shared__ __attribute__((aligned(16))) uint16_t lds[NST][2][PT * KS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int MT = (M + PT - 1) / PT, NT = N / PT;
   // XCD x (blocks x, x + 8, ...) takes an eighth of the tile grid, split along the longer side
   // when that side divides by eight; inside it, bands of up to 8 row tiles, rows fastest, so
@@ -230,44 +236,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const_cast<uint16_t*>(X + int64_t(m0) * K), 0, min(M - m0, PT) * K * 2, BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(W + int64_t(n0) * K), 0, PT * K * 2, BUF_DWORD3);
-  // wave instruction i fills tile rows RPI (4 i + wave) .. + RPI; lane: row + lane / CPR, LDS chunk lane % CPR
+  // wave instruction i fills tile rows RPI (NW i + wave) .. + RPI; lane: row + lane / CPR, LDS chunk lane % CPR
   const int lrow = RPI * wave + lane / CPR;
   const int voff = lrow * K * 2 + 16 * ((lane % CPR) ^ pt_swz<KS>(lrow));
-  const int rstep = 4 * RPI * K * 2;
+  const int rstep = NW * RPI * K * 2;
   auto issue = [&](int k0, int buf) {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&lds[buf][0][RPI * (4 * i + wave) * KS], 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&lds[buf][0][RPI * (NW * i + wave) * KS], 16,
                                                voff + i * rstep + 2 * k0, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&lds[buf][1][RPI * (4 * i + wave) * KS], 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&lds[buf][1][RPI * (NW * i + wave) * KS], 16,
                                                voff + i * rstep + 2 * k0, 0, 0, 0);
     }
   };
-  f32x16 acc[4][4];
+  f32x16 acc[4][JN];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = f32x16{};
+    for (int j = 0; j < JN; j++) acc[i][j] = f32x16{};
   const int nk = K / KS;
   const int lr32 = lane & 31, lh = lane >> 5;
-  u32x4 af[2][4], bf[2][4];
+  u32x4 af[2][4], bf[2][JN];
   auto frags = [&](int buf, int s, int slot) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int ra_ = 128 * wm + 32 * i + lr32, rb_ = 128 * wn + 32 * i + lr32;
+      const int ra_ = 128 * wm + 32 * i + lr32;
       af[slot][i] = *reinterpret_cast<const u32x4*>(&lds[buf][0][ra_ * KS + 8 * ((2 * s + lh) ^ pt_swz<KS>(ra_))]);
-      bf[slot][i] = *reinterpret_cast<const u32x4*>(&lds[buf][1][rb_ * KS + 8 * ((2 * s + lh) ^ pt_swz<KS>(rb_))]);
+    }
+#pragma unroll
+    for (int j = 0; j < JN; j++) {
+      const int rb_ = 32 * JN * wn + 32 * j + lr32;
+      bf[slot][j] = *reinterpret_cast<const u32x4*>(&lds[buf][1][rb_ * KS + 8 * ((2 * s + lh) ^ pt_swz<KS>(rb_))]);
     }
   };
-  // MFMAs number e0 .. e1 - 1 of a step (e = 4 i + j: A block i, B block j)
+  // MFMAs number e0 .. e1 - 1 of a step (e = JN i + j: A block i, B block j)
   auto mfmas = [&](int slot, int e0, int e1) {
 #pragma unroll
-    for (int e = e0; e < e1; e++) acc[e >> 2][e & 3] = mfma32_bf16(af[slot][e >> 2], bf[slot][e & 3], acc[e >> 2][e & 3]);
+    for (int e = e0; e < e1; e++) acc[e / JN][e % JN] = mfma32_bf16(af[slot][e / JN], bf[slot][e % JN], acc[e / JN][e % JN]);
   };
   auto issue_one = [&](int k0, int buf, int i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&lds[buf][0][RPI * (4 * i + wave) * KS], 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&lds[buf][0][RPI * (NW * i + wave) * KS], 16,
                                              voff + i * rstep + 2 * k0, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&lds[buf][1][RPI * (4 * i + wave) * KS], 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&lds[buf][1][RPI * (NW * i + wave) * KS], 16,
                                              voff + i * rstep + 2 * k0, 0, 0, 0);
   };
   constexpr int S = KS / 16;  // 32x32x16 steps per stage
@@ -294,7 +304,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_sched_barrier(0);
       frags(buf, s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(s & 1, 2, 16);
+      mfmas(s & 1, 2, TOT);
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * NI * (NST - 2)) : "memory");
@@ -306,11 +316,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     frags((kt + 1) % NST, 0, S & 1);
     __builtin_amdgcn_sched_barrier(0);
     const int kn = KS * min(kt + NST, nk - 1);
-    // the other fourteen MFMAs with the NI load pairs spread over them
+    // the step's other MFMAs with the NI load pairs spread over them
 #pragma unroll
     for (int q = 0; q < NI; q++) {
       issue_one(kn, buf, q);
-      mfmas(L, 2 + 14 * q / NI, 2 + 14 * (q + 1) / NI);
+      mfmas(L, 2 + (TOT - 2) * q / NI, 2 + (TOT - 2) * (q + 1) / NI);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -323,9 +333,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int e = 0; e < 16; e++) {
       const int m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
       if (m >= M) continue;
-      float* prow = P + int64_t(m) * N + n0 + 128 * wn + lr32;
+      float* prow = P + int64_t(m) * N + n0 + 32 * JN * wn + lr32;
 #pragma unroll
-      for (int j = 0; j < 4; j++) prow[32 * j] = acc[i][j][e];
+      for (int j = 0; j < JN; j++) prow[32 * j] = acc[i][j][e];
     }
   }
 }
@@ -486,7 +496,7 @@ vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int 
       VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: prefill tiles use one split");
       if (N % PT == 0 && K <= (1 << 20)) {  // tile offsets (256 K 2 bytes) stay within 32 bits
         const int T = int(cdiv(M, PT)) * (N / PT);
-        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(gemm_tile256_bf16<GEMM_KS, GEMM_NST>), dim3(T), dim3(256), 0, s, ev_start, ev_stop, 0,
+        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(gemm_tile256_bf16<GEMM_KS, GEMM_NST, GEMM_NW>), dim3(T), dim3(64 * GEMM_NW), 0, s, ev_start, ev_stop, 0,
                               static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K);
       } else {
         VC_REQUIRE(N % 128 == 0, VC_ERR_UNSUPPORTED, "gemm: N=%d not a multiple of 128", N);

@@ -32,7 +32,10 @@ and the equivalence with complex multiplication by exp(i pos theta_i); silu at
 closed-form points (sigma(ln 3) = 3/4) and its odd-part identity; the SwiGLU
 gate/up assignment on a crafted one-layer model; and the cached row-by-row
 greedy decode against a brute-force recomputation of the whole sequence in
-matrix form with no cache (``sequence_logits``).
+matrix form with no cache (``sequence_logits``); and the full-size forms at the
+end of this file (``LayerWeights``, ``embed_rows``, ``head_logits``,
+``layer_forward_rows``) against ``Weights``, ``head_forward`` and
+``layer_forward`` on small shapes.
 """
 from __future__ import annotations
 
@@ -215,3 +218,104 @@ def sequence_logits(W: Weights, tokens, rdtype: str | None = None) -> np.ndarray
         H = R(H + M @ W.W2[l].T)
     Z = R(rmsnorm(H, W.gF, s.eps))
     return Z @ W.Wlm.T
+
+
+# ---------------------------------------------------------------- full-size forms (8B shapes)
+# At the 8B shapes the whole model does not fit in host memory as float64 (64 GB), and one row at
+# a time against a 65536-row cache is slow.  These forms compute the same values as Weights,
+# head_forward and layer_forward, one layer at a time; tests/test_oracle_model.py pins each to
+# the form above on small shapes.
+
+def _stored_chunked(stream: int, out_dim: int, in_dim: int, seed: int, dtype: str, pool, rows: int = 2048):
+    """One [out][in] matrix of the Weights recipe, generated in row chunks (the draws are
+    counter based: chunk r0 starts at element r0 * in_dim), possibly on a thread pool."""
+    def chunk(r0):
+        r1 = min(out_dim, r0 + rows)
+        x = synth.xavier(stream, (r1 - r0, in_dim), in_dim, out_dim, seed, start=r0 * in_dim)
+        return _stored(x, dtype)
+    starts = range(0, out_dim, rows)
+    parts = list(pool.map(chunk, starts)) if pool is not None else [chunk(r0) for r0 in starts]
+    return np.concatenate(parts)
+
+
+class LayerWeights:
+    """Layer l's weights only, with the attribute layout of Weights (Wq[l], ..., g1[l]) so that
+    layer_forward and layer_forward_rows take it in place of a whole model."""
+
+    def __init__(self, shape: ModelShape, l: int, seed: int = 0, dtype: str | None = None, pool=None):
+        s = shape
+        dt = dtype or s.dtype
+        self.shape, self.dtype = s, dt
+        D = s.head_dim
+        st = lambda t: synth.layer_stream(l, t)
+        mat = lambda t, o, i: _stored_chunked(st(t), o, i, seed, dt, pool)
+        self.Wq = {l: mat(synth.T_WQ, s.n_q_heads * D, s.d_model)}
+        self.Wk = {l: mat(synth.T_WK, s.n_kv_heads * D, s.d_model)}
+        self.Wv = {l: mat(synth.T_WV, s.n_kv_heads * D, s.d_model)}
+        self.Wo = {l: mat(synth.T_WO, s.d_model, s.n_q_heads * D)}
+        self.W1 = {l: mat(synth.T_W1, s.ffn, s.d_model)}
+        self.W3 = {l: mat(synth.T_W3, s.ffn, s.d_model)}
+        self.W2 = {l: mat(synth.T_W2, s.d_model, s.ffn)}
+        self.g1 = {l: np.ones(s.d_model)}
+        self.g2 = {l: np.ones(s.d_model)}
+
+
+def embed_rows(shape: ModelShape, tokens, seed: int = 0, dtype: str | None = None) -> np.ndarray:
+    """Rows E[tok] of the embedding (Weights.E), generated one row at a time."""
+    s = shape
+    dt = dtype or s.dtype
+    return np.stack([_stored(synth.xavier(synth.S_EMBED, (1, s.d_model), s.d_model, s.vocab, seed,
+                                          start=int(t) * s.d_model), dt)[0] for t in tokens])
+
+
+def head_logits(shape: ModelShape, H: np.ndarray, seed: int = 0, dtype: str | None = None, pool=None,
+                rows: int = 4096) -> np.ndarray:
+    """head_forward for rows H [n][d]: final norm, then Wlm in row chunks -> logits [n][V]."""
+    s = shape
+    dt = dtype or s.dtype
+    R = storage_round(dt)
+    Z = R(rmsnorm(H, np.ones(s.d_model), s.eps))
+
+    def chunk(r0):
+        r1 = min(s.vocab, r0 + rows)
+        Wc = _stored(synth.xavier(synth.S_LMHEAD, (r1 - r0, s.d_model), s.d_model, s.vocab, seed,
+                                  start=r0 * s.d_model), dt)
+        return Z @ Wc.T
+    starts = range(0, s.vocab, rows)
+    parts = list(pool.map(chunk, starts)) if pool is not None else [chunk(r0) for r0 in starts]
+    return np.concatenate(parts, axis=1)
+
+
+def layer_forward_rows(W, l: int, H: np.ndarray, pos0: int, Kp: np.ndarray, Vp: np.ndarray,
+                       rdtype: str | None = None):
+    """layer_forward for n consecutive rows at positions pos0 .. pos0 + n - 1 (residuals H [n][d]):
+    row i sees the cached rows Kp, Vp [Hkv][T][D] and rows 0..i of this call, in absolute-position
+    order.  The projections take all rows at once, and the G query heads of a KV head are scored
+    against the cached rows together; every row's values are those of layer_forward (up to the
+    order of float64 sums).  Returns (H_out [n][d], K [n][Hkv][D], V [n][Hkv][D])."""
+    s = W.shape
+    R = storage_round(rdtype or W.dtype)
+    D, G, Hq, Hkv = s.head_dim, s.group, s.n_q_heads, s.n_kv_heads
+    n = H.shape[0]
+    A = R(rmsnorm(H, W.g1[l], s.eps))
+    Q = A @ W.Wq[l].T
+    Kn = A @ W.Wk[l].T
+    Q = R(np.stack([rope(Q[i].reshape(Hq, D), pos0 + i, s.rope_theta) for i in range(n)]))     # [n][Hq][D]
+    Kn = R(np.stack([rope(Kn[i].reshape(Hkv, D), pos0 + i, s.rope_theta) for i in range(n)]))  # [n][Hkv][D]
+    Vn = R((A @ W.Wv[l].T).reshape(n, Hkv, D))
+    O = np.empty((n, Hq, D))
+    mask = np.repeat(np.tril(np.ones((n, n), dtype=bool)), G, axis=0)      # [(row, head)][row of this call]
+    for j in range(Hkv):
+        Qj = Q[:, j * G:(j + 1) * G, :].reshape(n * G, D)                  # (row, head) pairs
+        Sc = (Qj @ Kp[j].T) / math.sqrt(D)                                  # against the cached rows
+        Sn = np.where(mask, (Qj @ Kn[:, j, :].T) / math.sqrt(D), -np.inf)  # against this call's rows
+        mx = np.maximum(Sc.max(axis=1), Sn.max(axis=1))[:, None]
+        Pc, Pn = np.exp(Sc - mx), np.exp(Sn - mx)
+        den = (Pc.sum(axis=1) + Pn.sum(axis=1))[:, None]
+        O[:, j * G:(j + 1) * G, :] = ((Pc @ Vp[j] + Pn @ Vn[:, j, :]) / den).reshape(n, G, D)
+    O = R(O)
+    H = R(H + O.reshape(n, -1) @ W.Wo[l].T)
+    F = R(rmsnorm(H, W.g2[l], s.eps))
+    M = R(silu(F @ W.W1[l].T) * (F @ W.W3[l].T))
+    H = R(H + M @ W.W2[l].T)
+    return H, Kn, Vn

@@ -184,3 +184,83 @@ def test_bf16_mode_close_to_fp64():
     a = sequence_logits(W64, list(p))
     b = sequence_logits(W64, list(p), rdtype="bf16")
     assert np.max(np.abs(a - b)) < 0.05 * np.max(np.abs(a))
+
+
+# ---------------------------------------------------------------- the full-size forms
+GQA = ModelShape(n_layers=2, d_model=32, n_q_heads=4, n_kv_heads=2, head_dim=8, ffn=48, vocab=37,
+                 rope_theta=10000.0, dtype="bf16")
+
+
+def test_layer_weights_and_embedding_rows_are_the_weights_recipe():
+    """LayerWeights (row chunks, on a thread pool or not) and embed_rows give exactly the values
+    of Weights."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle.model import LayerWeights, _stored_chunked, embed_rows
+    W = Weights(GQA)
+    with ThreadPoolExecutor(3) as pool:
+        for l in range(GQA.n_layers):
+            Lw = LayerWeights(GQA, l, pool=pool)
+            for name in ("Wq", "Wk", "Wv", "Wo", "W1", "W3", "W2"):
+                assert np.array_equal(getattr(Lw, name)[l], getattr(W, name)[l]), name
+        st = synth.layer_stream(1, synth.T_W1)
+        assert np.array_equal(_stored_chunked(st, GQA.ffn, GQA.d_model, 0, "bf16", pool, rows=5), W.W1[1])
+    toks = [0, 5, 36, 5]
+    assert np.array_equal(embed_rows(GQA, toks), W.E[toks])
+
+
+def test_head_logits_equals_head_forward():
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle.model import head_forward, head_logits
+    W = Weights(GQA)
+    rng = np.random.default_rng(3)
+    H = to_bf16(rng.standard_normal((3, GQA.d_model)))
+    ref = np.stack([head_forward(W, h) for h in H])
+    with ThreadPoolExecutor(2) as pool:
+        got = head_logits(GQA, H, pool=pool, rows=7)          # 37 rows in chunks of 7
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("rdtype", ["fp64", "bf16"])
+def test_layer_forward_rows_equals_row_by_row(rdtype):
+    """n rows through one layer at once against layer_forward one row at a time, each row seeing
+    the same cached prefix and the earlier rows of the call (fp64: to rounding of sums; bf16: the
+    stored values may differ where a float64 sum sits on a bf16 rounding boundary, by one ulp)."""
+    from oracle.model import layer_forward, layer_forward_rows
+    W = Weights(GQA)
+    rng = np.random.default_rng(7)
+    T, n, pos0 = 9, 4, 9
+    R = (lambda x: x) if rdtype == "fp64" else to_bf16
+    Kp = R(rng.standard_normal((GQA.n_kv_heads, T, GQA.head_dim)))
+    Vp = R(rng.standard_normal((GQA.n_kv_heads, T, GQA.head_dim)))
+    H = R(rng.standard_normal((n, GQA.d_model)))
+    for l in range(GQA.n_layers):
+        Hg, Kg, Vg = layer_forward_rows(W, l, H, pos0, Kp, Vp, rdtype)
+        ks, vs = [], []
+        for i in range(n):
+            def past(j, i=i):
+                return (np.concatenate([Kp[j]] + [k[j][None] for k in ks]),
+                        np.concatenate([Vp[j]] + [v[j][None] for v in vs]))
+            h, k, v, _, _ = layer_forward(W, l, H[i], pos0 + i, past, rdtype)
+            ks.append(k)
+            vs.append(v)
+            tol = 1e-12 if rdtype == "fp64" else 2.0 ** -7
+            for got, ref in ((Hg[i], h), (Kg[i], k), (Vg[i], v)):
+                assert np.abs(got - ref).max() <= tol * np.abs(ref).max(), (l, i)
+        H = Hg
+
+
+def test_layer_forward_rows_catches_a_planted_mistake():
+    """A row that also sees the row after it (a causal-mask mistake) changes the outputs."""
+    from oracle.model import layer_forward_rows
+    W = Weights(GQA)
+    rng = np.random.default_rng(8)
+    Kp = rng.standard_normal((GQA.n_kv_heads, 5, GQA.head_dim))
+    Vp = rng.standard_normal((GQA.n_kv_heads, 5, GQA.head_dim))
+    H = rng.standard_normal((3, GQA.d_model))
+    ref, _, _ = layer_forward_rows(W, 0, H, 5, Kp, Vp, "fp64")
+    # rows 0 and 1 alone: row 0 must not change when row 1 is dropped (it never sees it)
+    one, _, _ = layer_forward_rows(W, 0, H[:1], 5, Kp, Vp, "fp64")
+    assert np.abs(one[0] - ref[0]).max() <= 1e-12 * np.abs(ref[0]).max()
+    # but a prefix with one more key changes every row
+    more, _, _ = layer_forward_rows(W, 0, H, 5, np.concatenate([Kp, Kp[:, :1]], 1), np.concatenate([Vp, Vp[:, :1]], 1), "fp64")
+    assert np.abs(more - ref).max() > 1e-6

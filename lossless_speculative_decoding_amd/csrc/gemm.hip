@@ -2,9 +2,9 @@
 //
 // Decode / verify (M <= 64) are weight-streaming: every weight is read once
 // per forward.  gemm_skinny_bf16: a workgroup owns 64 output columns (16 per
-// wave) and one K range; the activations of that range are staged in LDS
-// 256 columns at a time and every wave runs 16x16x32 bf16 MFMAs over all
-// M rows (padded to 16) while its next weight fragments are in flight.
+// wave) and one K range; the activations are staged in a double-buffered LDS
+// tile 256 columns at a time and every wave runs 16x16x32 bf16 MFMAs over all
+// M rows (padded to 16) while its next two chunks of weight fragments are in flight.
 // Prefill chunks (M > 64) are plain bf16 GEMMs with float32 output: gemm_tile256_bf16 (256 x 256
 // tiles, eight waves of 128 x 64, two per SIMD) where N is a multiple of 256, else
 // gemm_big_bf16 (128 x 128 x 32 tiles).  The fp32 model uses a 16x16 tiled VALU kernel whose
@@ -20,78 +20,153 @@ namespace {
 
 constexpr int SK_NB = 64;
 constexpr int SK_KC = 256;
-constexpr int SK_XP = SK_KC + 8;
+#ifndef SK_NT
+#define SK_NT 0  // weight loads marked non-temporal
+#endif
 
 // PACKED: W in the fragment-major layout of pack_weights (each wave's 16 B per lane weight loads
-// read one contiguous 1 KB tile); otherwise row-major [N][K].  Same MFMAs in the same order.
-template <bool PACKED>
-__global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-                                                        float* __restrict__ P, int M, int N, int K, int kps) {
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[64 * SK_XP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// read one contiguous 1 KB tile); otherwise row-major [N][K].  NMT: 16-row tiles of X (M <= 16
+// NMT).  Same MFMAs in the same order for every variant.
+//
+// k advances SK_KC = 256 at a time.  Weights go to registers, two chunks ahead: chunk i + 2 is
+// loaded into the register set chunk i has just used (two sets, alternating), so every wave has
+// up to 16 KB of weights in flight.  X (M rows padded to 16 NMT) goes to a double-buffered LDS
+// tile of 512-byte rows by direct-to-LDS buffer loads, one chunk ahead; the buffer resource ends
+// at row M, so the padding rows load as zero.  Within a row the 16-byte chunks are XOR-swizzled
+// by the row's low four bits, so the sixteen rows one fragment read touches fall in distinct
+// banks.  One barrier per chunk, after a wait for this wave's loads of the chunk (X chunk i and,
+// older, weight chunk i; only weight chunk i + 1 may stay in flight); it carries no memory fence,
+// which would wait for every load in flight.  After it no wave still reads the other X buffer,
+// which is then refilled with chunk i + 1.  Every chunk loads all eight weight tiles per lane
+// (the second half of a 128-long last chunk re-reads the first half's tiles, unused), and the
+// main loop (pairs of chunks, both register sets) issues its loads unconditionally, so the
+// compiler's own waits before each MFMA count exactly the loads issued after its operand's.
+template <bool PACKED, int NMT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gemm_skinny_bf16(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, float* __restrict__ P, int M, int N, int K,
+    int kps) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int ROWS = 16 * NMT, NX = ROWS / 8;  // X rows in LDS; X instructions per wave and chunk
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2 * ROWS * SK_KC];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int n0 = blockIdx.x * SK_NB + wave * 16;
   const int s = blockIdx.y;
   const int k_lo = s * kps, k_hi = min(K, k_lo + kps);
-  const int n_mt = (M + 15) >> 4;
-  f32x4 acc[4];
+  const int nch = (k_hi - k_lo + SK_KC - 1) / SK_KC;
+  f32x4 acc[NMT];
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4{0, 0, 0, 0};
-  const uint16_t* wrow = PACKED ? W + int64_t(n0 >> 4) * (K >> 5) * 512 + 8 * lane : W + int64_t(n0 + r) * K;
-
-  u32x4 wf[2][4];
-  auto load_w = [&](int kc) {
-    const int klen = min(SK_KC, k_hi - kc);
+  for (int mt = 0; mt < NMT; mt++) acc[mt] = f32x4{0, 0, 0, 0};
+  // this wave's weights through a buffer resource: the chunk's byte offset is uniform (soffset),
+  // the lane's and the tile's are the constant voffset and immediate, so a load holds no address
+  // registers.  PACKED: the wave's 16 rows are K / 32 consecutive 1 KB tiles; else 16 rows of K.
+  const uint16_t* wbase = PACKED ? W + int64_t(n0 >> 4) * (K >> 5) * 512 : W + int64_t(n0) * K;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wbase), 0, 16 * K * 2, BUF_DWORD3);
+  const int wlane = PACKED ? 16 * lane : r * K * 2 + 16 * g;
+  auto load_w = [&](u32x4(&S)[8], int i) {
+    const int kc = k_lo + SK_KC * i, klen = min(SK_KC, k_hi - kc);
+    const int half = 128 < klen ? 1 : 0;  // a 128-long chunk re-reads its first half as the second
 #pragma unroll
     for (int h = 0; h < 2; h++) {
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const uint16_t* src = PACKED ? wrow + int64_t((kc + 128 * h + 32 * e) >> 5) * 512
-                                     : wrow + kc + 128 * h + 32 * e + 8 * g;
-        wf[h][e] = (128 * h < klen) ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+        const int kt = PACKED ? (kc >> 5) * 1024 : 2 * kc;                  // chunk (uniform)
+        const int ko = PACKED ? (4 * h * half + e) * 1024 : 2 * (128 * h * half + 32 * e);
+        S[4 * h + e] = __builtin_amdgcn_raw_buffer_load_b128(rw, wlane + (h ? 0 : ko), kt + (h ? ko : 0),
+                                                             SK_NT ? 2 : 0);
       }
     }
   };
-  if (k_lo < k_hi) load_w(k_lo);
-  for (int kc = k_lo; kc < k_hi; kc += SK_KC) {
-    const int klen = min(SK_KC, k_hi - kc);
-    __syncthreads();
-    const int rows = n_mt * 16;
-    for (int idx = tid; idx < rows * (SK_KC / 8); idx += 256) {
-      const int row = idx / (SK_KC / 8), c8 = idx % (SK_KC / 8);
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (row < M && 8 * c8 < klen) v = *reinterpret_cast<const u32x4*>(X + int64_t(row) * K + kc + 8 * c8);
-      *reinterpret_cast<u32x4*>(Xs + row * SK_XP + 8 * c8) = v;
+  // X chunk i -> buffer buf = i & 1 (a literal at every call): wave instruction j (= 4 t + wave) fills rows 2 j, 2 j + 1; lane ->
+  // row 2 j + lane / 32, LDS slot lane % 32, which holds source chunk slot ^ (row & 15)
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, M * K * 2, BUF_DWORD3);
+  auto load_x = [&](int i, int buf) {
+    const int kc = k_lo + SK_KC * i;
+#pragma unroll
+    for (int t = 0; t < NX; t++) {
+      const int j = 4 * t + wave, row = 2 * j + (lane >> 5);
+      const int c = (lane & 31) ^ (row & 15);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&Xs[(buf * ROWS + 2 * j) * SK_KC], 16,
+                                               row * K * 2 + 2 * (kc + 8 * c), 0, 0, 0);
     }
-    __syncthreads();
-    u32x4 cur[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; h++)
-#pragma unroll
-      for (int e = 0; e < 4; e++) cur[h][e] = wf[h][e];
-    if (kc + SK_KC < k_hi) load_w(kc + SK_KC);
+  };
+  auto compute = [&](const u32x4(&S)[8], int i, int buf) {
+    const int klen = min(SK_KC, k_hi - k_lo - SK_KC * i);
+    const uint16_t* xb = Xs + (buf * ROWS + r) * SK_KC;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       if (128 * h >= klen) break;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
+        const int c = (16 * h + 4 * e + g) ^ r;
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
-          if (mt >= n_mt) break;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(Xs + (16 * mt + r) * SK_XP + 128 * h + 32 * e + 8 * g);
-          acc[mt] = mfma_bf16(a, cur[h][e], acc[mt]);
+        for (int mt = 0; mt < NMT; mt++) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(xb + 16 * mt * SK_KC + 8 * c);
+          acc[mt] = mfma_bf16(a, S[4 * h + e], acc[mt]);
         }
+        // one k step's fragments live at a time (the chunk's MFMAs take a few hundred cycles,
+        // its loads microseconds: no need to read ahead)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  auto sync = [&]() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  u32x4 wa[8], wb[8];
+  // chunk 1 clamped to chunk 0 when there is only one: a redundant load, so the count is fixed
+  load_w(wa, 0);
+  load_x(0, 0);
+  load_w(wb, min(1, nch - 1));
+  int i = 0;
+  for (; i + 3 < nch; i += 2) {  // both steps load: X chunks i + 1, i + 2, weight chunks i + 2, i + 3
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    sync();
+    load_x(i + 1, 1);
+    compute(wa, i, 0);
+    load_w(wa, i + 2);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    sync();
+    load_x(i + 2, 0);
+    compute(wb, i + 1, 1);
+    load_w(wb, i + 3);
   }
+  // the last one to three chunks: loads only of chunks that exist, and the wait for chunk i
+  // leaves weight chunk i + 1 in flight only where it was loaded
+  auto tail = [&](u32x4(&S)[8], int c, int buf) {  // X chunk c is in buffer c & 1 = buf
+    if (c + 1 < nch) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    sync();
+    if (c + 1 < nch) load_x(c + 1, buf ^ 1);
+    compute(S, c, buf);
+    if (c + 2 < nch) load_w(S, c + 2);
+  };
+  if (i < nch) tail(wa, i, 0);  // i is even
+  if (i + 1 < nch) tail(wb, i + 1, 1);
+  if (i + 2 < nch) tail(wa, i + 2, 0);
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++) {
-    if (mt >= n_mt) break;
+  for (int mt = 0; mt < NMT; mt++) {
 #pragma unroll
     for (int jj = 0; jj < 4; jj++) {
       const int m = 16 * mt + 4 * g + jj;
       if (m < M) P[(int64_t(s) * M + m) * N + n0 + r] = acc[mt][jj];
     }
+  }
+}
+
+template <bool PACKED>
+void launch_skinny(const uint16_t* X, const uint16_t* W, float* P, int M, int N, int K, int S, int kps,
+                   hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const dim3 grid(N / SK_NB, S);
+  switch ((M + 15) / 16) {
+    case 1: hipExtLaunchKernelGGL(HIP_KERNEL_NAME(gemm_skinny_bf16<PACKED, 1>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, X, W, P, M, N, K, kps); break;
+    case 2: hipExtLaunchKernelGGL(HIP_KERNEL_NAME(gemm_skinny_bf16<PACKED, 2>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, X, W, P, M, N, K, kps); break;
+    case 3: hipExtLaunchKernelGGL(HIP_KERNEL_NAME(gemm_skinny_bf16<PACKED, 3>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, X, W, P, M, N, K, kps); break;
+    default: hipExtLaunchKernelGGL(HIP_KERNEL_NAME(gemm_skinny_bf16<PACKED, 4>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, X, W, P, M, N, K, kps); break;
   }
 }
 
@@ -486,12 +561,13 @@ vc_status gemm(const void* X, const void* W, float* P, int M, int N, int K, int 
       const int want = S;
       const int kps = int(cdiv(cdiv(K, want), 128) * 128);
       VC_REQUIRE(cdiv(K, kps) == S, VC_ERR_ARG, "gemm: split count %d inconsistent", S);
+      VC_REQUIRE(K <= (1 << 20), VC_ERR_UNSUPPORTED, "gemm: K=%d beyond the 32-bit X offsets", K);
       if (packed)
-        hipExtLaunchKernelGGL(gemm_skinny_bf16<true>, dim3(N / SK_NB, S), dim3(256), 0, s, ev_start, ev_stop, 0,
-                              static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wp), P, M, N, K, kps);
+        launch_skinny<true>(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wp), P, M, N, K, S, kps, s,
+                            ev_start, ev_stop);
       else
-        hipExtLaunchKernelGGL(gemm_skinny_bf16<false>, dim3(N / SK_NB, S), dim3(256), 0, s, ev_start, ev_stop, 0,
-                              static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K, kps);
+        launch_skinny<false>(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), P, M, N, K, S, kps, s,
+                             ev_start, ev_stop);
     } else {
       VC_REQUIRE(S == 1, VC_ERR_ARG, "gemm: prefill tiles use one split");
       if (N % PT == 0 && K <= (1 << 20)) {  // tile offsets (256 K 2 bytes) stay within 32 bits

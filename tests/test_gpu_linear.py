@@ -8,7 +8,8 @@ or repeated k slice, a swapped operand chunk or a wrong output index exceeds
 by orders of magnitude on these inputs.  Shapes span the 256 x 256 prefill tile
 (several tiles, a ragged last row tile, block counts with and without a
 multiple of eight), the 128 x 128 tile (N not a multiple of 256) and the
-weight-streaming kernel (M <= 64); the Llama-3-8B projection shapes of a
+weight-streaming kernel (M <= 64: one to four 16-row tiles, k ranges of one
+to 56 chunks of 256, with and without a 128-long last chunk); the Llama-3-8B projection shapes of a
 2048-row prefill chunk are checked on sampled rows.
 """
 import numpy as np
@@ -51,7 +52,12 @@ def _check(y, x64, w64, rows, label):
     (512, 2048, 1024, "bf16"),    # 2 x 8 = 16 blocks: XCD-grouped block order
     (65, 256, 4096, "bf16"),      # one ragged row tile, K of the 8B width
     (200, 384, 256, "bf16"),      # N not a multiple of 256: 128 x 128 tiles
-    (33, 512, 1024, "bf16"),      # weight-streaming kernel
+    (33, 512, 1024, "bf16"),      # weight-streaming kernel: 3 row tiles, 4 k chunks (main loop once)
+    (16, 1024, 384, "bf16"),      # 1 row tile, 1.5 k chunks (a 128-long last chunk, tail only)
+    (20, 512, 640, "bf16"),       # 2 row tiles, 2.5 k chunks
+    (40, 768, 1152, "bf16"),      # 3 row tiles, 4.5 k chunks (main loop, then a 3-chunk tail)
+    (64, 256, 4096, "bf16"),      # 4 row tiles, 16 k chunks
+    (1, 4096, 14336, "bf16"),     # one row, 56 k chunks (the 8B down projection's K)
     (100, 96, 80, "f32"),         # fp32 model's kernel
 ])
 def test_linear_matches_definition(M, N, K, dtype):

@@ -21,7 +21,7 @@ namespace {
 constexpr int SK_NB = 64;
 constexpr int SK_KC = 256;
 #ifndef SK_NT
-#define SK_NT 0  // weight loads marked non-temporal
+#define SK_NT 1  // weight loads marked non-temporal: streamed once, they leave X and the partials in L2
 #endif
 
 // PACKED: W in the fragment-major layout of pack_weights (each wave's 16 B per lane weight loads
